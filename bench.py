@@ -1,0 +1,204 @@
+"""Benchmark of the MI355X Muon step.
+
+Workload: one grouped Muon step over the GPT-2-small hidden weight set
+(12 layers x {Q, K, V, attn-out 768x768, MLP-up 3072x768, MLP-down
+768x3072} = 72 bf16 matrices, Gaussian gradients with per-matrix scale, zero
+initial momentum), mu 0.95 Nesterov, 5 quintic Newton-Schulz iterations,
+lr 0.02, wd 0.01.  Inputs are generated once and stay resident in HBM.
+
+Prints ONE JSON line: steps/s of the whole step, plus the roofline of the
+dominant kernel (per-launch duration from HIP events recorded between the
+launches on the launch stream) and the float64 CPU oracle timed on a bounded
+sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+METRIC = "Muon steps/sec over a GPT-2-small weight set; NS TFLOP/s as % of bf16 MFMA peak"
+
+
+def ns_flops(m, n):
+    """Algorithmic flops of the three NS products of one iteration, using the
+    symmetry of A and B: Gram m(m+1)n, square m^2(m+1), update 2 m^2 n."""
+    return {"gram": m * (m + 1) * n, "square": m * m * (m + 1), "bx": 2 * m * m * n}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "matrix_aware_optimizer_muon_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, src_hash):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if
+    they were taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", "traffic_gpt2s.json")
+    try:
+        with open(p) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_hash") != src_hash:
+        return None
+    return d.get("per_launch_bytes", {}).get(kernel)
+
+
+def cpu_baseline(wl, hp, budget_s):
+    """The float64 oracle on whole layers of the same workload until the
+    time budget is spent; steps/s scaled from the layers done."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    import synth
+    from oracle import muon_oracle as orc
+    layers = sorted({t.layer for t in wl.tensors})
+    done, spent = 0, 0.0
+    for layer in layers:
+        specs = [t for t in wl.tensors if t.layer == layer]
+        inputs = [(orc.bf16_bits_to_f64(synth.weight(wl, s)), orc.bf16_bits_to_f64(synth.gradient(wl, s)),
+                   synth.momentum0(wl, s)) for s in specs]
+        t0 = time.perf_counter()
+        for (W, G, M) in inputs:
+            orc.muon_step(W, G, M, lr=float(hp.lr), weight_decay=float(hp.weight_decay),
+                          momentum=float(hp.momentum), eps=float(hp.eps))
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= budget_s:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    frac = done / len(layers)
+    return {"value": frac / spent, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 oracle on {done} of {len(layers)} layers ({6 * done} of {len(wl.tensors)} "
+                      f"matrices) in {spent:.1f} s, scaled to one whole step"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (no collectives); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import matrix_aware_optimizer_muon_amd as mm
+    import synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    wl = synth.workload("gpt2s")
+    hp = mm.default_hparams()
+    keep, descs = [], []
+    for s in wl.tensors:
+        G, W, M = synth.gradient(wl, s), synth.weight(wl, s), synth.momentum0(wl, s)
+        tg = torch.from_numpy(G.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        tw = torch.from_numpy(W.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        tm = torch.from_numpy(M).to(dev)
+        keep += [tg, tw, tm]
+        descs.append(mm.tensor_desc(tw, tg, tm))
+    st = mm.MuonStep(descs, hp, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        st.step()
+    torch.cuda.synchronize(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        st.step()
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    # per-launch durations: HIP events recorded between launches on the
+    # launch stream, over a second run of the same steps
+    per = {}
+    nprof = max(3, min(args.steps, 20))
+    for _ in range(nprof):
+        for name, ms in st.step_timed():
+            kind = name.split("/")[0]
+            per.setdefault(kind, []).append(ms)
+    assert st.flags() == 0, "non-finite values in the benchmark step"
+    st.close()
+
+    units = [(min(s.rows, s.cols), max(s.rows, s.cols)) for s in wl.tensors]
+    flops = {"gram": 0, "square": 0, "bx": 0}
+    for m, n in units:
+        for k, v in ns_flops(m, n).items():
+            flops[k] += v
+    elems = sum(s.rows * s.cols for s in wl.tensors)
+    bytes_per_launch = {"momentum": 14 * elems, "update": 8 * elems}
+    totals = {k: sum(v) / nprof for k, v in per.items()}          # ms per step by kernel kind
+    avg = {k: sum(v) / len(v) for k, v in per.items()}             # ms per launch
+    ns_ms = sum(totals[k] for k in ("gram", "square", "bx"))
+    ns_tflop = hp.ns_steps * sum(flops.values()) / 1e12
+    dom = max(totals, key=totals.get)
+    src_hash = kernel_source_hash()
+    if dom in flops:
+        achieved = flops[dom] / (avg[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    else:
+        achieved = bytes_per_launch[dom] / (avg[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["kernel"] = dom
+    roof["avg_launch_ms"] = round(avg[dom], 5)
+    roof["traffic"] = load_traffic(dom, src_hash)
+
+    out = {
+        "metric": METRIC,
+        "value": round(1000.0 / ms_per_step, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gpt2s: GPT-2-small hidden weights, 12 layers x {Q,K,V,O 768x768, "
+                               "MLP-up 3072x768, MLP-down 768x3072} = 72 bf16 matrices; one grouped Muon "
+                               "step (mu 0.95 Nesterov, 5 quintic NS, lr 0.02, wd 0.01)",
+                   "matrices": len(wl.tensors), "params": elems, "parallelism": "single GPU"},
+        "matrices_per_s": round(len(wl.tensors) * 1000.0 / ms_per_step, 1),
+        "ns_tflops": round(ns_tflop / (ns_ms * 1e-3), 2),
+        "ns_frac_bf16_peak": round(ns_tflop / (ns_ms * 1e-3) / PEAK_BF16_TFLOPS, 4),
+        "phase_ms_per_step": {k: round(v, 4) for k, v in totals.items()},
+        "phase_avg_launch_ms": {k: round(v, 5) for k, v in avg.items()},
+        "wall_s_timed": round(wall, 3),
+        "kernel_source_hash": src_hash,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, hp, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

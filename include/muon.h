@@ -1,0 +1,193 @@
+/*
+ * muon.h -- C ABI of the MI355X (gfx950) Muon optimizer step.
+ *
+ * One call of muon_step() applies one Muon step to a list of hidden 2-D
+ * weight matrices on one GPU:
+ *
+ *   momentum with Nesterov look-ahead   (Muon README, "Hyperparameter tuning":
+ *                                        momentum 0.95, Nesterov on)
+ *   Frobenius normalisation of the update (Muon blog by Venkatramana, sec. 3)
+ *   ns_steps quintic Newton-Schulz iterations on the short side
+ *       A = X X^T,  B = b A + c A A,  X <- a X + B X   (same blog, sec. 3;
+ *       a, b, c = 3.4445, -4.7750, 2.0315)
+ *   W <- W - lr*wd*W - lr*scale*O        (Muon README, "Usage": decoupled
+ *                                        weight decay; blog sec. 2: shape scale)
+ *
+ * optionally after the Newton-Muon right-preconditioner G <- G S^-1 built
+ * from a d x d activation second moment (Newton-Muon README, "What Is
+ * Newton-Muon?").
+ *
+ * Memory and ownership
+ *   All tensor pointers are DEVICE pointers owned by the caller (param,
+ *   grad, momentum, update_out, activations) together with one caller-
+ *   allocated device WORKSPACE whose size muon_workspace_size() reports.  The
+ *   library never allocates device memory.  Everything registered at
+ *   muon_init() must stay allocated and unmoved until muon_destroy(); re-init
+ *   after reallocating any of it.  The library owns only a small host-side
+ *   handle.
+ *   Layout: row-major, rows = out-features, element (i, j) at ptr[i*ld + j],
+ *   ld >= cols.  param and grad share one dtype; momentum is always float32.
+ *
+ * Errors
+ *   Argument errors are returned synchronously by muon_workspace_size() and
+ *   muon_init() (and muon_precond_refresh()).  muon_step() only enqueues
+ *   work on the given stream: it never synchronises, never allocates, and
+ *   returns MUON_ERR_HIP only if a launch fails.  Nothing aborts or throws
+ *   across the ABI.  A human-readable detail of the last error on the
+ *   calling thread is available from muon_last_error().  Non-finite values
+ *   propagate as in the plain arithmetic and set bit 0 of the flags word.
+ *
+ * Threading: one handle may be used by one stream at a time.
+ * Streams: `stream` arguments are hipStream_t values passed as void*;
+ *   NULL means the default stream.
+ */
+#ifndef MUON_H
+#define MUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct muon_handle_s* muon_handle_t;
+
+typedef enum {
+  MUON_OK = 0,
+  MUON_ERR_NULL_ARG = 1,           /* a required pointer is NULL                 */
+  MUON_ERR_BAD_SHAPE = 2,          /* rows/cols < 1, ld < cols, bad split        */
+  MUON_ERR_BAD_DTYPE = 3,          /* unknown dtype                              */
+  MUON_ERR_ALIGNMENT = 4,          /* pointer not aligned to its element size    */
+  MUON_ERR_ALIASING = 5,           /* two registered buffers overlap             */
+  MUON_ERR_WORKSPACE_TOO_SMALL = 6,
+  MUON_ERR_UNSUPPORTED = 7,        /* valid request the library does not support */
+  MUON_ERR_HIP = 8,                /* a HIP runtime call or launch failed        */
+  MUON_ERR_BAD_ARG = 9             /* other invalid argument (hyper-parameters)  */
+} muon_status_t;
+
+typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype_t;
+
+/* Shape-dependent lr factor.  The pages name several conventions without
+ * printing a formula; the library offers:
+ *   NONE            1
+ *   ORIGINAL        sqrt(max(1, rows/cols))          (default)
+ *   MATCH_RMS_ADAMW 0.2*sqrt(max(rows, cols))
+ * rows/cols are those of the orthogonalised block (split_rows if set). */
+typedef enum {
+  MUON_SCALE_NONE = 0,
+  MUON_SCALE_ORIGINAL = 1,
+  MUON_SCALE_MATCH_RMS_ADAMW = 2
+} muon_scale_t;
+
+/* Momentum form (the pages give "momentum 0.95, nesterov" only):
+ *   EMA: M' = mu M + (1-mu) G;  U = (1-mu) G + mu M'   (default)
+ *   SGD: M' = mu M + G;         U = G + mu M'
+ * Without Nesterov U = M'. */
+typedef enum { MUON_MOM_EMA = 0, MUON_MOM_SGD = 1 } muon_momentum_form_t;
+
+/* One hidden weight matrix. */
+typedef struct {
+  void* param;          /* rows x cols, dtype; updated in place               */
+  const void* grad;     /* rows x cols, dtype; read only                      */
+  float* momentum;      /* rows x cols float32; updated in place              */
+  int64_t rows, cols;
+  int64_t ld_param, ld_grad, ld_momentum;  /* elements; >= cols               */
+  int32_t dtype;        /* muon_dtype_t of param and grad                     */
+  int32_t split_rows;   /* 0: whole matrix; h > 0: orthogonalise each block of
+                           h consecutive rows separately (packed Q/K/V; Muon
+                           blog sec. 1); h must divide rows                   */
+  int32_t precond;      /* -1: none; else preconditioner slot index           */
+  float lr_mult;        /* per-matrix lr multiplier (1.0 = none)              */
+  float* update_out;    /* optional: rows x cols float32, contiguous (ld =
+                           cols); receives the orthogonalised update O of this
+                           step, before lr/scale.  NULL = not written.        */
+} muon_tensor_t;
+
+/* A preconditioner slot: nblocks inverse second moments of size d x d.  A
+ * matrix using the slot must have cols == d * nblocks; block k acts on
+ * columns [k*d, (k+1)*d) (Newton-Muon README: the MLP contraction uses four
+ * diagonal blocks; Q/K/V, attention output and MLP expansion share one). */
+typedef struct {
+  int64_t d;
+  int32_t nblocks;
+  int32_t reserved;
+} muon_precond_t;
+
+typedef struct {
+  float lr;              /* default 0.02 (Muon README, "Usage")               */
+  float momentum;        /* 0.95                                              */
+  float weight_decay;    /* 0.01                                              */
+  float eps;             /* 1e-7, added to ||U||_F before dividing            */
+  int32_t nesterov;      /* 1                                                 */
+  int32_t ns_steps;      /* 5; 0 <= ns_steps <= 64                            */
+  float ns_a, ns_b, ns_c;/* 3.4445, -4.7750, 2.0315                           */
+  int32_t scale_mode;    /* muon_scale_t, default ORIGINAL                    */
+  int32_t momentum_form; /* muon_momentum_form_t, default EMA                 */
+} muon_hparams_t;
+
+/* Fills the defaults listed above. */
+void muon_default_hparams(muon_hparams_t* hp);
+
+/* Pure host: validates the request and reports the workspace bytes that
+ * muon_init() needs for it.  No GPU call. */
+muon_status_t muon_workspace_size(const muon_tensor_t* tensors, int32_t n_tensors,
+                                  const muon_precond_t* preconds, int32_t n_preconds,
+                                  const muon_hparams_t* hp, size_t* bytes);
+
+/* Validates, plans and binds a handle to the tensors and the workspace
+ * (device memory, >= muon_workspace_size() bytes, 256-byte aligned).  Enqueues
+ * the workspace initialisation (descriptor upload and zero fill) on
+ * `stream`.  The tensors array is copied; the pointers it holds are kept. */
+muon_status_t muon_init(muon_handle_t* out, const muon_tensor_t* tensors, int32_t n_tensors,
+                        const muon_precond_t* preconds, int32_t n_preconds,
+                        const muon_hparams_t* hp, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Newton-Muon: rebuilds block `block` of preconditioner slot `slot` from
+ * n_rows x d activations (row-major, leading dimension ld, dtype) of the
+ * layer input: S = X^T X / n_rows + damping * I (float32), then S^-1 by a
+ * Cholesky factorisation done in float64 (Newton-Muon README, "What Is
+ * Newton-Muon?").  Asynchronous on `stream`.  If S is not numerically
+ * positive definite the slot is filled with NaN and flag bit 1 is set. */
+muon_status_t muon_precond_refresh(muon_handle_t h, int32_t slot, int32_t block,
+                                   const void* acts, int64_t n_rows, int64_t ld,
+                                   int32_t dtype, float damping, void* stream);
+
+/* One Muon step over every registered matrix; lr < 0 uses hp.lr.
+ * Asynchronous on `stream`; no allocation, no synchronisation. */
+muon_status_t muon_step(muon_handle_t h, float lr, void* stream);
+
+/* Like muon_step(), but records HIP events around each kernel phase and
+ * synchronises `stream` at the end; phase_ms[i] receives the elapsed
+ * milliseconds of phase i (see muon_phase_name) and *n_phases their count
+ * (at most max_phases are written).  For profiling only. */
+muon_status_t muon_step_timed(muon_handle_t h, float lr, void* stream,
+                              float* phase_ms, int32_t max_phases, int32_t* n_phases);
+const char* muon_phase_name(muon_handle_t h, int32_t phase);
+
+/* Synchronises `stream` and returns the sticky flag word:
+ * bit 0 = a non-finite value was seen in an update, bit 1 = a
+ * preconditioner factorisation failed.  reset != 0 clears it. */
+muon_status_t muon_get_flags(muon_handle_t h, void* stream, int32_t reset, uint32_t* flags);
+
+/* Synchronises the last stream used and frees the host handle. */
+muon_status_t muon_destroy(muon_handle_t h);
+
+/* Pure host: a JSON description of the plan muon_init() would build
+ * (units, sides, padded sizes, per-phase tile counts, launch order).
+ * Writes at most `len` bytes including the terminator; returns the full
+ * length needed in *needed. */
+muon_status_t muon_plan_describe(const muon_tensor_t* tensors, int32_t n_tensors,
+                                 const muon_precond_t* preconds, int32_t n_preconds,
+                                 const muon_hparams_t* hp, char* buf, size_t len,
+                                 size_t* needed);
+
+const char* muon_status_str(muon_status_t s);
+const char* muon_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_H */

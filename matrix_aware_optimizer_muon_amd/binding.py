@@ -1,0 +1,270 @@
+"""ctypes binding of libmuon.so (include/muon.h).  Argument marshalling only:
+every step of the Muon update runs in the library's HIP kernels.
+
+The library is loaded from this package's lib/ directory.  If it is missing
+or cannot be loaded, every entry point raises: there is no CPU fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+import re
+from typing import List, Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libmuon.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "muon.h")
+
+MUON_OK = 0
+STATUS_NAMES = {
+    0: "MUON_OK", 1: "MUON_ERR_NULL_ARG", 2: "MUON_ERR_BAD_SHAPE", 3: "MUON_ERR_BAD_DTYPE",
+    4: "MUON_ERR_ALIGNMENT", 5: "MUON_ERR_ALIASING", 6: "MUON_ERR_WORKSPACE_TOO_SMALL",
+    7: "MUON_ERR_UNSUPPORTED", 8: "MUON_ERR_HIP", 9: "MUON_ERR_BAD_ARG",
+}
+MUON_F32, MUON_BF16 = 0, 1
+SCALE_NONE, SCALE_ORIGINAL, SCALE_MATCH_RMS_ADAMW = 0, 1, 2
+MOM_EMA, MOM_SGD = 0, 1
+
+
+class MuonTensor(ctypes.Structure):
+    _fields_ = [
+        ("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("momentum", ctypes.c_void_p),
+        ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+        ("ld_param", ctypes.c_int64), ("ld_grad", ctypes.c_int64), ("ld_momentum", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("split_rows", ctypes.c_int32), ("precond", ctypes.c_int32),
+        ("lr_mult", ctypes.c_float), ("update_out", ctypes.c_void_p),
+    ]
+
+
+class MuonPrecond(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int64), ("nblocks", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class MuonHparams(ctypes.Structure):
+    _fields_ = [
+        ("lr", ctypes.c_float), ("momentum", ctypes.c_float), ("weight_decay", ctypes.c_float),
+        ("eps", ctypes.c_float), ("nesterov", ctypes.c_int32), ("ns_steps", ctypes.c_int32),
+        ("ns_a", ctypes.c_float), ("ns_b", ctypes.c_float), ("ns_c", ctypes.c_float),
+        ("scale_mode", ctypes.c_int32), ("momentum_form", ctypes.c_int32),
+    ]
+
+
+class MuonError(RuntimeError):
+    def __init__(self, status, detail=""):
+        self.status = status
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {detail}")
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libmuon.so and declare its signatures.  Raises if it is absent."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"libmuon.so not built: {p} is missing (run __graft_entry__.build())")
+    # One HIP runtime per process: torch ships its own libamdhip64.so.7.  If
+    # torch is importable, load it first so the library's libamdhip64.so.7
+    # dependency resolves to the runtime that owns torch's memory and streams.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(p)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    PT = ctypes.POINTER(MuonTensor)
+    PP = ctypes.POINTER(MuonPrecond)
+    PH = ctypes.POINTER(MuonHparams)
+    sigs = {
+        "muon_default_hparams": (None, [PH]),
+        "muon_workspace_size": (i32, [PT, i32, PP, i32, PH, ctypes.POINTER(sz)]),
+        "muon_init": (i32, [ctypes.POINTER(vp), PT, i32, PP, i32, PH, vp, sz, vp]),
+        "muon_precond_refresh": (i32, [vp, i32, i32, vp, i64, i64, i32, f32, vp]),
+        "muon_step": (i32, [vp, f32, vp]),
+        "muon_step_timed": (i32, [vp, f32, vp, ctypes.POINTER(f32), i32, ctypes.POINTER(i32)]),
+        "muon_phase_name": (ctypes.c_char_p, [vp, i32]),
+        "muon_get_flags": (i32, [vp, vp, i32, ctypes.POINTER(ctypes.c_uint32)]),
+        "muon_destroy": (i32, [vp]),
+        "muon_plan_describe": (i32, [PT, i32, PP, i32, PH, ctypes.c_char_p, sz, ctypes.POINTER(sz)]),
+        "muon_status_str": (ctypes.c_char_p, [i32]),
+        "muon_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def header_functions() -> List[str]:
+    """Names of the functions declared in include/muon.h."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(muon_[a-z_]+)\s*\(", text)))
+
+
+def _check(status, lib=None):
+    if status != MUON_OK:
+        lib = lib or load_library()
+        raise MuonError(status, lib.muon_last_error().decode())
+
+
+def default_hparams(**overrides) -> MuonHparams:
+    hp = MuonHparams()
+    load_library().muon_default_hparams(ctypes.byref(hp))
+    for k, v in overrides.items():
+        if not hasattr(hp, k):
+            raise KeyError(k)
+        setattr(hp, k, v)
+    return hp
+
+
+def _array(items, cls):
+    n = len(items)
+    arr = (cls * max(n, 1))()
+    for i, it in enumerate(items):
+        arr[i] = it
+    return arr, n
+
+
+def workspace_size(tensors: Sequence[MuonTensor], hp: MuonHparams,
+                   preconds: Sequence[MuonPrecond] = ()) -> int:
+    lib = load_library()
+    ta, n = _array(tensors, MuonTensor)
+    pa, npc = _array(preconds, MuonPrecond)
+    out = ctypes.c_size_t(0)
+    _check(lib.muon_workspace_size(ta, n, pa, npc, ctypes.byref(hp), ctypes.byref(out)))
+    return out.value
+
+
+def plan_describe(tensors: Sequence[MuonTensor], hp: MuonHparams,
+                  preconds: Sequence[MuonPrecond] = ()) -> dict:
+    lib = load_library()
+    ta, n = _array(tensors, MuonTensor)
+    pa, npc = _array(preconds, MuonPrecond)
+    need = ctypes.c_size_t(0)
+    _check(lib.muon_plan_describe(ta, n, pa, npc, ctypes.byref(hp), None, 0, ctypes.byref(need)))
+    buf = ctypes.create_string_buffer(need.value)
+    _check(lib.muon_plan_describe(ta, n, pa, npc, ctypes.byref(hp), buf, need.value, ctypes.byref(need)))
+    return json.loads(buf.value.decode())
+
+
+def status_of(fn_result) -> str:
+    return STATUS_NAMES.get(fn_result, str(fn_result))
+
+
+# ---------------------------------------------------------------------------
+# torch-facing wrapper (torch supplies device memory and the stream)
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def tensor_desc(param, grad, momentum, *, split_rows=0, precond=-1, lr_mult=1.0,
+                update_out=None) -> MuonTensor:
+    torch = _torch()
+    if param.dim() != 2 or grad.shape != param.shape or momentum.shape != param.shape:
+        raise ValueError("param, grad and momentum must be 2-D with one shape")
+    for t in (param, grad, momentum):
+        if t.stride(1) != 1:
+            raise ValueError("tensors must be row-major (unit column stride)")
+    if param.dtype != grad.dtype:
+        raise ValueError("param and grad must share a dtype")
+    if momentum.dtype != torch.float32:
+        raise ValueError("momentum must be float32")
+    dt = {torch.float32: MUON_F32, torch.bfloat16: MUON_BF16}.get(param.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {param.dtype}")
+    d = MuonTensor()
+    d.param, d.grad, d.momentum = param.data_ptr(), grad.data_ptr(), momentum.data_ptr()
+    d.rows, d.cols = param.shape
+    d.ld_param, d.ld_grad, d.ld_momentum = param.stride(0), grad.stride(0), momentum.stride(0)
+    d.dtype, d.split_rows, d.precond, d.lr_mult = dt, split_rows, precond, lr_mult
+    if update_out is not None:
+        if update_out.dtype != torch.float32 or not update_out.is_contiguous() or update_out.shape != param.shape:
+            raise ValueError("update_out must be a contiguous float32 tensor of the param's shape")
+        d.update_out = update_out.data_ptr()
+    else:
+        d.update_out = None
+    return d
+
+
+class MuonStep:
+    """One handle over a list of (param, grad, momentum) device tensors.
+
+    The workspace is a torch uint8 tensor owned by this object; the tensors
+    registered must stay alive and unmoved while the object is used.
+    """
+
+    def __init__(self, descs: Sequence[MuonTensor], hp: Optional[MuonHparams] = None,
+                 preconds: Sequence[MuonPrecond] = (), device=None, keepalive=()):
+        torch = _torch()
+        self._lib = load_library()
+        self.hp = hp if hp is not None else default_hparams()
+        self._descs, self._n = _array(list(descs), MuonTensor)
+        self._pcs, self._npc = _array(list(preconds), MuonPrecond)
+        self.workspace_bytes = workspace_size(descs, self.hp, preconds)
+        self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.workspace = torch.empty(max(self.workspace_bytes, 256), dtype=torch.uint8, device=self.device)
+        self._keep = list(keepalive)
+        h = ctypes.c_void_p()
+        _check(self._lib.muon_init(ctypes.byref(h), self._descs, self._n, self._pcs, self._npc,
+                                   ctypes.byref(self.hp), ctypes.c_void_p(self.workspace.data_ptr()),
+                                   self.workspace.numel(), self._stream(None)))
+        self._h = h
+
+    def _stream(self, stream):
+        torch = _torch()
+        s = stream if stream is not None else torch.cuda.current_stream(self.device)
+        return ctypes.c_void_p(s.cuda_stream)
+
+    def step(self, lr: float = -1.0, stream=None):
+        _check(self._lib.muon_step(self._h, ctypes.c_float(lr), self._stream(stream)))
+
+    def step_timed(self, lr: float = -1.0, stream=None):
+        """Run one step with HIP events between launches; returns
+        [(phase_name, ms), ...] (synchronises the stream)."""
+        cap = 4096
+        ms = (ctypes.c_float * cap)()
+        n = ctypes.c_int32(0)
+        _check(self._lib.muon_step_timed(self._h, ctypes.c_float(lr), self._stream(stream), ms, cap,
+                                         ctypes.byref(n)))
+        return [(self._lib.muon_phase_name(self._h, i).decode(), ms[i]) for i in range(min(n.value, cap))]
+
+    def precond_refresh(self, slot: int, block: int, acts, damping: float = 1e-4, stream=None):
+        torch = _torch()
+        if acts.dim() != 2 or acts.stride(1) != 1:
+            raise ValueError("activations must be 2-D row-major")
+        dt = {torch.float32: MUON_F32, torch.bfloat16: MUON_BF16}.get(acts.dtype)
+        if dt is None:
+            raise ValueError(f"unsupported activation dtype {acts.dtype}")
+        self._keep.append(acts)
+        _check(self._lib.muon_precond_refresh(self._h, slot, block, ctypes.c_void_p(acts.data_ptr()),
+                                              acts.shape[0], acts.stride(0), dt, ctypes.c_float(damping),
+                                              self._stream(stream)))
+
+    def flags(self, reset: bool = False, stream=None) -> int:
+        v = ctypes.c_uint32(0)
+        _check(self._lib.muon_get_flags(self._h, self._stream(stream), int(reset), ctypes.byref(v)))
+        return v.value
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _check(self._lib.muon_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

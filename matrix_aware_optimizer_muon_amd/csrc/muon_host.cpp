@@ -1,0 +1,590 @@
+// Host side of the Muon C ABI: validation, planning (units, sides, padding,
+// tile lists, workspace carve-up), descriptor upload and kernel sequencing.
+//
+// Plan of one step (per dtype group, all matrices of the group at once):
+//   momentum  (1 launch)      Muon README "Hyperparameter tuning"
+//   ns_steps x {gram, square, bx}  (3 launches each)   Muon blog sec. 3
+//   update    (1 launch)      Muon README "Usage"
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/muon.h"
+#include "muon_internal.h"
+
+using namespace muon;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+muon_status_t fail(muon_status_t s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+struct UnitPlan {
+  int tensor = 0, block = 0;
+  int64_t row0 = 0;
+  int rows = 0, cols = 0, side = 0, m = 0, n = 0, mp = 0, np = 0;
+  bool f32 = false;
+  float lr_scale = 1.f;
+  size_t off_xh = 0, off_xl = 0, off_xt0 = 0, off_xt1 = 0, off_a = 0, off_b = 0;
+  int k1_tile0 = 0, k1_ntiles = 0, k1_tr = 0, k1_tc = 0;
+  int group_index = 0;  // index inside its dtype group
+};
+
+struct Group {
+  bool f32 = false;
+  std::vector<int> units;  // global unit ids
+  std::vector<EwTask> ew;
+  std::vector<GemmTask> gram, sq, bx;
+  size_t off_units = 0, off_ew = 0, off_gram = 0, off_sq = 0, off_bx = 0;
+};
+
+struct Plan {
+  std::vector<UnitPlan> units;
+  Group groups[2];  // [0] bf16, [1] float32
+  size_t off_flags = 0, off_inv = 0, off_counter = 0, off_partials = 0;
+  size_t meta_bytes = 0, total = 0;
+  int total_k1_tiles = 0;
+  int64_t zero_bytes = 0;  // bytes of NS buffers (zero-filled at init)
+};
+
+bool finite(float x) { return std::isfinite(x); }
+
+float shape_scale(int64_t rows, int64_t cols, int mode) {
+  switch (mode) {
+    case MUON_SCALE_NONE: return 1.f;
+    case MUON_SCALE_ORIGINAL: return std::sqrt(std::max(1.0, double(rows) / double(cols)));
+    case MUON_SCALE_MATCH_RMS_ADAMW: return float(0.2 * std::sqrt(double(std::max(rows, cols))));
+    default: return 1.f;
+  }
+}
+
+muon_status_t validate(const muon_tensor_t* ts, int32_t n, const muon_precond_t* pcs, int32_t npc,
+                       const muon_hparams_t* hp) {
+  if (!hp) return fail(MUON_ERR_NULL_ARG, "hparams is NULL");
+  if (n < 0) return fail(MUON_ERR_BAD_ARG, "n_tensors < 0");
+  if (n > 0 && !ts) return fail(MUON_ERR_NULL_ARG, "tensors is NULL");
+  if (npc < 0) return fail(MUON_ERR_BAD_ARG, "n_preconds < 0");
+  if (npc > 0 && !pcs) return fail(MUON_ERR_NULL_ARG, "preconds is NULL");
+  if (hp->ns_steps < 0 || hp->ns_steps > 64) return fail(MUON_ERR_BAD_ARG, "ns_steps must be in [0, 64]");
+  if (!finite(hp->lr) || !finite(hp->momentum) || !finite(hp->weight_decay) || !finite(hp->eps) ||
+      !finite(hp->ns_a) || !finite(hp->ns_b) || !finite(hp->ns_c))
+    return fail(MUON_ERR_BAD_ARG, "non-finite hyper-parameter");
+  if (hp->eps < 0.f) return fail(MUON_ERR_BAD_ARG, "eps must be >= 0");
+  if (hp->scale_mode < MUON_SCALE_NONE || hp->scale_mode > MUON_SCALE_MATCH_RMS_ADAMW)
+    return fail(MUON_ERR_BAD_ARG, "unknown scale_mode");
+  if (hp->momentum_form != MUON_MOM_EMA && hp->momentum_form != MUON_MOM_SGD)
+    return fail(MUON_ERR_BAD_ARG, "unknown momentum_form");
+  for (int32_t k = 0; k < npc; ++k) {
+    if (pcs[k].d < 1 || pcs[k].nblocks < 1 || pcs[k].d > 16384 || pcs[k].nblocks > 64)
+      return fail(MUON_ERR_BAD_SHAPE, "preconditioner " + std::to_string(k) + ": bad d or nblocks");
+  }
+  struct Range { uintptr_t lo, hi; int t; const char* what; };
+  std::vector<Range> ranges;
+  for (int32_t i = 0; i < n; ++i) {
+    const muon_tensor_t& t = ts[i];
+    const std::string who = "tensor " + std::to_string(i) + ": ";
+    if (!t.param || !t.grad || !t.momentum) return fail(MUON_ERR_NULL_ARG, who + "param, grad and momentum are required");
+    if (t.dtype != MUON_F32 && t.dtype != MUON_BF16) return fail(MUON_ERR_BAD_DTYPE, who + "dtype must be MUON_F32 or MUON_BF16");
+    if (t.rows < 1 || t.cols < 1 || t.rows > (1 << 20) || t.cols > (1 << 20))
+      return fail(MUON_ERR_BAD_SHAPE, who + "rows and cols must be in [1, 2^20]");
+    if (t.ld_param < t.cols || t.ld_grad < t.cols || t.ld_momentum < t.cols)
+      return fail(MUON_ERR_BAD_SHAPE, who + "leading dimensions must be >= cols");
+    if (t.split_rows < 0 || (t.split_rows > 0 && t.rows % t.split_rows != 0))
+      return fail(MUON_ERR_BAD_SHAPE, who + "split_rows must be 0 or divide rows");
+    if (t.precond < -1 || t.precond >= npc) return fail(MUON_ERR_BAD_ARG, who + "precond slot out of range");
+    if (t.precond >= 0) {
+      const muon_precond_t& pc = pcs[t.precond];
+      if (t.cols != pc.d * pc.nblocks)
+        return fail(MUON_ERR_BAD_SHAPE, who + "cols must equal d * nblocks of its preconditioner");
+    }
+    if (!finite(t.lr_mult)) return fail(MUON_ERR_BAD_ARG, who + "lr_mult is not finite");
+    const size_t es = t.dtype == MUON_F32 ? 4 : 2;
+    if (reinterpret_cast<uintptr_t>(t.param) % es || reinterpret_cast<uintptr_t>(t.grad) % es ||
+        reinterpret_cast<uintptr_t>(t.momentum) % 4 || reinterpret_cast<uintptr_t>(t.update_out) % 4)
+      return fail(MUON_ERR_ALIGNMENT, who + "pointers must be aligned to their element size");
+    const int64_t h = t.split_rows ? t.split_rows : t.rows;
+    const int64_t m = std::min<int64_t>(h, t.cols), nn = std::max<int64_t>(h, t.cols);
+    const int64_t T = t.dtype == MUON_F32 ? kTileF32 : kTileBf16;
+    if (round_up(m, T) * round_up(nn, T) > (int64_t(1) << 31))
+      return fail(MUON_ERR_UNSUPPORTED, who + "matrix too large for one orthogonalisation unit");
+    auto add = [&](const void* p, int64_t ld, size_t esz, const char* what) {
+      const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+      const uintptr_t hi = lo + (size_t((t.rows - 1) * ld + t.cols)) * esz;
+      ranges.push_back({lo, hi, i, what});
+    };
+    add(t.param, t.ld_param, es, "param");
+    add(t.grad, t.ld_grad, es, "grad");
+    add(t.momentum, t.ld_momentum, 4, "momentum");
+    if (t.update_out) add(t.update_out, t.cols, 4, "update_out");
+  }
+  std::sort(ranges.begin(), ranges.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  for (size_t k = 1; k < ranges.size(); ++k)
+    if (ranges[k].lo < ranges[k - 1].hi)
+      return fail(MUON_ERR_ALIASING, std::string("buffers overlap: tensor ") + std::to_string(ranges[k - 1].t) +
+                                         " " + ranges[k - 1].what + " and tensor " + std::to_string(ranges[k].t) +
+                                         " " + ranges[k].what);
+  return MUON_OK;
+}
+
+// Longest-processing-time-first order of tiles: larger K first; ties keep
+// unit order so tiles of one matrix stay adjacent (L2 reuse).
+void lpt_sort(std::vector<GemmTask>& v, const std::vector<UnitPlan>& units, const Group& g, int phase) {
+  auto cost = [&](const GemmTask& t) {
+    const UnitPlan& u = units[g.units[t.unit]];
+    return phase == kGram ? int64_t(u.np) : int64_t(u.mp);
+  };
+  std::stable_sort(v.begin(), v.end(), [&](const GemmTask& a, const GemmTask& b) { return cost(a) > cost(b); });
+}
+
+muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_t* pcs, int32_t npc,
+                         const muon_hparams_t* hp, Plan& plan) {
+  muon_status_t st = validate(ts, n, pcs, npc, hp);
+  if (st != MUON_OK) return st;
+  for (int32_t i = 0; i < n; ++i)
+    if (ts[i].precond >= 0)
+      return fail(MUON_ERR_UNSUPPORTED, "tensor " + std::to_string(i) + ": preconditioning not available in this build");
+  plan = Plan();
+  // units
+  for (int32_t i = 0; i < n; ++i) {
+    const muon_tensor_t& t = ts[i];
+    const int64_t h = t.split_rows ? t.split_rows : t.rows;
+    for (int64_t b = 0; b < t.rows / h; ++b) {
+      UnitPlan u;
+      u.tensor = i;
+      u.block = int(b);
+      u.row0 = b * h;
+      u.rows = int(h);
+      u.cols = int(t.cols);
+      u.side = h > t.cols ? kRight : kLeft;
+      u.m = int(std::min<int64_t>(h, t.cols));
+      u.n = int(std::max<int64_t>(h, t.cols));
+      u.f32 = t.dtype == MUON_F32 || u.m < kMinBf16NsSide;   // NS precision of the unit
+      const int T = u.f32 ? kTileF32 : kTileBf16;
+      u.mp = int(round_up(u.m, T));
+      u.np = int(round_up(u.n, T));
+      u.lr_scale = shape_scale(h, t.cols, hp->scale_mode) * t.lr_mult;
+      u.k1_tr = int((h + kEwTile - 1) / kEwTile);
+      u.k1_tc = int((t.cols + kEwTile - 1) / kEwTile);
+      u.k1_ntiles = u.k1_tr * u.k1_tc;
+      u.k1_tile0 = plan.total_k1_tiles;
+      plan.total_k1_tiles += u.k1_ntiles;
+      Group& g = plan.groups[u.f32 ? 1 : 0];
+      g.f32 = u.f32;
+      u.group_index = int(g.units.size());
+      g.units.push_back(int(plan.units.size()));
+      plan.units.push_back(u);
+    }
+  }
+  // tile lists
+  for (Group& g : plan.groups) {
+    for (size_t gi = 0; gi < g.units.size(); ++gi) {
+      const UnitPlan& u = plan.units[g.units[gi]];
+      for (int r = 0; r < u.k1_tr; ++r)
+        for (int c = 0; c < u.k1_tc; ++c) g.ew.push_back({int(gi), r, c, r * u.k1_tc + c});
+      const int T = u.f32 ? kTileF32 : kTileBf16;
+      const int tm = u.mp / T, tn = u.np / T;
+      for (int a = 0; a < tm; ++a)
+        for (int b = a; b < tm; ++b) {
+          g.gram.push_back({int(gi), a, b, 0});
+          g.sq.push_back({int(gi), a, b, 0});
+        }
+      for (int a = 0; a < tm; ++a)
+        for (int b = 0; b < tn; ++b) g.bx.push_back({int(gi), a, b, 0});
+    }
+    lpt_sort(g.gram, plan.units, g, kGram);
+    lpt_sort(g.sq, plan.units, g, kSquare);
+    lpt_sort(g.bx, plan.units, g, kBX);
+  }
+  // workspace: metadata first, then the NS buffers
+  size_t off = 0;
+  plan.off_flags = off; off += kAlign;
+  plan.off_inv = off; off = align_up(off + sizeof(float) * plan.units.size());
+  plan.off_counter = off; off = align_up(off + sizeof(uint32_t) * plan.units.size());
+  plan.off_partials = off; off = align_up(off + sizeof(float) * plan.total_k1_tiles);
+  for (Group& g : plan.groups) {
+    g.off_units = off; off = align_up(off + sizeof(UnitDev) * g.units.size());
+    g.off_ew = off; off = align_up(off + sizeof(EwTask) * g.ew.size());
+    g.off_gram = off; off = align_up(off + sizeof(GemmTask) * g.gram.size());
+    g.off_sq = off; off = align_up(off + sizeof(GemmTask) * g.sq.size());
+    g.off_bx = off; off = align_up(off + sizeof(GemmTask) * g.bx.size());
+  }
+  plan.meta_bytes = off;
+  for (UnitPlan& u : plan.units) {
+    const size_t es = u.f32 ? 4 : 2;
+    const size_t xs = size_t(u.mp) * u.np * es, as = size_t(u.mp) * u.mp * es;
+    u.off_xh = off; off = align_up(off + xs);
+    if (!u.f32) { u.off_xl = off; off = align_up(off + xs); }
+    u.off_xt0 = off; off = align_up(off + xs);
+    u.off_xt1 = off; off = align_up(off + xs);
+    u.off_a = off; off = align_up(off + as);
+    u.off_b = off; off = align_up(off + as);
+  }
+  plan.total = std::max<size_t>(off, kAlign);
+  plan.zero_bytes = int64_t(plan.total - plan.meta_bytes);
+  return MUON_OK;
+}
+
+std::vector<uint8_t> build_meta(const Plan& plan, const muon_tensor_t* ts, uint8_t* ws) {
+  std::vector<uint8_t> meta(plan.meta_bytes, 0);
+  for (const Group& g : plan.groups) {
+    for (size_t gi = 0; gi < g.units.size(); ++gi) {
+      const UnitPlan& up = plan.units[g.units[gi]];
+      const muon_tensor_t& t = ts[up.tensor];
+      const size_t es = t.dtype == MUON_F32 ? 4 : 2;   // element size of param/grad
+      UnitDev d;
+      std::memset(&d, 0, sizeof(d));
+      d.grad = static_cast<const uint8_t*>(t.grad) + size_t(up.row0) * t.ld_grad * es;
+      d.ld_grad = t.ld_grad;
+      d.grad_f32 = t.dtype == MUON_F32;
+      d.vec_grad = reinterpret_cast<uintptr_t>(t.grad) % 16 == 0 && (t.ld_grad * es) % 16 == 0;
+      d.mom = t.momentum + size_t(up.row0) * t.ld_momentum;
+      d.ld_mom = t.ld_momentum;
+      d.vec_mom = reinterpret_cast<uintptr_t>(t.momentum) % 16 == 0 && (t.ld_momentum * 4) % 16 == 0;
+      d.param = static_cast<uint8_t*>(t.param) + size_t(up.row0) * t.ld_param * es;
+      d.ld_param = t.ld_param;
+      d.param_f32 = t.dtype == MUON_F32;
+      d.vec_param = reinterpret_cast<uintptr_t>(t.param) % 16 == 0 && (t.ld_param * es) % 16 == 0;
+      d.update_out = t.update_out ? t.update_out + size_t(up.row0) * t.cols : nullptr;
+      d.ld_out = t.cols;
+      d.vec_out = t.update_out && reinterpret_cast<uintptr_t>(t.update_out) % 16 == 0 && (t.cols * 4) % 16 == 0;
+      d.rows = up.rows;
+      d.cols = up.cols;
+      d.side = up.side;
+      d.m = up.m; d.n = up.n; d.mp = up.mp; d.np = up.np;
+      d.xh = ws + up.off_xh;
+      d.xl = up.f32 ? nullptr : ws + up.off_xl;
+      d.xt[0] = ws + up.off_xt0;
+      d.xt[1] = ws + up.off_xt1;
+      d.a = ws + up.off_a;
+      d.b = ws + up.off_b;
+      if (up.side == kLeft) {
+        d.nat_hi = d.xh; d.nat_lo = d.xl; d.ld_nat = up.np;
+        d.tr_hi = d.xt[0]; d.tr_lo = nullptr; d.ld_tr = up.mp;
+      } else {
+        d.nat_hi = d.xt[0]; d.nat_lo = nullptr; d.ld_nat = up.mp;
+        d.tr_hi = d.xh; d.tr_lo = d.xl; d.ld_tr = up.np;
+      }
+      const size_t uid = size_t(&up - plan.units.data());
+      d.partials = reinterpret_cast<float*>(ws + plan.off_partials) + up.k1_tile0;
+      d.inv = reinterpret_cast<float*>(ws + plan.off_inv) + uid;
+      d.counter = reinterpret_cast<uint32_t*>(ws + plan.off_counter) + uid;
+      d.k1_tile0 = up.k1_tile0;
+      d.k1_ntiles = up.k1_ntiles;
+      d.lr_scale = up.lr_scale;
+      std::memcpy(meta.data() + g.off_units + gi * sizeof(UnitDev), &d, sizeof(d));
+    }
+    auto put = [&](size_t o, const void* src, size_t bytes) {
+      if (bytes) std::memcpy(meta.data() + o, src, bytes);
+    };
+    put(g.off_ew, g.ew.data(), g.ew.size() * sizeof(EwTask));
+    put(g.off_gram, g.gram.data(), g.gram.size() * sizeof(GemmTask));
+    put(g.off_sq, g.sq.data(), g.sq.size() * sizeof(GemmTask));
+    put(g.off_bx, g.bx.data(), g.bx.size() * sizeof(GemmTask));
+  }
+  return meta;
+}
+
+}  // namespace
+
+struct muon_handle_s {
+  Plan plan;
+  muon_hparams_t hp;
+  std::vector<muon_tensor_t> tensors;
+  uint8_t* ws = nullptr;
+  std::vector<uint8_t> meta;  // host copy of the uploaded descriptors (kept for the async copy)
+  hipStream_t last_stream = nullptr;
+  std::vector<hipEvent_t> events;
+  std::vector<std::string> phase_names;
+};
+
+namespace {
+
+// Enqueue one whole step.  With `ev` non-null, record ev[k] before launch k
+// and ev[last] after the final one.
+muon_status_t enqueue_step(muon_handle_t h, float lr, hipStream_t s, std::vector<hipEvent_t>* ev) {
+  const Plan& plan = h->plan;
+  const muon_hparams_t& hp = h->hp;
+  size_t ek = 0;
+  auto mark = [&]() -> bool {
+    if (!ev) return true;
+    return hipEventRecord((*ev)[ek++], s) == hipSuccess;
+  };
+  if (!mark()) return fail(MUON_ERR_HIP, "hipEventRecord failed");
+  for (const Group& g : plan.groups) {
+    if (g.units.empty()) continue;
+    const UnitDev* units = reinterpret_cast<const UnitDev*>(h->ws + g.off_units);
+    K1Params k1{hp.momentum, hp.eps, hp.nesterov, hp.momentum_form == MUON_MOM_SGD,
+                reinterpret_cast<uint32_t*>(h->ws + plan.off_flags)};
+    hipError_t e = launch_momentum(g.f32, units, reinterpret_cast<const EwTask*>(h->ws + g.off_ew),
+                                   int(g.ew.size()), k1, s);
+    if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("momentum launch: ") + hipGetErrorString(e));
+    for (int it = 0; it < hp.ns_steps; ++it) {
+      GemmParams gp{hp.ns_a, hp.ns_b, hp.ns_c, it == 0, it & 1};
+      e = launch_gemm(kGram, g.f32, units, reinterpret_cast<const GemmTask*>(h->ws + g.off_gram),
+                      int(g.gram.size()), gp, s);
+      if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("gram launch: ") + hipGetErrorString(e));
+      e = launch_gemm(kSquare, g.f32, units, reinterpret_cast<const GemmTask*>(h->ws + g.off_sq),
+                      int(g.sq.size()), gp, s);
+      if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("square launch: ") + hipGetErrorString(e));
+      e = launch_gemm(kBX, g.f32, units, reinterpret_cast<const GemmTask*>(h->ws + g.off_bx),
+                      int(g.bx.size()), gp, s);
+      if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("bx launch: ") + hipGetErrorString(e));
+    }
+    K5Params k5{lr, hp.weight_decay, hp.ns_steps == 0, 0};
+    e = launch_update(g.f32, units, reinterpret_cast<const EwTask*>(h->ws + g.off_ew), int(g.ew.size()), k5, s);
+    if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("update launch: ") + hipGetErrorString(e));
+  }
+  h->last_stream = s;
+  return MUON_OK;
+}
+
+std::string plan_json(const Plan& plan, const muon_hparams_t& hp) {
+  std::string s = "{\"units\":[";
+  char buf[512];
+  for (size_t i = 0; i < plan.units.size(); ++i) {
+    const UnitPlan& u = plan.units[i];
+    std::snprintf(buf, sizeof(buf),
+                  "%s{\"tensor\":%d,\"block\":%d,\"row0\":%lld,\"rows\":%d,\"cols\":%d,\"side\":\"%s\","
+                  "\"m\":%d,\"n\":%d,\"mp\":%d,\"np\":%d,\"ns\":\"%s\",\"lr_scale\":%.9g,\"k1_tiles\":%d}",
+                  i ? "," : "", u.tensor, u.block, (long long)u.row0, u.rows, u.cols,
+                  u.side == kLeft ? "left" : "right", u.m, u.n, u.mp, u.np, u.f32 ? "f32" : "bf16",
+                  double(u.lr_scale), u.k1_ntiles);
+    s += buf;
+  }
+  s += "],\"groups\":[";
+  bool first = true;
+  for (const Group& g : plan.groups) {
+    if (g.units.empty()) continue;
+    std::snprintf(buf, sizeof(buf),
+                  "%s{\"ns\":\"%s\",\"units\":%zu,\"momentum_tiles\":%zu,\"gram_tiles\":%zu,"
+                  "\"square_tiles\":%zu,\"bx_tiles\":%zu,\"tile\":%d}",
+                  first ? "" : ",", g.f32 ? "f32" : "bf16", g.units.size(), g.ew.size(), g.gram.size(),
+                  g.sq.size(), g.bx.size(), g.f32 ? kTileF32 : kTileBf16);
+    s += buf;
+    first = false;
+  }
+  s += "],\"launch_order\":[";
+  first = true;
+  for (const Group& g : plan.groups) {
+    if (g.units.empty()) continue;
+    const char* dt = g.f32 ? "f32" : "bf16";
+    std::snprintf(buf, sizeof(buf), "%s\"momentum/%s\"", first ? "" : ",", dt);
+    s += buf;
+    first = false;
+    for (int it = 0; it < hp.ns_steps; ++it) {
+      std::snprintf(buf, sizeof(buf), ",\"gram/%s\",\"square/%s\",\"bx/%s\"", dt, dt, dt);
+      s += buf;
+    }
+    std::snprintf(buf, sizeof(buf), ",\"update/%s\"", dt);
+    s += buf;
+  }
+  std::snprintf(buf, sizeof(buf), "],\"workspace_bytes\":%zu,\"meta_bytes\":%zu}", plan.total, plan.meta_bytes);
+  s += buf;
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+void muon_default_hparams(muon_hparams_t* hp) {
+  if (!hp) return;
+  hp->lr = 0.02f;
+  hp->momentum = 0.95f;
+  hp->weight_decay = 0.01f;
+  hp->eps = 1e-7f;
+  hp->nesterov = 1;
+  hp->ns_steps = 5;
+  hp->ns_a = 3.4445f;
+  hp->ns_b = -4.7750f;
+  hp->ns_c = 2.0315f;
+  hp->scale_mode = MUON_SCALE_ORIGINAL;
+  hp->momentum_form = MUON_MOM_EMA;
+}
+
+muon_status_t muon_workspace_size(const muon_tensor_t* tensors, int32_t n_tensors, const muon_precond_t* preconds,
+                                  int32_t n_preconds, const muon_hparams_t* hp, size_t* bytes) {
+  if (!bytes) return fail(MUON_ERR_NULL_ARG, "bytes is NULL");
+  Plan plan;
+  muon_status_t st = build_plan(tensors, n_tensors, preconds, n_preconds, hp, plan);
+  if (st != MUON_OK) return st;
+  *bytes = plan.total;
+  return MUON_OK;
+}
+
+muon_status_t muon_plan_describe(const muon_tensor_t* tensors, int32_t n_tensors, const muon_precond_t* preconds,
+                                 int32_t n_preconds, const muon_hparams_t* hp, char* buf, size_t len,
+                                 size_t* needed) {
+  Plan plan;
+  muon_status_t st = build_plan(tensors, n_tensors, preconds, n_preconds, hp, plan);
+  if (st != MUON_OK) return st;
+  const std::string js = plan_json(plan, *hp);
+  if (needed) *needed = js.size() + 1;
+  if (buf && len) {
+    const size_t k = std::min(len - 1, js.size());
+    std::memcpy(buf, js.data(), k);
+    buf[k] = 0;
+  }
+  return MUON_OK;
+}
+
+muon_status_t muon_init(muon_handle_t* out, const muon_tensor_t* tensors, int32_t n_tensors,
+                        const muon_precond_t* preconds, int32_t n_preconds, const muon_hparams_t* hp,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!out) return fail(MUON_ERR_NULL_ARG, "out is NULL");
+  *out = nullptr;
+  Plan plan;
+  muon_status_t st = build_plan(tensors, n_tensors, preconds, n_preconds, hp, plan);
+  if (st != MUON_OK) return st;
+  if (!workspace) return fail(MUON_ERR_NULL_ARG, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(MUON_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  if (workspace_bytes < plan.total)
+    return fail(MUON_ERR_WORKSPACE_TOO_SMALL,
+                "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " + std::to_string(plan.total));
+  const uintptr_t wlo = reinterpret_cast<uintptr_t>(workspace), whi = wlo + plan.total;
+  for (int32_t i = 0; i < n_tensors; ++i) {
+    const muon_tensor_t& t = tensors[i];
+    const size_t es = t.dtype == MUON_F32 ? 4 : 2;
+    const void* ps[4] = {t.param, t.grad, t.momentum, t.update_out};
+    const int64_t lds[4] = {t.ld_param, t.ld_grad, t.ld_momentum, t.cols};
+    const size_t ess[4] = {es, es, 4, 4};
+    for (int k = 0; k < 4; ++k) {
+      if (!ps[k]) continue;
+      const uintptr_t lo = reinterpret_cast<uintptr_t>(ps[k]);
+      const uintptr_t hi = lo + size_t((t.rows - 1) * lds[k] + t.cols) * ess[k];
+      if (lo < whi && wlo < hi)
+        return fail(MUON_ERR_ALIASING, "tensor " + std::to_string(i) + " overlaps the workspace");
+    }
+  }
+  muon_handle_s* h = new (std::nothrow) muon_handle_s();
+  if (!h) return fail(MUON_ERR_UNSUPPORTED, "host allocation failed");
+  h->plan = std::move(plan);
+  h->hp = *hp;
+  h->tensors.assign(tensors, tensors + n_tensors);
+  h->ws = static_cast<uint8_t*>(workspace);
+  h->meta = build_meta(h->plan, tensors, h->ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemsetAsync(h->ws, 0, h->plan.total, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(h->ws, h->meta.data(), h->meta.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);  // the host copy of meta may be reused after init
+  if (e != hipSuccess) {
+    delete h;
+    return fail(MUON_ERR_HIP, std::string("workspace initialisation: ") + hipGetErrorString(e));
+  }
+  h->last_stream = s;
+  for (const Group& g : h->plan.groups) {
+    if (g.units.empty()) continue;
+    const std::string dt = g.f32 ? "/f32" : "/bf16";
+    h->phase_names.push_back("momentum" + dt);
+    for (int it = 0; it < hp->ns_steps; ++it) {
+      h->phase_names.push_back("gram" + dt + "#" + std::to_string(it + 1));
+      h->phase_names.push_back("square" + dt + "#" + std::to_string(it + 1));
+      h->phase_names.push_back("bx" + dt + "#" + std::to_string(it + 1));
+    }
+    h->phase_names.push_back("update" + dt);
+  }
+  *out = h;
+  return MUON_OK;
+}
+
+muon_status_t muon_precond_refresh(muon_handle_t h, int32_t, int32_t, const void*, int64_t, int64_t, int32_t,
+                                   float, void*) {
+  if (!h) return fail(MUON_ERR_NULL_ARG, "handle is NULL");
+  return fail(MUON_ERR_UNSUPPORTED, "preconditioning not available in this build");
+}
+
+muon_status_t muon_step(muon_handle_t h, float lr, void* stream) {
+  if (!h) return fail(MUON_ERR_NULL_ARG, "handle is NULL");
+  if (!std::isfinite(lr)) return fail(MUON_ERR_BAD_ARG, "lr is not finite");
+  return enqueue_step(h, lr < 0.f ? h->hp.lr : lr, static_cast<hipStream_t>(stream), nullptr);
+}
+
+muon_status_t muon_step_timed(muon_handle_t h, float lr, void* stream, float* phase_ms, int32_t max_phases,
+                              int32_t* n_phases) {
+  if (!h) return fail(MUON_ERR_NULL_ARG, "handle is NULL");
+  if (!std::isfinite(lr)) return fail(MUON_ERR_BAD_ARG, "lr is not finite");
+  const size_t np = h->phase_names.size();
+  if (h->events.size() < np + 1) {
+    while (h->events.size() < np + 1) {
+      hipEvent_t ev;
+      if (hipEventCreate(&ev) != hipSuccess) return fail(MUON_ERR_HIP, "hipEventCreate failed");
+      h->events.push_back(ev);
+    }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  muon_status_t st = enqueue_step(h, lr < 0.f ? h->hp.lr : lr, s, &h->events);
+  if (st != MUON_OK) return st;
+  if (hipEventSynchronize(h->events[np]) != hipSuccess) return fail(MUON_ERR_HIP, "hipEventSynchronize failed");
+  const size_t k = std::min<size_t>(np, max_phases > 0 ? size_t(max_phases) : 0);
+  for (size_t i = 0; i < k; ++i) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, h->events[i], h->events[i + 1]) != hipSuccess)
+      return fail(MUON_ERR_HIP, "hipEventElapsedTime failed");
+    if (phase_ms) phase_ms[i] = ms;
+  }
+  if (n_phases) *n_phases = int32_t(np);
+  return MUON_OK;
+}
+
+const char* muon_phase_name(muon_handle_t h, int32_t phase) {
+  if (!h || phase < 0 || size_t(phase) >= h->phase_names.size()) return "";
+  return h->phase_names[size_t(phase)].c_str();
+}
+
+muon_status_t muon_get_flags(muon_handle_t h, void* stream, int32_t reset, uint32_t* flags) {
+  if (!h || !flags) return fail(MUON_ERR_NULL_ARG, "handle or flags is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipMemcpy(&v, h->ws + h->plan.off_flags, sizeof(v), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && reset) {
+    e = hipMemsetAsync(h->ws + h->plan.off_flags, 0, sizeof(uint32_t), s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+  }
+  if (e != hipSuccess) return fail(MUON_ERR_HIP, std::string("flags: ") + hipGetErrorString(e));
+  *flags = v;
+  return MUON_OK;
+}
+
+muon_status_t muon_destroy(muon_handle_t h) {
+  if (!h) return MUON_OK;
+  hipError_t e = hipStreamSynchronize(h->last_stream);
+  for (hipEvent_t ev : h->events) (void)hipEventDestroy(ev);
+  delete h;
+  if (e != hipSuccess) return fail(MUON_ERR_HIP, std::string("destroy: ") + hipGetErrorString(e));
+  return MUON_OK;
+}
+
+const char* muon_status_str(muon_status_t s) {
+  switch (s) {
+    case MUON_OK: return "MUON_OK";
+    case MUON_ERR_NULL_ARG: return "MUON_ERR_NULL_ARG";
+    case MUON_ERR_BAD_SHAPE: return "MUON_ERR_BAD_SHAPE";
+    case MUON_ERR_BAD_DTYPE: return "MUON_ERR_BAD_DTYPE";
+    case MUON_ERR_ALIGNMENT: return "MUON_ERR_ALIGNMENT";
+    case MUON_ERR_ALIASING: return "MUON_ERR_ALIASING";
+    case MUON_ERR_WORKSPACE_TOO_SMALL: return "MUON_ERR_WORKSPACE_TOO_SMALL";
+    case MUON_ERR_UNSUPPORTED: return "MUON_ERR_UNSUPPORTED";
+    case MUON_ERR_HIP: return "MUON_ERR_HIP";
+    case MUON_ERR_BAD_ARG: return "MUON_ERR_BAD_ARG";
+  }
+  return "MUON_ERR_UNKNOWN";
+}
+
+const char* muon_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

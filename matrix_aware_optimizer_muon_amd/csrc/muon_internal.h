@@ -1,0 +1,91 @@
+// Internal types shared by the host planner (muon_host.cpp) and the gfx950
+// kernels (*.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace muon {
+
+// Output tile edge of the Newton-Schulz GEMM phases.  bf16 matrices use
+// 256x256 tiles (4 waves of 128x128, bf16 MFMA 32x32x16); float32 matrices
+// use 64x64 tiles (4 waves of 32x32, fp32 MFMA 32x32x2).  Every NS buffer is
+// zero-padded to a multiple of the tile in both dimensions; zero padding is
+// exact under X X^T, A A and B X.
+constexpr int kTileBf16 = 256;
+constexpr int kTileF32 = 64;
+// Edge of the square tiles of the elementwise phases (momentum, update).
+constexpr int kEwTile = 64;
+// bf16 matrices whose short side is below this run their Newton-Schulz
+// iteration on the float32 path: at such sizes the bf16 iteration's own
+// rounding error approaches 2e-2 relative, and the float32 path costs
+// nothing measurable.
+constexpr int kMinBf16NsSide = 128;
+
+enum Side : int32_t { kLeft = 0, kRight = 1 };
+
+// One orthogonalisation problem ("unit"): a whole matrix, or one row block
+// of a matrix registered with split_rows.  Stored shape rows x cols.  Left
+// side (rows <= cols): X = U (m = rows, n = cols).  Right side: X = U^T
+// (m = cols, n = rows).  X is kept in the canonical m x n orientation in the
+// workspace, so the GEMM phases never see a transpose.
+struct UnitDev {
+  // caller tensors (views of this unit's rows)
+  const void* grad;  int64_t ld_grad;  int32_t grad_f32;  int32_t vec_grad;
+  float* mom;        int64_t ld_mom;   int32_t vec_mom;   int32_t pad0;
+  void* param;       int64_t ld_param; int32_t param_f32; int32_t vec_param;
+  float* update_out; int64_t ld_out;   int32_t vec_out;   int32_t pad1;
+  int32_t rows, cols;        // stored shape of the unit
+  int32_t side, m, n, mp, np, pad2;
+  // workspace buffers: bf16 path uses xh/xl (hi/lo master, m x n),
+  // xt[2] (hi of X^T, n x m, ping-pong), a and b (m x m); the fp32 path uses
+  // xh as the fp32 master, xt[2] fp32 and a/b fp32 (xl unused).
+  void* xh; void* xl; void* xt[2]; void* a; void* b;
+  // momentum-phase destinations: "natural" keeps the stored orientation,
+  // "transposed" swaps it (left: nat = X, tr = X^T; right: nat = X^T, tr = X)
+  void* nat_hi; void* nat_lo; int64_t ld_nat;
+  void* tr_hi;  void* tr_lo;  int64_t ld_tr;
+  float* partials;           // one partial sum of squares per momentum tile
+  float* inv;                // 1 / (||U||_F + eps)
+  uint32_t* counter;         // momentum tiles finished (last one resets it)
+  int32_t k1_tile0, k1_ntiles;
+  float lr_scale;            // shape scale * lr_mult
+  int32_t pad3;
+};
+
+struct EwTask { int32_t unit, tr, tc, local; };      // 64x64 tile of a unit
+struct GemmTask { int32_t unit, ti, tj, pad; };      // output tile (ti, tj)
+
+struct K1Params {
+  float mu;
+  float eps;
+  int32_t nesterov;
+  int32_t sgd_form;
+  uint32_t* flags;
+};
+
+struct GemmParams {
+  float a, b, c;
+  int32_t first;       // first NS iteration: fold the norm scale in
+  int32_t xt_in;       // which X^T buffer holds the current iterate
+};
+
+struct K5Params {
+  float lr;
+  float weight_decay;
+  int32_t scale_by_inv;  // ns_steps == 0: O is the normalised U itself
+  int32_t pad;
+};
+
+enum Phase : int32_t { kGram = 0, kSquare = 1, kBX = 2 };
+
+// Launchers (defined in the .hip files).
+hipError_t launch_momentum(bool f32, const UnitDev* units, const EwTask* tasks, int n_tasks,
+                           const K1Params& p, hipStream_t s);
+hipError_t launch_gemm(int phase, bool f32, const UnitDev* units, const GemmTask* tasks,
+                       int n_tasks, const GemmParams& p, hipStream_t s);
+hipError_t launch_update(bool f32, const UnitDev* units, const EwTask* tasks, int n_tasks,
+                         const K5Params& p, hipStream_t s);
+
+}  // namespace muon

@@ -1,0 +1,199 @@
+"""Host-only checks of the C ABI (no GPU): the library loads, exports every
+function include/muon.h declares, validates arguments with the documented
+status codes, and plans the workloads as designed.  Pointers here are fake
+addresses that the library only compares and never dereferences."""
+
+import ctypes
+import math
+import subprocess
+
+import pytest
+
+import matrix_aware_optimizer_muon_amd as mm
+from matrix_aware_optimizer_muon_amd import binding as B
+import synth
+
+lib = pytest.importorskip("matrix_aware_optimizer_muon_amd.binding").load_library()
+
+BASE = 1 << 36
+
+
+def fake(rows, cols, dtype=B.MUON_BF16, base=BASE, split=0, precond=-1, ld=None, out=False):
+    es = 4 if dtype == B.MUON_F32 else 2
+    ld = ld or cols
+    span = ((rows * ld * es + 4095) // 4096 + 1) * 4096
+    mspan = ((rows * ld * 4 + 4095) // 4096 + 1) * 4096
+    t = B.MuonTensor()
+    t.param, t.grad, t.momentum = base, base + span, base + 2 * span
+    t.rows, t.cols = rows, cols
+    t.ld_param = t.ld_grad = t.ld_momentum = ld
+    t.dtype, t.split_rows, t.precond, t.lr_mult = dtype, split, precond, 1.0
+    t.update_out = base + 2 * span + mspan if out else None
+    return t, 3 * span + 2 * mspan
+
+
+def fakes(shapes, dtype=B.MUON_BF16):
+    out, base = [], BASE
+    for r, c in shapes:
+        t, span = fake(r, c, dtype, base)
+        out.append(t)
+        base += span
+    return out
+
+
+def ws_status(tensors, hp=None, preconds=()):
+    hp = hp or mm.default_hparams()
+    ta, n = B._array(tensors, B.MuonTensor)
+    pa, npc = B._array(list(preconds), B.MuonPrecond)
+    out = ctypes.c_size_t(0)
+    st = lib.muon_workspace_size(ta, n, pa, npc, ctypes.byref(hp), ctypes.byref(out))
+    return B.STATUS_NAMES[st], out.value
+
+
+def test_exports_every_declared_symbol():
+    names = mm.header_functions()
+    assert len(names) >= 10
+    dyn = subprocess.run(["nm", "-D", "--defined-only", mm.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
+    exported = {l.split()[-1] for l in dyn.splitlines() if l.strip()}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_default_hparams_are_the_pages_values():
+    hp = mm.default_hparams()
+    assert math.isclose(hp.lr, 0.02, rel_tol=1e-7)
+    assert math.isclose(hp.momentum, 0.95, rel_tol=1e-7)
+    assert math.isclose(hp.weight_decay, 0.01, rel_tol=1e-7)
+    assert hp.nesterov == 1 and hp.ns_steps == 5
+    assert (hp.ns_a, hp.ns_b, hp.ns_c) == tuple(float(ctypes.c_float(x).value) for x in (3.4445, -4.7750, 2.0315))
+    assert hp.scale_mode == B.SCALE_ORIGINAL and hp.momentum_form == B.MOM_EMA
+
+
+def test_status_strings():
+    for code, name in B.STATUS_NAMES.items():
+        assert lib.muon_status_str(code).decode() == name
+
+
+def test_validation_errors():
+    ok = fakes([(64, 128)])
+    assert ws_status(ok)[0] == "MUON_OK"
+    # empty list is a valid no-op
+    assert ws_status([])[0] == "MUON_OK"
+    t = fakes([(64, 128)])[0]; t.rows = 0
+    assert ws_status([t])[0] == "MUON_ERR_BAD_SHAPE"
+    t = fakes([(64, 128)])[0]; t.ld_grad = 100
+    assert ws_status([t])[0] == "MUON_ERR_BAD_SHAPE"
+    t = fakes([(64, 128)])[0]; t.dtype = 7
+    assert ws_status([t])[0] == "MUON_ERR_BAD_DTYPE"
+    t = fakes([(64, 128)])[0]; t.param = BASE + 1
+    assert ws_status([t])[0] == "MUON_ERR_ALIGNMENT"
+    t = fakes([(64, 128)])[0]; t.momentum = t.momentum + 2
+    assert ws_status([t])[0] == "MUON_ERR_ALIGNMENT"
+    t = fakes([(64, 128)])[0]; t.grad = None
+    assert ws_status([t])[0] == "MUON_ERR_NULL_ARG"
+    t = fakes([(96, 128)])[0]; t.split_rows = 40
+    assert ws_status([t])[0] == "MUON_ERR_BAD_SHAPE"
+    t = fakes([(64, 128)])[0]; t.grad = t.param + 64
+    assert ws_status([t])[0] == "MUON_ERR_ALIASING"
+    a, b = fakes([(64, 128), (64, 128)])
+    b.momentum = a.momentum + 128
+    assert ws_status([a, b])[0] == "MUON_ERR_ALIASING"
+    t = fakes([(64, 128)])[0]; t.precond = 0
+    assert ws_status([t])[0] == "MUON_ERR_BAD_ARG"          # no such slot
+    t = fakes([(64, 128)])[0]; t.lr_mult = float("nan")
+    assert ws_status([t])[0] == "MUON_ERR_BAD_ARG"
+    hp = mm.default_hparams(ns_steps=65)
+    assert ws_status(ok, hp)[0] == "MUON_ERR_BAD_ARG"
+    hp = mm.default_hparams(scale_mode=9)
+    assert ws_status(ok, hp)[0] == "MUON_ERR_BAD_ARG"
+    hp = mm.default_hparams(momentum_form=5)
+    assert ws_status(ok, hp)[0] == "MUON_ERR_BAD_ARG"
+    # the message names the offending tensor
+    t = fakes([(64, 128)])[0]; t.ld_param = 3
+    ws_status([t])
+    assert "tensor 0" in lib.muon_last_error().decode()
+
+
+def test_init_rejects_bad_workspace_without_touching_the_gpu():
+    ts = fakes([(64, 128)])
+    ta, n = B._array(ts, B.MuonTensor)
+    pa, npc = B._array([], B.MuonPrecond)
+    hp = mm.default_hparams()
+    need = ws_status(ts)[1]
+    h = ctypes.c_void_p()
+    st = lib.muon_init(ctypes.byref(h), ta, n, pa, npc, ctypes.byref(hp), ctypes.c_void_p(1 << 40), need - 1, None)
+    assert B.STATUS_NAMES[st] == "MUON_ERR_WORKSPACE_TOO_SMALL"
+    st = lib.muon_init(ctypes.byref(h), ta, n, pa, npc, ctypes.byref(hp), ctypes.c_void_p((1 << 40) + 16), need, None)
+    assert B.STATUS_NAMES[st] == "MUON_ERR_ALIGNMENT"
+    st = lib.muon_init(ctypes.byref(h), ta, n, pa, npc, ctypes.byref(hp), None, need, None)
+    assert B.STATUS_NAMES[st] == "MUON_ERR_NULL_ARG"
+    st = lib.muon_init(ctypes.byref(h), ta, n, pa, npc, ctypes.byref(hp), ctypes.c_void_p(ts[0].param), need, None)
+    assert B.STATUS_NAMES[st] == "MUON_ERR_ALIASING"
+    assert B.STATUS_NAMES[lib.muon_step(None, 0.02, None)] == "MUON_ERR_NULL_ARG"
+
+
+def _workload_fakes(name, layers=None):
+    w = synth.workload(name, layers)
+    ts, base = [], BASE
+    for s in w.tensors:
+        dt = B.MUON_F32 if s.dtype == "f32" else B.MUON_BF16
+        t, span = fake(s.rows, s.cols, dt, base, split=s.split_rows)
+        ts.append(t)
+        base += span
+    return ts
+
+
+def test_plan_gpt2_small():
+    plan = mm.plan_describe(_workload_fakes("gpt2s"), mm.default_hparams())
+    units = plan["units"]
+    assert len(units) == 72
+    assert all(u["m"] == 768 for u in units)
+    right = [u for u in units if u["side"] == "right"]
+    assert len(right) == 12 and all((u["rows"], u["cols"], u["n"]) == (3072, 768, 3072) for u in right)
+    assert sum(u["n"] == 3072 for u in units) == 24
+    assert all(abs(u["lr_scale"] - (2.0 if u["side"] == "right" else 1.0)) < 1e-7 for u in units)
+    (g,) = plan["groups"]
+    assert g["gram_tiles"] == 72 * 6 and g["square_tiles"] == 72 * 6
+    assert g["bx_tiles"] == 48 * 9 + 24 * 36
+    assert g["momentum_tiles"] == 12 * (4 * 144 + 2 * 576)
+    order = plan["launch_order"]
+    assert order[0] == "momentum/bf16" and order[-1] == "update/bf16" and len(order) == 17
+    assert order[1:4] == ["gram/bf16", "square/bf16", "bx/bf16"]
+
+
+def test_plan_gpt2_xl_and_padding():
+    plan = mm.plan_describe(_workload_fakes("gpt2xl", layers=2), mm.default_hparams())
+    units = plan["units"]
+    assert all(u["m"] == 1600 and u["mp"] == 1792 for u in units)
+    assert {u["np"] for u in units} == {1792, 6400}
+    assert sum(u["side"] == "right" for u in units) == 2
+
+
+def test_plan_split_rows_and_fp32():
+    t = fakes([(3 * 128, 128)])[0]
+    t.split_rows = 128
+    f = fake(256, 512, B.MUON_F32, base=BASE + (1 << 30))[0]
+    small = fake(17, 33, B.MUON_BF16, base=BASE + (1 << 31))[0]
+    plan = mm.plan_describe([t, f, small], mm.default_hparams())
+    u = plan["units"]
+    assert [x["row0"] for x in u[:3]] == [0, 128, 256]
+    assert all(x["lr_scale"] == 1.0 and x["side"] == "left" and x["ns"] == "bf16" for x in u[:3])
+    assert u[3]["ns"] == "f32" and u[3]["mp"] == 256 and u[3]["np"] == 512
+    # a bf16 matrix with a short side below 128 runs its iteration in float32
+    assert u[4]["ns"] == "f32" and (u[4]["mp"], u[4]["np"]) == (64, 64)
+    assert [g["ns"] for g in plan["groups"]] == ["bf16", "f32"]
+    assert [g["units"] for g in plan["groups"]] == [3, 2]
+    assert len(plan["launch_order"]) == 34
+
+
+def test_workspace_size_formula():
+    # bf16 unit: X hi, X lo, two X^T copies (m_p x n_p bf16 each) + A, B (m_p^2 bf16)
+    ts = fakes([(768, 3072)])
+    need = ws_status(ts)[1]
+    plan = mm.plan_describe(ts, mm.default_hparams())
+    per_unit = 4 * 768 * 3072 * 2 + 2 * 768 * 768 * 2
+    assert need - plan["meta_bytes"] == per_unit
+    # ns_steps does not change the footprint
+    assert ws_status(ts, mm.default_hparams(ns_steps=1))[1] == need

@@ -1,0 +1,306 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on
+identical seeded inputs.
+
+Bars (rel_F = ||x - ref||_F / ||ref||_F in float64, max over matrices):
+  momentum buffer                        <= 1e-6
+  orthogonalised update O, bf16 path     <= 2e-2
+  orthogonalised update O, fp32 path     <= 1e-5
+  new weight, fp32                       rel_F(W' - W) <= 1e-5
+  new weight, bf16                       every element within 1 bf16 ulp of
+                                         RNE(oracle W'), at most 15% off by one
+"""
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import matrix_aware_optimizer_muon_amd as mm
+from matrix_aware_optimizer_muon_amd import binding as B
+import synth
+from synth.workloads import TensorSpec, Workload
+from tests.parity_common import (bf16_ulp_distance, check_w_bf16, from_device, oracle_step, rel_f,
+                                 say, to_device)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+TOL_O = {"bf16": 2e-2, "f32": 1e-5}
+TOL_M = 1e-6
+
+
+class Case:
+    """Device tensors + oracle inputs for one list of matrices."""
+
+    def __init__(self, wl, specs, step=0, M0=None, W0=None):
+        self.wl, self.specs = wl, specs
+        self.G = [synth.gradient(wl, s, step) for s in specs]
+        self.M = M0 if M0 is not None else [synth.momentum0(wl, s) for s in specs]
+        self.W = W0 if W0 is not None else [synth.weight(wl, s) for s in specs]
+        self.dW = [to_device(torch, w, s.dtype) for w, s in zip(self.W, specs)]
+        self.dG = [to_device(torch, g, s.dtype) for g, s in zip(self.G, specs)]
+        self.dM = [torch.from_numpy(m.copy()).cuda() for m in self.M]
+        self.dO = [torch.empty(s.rows, s.cols, dtype=torch.float32, device="cuda") for s in specs]
+
+    def descs(self, lr_mults=None):
+        out = []
+        for k, s in enumerate(self.specs):
+            out.append(mm.tensor_desc(self.dW[k], self.dG[k], self.dM[k], split_rows=s.split_rows,
+                                      lr_mult=1.0 if lr_mults is None else lr_mults[k],
+                                      update_out=self.dO[k]))
+        return out
+
+    def run(self, hp, lr=-1.0, lr_mults=None):
+        st = mm.MuonStep(self.descs(lr_mults), hp)
+        st.step(lr)
+        torch.cuda.synchronize()
+        flags = st.flags()
+        st.close()
+        return flags
+
+    def results(self, k):
+        s = self.specs[k]
+        return (from_device(torch, self.dW[k], s.dtype), self.dM[k].cpu().numpy(),
+                self.dO[k].cpu().numpy())
+
+
+def check(case, hp, idx=None, lr=None, lr_mults=None, label=""):
+    worst = {"M": 0.0, "O": 0.0, "W": 0.0, "Woff": 0.0}
+    for k in (range(len(case.specs)) if idx is None else idx):
+        s = case.specs[k]
+        ref = oracle_step(case.W[k], case.G[k], case.M[k], s.dtype, hp, split_rows=s.split_rows,
+                          lr=lr, lr_mult=1.0 if lr_mults is None else lr_mults[k])
+        W1, M1, O1 = case.results(k)
+        eM, eO = rel_f(M1, ref["M"]), rel_f(O1, ref["O"])
+        assert eM <= TOL_M, f"{label} matrix {k} {s.rows}x{s.cols}: momentum rel_F {eM:.3e}"
+        assert eO <= TOL_O[s.dtype], f"{label} matrix {k} {s.rows}x{s.cols}: O rel_F {eO:.3e}"
+        if s.dtype == "bf16":
+            lr_used = float(hp.lr) if lr is None else lr
+            err, bound, frac = check_w_bf16(W1, ref, lr_used, ref["scale"])
+            assert err <= bound, f"{label} matrix {k}: ||W'-W'_ref|| {err:.3e} > bound {bound:.3e}"
+            if hp.ns_steps == 0:
+                # O is exact to float32 here: W' must be the correctly rounded value
+                assert bf16_ulp_distance(W1, ref["W_bits"]).max() <= 1, f"{label} matrix {k}: W ulp"
+            worst["Woff"] = max(worst["Woff"], 1.0 - frac)
+        else:
+            W0 = np.asarray(case.W[k], np.float64)
+            eW = rel_f(np.asarray(W1, np.float64) - W0, ref["W"] - W0)
+            assert eW <= 1e-5, f"{label} matrix {k}: rel_F(dW) {eW:.3e}"
+            worst["W"] = max(worst["W"], eW)
+        worst["M"] = max(worst["M"], eM)
+        worst["O"] = max(worst["O"], eO)
+    say(f"  {label}: max rel_F M {worst['M']:.2e}  O {worst['O']:.2e}  dW {worst['W']:.2e}  "
+        f"W not bitwise {worst['Woff']:.1%}")
+    return worst
+
+
+def adhoc(name, shapes, dtype, law="gauss", mom0=1e-2, split=None, std=1.0):
+    specs = [TensorSpec(f"m{k}", 0, 1000 + k, r, c, dtype, split_rows=(split or {}).get(k, 0))
+             for k, (r, c) in enumerate(shapes)]
+    return Workload("tiny", specs, grad_law=law, grad_std=std, mom0_std=mom0)
+
+
+# ---------------------------------------------------------------------------
+
+def test_tiny_fp32_workload():
+    say("case: tiny 256x512 fp32, one step")
+    wl = synth.workload("tiny")
+    c = Case(wl, wl.tensors)
+    hp = mm.default_hparams()
+    assert c.run(hp) == 0
+    check(c, hp, label="tiny")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_shapes(dtype):
+    shapes = [(300, 520), (520, 300), (17, 33), (33, 17), (1, 7), (7, 1), (1, 1),
+              (257, 1000), (1000, 257), (64, 64), (3 * 96, 96), (129, 129)]
+    say(f"case: ragged shapes {dtype}")
+    wl = adhoc("ragged", shapes, dtype, split={10: 96})
+    c = Case(wl, wl.tensors)
+    hp = mm.default_hparams()
+    c.run(hp)
+    check(c, hp, label=f"ragged/{dtype}")
+
+
+@pytest.mark.parametrize("variant", ["sgd", "no_nesterov", "ns0", "ns1", "ns3", "scale_none",
+                                     "scale_rms", "lr_mult", "wd0", "lr0", "lr_override"])
+def test_hyperparameter_variants(variant):
+    shapes = [(200, 136), (136, 200), (3 * 64, 64)]
+    say(f"case: variant {variant}")
+    wl = adhoc("var", shapes, "bf16", split={2: 64})
+    c = Case(wl, wl.tensors)
+    kw, lr, mults = {}, -1.0, None
+    if variant == "sgd": kw = dict(momentum_form=B.MOM_SGD)
+    if variant == "no_nesterov": kw = dict(nesterov=0)
+    if variant == "ns0": kw = dict(ns_steps=0)
+    if variant == "ns1": kw = dict(ns_steps=1)
+    if variant == "ns3": kw = dict(ns_steps=3)
+    if variant == "scale_none": kw = dict(scale_mode=B.SCALE_NONE)
+    if variant == "scale_rms": kw = dict(scale_mode=B.SCALE_MATCH_RMS_ADAMW)
+    if variant == "wd0": kw = dict(weight_decay=0.0)
+    if variant == "lr0": lr = 0.0
+    if variant == "lr_override": lr = 0.05
+    if variant == "lr_mult": mults = [0.5, 2.0, 1.5]
+    hp = mm.default_hparams(**kw)
+    c.run(hp, lr=lr, lr_mults=mults)
+    check(c, hp, lr=None if lr < 0 else float(np.float32(lr)),
+          lr_mults=None if mults is None else [float(np.float32(x)) for x in mults], label=variant)
+    if variant == "lr0":
+        for k, s in enumerate(c.specs):
+            assert np.array_equal(c.results(k)[0], c.W[k])
+
+
+def test_zero_gradient_and_nonfinite_flag():
+    say("case: zero gradient / non-finite flag")
+    wl = adhoc("zero", [(64, 96)], "bf16", mom0=0.0)
+    c = Case(wl, wl.tensors)
+    c.dG[0].zero_()
+    c.G[0] = np.zeros_like(c.G[0])
+    hp = mm.default_hparams()
+    assert c.run(hp) == 0
+    W1, M1, O1 = c.results(0)
+    assert np.all(O1 == 0) and np.all(M1 == 0)
+    ref = oracle_step(c.W[0], c.G[0], c.M[0], "bf16", hp)
+    assert bf16_ulp_distance(W1, ref["W_bits"]).max() <= 1     # O = 0: pure decay
+    c2 = Case(wl, wl.tensors)
+    c2.dG[0][3, 5] = float("nan")
+    assert c2.run(hp) & 1
+
+
+def test_gpt2_small_full_grouped_step():
+    say("case: gpt2s full 72-matrix grouped step")
+    wl = synth.workload("gpt2s")
+    c = Case(wl, wl.tensors)
+    hp = mm.default_hparams()
+    assert c.run(hp) == 0
+    # momentum of every matrix (elementwise, cheap); O and W on layers 0 and 11
+    for k, s in enumerate(c.specs):
+        mu = float(hp.momentum)
+        from oracle import muon_oracle as orc
+        Mref, _ = orc.momentum_update(c.M[k], orc.bf16_bits_to_f64(c.G[k]), mu)
+        assert rel_f(c.dM[k].cpu().numpy(), Mref) <= TOL_M
+    sample = [k for k, s in enumerate(c.specs) if s.layer in (0, 11)]
+    w = check(c, hp, idx=sample, label="gpt2s sampled layers 0,11")
+    assert w["O"] < 2e-2
+
+
+def test_square_4096_ten_steps():
+    say("case: square 4096x4096 bf16, 10 consecutive steps")
+    wl = synth.workload("square")
+    spec = wl.tensors[0]
+    c = Case(wl, [spec], step=0)
+    hp = mm.default_hparams()
+    st = mm.MuonStep(c.descs(), hp)
+    from oracle import muon_oracle as orc
+    M_ref = np.asarray(c.M[0], np.float64)
+    W_first = None
+    for step in range(10):
+        G = synth.gradient(wl, spec, step)
+        c.dG[0].copy_(to_device(torch, G, "bf16"))
+        if step == 0:
+            W_first = c.W[0]
+        st.step()
+        torch.cuda.synchronize()
+        M_prev = M_ref
+        M_ref, U = orc.momentum_update(M_ref, orc.bf16_bits_to_f64(G), float(hp.momentum))
+        eM = rel_f(c.dM[0].cpu().numpy(), M_ref)
+        assert eM <= TOL_M, f"step {step}: momentum rel_F {eM:.3e}"
+        if step in (0, 9):
+            O_ref = orc.orthogonalise(U, hp.ns_steps, float(hp.eps), float(hp.ns_a), float(hp.ns_b), float(hp.ns_c))
+            eO = rel_f(c.dO[0].cpu().numpy(), O_ref)
+            say(f"  step {step + 1}: momentum {eM:.2e}  O {eO:.2e}")
+            assert eO <= TOL_O["bf16"]
+            if step == 0:
+                Wref = orc.apply_update(orc.bf16_bits_to_f64(W_first), O_ref, float(hp.lr),
+                                        float(hp.weight_decay), 1.0)
+                ref = {"W": Wref, "O": O_ref, "W_bits": orc.f64_to_bf16_bits(Wref)}
+                err, bound, frac = check_w_bf16(from_device(torch, c.dW[0], "bf16"), ref,
+                                                float(hp.lr), [1.0] * spec.rows)
+                say(f"  step 1: ||dW err|| {err:.3e} <= {bound:.3e}; bitwise {frac:.1%}")
+                assert err <= bound
+    assert st.flags() == 0
+    st.close()
+
+
+def test_gpt2_xl_full_grouped_step_sampled():
+    say("case: gpt2xl full 288-matrix grouped step (sampled check)")
+    wl = synth.workload("gpt2xl")
+    specs = wl.tensors
+    checked = [k for k, s in enumerate(specs) if s.layer == 0 or (s.layer == 47 and s.name in ("mlp_up", "mlp_down"))]
+    gen = torch.Generator(device="cuda").manual_seed(4747)
+    dW, dG, dM, dO, G, W, M = [], [], [], [], {}, {}, {}
+    for k, s in enumerate(specs):
+        if k in checked:
+            G[k], W[k], M[k] = synth.gradient(wl, s), synth.weight(wl, s), synth.momentum0(wl, s)
+            dG.append(to_device(torch, G[k], "bf16"))
+            dW.append(to_device(torch, W[k], "bf16"))
+        else:
+            L = torch.randn(s.rows, 64, device="cuda", generator=gen) / torch.arange(1, 65, device="cuda")
+            R = torch.randn(s.cols, 64, device="cuda", generator=gen)
+            g = L @ R.T / 8.0 + 1e-3 * torch.randn(s.rows, s.cols, device="cuda", generator=gen)
+            dG.append(g.to(torch.bfloat16))
+            dW.append((0.02 * torch.randn(s.rows, s.cols, device="cuda", generator=gen)).to(torch.bfloat16))
+        dM.append(torch.zeros(s.rows, s.cols, device="cuda"))
+        dO.append(torch.empty(s.rows, s.cols, device="cuda") if k in checked else None)
+    descs = [mm.tensor_desc(dW[k], dG[k], dM[k], update_out=dO[k]) for k in range(len(specs))]
+    hp = mm.default_hparams()
+    st = mm.MuonStep(descs, hp)
+    st.step()
+    torch.cuda.synchronize()
+    assert st.flags() == 0
+    st.close()
+    worst = 0.0
+    for k in checked:
+        s = specs[k]
+        ref = oracle_step(W[k], G[k], M[k], "bf16", hp)
+        eO = rel_f(dO[k].cpu().numpy(), ref["O"])
+        eM = rel_f(dM[k].cpu().numpy(), ref["M"])
+        err, bound, frac = check_w_bf16(from_device(torch, dW[k], "bf16"), ref, float(hp.lr), ref["scale"])
+        say(f"  {s.name} layer {s.layer} {s.rows}x{s.cols}: O {eO:.2e}  M {eM:.2e}  "
+            f"W err/bound {err / bound:.2f} bitwise {frac:.1%}")
+        assert eO <= TOL_O["bf16"] and eM <= TOL_M and err <= bound
+        worst = max(worst, eO)
+
+
+def test_determinism_and_resume():
+    say("case: determinism and resume")
+    wl = adhoc("det", [(384, 640), (640, 384)], "bf16")
+    hp = mm.default_hparams()
+
+    def run(steps_a, steps_b):
+        c = Case(wl, wl.tensors)
+        st = mm.MuonStep(c.descs(), hp)
+        for _ in range(steps_a):
+            st.step()
+        torch.cuda.synchronize()
+        st.close()
+        # save and reload the optimizer state (momentum) and weights
+        saved = [(w.clone(), m.clone()) for w, m in zip(c.dW, c.dM)]
+        for k, (w, m) in enumerate(saved):
+            c.dW[k] = w
+            c.dM[k] = m
+        st = mm.MuonStep(c.descs(), hp)
+        for _ in range(steps_b):
+            st.step()
+        torch.cuda.synchronize()
+        st.close()
+        return [from_device(torch, w, "bf16") for w in c.dW] + [m.cpu().numpy() for m in c.dM]
+
+    a = run(3, 0)
+    b = run(3, 0)
+    r = run(2, 1)
+    for x, y, z in zip(a, b, r):
+        assert np.array_equal(x, y)
+        assert np.array_equal(x, z)
+
+
+def test_step_timed_reports_every_launch():
+    wl = adhoc("timed", [(256, 512)], "bf16")
+    c = Case(wl, wl.tensors)
+    st = mm.MuonStep(c.descs(), mm.default_hparams())
+    ph = st.step_timed()
+    st.close()
+    names = [n for n, _ in ph]
+    assert names[0] == "momentum/bf16" and names[-1] == "update/bf16" and len(names) == 17
+    assert all(ms >= 0 for _, ms in ph)
