@@ -1,0 +1,110 @@
+// Device helpers shared by the gfx950 kernels: bf16 <-> float32 conversion
+// and 16-byte vector accesses through address-space-1 (global) pointers, so
+// the compiler emits global_load/store_dwordx4 rather than flat accesses
+// (flat accesses also count against the LDS wait counter).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+#define MUON_GLOBAL __attribute__((address_space(1)))
+
+template <typename T>
+__device__ __forceinline__ T gld(const void* p) {
+  return *(const MUON_GLOBAL T*)p;
+}
+template <typename T>
+__device__ __forceinline__ void gst(void* p, const T& v) {
+  *(MUON_GLOBAL T*)p = v;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// float32 -> bf16, round to nearest even (the compiler's fptrunc, which
+// gfx950 implements with its bf16 conversion instruction).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ u32x4_t pack8_bf16(const float* v) {
+  u32x4_t w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    w[e] = static_cast<uint32_t>(f32_to_bf16(v[2 * e])) |
+           (static_cast<uint32_t>(f32_to_bf16(v[2 * e + 1])) << 16);
+  return w;
+}
+
+__device__ __forceinline__ void unpack8_bf16(const u32x4_t& w, float* v) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = __uint_as_float(w[e] << 16);
+    v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+  }
+}
+
+// 8 consecutive float32 or bf16 elements at element offset `off` of `base`.
+__device__ __forceinline__ void ld8_f32(const void* base, size_t off, float* v) {
+  const float* p = static_cast<const float*>(base) + off;
+  const f32x4_t a = gld<f32x4_t>(p), b = gld<f32x4_t>(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
+}
+__device__ __forceinline__ void st8_f32(void* base, size_t off, const float* v) {
+  float* p = static_cast<float*>(base) + off;
+  f32x4_t a, b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { a[e] = v[e]; b[e] = v[4 + e]; }
+  gst(p, a);
+  gst(p + 4, b);
+}
+__device__ __forceinline__ void ld8_bf16(const void* base, size_t off, float* v) {
+  unpack8_bf16(gld<u32x4_t>(static_cast<const uint16_t*>(base) + off), v);
+}
+__device__ __forceinline__ void st8_bf16(void* base, size_t off, const float* v) {
+  gst(static_cast<uint16_t*>(base) + off, pack8_bf16(v));
+}
+
+template <bool F32>
+__device__ __forceinline__ void ld8(const void* base, size_t off, float* v) {
+  if constexpr (F32) ld8_f32(base, off, v); else ld8_bf16(base, off, v);
+}
+template <bool F32>
+__device__ __forceinline__ void st8(void* base, size_t off, const float* v) {
+  if constexpr (F32) st8_f32(base, off, v); else st8_bf16(base, off, v);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace muon
+
+namespace muon {
+
+// 1 / (||U||_F + eps) of one unit from its per-tile partial sums of squares,
+// folded by a whole 256-thread block in a fixed order (thread t takes
+// partials t, t+256, ...; then a fixed shuffle tree and a fixed sum of the
+// four wave totals), so every block that calls it gets the same bits.
+// `red` is 4 floats of shared memory.  Must be called by all threads.
+__device__ __forceinline__ float unit_inv_norm(const float* partials, int n, float eps, float* red) {
+  float acc = 0.f;
+  for (int k = threadIdx.x; k < n; k += 256) acc += gld<float>(partials + k);
+  acc = wave_sum(acc);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = acc;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  return 1.0f / (sqrtf(tot) + eps);
+}
+
+}  // namespace muon

@@ -54,7 +54,7 @@ struct Group {
 struct Plan {
   std::vector<UnitPlan> units;
   Group groups[2];  // [0] bf16, [1] float32
-  size_t off_flags = 0, off_inv = 0, off_counter = 0, off_partials = 0;
+  size_t off_flags = 0, off_partials = 0;
   size_t meta_bytes = 0, total = 0;
   int total_k1_tiles = 0;
   int64_t zero_bytes = 0;  // bytes of NS buffers (zero-filled at init)
@@ -211,8 +211,6 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
   // workspace: metadata first, then the NS buffers
   size_t off = 0;
   plan.off_flags = off; off += kAlign;
-  plan.off_inv = off; off = align_up(off + sizeof(float) * plan.units.size());
-  plan.off_counter = off; off = align_up(off + sizeof(uint32_t) * plan.units.size());
   plan.off_partials = off; off = align_up(off + sizeof(float) * plan.total_k1_tiles);
   for (Group& g : plan.groups) {
     g.off_units = off; off = align_up(off + sizeof(UnitDev) * g.units.size());
@@ -277,10 +275,7 @@ std::vector<uint8_t> build_meta(const Plan& plan, const muon_tensor_t* ts, uint8
         d.nat_hi = d.xt[0]; d.nat_lo = nullptr; d.ld_nat = up.mp;
         d.tr_hi = d.xh; d.tr_lo = d.xl; d.ld_tr = up.np;
       }
-      const size_t uid = size_t(&up - plan.units.data());
       d.partials = reinterpret_cast<float*>(ws + plan.off_partials) + up.k1_tile0;
-      d.inv = reinterpret_cast<float*>(ws + plan.off_inv) + uid;
-      d.counter = reinterpret_cast<uint32_t*>(ws + plan.off_counter) + uid;
       d.k1_tile0 = up.k1_tile0;
       d.k1_ntiles = up.k1_ntiles;
       d.lr_scale = up.lr_scale;
@@ -326,13 +321,13 @@ muon_status_t enqueue_step(muon_handle_t h, float lr, hipStream_t s, std::vector
   for (const Group& g : plan.groups) {
     if (g.units.empty()) continue;
     const UnitDev* units = reinterpret_cast<const UnitDev*>(h->ws + g.off_units);
-    K1Params k1{hp.momentum, hp.eps, hp.nesterov, hp.momentum_form == MUON_MOM_SGD,
+    K1Params k1{hp.momentum, hp.nesterov, hp.momentum_form == MUON_MOM_SGD,
                 reinterpret_cast<uint32_t*>(h->ws + plan.off_flags)};
     hipError_t e = launch_momentum(g.f32, units, reinterpret_cast<const EwTask*>(h->ws + g.off_ew),
                                    int(g.ew.size()), k1, s);
     if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("momentum launch: ") + hipGetErrorString(e));
     for (int it = 0; it < hp.ns_steps; ++it) {
-      GemmParams gp{hp.ns_a, hp.ns_b, hp.ns_c, it == 0, it & 1};
+      GemmParams gp{hp.ns_a, hp.ns_b, hp.ns_c, hp.eps, it == 0, it & 1};
       e = launch_gemm(kGram, g.f32, units, reinterpret_cast<const GemmTask*>(h->ws + g.off_gram),
                       int(g.gram.size()), gp, s);
       if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("gram launch: ") + hipGetErrorString(e));
@@ -343,7 +338,7 @@ muon_status_t enqueue_step(muon_handle_t h, float lr, hipStream_t s, std::vector
                       int(g.bx.size()), gp, s);
       if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("bx launch: ") + hipGetErrorString(e));
     }
-    K5Params k5{lr, hp.weight_decay, hp.ns_steps == 0, 0};
+    K5Params k5{lr, hp.weight_decay, hp.eps, hp.ns_steps == 0};
     e = launch_update(g.f32, units, reinterpret_cast<const EwTask*>(h->ws + g.off_ew), int(g.ew.size()), k5, s);
     if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("update launch: ") + hipGetErrorString(e));
   }

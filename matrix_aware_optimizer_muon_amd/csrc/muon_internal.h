@@ -9,11 +9,11 @@
 namespace muon {
 
 // Output tile edge of the Newton-Schulz GEMM phases.  bf16 matrices use
-// 256x256 tiles (4 waves of 128x128, bf16 MFMA 32x32x16); float32 matrices
+// 128x128 tiles (4 waves of 64x64, bf16 MFMA 32x32x16); float32 matrices
 // use 64x64 tiles (4 waves of 32x32, fp32 MFMA 32x32x2).  Every NS buffer is
 // zero-padded to a multiple of the tile in both dimensions; zero padding is
 // exact under X X^T, A A and B X.
-constexpr int kTileBf16 = 256;
+constexpr int kTileBf16 = 128;
 constexpr int kTileF32 = 64;
 // Edge of the square tiles of the elementwise phases (momentum, update).
 constexpr int kEwTile = 64;
@@ -47,8 +47,6 @@ struct UnitDev {
   void* nat_hi; void* nat_lo; int64_t ld_nat;
   void* tr_hi;  void* tr_lo;  int64_t ld_tr;
   float* partials;           // one partial sum of squares per momentum tile
-  float* inv;                // 1 / (||U||_F + eps)
-  uint32_t* counter;         // momentum tiles finished (last one resets it)
   int32_t k1_tile0, k1_ntiles;
   float lr_scale;            // shape scale * lr_mult
   int32_t pad3;
@@ -59,7 +57,6 @@ struct GemmTask { int32_t unit, ti, tj, pad; };      // output tile (ti, tj)
 
 struct K1Params {
   float mu;
-  float eps;
   int32_t nesterov;
   int32_t sgd_form;
   uint32_t* flags;
@@ -67,6 +64,7 @@ struct K1Params {
 
 struct GemmParams {
   float a, b, c;
+  float eps;           // Frobenius normalisation guard
   int32_t first;       // first NS iteration: fold the norm scale in
   int32_t xt_in;       // which X^T buffer holds the current iterate
 };
@@ -74,8 +72,8 @@ struct GemmParams {
 struct K5Params {
   float lr;
   float weight_decay;
+  float eps;
   int32_t scale_by_inv;  // ns_steps == 0: O is the normalised U itself
-  int32_t pad;
 };
 
 enum Phase : int32_t { kGram = 0, kSquare = 1, kBX = 2 };

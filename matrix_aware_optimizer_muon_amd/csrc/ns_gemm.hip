@@ -13,11 +13,13 @@
 // with both operands K-contiguous: A is symmetric, so A A = A A^T, and B X
 // reads X^T, which the update epilogue writes alongside X.
 //
-// bf16 path: 256x256 output tile, 4 waves each owning 128x128 (4x4 blocks of
+// bf16 path: 128x128 output tile, 4 waves each owning 64x64 (2x2 blocks of
 // v_mfma_f32_32x32x16_bf16), K staged through LDS 64 deep, double-buffered
-// with register prefetch; X is held as a bf16 hi/lo pair so the a*X term
+// with register prefetch; two blocks fit per CU (74 KB LDS each) so one
+// block's epilogue traffic overlaps the other's MFMA loop; X is held as a bf16 hi/lo pair so the a*X term
 // keeps ~16 significant bits while the MFMA operand is the hi part.
 // fp32 path: 64x64 tile, 4 waves of 32x32, v_mfma_f32_32x32x2f32.
+#include "device_common.h"
 #include "muon_internal.h"
 
 namespace muon {
@@ -25,68 +27,22 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(1))) const u32x4_t gu32x4_t;   // global memory
 
 constexpr int kThreads = 256;
 
 template <bool F32> struct Cfg;
 template <> struct Cfg<false> {
   using E = uint16_t;
-  static constexpr int BT = kTileBf16, WT = 128, BK = 64, PAD = 8;
+  static constexpr int BT = kTileBf16, WT = kTileBf16 / 2, BK = 64, PAD = 8;
 };
 template <> struct Cfg<true> {
   using E = float;
   static constexpr int BT = kTileF32, WT = 32, BK = 32, PAD = 4;
 };
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
-  return __uint_as_float(static_cast<uint32_t>(h) << 16);
-}
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
-}
-__device__ __forceinline__ uint4 pack8_bf16(const float* v) {
-  uint32_t w[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    w[e] = static_cast<uint32_t>(f32_to_bf16(v[2 * e])) |
-           (static_cast<uint32_t>(f32_to_bf16(v[2 * e + 1])) << 16);
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-__device__ __forceinline__ void unpack8_bf16(const uint4& u, float* v) {
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    v[2 * e] = __uint_as_float(w[e] << 16);
-    v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-  }
-}
-
-// Load / store 8 consecutive elements of an NS buffer as float.
-template <bool F32>
-__device__ __forceinline__ void ld8(const void* base, size_t off, float* v) {
-  if constexpr (F32) {
-    const float* p = static_cast<const float*>(base) + off;
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
-    unpack8_bf16(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off), v);
-  }
-}
-template <bool F32>
-__device__ __forceinline__ void st8(void* base, size_t off, const float* v) {
-  if constexpr (F32) {
-    float* p = static_cast<float*>(base) + off;
-    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
-  } else {
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off) = pack8_bf16(v);
-  }
-}
-
 template <bool F32, int PH>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads, 2)
 void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restrict__ tasks,
                     GemmParams p) {
   using C = Cfg<F32>;
@@ -104,6 +60,7 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
                 "epilogue staging must fit in the operand LDS");
 
   __shared__ __attribute__((aligned(16))) E lds[2][2][BT][LDP];
+  __shared__ float red[4];
 
   const GemmTask t = tasks[blockIdx.x];
   const UnitDev& u = units[t.unit];
@@ -131,7 +88,6 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   const int wm = wave >> 1, wn = wave & 1;
   const int lrow = tid / CPR, lchunk = tid % CPR;
 
-  uint4 ra[NPASS], rb[NPASS];
   f32x16_t acc[NB][NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i)
@@ -140,22 +96,36 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto gload = [&](int k0) {
+  // Global (address space 1) views of the two operands, pre-offset to this
+  // thread's first chunk; rows advance by RPP per load pass.
+  const gu32x4_t* ga = (const gu32x4_t*)(pa + static_cast<size_t>(lrow) * ld + lchunk * EPE);
+  const gu32x4_t* gb = (const gu32x4_t*)(pb + static_cast<size_t>(lrow) * ld + lchunk * EPE);
+  const size_t pass_stride = static_cast<size_t>(RPP) * ld / EPE;   // in 16-byte chunks
+  u32x4_t ra[NPASS], rb[NPASS];
 #pragma unroll
-    for (int q = 0; q < NPASS; ++q) {
-      const size_t off = static_cast<size_t>(lrow + q * RPP) * ld + k0 + lchunk * EPE;
-      ra[q] = *reinterpret_cast<const uint4*>(pa + off);
-      rb[q] = *reinterpret_cast<const uint4*>(pb + off);
-    }
-  };
-  auto sstore = [&](int buf) {
+  for (int q = 0; q < NPASS; ++q) {
+    ra[q] = ga[q * pass_stride];
+    rb[q] = gb[q * pass_stride];
+  }
 #pragma unroll
-    for (int q = 0; q < NPASS; ++q) {
-      *reinterpret_cast<uint4*>(&lds[buf][0][lrow + q * RPP][lchunk * EPE]) = ra[q];
-      *reinterpret_cast<uint4*>(&lds[buf][1][lrow + q * RPP][lchunk * EPE]) = rb[q];
+  for (int q = 0; q < NPASS; ++q) {
+    *reinterpret_cast<u32x4_t*>(&lds[0][0][lrow + q * RPP][lchunk * EPE]) = ra[q];
+    *reinterpret_cast<u32x4_t*>(&lds[0][1][lrow + q * RPP][lchunk * EPE]) = rb[q];
+  }
+  __syncthreads();
+
+  const int KT = K / BK;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    const bool more = kt + 1 < KT;
+    if (more) {
+      const size_t koff = static_cast<size_t>(kt + 1) * (BK / EPE);
+#pragma unroll
+      for (int q = 0; q < NPASS; ++q) {
+        ra[q] = ga[q * pass_stride + koff];
+        rb[q] = gb[q * pass_stride + koff];
+      }
     }
-  };
-  auto compute = [&](int buf) {
     if constexpr (!F32) {
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
@@ -197,17 +167,13 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
           }
       }
     }
-  };
-
-  const int KT = K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK);
-    compute(buf);
-    if (kt + 1 < KT) sstore(buf ^ 1);
+    if (more) {
+#pragma unroll
+      for (int q = 0; q < NPASS; ++q) {
+        *reinterpret_cast<u32x4_t*>(&lds[buf ^ 1][0][lrow + q * RPP][lchunk * EPE]) = ra[q];
+        *reinterpret_cast<u32x4_t*>(&lds[buf ^ 1][1][lrow + q * RPP][lchunk * EPE]) = rb[q];
+      }
+    }
     __syncthreads();
   }
 
@@ -216,10 +182,11 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   // segments (natural layout) and column segments (mirror / X^T) as 16-byte
   // vector stores.
   float scale = 1.f;
-  if constexpr (PH == kGram) {
-    if (p.first) { const float iv = *u.inv; scale = iv * iv; }
-  } else if constexpr (PH == kBX) {
-    if (p.first) scale = *u.inv;
+  if constexpr (PH == kGram || PH == kBX) {
+    if (p.first) {
+      const float iv = unit_inv_norm(u.partials, u.k1_ntiles, p.eps, red);
+      scale = PH == kGram ? iv * iv : iv;
+    }
   }
   const bool mirror = (PH == kBX) || (ti != tj);
   float* ep = reinterpret_cast<float*>(&lds[0][0][0][0]) + wave * (32 * EPP);

@@ -155,8 +155,8 @@ def test_plan_gpt2_small():
     assert sum(u["n"] == 3072 for u in units) == 24
     assert all(abs(u["lr_scale"] - (2.0 if u["side"] == "right" else 1.0)) < 1e-7 for u in units)
     (g,) = plan["groups"]
-    assert g["gram_tiles"] == 72 * 6 and g["square_tiles"] == 72 * 6
-    assert g["bx_tiles"] == 48 * 9 + 24 * 36
+    assert g["gram_tiles"] == 72 * 21 and g["square_tiles"] == 72 * 21
+    assert g["bx_tiles"] == 48 * 36 + 24 * 144
     assert g["momentum_tiles"] == 12 * (4 * 144 + 2 * 576)
     order = plan["launch_order"]
     assert order[0] == "momentum/bf16" and order[-1] == "update/bf16" and len(order) == 17
@@ -166,8 +166,8 @@ def test_plan_gpt2_small():
 def test_plan_gpt2_xl_and_padding():
     plan = mm.plan_describe(_workload_fakes("gpt2xl", layers=2), mm.default_hparams())
     units = plan["units"]
-    assert all(u["m"] == 1600 and u["mp"] == 1792 for u in units)
-    assert {u["np"] for u in units} == {1792, 6400}
+    assert all(u["m"] == 1600 and u["mp"] == 1664 for u in units)
+    assert {u["np"] for u in units} == {1664, 6400}
     assert sum(u["side"] == "right" for u in units) == 2
 
 
