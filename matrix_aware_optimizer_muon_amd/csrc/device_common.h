@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "muon_internal.h"
+
 namespace muon {
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -105,6 +107,63 @@ __device__ __forceinline__ float unit_inv_norm(const float* partials, int n, flo
   __syncthreads();
   const float tot = (red[0] + red[1]) + (red[2] + red[3]);
   return 1.0f / (sqrtf(tot) + eps);
+}
+
+}  // namespace muon
+
+namespace muon {
+
+// 8 elements of a row of a caller tensor (float32 or bf16), bounds- and
+// alignment-aware: the vector path needs 16-byte alignment (`vec`) and the
+// whole segment inside the row; otherwise elements are accessed one by one.
+__device__ __forceinline__ void load_row8(const void* base, bool is_f32, int64_t ld, int i, int j0,
+                                          int cols, bool vec, float* v) {
+  const size_t off = static_cast<size_t>(i) * ld + j0;
+  if (vec && j0 + 8 <= cols) {
+    if (is_f32) ld8_f32(base, off, v); else ld8_bf16(base, off, v);
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    v[e] = 0.f;
+    if (j0 + e < cols)
+      v[e] = is_f32 ? gld<float>(static_cast<const float*>(base) + off + e)
+                    : bf16_to_f32(gld<uint16_t>(static_cast<const uint16_t*>(base) + off + e));
+  }
+}
+
+__device__ __forceinline__ void store_row8(void* base, bool is_f32, int64_t ld, int i, int j0,
+                                           int cols, bool vec, const float* v) {
+  const size_t off = static_cast<size_t>(i) * ld + j0;
+  if (vec && j0 + 8 <= cols) {
+    if (is_f32) st8_f32(base, off, v); else st8_bf16(base, off, v);
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (j0 + e < cols) {
+      if (is_f32) gst(static_cast<float*>(base) + off + e, v[e]);
+      else gst(static_cast<uint16_t*>(base) + off + e, f32_to_bf16(v[e]));
+    }
+  }
+}
+
+}  // namespace muon
+
+namespace muon {
+
+// Decoupled decay and the orthogonalised step for one 8-element row segment
+// of a unit's weight: W' = W - lr*wd*W - lr*scale*O (Muon README, "Usage"),
+// computed in float32 and stored with one rounding; O is also copied out if
+// the caller asked for it.  Row i and columns j0.. are unit-local.
+__device__ __forceinline__ void update_w8(const UnitDev& u, int i, int j0, const float* o,
+                                          float decay, float step) {
+  float w[8];
+  load_row8(u.param, u.param_f32, u.ld_param, i, j0, u.cols, u.vec_param, w);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) w[e] = w[e] - decay * w[e] - step * o[e];
+  store_row8(u.param, u.param_f32, u.ld_param, i, j0, u.cols, u.vec_param, w);
+  if (u.update_out) store_row8(u.update_out, true, u.ld_out, i, j0, u.cols, u.vec_out, o);
 }
 
 }  // namespace muon

@@ -4,11 +4,12 @@
 //                    partial sum of U^2 per tile (for the Frobenius
 //                    normalisation), and U written into the NS workspace as a
 //                    bf16 hi/lo pair (or float32) in the canonical
-//                    short-side-first orientation, plus the bf16 X^T operand.
+//                    short-side-first orientation.
 //                    (Muon README, "Hyperparameter tuning"; Muon blog by
 //                    Venkatramana, section 3: X = G / ||G||_F.)
-//   update_kernel    W' = W - lr*wd*W - lr*scale*O, one round-to-nearest-even
-//                    to bf16 (Muon README, "Usage": decoupled weight decay).
+//   update_kernel    W' = W - lr*wd*W - lr*scale*O with O = U/||U||, for
+//                    ns_steps == 0 only (otherwise the last Newton-Schulz
+//                    phase applies the update).
 //
 // Both walk 64x64 tiles of each matrix: every thread owns two 8-element row
 // segments, so global traffic is 16-byte vector accesses along rows; the
@@ -39,39 +40,6 @@ __device__ __forceinline__ void store_seg(void* hi, void* lo, int64_t ld, int r,
     }
     st8_bf16(hi, off, h);
     if (lo) st8_bf16(lo, off, l);
-  }
-}
-
-// Load 8 elements of a caller tensor row (bounds- and alignment-aware).
-__device__ __forceinline__ void load_row8(const void* base, bool is_f32, int64_t ld, int i, int j0,
-                                          int cols, bool vec, float* v) {
-  const size_t off = static_cast<size_t>(i) * ld + j0;
-  if (vec && j0 + 8 <= cols) {
-    if (is_f32) ld8_f32(base, off, v); else ld8_bf16(base, off, v);
-    return;
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    v[e] = 0.f;
-    if (j0 + e < cols)
-      v[e] = is_f32 ? gld<float>(static_cast<const float*>(base) + off + e)
-                    : bf16_to_f32(gld<uint16_t>(static_cast<const uint16_t*>(base) + off + e));
-  }
-}
-
-__device__ __forceinline__ void store_row8(void* base, bool is_f32, int64_t ld, int i, int j0,
-                                           int cols, bool vec, const float* v) {
-  const size_t off = static_cast<size_t>(i) * ld + j0;
-  if (vec && j0 + 8 <= cols) {
-    if (is_f32) st8_f32(base, off, v); else st8_bf16(base, off, v);
-    return;
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    if (j0 + e < cols) {
-      if (is_f32) gst(static_cast<float*>(base) + off + e, v[e]);
-      else gst(static_cast<uint16_t*>(base) + off + e, f32_to_bf16(v[e]));
-    }
   }
 }
 
@@ -122,22 +90,27 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const UnitDev* __res
     for (int e = 0; e < 8; ++e) {
       ss = fmaf(uv[e], uv[e], ss);
       bad |= !isfinite(uv[e]);
-      tile[lr][lc + e] = uv[e];
     }
-    // natural orientation: rows of the unit stay rows (padding gets zeros)
-    store_seg<F32>(u.nat_hi, u.nat_lo, u.ld_nat, i, j0, uv);
+    if (u.side == kLeft) {
+      // X = U: rows of the unit stay rows (padding gets zeros)
+      store_seg<F32>(u.xh[0], u.xl, u.np, i, j0, uv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tile[lr][lc + e] = uv[e];
+    }
   }
-  __syncthreads();
-
-  // transposed orientation: column segments of the tile become row segments
+  if (u.side == kRight) {
+    // X = U^T: column segments of the tile become row segments of X
+    __syncthreads();
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int s = threadIdx.x + kThreads * q;
-    const int lc = s & (kEwTile - 1), rseg = s >> 6;
-    float v[8];
+    for (int q = 0; q < 2; ++q) {
+      const int s = threadIdx.x + kThreads * q;
+      const int lc = s & (kEwTile - 1), rseg = s >> 6;
+      float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = tile[rseg * 8 + e][lc];
-    store_seg<F32>(u.tr_hi, u.tr_lo, u.ld_tr, c0 + lc, r0 + rseg * 8, v);
+      for (int e = 0; e < 8; ++e) v[e] = tile[rseg * 8 + e][lc];
+      store_seg<F32>(u.xh[0], u.xl, u.np, c0 + lc, r0 + rseg * 8, v);
+    }
   }
 
   // per-tile partial of sum(U^2), in a fixed order
@@ -149,14 +122,16 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const UnitDev* __res
   if (threadIdx.x == 0) gst(u.partials + t.local, (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]));
 }
 
+// X master of the stand-alone update (ns_steps == 0: the iterate the
+// momentum phase wrote, buffer 0).
 template <bool F32>
 __device__ __forceinline__ void load_master_seg(const UnitDev& u, int r, int c, float* v) {
   const size_t off = static_cast<size_t>(r) * u.np + c;
   if constexpr (F32) {
-    ld8_f32(u.xh, off, v);
+    ld8_f32(u.xh[0], off, v);
   } else {
     float l[8];
-    ld8_bf16(u.xh, off, v);
+    ld8_bf16(u.xh[0], off, v);
     ld8_bf16(u.xl, off, l);
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] += l[e];
@@ -172,9 +147,9 @@ __global__ __launch_bounds__(kThreads) void update_kernel(const UnitDev* __restr
   const EwTask t = tasks[blockIdx.x];
   const UnitDev& u = units[t.unit];
   const int r0 = t.tr * kEwTile, c0 = t.tc * kEwTile;
-  const int rows = u.rows, cols = u.cols;
+  const int rows = u.rows;
   // with no Newton-Schulz iteration O is the normalised U itself
-  const float oscale = p.scale_by_inv ? unit_inv_norm(u.partials, u.k1_ntiles, p.eps, red) : 1.0f;
+  const float inv = unit_inv_norm(u.partials, u.k1_ntiles, p.eps, red);
 
   if (u.side == kRight) {
     // O[i][j] = X[j][i]: read X row segments (j fixed, i contiguous) into
@@ -207,13 +182,8 @@ __global__ __launch_bounds__(kThreads) void update_kernel(const UnitDev* __restr
       load_master_seg<F32>(u, i, j0, o);
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] *= oscale;
-    float w[8];
-    load_row8(u.param, u.param_f32, u.ld_param, i, j0, cols, u.vec_param, w);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = w[e] - decay * w[e] - step * o[e];
-    store_row8(u.param, u.param_f32, u.ld_param, i, j0, cols, u.vec_param, w);
-    if (u.update_out) store_row8(u.update_out, true, u.ld_out, i, j0, cols, u.vec_out, o);
+    for (int e = 0; e < 8; ++e) o[e] *= inv;
+    update_w8(u, i, j0, o, decay, step);
   }
 }
 

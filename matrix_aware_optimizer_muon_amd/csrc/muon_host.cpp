@@ -1,10 +1,11 @@
 // Host side of the Muon C ABI: validation, planning (units, sides, padding,
 // tile lists, workspace carve-up), descriptor upload and kernel sequencing.
 //
-// Plan of one step (per dtype group, all matrices of the group at once):
+// Plan of one step (per NS-precision group, all matrices of the group at once):
 //   momentum  (1 launch)      Muon README "Hyperparameter tuning"
-//   ns_steps x {gram, square, bx}  (3 launches each)   Muon blog sec. 3
-//   update    (1 launch)      Muon README "Usage"
+//   ns_steps x {gram, square, bx}  (3 launches each)   Muon blog sec. 3;
+//             the last bx applies the update (Muon README "Usage")
+//   update    (1 launch, only when ns_steps == 0)
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -38,7 +39,7 @@ struct UnitPlan {
   int rows = 0, cols = 0, side = 0, m = 0, n = 0, mp = 0, np = 0;
   bool f32 = false;
   float lr_scale = 1.f;
-  size_t off_xh = 0, off_xl = 0, off_xt0 = 0, off_xt1 = 0, off_a = 0, off_b = 0;
+  size_t off_xh0 = 0, off_xh1 = 0, off_xl = 0, off_a = 0, off_b = 0;
   int k1_tile0 = 0, k1_ntiles = 0, k1_tr = 0, k1_tc = 0;
   int group_index = 0;  // index inside its dtype group
 };
@@ -139,14 +140,55 @@ muon_status_t validate(const muon_tensor_t* ts, int32_t n, const muon_precond_t*
   return MUON_OK;
 }
 
-// Longest-processing-time-first order of tiles: larger K first; ties keep
-// unit order so tiles of one matrix stay adjacent (L2 reuse).
-void lpt_sort(std::vector<GemmTask>& v, const std::vector<UnitPlan>& units, const Group& g, int phase) {
-  auto cost = [&](const GemmTask& t) {
+constexpr int kXcds = 8;   // MI355X: 8 accelerator complex dies, one L2 each
+
+// XCD-aware order of one phase's tiles.  The dispatcher hands block b to XCD
+// b mod 8, and each XCD has its own L2, so tiles that share operand rows
+// (all tiles of one matrix) should run on one XCD.  Whole matrices are
+// assigned to XCDs longest-processing-time first (by the phase's cost), each
+// XCD's sequence lists its matrices' tiles costliest first, and the
+// sequences are interleaved so block 8*s + x runs the s-th tile of XCD x.
+// Shorter sequences are padded with empty tasks (unit = -1).
+std::vector<GemmTask> xcd_order(const std::vector<GemmTask>& tiles, const std::vector<UnitPlan>& units,
+                                const Group& g, int phase) {
+  auto tile_cost = [&](const GemmTask& t) {
     const UnitPlan& u = units[g.units[t.unit]];
     return phase == kGram ? int64_t(u.np) : int64_t(u.mp);
   };
-  std::stable_sort(v.begin(), v.end(), [&](const GemmTask& a, const GemmTask& b) { return cost(a) > cost(b); });
+  std::vector<int64_t> ucost(g.units.size(), 0);
+  std::vector<std::vector<GemmTask>> per_unit(g.units.size());
+  for (const GemmTask& t : tiles) {
+    ucost[t.unit] += tile_cost(t);
+    per_unit[t.unit].push_back(t);
+  }
+  std::vector<int> order(g.units.size());
+  for (size_t i = 0; i < order.size(); ++i) order[i] = int(i);
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return ucost[a] > ucost[b]; });
+  std::vector<int64_t> load(kXcds, 0);
+  std::vector<std::vector<int>> bins(kXcds);
+  for (int uidx : order) {
+    if (ucost[uidx] == 0) continue;
+    const int x = int(std::min_element(load.begin(), load.end()) - load.begin());
+    load[x] += ucost[uidx];
+    bins[x].push_back(uidx);
+  }
+  std::vector<std::vector<GemmTask>> seq(kXcds);
+  size_t longest = 0;
+  for (int x = 0; x < kXcds; ++x) {
+    for (int uidx : bins[x])
+      for (const GemmTask& t : per_unit[uidx]) seq[x].push_back(t);
+    std::stable_sort(seq[x].begin(), seq[x].end(),
+                     [&](const GemmTask& a, const GemmTask& b) { return tile_cost(a) > tile_cost(b); });
+    longest = std::max(longest, seq[x].size());
+  }
+  std::vector<GemmTask> out;
+  out.reserve(longest * kXcds);
+  for (size_t sidx = 0; sidx < longest; ++sidx)
+    for (int x = 0; x < kXcds; ++x)
+      out.push_back(sidx < seq[x].size() ? seq[x][sidx] : GemmTask{-1, 0, 0, 0});
+  // drop trailing empty tasks
+  while (!out.empty() && out.back().unit < 0) out.pop_back();
+  return out;
 }
 
 muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_t* pcs, int32_t npc,
@@ -204,9 +246,9 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
       for (int a = 0; a < tm; ++a)
         for (int b = 0; b < tn; ++b) g.bx.push_back({int(gi), a, b, 0});
     }
-    lpt_sort(g.gram, plan.units, g, kGram);
-    lpt_sort(g.sq, plan.units, g, kSquare);
-    lpt_sort(g.bx, plan.units, g, kBX);
+    g.gram = xcd_order(g.gram, plan.units, g, kGram);
+    g.sq = xcd_order(g.sq, plan.units, g, kSquare);
+    g.bx = xcd_order(g.bx, plan.units, g, kBX);
   }
   // workspace: metadata first, then the NS buffers
   size_t off = 0;
@@ -223,10 +265,9 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
   for (UnitPlan& u : plan.units) {
     const size_t es = u.f32 ? 4 : 2;
     const size_t xs = size_t(u.mp) * u.np * es, as = size_t(u.mp) * u.mp * es;
-    u.off_xh = off; off = align_up(off + xs);
+    u.off_xh0 = off; off = align_up(off + xs);
+    u.off_xh1 = off; off = align_up(off + xs);
     if (!u.f32) { u.off_xl = off; off = align_up(off + xs); }
-    u.off_xt0 = off; off = align_up(off + xs);
-    u.off_xt1 = off; off = align_up(off + xs);
     u.off_a = off; off = align_up(off + as);
     u.off_b = off; off = align_up(off + as);
   }
@@ -262,19 +303,11 @@ std::vector<uint8_t> build_meta(const Plan& plan, const muon_tensor_t* ts, uint8
       d.cols = up.cols;
       d.side = up.side;
       d.m = up.m; d.n = up.n; d.mp = up.mp; d.np = up.np;
-      d.xh = ws + up.off_xh;
+      d.xh[0] = ws + up.off_xh0;
+      d.xh[1] = ws + up.off_xh1;
       d.xl = up.f32 ? nullptr : ws + up.off_xl;
-      d.xt[0] = ws + up.off_xt0;
-      d.xt[1] = ws + up.off_xt1;
       d.a = ws + up.off_a;
       d.b = ws + up.off_b;
-      if (up.side == kLeft) {
-        d.nat_hi = d.xh; d.nat_lo = d.xl; d.ld_nat = up.np;
-        d.tr_hi = d.xt[0]; d.tr_lo = nullptr; d.ld_tr = up.mp;
-      } else {
-        d.nat_hi = d.xt[0]; d.nat_lo = nullptr; d.ld_nat = up.mp;
-        d.tr_hi = d.xh; d.tr_lo = d.xl; d.ld_tr = up.np;
-      }
       d.partials = reinterpret_cast<float*>(ws + plan.off_partials) + up.k1_tile0;
       d.k1_tile0 = up.k1_tile0;
       d.k1_ntiles = up.k1_ntiles;
@@ -327,7 +360,8 @@ muon_status_t enqueue_step(muon_handle_t h, float lr, hipStream_t s, std::vector
                                    int(g.ew.size()), k1, s);
     if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("momentum launch: ") + hipGetErrorString(e));
     for (int it = 0; it < hp.ns_steps; ++it) {
-      GemmParams gp{hp.ns_a, hp.ns_b, hp.ns_c, hp.eps, it == 0, it & 1};
+      GemmParams gp{hp.ns_a, hp.ns_b, hp.ns_c, hp.eps, it == 0, it == hp.ns_steps - 1, it & 1, 0,
+                    lr, hp.weight_decay};
       e = launch_gemm(kGram, g.f32, units, reinterpret_cast<const GemmTask*>(h->ws + g.off_gram),
                       int(g.gram.size()), gp, s);
       if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("gram launch: ") + hipGetErrorString(e));
@@ -338,9 +372,11 @@ muon_status_t enqueue_step(muon_handle_t h, float lr, hipStream_t s, std::vector
                       int(g.bx.size()), gp, s);
       if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("bx launch: ") + hipGetErrorString(e));
     }
-    K5Params k5{lr, hp.weight_decay, hp.eps, hp.ns_steps == 0};
-    e = launch_update(g.f32, units, reinterpret_cast<const EwTask*>(h->ws + g.off_ew), int(g.ew.size()), k5, s);
-    if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("update launch: ") + hipGetErrorString(e));
+    if (hp.ns_steps == 0) {   // otherwise the last B X phase applies the update
+      K5Params k5{lr, hp.weight_decay, hp.eps, 0};
+      e = launch_update(g.f32, units, reinterpret_cast<const EwTask*>(h->ws + g.off_ew), int(g.ew.size()), k5, s);
+      if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("update launch: ") + hipGetErrorString(e));
+    }
   }
   h->last_stream = s;
   return MUON_OK;
@@ -363,11 +399,15 @@ std::string plan_json(const Plan& plan, const muon_hparams_t& hp) {
   bool first = true;
   for (const Group& g : plan.groups) {
     if (g.units.empty()) continue;
+    auto real = [](const std::vector<GemmTask>& v) {
+      return size_t(std::count_if(v.begin(), v.end(), [](const GemmTask& t) { return t.unit >= 0; }));
+    };
     std::snprintf(buf, sizeof(buf),
                   "%s{\"ns\":\"%s\",\"units\":%zu,\"momentum_tiles\":%zu,\"gram_tiles\":%zu,"
-                  "\"square_tiles\":%zu,\"bx_tiles\":%zu,\"tile\":%d}",
-                  first ? "" : ",", g.f32 ? "f32" : "bf16", g.units.size(), g.ew.size(), g.gram.size(),
-                  g.sq.size(), g.bx.size(), g.f32 ? kTileF32 : kTileBf16);
+                  "\"square_tiles\":%zu,\"bx_tiles\":%zu,\"gram_blocks\":%zu,\"square_blocks\":%zu,"
+                  "\"bx_blocks\":%zu,\"tile\":%d}",
+                  first ? "" : ",", g.f32 ? "f32" : "bf16", g.units.size(), g.ew.size(), real(g.gram),
+                  real(g.sq), real(g.bx), g.gram.size(), g.sq.size(), g.bx.size(), g.f32 ? kTileF32 : kTileBf16);
     s += buf;
     first = false;
   }
@@ -383,8 +423,10 @@ std::string plan_json(const Plan& plan, const muon_hparams_t& hp) {
       std::snprintf(buf, sizeof(buf), ",\"gram/%s\",\"square/%s\",\"bx/%s\"", dt, dt, dt);
       s += buf;
     }
-    std::snprintf(buf, sizeof(buf), ",\"update/%s\"", dt);
-    s += buf;
+    if (hp.ns_steps == 0) {
+      std::snprintf(buf, sizeof(buf), ",\"update/%s\"", dt);
+      s += buf;
+    }
   }
   std::snprintf(buf, sizeof(buf), "],\"workspace_bytes\":%zu,\"meta_bytes\":%zu}", plan.total, plan.meta_bytes);
   s += buf;
@@ -490,7 +532,7 @@ muon_status_t muon_init(muon_handle_t* out, const muon_tensor_t* tensors, int32_
       h->phase_names.push_back("square" + dt + "#" + std::to_string(it + 1));
       h->phase_names.push_back("bx" + dt + "#" + std::to_string(it + 1));
     }
-    h->phase_names.push_back("update" + dt);
+    if (hp->ns_steps == 0) h->phase_names.push_back("update" + dt);
   }
   *out = h;
   return MUON_OK;

@@ -38,14 +38,13 @@ struct UnitDev {
   float* update_out; int64_t ld_out;   int32_t vec_out;   int32_t pad1;
   int32_t rows, cols;        // stored shape of the unit
   int32_t side, m, n, mp, np, pad2;
-  // workspace buffers: bf16 path uses xh/xl (hi/lo master, m x n),
-  // xt[2] (hi of X^T, n x m, ping-pong), a and b (m x m); the fp32 path uses
-  // xh as the fp32 master, xt[2] fp32 and a/b fp32 (xl unused).
-  void* xh; void* xl; void* xt[2]; void* a; void* b;
-  // momentum-phase destinations: "natural" keeps the stored orientation,
-  // "transposed" swaps it (left: nat = X, tr = X^T; right: nat = X^T, tr = X)
-  void* nat_hi; void* nat_lo; int64_t ld_nat;
-  void* tr_hi;  void* tr_lo;  int64_t ld_tr;
+  // workspace buffers (row-major, leading dimension np for X, mp for A/B).
+  // bf16 NS: xh/xl are the hi/lo bf16 parts of the X master (xh is also the
+  // MFMA operand), a and b are bf16.  float32 NS: xh is the float32 X, xl is
+  // unused, a and b are float32.  xh is double-buffered: the B X phase reads
+  // the whole current iterate as an operand while its tiles write the next
+  // one; xl is read and written only by the tile that owns each region.
+  void* xh[2]; void* xl; void* a; void* b;
   float* partials;           // one partial sum of squares per momentum tile
   int32_t k1_tile0, k1_ntiles;
   float lr_scale;            // shape scale * lr_mult
@@ -66,14 +65,18 @@ struct GemmParams {
   float a, b, c;
   float eps;           // Frobenius normalisation guard
   int32_t first;       // first NS iteration: fold the norm scale in
-  int32_t xt_in;       // which X^T buffer holds the current iterate
+  int32_t last;        // last NS iteration: apply the weight update in place of storing X
+  int32_t x_in;        // which xh buffer holds the current iterate
+  int32_t pad;
+  float lr;            // weight update of the last iteration
+  float weight_decay;
 };
 
-struct K5Params {
+struct K5Params {      // stand-alone update, used when ns_steps == 0
   float lr;
   float weight_decay;
   float eps;
-  int32_t scale_by_inv;  // ns_steps == 0: O is the normalised U itself
+  int32_t pad;
 };
 
 enum Phase : int32_t { kGram = 0, kSquare = 1, kBX = 2 };

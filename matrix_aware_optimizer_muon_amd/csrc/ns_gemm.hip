@@ -9,15 +9,22 @@
 //
 // s folds the Frobenius normalisation into the first iteration (s = 1/||U||^2
 // for the Gram, 1/||U|| for the update) so the norm never round-trips to the
-// host.  All three are "rows x rows" products C[i][j] = sum_k P[i][k] Q[j][k]
-// with both operands K-contiguous: A is symmetric, so A A = A A^T, and B X
-// reads X^T, which the update epilogue writes alongside X.
+// host.  In the last iteration kBX applies the weight update itself
+// (W' = W - lr*wd*W - lr*scale*X, Muon README "Usage") instead of storing X.
+//
+// Operands.  The Gram and the square are "rows x rows" products
+// C[i][j] = sum_k P[i][k] Q[j][k] with both operands K-contiguous (A is
+// symmetric, so A A = A A^T).  In B X the X operand is K-major (row k of X
+// holds the n-direction): its tile is staged in LDS in its natural [k][j]
+// layout and the MFMA fragments are read with gfx950's transposing LDS read
+// (ds_read_b64_tr_b16), so no transposed copy of X is ever stored.
 //
 // bf16 path: 128x128 output tile, 4 waves each owning 64x64 (2x2 blocks of
 // v_mfma_f32_32x32x16_bf16), K staged through LDS 64 deep, double-buffered
-// with register prefetch; two blocks fit per CU (74 KB LDS each) so one
-// block's epilogue traffic overlaps the other's MFMA loop; X is held as a bf16 hi/lo pair so the a*X term
-// keeps ~16 significant bits while the MFMA operand is the hi part.
+// with register prefetch; two blocks fit per CU (<= 78 KB LDS each) so one
+// block's epilogue traffic overlaps the other's MFMA loop.  X is held as a
+// bf16 hi/lo pair so the a*X term keeps ~16 significant bits while the MFMA
+// operand is the hi part.
 // fp32 path: 64x64 tile, 4 waves of 32x32, v_mfma_f32_32x32x2f32.
 #include "device_common.h"
 #include "muon_internal.h"
@@ -26,20 +33,35 @@ namespace muon {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(1))) const u32x4_t gu32x4_t;   // global memory
+typedef __attribute__((address_space(1))) const u32x4_t gu32x4_t;     // global memory
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;       // LDS
 
 constexpr int kThreads = 256;
 
 template <bool F32> struct Cfg;
 template <> struct Cfg<false> {
   using E = uint16_t;
-  static constexpr int BT = kTileBf16, WT = kTileBf16 / 2, BK = 64, PAD = 8;
+  static constexpr int BT = kTileBf16, WT = kTileBf16 / 2, BK = 64;
+  static constexpr int PAD = 8;    // K-contiguous tiles: 144-byte rows
+  static constexpr int XPAD = 32;  // K-major X tile: 320-byte rows, conflict-free transposing reads
 };
 template <> struct Cfg<true> {
   using E = float;
-  static constexpr int BT = kTileF32, WT = 32, BK = 32, PAD = 4;
+  static constexpr int BT = kTileF32, WT = kTileF32 / 2, BK = 32;
+  static constexpr int PAD = 4;
+  static constexpr int XPAD = 4;
 };
+
+// Transposing LDS read (gfx950).  Within each 16-lane group the 8-byte words
+// addressed by the lanes form a 16 x 4 matrix W[lane][e]; lane i receives
+// W[4e + i/4][i%4] for e = 0..3.  If lane 4e+q points at X[k+e][j+4q..+3],
+// lane i therefore gets X[k+e][j+i], e = 0..3: four consecutive k of one
+// column, which is what an MFMA operand lane holds.
+__device__ __forceinline__ bf16x4_t lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
+}
 
 template <bool F32, int PH>
 __global__ __launch_bounds__(kThreads, 2)
@@ -48,45 +70,64 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   using C = Cfg<F32>;
   using E = typename C::E;
   constexpr int BT = C::BT, WT = C::WT, BK = C::BK;
-  constexpr int LDP = BK + C::PAD;                 // LDS row pitch (elements)
+  constexpr bool KMAJOR_B = PH == kBX;             // X operand of B X is K-major
+  constexpr int LDA = BK + C::PAD;                 // pitch of K-contiguous tiles
+  constexpr int LDX = BT + C::XPAD;                // pitch of the K-major tile
   constexpr int NB = WT / 32;                      // 32x32 blocks per wave edge
   constexpr int EPE = 16 / sizeof(E);              // elements per 16-byte chunk
-  constexpr int CPR = BK / EPE;                    // chunks per operand row
+  constexpr int CPR = BK / EPE;                    // chunks per K-contiguous row
   constexpr int RPP = kThreads / CPR;              // rows per load pass
-  constexpr int NPASS = BT / RPP;                  // load passes per operand
+  constexpr int NPA = BT / RPP;                    // load passes, K-contiguous tile
+  constexpr int CPRX = BT / EPE;                   // chunks per K-major row
+  constexpr int RPPX = kThreads / CPRX;
+  constexpr int NPX = BK / RPPX;                   // load passes, K-major tile
+  constexpr int NPB = KMAJOR_B ? NPX : NPA;
+  constexpr int A_ELEMS = BT * LDA;
+  constexpr int B_ELEMS = KMAJOR_B ? BK * LDX : BT * LDA;
   constexpr int EPP = WT + 8;                      // epilogue LDS pitch (floats)
-  static_assert(CPR * RPP == kThreads && NPASS * RPP == BT, "tile/thread mismatch");
-  static_assert(4 * 32 * EPP * 4 <= 2 * 2 * BT * LDP * static_cast<int>(sizeof(E)),
+  static_assert(CPR * RPP == kThreads && NPA * RPP == BT, "tile/thread mismatch");
+  static_assert(CPRX * RPPX == kThreads && NPX * RPPX == BK, "tile/thread mismatch");
+  static_assert(4 * 32 * EPP * 4 <= 2 * (A_ELEMS + B_ELEMS) * static_cast<int>(sizeof(E)),
                 "epilogue staging must fit in the operand LDS");
 
-  __shared__ __attribute__((aligned(16))) E lds[2][2][BT][LDP];
+  __shared__ __attribute__((aligned(16))) E smem[2 * (A_ELEMS + B_ELEMS)];
   __shared__ float red[4];
+  E* const lds_a = smem;
+  E* const lds_b = smem + 2 * A_ELEMS;
 
   const GemmTask t = tasks[blockIdx.x];
+  if (t.unit < 0) return;   // padding of the XCD-interleaved task order
   const UnitDev& u = units[t.unit];
   const int mp = u.mp, np = u.np;
   const int ti = t.ti, tj = t.tj;
 
+  // operand A: rows [ti*BT, +BT) over K; operand B: rows [tj*BT, +BT) over K
+  // (Gram, square) or K rows x columns [tj*BT, +BT) (B X)
   const E* pa;
   const E* pb;
-  int ld, K;
+  int lda_g, ldb_g, K;
+  const E* xcur = static_cast<const E*>(u.xh[p.x_in]);
   if constexpr (PH == kGram) {
-    pa = static_cast<const E*>(u.xh) + static_cast<size_t>(ti) * BT * np;
-    pb = static_cast<const E*>(u.xh) + static_cast<size_t>(tj) * BT * np;
-    ld = np; K = np;
+    pa = xcur + static_cast<size_t>(ti) * BT * np;
+    pb = xcur + static_cast<size_t>(tj) * BT * np;
+    lda_g = ldb_g = np; K = np;
   } else if constexpr (PH == kSquare) {
     pa = static_cast<const E*>(u.a) + static_cast<size_t>(ti) * BT * mp;
     pb = static_cast<const E*>(u.a) + static_cast<size_t>(tj) * BT * mp;
-    ld = mp; K = mp;
+    lda_g = ldb_g = mp; K = mp;
   } else {
     pa = static_cast<const E*>(u.b) + static_cast<size_t>(ti) * BT * mp;
-    pb = static_cast<const E*>(u.xt[p.xt_in]) + static_cast<size_t>(tj) * BT * mp;
-    ld = mp; K = mp;
+    pb = xcur + static_cast<size_t>(tj) * BT;
+    lda_g = mp; ldb_g = np; K = mp;
   }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int lrow = tid / CPR, lchunk = tid % CPR;
+  const int arow = tid / CPR, achunk = tid % CPR;                       // K-contiguous loads
+  const int brow = KMAJOR_B ? tid / CPRX : arow;
+  const int bchunk = KMAJOR_B ? tid % CPRX : achunk;
+  constexpr int BRPP = KMAJOR_B ? RPPX : RPP;
+  constexpr int BLDS = KMAJOR_B ? LDX : LDA;
 
   f32x16_t acc[NB][NB];
 #pragma unroll
@@ -96,35 +137,38 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // Global (address space 1) views of the two operands, pre-offset to this
-  // thread's first chunk; rows advance by RPP per load pass.
-  const gu32x4_t* ga = (const gu32x4_t*)(pa + static_cast<size_t>(lrow) * ld + lchunk * EPE);
-  const gu32x4_t* gb = (const gu32x4_t*)(pb + static_cast<size_t>(lrow) * ld + lchunk * EPE);
-  const size_t pass_stride = static_cast<size_t>(RPP) * ld / EPE;   // in 16-byte chunks
-  u32x4_t ra[NPASS], rb[NPASS];
+  const gu32x4_t* ga = (const gu32x4_t*)(pa + static_cast<size_t>(arow) * lda_g + achunk * EPE);
+  const gu32x4_t* gb = (const gu32x4_t*)(pb + static_cast<size_t>(brow) * ldb_g + bchunk * EPE);
+  const size_t a_pass = static_cast<size_t>(RPP) * lda_g / EPE;           // 16-byte chunks
+  const size_t b_pass = static_cast<size_t>(BRPP) * ldb_g / EPE;
+  // advance per K step: along the row for K-contiguous tiles, down BK rows
+  // for the K-major tile
+  const size_t a_step = BK / EPE;
+  const size_t b_step = KMAJOR_B ? static_cast<size_t>(BK) * ldb_g / EPE : BK / EPE;
+
+  u32x4_t ra[NPA], rb[NPB];
 #pragma unroll
-  for (int q = 0; q < NPASS; ++q) {
-    ra[q] = ga[q * pass_stride];
-    rb[q] = gb[q * pass_stride];
-  }
+  for (int q = 0; q < NPA; ++q) ra[q] = ga[q * a_pass];
 #pragma unroll
-  for (int q = 0; q < NPASS; ++q) {
-    *reinterpret_cast<u32x4_t*>(&lds[0][0][lrow + q * RPP][lchunk * EPE]) = ra[q];
-    *reinterpret_cast<u32x4_t*>(&lds[0][1][lrow + q * RPP][lchunk * EPE]) = rb[q];
-  }
+  for (int q = 0; q < NPB; ++q) rb[q] = gb[q * b_pass];
+#pragma unroll
+  for (int q = 0; q < NPA; ++q)
+    *reinterpret_cast<u32x4_t*>(&lds_a[(arow + q * RPP) * LDA + achunk * EPE]) = ra[q];
+#pragma unroll
+  for (int q = 0; q < NPB; ++q)
+    *reinterpret_cast<u32x4_t*>(&lds_b[(brow + q * BRPP) * BLDS + bchunk * EPE]) = rb[q];
   __syncthreads();
 
   const int KT = K / BK;
   for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
+    const E* la = lds_a + (kt & 1) * A_ELEMS;
+    const E* lb = lds_b + (kt & 1) * B_ELEMS;
     const bool more = kt + 1 < KT;
     if (more) {
-      const size_t koff = static_cast<size_t>(kt + 1) * (BK / EPE);
 #pragma unroll
-      for (int q = 0; q < NPASS; ++q) {
-        ra[q] = ga[q * pass_stride + koff];
-        rb[q] = gb[q * pass_stride + koff];
-      }
+      for (int q = 0; q < NPA; ++q) ra[q] = ga[q * a_pass + (kt + 1) * a_step];
+#pragma unroll
+      for (int q = 0; q < NPB; ++q) rb[q] = gb[q * b_pass + (kt + 1) * b_step];
     }
     if constexpr (!F32) {
 #pragma unroll
@@ -133,10 +177,22 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
         const int kk = ks * 16 + (lane >> 5) * 8;
 #pragma unroll
         for (int i = 0; i < NB; ++i)
-          fa[i] = *reinterpret_cast<const bf16x8_t*>(&lds[buf][0][wm * WT + i * 32 + (lane & 31)][kk]);
+          fa[i] = *reinterpret_cast<const bf16x8_t*>(&la[(wm * WT + i * 32 + (lane & 31)) * LDA + kk]);
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
-          fb[j] = *reinterpret_cast<const bf16x8_t*>(&lds[buf][1][wn * WT + j * 32 + (lane & 31)][kk]);
+        for (int j = 0; j < NB; ++j) {
+          if constexpr (!KMAJOR_B) {
+            fb[j] = *reinterpret_cast<const bf16x8_t*>(&lb[(wn * WT + j * 32 + (lane & 31)) * LDA + kk]);
+          } else {
+            // lane group g = lane/16 covers columns 16*(g%2).. and k-half g/2;
+            // lane r of the group points at row k + r/4, columns 4*(r%4)..
+            const int g = lane >> 4, r = lane & 15;
+            const int krow = ks * 16 + 8 * (g >> 1) + (r >> 2);
+            const int col = wn * WT + j * 32 + 16 * (g & 1) + 4 * (r & 3);
+            const bf16x4_t lo = lds_read_tr(&lb[krow * LDX + col]);
+            const bf16x4_t hi = lds_read_tr(&lb[(krow + 4) * LDX + col]);
+            fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+        }
 #pragma unroll
         for (int i = 0; i < NB; ++i)
 #pragma unroll
@@ -144,43 +200,51 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
       }
     } else {
-      // each lane half takes 16 consecutive k of the 32-deep slab; step e of
-      // the MFMA pairs k = e (half 0) with k = 16 + e (half 1)
+      // v_mfma_f32_32x32x2f32: lane half h holds k = h*16 + e at step e of
+      // the 32-deep slab, for both operands
       const int k0 = (lane >> 5) * 16;
 #pragma unroll
       for (int kq = 0; kq < 4; ++kq) {
-        float4 fa[NB], fb[NB];
+        f32x4_t fa[NB], fb[NB];
 #pragma unroll
         for (int i = 0; i < NB; ++i)
-          fa[i] = *reinterpret_cast<const float4*>(&lds[buf][0][wm * WT + i * 32 + (lane & 31)][k0 + kq * 4]);
+          fa[i] = *reinterpret_cast<const f32x4_t*>(&la[(wm * WT + i * 32 + (lane & 31)) * LDA + k0 + kq * 4]);
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
-          fb[j] = *reinterpret_cast<const float4*>(&lds[buf][1][wn * WT + j * 32 + (lane & 31)][k0 + kq * 4]);
+        for (int j = 0; j < NB; ++j) {
+          if constexpr (!KMAJOR_B) {
+            fb[j] = *reinterpret_cast<const f32x4_t*>(&lb[(wn * WT + j * 32 + (lane & 31)) * LDA + k0 + kq * 4]);
+          } else {
 #pragma unroll
-        for (int i = 0; i < NB; ++i)
-#pragma unroll
-          for (int j = 0; j < NB; ++j) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i].x, fb[j].x, acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i].y, fb[j].y, acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i].z, fb[j].z, acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i].w, fb[j].w, acc[i][j], 0, 0, 0);
+            for (int e = 0; e < 4; ++e) fb[j][e] = lb[(k0 + kq * 4 + e) * LDX + wn * WT + j * 32 + (lane & 31)];
           }
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][e], fb[j][e], acc[i][j], 0, 0, 0);
       }
     }
     if (more) {
+      E* na = lds_a + ((kt + 1) & 1) * A_ELEMS;
+      E* nb = lds_b + ((kt + 1) & 1) * B_ELEMS;
 #pragma unroll
-      for (int q = 0; q < NPASS; ++q) {
-        *reinterpret_cast<u32x4_t*>(&lds[buf ^ 1][0][lrow + q * RPP][lchunk * EPE]) = ra[q];
-        *reinterpret_cast<u32x4_t*>(&lds[buf ^ 1][1][lrow + q * RPP][lchunk * EPE]) = rb[q];
-      }
+      for (int q = 0; q < NPA; ++q)
+        *reinterpret_cast<u32x4_t*>(&na[(arow + q * RPP) * LDA + achunk * EPE]) = ra[q];
+#pragma unroll
+      for (int q = 0; q < NPB; ++q)
+        *reinterpret_cast<u32x4_t*>(&nb[(brow + q * BRPP) * BLDS + bchunk * EPE]) = rb[q];
     }
     __syncthreads();
   }
 
   // ---------------------------------------------------------------- epilogue
-  // Stage each wave's 32-row strip of accumulators in LDS, then write row
-  // segments (natural layout) and column segments (mirror / X^T) as 16-byte
-  // vector stores.
+  // Each wave stages one 32-row strip of its accumulators in LDS, then
+  // writes row segments (natural layout) and, where needed, column segments
+  // (mirror tiles of A and B; weight rows of a tall matrix in the last
+  // iteration) as 16-byte vector accesses.
   float scale = 1.f;
   if constexpr (PH == kGram || PH == kBX) {
     if (p.first) {
@@ -188,8 +252,11 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
       scale = PH == kGram ? iv * iv : iv;
     }
   }
-  const bool mirror = (PH == kBX) || (ti != tj);
-  float* ep = reinterpret_cast<float*>(&lds[0][0][0][0]) + wave * (32 * EPP);
+  const bool last = PH == kBX && p.last;
+  const bool mirror = PH == kBX ? (last && u.side == kRight) : (ti != tj);
+  const float decay = p.lr * p.weight_decay;
+  const float step = p.lr * u.lr_scale;
+  float* ep = reinterpret_cast<float*>(smem) + wave * (32 * EPP);
   const int row_base = ti * BT + wm * WT;
   const int col_base = tj * BT + wn * WT;
   constexpr int SEGS = WT / 8;                       // row segments per strip row
@@ -210,10 +277,10 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
       const int s = lane + 64 * q;
       const int row = s / SEGS, cseg = s % SEGS;
       float v[8];
-      const float4 v0 = *reinterpret_cast<const float4*>(&ep[row * EPP + cseg * 8]);
-      const float4 v1 = *reinterpret_cast<const float4*>(&ep[row * EPP + cseg * 8 + 4]);
-      v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
-      v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+      const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(&ep[row * EPP + cseg * 8]);
+      const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(&ep[row * EPP + cseg * 8 + 4]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { v[e] = v0[e]; v[4 + e] = v1[e]; }
       const int gr = row_base + pi * 32 + row;
       const int gc = col_base + cseg * 8;
       if constexpr (PH == kGram) {
@@ -230,30 +297,35 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
         const size_t off = static_cast<size_t>(gr) * np + gc;
         float xm[8];
         if constexpr (F32) {
-          ld8<true>(u.xh, off, xm);
+          ld8<true>(xcur, off, xm);
         } else {
           float xl[8];
-          ld8<false>(u.xh, off, xm);
+          ld8<false>(xcur, off, xm);
           ld8<false>(u.xl, off, xl);
 #pragma unroll
           for (int e = 0; e < 8; ++e) xm[e] += xl[e];
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = scale * fmaf(p.a, xm[e], v[e]);
-        if constexpr (F32) {
-          st8<true>(u.xh, off, v);
-        } else {
-          float hi[8], lo[8];
+        if (!last) {
+          if constexpr (F32) {
+            st8<true>(u.xh[p.x_in ^ 1], off, v);
+          } else {
+            float hi[8], lo[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            hi[e] = bf16_to_f32(f32_to_bf16(v[e]));
-            lo[e] = v[e] - hi[e];
+            for (int e = 0; e < 8; ++e) {
+              hi[e] = bf16_to_f32(f32_to_bf16(v[e]));
+              lo[e] = v[e] - hi[e];
+            }
+            st8<false>(u.xh[p.x_in ^ 1], off, hi);
+            st8<false>(u.xl, off, lo);
           }
-          st8<false>(u.xh, off, hi);
-          st8<false>(u.xl, off, lo);
+        } else if (u.side == kLeft) {
+          if (gr < u.rows) update_w8(u, gr, gc, v, decay, step);
+        } else {
+          *reinterpret_cast<f32x4_t*>(&ep[row * EPP + cseg * 8]) = f32x4_t{v[0], v[1], v[2], v[3]};
+          *reinterpret_cast<f32x4_t*>(&ep[row * EPP + cseg * 8 + 4]) = f32x4_t{v[4], v[5], v[6], v[7]};
         }
-        *reinterpret_cast<float4*>(&ep[row * EPP + cseg * 8]) = make_float4(v[0], v[1], v[2], v[3]);
-        *reinterpret_cast<float4*>(&ep[row * EPP + cseg * 8 + 4]) = make_float4(v[4], v[5], v[6], v[7]);
       }
     }
     __syncthreads();
@@ -279,7 +351,8 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
           for (int e = 0; e < 8; ++e) v[e] = fmaf(p.b, av[e], p.c * v[e]);
           st8<F32>(u.b, static_cast<size_t>(gc) * mp + gr, v);
         } else {
-          st8<F32>(u.xt[p.xt_in ^ 1], static_cast<size_t>(gc) * mp + gr, v);
+          // tall matrix: O[i][j] = X[j][i], so X column gc is weight row gc
+          if (gc < u.rows) update_w8(u, gc, gr, v, decay, step);
         }
       }
     }

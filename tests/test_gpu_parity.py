@@ -302,5 +302,5 @@ def test_step_timed_reports_every_launch():
     ph = st.step_timed()
     st.close()
     names = [n for n, _ in ph]
-    assert names[0] == "momentum/bf16" and names[-1] == "update/bf16" and len(names) == 17
+    assert names[0] == "momentum/bf16" and names[-1] == "bx/bf16#5" and len(names) == 16
     assert all(ms >= 0 for _, ms in ph)
