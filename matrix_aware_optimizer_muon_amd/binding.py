@@ -249,6 +249,8 @@ class MuonStep:
         if dt is None:
             raise ValueError(f"unsupported activation dtype {acts.dtype}")
         self._keep.append(acts)
+        # the refresh is asynchronous: keep the activations alive until the
+        # stream has consumed them (the next flags()/close() synchronises)
         _check(self._lib.muon_precond_refresh(self._h, slot, block, ctypes.c_void_p(acts.data_ptr()),
                                               acts.shape[0], acts.stride(0), dt, ctypes.c_float(damping),
                                               self._stream(stream)))

@@ -52,8 +52,19 @@ struct Group {
   size_t off_units = 0, off_ew = 0, off_gram = 0, off_sq = 0, off_bx = 0;
 };
 
+struct SlotPlan {
+  int64_t d = 0;
+  int nblocks = 0, dp = 0;
+  size_t off_s = 0, off_l = 0, off_li = 0, off_sinv = 0;   // nblocks consecutive dp x dp blocks each
+};
+
 struct Plan {
   std::vector<UnitPlan> units;
+  std::vector<SlotPlan> slots;
+  std::vector<int> prec_tensors;     // tensors with a preconditioner, in tensor order
+  std::vector<size_t> off_p;         // their P buffers (float32, rows x cols)
+  std::vector<ApplyTask> apply;
+  size_t off_pdev = 0, off_apply = 0;
   Group groups[2];  // [0] bf16, [1] float32
   size_t off_flags = 0, off_partials = 0;
   size_t meta_bytes = 0, total = 0;
@@ -195,10 +206,25 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
                          const muon_hparams_t* hp, Plan& plan) {
   muon_status_t st = validate(ts, n, pcs, npc, hp);
   if (st != MUON_OK) return st;
-  for (int32_t i = 0; i < n; ++i)
-    if (ts[i].precond >= 0)
-      return fail(MUON_ERR_UNSUPPORTED, "tensor " + std::to_string(i) + ": preconditioning not available in this build");
   plan = Plan();
+  // Newton-Muon slots and preconditioned tensors
+  for (int32_t k = 0; k < npc; ++k) {
+    SlotPlan sp;
+    sp.d = pcs[k].d;
+    sp.nblocks = pcs[k].nblocks;
+    sp.dp = int(round_up(sp.d, kPrecondPad));
+    plan.slots.push_back(sp);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    if (ts[i].precond < 0) continue;
+    const int pi = int(plan.prec_tensors.size());
+    plan.prec_tensors.push_back(i);
+    const SlotPlan& sp = plan.slots[ts[i].precond];
+    const int trs = int((ts[i].rows + 63) / 64), tcs = int((sp.d + 63) / 64);
+    for (int blk = 0; blk < sp.nblocks; ++blk)
+      for (int r = 0; r < trs; ++r)
+        for (int c = 0; c < tcs; ++c) plan.apply.push_back({pi, r, c, blk});
+  }
   // units
   for (int32_t i = 0; i < n; ++i) {
     const muon_tensor_t& t = ts[i];
@@ -261,6 +287,8 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
     g.off_sq = off; off = align_up(off + sizeof(GemmTask) * g.sq.size());
     g.off_bx = off; off = align_up(off + sizeof(GemmTask) * g.bx.size());
   }
+  plan.off_pdev = off; off = align_up(off + sizeof(PrecondDev) * plan.prec_tensors.size());
+  plan.off_apply = off; off = align_up(off + sizeof(ApplyTask) * plan.apply.size());
   plan.meta_bytes = off;
   for (UnitPlan& u : plan.units) {
     const size_t es = u.f32 ? 4 : 2;
@@ -270,6 +298,17 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
     if (!u.f32) { u.off_xl = off; off = align_up(off + xs); }
     u.off_a = off; off = align_up(off + as);
     u.off_b = off; off = align_up(off + as);
+  }
+  for (SlotPlan& sp : plan.slots) {
+    const size_t blk = size_t(sp.dp) * sp.dp * sp.nblocks;
+    sp.off_s = off; off = align_up(off + blk * sizeof(float));
+    sp.off_l = off; off = align_up(off + blk * sizeof(double));
+    sp.off_li = off; off = align_up(off + blk * sizeof(double));
+    sp.off_sinv = off; off = align_up(off + blk * sizeof(float));
+  }
+  for (int ti : plan.prec_tensors) {
+    plan.off_p.push_back(off);
+    off = align_up(off + size_t(ts[ti].rows) * ts[ti].cols * sizeof(float));
   }
   plan.total = std::max<size_t>(off, kAlign);
   plan.zero_bytes = int64_t(plan.total - plan.meta_bytes);
@@ -285,10 +324,19 @@ std::vector<uint8_t> build_meta(const Plan& plan, const muon_tensor_t* ts, uint8
       const size_t es = t.dtype == MUON_F32 ? 4 : 2;   // element size of param/grad
       UnitDev d;
       std::memset(&d, 0, sizeof(d));
-      d.grad = static_cast<const uint8_t*>(t.grad) + size_t(up.row0) * t.ld_grad * es;
-      d.ld_grad = t.ld_grad;
-      d.grad_f32 = t.dtype == MUON_F32;
-      d.vec_grad = reinterpret_cast<uintptr_t>(t.grad) % 16 == 0 && (t.ld_grad * es) % 16 == 0;
+      if (t.precond < 0) {
+        d.grad = static_cast<const uint8_t*>(t.grad) + size_t(up.row0) * t.ld_grad * es;
+        d.ld_grad = t.ld_grad;
+        d.grad_f32 = t.dtype == MUON_F32;
+        d.vec_grad = reinterpret_cast<uintptr_t>(t.grad) % 16 == 0 && (t.ld_grad * es) % 16 == 0;
+      } else {   // the momentum phase reads P = G S^-1 (float32, ld = cols)
+        const size_t pi = size_t(std::find(plan.prec_tensors.begin(), plan.prec_tensors.end(), up.tensor) -
+                                 plan.prec_tensors.begin());
+        d.grad = ws + plan.off_p[pi] + size_t(up.row0) * t.cols * sizeof(float);
+        d.ld_grad = t.cols;
+        d.grad_f32 = 1;
+        d.vec_grad = (t.cols * sizeof(float)) % 16 == 0;
+      }
       d.mom = t.momentum + size_t(up.row0) * t.ld_momentum;
       d.ld_mom = t.ld_momentum;
       d.vec_mom = reinterpret_cast<uintptr_t>(t.momentum) % 16 == 0 && (t.ld_momentum * 4) % 16 == 0;
@@ -322,6 +370,27 @@ std::vector<uint8_t> build_meta(const Plan& plan, const muon_tensor_t* ts, uint8
     put(g.off_sq, g.sq.data(), g.sq.size() * sizeof(GemmTask));
     put(g.off_bx, g.bx.data(), g.bx.size() * sizeof(GemmTask));
   }
+  for (size_t pi = 0; pi < plan.prec_tensors.size(); ++pi) {
+    const muon_tensor_t& t = ts[plan.prec_tensors[pi]];
+    const SlotPlan& sp = plan.slots[t.precond];
+    const size_t es = t.dtype == MUON_F32 ? 4 : 2;
+    PrecondDev pd;
+    std::memset(&pd, 0, sizeof(pd));
+    pd.grad = t.grad;
+    pd.ld_grad = t.ld_grad;
+    pd.grad_f32 = t.dtype == MUON_F32;
+    pd.vec_grad = reinterpret_cast<uintptr_t>(t.grad) % 16 == 0 && (t.ld_grad * es) % 16 == 0 && sp.d % 8 == 0;
+    pd.p = reinterpret_cast<float*>(ws + plan.off_p[pi]);
+    pd.ld_p = t.cols;
+    pd.sinv = reinterpret_cast<const float*>(ws + sp.off_sinv);
+    pd.rows = int(t.rows);
+    pd.d = int(sp.d);
+    pd.dp = sp.dp;
+    pd.nblocks = sp.nblocks;
+    std::memcpy(meta.data() + plan.off_pdev + pi * sizeof(PrecondDev), &pd, sizeof(pd));
+  }
+  if (!plan.apply.empty())
+    std::memcpy(meta.data() + plan.off_apply, plan.apply.data(), plan.apply.size() * sizeof(ApplyTask));
   return meta;
 }
 
@@ -351,6 +420,12 @@ muon_status_t enqueue_step(muon_handle_t h, float lr, hipStream_t s, std::vector
     return hipEventRecord((*ev)[ek++], s) == hipSuccess;
   };
   if (!mark()) return fail(MUON_ERR_HIP, "hipEventRecord failed");
+  if (!plan.apply.empty()) {
+    hipError_t e = launch_precond_apply(reinterpret_cast<const PrecondDev*>(h->ws + plan.off_pdev),
+                                        reinterpret_cast<const ApplyTask*>(h->ws + plan.off_apply),
+                                        int(plan.apply.size()), s);
+    if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("precond apply launch: ") + hipGetErrorString(e));
+  }
   for (const Group& g : plan.groups) {
     if (g.units.empty()) continue;
     const UnitDev* units = reinterpret_cast<const UnitDev*>(h->ws + g.off_units);
@@ -411,8 +486,19 @@ std::string plan_json(const Plan& plan, const muon_hparams_t& hp) {
     s += buf;
     first = false;
   }
-  s += "],\"launch_order\":[";
+  s += "],\"preconds\":[";
+  for (size_t k = 0; k < plan.slots.size(); ++k) {
+    std::snprintf(buf, sizeof(buf), "%s{\"d\":%lld,\"nblocks\":%d,\"dp\":%d}", k ? "," : "",
+                  (long long)plan.slots[k].d, plan.slots[k].nblocks, plan.slots[k].dp);
+    s += buf;
+  }
+  std::snprintf(buf, sizeof(buf), "],\"apply_tiles\":%zu,\"launch_order\":[", plan.apply.size());
+  s += buf;
   first = true;
+  if (!plan.apply.empty()) {
+    s += "\"precond_apply\"";
+    first = false;
+  }
   for (const Group& g : plan.groups) {
     if (g.units.empty()) continue;
     const char* dt = g.f32 ? "f32" : "bf16";
@@ -517,12 +603,15 @@ muon_status_t muon_init(muon_handle_t* out, const muon_tensor_t* tensors, int32_
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipMemsetAsync(h->ws, 0, h->plan.total, s);
   if (e == hipSuccess) e = hipMemcpyAsync(h->ws, h->meta.data(), h->meta.size(), hipMemcpyHostToDevice, s);
+  for (const SlotPlan& sp : h->plan.slots)   // S^-1 = I until the slot's first refresh
+    if (e == hipSuccess) e = launch_identity(reinterpret_cast<float*>(h->ws + sp.off_sinv), sp.dp, sp.nblocks, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);  // the host copy of meta may be reused after init
   if (e != hipSuccess) {
     delete h;
     return fail(MUON_ERR_HIP, std::string("workspace initialisation: ") + hipGetErrorString(e));
   }
   h->last_stream = s;
+  if (!h->plan.apply.empty()) h->phase_names.push_back("precond_apply");
   for (const Group& g : h->plan.groups) {
     if (g.units.empty()) continue;
     const std::string dt = g.f32 ? "/f32" : "/bf16";
@@ -538,10 +627,31 @@ muon_status_t muon_init(muon_handle_t* out, const muon_tensor_t* tensors, int32_
   return MUON_OK;
 }
 
-muon_status_t muon_precond_refresh(muon_handle_t h, int32_t, int32_t, const void*, int64_t, int64_t, int32_t,
-                                   float, void*) {
-  if (!h) return fail(MUON_ERR_NULL_ARG, "handle is NULL");
-  return fail(MUON_ERR_UNSUPPORTED, "preconditioning not available in this build");
+muon_status_t muon_precond_refresh(muon_handle_t h, int32_t slot, int32_t block, const void* acts, int64_t n_rows,
+                                   int64_t ld, int32_t dtype, float damping, void* stream) {
+  if (!h || !acts) return fail(MUON_ERR_NULL_ARG, "handle or activations is NULL");
+  if (slot < 0 || size_t(slot) >= h->plan.slots.size()) return fail(MUON_ERR_BAD_ARG, "no such preconditioner slot");
+  const SlotPlan& sp = h->plan.slots[size_t(slot)];
+  if (block < 0 || block >= sp.nblocks) return fail(MUON_ERR_BAD_ARG, "no such block in the slot");
+  if (dtype != MUON_F32 && dtype != MUON_BF16) return fail(MUON_ERR_BAD_DTYPE, "activations must be f32 or bf16");
+  if (n_rows < 1 || ld < sp.d) return fail(MUON_ERR_BAD_SHAPE, "activations need n_rows >= 1 and ld >= d");
+  if (!std::isfinite(damping) || damping < 0.f) return fail(MUON_ERR_BAD_ARG, "damping must be finite and >= 0");
+  const size_t es = dtype == MUON_F32 ? 4 : 2;
+  if (reinterpret_cast<uintptr_t>(acts) % es) return fail(MUON_ERR_ALIGNMENT, "activations misaligned");
+  const size_t bo = size_t(block) * sp.dp * sp.dp;
+  PrecondBlockDev b;
+  b.s = reinterpret_cast<float*>(h->ws + sp.off_s) + bo;
+  b.l = reinterpret_cast<double*>(h->ws + sp.off_l) + bo;
+  b.li = reinterpret_cast<double*>(h->ws + sp.off_li) + bo;
+  b.sinv = reinterpret_cast<float*>(h->ws + sp.off_sinv) + bo;
+  b.d = int(sp.d);
+  b.dp = sp.dp;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_precond_refresh(b, acts, n_rows, ld, dtype == MUON_F32, damping,
+                                        reinterpret_cast<uint32_t*>(h->ws + h->plan.off_flags), s);
+  if (e != hipSuccess) return fail(MUON_ERR_HIP, std::string("precond refresh launch: ") + hipGetErrorString(e));
+  h->last_stream = s;
+  return MUON_OK;
 }
 
 muon_status_t muon_step(muon_handle_t h, float lr, void* stream) {

@@ -81,6 +81,28 @@ struct K5Params {      // stand-alone update, used when ns_steps == 0
 
 enum Phase : int32_t { kGram = 0, kSquare = 1, kBX = 2 };
 
+// ---- Newton-Muon preconditioner ------------------------------------------
+constexpr int kCholBlock = 64;    // Cholesky / inverse block edge (float64)
+constexpr int kPrecondPad = 128;  // S and S^-1 are padded to multiples of this
+
+// One preconditioned tensor of the apply phase: P = G S^-1 (block-wise).
+struct PrecondDev {
+  const void* grad; int64_t ld_grad; int32_t grad_f32; int32_t vec_grad;
+  float* p;         int64_t ld_p;     // P, float32, rows x (d * nblocks)
+  const float* sinv;                  // nblocks inverses of the slot, dp x dp each
+  int32_t rows, d, dp, nblocks;
+};
+struct ApplyTask { int32_t tensor, tr, tc, blk; };   // 64x64 tile (tr, tc) of block blk
+
+// Buffers of one S^-1 block for a refresh.
+struct PrecondBlockDev {
+  float* s;        // S, float32, dp x dp
+  double* l;       // Cholesky factor, float64
+  double* li;      // its inverse, float64
+  float* sinv;     // S^-1, float32
+  int32_t d, dp;
+};
+
 // Launchers (defined in the .hip files).
 hipError_t launch_momentum(bool f32, const UnitDev* units, const EwTask* tasks, int n_tasks,
                            const K1Params& p, hipStream_t s);
@@ -88,5 +110,9 @@ hipError_t launch_gemm(int phase, bool f32, const UnitDev* units, const GemmTask
                        int n_tasks, const GemmParams& p, hipStream_t s);
 hipError_t launch_update(bool f32, const UnitDev* units, const EwTask* tasks, int n_tasks,
                          const K5Params& p, hipStream_t s);
+hipError_t launch_precond_refresh(const PrecondBlockDev& b, const void* acts, int64_t n_rows, int64_t ld,
+                                  bool acts_f32, float damping, uint32_t* flags, hipStream_t s);
+hipError_t launch_precond_apply(const PrecondDev* pds, const ApplyTask* tasks, int n_tasks, hipStream_t s);
+hipError_t launch_identity(float* sinv, int dp, int nblocks, hipStream_t s);
 
 }  // namespace muon

@@ -202,3 +202,27 @@ def test_workspace_size_formula():
     assert need - plan["meta_bytes"] == per_unit
     # ns_steps does not change the footprint
     assert ws_status(ts, mm.default_hparams(ns_steps=1))[1] == need
+
+
+def test_plan_newton_muon_layer():
+    w = synth.workload("nmuon")
+    ts, base = [], BASE
+    for s in w.tensors:
+        t, span = fake(s.rows, s.cols, B.MUON_BF16, base, split=s.split_rows, precond=s.precond)
+        ts.append(t)
+        base += span
+    pcs = []
+    for d, nb in ((768, 1), (768, 4)):
+        p = B.MuonPrecond()
+        p.d, p.nblocks = d, nb
+        pcs.append(p)
+    plan = mm.plan_describe(ts, mm.default_hparams(), pcs)
+    assert plan["preconds"] == [{"d": 768, "nblocks": 1, "dp": 768}, {"d": 768, "nblocks": 4, "dp": 768}]
+    # 64x64 tiles of P: (2304 + 768 + 3072) x 768 with one block, 768 x 768 x 4 blocks
+    assert plan["apply_tiles"] == (36 + 12 + 48) * 12 + 4 * 12 * 12
+    assert plan["launch_order"][0] == "precond_apply"
+    assert len(plan["units"]) == 3 + 1 + 1 + 1          # packed QKV split into three blocks
+    # a preconditioned tensor must match d * nblocks of its slot
+    bad = ts[3]
+    bad.precond = 0
+    assert ws_status([bad], preconds=pcs)[0] == "MUON_ERR_BAD_SHAPE"
