@@ -27,6 +27,15 @@ PEAK_F32_TFLOPS = 157.3       # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 METRIC = "Muon steps/sec over a GPT-2-small weight set; NS TFLOP/s as % of bf16 MFMA peak"
+STEP_TEXT = "one grouped Muon step (mu 0.95 Nesterov, 5 quintic NS, lr 0.02, wd 0.01)"
+WORKLOAD_TEXT = {
+    "gpt2s": "gpt2s: GPT-2-small hidden weights, 12 layers x {Q,K,V,O 768x768, MLP-up 3072x768, "
+             "MLP-down 768x3072} = 72 bf16 matrices; " + STEP_TEXT,
+    "square": "square: one 4096x4096 bf16 matrix, rank-32 + noise gradient; " + STEP_TEXT,
+    "gpt2xl": "gpt2xl: GPT-2-XL hidden weights, 48 layers x {Q,K,V,O 1600x1600, MLP-up 6400x1600, "
+              "MLP-down 1600x6400} = 288 bf16 matrices; " + STEP_TEXT,
+    "tiny": "tiny: one 256x512 fp32 matrix; " + STEP_TEXT,
+}
 
 
 def ns_flops(m, n):
@@ -94,7 +103,23 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="gpt2s", choices=["gpt2s", "square", "gpt2xl", "tiny"],
+                    help="weight set to step (the headline metric is quoted on gpt2s)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run 3 device-to-device copies of BYTES each (HBM counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no collectives); use --gpus 1", file=sys.stderr)
         sys.exit(2)
@@ -106,13 +131,16 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    wl = synth.workload("gpt2s")
+    wl = synth.workload(args.workload)
     hp = mm.default_hparams()
     keep, descs = [], []
     for s in wl.tensors:
         G, W, M = synth.gradient(wl, s), synth.weight(wl, s), synth.momentum0(wl, s)
-        tg = torch.from_numpy(G.view(np.int16).copy()).view(torch.bfloat16).to(dev)
-        tw = torch.from_numpy(W.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        if s.dtype == "bf16":
+            tg = torch.from_numpy(G.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+            tw = torch.from_numpy(W.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        else:
+            tg, tw = torch.from_numpy(G).to(dev), torch.from_numpy(W).to(dev)
         tm = torch.from_numpy(M).to(dev)
         keep += [tg, tw, tm]
         descs.append(mm.tensor_desc(tw, tg, tm))
@@ -143,7 +171,10 @@ def main():
     assert st.flags() == 0, "non-finite values in the benchmark step"
     st.close()
 
-    units = [(min(s.rows, s.cols), max(s.rows, s.cols)) for s in wl.tensors]
+    units = []
+    for s in wl.tensors:
+        h = s.split_rows or s.rows
+        units += [(min(h, s.cols), max(h, s.cols))] * (s.rows // h)
     flops = {"gram": 0, "square": 0, "bx": 0}
     for m, n in units:
         for k, v in ns_flops(m, n).items():
@@ -181,9 +212,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "gpt2s: GPT-2-small hidden weights, 12 layers x {Q,K,V,O 768x768, "
-                               "MLP-up 3072x768, MLP-down 768x3072} = 72 bf16 matrices; one grouped Muon "
-                               "step (mu 0.95 Nesterov, 5 quintic NS, lr 0.02, wd 0.01)",
+        "config": {"workload": WORKLOAD_TEXT[args.workload],
                    "matrices": len(wl.tensors), "params": elems, "parallelism": "single GPU"},
         "matrices_per_s": round(len(wl.tensors) * 1000.0 / ms_per_step, 1),
         "ns_tflops": round(ns_tflop / (ns_ms * 1e-3), 2),
@@ -195,7 +224,10 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if args.workload != "gpt2s":
+        out["metric"] = f"Muon steps/sec, {args.workload} weight set (not the headline workload)"
+        out["dtype"] = "f32" if args.workload == "tiny" else "bf16"
+    if not args.no_cpu_baseline and args.workload == "gpt2s":
         out["cpu_baseline"] = cpu_baseline(wl, hp, args.cpu_budget)
     print(json.dumps(out), flush=True)
 

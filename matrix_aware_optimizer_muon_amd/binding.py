@@ -61,11 +61,13 @@ _lib = None
 
 
 def load_library(path: Optional[str] = None) -> ctypes.CDLL:
-    """Load libmuon.so and declare its signatures.  Raises if it is absent."""
+    """Load libmuon.so (this package's build, or the file named by the
+    MUON_LIBRARY environment variable) and declare its signatures.  Raises if
+    it is absent."""
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("MUON_LIBRARY") or LIB_PATH
     if not os.path.exists(p):
         raise ImportError(f"libmuon.so not built: {p} is missing (run __graft_entry__.build())")
     # One HIP runtime per process: torch ships its own libamdhip64.so.7.  If

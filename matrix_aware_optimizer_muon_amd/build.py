@@ -46,23 +46,27 @@ def _run(cmd, verbose):
         print(out)
 
 
-def build(verbose=False, extra_flags=()):
+def build(verbose=False, extra_flags=(), out=None, objdir=None):
+    """Compile every source and link the library (default: lib/libmuon.so).
+    `extra_flags` and a separate `out`/`objdir` allow variant builds."""
     hipcc = _hipcc()
-    os.makedirs(OBJ, exist_ok=True)
-    os.makedirs(LIBDIR, exist_ok=True)
+    obj_dir = objdir or OBJ
+    lib = out or LIB
+    os.makedirs(obj_dir, exist_ok=True)
+    os.makedirs(os.path.dirname(lib), exist_ok=True)
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         cmds.append([hipcc, *HIP_FLAGS, *extra_flags, f"-I{INCLUDE}", "-c",
                      os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(len(cmds), 4)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

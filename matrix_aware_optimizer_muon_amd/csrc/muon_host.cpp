@@ -155,11 +155,13 @@ constexpr int kXcds = 8;   // MI355X: 8 accelerator complex dies, one L2 each
 
 // XCD-aware order of one phase's tiles.  The dispatcher hands block b to XCD
 // b mod 8, and each XCD has its own L2, so tiles that share operand rows
-// (all tiles of one matrix) should run on one XCD.  Whole matrices are
-// assigned to XCDs longest-processing-time first (by the phase's cost), each
-// XCD's sequence lists its matrices' tiles costliest first, and the
-// sequences are interleaved so block 8*s + x runs the s-th tile of XCD x.
-// Shorter sequences are padded with empty tasks (unit = -1).
+// (the tiles of one matrix) should run on one XCD.  A matrix costing more
+// than an eighth of the phase is cut into contiguous parts (row-major tile
+// order) of about an eighth each; the parts and the remaining whole matrices
+// are then assigned to XCDs longest-processing-time first.  Each XCD's
+// sequence lists its tiles costliest first, and the sequences are
+// interleaved so block 8*s + x runs the s-th tile of XCD x; shorter
+// sequences are padded with empty tasks (unit = -1).
 std::vector<GemmTask> xcd_order(const std::vector<GemmTask>& tiles, const std::vector<UnitPlan>& units,
                                 const Group& g, int phase) {
   auto tile_cost = [&](const GemmTask& t) {
@@ -168,26 +170,36 @@ std::vector<GemmTask> xcd_order(const std::vector<GemmTask>& tiles, const std::v
   };
   std::vector<int64_t> ucost(g.units.size(), 0);
   std::vector<std::vector<GemmTask>> per_unit(g.units.size());
+  int64_t total = 0;
   for (const GemmTask& t : tiles) {
     ucost[t.unit] += tile_cost(t);
     per_unit[t.unit].push_back(t);
+    total += tile_cost(t);
   }
-  std::vector<int> order(g.units.size());
-  for (size_t i = 0; i < order.size(); ++i) order[i] = int(i);
-  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return ucost[a] > ucost[b]; });
+  const int64_t share = std::max<int64_t>(1, (total + kXcds - 1) / kXcds);
+  struct Part { std::vector<GemmTask> tiles; int64_t cost = 0; };
+  std::vector<Part> parts;
+  for (size_t uidx = 0; uidx < per_unit.size(); ++uidx) {
+    if (per_unit[uidx].empty()) continue;
+    const int64_t k = ucost[uidx] > share ? (ucost[uidx] + share - 1) / share : 1;
+    const int64_t target = (ucost[uidx] + k - 1) / k;
+    parts.emplace_back();
+    for (const GemmTask& t : per_unit[uidx]) {
+      if (parts.back().cost >= target) parts.emplace_back();
+      parts.back().tiles.push_back(t);
+      parts.back().cost += tile_cost(t);
+    }
+  }
+  std::stable_sort(parts.begin(), parts.end(), [](const Part& a, const Part& b) { return a.cost > b.cost; });
   std::vector<int64_t> load(kXcds, 0);
-  std::vector<std::vector<int>> bins(kXcds);
-  for (int uidx : order) {
-    if (ucost[uidx] == 0) continue;
-    const int x = int(std::min_element(load.begin(), load.end()) - load.begin());
-    load[x] += ucost[uidx];
-    bins[x].push_back(uidx);
-  }
   std::vector<std::vector<GemmTask>> seq(kXcds);
+  for (const Part& pt : parts) {
+    const int x = int(std::min_element(load.begin(), load.end()) - load.begin());
+    load[x] += pt.cost;
+    seq[x].insert(seq[x].end(), pt.tiles.begin(), pt.tiles.end());
+  }
   size_t longest = 0;
   for (int x = 0; x < kXcds; ++x) {
-    for (int uidx : bins[x])
-      for (const GemmTask& t : per_unit[uidx]) seq[x].push_back(t);
     std::stable_sort(seq[x].begin(), seq[x].end(),
                      [&](const GemmTask& a, const GemmTask& b) { return tile_cost(a) > tile_cost(b); });
     longest = std::max(longest, seq[x].size());

@@ -13,7 +13,10 @@ namespace muon {
 // use 64x64 tiles (4 waves of 32x32, fp32 MFMA 32x32x2).  Every NS buffer is
 // zero-padded to a multiple of the tile in both dimensions; zero padding is
 // exact under X X^T, A A and B X.
-constexpr int kTileBf16 = 128;
+#ifndef MUON_TILE_BF16
+#define MUON_TILE_BF16 128
+#endif
+constexpr int kTileBf16 = MUON_TILE_BF16;
 constexpr int kTileF32 = 64;
 // Edge of the square tiles of the elementwise phases (momentum, update).
 constexpr int kEwTile = 64;

@@ -44,12 +44,14 @@ template <bool F32> struct Cfg;
 template <> struct Cfg<false> {
   using E = uint16_t;
   static constexpr int BT = kTileBf16, WT = kTileBf16 / 2, BK = 64;
+  static constexpr int OCC = BT >= 256 ? 1 : 2;   // blocks per CU the registers allow
   static constexpr int PAD = 8;    // K-contiguous tiles: 144-byte rows
   static constexpr int XPAD = 32;  // K-major X tile: 320-byte rows, conflict-free transposing reads
 };
 template <> struct Cfg<true> {
   using E = float;
   static constexpr int BT = kTileF32, WT = kTileF32 / 2, BK = 32;
+  static constexpr int OCC = 2;
   static constexpr int PAD = 4;
   static constexpr int XPAD = 4;
 };
@@ -63,8 +65,92 @@ __device__ __forceinline__ bf16x4_t lds_read_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
 }
 
+template <int NPA, int NPB>
+__device__ __forceinline__ void load_stage(const gu32x4_t* ga, const gu32x4_t* gb, size_t a_pass, size_t b_pass,
+                                           int kt, size_t a_step, size_t b_step, u32x4_t (&ra)[NPA],
+                                           u32x4_t (&rb)[NPB]) {
+#pragma unroll
+  for (int q = 0; q < NPA; ++q) ra[q] = ga[q * a_pass + kt * a_step];
+#pragma unroll
+  for (int q = 0; q < NPB; ++q) rb[q] = gb[q * b_pass + kt * b_step];
+}
+
+template <int NPA, int NPB, typename E>
+__device__ __forceinline__ void store_stage(E* la, E* lb, int arow, int achunk, int rpp, int lda, int brow,
+                                            int bchunk, int brpp, int blds, int epe, const u32x4_t (&ra)[NPA],
+                                            const u32x4_t (&rb)[NPB]) {
+#pragma unroll
+  for (int q = 0; q < NPA; ++q) *reinterpret_cast<u32x4_t*>(&la[(arow + q * rpp) * lda + achunk * epe]) = ra[q];
+#pragma unroll
+  for (int q = 0; q < NPB; ++q) *reinterpret_cast<u32x4_t*>(&lb[(brow + q * brpp) * blds + bchunk * epe]) = rb[q];
+}
+
+// MFMAs of one BK-deep stage held in LDS (la: K-contiguous A tile; lb: the
+// B tile, K-contiguous or K-major).
+template <bool F32, bool KMAJOR_B, int NB, int WT, int BK, int LDA, int LDX, typename E>
+__device__ __forceinline__ void mma_stage(const E* la, const E* lb, f32x16_t (&acc)[NB][NB], int lane, int wm,
+                                          int wn) {
+  if constexpr (!F32) {
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8_t fa[NB], fb[NB];
+      const int kk = ks * 16 + (lane >> 5) * 8;
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8_t*>(&la[(wm * WT + i * 32 + (lane & 31)) * LDA + kk]);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if constexpr (!KMAJOR_B) {
+          fb[j] = *reinterpret_cast<const bf16x8_t*>(&lb[(wn * WT + j * 32 + (lane & 31)) * LDA + kk]);
+        } else {
+          // lane group g = lane/16 covers columns 16*(g%2).. and k-half g/2;
+          // lane r of the group points at row k + r/4, columns 4*(r%4)..
+          const int g = lane >> 4, r = lane & 15;
+          const int krow = ks * 16 + 8 * (g >> 1) + (r >> 2);
+          const int col = wn * WT + j * 32 + 16 * (g & 1) + 4 * (r & 3);
+          const bf16x4_t lo = lds_read_tr(&lb[krow * LDX + col]);
+          const bf16x4_t hi = lds_read_tr(&lb[(krow + 4) * LDX + col]);
+          fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  } else {
+    // v_mfma_f32_32x32x2f32: lane half h holds k = h*16 + e at step e of the
+    // 32-deep slab, for both operands
+    const int k0 = (lane >> 5) * 16;
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq) {
+      f32x4_t fa[NB], fb[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        fa[i] = *reinterpret_cast<const f32x4_t*>(&la[(wm * WT + i * 32 + (lane & 31)) * LDA + k0 + kq * 4]);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if constexpr (!KMAJOR_B) {
+          fb[j] = *reinterpret_cast<const f32x4_t*>(&lb[(wn * WT + j * 32 + (lane & 31)) * LDA + k0 + kq * 4]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) fb[j][e] = lb[(k0 + kq * 4 + e) * LDX + wn * WT + j * 32 + (lane & 31)];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][e], fb[j][e], acc[i][j], 0, 0, 0);
+    }
+  }
+}
+
 template <bool F32, int PH>
-__global__ __launch_bounds__(kThreads, 2)
+__global__ __launch_bounds__(kThreads, Cfg<F32>::OCC)
 void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restrict__ tasks,
                     GemmParams p) {
   using C = Cfg<F32>;
@@ -146,97 +232,35 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   const size_t a_step = BK / EPE;
   const size_t b_step = KMAJOR_B ? static_cast<size_t>(BK) * ldb_g / EPE : BK / EPE;
 
-  u32x4_t ra[NPA], rb[NPB];
-#pragma unroll
-  for (int q = 0; q < NPA; ++q) ra[q] = ga[q * a_pass];
-#pragma unroll
-  for (int q = 0; q < NPB; ++q) rb[q] = gb[q * b_pass];
-#pragma unroll
-  for (int q = 0; q < NPA; ++q)
-    *reinterpret_cast<u32x4_t*>(&lds_a[(arow + q * RPP) * LDA + achunk * EPE]) = ra[q];
-#pragma unroll
-  for (int q = 0; q < NPB; ++q)
-    *reinterpret_cast<u32x4_t*>(&lds_b[(brow + q * BRPP) * BLDS + bchunk * EPE]) = rb[q];
-  __syncthreads();
-
+  // Two register stages in flight: the loads for step kt+2 are issued
+  // before the MFMAs of step kt; the stage for kt+1 is stored to LDS after
+  // them.  The loop is unrolled by two so both register sets stay static,
+  // and it has no branches around memory operations (the prefetch index is
+  // clamped; the last two steps reload the final stage into the idle
+  // buffer), so the compiler's wait counts stay exact.  K is a multiple of
+  // 2*BK because every NS buffer is padded to the tile, which is 2*BK.
+  static_assert(BT % (2 * BK) == 0, "K steps must come in pairs");
+  u32x4_t ra0[NPA], rb0[NPB], ra1[NPA], rb1[NPB];
   const int KT = K / BK;
-  for (int kt = 0; kt < KT; ++kt) {
-    const E* la = lds_a + (kt & 1) * A_ELEMS;
-    const E* lb = lds_b + (kt & 1) * B_ELEMS;
-    const bool more = kt + 1 < KT;
-    if (more) {
-#pragma unroll
-      for (int q = 0; q < NPA; ++q) ra[q] = ga[q * a_pass + (kt + 1) * a_step];
-#pragma unroll
-      for (int q = 0; q < NPB; ++q) rb[q] = gb[q * b_pass + (kt + 1) * b_step];
-    }
-    if constexpr (!F32) {
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        bf16x8_t fa[NB], fb[NB];
-        const int kk = ks * 16 + (lane >> 5) * 8;
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-          fa[i] = *reinterpret_cast<const bf16x8_t*>(&la[(wm * WT + i * 32 + (lane & 31)) * LDA + kk]);
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          if constexpr (!KMAJOR_B) {
-            fb[j] = *reinterpret_cast<const bf16x8_t*>(&lb[(wn * WT + j * 32 + (lane & 31)) * LDA + kk]);
-          } else {
-            // lane group g = lane/16 covers columns 16*(g%2).. and k-half g/2;
-            // lane r of the group points at row k + r/4, columns 4*(r%4)..
-            const int g = lane >> 4, r = lane & 15;
-            const int krow = ks * 16 + 8 * (g >> 1) + (r >> 2);
-            const int col = wn * WT + j * 32 + 16 * (g & 1) + 4 * (r & 3);
-            const bf16x4_t lo = lds_read_tr(&lb[krow * LDX + col]);
-            const bf16x4_t hi = lds_read_tr(&lb[(krow + 4) * LDX + col]);
-            fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-#pragma unroll
-          for (int j = 0; j < NB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-      }
-    } else {
-      // v_mfma_f32_32x32x2f32: lane half h holds k = h*16 + e at step e of
-      // the 32-deep slab, for both operands
-      const int k0 = (lane >> 5) * 16;
-#pragma unroll
-      for (int kq = 0; kq < 4; ++kq) {
-        f32x4_t fa[NB], fb[NB];
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-          fa[i] = *reinterpret_cast<const f32x4_t*>(&la[(wm * WT + i * 32 + (lane & 31)) * LDA + k0 + kq * 4]);
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          if constexpr (!KMAJOR_B) {
-            fb[j] = *reinterpret_cast<const f32x4_t*>(&lb[(wn * WT + j * 32 + (lane & 31)) * LDA + k0 + kq * 4]);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) fb[j][e] = lb[(k0 + kq * 4 + e) * LDX + wn * WT + j * 32 + (lane & 31)];
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-#pragma unroll
-          for (int j = 0; j < NB; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][e], fb[j][e], acc[i][j], 0, 0, 0);
-      }
-    }
-    if (more) {
-      E* na = lds_a + ((kt + 1) & 1) * A_ELEMS;
-      E* nb = lds_b + ((kt + 1) & 1) * B_ELEMS;
-#pragma unroll
-      for (int q = 0; q < NPA; ++q)
-        *reinterpret_cast<u32x4_t*>(&na[(arow + q * RPP) * LDA + achunk * EPE]) = ra[q];
-#pragma unroll
-      for (int q = 0; q < NPB; ++q)
-        *reinterpret_cast<u32x4_t*>(&nb[(brow + q * BRPP) * BLDS + bchunk * EPE]) = rb[q];
-    }
+  load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, 0, a_step, b_step, ra0, rb0);
+  store_stage<NPA, NPB, E>(lds_a, lds_b, arow, achunk, RPP, LDA, brow, bchunk, BRPP, BLDS, EPE, ra0, rb0);
+  load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, 1, a_step, b_step, ra1, rb1);
+  __syncthreads();
+  // sched_barrier(0) keeps the scheduler from sinking the prefetch below
+  // the MFMAs (which would shrink the prefetch distance to one step).
+  for (int kt = 0; kt < KT; kt += 2) {
+    load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, min(kt + 2, KT - 1), a_step, b_step, ra0, rb0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_stage<F32, KMAJOR_B, NB, WT, BK, LDA, LDX>(lds_a, lds_b, acc, lane, wm, wn);
+    __builtin_amdgcn_sched_barrier(0);
+    store_stage<NPA, NPB, E>(lds_a + A_ELEMS, lds_b + B_ELEMS, arow, achunk, RPP, LDA, brow, bchunk, BRPP, BLDS,
+                             EPE, ra1, rb1);
+    __syncthreads();
+    load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, min(kt + 3, KT - 1), a_step, b_step, ra1, rb1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_stage<F32, KMAJOR_B, NB, WT, BK, LDA, LDX>(lds_a + A_ELEMS, lds_b + B_ELEMS, acc, lane, wm, wn);
+    __builtin_amdgcn_sched_barrier(0);
+    store_stage<NPA, NPB, E>(lds_a, lds_b, arow, achunk, RPP, LDA, brow, bchunk, BRPP, BLDS, EPE, ra0, rb0);
     __syncthreads();
   }
 
