@@ -129,7 +129,7 @@ muon_status_t validate(const muon_tensor_t* ts, int32_t n, const muon_precond_t*
       return fail(MUON_ERR_ALIGNMENT, who + "pointers must be aligned to their element size");
     const int64_t h = t.split_rows ? t.split_rows : t.rows;
     const int64_t m = std::min<int64_t>(h, t.cols), nn = std::max<int64_t>(h, t.cols);
-    const int64_t T = t.dtype == MUON_F32 ? kTileF32 : kTileBf16;
+    const int64_t T = t.dtype == MUON_F32 ? kTileF32 : kPadBf16;
     if (round_up(m, T) * round_up(nn, T) > (int64_t(1) << 31))
       return fail(MUON_ERR_UNSUPPORTED, who + "matrix too large for one orthogonalisation unit");
     auto add = [&](const void* p, int64_t ld, size_t esz, const char* what) {
@@ -252,7 +252,7 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
       u.m = int(std::min<int64_t>(h, t.cols));
       u.n = int(std::max<int64_t>(h, t.cols));
       u.f32 = t.dtype == MUON_F32 || u.m < kMinBf16NsSide;   // NS precision of the unit
-      const int T = u.f32 ? kTileF32 : kTileBf16;
+      const int T = u.f32 ? kTileF32 : kPadBf16;
       u.mp = int(round_up(u.m, T));
       u.np = int(round_up(u.n, T));
       u.lr_scale = shape_scale(h, t.cols, hp->scale_mode) * t.lr_mult;
@@ -274,15 +274,15 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
       const UnitPlan& u = plan.units[g.units[gi]];
       for (int r = 0; r < u.k1_tr; ++r)
         for (int c = 0; c < u.k1_tc; ++c) g.ew.push_back({int(gi), r, c, r * u.k1_tc + c});
-      const int T = u.f32 ? kTileF32 : kTileBf16;
-      const int tm = u.mp / T, tn = u.np / T;
-      for (int a = 0; a < tm; ++a)
-        for (int b = a; b < tm; ++b) {
+      const int tg = u.f32 ? kTileF32 : kTileGramBf16;    // Gram / square tile
+      const int tx = u.f32 ? kTileF32 : kTileBxBf16;      // B X tile
+      for (int a = 0; a < u.mp / tg; ++a)
+        for (int b = a; b < u.mp / tg; ++b) {
           g.gram.push_back({int(gi), a, b, 0});
           g.sq.push_back({int(gi), a, b, 0});
         }
-      for (int a = 0; a < tm; ++a)
-        for (int b = 0; b < tn; ++b) g.bx.push_back({int(gi), a, b, 0});
+      for (int a = 0; a < u.mp / tx; ++a)
+        for (int b = 0; b < u.np / tx; ++b) g.bx.push_back({int(gi), a, b, 0});
     }
     g.gram = xcd_order(g.gram, plan.units, g, kGram);
     g.sq = xcd_order(g.sq, plan.units, g, kSquare);
@@ -492,9 +492,10 @@ std::string plan_json(const Plan& plan, const muon_hparams_t& hp) {
     std::snprintf(buf, sizeof(buf),
                   "%s{\"ns\":\"%s\",\"units\":%zu,\"momentum_tiles\":%zu,\"gram_tiles\":%zu,"
                   "\"square_tiles\":%zu,\"bx_tiles\":%zu,\"gram_blocks\":%zu,\"square_blocks\":%zu,"
-                  "\"bx_blocks\":%zu,\"tile\":%d}",
+                  "\"bx_blocks\":%zu,\"tile\":%d,\"bx_tile\":%d}",
                   first ? "" : ",", g.f32 ? "f32" : "bf16", g.units.size(), g.ew.size(), real(g.gram),
-                  real(g.sq), real(g.bx), g.gram.size(), g.sq.size(), g.bx.size(), g.f32 ? kTileF32 : kTileBf16);
+                  real(g.sq), real(g.bx), g.gram.size(), g.sq.size(), g.bx.size(), g.f32 ? kTileF32 : kTileGramBf16,
+                  g.f32 ? kTileF32 : kTileBxBf16);
     s += buf;
     first = false;
   }

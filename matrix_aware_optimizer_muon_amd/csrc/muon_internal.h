@@ -8,15 +8,20 @@
 
 namespace muon {
 
-// Output tile edge of the Newton-Schulz GEMM phases.  bf16 matrices use
-// 128x128 tiles (4 waves of 64x64, bf16 MFMA 32x32x16); float32 matrices
-// use 64x64 tiles (4 waves of 32x32, fp32 MFMA 32x32x2).  Every NS buffer is
-// zero-padded to a multiple of the tile in both dimensions; zero padding is
-// exact under X X^T, A A and B X.
-#ifndef MUON_TILE_BF16
-#define MUON_TILE_BF16 128
+// Output tiles of the Newton-Schulz GEMM phases.  bf16 matrices use 128x128
+// tiles (4 waves of 64x64, two blocks per CU).  B X can be built with
+// 256x256 tiles (MUON_TILE_BX_BF16=256: 8 waves of 128x64, one block per CU,
+// half the operand bytes per flop); that helps single large matrices but
+// not the GPT-2-sized sets, whose tile counts it quantises.  float32
+// matrices use 64x64 tiles everywhere.  Every NS buffer is zero-padded to a multiple of the
+// largest tile of its precision (kPadBf16 / kTileF32) in both dimensions;
+// zero padding is exact under X X^T, A A and B X.
+#ifndef MUON_TILE_BX_BF16
+#define MUON_TILE_BX_BF16 128
 #endif
-constexpr int kTileBf16 = MUON_TILE_BF16;
+constexpr int kTileGramBf16 = 128;
+constexpr int kTileBxBf16 = MUON_TILE_BX_BF16;
+constexpr int kPadBf16 = kTileBxBf16 > kTileGramBf16 ? kTileBxBf16 : kTileGramBf16;
 constexpr int kTileF32 = 64;
 // Edge of the square tiles of the elementwise phases (momentum, update).
 constexpr int kEwTile = 64;

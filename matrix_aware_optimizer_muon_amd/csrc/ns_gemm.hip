@@ -38,20 +38,29 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(1))) const u32x4_t gu32x4_t;     // global memory
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;       // LDS
 
-constexpr int kThreads = 256;
-
-template <bool F32> struct Cfg;
-template <> struct Cfg<false> {
+// Tile configuration per precision and phase.  BT: square output tile;
+// NWM x NWN waves, each owning a (BT/NWM) x (BT/NWN) block of 32x32 MFMA
+// tiles; BK: K depth of one LDS stage; OCC: blocks per CU the registers and
+// LDS allow.
+template <bool F32, int PH> struct Cfg;
+template <int PH> struct Cfg<false, PH> {        // bf16, Gram and square
   using E = uint16_t;
-  static constexpr int BT = kTileBf16, WT = kTileBf16 / 2, BK = 64;
-  static constexpr int OCC = BT >= 256 ? 1 : 2;   // blocks per CU the registers allow
+  static constexpr int BT = kTileGramBf16, NWM = 2, NWN = 2, BK = 64, OCC = 2;
+  static constexpr int PF = 2;     // K stages prefetched in registers
   static constexpr int PAD = 8;    // K-contiguous tiles: 144-byte rows
-  static constexpr int XPAD = 32;  // K-major X tile: 320-byte rows, conflict-free transposing reads
+  static constexpr int XPAD = 32;  // K-major X tile: rows 64 bytes past a multiple of 256
 };
-template <> struct Cfg<true> {
+template <> struct Cfg<false, kBX> {             // bf16, B X: one 8-wave block per CU
+  using E = uint16_t;
+  static constexpr int BT = kTileBxBf16, NWM = 2, NWN = 4, BK = 64, OCC = 1;
+  static constexpr int PF = 1;     // 128 accumulators per lane leave room for one stage
+  static constexpr int PAD = 8;
+  static constexpr int XPAD = 32;
+};
+template <int PH> struct Cfg<true, PH> {         // float32, all phases
   using E = float;
-  static constexpr int BT = kTileF32, WT = kTileF32 / 2, BK = 32;
-  static constexpr int OCC = 2;
+  static constexpr int BT = kTileF32, NWM = 2, NWN = 2, BK = 32, OCC = 2;
+  static constexpr int PF = 2;
   static constexpr int PAD = 4;
   static constexpr int XPAD = 4;
 };
@@ -86,37 +95,38 @@ __device__ __forceinline__ void store_stage(E* la, E* lb, int arow, int achunk, 
 }
 
 // MFMAs of one BK-deep stage held in LDS (la: K-contiguous A tile; lb: the
-// B tile, K-contiguous or K-major).
-template <bool F32, bool KMAJOR_B, int NB, int WT, int BK, int LDA, int LDX, typename E>
-__device__ __forceinline__ void mma_stage(const E* la, const E* lb, f32x16_t (&acc)[NB][NB], int lane, int wm,
+// B tile, K-contiguous or K-major).  The wave owns rows wm*WTM.. and columns
+// wn*WTN.. of the block tile, as NBM x NBN tiles of 32x32.
+template <bool F32, bool KMAJOR_B, int NBM, int NBN, int WTM, int WTN, int BK, int LDA, int LDX, typename E>
+__device__ __forceinline__ void mma_stage(const E* la, const E* lb, f32x16_t (&acc)[NBM][NBN], int lane, int wm,
                                           int wn) {
   if constexpr (!F32) {
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8_t fa[NB], fb[NB];
+      bf16x8_t fa[NBM], fb[NBN];
       const int kk = ks * 16 + (lane >> 5) * 8;
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8_t*>(&la[(wm * WT + i * 32 + (lane & 31)) * LDA + kk]);
+      for (int i = 0; i < NBM; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8_t*>(&la[(wm * WTM + i * 32 + (lane & 31)) * LDA + kk]);
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
+      for (int j = 0; j < NBN; ++j) {
         if constexpr (!KMAJOR_B) {
-          fb[j] = *reinterpret_cast<const bf16x8_t*>(&lb[(wn * WT + j * 32 + (lane & 31)) * LDA + kk]);
+          fb[j] = *reinterpret_cast<const bf16x8_t*>(&lb[(wn * WTN + j * 32 + (lane & 31)) * LDA + kk]);
         } else {
           // lane group g = lane/16 covers columns 16*(g%2).. and k-half g/2;
           // lane r of the group points at row k + r/4, columns 4*(r%4)..
           const int g = lane >> 4, r = lane & 15;
           const int krow = ks * 16 + 8 * (g >> 1) + (r >> 2);
-          const int col = wn * WT + j * 32 + 16 * (g & 1) + 4 * (r & 3);
+          const int col = wn * WTN + j * 32 + 16 * (g & 1) + 4 * (r & 3);
           const bf16x4_t lo = lds_read_tr(&lb[krow * LDX + col]);
           const bf16x4_t hi = lds_read_tr(&lb[(krow + 4) * LDX + col]);
           fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
       }
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
+      for (int i = 0; i < NBM; ++i)
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
+        for (int j = 0; j < NBN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
   } else {
@@ -125,23 +135,23 @@ __device__ __forceinline__ void mma_stage(const E* la, const E* lb, f32x16_t (&a
     const int k0 = (lane >> 5) * 16;
 #pragma unroll
     for (int kq = 0; kq < 4; ++kq) {
-      f32x4_t fa[NB], fb[NB];
+      f32x4_t fa[NBM], fb[NBN];
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
-        fa[i] = *reinterpret_cast<const f32x4_t*>(&la[(wm * WT + i * 32 + (lane & 31)) * LDA + k0 + kq * 4]);
+      for (int i = 0; i < NBM; ++i)
+        fa[i] = *reinterpret_cast<const f32x4_t*>(&la[(wm * WTM + i * 32 + (lane & 31)) * LDA + k0 + kq * 4]);
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
+      for (int j = 0; j < NBN; ++j) {
         if constexpr (!KMAJOR_B) {
-          fb[j] = *reinterpret_cast<const f32x4_t*>(&lb[(wn * WT + j * 32 + (lane & 31)) * LDA + k0 + kq * 4]);
+          fb[j] = *reinterpret_cast<const f32x4_t*>(&lb[(wn * WTN + j * 32 + (lane & 31)) * LDA + k0 + kq * 4]);
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) fb[j][e] = lb[(k0 + kq * 4 + e) * LDX + wn * WT + j * 32 + (lane & 31)];
+          for (int e = 0; e < 4; ++e) fb[j][e] = lb[(k0 + kq * 4 + e) * LDX + wn * WTN + j * 32 + (lane & 31)];
         }
       }
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
+      for (int i = 0; i < NBM; ++i)
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
+        for (int j = 0; j < NBN; ++j)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][e], fb[j][e], acc[i][j], 0, 0, 0);
@@ -149,31 +159,45 @@ __device__ __forceinline__ void mma_stage(const E* la, const E* lb, f32x16_t (&a
   }
 }
 
+// Accumulators of one 32-row strip (NBN tiles of 32x32) into the wave's LDS
+// staging area, in row-major order (pitch EPP floats).  v_mfma 32x32 output:
+// lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+template <int NBN, int EPP>
+__device__ __forceinline__ void stage_strip(const f32x16_t (&row)[NBN], float* ep, int lane) {
+#pragma unroll
+  for (int j = 0; j < NBN; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      ep[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * EPP + j * 32 + (lane & 31)] = row[j][r];
+}
+
 template <bool F32, int PH>
-__global__ __launch_bounds__(kThreads, Cfg<F32>::OCC)
+__global__ __launch_bounds__((64 * Cfg<F32, PH>::NWM * Cfg<F32, PH>::NWN), (Cfg<F32, PH>::OCC))
 void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restrict__ tasks,
                     GemmParams p) {
-  using C = Cfg<F32>;
+  using C = Cfg<F32, PH>;
   using E = typename C::E;
-  constexpr int BT = C::BT, WT = C::WT, BK = C::BK;
+  constexpr int BT = C::BT, BK = C::BK, NWM = C::NWM, NWN = C::NWN;
+  constexpr int NT = 64 * NWM * NWN;               // threads per block
+  constexpr int WTM = BT / NWM, WTN = BT / NWN;    // wave tile
+  constexpr int NBM = WTM / 32, NBN = WTN / 32;    // 32x32 MFMA tiles per wave
   constexpr bool KMAJOR_B = PH == kBX;             // X operand of B X is K-major
   constexpr int LDA = BK + C::PAD;                 // pitch of K-contiguous tiles
   constexpr int LDX = BT + C::XPAD;                // pitch of the K-major tile
-  constexpr int NB = WT / 32;                      // 32x32 blocks per wave edge
   constexpr int EPE = 16 / sizeof(E);              // elements per 16-byte chunk
   constexpr int CPR = BK / EPE;                    // chunks per K-contiguous row
-  constexpr int RPP = kThreads / CPR;              // rows per load pass
+  constexpr int RPP = NT / CPR;                    // rows per load pass
   constexpr int NPA = BT / RPP;                    // load passes, K-contiguous tile
   constexpr int CPRX = BT / EPE;                   // chunks per K-major row
-  constexpr int RPPX = kThreads / CPRX;
+  constexpr int RPPX = NT / CPRX;
   constexpr int NPX = BK / RPPX;                   // load passes, K-major tile
   constexpr int NPB = KMAJOR_B ? NPX : NPA;
   constexpr int A_ELEMS = BT * LDA;
   constexpr int B_ELEMS = KMAJOR_B ? BK * LDX : BT * LDA;
-  constexpr int EPP = WT + 8;                      // epilogue LDS pitch (floats)
-  static_assert(CPR * RPP == kThreads && NPA * RPP == BT, "tile/thread mismatch");
-  static_assert(CPRX * RPPX == kThreads && NPX * RPPX == BK, "tile/thread mismatch");
-  static_assert(4 * 32 * EPP * 4 <= 2 * (A_ELEMS + B_ELEMS) * static_cast<int>(sizeof(E)),
+  constexpr int EPP = WTN + 8;                     // epilogue LDS pitch (floats)
+  static_assert(CPR * RPP == NT && NPA * RPP == BT, "tile/thread mismatch");
+  static_assert(CPRX * RPPX == NT && NPX * RPPX == BK, "tile/thread mismatch");
+  static_assert(NWM * NWN * 32 * EPP * 4 <= 2 * (A_ELEMS + B_ELEMS) * static_cast<int>(sizeof(E)),
                 "epilogue staging must fit in the operand LDS");
 
   __shared__ __attribute__((aligned(16))) E smem[2 * (A_ELEMS + B_ELEMS)];
@@ -208,18 +232,18 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / NWN, wn = wave % NWN;
   const int arow = tid / CPR, achunk = tid % CPR;                       // K-contiguous loads
   const int brow = KMAJOR_B ? tid / CPRX : arow;
   const int bchunk = KMAJOR_B ? tid % CPRX : achunk;
   constexpr int BRPP = KMAJOR_B ? RPPX : RPP;
   constexpr int BLDS = KMAJOR_B ? LDX : LDA;
 
-  f32x16_t acc[NB][NB];
+  f32x16_t acc[NBM][NBN];
 #pragma unroll
-  for (int i = 0; i < NB; ++i)
+  for (int i = 0; i < NBM; ++i)
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+    for (int j = 0; j < NBN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -232,36 +256,60 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   const size_t a_step = BK / EPE;
   const size_t b_step = KMAJOR_B ? static_cast<size_t>(BK) * ldb_g / EPE : BK / EPE;
 
-  // Two register stages in flight: the loads for step kt+2 are issued
-  // before the MFMAs of step kt; the stage for kt+1 is stored to LDS after
-  // them.  The loop is unrolled by two so both register sets stay static,
-  // and it has no branches around memory operations (the prefetch index is
-  // clamped; the last two steps reload the final stage into the idle
-  // buffer), so the compiler's wait counts stay exact.  K is a multiple of
-  // 2*BK because every NS buffer is padded to the tile, which is 2*BK.
-  static_assert(BT % (2 * BK) == 0, "K steps must come in pairs");
-  u32x4_t ra0[NPA], rb0[NPB], ra1[NPA], rb1[NPB];
+  // K pipeline.  PF = 2: two register stages in flight -- the loads for step
+  // kt+2 are issued before the MFMAs of step kt and the stage for kt+1 is
+  // stored to LDS after them; the loop is unrolled by two so both register
+  // sets stay static.  PF = 1: one stage in flight (loads for kt+1 issued
+  // before the MFMAs of kt).  There are no branches around memory
+  // operations (prefetch indices are clamped and the tail reloads the final
+  // stage into the idle buffer), so the compiler's wait counts stay exact.
+  // K is a multiple of 2*BK because every NS buffer is padded to at least
+  // the Gram tile, which is 2*BK.
+  static_assert(kTileGramBf16 % (2 * BK) == 0 || F32, "K steps must come in pairs");
   const int KT = K / BK;
+  u32x4_t ra0[NPA], rb0[NPB];
   load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, 0, a_step, b_step, ra0, rb0);
   store_stage<NPA, NPB, E>(lds_a, lds_b, arow, achunk, RPP, LDA, brow, bchunk, BRPP, BLDS, EPE, ra0, rb0);
-  load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, 1, a_step, b_step, ra1, rb1);
-  __syncthreads();
-  // sched_barrier(0) keeps the scheduler from sinking the prefetch below
-  // the MFMAs (which would shrink the prefetch distance to one step).
-  for (int kt = 0; kt < KT; kt += 2) {
-    load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, min(kt + 2, KT - 1), a_step, b_step, ra0, rb0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma_stage<F32, KMAJOR_B, NB, WT, BK, LDA, LDX>(lds_a, lds_b, acc, lane, wm, wn);
-    __builtin_amdgcn_sched_barrier(0);
-    store_stage<NPA, NPB, E>(lds_a + A_ELEMS, lds_b + B_ELEMS, arow, achunk, RPP, LDA, brow, bchunk, BRPP, BLDS,
-                             EPE, ra1, rb1);
+  if constexpr (C::PF == 2) {
+    u32x4_t ra1[NPA], rb1[NPB];
+    load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, 1, a_step, b_step, ra1, rb1);
     __syncthreads();
-    load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, min(kt + 3, KT - 1), a_step, b_step, ra1, rb1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma_stage<F32, KMAJOR_B, NB, WT, BK, LDA, LDX>(lds_a + A_ELEMS, lds_b + B_ELEMS, acc, lane, wm, wn);
-    __builtin_amdgcn_sched_barrier(0);
-    store_stage<NPA, NPB, E>(lds_a, lds_b, arow, achunk, RPP, LDA, brow, bchunk, BRPP, BLDS, EPE, ra0, rb0);
+    // sched_barrier(0) keeps the scheduler from sinking the prefetch below
+    // the MFMAs (which would shrink the prefetch distance to one step).
+    for (int kt = 0; kt < KT; kt += 2) {
+      load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, min(kt + 2, KT - 1), a_step, b_step, ra0, rb0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, LDA, LDX>(lds_a, lds_b, acc, lane, wm, wn);
+      __builtin_amdgcn_sched_barrier(0);
+      store_stage<NPA, NPB, E>(lds_a + A_ELEMS, lds_b + B_ELEMS, arow, achunk, RPP, LDA, brow, bchunk, BRPP, BLDS,
+                               EPE, ra1, rb1);
+      __syncthreads();
+      load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, min(kt + 3, KT - 1), a_step, b_step, ra1, rb1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, LDA, LDX>(lds_a + A_ELEMS, lds_b + B_ELEMS, acc, lane, wm,
+                                                                  wn);
+      __builtin_amdgcn_sched_barrier(0);
+      store_stage<NPA, NPB, E>(lds_a, lds_b, arow, achunk, RPP, LDA, brow, bchunk, BRPP, BLDS, EPE, ra0, rb0);
+      __syncthreads();
+    }
+  } else {
     __syncthreads();
+    for (int kt = 0; kt < KT; kt += 2) {
+      load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, kt + 1, a_step, b_step, ra0, rb0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, LDA, LDX>(lds_a, lds_b, acc, lane, wm, wn);
+      __builtin_amdgcn_sched_barrier(0);
+      store_stage<NPA, NPB, E>(lds_a + A_ELEMS, lds_b + B_ELEMS, arow, achunk, RPP, LDA, brow, bchunk, BRPP, BLDS,
+                               EPE, ra0, rb0);
+      __syncthreads();
+      load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, min(kt + 2, KT - 1), a_step, b_step, ra0, rb0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, LDA, LDX>(lds_a + A_ELEMS, lds_b + B_ELEMS, acc, lane, wm,
+                                                                  wn);
+      __builtin_amdgcn_sched_barrier(0);
+      store_stage<NPA, NPB, E>(lds_a, lds_b, arow, achunk, RPP, LDA, brow, bchunk, BRPP, BLDS, EPE, ra0, rb0);
+      __syncthreads();
+    }
   }
 
   // ---------------------------------------------------------------- epilogue
@@ -281,19 +329,18 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   const float decay = p.lr * p.weight_decay;
   const float step = p.lr * u.lr_scale;
   float* ep = reinterpret_cast<float*>(smem) + wave * (32 * EPP);
-  const int row_base = ti * BT + wm * WT;
-  const int col_base = tj * BT + wn * WT;
-  constexpr int SEGS = WT / 8;                       // row segments per strip row
+  const int row_base = ti * BT + wm * WTM;
+  const int col_base = tj * BT + wn * WTN;
+  constexpr int SEGS = WTN / 8;                      // row segments per strip row
   constexpr int RITER = 32 * SEGS / 64;              // row segments per lane
-  constexpr int CITER = WT * 4 / 64;                 // column segments per lane
+  constexpr int CITER = WTN * 4 / 64;                // column segments per lane
 
+  for (int pi = 0; pi < NBM; ++pi) {
+    // acc is only ever indexed with constants (a runtime index would move
+    // the whole accumulator array to scratch memory)
 #pragma unroll
-  for (int pi = 0; pi < NB; ++pi) {
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        ep[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * EPP + j * 32 + (lane & 31)] = acc[pi][j][r];
+    for (int c = 0; c < NBM; ++c)
+      if (c == pi) stage_strip<NBN, EPP>(acc[c], ep, lane);
     __syncthreads();
 
 #pragma unroll
@@ -358,7 +405,7 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
 #pragma unroll
       for (int q = 0; q < CITER; ++q) {
         const int s = lane + 64 * q;
-        const int col = s % WT, rseg = s / WT;
+        const int col = s % WTN, rseg = s / WTN;
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = ep[(rseg * 8 + e) * EPP + col];
@@ -384,13 +431,19 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   }
 }
 
+template <bool F32, int PH>
+void launch_one(const UnitDev* units, const GemmTask* tasks, int n, const GemmParams& p, hipStream_t s) {
+  constexpr int nt = 64 * Cfg<F32, PH>::NWM * Cfg<F32, PH>::NWN;
+  ns_gemm_kernel<F32, PH><<<n, nt, 0, s>>>(units, tasks, p);
+}
+
 template <bool F32>
 hipError_t launch_phase(int phase, const UnitDev* units, const GemmTask* tasks, int n,
                         const GemmParams& p, hipStream_t s) {
   switch (phase) {
-    case kGram: ns_gemm_kernel<F32, kGram><<<n, kThreads, 0, s>>>(units, tasks, p); break;
-    case kSquare: ns_gemm_kernel<F32, kSquare><<<n, kThreads, 0, s>>>(units, tasks, p); break;
-    default: ns_gemm_kernel<F32, kBX><<<n, kThreads, 0, s>>>(units, tasks, p); break;
+    case kGram: launch_one<F32, kGram>(units, tasks, n, p, s); break;
+    case kSquare: launch_one<F32, kSquare>(units, tasks, n, p, s); break;
+    default: launch_one<F32, kBX>(units, tasks, n, p, s); break;
   }
   return hipGetLastError();
 }

@@ -176,7 +176,7 @@ def test_plan_gpt2_xl_and_padding():
 
 def test_plan_split_rows_and_fp32():
     t = fakes([(3 * 128, 128)])[0]
-    t.split_rows = 128
+    t.split_rows = 128   # 128-row blocks pad to 256 for the B X tile
     f = fake(256, 512, B.MUON_F32, base=BASE + (1 << 30))[0]
     small = fake(17, 33, B.MUON_BF16, base=BASE + (1 << 31))[0]
     plan = mm.plan_describe([t, f, small], mm.default_hparams())
