@@ -50,10 +50,19 @@ template <int PH> struct Cfg<false, PH> {        // bf16, Gram and square
   static constexpr int PAD = 8;    // K-contiguous tiles: 144-byte rows
   static constexpr int XPAD = 32;  // K-major X tile: rows 64 bytes past a multiple of 256
 };
-template <> struct Cfg<false, kBX> {             // bf16, B X: one 8-wave block per CU
+#ifndef MUON_BX_NWN
+#define MUON_BX_NWN 4
+#endif
+#ifndef MUON_BX_OCC
+#define MUON_BX_OCC 1
+#endif
+#ifndef MUON_BX_PF
+#define MUON_BX_PF 1
+#endif
+template <> struct Cfg<false, kBX> {             // bf16, B X
   using E = uint16_t;
-  static constexpr int BT = kTileBxBf16, NWM = 2, NWN = 4, BK = 64, OCC = 1;
-  static constexpr int PF = 1;     // 128 accumulators per lane leave room for one stage
+  static constexpr int BT = kTileBxBf16, NWM = 2, NWN = MUON_BX_NWN, BK = 64, OCC = MUON_BX_OCC;
+  static constexpr int PF = MUON_BX_PF;
   static constexpr int PAD = 8;
   static constexpr int XPAD = 32;
 };
@@ -101,17 +110,22 @@ template <bool F32, bool KMAJOR_B, int NBM, int NBN, int WTM, int WTN, int BK, i
 __device__ __forceinline__ void mma_stage(const E* la, const E* lb, f32x16_t (&acc)[NBM][NBN], int lane, int wm,
                                           int wn) {
   if constexpr (!F32) {
+    // Every fragment of the stage is read first and the MFMAs follow as one
+    // stream: LDS returns in order, so each MFMA waits only for its own
+    // operands while the later reads are still in flight (reading just
+    // ahead of each MFMA exposes a full LDS round trip per 32x32 step).
+    constexpr int KS = BK / 16;
+    bf16x8_t fa[KS][NBM], fb[KS][NBN];
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8_t fa[NBM], fb[NBN];
+    for (int ks = 0; ks < KS; ++ks) {
       const int kk = ks * 16 + (lane >> 5) * 8;
 #pragma unroll
       for (int i = 0; i < NBM; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8_t*>(&la[(wm * WTM + i * 32 + (lane & 31)) * LDA + kk]);
+        fa[ks][i] = *reinterpret_cast<const bf16x8_t*>(&la[(wm * WTM + i * 32 + (lane & 31)) * LDA + kk]);
 #pragma unroll
       for (int j = 0; j < NBN; ++j) {
         if constexpr (!KMAJOR_B) {
-          fb[j] = *reinterpret_cast<const bf16x8_t*>(&lb[(wn * WTN + j * 32 + (lane & 31)) * LDA + kk]);
+          fb[ks][j] = *reinterpret_cast<const bf16x8_t*>(&lb[(wn * WTN + j * 32 + (lane & 31)) * LDA + kk]);
         } else {
           // lane group g = lane/16 covers columns 16*(g%2).. and k-half g/2;
           // lane r of the group points at row k + r/4, columns 4*(r%4)..
@@ -120,15 +134,18 @@ __device__ __forceinline__ void mma_stage(const E* la, const E* lb, f32x16_t (&a
           const int col = wn * WTN + j * 32 + 16 * (g & 1) + 4 * (r & 3);
           const bf16x4_t lo = lds_read_tr(&lb[krow * LDX + col]);
           const bf16x4_t hi = lds_read_tr(&lb[(krow + 4) * LDX + col]);
-          fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          fb[ks][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
       }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int i = 0; i < NBM; ++i)
 #pragma unroll
         for (int j = 0; j < NBN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
   } else {
     // v_mfma_f32_32x32x2f32: lane half h holds k = h*16 + e at step e of the
     // 32-deep slab, for both operands
@@ -313,6 +330,31 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   }
 
   // ---------------------------------------------------------------- epilogue
+  // B X: the X master of every row segment this lane will write (bf16: hi
+  // and lo; float32: the 8 values as two halves) is requested before the
+  // first LDS round, so one HBM latency is paid per tile, not per strip.
+  constexpr int SEGS = WTN / 8;                      // row segments per strip row
+  constexpr int RITER = 32 * SEGS / 64;              // row segments per lane
+  const int row_base = ti * BT + wm * WTM;
+  const int col_base = tj * BT + wn * WTN;
+  u32x4_t pre0[KMAJOR_B ? NBM : 1][RITER], pre1[KMAJOR_B ? NBM : 1][RITER];
+  if constexpr (KMAJOR_B) {
+#pragma unroll
+    for (int pi = 0; pi < NBM; ++pi)
+#pragma unroll
+      for (int q = 0; q < RITER; ++q) {
+        const int sg = lane + 64 * q;
+        const size_t off = static_cast<size_t>(row_base + pi * 32 + sg / SEGS) * np + col_base + (sg % SEGS) * 8;
+        if constexpr (F32) {
+          pre0[pi][q] = gld<u32x4_t>(xcur + off);
+          pre1[pi][q] = gld<u32x4_t>(xcur + off + 4);
+        } else {
+          pre0[pi][q] = gld<u32x4_t>(xcur + off);
+          pre1[pi][q] = gld<u32x4_t>(static_cast<const E*>(u.xl) + off);
+        }
+      }
+  }
+
   // Each wave stages one 32-row strip of its accumulators in LDS, then
   // writes row segments (natural layout) and, where needed, column segments
   // (mirror tiles of A and B; weight rows of a tall matrix in the last
@@ -329,18 +371,14 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   const float decay = p.lr * p.weight_decay;
   const float step = p.lr * u.lr_scale;
   float* ep = reinterpret_cast<float*>(smem) + wave * (32 * EPP);
-  const int row_base = ti * BT + wm * WTM;
-  const int col_base = tj * BT + wn * WTN;
-  constexpr int SEGS = WTN / 8;                      // row segments per strip row
-  constexpr int RITER = 32 * SEGS / 64;              // row segments per lane
   constexpr int CITER = WTN * 4 / 64;                // column segments per lane
 
-  for (int pi = 0; pi < NBM; ++pi) {
-    // acc is only ever indexed with constants (a runtime index would move
-    // the whole accumulator array to scratch memory)
+  // acc and the master registers are only ever indexed with constants (a
+  // runtime index would move the whole array to scratch memory), so the
+  // strip loop is unrolled.
 #pragma unroll
-    for (int c = 0; c < NBM; ++c)
-      if (c == pi) stage_strip<NBN, EPP>(acc[c], ep, lane);
+  for (int pi = 0; pi < NBM; ++pi) {
+    stage_strip<NBN, EPP>(acc[pi], ep, lane);
     __syncthreads();
 
 #pragma unroll
@@ -368,11 +406,15 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
         const size_t off = static_cast<size_t>(gr) * np + gc;
         float xm[8];
         if constexpr (F32) {
-          ld8<true>(xcur, off, xm);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xm[e] = __uint_as_float(pre0[pi][q][e]);
+            xm[4 + e] = __uint_as_float(pre1[pi][q][e]);
+          }
         } else {
           float xl[8];
-          ld8<false>(xcur, off, xm);
-          ld8<false>(u.xl, off, xl);
+          unpack8_bf16(pre0[pi][q], xm);
+          unpack8_bf16(pre1[pi][q], xl);
 #pragma unroll
           for (int e = 0; e < 8; ++e) xm[e] += xl[e];
         }
