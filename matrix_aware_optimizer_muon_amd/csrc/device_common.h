@@ -93,17 +93,19 @@ __device__ __forceinline__ float wave_sum(float v) {
 namespace muon {
 
 // 1 / (||U||_F + eps) of one unit from its per-tile partial sums of squares,
-// folded by a whole 256-thread block in a fixed order (thread t takes
-// partials t, t+256, ...; then a fixed shuffle tree and a fixed sum of the
-// four wave totals), so every block that calls it gets the same bits.
-// `red` is 4 floats of shared memory.  Must be called by all threads.
+// folded by the first 256 threads of the block in a fixed order (thread t
+// takes partials t, t+256, ...; then a fixed shuffle tree and a fixed sum of
+// the four wave totals), so every block that calls it, whatever its size
+// (a multiple of 256 threads), gets the same bits.  `red` is 4 floats of
+// shared memory.  Must be called by all threads.
 __device__ __forceinline__ float unit_inv_norm(const float* partials, int n, float eps, float* red) {
   float acc = 0.f;
-  for (int k = threadIdx.x; k < n; k += 256) acc += gld<float>(partials + k);
+  if (threadIdx.x < 256)
+    for (int k = threadIdx.x; k < n; k += 256) acc += gld<float>(partials + k);
   acc = wave_sum(acc);
   const int wave = threadIdx.x >> 6;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[wave] = acc;
+  if (wave < 4 && (threadIdx.x & 63) == 0) red[wave] = acc;
   __syncthreads();
   const float tot = (red[0] + red[1]) + (red[2] + red[3]);
   return 1.0f / (sqrtf(tot) + eps);
