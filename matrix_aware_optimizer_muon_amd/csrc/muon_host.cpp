@@ -281,8 +281,11 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
           g.gram.push_back({int(gi), a, b, 0});
           g.sq.push_back({int(gi), a, b, 0});
         }
-      for (int a = 0; a < u.mp / tx; ++a)
-        for (int b = 0; b < u.np / tx; ++b) g.bx.push_back({int(gi), a, b, 0});
+      // B X tiles column by column: the tiles that run together then share
+      // one column strip of X and all of B (a unit's B is the smaller
+      // operand), so each strip of X comes from HBM about once.
+      for (int b = 0; b < u.np / tx; ++b)
+        for (int a = 0; a < u.mp / tx; ++a) g.bx.push_back({int(gi), a, b, 0});
     }
     g.gram = xcd_order(g.gram, plan.units, g, kGram);
     g.sq = xcd_order(g.sq, plan.units, g, kSquare);

@@ -110,22 +110,17 @@ template <bool F32, bool KMAJOR_B, int NBM, int NBN, int WTM, int WTN, int BK, i
 __device__ __forceinline__ void mma_stage(const E* la, const E* lb, f32x16_t (&acc)[NBM][NBN], int lane, int wm,
                                           int wn) {
   if constexpr (!F32) {
-    // Every fragment of the stage is read first and the MFMAs follow as one
-    // stream: LDS returns in order, so each MFMA waits only for its own
-    // operands while the later reads are still in flight (reading just
-    // ahead of each MFMA exposes a full LDS round trip per 32x32 step).
-    constexpr int KS = BK / 16;
-    bf16x8_t fa[KS][NBM], fb[KS][NBN];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8_t fa[NBM], fb[NBN];
       const int kk = ks * 16 + (lane >> 5) * 8;
 #pragma unroll
       for (int i = 0; i < NBM; ++i)
-        fa[ks][i] = *reinterpret_cast<const bf16x8_t*>(&la[(wm * WTM + i * 32 + (lane & 31)) * LDA + kk]);
+        fa[i] = *reinterpret_cast<const bf16x8_t*>(&la[(wm * WTM + i * 32 + (lane & 31)) * LDA + kk]);
 #pragma unroll
       for (int j = 0; j < NBN; ++j) {
         if constexpr (!KMAJOR_B) {
-          fb[ks][j] = *reinterpret_cast<const bf16x8_t*>(&lb[(wn * WTN + j * 32 + (lane & 31)) * LDA + kk]);
+          fb[j] = *reinterpret_cast<const bf16x8_t*>(&lb[(wn * WTN + j * 32 + (lane & 31)) * LDA + kk]);
         } else {
           // lane group g = lane/16 covers columns 16*(g%2).. and k-half g/2;
           // lane r of the group points at row k + r/4, columns 4*(r%4)..
@@ -134,18 +129,15 @@ __device__ __forceinline__ void mma_stage(const E* la, const E* lb, f32x16_t (&a
           const int col = wn * WTN + j * 32 + 16 * (g & 1) + 4 * (r & 3);
           const bf16x4_t lo = lds_read_tr(&lb[krow * LDX + col]);
           const bf16x4_t hi = lds_read_tr(&lb[(krow + 4) * LDX + col]);
-          fb[ks][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
       }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int i = 0; i < NBM; ++i)
 #pragma unroll
         for (int j = 0; j < NBN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
   } else {
     // v_mfma_f32_32x32x2f32: lane half h holds k = h*16 + e at step e of the
     // 32-deep slab, for both operands
@@ -186,6 +178,29 @@ __device__ __forceinline__ void stage_strip(const f32x16_t (&row)[NBN], float* e
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       ep[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * EPP + j * 32 + (lane & 31)] = row[j][r];
+}
+
+// B X: the X master of the output tile's rows is part of the X operand (row
+// r of X is K step r), so while a K step whose rows overlap the tile sits in
+// LDS each lane copies out its own row segments: bf16 the hi half (the lo
+// half is not an operand and comes from HBM), float32 all 8 values.
+template <bool F32, int NBM, int RITER, int SEGS, int WTM, int BK, int LDX, typename E>
+__device__ __forceinline__ void capture_master(const E* lbx, int kt, int kt0, int wm, int col0, int lane,
+                                               u32x4_t (&pre0)[NBM][RITER], u32x4_t (&pre1)[NBM][RITER]) {
+  static_assert(BK % 32 == 0, "32-row strips must not straddle K steps");
+#pragma unroll
+  for (int pi = 0; pi < NBM; ++pi) {
+    const int r0 = wm * WTM + pi * 32;      // first tile row of the strip
+    if (kt == kt0 + r0 / BK) {
+#pragma unroll
+      for (int q = 0; q < RITER; ++q) {
+        const int sg = lane + 64 * q;
+        const E* src = lbx + (r0 % BK + sg / SEGS) * LDX + col0 + (sg % SEGS) * 8;
+        pre0[pi][q] = *reinterpret_cast<const u32x4_t*>(src);
+        if constexpr (F32) pre1[pi][q] = *reinterpret_cast<const u32x4_t*>(src + 4);
+      }
+    }
+  }
 }
 
 template <bool F32, int PH>
@@ -273,6 +288,17 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   const size_t a_step = BK / EPE;
   const size_t b_step = KMAJOR_B ? static_cast<size_t>(BK) * ldb_g / EPE : BK / EPE;
 
+  // row segments of the epilogue: per 32-row strip, SEGS segments of 8 per
+  // row, RITER per lane
+  constexpr int SEGS = WTN / 8;
+  constexpr int RITER = 32 * SEGS / 64;
+  constexpr int NPRE = KMAJOR_B ? NBM : 1;
+  u32x4_t pre0[NPRE][RITER], pre1[NPRE][RITER];
+  const int kt0 = ti * BT / BK;                      // K step of the tile's first row
+#define MUON_CAPTURE(LBX, KT)                                                                           \
+  if constexpr (KMAJOR_B)                                                                              \
+    capture_master<F32, NPRE, RITER, SEGS, WTM, BK, LDX>(LBX, KT, kt0, wm, wn * WTN, lane, pre0, pre1);
+
   // K pipeline.  PF = 2: two register stages in flight -- the loads for step
   // kt+2 are issued before the MFMAs of step kt and the stage for kt+1 is
   // stored to LDS after them; the loop is unrolled by two so both register
@@ -296,6 +322,7 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
     for (int kt = 0; kt < KT; kt += 2) {
       load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, min(kt + 2, KT - 1), a_step, b_step, ra0, rb0);
       __builtin_amdgcn_sched_barrier(0);
+      MUON_CAPTURE(lds_b, kt)
       mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, LDA, LDX>(lds_a, lds_b, acc, lane, wm, wn);
       __builtin_amdgcn_sched_barrier(0);
       store_stage<NPA, NPB, E>(lds_a + A_ELEMS, lds_b + B_ELEMS, arow, achunk, RPP, LDA, brow, bchunk, BRPP, BLDS,
@@ -303,6 +330,7 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
       __syncthreads();
       load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, min(kt + 3, KT - 1), a_step, b_step, ra1, rb1);
       __builtin_amdgcn_sched_barrier(0);
+      MUON_CAPTURE(lds_b + B_ELEMS, kt + 1)
       mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, LDA, LDX>(lds_a + A_ELEMS, lds_b + B_ELEMS, acc, lane, wm,
                                                                   wn);
       __builtin_amdgcn_sched_barrier(0);
@@ -314,6 +342,7 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
     for (int kt = 0; kt < KT; kt += 2) {
       load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, kt + 1, a_step, b_step, ra0, rb0);
       __builtin_amdgcn_sched_barrier(0);
+      MUON_CAPTURE(lds_b, kt)
       mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, LDA, LDX>(lds_a, lds_b, acc, lane, wm, wn);
       __builtin_amdgcn_sched_barrier(0);
       store_stage<NPA, NPB, E>(lds_a + A_ELEMS, lds_b + B_ELEMS, arow, achunk, RPP, LDA, brow, bchunk, BRPP, BLDS,
@@ -321,6 +350,7 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
       __syncthreads();
       load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, min(kt + 2, KT - 1), a_step, b_step, ra0, rb0);
       __builtin_amdgcn_sched_barrier(0);
+      MUON_CAPTURE(lds_b + B_ELEMS, kt + 1)
       mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, LDA, LDX>(lds_a + A_ELEMS, lds_b + B_ELEMS, acc, lane, wm,
                                                                   wn);
       __builtin_amdgcn_sched_barrier(0);
@@ -330,28 +360,20 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   }
 
   // ---------------------------------------------------------------- epilogue
-  // B X: the X master of every row segment this lane will write (bf16: hi
-  // and lo; float32: the 8 values as two halves) is requested before the
-  // first LDS round, so one HBM latency is paid per tile, not per strip.
-  constexpr int SEGS = WTN / 8;                      // row segments per strip row
-  constexpr int RITER = 32 * SEGS / 64;              // row segments per lane
+#undef MUON_CAPTURE
+  // B X, bf16: the lo half of the master (the hi half was captured from
+  // LDS) is requested before the first LDS round, so one HBM latency is
+  // paid per tile, not per strip.
   const int row_base = ti * BT + wm * WTM;
   const int col_base = tj * BT + wn * WTN;
-  u32x4_t pre0[KMAJOR_B ? NBM : 1][RITER], pre1[KMAJOR_B ? NBM : 1][RITER];
-  if constexpr (KMAJOR_B) {
+  if constexpr (KMAJOR_B && !F32) {
 #pragma unroll
     for (int pi = 0; pi < NBM; ++pi)
 #pragma unroll
       for (int q = 0; q < RITER; ++q) {
         const int sg = lane + 64 * q;
         const size_t off = static_cast<size_t>(row_base + pi * 32 + sg / SEGS) * np + col_base + (sg % SEGS) * 8;
-        if constexpr (F32) {
-          pre0[pi][q] = gld<u32x4_t>(xcur + off);
-          pre1[pi][q] = gld<u32x4_t>(xcur + off + 4);
-        } else {
-          pre0[pi][q] = gld<u32x4_t>(xcur + off);
-          pre1[pi][q] = gld<u32x4_t>(static_cast<const E*>(u.xl) + off);
-        }
+        pre1[pi][q] = gld<u32x4_t>(static_cast<const E*>(u.xl) + off);
       }
   }
 
