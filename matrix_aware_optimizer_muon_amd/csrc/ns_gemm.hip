@@ -19,10 +19,11 @@
 // layout and the MFMA fragments are read with gfx950's transposing LDS read
 // (ds_read_b64_tr_b16), so no transposed copy of X is ever stored.
 //
-// bf16 path: 128x128 output tile, 4 waves each owning 64x64 (2x2 blocks of
-// v_mfma_f32_32x32x16_bf16), K staged through LDS 64 deep, double-buffered
-// with register prefetch; two blocks fit per CU (<= 78 KB LDS each) so one
-// block's epilogue traffic overlaps the other's MFMA loop.  X is held as a
+// bf16 path: 128x128 output tile (4 waves of 64x64, or 8 waves of 64x32
+// for B X) of v_mfma_f32_32x32x16_bf16, K staged through LDS 64 deep in a
+// two-stage ring filled by direct-to-LDS loads (global_load_lds_dwordx4:
+// no VGPR staging, no LDS store instructions); two blocks fit per CU
+// (64 KB LDS each) so one block's epilogue overlaps the other's MFMA loop.  X is held as a
 // bf16 hi/lo pair so the a*X term keeps ~16 significant bits while the MFMA
 // operand is the hi part.
 // fp32 path: 64x64 tile, 4 waves of 32x32, v_mfma_f32_32x32x2f32.
@@ -40,39 +41,70 @@ typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;       // LDS
 
 // Tile configuration per precision and phase.  BT: square output tile;
 // NWM x NWN waves, each owning a (BT/NWM) x (BT/NWN) block of 32x32 MFMA
-// tiles; BK: K depth of one LDS stage; OCC: blocks per CU the registers and
-// LDS allow.
-template <bool F32, int PH> struct Cfg;
-template <int PH> struct Cfg<false, PH> {        // bf16, Gram and square
-  using E = uint16_t;
-  static constexpr int BT = kTileGramBf16, NWM = 2, NWN = 2, BK = 64, OCC = 2;
-  static constexpr int PF = 2;     // K stages prefetched in registers
-  static constexpr int PAD = 8;    // K-contiguous tiles: 144-byte rows
-  static constexpr int XPAD = 32;  // K-major X tile: rows 64 bytes past a multiple of 256
-};
+// tiles; BK: K depth of one LDS stage; NS: stages in the LDS ring (NS-1 in
+// flight while one is consumed); OCC: blocks per CU the registers and LDS
+// allow.
+#ifndef MUON_NS_BF16
+#define MUON_NS_BF16 2
+#endif
 #ifndef MUON_BX_NWN
 #define MUON_BX_NWN 4
 #endif
 #ifndef MUON_BX_OCC
-#define MUON_BX_OCC 1
+#define MUON_BX_OCC 2
 #endif
-#ifndef MUON_BX_PF
-#define MUON_BX_PF 1
+template <bool F32, int PH> struct Cfg;
+#ifndef MUON_G_NWN
+#define MUON_G_NWN 2
 #endif
+template <int PH> struct Cfg<false, PH> {        // bf16, Gram and square
+  using E = uint16_t;
+  static constexpr int BT = kTileGramBf16, NWM = 2, NWN = MUON_G_NWN, BK = 64, NS = MUON_NS_BF16;
+  static constexpr int OCC = NS <= 2 ? 2 : 1;
+};
 template <> struct Cfg<false, kBX> {             // bf16, B X
   using E = uint16_t;
-  static constexpr int BT = kTileBxBf16, NWM = 2, NWN = MUON_BX_NWN, BK = 64, OCC = MUON_BX_OCC;
-  static constexpr int PF = MUON_BX_PF;
-  static constexpr int PAD = 8;
-  static constexpr int XPAD = 32;
+  static constexpr int BT = kTileBxBf16, NWM = 2, NWN = MUON_BX_NWN, BK = 64, NS = MUON_NS_BF16;
+  static constexpr int OCC = NS <= 2 ? MUON_BX_OCC : 1;
 };
 template <int PH> struct Cfg<true, PH> {         // float32, all phases
   using E = float;
-  static constexpr int BT = kTileF32, NWM = 2, NWN = 2, BK = 32, OCC = 2;
-  static constexpr int PF = 2;
-  static constexpr int PAD = 4;
-  static constexpr int XPAD = 4;
+  static constexpr int BT = kTileF32, NWM = 2, NWN = 2, BK = 32, NS = 2, OCC = 2;
 };
+
+// LDS layout of a stage.  Tiles are stored unpadded as rows of 16-byte
+// chunks, with the chunk order of each row XOR-swizzled so the MFMA
+// fragment reads are free of bank conflicts:
+//   K-contiguous tile (row = M or N index, CPR chunks of K): chunk c of row
+//     r sits at position c ^ (r % 8);
+//   K-major tile of B X (row = k, 16 chunks of columns): chunk c of row k
+//     sits at position c ^ 4 (k % 4), which spreads the four rows a
+//     transposing read touches over distinct banks.
+__device__ __forceinline__ int swz_kc(int r, int c) { return c ^ (r & 7); }
+__device__ __forceinline__ int swz_km(int k, int c) { return c ^ ((k & 3) << 2); }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+// Wait until at most N vector-memory operations of this wave are pending
+// (asm, so the compiler, which does not see the asm loads, keeps it).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for the stage ring.  A __syncthreads fence would also
+// wait for every direct-to-LDS load in flight (they count as LDS writes)
+// and drain the ring; here each wave only completes its own LDS reads
+// (lgkmcnt(0): the buffer refilled after the barrier was read before it),
+// and callers wait for the loads they need with wait_vmcnt.  The asm
+// memory clobbers keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Transposing LDS read (gfx950).  Within each 16-lane group the 8-byte words
 // addressed by the lanes form a 16 x 4 matrix W[lane][e]; lane i receives
@@ -83,52 +115,69 @@ __device__ __forceinline__ bf16x4_t lds_read_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
 }
 
-template <int NPA, int NPB>
-__device__ __forceinline__ void load_stage(const gu32x4_t* ga, const gu32x4_t* gb, size_t a_pass, size_t b_pass,
-                                           int kt, size_t a_step, size_t b_step, u32x4_t (&ra)[NPA],
-                                           u32x4_t (&rb)[NPB]) {
-#pragma unroll
-  for (int q = 0; q < NPA; ++q) ra[q] = ga[q * a_pass + kt * a_step];
-#pragma unroll
-  for (int q = 0; q < NPB; ++q) rb[q] = gb[q * b_pass + kt * b_step];
+// Direct-to-LDS loads of one stage (global_load_lds_dwordx4): instruction i
+// of wave w fills the 1 KB at chunk (w*NI + i)*64 of the tile, lane L
+// writing chunk +L; aoff/boff hold each lane's byte offset of the global
+// chunk that belongs there (swizzle included).  No VGPR holds the data and
+// no LDS store instruction is issued.
+//
+// The instruction is written as inline asm (it has no register result): the
+// compiler treats the builtin form as an LDS store and puts a wait for every
+// outstanding vector-memory operation in front of the next LDS read, which
+// would drain the ring.  The stage waits are therefore explicit
+// (wait_vmcnt), and the asm's memory clobber keeps LDS accesses in order
+// around it.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
 }
 
-template <int NPA, int NPB, typename E>
-__device__ __forceinline__ void store_stage(E* la, E* lb, int arow, int achunk, int rpp, int lda, int brow,
-                                            int bchunk, int brpp, int blds, int epe, const u32x4_t (&ra)[NPA],
-                                            const u32x4_t (&rb)[NPB]) {
+template <int NA, int NB, typename E>
+__device__ __forceinline__ void issue_stage(const E* ga, const E* gb, const uint32_t (&aoff)[NA],
+                                            const uint32_t (&boff)[NB], uint32_t la, uint32_t lb, int wave) {
 #pragma unroll
-  for (int q = 0; q < NPA; ++q) *reinterpret_cast<u32x4_t*>(&la[(arow + q * rpp) * lda + achunk * epe]) = ra[q];
+  for (int i = 0; i < NA; ++i) dma16(ga, aoff[i], la + (wave * NA + i) * 1024);
 #pragma unroll
-  for (int q = 0; q < NPB; ++q) *reinterpret_cast<u32x4_t*>(&lb[(brow + q * brpp) * blds + bchunk * epe]) = rb[q];
+  for (int i = 0; i < NB; ++i) dma16(gb, boff[i], lb + (wave * NB + i) * 1024);
 }
 
-// MFMAs of one BK-deep stage held in LDS (la: K-contiguous A tile; lb: the
-// B tile, K-contiguous or K-major).  The wave owns rows wm*WTM.. and columns
-// wn*WTN.. of the block tile, as NBM x NBN tiles of 32x32.
-template <bool F32, bool KMAJOR_B, int NBM, int NBN, int WTM, int WTN, int BK, int LDA, int LDX, typename E>
+// LDS byte address of a shared-memory pointer.
+template <typename E>
+__device__ __forceinline__ uint32_t lds_addr(const E* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const E*)(p)));
+}
+
+// MFMAs of one BK-deep stage held in LDS (la: K-contiguous A tile, BT rows
+// of BK; lb: the B tile, K-contiguous like A or K-major, BK rows of BT).
+// The wave owns rows wm*WTM.. and columns wn*WTN.. of the block tile, as
+// NBM x NBN tiles of 32x32.
+template <bool F32, bool KMAJOR_B, int NBM, int NBN, int WTM, int WTN, int BK, int BT, typename E>
 __device__ __forceinline__ void mma_stage(const E* la, const E* lb, f32x16_t (&acc)[NBM][NBN], int lane, int wm,
                                           int wn) {
   if constexpr (!F32) {
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       bf16x8_t fa[NBM], fb[NBN];
-      const int kk = ks * 16 + (lane >> 5) * 8;
+      const int kc = ks * 2 + (lane >> 5);           // 16-byte chunk of K (8 bf16)
 #pragma unroll
-      for (int i = 0; i < NBM; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8_t*>(&la[(wm * WTM + i * 32 + (lane & 31)) * LDA + kk]);
+      for (int i = 0; i < NBM; ++i) {
+        const int r = wm * WTM + i * 32 + (lane & 31);
+        fa[i] = *reinterpret_cast<const bf16x8_t*>(&la[r * BK + swz_kc(r, kc) * 8]);
+      }
 #pragma unroll
       for (int j = 0; j < NBN; ++j) {
         if constexpr (!KMAJOR_B) {
-          fb[j] = *reinterpret_cast<const bf16x8_t*>(&lb[(wn * WTN + j * 32 + (lane & 31)) * LDA + kk]);
+          const int r = wn * WTN + j * 32 + (lane & 31);
+          fb[j] = *reinterpret_cast<const bf16x8_t*>(&lb[r * BK + swz_kc(r, kc) * 8]);
         } else {
           // lane group g = lane/16 covers columns 16*(g%2).. and k-half g/2;
           // lane r of the group points at row k + r/4, columns 4*(r%4)..
           const int g = lane >> 4, r = lane & 15;
           const int krow = ks * 16 + 8 * (g >> 1) + (r >> 2);
           const int col = wn * WTN + j * 32 + 16 * (g & 1) + 4 * (r & 3);
-          const bf16x4_t lo = lds_read_tr(&lb[krow * LDX + col]);
-          const bf16x4_t hi = lds_read_tr(&lb[(krow + 4) * LDX + col]);
+          const int cofs = swz_km(krow, col >> 3) * 8 + (col & 7);   // rows krow and krow+4 swizzle alike
+          const bf16x4_t lo = lds_read_tr(&lb[krow * BT + cofs]);
+          const bf16x4_t hi = lds_read_tr(&lb[(krow + 4) * BT + cofs]);
           fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
       }
@@ -145,16 +194,24 @@ __device__ __forceinline__ void mma_stage(const E* la, const E* lb, f32x16_t (&a
 #pragma unroll
     for (int kq = 0; kq < 4; ++kq) {
       f32x4_t fa[NBM], fb[NBN];
+      const int kc = (k0 >> 2) + kq;                 // 16-byte chunk of K (4 floats)
 #pragma unroll
-      for (int i = 0; i < NBM; ++i)
-        fa[i] = *reinterpret_cast<const f32x4_t*>(&la[(wm * WTM + i * 32 + (lane & 31)) * LDA + k0 + kq * 4]);
+      for (int i = 0; i < NBM; ++i) {
+        const int r = wm * WTM + i * 32 + (lane & 31);
+        fa[i] = *reinterpret_cast<const f32x4_t*>(&la[r * BK + swz_kc(r, kc) * 4]);
+      }
 #pragma unroll
       for (int j = 0; j < NBN; ++j) {
         if constexpr (!KMAJOR_B) {
-          fb[j] = *reinterpret_cast<const f32x4_t*>(&lb[(wn * WTN + j * 32 + (lane & 31)) * LDA + k0 + kq * 4]);
+          const int r = wn * WTN + j * 32 + (lane & 31);
+          fb[j] = *reinterpret_cast<const f32x4_t*>(&lb[r * BK + swz_kc(r, kc) * 4]);
         } else {
+          const int col = wn * WTN + j * 32 + (lane & 31);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) fb[j][e] = lb[(k0 + kq * 4 + e) * LDX + wn * WTN + j * 32 + (lane & 31)];
+          for (int e = 0; e < 4; ++e) {
+            const int k = k0 + kq * 4 + e;
+            fb[j][e] = lb[k * BT + swz_km(k, col >> 2) * 4 + (col & 3)];
+          }
         }
       }
 #pragma unroll
@@ -184,7 +241,7 @@ __device__ __forceinline__ void stage_strip(const f32x16_t (&row)[NBN], float* e
 // r of X is K step r), so while a K step whose rows overlap the tile sits in
 // LDS each lane copies out its own row segments: bf16 the hi half (the lo
 // half is not an operand and comes from HBM), float32 all 8 values.
-template <bool F32, int NBM, int RITER, int SEGS, int WTM, int BK, int LDX, typename E>
+template <bool F32, int NBM, int RITER, int SEGS, int WTM, int BK, int BT, typename E>
 __device__ __forceinline__ void capture_master(const E* lbx, int kt, int kt0, int wm, int col0, int lane,
                                                u32x4_t (&pre0)[NBM][RITER], u32x4_t (&pre1)[NBM][RITER]) {
   static_assert(BK % 32 == 0, "32-row strips must not straddle K steps");
@@ -195,9 +252,13 @@ __device__ __forceinline__ void capture_master(const E* lbx, int kt, int kt0, in
 #pragma unroll
       for (int q = 0; q < RITER; ++q) {
         const int sg = lane + 64 * q;
-        const E* src = lbx + (r0 % BK + sg / SEGS) * LDX + col0 + (sg % SEGS) * 8;
-        pre0[pi][q] = *reinterpret_cast<const u32x4_t*>(src);
-        if constexpr (F32) pre1[pi][q] = *reinterpret_cast<const u32x4_t*>(src + 4);
+        const int k = r0 % BK + sg / SEGS, col = col0 + (sg % SEGS) * 8;
+        if constexpr (F32) {
+          pre0[pi][q] = *reinterpret_cast<const u32x4_t*>(&lbx[k * BT + swz_km(k, col >> 2) * 4]);
+          pre1[pi][q] = *reinterpret_cast<const u32x4_t*>(&lbx[k * BT + swz_km(k, (col >> 2) + 1) * 4]);
+        } else {
+          pre0[pi][q] = *reinterpret_cast<const u32x4_t*>(&lbx[k * BT + swz_km(k, col >> 3) * 8]);
+        }
       }
     }
   }
@@ -214,28 +275,22 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   constexpr int WTM = BT / NWM, WTN = BT / NWN;    // wave tile
   constexpr int NBM = WTM / 32, NBN = WTN / 32;    // 32x32 MFMA tiles per wave
   constexpr bool KMAJOR_B = PH == kBX;             // X operand of B X is K-major
-  constexpr int LDA = BK + C::PAD;                 // pitch of K-contiguous tiles
-  constexpr int LDX = BT + C::XPAD;                // pitch of the K-major tile
+  constexpr int NS = C::NS;
   constexpr int EPE = 16 / sizeof(E);              // elements per 16-byte chunk
   constexpr int CPR = BK / EPE;                    // chunks per K-contiguous row
-  constexpr int RPP = NT / CPR;                    // rows per load pass
-  constexpr int NPA = BT / RPP;                    // load passes, K-contiguous tile
   constexpr int CPRX = BT / EPE;                   // chunks per K-major row
-  constexpr int RPPX = NT / CPRX;
-  constexpr int NPX = BK / RPPX;                   // load passes, K-major tile
-  constexpr int NPB = KMAJOR_B ? NPX : NPA;
-  constexpr int A_ELEMS = BT * LDA;
-  constexpr int B_ELEMS = KMAJOR_B ? BK * LDX : BT * LDA;
+  constexpr int T_ELEMS = BT * BK;                 // one operand tile
+  constexpr int T_CH = T_ELEMS / EPE;              // its 16-byte chunks
+  constexpr int NI = T_CH / NT;                    // DMA instructions per lane per tile
+  constexpr int STAGE = 2 * T_ELEMS;               // A tile then B tile
   constexpr int EPP = WTN + 8;                     // epilogue LDS pitch (floats)
-  static_assert(CPR * RPP == NT && NPA * RPP == BT, "tile/thread mismatch");
-  static_assert(CPRX * RPPX == NT && NPX * RPPX == BK, "tile/thread mismatch");
-  static_assert(NWM * NWN * 32 * EPP * 4 <= 2 * (A_ELEMS + B_ELEMS) * static_cast<int>(sizeof(E)),
+  static_assert(NI * NT == T_CH, "tile/thread mismatch");
+  static_assert(CPR == 8 && CPRX == 16, "swizzles assume 8-chunk K rows and 16-chunk K-major rows");
+  static_assert(NWM * NWN * 32 * EPP * 4 <= NS * STAGE * static_cast<int>(sizeof(E)),
                 "epilogue staging must fit in the operand LDS");
 
-  __shared__ __attribute__((aligned(16))) E smem[2 * (A_ELEMS + B_ELEMS)];
+  __shared__ __attribute__((aligned(16))) E smem[NS * STAGE];
   __shared__ float red[4];
-  E* const lds_a = smem;
-  E* const lds_b = smem + 2 * A_ELEMS;
 
   const GemmTask t = tasks[blockIdx.x];
   if (t.unit < 0) return;   // padding of the XCD-interleaved task order
@@ -263,13 +318,29 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
     lda_g = mp; ldb_g = np; K = mp;
   }
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / NWN, wn = wave % NWN;
-  const int arow = tid / CPR, achunk = tid % CPR;                       // K-contiguous loads
-  const int brow = KMAJOR_B ? tid / CPRX : arow;
-  const int bchunk = KMAJOR_B ? tid % CPRX : achunk;
-  constexpr int BRPP = KMAJOR_B ? RPPX : RPP;
-  constexpr int BLDS = KMAJOR_B ? LDX : LDA;
+
+  // each lane's global element offset (within a stage) for its DMA chunks
+  uint32_t aoff[NI], boff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int c = (wave * NI + i) * 64 + lane;       // chunk position in the tile
+    const int ar = c / CPR;
+    aoff[i] = static_cast<uint32_t>((ar * lda_g + swz_kc(ar, c % CPR) * EPE) * sizeof(E));
+    if constexpr (KMAJOR_B) {
+      const int k = c / CPRX;
+      boff[i] = static_cast<uint32_t>((k * ldb_g + swz_km(k, c % CPRX) * EPE) * sizeof(E));
+    } else {
+      boff[i] = static_cast<uint32_t>((ar * ldb_g + swz_kc(ar, c % CPR) * EPE) * sizeof(E));
+    }
+  }
+  const uint32_t ring0 = lds_addr(smem);
+  // advance per K step: along the rows for K-contiguous tiles, down BK rows
+  // for the K-major tile
+  const size_t a_step = BK;
+  const size_t b_step = KMAJOR_B ? static_cast<size_t>(BK) * ldb_g : BK;
 
   f32x16_t acc[NBM][NBN];
 #pragma unroll
@@ -279,15 +350,6 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const gu32x4_t* ga = (const gu32x4_t*)(pa + static_cast<size_t>(arow) * lda_g + achunk * EPE);
-  const gu32x4_t* gb = (const gu32x4_t*)(pb + static_cast<size_t>(brow) * ldb_g + bchunk * EPE);
-  const size_t a_pass = static_cast<size_t>(RPP) * lda_g / EPE;           // 16-byte chunks
-  const size_t b_pass = static_cast<size_t>(BRPP) * ldb_g / EPE;
-  // advance per K step: along the row for K-contiguous tiles, down BK rows
-  // for the K-major tile
-  const size_t a_step = BK / EPE;
-  const size_t b_step = KMAJOR_B ? static_cast<size_t>(BK) * ldb_g / EPE : BK / EPE;
-
   // row segments of the epilogue: per 32-row strip, SEGS segments of 8 per
   // row, RITER per lane
   constexpr int SEGS = WTN / 8;
@@ -295,72 +357,38 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   constexpr int NPRE = KMAJOR_B ? NBM : 1;
   u32x4_t pre0[NPRE][RITER], pre1[NPRE][RITER];
   const int kt0 = ti * BT / BK;                      // K step of the tile's first row
-#define MUON_CAPTURE(LBX, KT)                                                                           \
-  if constexpr (KMAJOR_B)                                                                              \
-    capture_master<F32, NPRE, RITER, SEGS, WTM, BK, LDX>(LBX, KT, kt0, wm, wn * WTN, lane, pre0, pre1);
 
-  // K pipeline.  PF = 2: two register stages in flight -- the loads for step
-  // kt+2 are issued before the MFMAs of step kt and the stage for kt+1 is
-  // stored to LDS after them; the loop is unrolled by two so both register
-  // sets stay static.  PF = 1: one stage in flight (loads for kt+1 issued
-  // before the MFMAs of kt).  There are no branches around memory
-  // operations (prefetch indices are clamped and the tail reloads the final
-  // stage into the idle buffer), so the compiler's wait counts stay exact.
-  // K is a multiple of 2*BK because every NS buffer is padded to at least
-  // the Gram tile, which is 2*BK.
-  static_assert(kTileGramBf16 % (2 * BK) == 0 || F32, "K steps must come in pairs");
+  // K pipeline: a ring of NS stages filled by direct-to-LDS loads.  Step kt
+  // waits for its own stage (the stages issued after it may stay in
+  // flight), passes a barrier (every wave's part of the stage has landed,
+  // and every wave is done with step kt-1, whose buffer is refilled next),
+  // issues stage kt+NS-1 into that buffer and runs the MFMAs of stage kt.
+  // Stage indices past the end are clamped to the last stage (its copy lands
+  // in a buffer nobody reads again), so every step has the same NS-2 newer
+  // stages in flight and a fixed wait count.
   const int KT = K / BK;
-  u32x4_t ra0[NPA], rb0[NPB];
-  load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, 0, a_step, b_step, ra0, rb0);
-  store_stage<NPA, NPB, E>(lds_a, lds_b, arow, achunk, RPP, LDA, brow, bchunk, BRPP, BLDS, EPE, ra0, rb0);
-  if constexpr (C::PF == 2) {
-    u32x4_t ra1[NPA], rb1[NPB];
-    load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, 1, a_step, b_step, ra1, rb1);
-    __syncthreads();
-    // sched_barrier(0) keeps the scheduler from sinking the prefetch below
-    // the MFMAs (which would shrink the prefetch distance to one step).
-    for (int kt = 0; kt < KT; kt += 2) {
-      load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, min(kt + 2, KT - 1), a_step, b_step, ra0, rb0);
-      __builtin_amdgcn_sched_barrier(0);
-      MUON_CAPTURE(lds_b, kt)
-      mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, LDA, LDX>(lds_a, lds_b, acc, lane, wm, wn);
-      __builtin_amdgcn_sched_barrier(0);
-      store_stage<NPA, NPB, E>(lds_a + A_ELEMS, lds_b + B_ELEMS, arow, achunk, RPP, LDA, brow, bchunk, BRPP, BLDS,
-                               EPE, ra1, rb1);
-      __syncthreads();
-      load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, min(kt + 3, KT - 1), a_step, b_step, ra1, rb1);
-      __builtin_amdgcn_sched_barrier(0);
-      MUON_CAPTURE(lds_b + B_ELEMS, kt + 1)
-      mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, LDA, LDX>(lds_a + A_ELEMS, lds_b + B_ELEMS, acc, lane, wm,
-                                                                  wn);
-      __builtin_amdgcn_sched_barrier(0);
-      store_stage<NPA, NPB, E>(lds_a, lds_b, arow, achunk, RPP, LDA, brow, bchunk, BRPP, BLDS, EPE, ra0, rb0);
-      __syncthreads();
-    }
-  } else {
-    __syncthreads();
-    for (int kt = 0; kt < KT; kt += 2) {
-      load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, kt + 1, a_step, b_step, ra0, rb0);
-      __builtin_amdgcn_sched_barrier(0);
-      MUON_CAPTURE(lds_b, kt)
-      mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, LDA, LDX>(lds_a, lds_b, acc, lane, wm, wn);
-      __builtin_amdgcn_sched_barrier(0);
-      store_stage<NPA, NPB, E>(lds_a + A_ELEMS, lds_b + B_ELEMS, arow, achunk, RPP, LDA, brow, bchunk, BRPP, BLDS,
-                               EPE, ra0, rb0);
-      __syncthreads();
-      load_stage<NPA, NPB>(ga, gb, a_pass, b_pass, min(kt + 2, KT - 1), a_step, b_step, ra0, rb0);
-      __builtin_amdgcn_sched_barrier(0);
-      MUON_CAPTURE(lds_b + B_ELEMS, kt + 1)
-      mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, LDA, LDX>(lds_a + A_ELEMS, lds_b + B_ELEMS, acc, lane, wm,
-                                                                  wn);
-      __builtin_amdgcn_sched_barrier(0);
-      store_stage<NPA, NPB, E>(lds_a, lds_b, arow, achunk, RPP, LDA, brow, bchunk, BRPP, BLDS, EPE, ra0, rb0);
-      __syncthreads();
-    }
+  constexpr uint32_t STAGE_B = STAGE * sizeof(E), TILE_B = T_ELEMS * sizeof(E);
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) {
+    const int sc = min(s, KT - 1);
+    issue_stage<NI, NI, E>(pa + sc * a_step, pb + sc * b_step, aoff, boff, ring0 + s * STAGE_B,
+                           ring0 + s * STAGE_B + TILE_B, wave);
   }
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_vmcnt<(NS - 2) * 2 * NI>();
+    ring_barrier();
+    const int nx = min(kt + NS - 1, KT - 1);
+    const uint32_t ls = ring0 + ((kt + NS - 1) % NS) * STAGE_B;
+    issue_stage<NI, NI, E>(pa + nx * a_step, pb + nx * b_step, aoff, boff, ls, ls + TILE_B, wave);
+    const E* cs = smem + (kt % NS) * STAGE;
+    if constexpr (KMAJOR_B)
+      capture_master<F32, NPRE, RITER, SEGS, WTM, BK, BT>(cs + T_ELEMS, kt, kt0, wm, wn * WTN, lane, pre0, pre1);
+    mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, BT>(cs, cs + T_ELEMS, acc, lane, wm, wn);
+  }
+  wait_vmcnt<0>();   // the clamped copies of the last stage
+  __syncthreads();   // the epilogue reuses the ring as staging
 
   // ---------------------------------------------------------------- epilogue
-#undef MUON_CAPTURE
   // B X, bf16: the lo half of the master (the hi half was captured from
   // LDS) is requested before the first LDS round, so one HBM latency is
   // paid per tile, not per strip.
