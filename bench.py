@@ -13,7 +13,6 @@ sample of the same workload.
 """
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -44,19 +43,24 @@ def ns_flops(m, n):
     return {"gram": m * (m + 1) * n, "square": m * m * (m + 1), "bx": 2 * m * m * n}
 
 
-def kernel_source_hash():
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "matrix_aware_optimizer_muon_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(fh.read())
-    return h.hexdigest()[:16]
+def ns_bytes(m, n, es):
+    """Algorithmic HBM bytes of the three NS launches of one iteration for an
+    m x n unit whose NS buffers hold `es`-byte elements (bf16 X as a hi/lo
+    pair, so 2*es per X element; float32 X as one float):
+    Gram reads X (hi) and writes A; the square reads A and writes B; B X
+    reads B, X (hi, the operand) and the master's second half, and writes
+    the next X (hi and lo) -- or, in the last iteration, reads and writes the
+    weight, the same count for bf16 weights."""
+    x2 = 2 * es if es == 2 else es          # bytes of one X master element
+    return {"gram": es * m * n + es * m * m,
+            "square": 2 * es * m * m,
+            "bx": es * m * m + es * m * n + (x2 - es) * m * n + x2 * m * n}
 
 
 def load_traffic(kernel, src_hash):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if
-    they were taken on the current kernel sources."""
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (written by `python -m matrix_aware_optimizer_muon_amd.profiling
+    traffic`), if it was taken on the current kernel sources."""
     p = os.path.join(ROOT, "profiles", "traffic_gpt2s.json")
     try:
         with open(p) as f:
@@ -69,15 +73,16 @@ def load_traffic(kernel, src_hash):
 
 
 def cpu_baseline(wl, hp, budget_s):
-    """The float64 oracle on whole layers of the same workload until the
-    time budget is spent; steps/s scaled from the layers done."""
+    """The float64 oracle on whole layers of the same workload, cycling
+    through the layers until the time budget is spent (at most three passes);
+    steps/s scaled from the layers done."""
     import numpy as np
     from threadpoolctl import threadpool_info
     import synth
     from oracle import muon_oracle as orc
     layers = sorted({t.layer for t in wl.tensors})
     done, spent = 0, 0.0
-    for layer in layers:
+    for layer in layers * 3:
         specs = [t for t in wl.tensors if t.layer == layer]
         inputs = [(orc.bf16_bits_to_f64(synth.weight(wl, s)), orc.bf16_bits_to_f64(synth.gradient(wl, s)),
                    synth.momentum0(wl, s)) for s in specs]
@@ -92,8 +97,9 @@ def cpu_baseline(wl, hp, budget_s):
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     frac = done / len(layers)
     return {"value": frac / spent, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"float64 oracle on {done} of {len(layers)} layers ({6 * done} of {len(wl.tensors)} "
-                      f"matrices) in {spent:.1f} s, scaled to one whole step"}
+            "sample": f"float64 oracle on {done} layer steps ({6 * done} matrix steps; one whole step is "
+                      f"{len(layers)} layers, {len(wl.tensors)} matrices) in {spent:.1f} s, scaled to one "
+                      f"whole step"}
 
 
 def main():
@@ -127,6 +133,7 @@ def main():
     import numpy as np
     import torch
     import matrix_aware_optimizer_muon_amd as mm
+    from matrix_aware_optimizer_muon_amd.profiling import kernel_source_hash
     import synth
 
     dev = torch.device("cuda", 0)
@@ -174,30 +181,45 @@ def main():
     units = []
     for s in wl.tensors:
         h = s.split_rows or s.rows
-        units += [(min(h, s.cols), max(h, s.cols))] * (s.rows // h)
+        m = min(h, s.cols)
+        es = 4 if (s.dtype == "f32" or m < 128) else 2     # NS precision of the unit
+        units += [(m, max(h, s.cols), es)] * (s.rows // h)
     flops = {"gram": 0, "square": 0, "bx": 0}
-    for m, n in units:
+    nbytes = {"gram": 0, "square": 0, "bx": 0}
+    for m, n, es in units:
         for k, v in ns_flops(m, n).items():
             flops[k] += v
+        for k, v in ns_bytes(m, n, es).items():
+            nbytes[k] += v
     elems = sum(s.rows * s.cols for s in wl.tensors)
-    bytes_per_launch = {"momentum": 14 * elems, "update": 8 * elems}
+    nbytes["momentum"] = 14 * elems          # G (bf16) + M read, M + X hi/lo written
+    nbytes["update"] = 8 * elems
     totals = {k: sum(v) / nprof for k, v in per.items()}          # ms per step by kernel kind
     avg = {k: sum(v) / len(v) for k, v in per.items()}             # ms per launch
     ns_ms = sum(totals[k] for k in ("gram", "square", "bx"))
     ns_tflop = hp.ns_steps * sum(flops.values()) / 1e12
     dom = max(totals, key=totals.get)
     src_hash = kernel_source_hash()
-    if dom in flops:
+    # The dominant kernel's roofline bound follows from its algorithmic
+    # intensity: below the bf16 ridge (peak flops / peak bytes) it is HBM.
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    intensity = flops.get(dom, 0) / nbytes[dom]
+    if dom in flops and intensity >= ridge:
         achieved = flops[dom] / (avg[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
     else:
-        achieved = bytes_per_launch[dom] / (avg[dom] * 1e-3) / 1e9
+        achieved = nbytes[dom] / (avg[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = load_traffic(dom, src_hash)
     roof["kernel"] = dom
     roof["avg_launch_ms"] = round(avg[dom], 5)
-    roof["traffic"] = load_traffic(dom, src_hash)
+    roof["algorithmic_bytes"] = nbytes[dom]
+    if dom in flops:
+        roof["algorithmic_flops"] = flops[dom]
+        roof["intensity_flop_per_byte"] = round(intensity, 1)
+        roof["mfma_tflops"] = round(flops[dom] / (avg[dom] * 1e-3) / 1e12, 2)
 
     out = {
         "metric": METRIC,
@@ -222,6 +244,7 @@ def main():
         "wall_s_timed": round(wall, 3),
         "kernel_source_hash": src_hash,
         "roofline": roof,
+        "phase_hbm_gbs": {k: round(nbytes[k] / (avg[k] * 1e-3) / 1e9, 1) for k in avg if k in nbytes},
         "cpu_baseline": None,
     }
     if args.workload != "gpt2s":

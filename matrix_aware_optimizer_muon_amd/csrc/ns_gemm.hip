@@ -19,12 +19,12 @@
 // layout and the MFMA fragments are read with gfx950's transposing LDS read
 // (ds_read_b64_tr_b16), so no transposed copy of X is ever stored.
 //
-// bf16 path: 128x128 output tile (4 waves of 64x64, or 8 waves of 64x32
-// for B X) of v_mfma_f32_32x32x16_bf16, K staged through LDS 64 deep in a
-// two-stage ring filled by direct-to-LDS loads (global_load_lds_dwordx4:
-// no VGPR staging, no LDS store instructions); two blocks fit per CU
-// (64 KB LDS each) so one block's epilogue overlaps the other's MFMA loop.  X is held as a
-// bf16 hi/lo pair so the a*X term keeps ~16 significant bits while the MFMA
+// bf16 path: 128x128 output tile, 8 waves of 64x32 (2x1 blocks of
+// v_mfma_f32_32x32x16_bf16), K staged through LDS 64 deep in a two-stage
+// ring filled by direct-to-LDS loads (global_load_lds_dwordx4: no VGPR
+// staging, no LDS store instructions); two blocks fit per CU (64 KB LDS
+// each) so one block's epilogue overlaps the other's MFMA loop.  X is held
+// as a bf16 hi/lo pair so the a*X term keeps ~16 significant bits while the MFMA
 // operand is the hi part.
 // fp32 path: 64x64 tile, 4 waves of 32x32, v_mfma_f32_32x32x2f32.
 #include "device_common.h"
@@ -55,7 +55,7 @@ typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;       // LDS
 #endif
 template <bool F32, int PH> struct Cfg;
 #ifndef MUON_G_NWN
-#define MUON_G_NWN 2
+#define MUON_G_NWN 4
 #endif
 template <int PH> struct Cfg<false, PH> {        // bf16, Gram and square
   using E = uint16_t;

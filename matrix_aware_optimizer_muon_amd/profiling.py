@@ -1,0 +1,181 @@
+"""Summaries of rocprofv3 output for the Muon step kernels.
+
+    python -m matrix_aware_optimizer_muon_amd.profiling trace DIR [--title T] [--command C]
+        Markdown table of a `rocprofv3 --kernel-trace --stats --output-format csv`
+        run (per-kernel calls, total and average duration, grid, LDS bytes).
+
+    python -m matrix_aware_optimizer_muon_amd.profiling traffic \
+        --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --copy-bytes N \
+        [--out JSON] [--command C ...]
+        HBM bytes per launch from two `rocprofv3 --pmc` passes (FETCH_SIZE, then
+        WRITE_SIZE; KiB per dispatch), each scaled by what the same counter
+        reads for device-to-device copies of a known size, as JSON.
+
+Kernels are named by phase: gram (A = s X X^T), square (B = bA + cA^2),
+bx (X <- s(aX + BX), weight update in the last iteration), momentum, update,
+and the Newton-Muon kernels by their own names.
+"""
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+
+
+def kernel_source_hash():
+    """Hash of the kernel sources (csrc/*.hip, *.h, *.cpp): counter figures
+    are only valid for the sources they were taken on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(PKG, "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_kind(name):
+    m = re.search(r"ns_gemm_kernel<(\w+), (\d)>", name) or re.search(r"ns_gemm_kernelILb(\d)ELi(\d)E", name)
+    if m:
+        f32 = m.group(1) in ("true", "1")
+        return ["gram", "square", "bx"][int(m.group(2))] + ("/f32" if f32 else "")
+    for k, v in (("momentum_kernel", "momentum"), ("update_kernel", "update"), ("copyBuffer", "copy"),
+                 ("fillBuffer", "fill")):
+        if k in name:
+            m2 = re.search(r"<(\w+)>", name) or re.search(r"ILb(\d)E", name)
+            f32 = bool(m2) and m2.group(1) in ("true", "1")
+            return v + ("/f32" if f32 and v in ("momentum", "update") else "")
+    m = re.search(r"(\w+_kernel)", name)
+    return m.group(1) if m else name[:40]
+
+
+def _one(dirpath, pattern):
+    hits = sorted(glob.glob(os.path.join(dirpath, "**", pattern), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no {pattern} under {dirpath}")
+    return hits[0]
+
+
+def _num(row, *keys, default=0.0):
+    for k in keys:
+        if k in row and row[k] not in ("", None):
+            return float(row[k])
+    return default
+
+
+def trace_table(dirpath):
+    """Per-kernel rows from the kernel-trace CSV: calls, total/avg µs, grid
+    workgroups, LDS bytes."""
+    path = _one(dirpath, "*kernel_trace.csv")
+    rows = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r.get("Kernel_Name", "")
+            kind = kernel_kind(name)
+            dur = (_num(r, "End_Timestamp") - _num(r, "Start_Timestamp")) / 1e3
+            wg = _num(r, "Workgroup_Size_X", "Workgroup_Size", default=1.0) or 1.0
+            grid = _num(r, "Grid_Size_X", "Grid_Size", default=0.0)
+            e = rows.setdefault(kind, {"calls": 0, "total_us": 0.0, "grid": int(grid // wg),
+                                       "lds": int(_num(r, "Group_Segment_Size", "LDS_Block_Size"))})
+            e["calls"] += 1
+            e["total_us"] += dur
+    tot = sum(e["total_us"] for e in rows.values()) or 1.0
+    for e in rows.values():
+        e["avg_us"] = e["total_us"] / e["calls"]
+        e["pct"] = 100.0 * e["total_us"] / tot
+    return rows
+
+
+def trace_markdown(dirpath, title, command):
+    rows = trace_table(dirpath)
+    out = [f"# {title}", "", "Commands (repository root on one MI355X, `libmuon.so` built):", "", "```",
+           command.strip(), "```", "",
+           "| kernel | calls | total µs | avg µs | % | grid (workgroups) | LDS B |",
+           "|---|---:|---:|---:|---:|---:|---:|"]
+    for k, e in sorted(rows.items(), key=lambda kv: -kv[1]["total_us"]):
+        out.append(f"| {k} | {e['calls']} | {e['total_us']:.1f} | {e['avg_us']:.2f} | {e['pct']:.1f} | "
+                   f"{e['grid']} | {e['lds']} |")
+    return "\n".join(out) + "\n"
+
+
+def counter_per_dispatch(dirpath, counter):
+    """Mean value of `counter` per dispatch, by kernel kind (values of the
+    same dispatch are summed over the counter's instances)."""
+    path = _one(dirpath, "*counter_collection.csv")
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") != counter:
+                continue
+            kind = kernel_kind(r.get("Kernel_Name", ""))
+            d = per.setdefault(kind, {})
+            key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            d[key] = d.get(key, 0.0) + float(r["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in per.items()}
+
+
+def traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes, commands):
+    fetch = counter_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = counter_per_dispatch(write_dir, "WRITE_SIZE")
+    cf = counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE").get("copy")
+    cw = counter_per_dispatch(copy_write_dir, "WRITE_SIZE").get("copy")
+    if not cf or not cw:
+        raise RuntimeError("no copy kernel in the calibration runs")
+    # a copy of N bytes reads N and writes N; KiB per dispatch -> bytes
+    f_scale = copy_bytes / (cf * 1024.0)
+    w_scale = copy_bytes / (cw * 1024.0)
+    per = {}
+    for k in sorted(set(fetch) | set(write)):
+        if k in ("copy", "fill"):
+            continue
+        rd = fetch.get(k, 0.0) * 1024.0 * f_scale
+        wr = write.get(k, 0.0) * 1024.0 * w_scale
+        per[k] = int(round(rd + wr))
+    return {
+        "kernel_source_hash": kernel_source_hash(),
+        "per_launch_bytes": per,
+        "per_launch_read_bytes": {k: int(round(fetch.get(k, 0.0) * 1024.0 * f_scale)) for k in per},
+        "per_launch_write_bytes": {k: int(round(write.get(k, 0.0) * 1024.0 * w_scale)) for k in per},
+        "raw_kib_per_dispatch": {"FETCH_SIZE": fetch, "WRITE_SIZE": write},
+        "calibration": {"copy_bytes": copy_bytes, "copy_FETCH_SIZE_kib": cf, "copy_WRITE_SIZE_kib": cw,
+                        "fetch_scale": f_scale, "write_scale": w_scale},
+        "commands": commands,
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(prog="python -m matrix_aware_optimizer_muon_amd.profiling")
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("dir")
+    t.add_argument("--title", default="Kernel trace")
+    t.add_argument("--command", default="")
+    t.add_argument("--out")
+    c = sub.add_parser("traffic")
+    for a in ("--fetch", "--write", "--copy-fetch", "--copy-write"):
+        c.add_argument(a, required=True)
+    c.add_argument("--copy-bytes", type=int, required=True)
+    c.add_argument("--command", action="append", default=[])
+    c.add_argument("--out")
+    args = ap.parse_args(argv)
+    if args.cmd == "trace":
+        text = trace_markdown(args.dir, args.title, args.command)
+    else:
+        text = json.dumps(traffic(args.fetch, args.write, args.copy_fetch, args.copy_write, args.copy_bytes,
+                                  args.command), indent=1) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    else:
+        sys.stdout.write(text)
+
+
+if __name__ == "__main__":
+    main()
