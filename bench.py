@@ -45,16 +45,17 @@ def ns_flops(m, n):
 
 def ns_bytes(m, n, es):
     """Algorithmic HBM bytes of the three NS launches of one iteration for an
-    m x n unit whose NS buffers hold `es`-byte elements (bf16 X as a hi/lo
-    pair, so 2*es per X element; float32 X as one float):
+    m x n unit whose NS buffers hold `es`-byte elements (bf16: X master =
+    bf16 hi + one int8 correction, 3 bytes; float32: X is one float):
     Gram reads X (hi) and writes A; the square reads A and writes B; B X
-    reads B, X (hi, the operand) and the master's second half, and writes
-    the next X (hi and lo) -- or, in the last iteration, reads and writes the
-    weight, the same count for bf16 weights."""
-    x2 = 2 * es if es == 2 else es          # bytes of one X master element
+    reads B, X (hi, the operand) and the master's correction, and writes the
+    next X (hi and correction) -- or, in the last iteration, reads and writes
+    the weight (4 bytes per element for bf16 weights, one more than the
+    master it replaces)."""
+    xm = es + 1 if es == 2 else es          # bytes of one X master element
     return {"gram": es * m * n + es * m * m,
             "square": 2 * es * m * m,
-            "bx": es * m * m + es * m * n + (x2 - es) * m * n + x2 * m * n}
+            "bx": es * m * m + es * m * n + (xm - es) * m * n + xm * m * n}
 
 
 def load_traffic(kernel, src_hash):
@@ -192,7 +193,7 @@ def main():
         for k, v in ns_bytes(m, n, es).items():
             nbytes[k] += v
     elems = sum(s.rows * s.cols for s in wl.tensors)
-    nbytes["momentum"] = 14 * elems          # G (bf16) + M read, M + X hi/lo written
+    nbytes["momentum"] = 13 * elems          # G (bf16) + M read, M + X master (hi, int8) written
     nbytes["update"] = 8 * elems
     totals = {k: sum(v) / nprof for k, v in per.items()}          # ms per step by kernel kind
     avg = {k: sum(v) / len(v) for k, v in per.items()}             # ms per launch

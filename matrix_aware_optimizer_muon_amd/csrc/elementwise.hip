@@ -2,8 +2,8 @@
 //
 //   momentum_kernel  M' = mu M + (1-mu) G, the Nesterov look-ahead U, one
 //                    partial sum of U^2 per tile (for the Frobenius
-//                    normalisation), and U written into the NS workspace as a
-//                    bf16 hi/lo pair (or float32) in the canonical
+//                    normalisation), and U written into the NS workspace as
+//                    the two-part X master (or float32) in the canonical
 //                    short-side-first orientation.
 //                    (Muon README, "Hyperparameter tuning"; Muon blog by
 //                    Venkatramana, section 3: X = G / ||G||_F.)
@@ -24,22 +24,20 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Store one 8-element row segment of an NS buffer: bf16 hi (and lo if
-// `lo` is set) or float32.
+// Store one 8-element row segment of the X master: bf16 hi and its int8
+// correction (element offsets are shared, the correction array holds one
+// byte per element), or float32.
 template <bool F32>
 __device__ __forceinline__ void store_seg(void* hi, void* lo, int64_t ld, int r, int c, const float* v) {
   const size_t off = static_cast<size_t>(r) * ld + c;
   if constexpr (F32) {
     st8_f32(hi, off, v);
   } else {
-    float h[8], l[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      h[e] = bf16_to_f32(f32_to_bf16(v[e]));
-      l[e] = v[e] - h[e];
-    }
-    st8_bf16(hi, off, h);
-    if (lo) st8_bf16(lo, off, l);
+    u32x4_t h;
+    u32x2_t q;
+    master_encode8(v, h, q);
+    gst(static_cast<uint16_t*>(hi) + off, h);
+    gst(static_cast<int8_t*>(lo) + off, q);
   }
 }
 
@@ -130,11 +128,8 @@ __device__ __forceinline__ void load_master_seg(const UnitDev& u, int r, int c, 
   if constexpr (F32) {
     ld8_f32(u.xh[0], off, v);
   } else {
-    float l[8];
-    ld8_bf16(u.xh[0], off, v);
-    ld8_bf16(u.xl, off, l);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] += l[e];
+    master_decode8(gld<u32x4_t>(static_cast<const uint16_t*>(u.xh[0]) + off),
+                   gld<u32x2_t>(static_cast<const int8_t*>(u.xl) + off), v);
   }
 }
 

@@ -310,7 +310,7 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
     const size_t xs = size_t(u.mp) * u.np * es, as = size_t(u.mp) * u.mp * es;
     u.off_xh0 = off; off = align_up(off + xs);
     u.off_xh1 = off; off = align_up(off + xs);
-    if (!u.f32) { u.off_xl = off; off = align_up(off + xs); }
+    if (!u.f32) { u.off_xl = off; off = align_up(off + size_t(u.mp) * u.np); }   // int8 master corrections
     u.off_a = off; off = align_up(off + as);
     u.off_b = off; off = align_up(off + as);
   }

@@ -355,7 +355,8 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   constexpr int SEGS = WTN / 8;
   constexpr int RITER = 32 * SEGS / 64;
   constexpr int NPRE = KMAJOR_B ? NBM : 1;
-  u32x4_t pre0[NPRE][RITER], pre1[NPRE][RITER];
+  u32x4_t pre0[NPRE][RITER], pre1[NPRE][RITER];     // master: hi (bf16) / first..last 4 (float32)
+  u32x2_t preq[NPRE][RITER];                          // master: int8 corrections (bf16)
   const int kt0 = ti * BT / BK;                      // K step of the tile's first row
 
   // K pipeline: a ring of NS stages filled by direct-to-LDS loads.  Step kt
@@ -401,7 +402,7 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
       for (int q = 0; q < RITER; ++q) {
         const int sg = lane + 64 * q;
         const size_t off = static_cast<size_t>(row_base + pi * 32 + sg / SEGS) * np + col_base + (sg % SEGS) * 8;
-        pre1[pi][q] = gld<u32x4_t>(static_cast<const E*>(u.xl) + off);
+        preq[pi][q] = gld<u32x2_t>(static_cast<const int8_t*>(u.xl) + off);
       }
   }
 
@@ -462,11 +463,7 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
             xm[4 + e] = __uint_as_float(pre1[pi][q][e]);
           }
         } else {
-          float xl[8];
-          unpack8_bf16(pre0[pi][q], xm);
-          unpack8_bf16(pre1[pi][q], xl);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) xm[e] += xl[e];
+          master_decode8(pre0[pi][q], preq[pi][q], xm);
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = scale * fmaf(p.a, xm[e], v[e]);
@@ -474,14 +471,11 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
           if constexpr (F32) {
             st8<true>(u.xh[p.x_in ^ 1], off, v);
           } else {
-            float hi[8], lo[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              hi[e] = bf16_to_f32(f32_to_bf16(v[e]));
-              lo[e] = v[e] - hi[e];
-            }
-            st8<false>(u.xh[p.x_in ^ 1], off, hi);
-            st8<false>(u.xl, off, lo);
+            u32x4_t hq;
+            u32x2_t lq;
+            master_encode8(v, hq, lq);
+            gst(static_cast<uint16_t*>(u.xh[p.x_in ^ 1]) + off, hq);
+            gst(static_cast<int8_t*>(u.xl) + off, lq);
           }
         } else if (u.side == kLeft) {
           if (gr < u.rows) update_w8(u, gr, gc, v, decay, step);

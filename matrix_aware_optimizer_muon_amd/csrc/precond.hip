@@ -420,7 +420,6 @@ void apply_kernel(const PrecondDev* __restrict__ pds, const ApplyTask* __restric
           if (pd.grad_f32) {
             v = gld<f32x4_t>(static_cast<const float*>(pd.grad) + off);
           } else {
-            typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
             const u32x2_t w = gld<u32x2_t>(static_cast<const uint16_t*>(pd.grad) + off);
             v[0] = __uint_as_float(w[0] << 16); v[1] = __uint_as_float(w[0] & 0xffff0000u);
             v[2] = __uint_as_float(w[1] << 16); v[3] = __uint_as_float(w[1] & 0xffff0000u);

@@ -194,11 +194,12 @@ def test_plan_split_rows_and_fp32():
 
 
 def test_workspace_size_formula():
-    # bf16 unit: two X hi buffers and X lo (m_p x n_p bf16 each) + A, B (m_p^2 bf16)
+    # bf16 unit: two X hi buffers (m_p x n_p bf16 each), the int8 master
+    # corrections (m_p x n_p bytes) + A, B (m_p^2 bf16)
     ts = fakes([(768, 3072)])
     need = ws_status(ts)[1]
     plan = mm.plan_describe(ts, mm.default_hparams())
-    per_unit = 3 * 768 * 3072 * 2 + 2 * 768 * 768 * 2
+    per_unit = 2 * 768 * 3072 * 2 + 768 * 3072 + 2 * 768 * 768 * 2
     assert need - plan["meta_bytes"] == per_unit
     # ns_steps does not change the footprint
     assert ws_status(ts, mm.default_hparams(ns_steps=1))[1] == need
