@@ -43,19 +43,19 @@ def ns_flops(m, n):
     return {"gram": m * (m + 1) * n, "square": m * m * (m + 1), "bx": 2 * m * m * n}
 
 
-def ns_bytes(m, n, es):
-    """Algorithmic HBM bytes of the three NS launches of one iteration for an
-    m x n unit whose NS buffers hold `es`-byte elements (bf16: X master =
-    bf16 hi + one int8 correction, 3 bytes; float32: X is one float):
-    Gram reads X (hi) and writes A; the square reads A and writes B; B X
-    reads B, X (hi, the operand) and the master's correction, and writes the
-    next X (hi and correction) -- or, in the last iteration, reads and writes
-    the weight (4 bytes per element for bf16 weights, one more than the
-    master it replaces)."""
+def ns_bytes(m, n, es, w_es, ns_steps):
+    """Algorithmic HBM bytes per launch of the three NS phases (averaged over
+    the ns_steps iterations of a step) for an m x n unit whose NS buffers
+    hold `es`-byte elements (bf16: the X master is bf16 hi + one int8
+    correction, 3 bytes; float32: X is one float) and whose weight has
+    `w_es`-byte elements.  Gram reads X (hi) and writes A; the square reads
+    A and writes B; B X reads B, X (hi, the operand) and the master's
+    correction, and writes the next X master -- except in the last
+    iteration, which reads and writes the weight instead."""
     xm = es + 1 if es == 2 else es          # bytes of one X master element
-    return {"gram": es * m * n + es * m * m,
-            "square": 2 * es * m * m,
-            "bx": es * m * m + es * m * n + (xm - es) * m * n + xm * m * n}
+    bx_in = es * m * m + es * m * n + (xm - es) * m * n
+    bx = ((ns_steps - 1) * (bx_in + xm * m * n) + (bx_in + 2 * w_es * m * n)) / ns_steps
+    return {"gram": es * m * n + es * m * m, "square": 2 * es * m * m, "bx": bx}
 
 
 def load_traffic(kernel, src_hash):
@@ -184,13 +184,14 @@ def main():
         h = s.split_rows or s.rows
         m = min(h, s.cols)
         es = 4 if (s.dtype == "f32" or m < 128) else 2     # NS precision of the unit
-        units += [(m, max(h, s.cols), es)] * (s.rows // h)
+        w_es = 4 if s.dtype == "f32" else 2
+        units += [(m, max(h, s.cols), es, w_es)] * (s.rows // h)
     flops = {"gram": 0, "square": 0, "bx": 0}
     nbytes = {"gram": 0, "square": 0, "bx": 0}
-    for m, n, es in units:
+    for m, n, es, w_es in units:
         for k, v in ns_flops(m, n).items():
             flops[k] += v
-        for k, v in ns_bytes(m, n, es).items():
+        for k, v in ns_bytes(m, n, es, w_es, max(1, hp.ns_steps)).items():
             nbytes[k] += v
     elems = sum(s.rows * s.cols for s in wl.tensors)
     nbytes["momentum"] = 13 * elems          # G (bf16) + M read, M + X master (hi, int8) written
@@ -216,7 +217,7 @@ def main():
     roof["traffic"] = load_traffic(dom, src_hash)
     roof["kernel"] = dom
     roof["avg_launch_ms"] = round(avg[dom], 5)
-    roof["algorithmic_bytes"] = nbytes[dom]
+    roof["algorithmic_bytes"] = int(nbytes[dom])
     if dom in flops:
         roof["algorithmic_flops"] = flops[dom]
         roof["intensity_flop_per_byte"] = round(intensity, 1)
