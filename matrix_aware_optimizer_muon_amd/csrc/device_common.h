@@ -56,17 +56,9 @@ __device__ __forceinline__ void unpack8_bf16(const u32x4_t& w, float* v) {
 // operand) and an int8 correction q with x ~= hi + q * ulp(hi)/256, i.e. 15
 // more bits below hi's last one (|x - hi| <= ulp(hi)/2, so |q| <= 128, kept
 // in [-127, 127]).  For bf16 exponent field E the step ulp(hi)/256 is
-// 2^(E-142); values with E < 16 (|x| < 2^-111) keep hi only.  hi + q*step
-// has at most 16 significant bits, so the float32 sum is exact.
-__device__ __forceinline__ float master_step(uint32_t hi_bits) {
-  const uint32_t e = (hi_bits >> 7) & 0xFFu;
-  return e >= 16u ? __uint_as_float((e - 15u) << 23) : 0.f;
-}
-// 1 / master_step (2^(142-E)); 0 where the step is 0.
-__device__ __forceinline__ float master_inv_step(uint32_t hi_bits) {
-  const uint32_t e = (hi_bits >> 7) & 0xFFu;
-  return e >= 16u ? __uint_as_float((269u - e) << 23) : 0.f;
-}
+// 2^(E-142) (ldexp underflows gracefully for tiny hi); hi + q*step has at
+// most 16 significant bits, so the float32 sum is exact.
+__device__ __forceinline__ int master_exp(uint32_t hi_bits) { return static_cast<int>((hi_bits >> 7) & 0xFFu); }
 
 // hi (bf16 bits) and q of 8 values; q packed little-endian into 2 words.
 __device__ __forceinline__ void master_encode8(const float* v, u32x4_t& hi, u32x2_t& lo) {
@@ -74,9 +66,8 @@ __device__ __forceinline__ void master_encode8(const float* v, u32x4_t& hi, u32x
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const uint16_t h = f32_to_bf16(v[e]);
-    const float r = (v[e] - bf16_to_f32(h)) * master_inv_step(h);   // exact: a power-of-2 scale
-    const int qi = static_cast<int>(rintf(fminf(fmaxf(r, -127.f), 127.f)));
-    q[e] = static_cast<uint32_t>(qi) & 0xFFu;
+    const float r = ldexpf(v[e] - bf16_to_f32(h), 142 - master_exp(h));   // exact: a power-of-2 scale
+    q[e] = static_cast<uint32_t>(static_cast<int>(rintf(__builtin_amdgcn_fmed3f(r, -127.f, 127.f)))) & 0xFFu;
     if (e & 1) hi[e >> 1] |= static_cast<uint32_t>(h) << 16; else hi[e >> 1] = h;
   }
   lo[0] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
@@ -88,7 +79,7 @@ __device__ __forceinline__ void master_decode8(const u32x4_t& hi, const u32x2_t&
   for (int e = 0; e < 8; ++e) {
     const uint32_t h = (e & 1) ? (hi[e >> 1] >> 16) : (hi[e >> 1] & 0xFFFFu);
     const int q = static_cast<int8_t>((lo[e >> 2] >> (8 * (e & 3))) & 0xFFu);
-    v[e] = fmaf(static_cast<float>(q), master_step(h), __uint_as_float(h << 16));
+    v[e] = ldexpf(static_cast<float>(q), master_exp(h) - 142) + __uint_as_float(h << 16);
   }
 }
 
