@@ -33,6 +33,8 @@ WORKLOAD_TEXT = {
     "square": "square: one 4096x4096 bf16 matrix, rank-32 + noise gradient; " + STEP_TEXT,
     "gpt2xl": "gpt2xl: GPT-2-XL hidden weights, 48 layers x {Q,K,V,O 1600x1600, MLP-up 6400x1600, "
               "MLP-down 1600x6400} = 288 bf16 matrices; " + STEP_TEXT,
+    "conv": "conv: 3x3 convolution filters of a CIFAR-10-style network as out x (in*9) matrices, 6 bf16 "
+            "filters (64x288, 64x576, 256x576, 3 x 256x2304); " + STEP_TEXT,
     "tiny": "tiny: one 256x512 fp32 matrix; " + STEP_TEXT,
 }
 
@@ -110,7 +112,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="gpt2s", choices=["gpt2s", "square", "gpt2xl", "tiny"],
+    ap.add_argument("--workload", default="gpt2s", choices=["gpt2s", "square", "gpt2xl", "conv", "tiny"],
                     help="weight set to step (the headline metric is quoted on gpt2s)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 3 device-to-device copies of BYTES each (HBM counter calibration)")

@@ -172,11 +172,28 @@ def _torch():
     return torch
 
 
+def _as_matrix(t):
+    """A >= 2-D tensor as the row-major matrix (shape[0], prod(shape[1:])):
+    a convolution filter (out, in, kh, kw) becomes out x (in*kh*kw), the 2-D
+    view Muon orthogonalises.  The trailing dimensions must be contiguous."""
+    if t.dim() == 2:
+        return t
+    if t.dim() < 2:
+        raise ValueError("Muon tensors must have at least 2 dimensions")
+    inner = t[0].numel() if t.shape[0] > 0 else 0
+    if not t[0].is_contiguous() or (t.shape[0] > 1 and t.stride(0) < inner):
+        raise ValueError("the trailing dimensions of a filter must be contiguous")
+    return t.as_strided((t.shape[0], inner), (t.stride(0), 1))
+
+
 def tensor_desc(param, grad, momentum, *, split_rows=0, precond=-1, lr_mult=1.0,
                 update_out=None) -> MuonTensor:
     torch = _torch()
-    if param.dim() != 2 or grad.shape != param.shape or momentum.shape != param.shape:
-        raise ValueError("param, grad and momentum must be 2-D with one shape")
+    if grad.shape != param.shape or momentum.shape != param.shape:
+        raise ValueError("param, grad and momentum must share one shape")
+    param, grad, momentum = _as_matrix(param), _as_matrix(grad), _as_matrix(momentum)
+    if update_out is not None:
+        update_out = _as_matrix(update_out)
     for t in (param, grad, momentum):
         if t.stride(1) != 1:
             raise ValueError("tensors must be row-major (unit column stride)")

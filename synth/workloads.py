@@ -28,7 +28,7 @@ import numpy as np
 F32 = "f32"
 BF16 = "bf16"
 
-_WL_ID = {"tiny": 1, "square": 2, "gpt2s": 3, "gpt2xl": 4, "nmuon": 5}
+_WL_ID = {"tiny": 1, "square": 2, "gpt2s": 3, "gpt2xl": 4, "nmuon": 5, "conv": 6}
 _KIND_ID = {"grad": 1, "mom": 2, "weight": 3, "acts": 4, "scale": 5,
             "gfac": 6, "gnoise": 7, "sigma": 8}
 
@@ -117,6 +117,15 @@ def workload(name: str, layers: Optional[int] = None) -> Workload:
         ts = [t for l in range(n) for t in _gpt2_layer(l, 6 * l, 1600, BF16)]
         return Workload("gpt2xl", ts, grad_law="lowrank", grad_rank=64,
                         noise_std=1e-3)
+    if name == "conv":
+        # convolution filters of a small CIFAR-10-style network as the 2-D
+        # views Muon orthogonalises, out x (in*kh*kw): three blocks of two
+        # 3x3 convolutions (widths 64, 256, 256); the first (input) layer is
+        # left to the auxiliary optimiser and is not part of the set
+        shapes = [(64, 32 * 9), (64, 64 * 9), (256, 64 * 9), (256, 256 * 9), (256, 256 * 9),
+                  (256, 256 * 9)]
+        ts = [TensorSpec(f"conv{i}", i, i, r, c, BF16) for i, (r, c) in enumerate(shapes)]
+        return Workload("conv", ts, grad_law="gauss_scaled", grad_std=1e-2)
     if name == "nmuon":
         d = 768
         ts = [TensorSpec("qkv", 0, 0, 3 * d, d, BF16, split_rows=d, precond=0),
@@ -129,7 +138,7 @@ def workload(name: str, layers: Optional[int] = None) -> Workload:
     raise KeyError(name)
 
 
-WORKLOADS = ("tiny", "square", "gpt2s", "gpt2xl", "nmuon")
+WORKLOADS = ("tiny", "square", "gpt2s", "gpt2xl", "conv", "nmuon")
 
 
 def _store(x: np.ndarray, dtype: str) -> np.ndarray:

@@ -227,3 +227,25 @@ def test_plan_newton_muon_layer():
     bad = ts[3]
     bad.precond = 0
     assert ws_status([bad], preconds=pcs)[0] == "MUON_ERR_BAD_SHAPE"
+
+
+def test_filter_tensors_become_matrices():
+    # a (out, in, kh, kw) convolution filter is described as out x (in*kh*kw)
+    torch = pytest.importorskip("torch")
+    w = torch.zeros(8, 4, 3, 3, dtype=torch.bfloat16)
+    g = torch.zeros_like(w)
+    m = torch.zeros(8, 4, 3, 3, dtype=torch.float32)
+    d = mm.tensor_desc(w, g, m)
+    assert (d.rows, d.cols, d.ld_param, d.ld_momentum) == (8, 36, 36, 36)
+    # a filter whose trailing dimensions are not contiguous is refused
+    wt = w.permute(0, 2, 3, 1)
+    with pytest.raises(ValueError):
+        mm.tensor_desc(wt, wt, m.permute(0, 2, 3, 1))
+    with pytest.raises(ValueError):
+        mm.tensor_desc(w[:, :, 0, 0].reshape(-1), g[:, :, 0, 0].reshape(-1), m[:, :, 0, 0].reshape(-1))
+    # the conv workload plans one float32 group (m = 64) and one bf16 group (m = 256)
+    wl = synth.workload("conv")
+    ts = fakes([(s.rows, s.cols) for s in wl.tensors])
+    plan = mm.plan_describe(ts, mm.default_hparams())
+    assert sorted(u["m"] for u in plan["units"]) == [64, 64, 256, 256, 256, 256]
+    assert [g["units"] for g in plan["groups"]] == [4, 2]

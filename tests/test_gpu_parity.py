@@ -42,16 +42,20 @@ class Case:
         self.dM = [torch.from_numpy(m.copy()).cuda() for m in self.M]
         self.dO = [torch.empty(s.rows, s.cols, dtype=torch.float32, device="cuda") for s in specs]
 
-    def descs(self, lr_mults=None):
+    def descs(self, lr_mults=None, filters=False):
         out = []
         for k, s in enumerate(self.specs):
-            out.append(mm.tensor_desc(self.dW[k], self.dG[k], self.dM[k], split_rows=s.split_rows,
+            ts = (self.dW[k], self.dG[k], self.dM[k], self.dO[k])
+            if filters:
+                # the same storage as 4-D 3x3 convolution filters (out, in, 3, 3)
+                ts = tuple(t.view(s.rows, s.cols // 9, 3, 3) for t in ts)
+            out.append(mm.tensor_desc(ts[0], ts[1], ts[2], split_rows=s.split_rows,
                                       lr_mult=1.0 if lr_mults is None else lr_mults[k],
-                                      update_out=self.dO[k]))
+                                      update_out=ts[3]))
         return out
 
-    def run(self, hp, lr=-1.0, lr_mults=None):
-        st = mm.MuonStep(self.descs(lr_mults), hp)
+    def run(self, hp, lr=-1.0, lr_mults=None, filters=False):
+        st = mm.MuonStep(self.descs(lr_mults, filters), hp)
         st.step(lr)
         torch.cuda.synchronize()
         flags = st.flags()
@@ -182,6 +186,19 @@ def test_gpt2_small_full_grouped_step():
         assert rel_f(c.dM[k].cpu().numpy(), Mref) <= TOL_M
     sample = [k for k, s in enumerate(c.specs) if s.layer in (0, 11)]
     w = check(c, hp, idx=sample, label="gpt2s sampled layers 0,11")
+    assert w["O"] < 2e-2
+
+
+def test_conv_filters_as_4d_tensors():
+    # convolution filters handed over as (out, in, 3, 3) tensors: Muon works
+    # on their out x (in*9) views; m = 64 filters run the float32 path, m =
+    # 256 the bf16 path
+    say("case: conv filter set, 4-D tensors")
+    wl = synth.workload("conv")
+    c = Case(wl, wl.tensors)
+    hp = mm.default_hparams()
+    assert c.run(hp, filters=True) == 0
+    w = check(c, hp, label="conv filters")
     assert w["O"] < 2e-2
 
 

@@ -47,3 +47,17 @@ def test_lowrank_spectrum_decays():
     g = synth.bf16_bits_to_f32(synth.gradient(w, t)).astype(np.float64)
     s = np.linalg.svd(g, compute_uv=False)
     assert s[0] > 5 * s[8] and s[40] < 0.1   # rank-32 decaying part, then the 1e-3 noise bulk
+
+
+def test_every_workload_generates():
+    # one tensor of each workload draws its inputs (seed ids cover every name)
+    for name in wl_mod.WORKLOADS:
+        w = synth.workload(name, layers=1) if name in ("gpt2s", "gpt2xl") else synth.workload(name)
+        t = min(w.tensors, key=lambda s: s.rows * s.cols)
+        g = synth.gradient(w, t)
+        assert g.shape == (t.rows, t.cols)
+        assert synth.weight(w, t).shape == (t.rows, t.cols)
+        assert synth.momentum0(w, t).shape == (t.rows, t.cols)
+    c = synth.workload("conv")
+    assert [(t.rows, t.cols) for t in c.tensors] == [(64, 288), (64, 576), (256, 576), (256, 2304),
+                                                      (256, 2304), (256, 2304)]
