@@ -406,10 +406,11 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
       }
   }
 
-  // Each wave stages one 32-row strip of its accumulators in LDS, then
-  // writes row segments (natural layout) and, where needed, column segments
-  // (mirror tiles of A and B; weight rows of a tall matrix in the last
-  // iteration) as 16-byte vector accesses.
+  // Each wave stages one 32-row strip of its accumulators in its own LDS
+  // area (so the strips need no block barrier: one wave's LDS accesses take
+  // effect in order), then writes row segments (natural layout) and, where
+  // needed, column segments (mirror tiles of A and B; weight rows of a tall
+  // matrix in the last iteration) as 16-byte vector accesses.
   float scale = 1.f;
   if constexpr (PH == kGram || PH == kBX) {
     if (p.first) {
@@ -430,7 +431,6 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
 #pragma unroll
   for (int pi = 0; pi < NBM; ++pi) {
     stage_strip<NBN, EPP>(acc[pi], ep, lane);
-    __syncthreads();
 
 #pragma unroll
     for (int q = 0; q < RITER; ++q) {
@@ -485,7 +485,6 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
         }
       }
     }
-    __syncthreads();
 
     if (mirror) {
 #pragma unroll
@@ -513,7 +512,6 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
         }
       }
     }
-    __syncthreads();
   }
 }
 
