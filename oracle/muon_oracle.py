@@ -12,6 +12,9 @@ here.
 Every step is written for readability, not speed: one matrix at a time, the
 library matmul as the only primitive, no blocking, fusion or reordering.
 
+The module also holds AdamW, which the pages assign to the parameters Muon
+does not take (embeddings, heads, gains, biases).
+
 Sources (cited by page title and section):
   [README]  "Muon: An optimizer for the hidden layers of neural networks"
             (the KellerJordan/Muon README), sections "Usage" and
@@ -27,7 +30,8 @@ listed with their justification in the design notes of the repository:
   * epsilon in the Frobenius normalisation (1e-7),
   * shape-dependent learning-rate factor (three conventions),
   * decoupled decay applied to the pre-update weight,
-  * float32 momentum buffer, one round-to-nearest-even to bfloat16 for W.
+  * float32 momentum buffer, one round-to-nearest-even to bfloat16 for W,
+  * AdamW: standard bias correction, eps 1e-8 added to sqrt(v_hat).
 
 Pinning: every function here is pinned by tests that do not re-type it (see
 tests/test_oracle_pins.py): the scalar-polynomial closed form verified by
@@ -232,6 +236,47 @@ def precondition(G, S_invs):
     for k, S_inv in enumerate(S_invs):
         out[:, k * d:(k + 1) * d] = G[:, k * d:(k + 1) * d] @ S_inv
     return out
+
+
+# ----------------------------------------------------------------------------
+# AdamW for the parameters Muon does not take ([README] "Usage": embeddings,
+# classifier heads, hidden gains and biases go to AdamW, with lr 3e-4, betas
+# (0.9, 0.95) and weight decay 0.01; [BLOG] section 1 gives the two moment
+# recurrences).
+# ----------------------------------------------------------------------------
+
+DEFAULT_ADAM_LR = 3e-4
+DEFAULT_ADAM_BETAS = (0.9, 0.95)
+DEFAULT_ADAM_WEIGHT_DECAY = 0.01
+DEFAULT_ADAM_EPS = 1e-8        # READING: the README's AdamW line leaves eps at its default
+
+
+def adamw_update(W, G, M, V, t, lr=DEFAULT_ADAM_LR, betas=DEFAULT_ADAM_BETAS,
+                 eps=DEFAULT_ADAM_EPS, weight_decay=DEFAULT_ADAM_WEIGHT_DECAY):
+    """Step t (1-based) of AdamW on one parameter tensor, all in float64.
+
+    First and second moments follow the blog's recurrences,
+        M' = b1*M + (1-b1)*G,   V' = b2*V + (1-b2)*G^2,
+    and the update divides the moments' bias-corrected values,
+        Mh = M'/(1-b1^t),  Vh = V'/(1-b2^t),
+    W' = W - lr*wd*W - lr * Mh / (sqrt(Vh) + eps).
+    READING: the bias correction and eps are the standard Adam ones (the
+    blog's "roughly" form omits both); the decay is decoupled and acts on
+    the pre-update W, as for the Muon update.
+    Returns (W', M', V')."""
+    if t < 1:
+        raise ValueError("Adam steps count from 1")
+    W = np.asarray(W, dtype=np.float64)
+    G = np.asarray(G, dtype=np.float64)
+    M = np.asarray(M, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    b1, b2 = betas
+    M_new = b1 * M + (1.0 - b1) * G
+    V_new = b2 * V + (1.0 - b2) * G * G
+    m_hat = M_new / (1.0 - b1 ** t)
+    v_hat = V_new / (1.0 - b2 ** t)
+    W_new = W - lr * weight_decay * W - lr * m_hat / (np.sqrt(v_hat) + eps)
+    return W_new, M_new, V_new
 
 
 # ----------------------------------------------------------------------------

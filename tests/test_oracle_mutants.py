@@ -69,7 +69,46 @@ def _ortho_no_transpose_back(U, steps=5, eps=orc.DEFAULT_EPS, a=orc.NS_A, b=orc.
     return _ORIG_ORTHO(U, steps, eps, a, b, c)
 
 
+def _adam_no_bias_correction(W, G, M, V, t, lr=orc.DEFAULT_ADAM_LR, betas=orc.DEFAULT_ADAM_BETAS,
+                             eps=orc.DEFAULT_ADAM_EPS, weight_decay=orc.DEFAULT_ADAM_WEIGHT_DECAY):
+    b1, b2 = betas
+    M1 = b1 * M + (1 - b1) * G
+    V1 = b2 * V + (1 - b2) * G * G
+    return W - lr * weight_decay * W - lr * M1 / (np.sqrt(V1) + eps), M1, V1
+
+
+def _adam_eps_in_sqrt(W, G, M, V, t, lr=orc.DEFAULT_ADAM_LR, betas=orc.DEFAULT_ADAM_BETAS,
+                      eps=orc.DEFAULT_ADAM_EPS, weight_decay=orc.DEFAULT_ADAM_WEIGHT_DECAY):
+    b1, b2 = betas
+    M1 = b1 * M + (1 - b1) * G
+    V1 = b2 * V + (1 - b2) * G * G
+    mh, vh = M1 / (1 - b1 ** t), V1 / (1 - b2 ** t)
+    return W - lr * weight_decay * W - lr * mh / np.sqrt(vh + eps), M1, V1
+
+
+def _adam_decay_after_update(W, G, M, V, t, lr=orc.DEFAULT_ADAM_LR, betas=orc.DEFAULT_ADAM_BETAS,
+                             eps=orc.DEFAULT_ADAM_EPS, weight_decay=orc.DEFAULT_ADAM_WEIGHT_DECAY):
+    b1, b2 = betas
+    M1 = b1 * M + (1 - b1) * G
+    V1 = b2 * V + (1 - b2) * G * G
+    mh, vh = M1 / (1 - b1 ** t), V1 / (1 - b2 ** t)
+    W1 = W - lr * mh / (np.sqrt(vh) + eps)
+    return W1 - lr * weight_decay * W1, M1, V1
+
+
+_ORIG_ADAM = orc.adamw_update
+
+
+def _adam_betas_swapped(W, G, M, V, t, lr=orc.DEFAULT_ADAM_LR, betas=orc.DEFAULT_ADAM_BETAS,
+                        eps=orc.DEFAULT_ADAM_EPS, weight_decay=orc.DEFAULT_ADAM_WEIGHT_DECAY):
+    return _ORIG_ADAM(W, G, M, V, t, lr, (betas[1], betas[0]), eps, weight_decay)
+
+
 MUTANTS = {
+    "adam_no_bias_correction": ("adamw_update", _adam_no_bias_correction),
+    "adam_eps_inside_sqrt": ("adamw_update", _adam_eps_in_sqrt),
+    "adam_decay_after_update": ("adamw_update", _adam_decay_after_update),
+    "adam_betas_swapped": ("adamw_update", _adam_betas_swapped),
     "b_sign_flipped": ("newton_schulz", _ns_coeffs(lambda a: a, lambda b: -b, lambda c: c)),
     "c_term_dropped": ("newton_schulz", _ns_coeffs(lambda a: a, lambda b: b, lambda c: 0.0)),
     "a_rounded": ("newton_schulz", _ns_coeffs(lambda a: 3.44, lambda b: b, lambda c: c)),
@@ -90,6 +129,10 @@ PIN_TESTS = [
     pins.test_transpose_equivariance,
     pins.test_momentum_geometric_series,
     pins.test_split_rows_blocks_are_independent,
+    pins.test_adamw_first_step_is_a_signed_step,
+    pins.test_adamw_constant_gradient_keeps_the_signed_step,
+    pins.test_adamw_first_moment_off_sees_every_gradient_alone,
+    pins.test_adamw_decay_and_zero_lr,
 ]
 
 

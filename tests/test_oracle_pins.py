@@ -338,3 +338,76 @@ def test_second_moment_brute_force_and_inverse():
     S2 = Q @ np.diag(lam) @ Q.T + 1e-4 * np.eye(30)
     kappa = np.linalg.cond(S2)
     assert np.abs(orc.spd_inverse(S2) @ S2 - np.eye(30)).max() < kappa * 1e-14
+
+
+# -- AdamW for the non-Muon parameters --------------------------------------
+
+def test_adam_printed_constants():
+    g = _load("page_constants.json")
+    assert orc.DEFAULT_ADAM_LR == g["adam_lr"]["value"]
+    assert list(orc.DEFAULT_ADAM_BETAS) == g["adam_betas"]["value"]
+    assert orc.DEFAULT_ADAM_WEIGHT_DECAY == g["adam_weight_decay"]["value"]
+
+
+def test_adamw_first_step_is_a_signed_step():
+    # from zero moments the bias-corrected moments are exactly g and g^2, so
+    # the step is lr*g/(|g| + eps): lr*sign(g) where |g| >> eps
+    rng = np.random.default_rng(7)
+    W = rng.standard_normal((5, 9))
+    G = rng.standard_normal((5, 9)) * np.logspace(-6, 2, 9)
+    G[0, 0] = 0.0
+    lr, wd, eps = 3e-4, 0.01, 1e-8
+    W1, M1, V1 = orc.adamw_update(W, G, np.zeros_like(G), np.zeros_like(G), 1, lr=lr, eps=eps, weight_decay=wd)
+    step = W * (1 - lr * wd) - W1
+    # (step is a difference of O(1) weights: relative 1e-9 is its float64 floor)
+    assert np.allclose(step, lr * G / (np.abs(G) + eps), rtol=1e-9, atol=1e-18)
+    assert abs(step[0, 0]) < 1e-18
+    big = np.abs(G) > 1e-3
+    assert np.allclose(step[big], lr * np.sign(G[big]), rtol=1e-5)
+    assert np.allclose(M1, 0.1 * G) and np.allclose(V1, 0.05 * G * G)
+
+
+def test_adamw_constant_gradient_keeps_the_signed_step():
+    # with a constant gradient the bias correction makes Mh = g and Vh = g^2
+    # at every step, so every step is the same lr*g/(|g|+eps)
+    rng = np.random.default_rng(8)
+    G = rng.standard_normal((4, 6))
+    W = rng.standard_normal((4, 6))
+    M = np.zeros_like(G)
+    V = np.zeros_like(G)
+    lr = 1e-3
+    for t in range(1, 12):
+        W1, M, V = orc.adamw_update(W, G, M, V, t, lr=lr, weight_decay=0.0)
+        assert np.allclose(W - W1, lr * G / (np.abs(G) + orc.DEFAULT_ADAM_EPS), rtol=1e-10)
+        assert np.allclose(M, (1 - 0.9 ** t) * G, rtol=1e-12)
+        assert np.allclose(V, (1 - 0.95 ** t) * G * G, rtol=1e-12)
+        W = W1
+
+
+def test_adamw_first_moment_off_sees_every_gradient_alone():
+    # b1 = 0: Mh is the current gradient; with gradients of alternating sign
+    # and fixed size c, Vh stays c^2, so the steps alternate +-lr*c/(c+eps)
+    c, lr = 0.5, 1e-2
+    W = np.zeros(3)
+    M = np.zeros(3)
+    V = np.zeros(3)
+    for t in range(1, 8):
+        g = np.full(3, c * (-1) ** t)
+        W1, M, V = orc.adamw_update(W, g, M, V, t, lr=lr, betas=(0.0, 0.95), weight_decay=0.0)
+        assert np.allclose(W - W1, lr * g / (c + orc.DEFAULT_ADAM_EPS), rtol=1e-12)
+        W = W1
+
+
+def test_adamw_decay_and_zero_lr():
+    rng = np.random.default_rng(9)
+    W = rng.standard_normal((3, 3))
+    G = rng.standard_normal((3, 3))
+    W1, M1, V1 = orc.adamw_update(W, G, np.zeros_like(W), np.zeros_like(W), 1, lr=0.0)
+    assert np.array_equal(W1, W)          # lr = 0: weight unchanged, moments still move
+    assert np.allclose(M1, 0.1 * G)
+    # a zero gradient from zero moments: only the decoupled decay acts
+    W2, _, _ = orc.adamw_update(W, np.zeros_like(W), np.zeros_like(W), np.zeros_like(W), 1, lr=0.1,
+                                weight_decay=0.5)
+    assert np.allclose(W2, W * (1 - 0.05), rtol=1e-15)
+    with pytest.raises(ValueError):
+        orc.adamw_update(W, G, W, W, 0)
