@@ -409,5 +409,9 @@ def test_adamw_decay_and_zero_lr():
     W2, _, _ = orc.adamw_update(W, np.zeros_like(W), np.zeros_like(W), np.zeros_like(W), 1, lr=0.1,
                                 weight_decay=0.5)
     assert np.allclose(W2, W * (1 - 0.05), rtol=1e-15)
+
+
+def test_adamw_steps_count_from_one():
+    W = np.zeros((2, 2))
     with pytest.raises(ValueError):
-        orc.adamw_update(W, G, W, W, 0)
+        orc.adamw_update(W, W, W, W, 0)
