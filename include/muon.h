@@ -86,7 +86,16 @@ typedef enum {
  * Without Nesterov U = M'. */
 typedef enum { MUON_MOM_EMA = 0, MUON_MOM_SGD = 1 } muon_momentum_form_t;
 
-/* One hidden weight matrix. */
+/* What a registered tensor is stepped with.  Muon takes the hidden weight
+ * matrices; the other parameters (embeddings, classifier heads, hidden gains
+ * and biases) take AdamW (Muon README, "Usage"), in the same muon_step. */
+typedef enum { MUON_KIND_MUON = 0, MUON_KIND_ADAMW = 1 } muon_kind_t;
+
+/* One parameter tensor.  For kind MUON: a hidden weight matrix.  For kind
+ * ADAMW: any parameter viewed as rows x cols (a vector as 1 x n); momentum
+ * holds AdamW's first moment and exp_avg_sq its second (both float32, same
+ * leading dimension ld_momentum); split_rows, precond and update_out must be
+ * 0, -1 and NULL. */
 typedef struct {
   void* param;          /* rows x cols, dtype; updated in place               */
   const void* grad;     /* rows x cols, dtype; read only                      */
@@ -102,6 +111,10 @@ typedef struct {
   float* update_out;    /* optional: rows x cols float32, contiguous (ld =
                            cols); receives the orthogonalised update O of this
                            step, before lr/scale.  NULL = not written.        */
+  int32_t kind;         /* muon_kind_t; 0 (MUON) in a zero-filled struct      */
+  int32_t reserved;     /* 0                                                  */
+  float* exp_avg_sq;    /* kind ADAMW: rows x cols float32 second moment,
+                           leading dimension ld_momentum; NULL for MUON       */
 } muon_tensor_t;
 
 /* A preconditioner slot: nblocks inverse second moments of size d x d.  A
@@ -124,6 +137,15 @@ typedef struct {
   float ns_a, ns_b, ns_c;/* 3.4445, -4.7750, 2.0315                           */
   int32_t scale_mode;    /* muon_scale_t, default ORIGINAL                    */
   int32_t momentum_form; /* muon_momentum_form_t, default EMA                 */
+  /* AdamW for kind-ADAMW tensors (Muon README, "Usage": lr 3e-4, betas
+   * (0.9, 0.95), weight_decay 0.01; eps is AdamW's usual 1e-8).  Step t of
+   * the AdamW count: M = b1 M + (1-b1) G, V = b2 V + (1-b2) G^2,
+   * W = W - lr*wd*W - lr * (M/(1-b1^t)) / (sqrt(V/(1-b2^t)) + eps). */
+  float adam_lr;         /* 3e-4 (times the tensor's lr_mult)                 */
+  float adam_beta1;      /* 0.9;  0 <= beta1 < 1                              */
+  float adam_beta2;      /* 0.95; 0 <= beta2 < 1                              */
+  float adam_eps;        /* 1e-8                                              */
+  float adam_weight_decay; /* 0.01                                            */
 } muon_hparams_t;
 
 /* Fills the defaults listed above. */
@@ -154,7 +176,8 @@ muon_status_t muon_precond_refresh(muon_handle_t h, int32_t slot, int32_t block,
                                    const void* acts, int64_t n_rows, int64_t ld,
                                    int32_t dtype, float damping, void* stream);
 
-/* One Muon step over every registered matrix; lr < 0 uses hp.lr.
+/* One optimizer step over every registered tensor: Muon on the kind-MUON
+ * matrices (lr < 0 uses hp.lr), AdamW on the kind-ADAMW tensors (hp.adam_lr).
  * Asynchronous on `stream`; no allocation, no synchronisation. */
 muon_status_t muon_step(muon_handle_t h, float lr, void* stream);
 
@@ -165,6 +188,15 @@ muon_status_t muon_step(muon_handle_t h, float lr, void* stream);
 muon_status_t muon_step_timed(muon_handle_t h, float lr, void* stream,
                               float* phase_ms, int32_t max_phases, int32_t* n_phases);
 const char* muon_phase_name(muon_handle_t h, int32_t phase);
+
+/* AdamW step count.  The count lives in the workspace: muon_init() sets it
+ * to 0 and every muon_step() that has kind-ADAMW tensors advances it by one
+ * on the device before using it (so the first step is t = 1).  To resume,
+ * set the number of steps already taken; both calls are asynchronous on
+ * `stream` except that muon_get_adam_step() synchronises it to return the
+ * value. */
+muon_status_t muon_set_adam_step(muon_handle_t h, int64_t steps_taken, void* stream);
+muon_status_t muon_get_adam_step(muon_handle_t h, void* stream, int64_t* steps_taken);
 
 /* Synchronises `stream` and returns the sticky flag word:
  * bit 0 = a non-finite value was seen in an update, bit 1 = a

@@ -26,6 +26,7 @@ STATUS_NAMES = {
 MUON_F32, MUON_BF16 = 0, 1
 SCALE_NONE, SCALE_ORIGINAL, SCALE_MATCH_RMS_ADAMW = 0, 1, 2
 MOM_EMA, MOM_SGD = 0, 1
+KIND_MUON, KIND_ADAMW = 0, 1
 
 
 class MuonTensor(ctypes.Structure):
@@ -35,6 +36,7 @@ class MuonTensor(ctypes.Structure):
         ("ld_param", ctypes.c_int64), ("ld_grad", ctypes.c_int64), ("ld_momentum", ctypes.c_int64),
         ("dtype", ctypes.c_int32), ("split_rows", ctypes.c_int32), ("precond", ctypes.c_int32),
         ("lr_mult", ctypes.c_float), ("update_out", ctypes.c_void_p),
+        ("kind", ctypes.c_int32), ("reserved", ctypes.c_int32), ("exp_avg_sq", ctypes.c_void_p),
     ]
 
 
@@ -48,6 +50,8 @@ class MuonHparams(ctypes.Structure):
         ("eps", ctypes.c_float), ("nesterov", ctypes.c_int32), ("ns_steps", ctypes.c_int32),
         ("ns_a", ctypes.c_float), ("ns_b", ctypes.c_float), ("ns_c", ctypes.c_float),
         ("scale_mode", ctypes.c_int32), ("momentum_form", ctypes.c_int32),
+        ("adam_lr", ctypes.c_float), ("adam_beta1", ctypes.c_float), ("adam_beta2", ctypes.c_float),
+        ("adam_eps", ctypes.c_float), ("adam_weight_decay", ctypes.c_float),
     ]
 
 
@@ -91,6 +95,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "muon_step_timed": (i32, [vp, f32, vp, ctypes.POINTER(f32), i32, ctypes.POINTER(i32)]),
         "muon_phase_name": (ctypes.c_char_p, [vp, i32]),
         "muon_get_flags": (i32, [vp, vp, i32, ctypes.POINTER(ctypes.c_uint32)]),
+        "muon_set_adam_step": (i32, [vp, i64, vp]),
+        "muon_get_adam_step": (i32, [vp, vp, ctypes.POINTER(i64)]),
         "muon_destroy": (i32, [vp]),
         "muon_plan_describe": (i32, [PT, i32, PP, i32, PH, ctypes.c_char_p, sz, ctypes.POINTER(sz)]),
         "muon_status_str": (ctypes.c_char_p, [i32]),
@@ -218,6 +224,41 @@ def tensor_desc(param, grad, momentum, *, split_rows=0, precond=-1, lr_mult=1.0,
     return d
 
 
+def adam_tensor_desc(param, grad, exp_avg, exp_avg_sq, *, lr_mult=1.0) -> MuonTensor:
+    """A parameter stepped with AdamW (embedding, head, gain, bias): any
+    shape, viewed as rows x cols (a vector as 1 x n, a >= 2-D tensor as
+    shape[0] x rest); exp_avg and exp_avg_sq are its float32 moments."""
+    torch = _torch()
+    if not (grad.shape == param.shape == exp_avg.shape == exp_avg_sq.shape):
+        raise ValueError("param, grad and both moments must share one shape")
+    if exp_avg.stride() != exp_avg_sq.stride():
+        raise ValueError("the two moments must share one layout")
+    if param.dim() == 1:
+        param, grad, exp_avg, exp_avg_sq = (t.view(1, -1) if t.is_contiguous() else t.unsqueeze(0)
+                                            for t in (param, grad, exp_avg, exp_avg_sq))
+    else:
+        param, grad, exp_avg, exp_avg_sq = (_as_matrix(t) for t in (param, grad, exp_avg, exp_avg_sq))
+    for t in (param, grad, exp_avg, exp_avg_sq):
+        if t.stride(1) != 1:
+            raise ValueError("tensors must be row-major (unit column stride)")
+    if param.dtype != grad.dtype:
+        raise ValueError("param and grad must share a dtype")
+    if exp_avg.dtype != torch.float32 or exp_avg_sq.dtype != torch.float32:
+        raise ValueError("the moments must be float32")
+    dt = {torch.float32: MUON_F32, torch.bfloat16: MUON_BF16}.get(param.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {param.dtype}")
+    d = MuonTensor()
+    d.param, d.grad, d.momentum = param.data_ptr(), grad.data_ptr(), exp_avg.data_ptr()
+    d.exp_avg_sq = exp_avg_sq.data_ptr()
+    d.rows, d.cols = param.shape
+    d.ld_param, d.ld_grad, d.ld_momentum = param.stride(0), grad.stride(0), exp_avg.stride(0)
+    d.dtype, d.split_rows, d.precond, d.lr_mult = dt, 0, -1, lr_mult
+    d.kind = KIND_ADAMW
+    d.update_out = None
+    return d
+
+
 class MuonStep:
     """One handle over a list of (param, grad, momentum) device tensors.
 
@@ -273,6 +314,16 @@ class MuonStep:
         _check(self._lib.muon_precond_refresh(self._h, slot, block, ctypes.c_void_p(acts.data_ptr()),
                                               acts.shape[0], acts.stride(0), dt, ctypes.c_float(damping),
                                               self._stream(stream)))
+
+    def set_adam_step(self, steps_taken: int, stream=None):
+        """Resume the AdamW step count (steps already taken)."""
+        _check(self._lib.muon_set_adam_step(self._h, int(steps_taken), self._stream(stream)))
+
+    def adam_step(self, stream=None) -> int:
+        """AdamW steps taken so far (synchronises the stream)."""
+        v = ctypes.c_int64(0)
+        _check(self._lib.muon_get_adam_step(self._h, self._stream(stream), ctypes.byref(v)))
+        return v.value
 
     def flags(self, reset: bool = False, stream=None) -> int:
         v = ctypes.c_uint32(0)

@@ -17,7 +17,7 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libmuon.so")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 
-SOURCES = ["muon_host.cpp", "elementwise.hip", "ns_gemm.hip", "precond.hip"]
+SOURCES = ["muon_host.cpp", "elementwise.hip", "ns_gemm.hip", "precond.hip", "adamw.hip"]
 
 ARCH = "gfx950"
 HIP_FLAGS = [

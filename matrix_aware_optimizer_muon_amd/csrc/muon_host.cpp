@@ -1,7 +1,10 @@
 // Host side of the Muon C ABI: validation, planning (units, sides, padding,
 // tile lists, workspace carve-up), descriptor upload and kernel sequencing.
 //
-// Plan of one step (per NS-precision group, all matrices of the group at once):
+// Plan of one step:
+//   adamw     (2 launches, only with kind-ADAMW tensors: count tick, update)
+//             Muon README "Usage"
+// then per NS-precision group, all matrices of the group at once:
 //   momentum  (1 launch)      Muon README "Hyperparameter tuning"
 //   ns_steps x {gram, square, bx}  (3 launches each)   Muon blog sec. 3;
 //             the last bx applies the update (Muon README "Usage")
@@ -66,6 +69,9 @@ struct Plan {
   std::vector<ApplyTask> apply;
   size_t off_pdev = 0, off_apply = 0;
   Group groups[2];  // [0] bf16, [1] float32
+  std::vector<int> adam_tensors;     // kind-ADAMW tensors, in tensor order
+  std::vector<AdamTask> adam_tasks;
+  size_t off_adam_dev = 0, off_adam_tasks = 0, off_adam_state = 0;
   size_t off_flags = 0, off_partials = 0;
   size_t meta_bytes = 0, total = 0;
   int total_k1_tiles = 0;
@@ -99,6 +105,10 @@ muon_status_t validate(const muon_tensor_t* ts, int32_t n, const muon_precond_t*
     return fail(MUON_ERR_BAD_ARG, "unknown scale_mode");
   if (hp->momentum_form != MUON_MOM_EMA && hp->momentum_form != MUON_MOM_SGD)
     return fail(MUON_ERR_BAD_ARG, "unknown momentum_form");
+  if (!finite(hp->adam_lr) || !finite(hp->adam_eps) || !finite(hp->adam_weight_decay) ||
+      !(hp->adam_beta1 >= 0.f && hp->adam_beta1 < 1.f) || !(hp->adam_beta2 >= 0.f && hp->adam_beta2 < 1.f) ||
+      hp->adam_eps < 0.f)
+    return fail(MUON_ERR_BAD_ARG, "AdamW hyper-parameters: finite lr, eps >= 0, decay, betas in [0, 1)");
   for (int32_t k = 0; k < npc; ++k) {
     if (pcs[k].d < 1 || pcs[k].nblocks < 1 || pcs[k].d > 16384 || pcs[k].nblocks > 64)
       return fail(MUON_ERR_BAD_SHAPE, "preconditioner " + std::to_string(k) + ": bad d or nblocks");
@@ -114,6 +124,17 @@ muon_status_t validate(const muon_tensor_t* ts, int32_t n, const muon_precond_t*
       return fail(MUON_ERR_BAD_SHAPE, who + "rows and cols must be in [1, 2^20]");
     if (t.ld_param < t.cols || t.ld_grad < t.cols || t.ld_momentum < t.cols)
       return fail(MUON_ERR_BAD_SHAPE, who + "leading dimensions must be >= cols");
+    if (t.kind != MUON_KIND_MUON && t.kind != MUON_KIND_ADAMW)
+      return fail(MUON_ERR_BAD_ARG, who + "kind must be MUON_KIND_MUON or MUON_KIND_ADAMW");
+    const bool adam = t.kind == MUON_KIND_ADAMW;
+    if (adam) {
+      if (!t.exp_avg_sq) return fail(MUON_ERR_NULL_ARG, who + "an AdamW tensor needs exp_avg_sq");
+      if (t.split_rows != 0 || t.precond != -1 || t.update_out)
+        return fail(MUON_ERR_BAD_ARG, who + "an AdamW tensor takes no split_rows, precond or update_out");
+      if (reinterpret_cast<uintptr_t>(t.exp_avg_sq) % 4) return fail(MUON_ERR_ALIGNMENT, who + "exp_avg_sq misaligned");
+    } else if (t.exp_avg_sq) {
+      return fail(MUON_ERR_BAD_ARG, who + "exp_avg_sq is only for AdamW tensors");
+    }
     if (t.split_rows < 0 || (t.split_rows > 0 && t.rows % t.split_rows != 0))
       return fail(MUON_ERR_BAD_SHAPE, who + "split_rows must be 0 or divide rows");
     if (t.precond < -1 || t.precond >= npc) return fail(MUON_ERR_BAD_ARG, who + "precond slot out of range");
@@ -130,7 +151,7 @@ muon_status_t validate(const muon_tensor_t* ts, int32_t n, const muon_precond_t*
     const int64_t h = t.split_rows ? t.split_rows : t.rows;
     const int64_t m = std::min<int64_t>(h, t.cols), nn = std::max<int64_t>(h, t.cols);
     const int64_t T = t.dtype == MUON_F32 ? kTileF32 : kPadBf16;
-    if (round_up(m, T) * round_up(nn, T) > (int64_t(1) << 31))
+    if (!adam && round_up(m, T) * round_up(nn, T) > (int64_t(1) << 31))
       return fail(MUON_ERR_UNSUPPORTED, who + "matrix too large for one orthogonalisation unit");
     auto add = [&](const void* p, int64_t ld, size_t esz, const char* what) {
       const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
@@ -141,6 +162,7 @@ muon_status_t validate(const muon_tensor_t* ts, int32_t n, const muon_precond_t*
     add(t.grad, t.ld_grad, es, "grad");
     add(t.momentum, t.ld_momentum, 4, "momentum");
     if (t.update_out) add(t.update_out, t.cols, 4, "update_out");
+    if (t.exp_avg_sq) add(t.exp_avg_sq, t.ld_momentum, 4, "exp_avg_sq");
   }
   std::sort(ranges.begin(), ranges.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
   for (size_t k = 1; k < ranges.size(); ++k)
@@ -237,9 +259,22 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
       for (int r = 0; r < trs; ++r)
         for (int c = 0; c < tcs; ++c) plan.apply.push_back({pi, r, c, blk});
   }
+  // AdamW tensors: rows of `len` elements in chunks of kAdamChunk; a fully
+  // contiguous tensor is one row of rows*cols elements
+  for (int32_t i = 0; i < n; ++i) {
+    const muon_tensor_t& t = ts[i];
+    if (t.kind != MUON_KIND_ADAMW) continue;
+    const int ai = int(plan.adam_tensors.size());
+    plan.adam_tensors.push_back(i);
+    const bool flat = t.ld_param == t.cols && t.ld_grad == t.cols && t.ld_momentum == t.cols;
+    const int64_t nrows = flat ? 1 : t.rows, len = flat ? t.rows * t.cols : t.cols;
+    for (int64_t r = 0; r < nrows; ++r)
+      for (int64_t c0 = 0; c0 < len; c0 += kAdamChunk) plan.adam_tasks.push_back({ai, int32_t(r), c0});
+  }
   // units
   for (int32_t i = 0; i < n; ++i) {
     const muon_tensor_t& t = ts[i];
+    if (t.kind == MUON_KIND_ADAMW) continue;
     const int64_t h = t.split_rows ? t.split_rows : t.rows;
     for (int64_t b = 0; b < t.rows / h; ++b) {
       UnitPlan u;
@@ -304,6 +339,9 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
   }
   plan.off_pdev = off; off = align_up(off + sizeof(PrecondDev) * plan.prec_tensors.size());
   plan.off_apply = off; off = align_up(off + sizeof(ApplyTask) * plan.apply.size());
+  plan.off_adam_dev = off; off = align_up(off + sizeof(AdamDev) * plan.adam_tensors.size());
+  plan.off_adam_tasks = off; off = align_up(off + sizeof(AdamTask) * plan.adam_tasks.size());
+  plan.off_adam_state = off; off = align_up(off + sizeof(AdamState));
   plan.meta_bytes = off;
   for (UnitPlan& u : plan.units) {
     const size_t es = u.f32 ? 4 : 2;
@@ -406,6 +444,29 @@ std::vector<uint8_t> build_meta(const Plan& plan, const muon_tensor_t* ts, uint8
   }
   if (!plan.apply.empty())
     std::memcpy(meta.data() + plan.off_apply, plan.apply.data(), plan.apply.size() * sizeof(ApplyTask));
+  for (size_t ai = 0; ai < plan.adam_tensors.size(); ++ai) {
+    const muon_tensor_t& t = ts[plan.adam_tensors[ai]];
+    const size_t es = t.dtype == MUON_F32 ? 4 : 2;
+    const bool flat = t.ld_param == t.cols && t.ld_grad == t.cols && t.ld_momentum == t.cols;
+    AdamDev d;
+    std::memset(&d, 0, sizeof(d));
+    d.param = t.param;
+    d.grad = t.grad;
+    d.m = t.momentum;
+    d.v = t.exp_avg_sq;
+    d.ld_param = t.ld_param;
+    d.ld_grad = t.ld_grad;
+    d.ld_mom = t.ld_momentum;
+    d.len = flat ? t.rows * t.cols : t.cols;
+    d.f32 = t.dtype == MUON_F32;
+    auto al = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+    d.vec = al(t.param) && al(t.grad) && al(t.momentum) && al(t.exp_avg_sq) &&
+            (flat || ((t.ld_param * es) % 16 == 0 && (t.ld_grad * es) % 16 == 0 && (t.ld_momentum * 4) % 16 == 0));
+    d.lr_mult = t.lr_mult;
+    std::memcpy(meta.data() + plan.off_adam_dev + ai * sizeof(AdamDev), &d, sizeof(d));
+  }
+  if (!plan.adam_tasks.empty())
+    std::memcpy(meta.data() + plan.off_adam_tasks, plan.adam_tasks.data(), plan.adam_tasks.size() * sizeof(AdamTask));
   return meta;
 }
 
@@ -435,6 +496,17 @@ muon_status_t enqueue_step(muon_handle_t h, float lr, hipStream_t s, std::vector
     return hipEventRecord((*ev)[ek++], s) == hipSuccess;
   };
   if (!mark()) return fail(MUON_ERR_HIP, "hipEventRecord failed");
+  if (!plan.adam_tasks.empty()) {
+    AdamState* st = reinterpret_cast<AdamState*>(h->ws + plan.off_adam_state);
+    hipError_t e = launch_adam_tick(st, hp.adam_beta1, hp.adam_beta2, s);
+    AdamParams ap{hp.adam_lr, hp.adam_beta1, hp.adam_beta2, hp.adam_eps, hp.adam_weight_decay, st,
+                  reinterpret_cast<uint32_t*>(h->ws + plan.off_flags)};
+    if (e == hipSuccess)
+      e = launch_adamw(reinterpret_cast<const AdamDev*>(h->ws + plan.off_adam_dev),
+                       reinterpret_cast<const AdamTask*>(h->ws + plan.off_adam_tasks), int(plan.adam_tasks.size()),
+                       ap, s);
+    if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("adamw launch: ") + hipGetErrorString(e));
+  }
   if (!plan.apply.empty()) {
     hipError_t e = launch_precond_apply(reinterpret_cast<const PrecondDev*>(h->ws + plan.off_pdev),
                                         reinterpret_cast<const ApplyTask*>(h->ws + plan.off_apply),
@@ -508,10 +580,16 @@ std::string plan_json(const Plan& plan, const muon_hparams_t& hp) {
                   (long long)plan.slots[k].d, plan.slots[k].nblocks, plan.slots[k].dp);
     s += buf;
   }
-  std::snprintf(buf, sizeof(buf), "],\"apply_tiles\":%zu,\"launch_order\":[", plan.apply.size());
+  std::snprintf(buf, sizeof(buf), "],\"apply_tiles\":%zu,\"adamw_tensors\":%zu,\"adamw_tasks\":%zu,"
+                "\"launch_order\":[", plan.apply.size(), plan.adam_tensors.size(), plan.adam_tasks.size());
   s += buf;
   first = true;
+  if (!plan.adam_tasks.empty()) {
+    s += "\"adam_tick\",\"adamw\"";
+    first = false;
+  }
   if (!plan.apply.empty()) {
+    if (!first) s += ",";
     s += "\"precond_apply\"";
     first = false;
   }
@@ -552,6 +630,11 @@ void muon_default_hparams(muon_hparams_t* hp) {
   hp->ns_c = 2.0315f;
   hp->scale_mode = MUON_SCALE_ORIGINAL;
   hp->momentum_form = MUON_MOM_EMA;
+  hp->adam_lr = 3e-4f;
+  hp->adam_beta1 = 0.9f;
+  hp->adam_beta2 = 0.95f;
+  hp->adam_eps = 1e-8f;
+  hp->adam_weight_decay = 0.01f;
 }
 
 muon_status_t muon_workspace_size(const muon_tensor_t* tensors, int32_t n_tensors, const muon_precond_t* preconds,
@@ -598,10 +681,10 @@ muon_status_t muon_init(muon_handle_t* out, const muon_tensor_t* tensors, int32_
   for (int32_t i = 0; i < n_tensors; ++i) {
     const muon_tensor_t& t = tensors[i];
     const size_t es = t.dtype == MUON_F32 ? 4 : 2;
-    const void* ps[4] = {t.param, t.grad, t.momentum, t.update_out};
-    const int64_t lds[4] = {t.ld_param, t.ld_grad, t.ld_momentum, t.cols};
-    const size_t ess[4] = {es, es, 4, 4};
-    for (int k = 0; k < 4; ++k) {
+    const void* ps[5] = {t.param, t.grad, t.momentum, t.update_out, t.exp_avg_sq};
+    const int64_t lds[5] = {t.ld_param, t.ld_grad, t.ld_momentum, t.cols, t.ld_momentum};
+    const size_t ess[5] = {es, es, 4, 4, 4};
+    for (int k = 0; k < 5; ++k) {
       if (!ps[k]) continue;
       const uintptr_t lo = reinterpret_cast<uintptr_t>(ps[k]);
       const uintptr_t hi = lo + size_t((t.rows - 1) * lds[k] + t.cols) * ess[k];
@@ -627,6 +710,7 @@ muon_status_t muon_init(muon_handle_t* out, const muon_tensor_t* tensors, int32_
     return fail(MUON_ERR_HIP, std::string("workspace initialisation: ") + hipGetErrorString(e));
   }
   h->last_stream = s;
+  if (!h->plan.adam_tasks.empty()) h->phase_names.push_back("adamw");
   if (!h->plan.apply.empty()) h->phase_names.push_back("precond_apply");
   for (const Group& g : h->plan.groups) {
     if (g.units.empty()) continue;
@@ -706,6 +790,28 @@ muon_status_t muon_step_timed(muon_handle_t h, float lr, void* stream, float* ph
 const char* muon_phase_name(muon_handle_t h, int32_t phase) {
   if (!h || phase < 0 || size_t(phase) >= h->phase_names.size()) return "";
   return h->phase_names[size_t(phase)].c_str();
+}
+
+muon_status_t muon_set_adam_step(muon_handle_t h, int64_t steps_taken, void* stream) {
+  if (!h) return fail(MUON_ERR_NULL_ARG, "handle is NULL");
+  if (steps_taken < 0 || steps_taken > int64_t(UINT32_MAX) - 1) return fail(MUON_ERR_BAD_ARG, "step count out of range");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_adam_set(reinterpret_cast<AdamState*>(h->ws + h->plan.off_adam_state),
+                                 uint32_t(steps_taken), s);
+  if (e != hipSuccess) return fail(MUON_ERR_HIP, std::string("adam step set: ") + hipGetErrorString(e));
+  h->last_stream = s;
+  return MUON_OK;
+}
+
+muon_status_t muon_get_adam_step(muon_handle_t h, void* stream, int64_t* steps_taken) {
+  if (!h || !steps_taken) return fail(MUON_ERR_NULL_ARG, "handle or output is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  AdamState st;
+  hipError_t e = hipMemcpyAsync(&st, h->ws + h->plan.off_adam_state, sizeof(st), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(MUON_ERR_HIP, std::string("adam step read: ") + hipGetErrorString(e));
+  *steps_taken = int64_t(st.t);
+  return MUON_OK;
 }
 
 muon_status_t muon_get_flags(muon_handle_t h, void* stream, int32_t reset, uint32_t* flags) {

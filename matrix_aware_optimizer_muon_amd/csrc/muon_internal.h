@@ -112,6 +112,32 @@ struct PrecondBlockDev {
 };
 
 // Launchers (defined in the .hip files).
+// AdamW tensors (parameters Muon does not take).  Each is stepped as a set
+// of "rows" of `len` elements; a tensor whose param, grad and moments are all
+// contiguous is one row of rows*cols elements.
+struct AdamDev {
+  void* param; const void* grad; float* m; float* v;
+  int64_t ld_param, ld_grad, ld_mom;   // elements between rows
+  int64_t len;                         // elements per row
+  int32_t f32;                         // param/grad float32 (else bf16)
+  int32_t vec;                         // 16-byte aligned rows: vector accesses
+  float lr_mult;
+  int32_t pad;
+};
+constexpr int kAdamChunk = 2048;       // elements of one row per block (256 threads x 8)
+struct AdamTask { int32_t tensor, row; int64_t c0; };
+struct AdamState {                     // on the device, in the workspace
+  uint32_t t;                          // steps taken
+  float inv_bc1;                       // 1 / (1 - b1^t)
+  float inv_sqrt_bc2;                  // 1 / sqrt(1 - b2^t)
+  uint32_t pad;
+};
+struct AdamParams {
+  float lr, beta1, beta2, eps, weight_decay;
+  const AdamState* state;
+  uint32_t* flags;
+};
+
 hipError_t launch_momentum(bool f32, const UnitDev* units, const EwTask* tasks, int n_tasks,
                            const K1Params& p, hipStream_t s);
 hipError_t launch_gemm(int phase, bool f32, const UnitDev* units, const GemmTask* tasks,
@@ -122,5 +148,9 @@ hipError_t launch_precond_refresh(const PrecondBlockDev& b, const void* acts, in
                                   bool acts_f32, float damping, uint32_t* flags, hipStream_t s);
 hipError_t launch_precond_apply(const PrecondDev* pds, const ApplyTask* tasks, int n_tasks, hipStream_t s);
 hipError_t launch_identity(float* sinv, int dp, int nblocks, hipStream_t s);
+hipError_t launch_adam_tick(AdamState* st, float beta1, float beta2, hipStream_t s);
+hipError_t launch_adam_set(AdamState* st, uint32_t t, hipStream_t s);
+hipError_t launch_adamw(const AdamDev* tensors, const AdamTask* tasks, int n_tasks, const AdamParams& p,
+                        hipStream_t s);
 
 }  // namespace muon

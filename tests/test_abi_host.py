@@ -249,3 +249,51 @@ def test_filter_tensors_become_matrices():
     plan = mm.plan_describe(ts, mm.default_hparams())
     assert sorted(u["m"] for u in plan["units"]) == [64, 64, 256, 256, 256, 256]
     assert [g["units"] for g in plan["groups"]] == [4, 2]
+
+
+def fake_adam(rows, cols, base, dtype=B.MUON_BF16, ld=None):
+    """An AdamW descriptor with fake pointers: param, grad, exp_avg, exp_avg_sq
+    laid out one after the other from `base`; returns (desc, bytes used)."""
+    t, span = fake(rows, cols, dtype, base, ld=ld)
+    mspan = ((rows * (ld or cols) * 4 + 4095) // 4096 + 1) * 4096
+    t.kind = B.KIND_ADAMW
+    t.exp_avg_sq = base + span
+    return t, span + mspan
+
+
+def test_adamw_descriptors_validate_and_plan():
+    muon = fakes([(64, 128), (128, 64)])
+    base = BASE + (1 << 32)
+    vec, n1 = fake_adam(1, 768, base)
+    mat, n2 = fake_adam(100, 50, base + n1, dtype=B.MUON_F32)           # contiguous: one flat row
+    strided, n3 = fake_adam(10, 30, base + n1 + n2, ld=40)               # ld > cols: ten rows
+    ts = muon + [vec, mat, strided]
+    assert ws_status(ts)[0] == "MUON_OK"
+    plan = mm.plan_describe(ts, mm.default_hparams())
+    assert plan["adamw_tensors"] == 3
+    assert plan["adamw_tasks"] == 1 + 3 + 10        # 768 / 2048, 5000 / 2048, 10 rows of 30
+    assert plan["launch_order"][:3] == ["adam_tick", "adamw", "momentum/f32"]   # m = 64: float32 NS
+    assert len(plan["units"]) == 2                   # AdamW tensors are not orthogonalised
+    # AdamW-only requests are valid
+    assert mm.plan_describe([vec], mm.default_hparams())["launch_order"] == ["adam_tick", "adamw"]
+    # descriptor errors
+    t, _ = fake_adam(4, 8, base); t.exp_avg_sq = None
+    assert ws_status([t])[0] == "MUON_ERR_NULL_ARG"
+    t, _ = fake_adam(4, 8, base); t.split_rows = 2
+    assert ws_status([t])[0] == "MUON_ERR_BAD_ARG"
+    t, _ = fake_adam(4, 8, base); t.kind = 3
+    assert ws_status([t])[0] == "MUON_ERR_BAD_ARG"
+    t = fakes([(64, 128)])[0]; t.exp_avg_sq = base
+    assert ws_status([t])[0] == "MUON_ERR_BAD_ARG"       # only AdamW tensors carry a second moment
+    t, _ = fake_adam(4, 8, base); t.exp_avg_sq = t.momentum + 16
+    assert ws_status([t])[0] == "MUON_ERR_ALIASING"
+    for bad in (dict(adam_beta1=1.0), dict(adam_beta2=-0.1), dict(adam_eps=-1.0), dict(adam_lr=float("inf"))):
+        assert ws_status([vec], mm.default_hparams(**bad))[0] == "MUON_ERR_BAD_ARG"
+
+
+def test_adam_default_hparams_are_the_pages_values():
+    hp = mm.default_hparams()
+    assert math.isclose(hp.adam_lr, 3e-4, rel_tol=1e-6)
+    assert math.isclose(hp.adam_beta1, 0.9, rel_tol=1e-6) and math.isclose(hp.adam_beta2, 0.95, rel_tol=1e-6)
+    assert math.isclose(hp.adam_weight_decay, 0.01, rel_tol=1e-6)
+    assert math.isclose(hp.adam_eps, 1e-8, rel_tol=1e-6)
