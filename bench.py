@@ -33,6 +33,9 @@ WORKLOAD_TEXT = {
     "square": "square: one 4096x4096 bf16 matrix, rank-32 + noise gradient; " + STEP_TEXT,
     "gpt2xl": "gpt2xl: GPT-2-XL hidden weights, 48 layers x {Q,K,V,O 1600x1600, MLP-up 6400x1600, "
               "MLP-down 1600x6400} = 288 bf16 matrices; " + STEP_TEXT,
+    "gpt2s_aux": "gpt2s_aux: the gpt2s hidden matrices (Muon) plus every other GPT-2-small parameter with AdamW "
+                 "(embeddings 50257x768 and 1024x768, 98 gain and bias vectors; 39.5M parameters, bf16); "
+                 + STEP_TEXT + "; AdamW lr 3e-4, betas (0.9, 0.95), wd 0.01",
     "conv": "conv: 3x3 convolution filters of a CIFAR-10-style network as out x (in*9) matrices, 6 bf16 "
             "filters (64x288, 64x576, 256x576, 3 x 256x2304); " + STEP_TEXT,
     "tiny": "tiny: one 256x512 fp32 matrix; " + STEP_TEXT,
@@ -112,7 +115,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="gpt2s", choices=["gpt2s", "square", "gpt2xl", "conv", "tiny"],
+    ap.add_argument("--workload", default="gpt2s", choices=["gpt2s", "gpt2s_aux", "square", "gpt2xl", "conv", "tiny"],
                     help="weight set to step (the headline metric is quoted on gpt2s)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 3 device-to-device copies of BYTES each (HBM counter calibration)")
@@ -152,6 +155,13 @@ def main():
         else:
             tg, tw = torch.from_numpy(G).to(dev), torch.from_numpy(W).to(dev)
         tm = torch.from_numpy(M).to(dev)
+        if s.kind == "adamw":               # embeddings, gains, biases: AdamW in the same step
+            shape = s.shape or (s.rows, s.cols)
+            tg, tw, tm = tg.view(shape), tw.view(shape), tm.view(shape)
+            tv = torch.zeros_like(tm)
+            keep += [tg, tw, tm, tv]
+            descs.append(mm.adam_tensor_desc(tw, tg, tm, tv))
+            continue
         keep += [tg, tw, tm]
         descs.append(mm.tensor_desc(tw, tg, tm))
     st = mm.MuonStep(descs, hp, device=dev)
@@ -183,6 +193,8 @@ def main():
 
     units = []
     for s in wl.tensors:
+        if s.kind != "muon":
+            continue
         h = s.split_rows or s.rows
         m = min(h, s.cols)
         es = 4 if (s.dtype == "f32" or m < 128) else 2     # NS precision of the unit
@@ -195,9 +207,12 @@ def main():
             flops[k] += v
         for k, v in ns_bytes(m, n, es, w_es, max(1, hp.ns_steps)).items():
             nbytes[k] += v
-    elems = sum(s.rows * s.cols for s in wl.tensors)
+    elems = sum(s.rows * s.cols for s in wl.tensors if s.kind == "muon")
     nbytes["momentum"] = 13 * elems          # G (bf16) + M read, M + X master (hi, int8) written
     nbytes["update"] = 8 * elems
+    # AdamW: W read and written, G read, both float32 moments read and written
+    nbytes["adamw"] = sum(s.rows * s.cols * (3 * (4 if s.dtype == "f32" else 2) + 16)
+                          for s in wl.tensors if s.kind == "adamw")
     totals = {k: sum(v) / nprof for k, v in per.items()}          # ms per step by kernel kind
     avg = {k: sum(v) / len(v) for k, v in per.items()}             # ms per launch
     ns_ms = sum(totals[k] for k in ("gram", "square", "bx"))
@@ -239,8 +254,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.workload],
-                   "matrices": len(wl.tensors), "params": elems, "parallelism": "single GPU"},
-        "matrices_per_s": round(len(wl.tensors) * 1000.0 / ms_per_step, 1),
+                   "matrices": sum(1 for s in wl.tensors if s.kind == "muon"), "params": elems,
+                   "adamw_params": sum(s.rows * s.cols for s in wl.tensors if s.kind == "adamw"),
+                   "parallelism": "single GPU"},
+        "matrices_per_s": round(sum(1 for s in wl.tensors if s.kind == "muon") * 1000.0 / ms_per_step, 1),
         "ns_tflops": round(ns_tflop / (ns_ms * 1e-3), 2),
         "ns_frac_bf16_peak": round(ns_tflop / (ns_ms * 1e-3) / PEAK_BF16_TFLOPS, 4),
         "phase_ms_per_step": {k: round(v, 4) for k, v in totals.items()},

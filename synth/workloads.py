@@ -28,7 +28,7 @@ import numpy as np
 F32 = "f32"
 BF16 = "bf16"
 
-_WL_ID = {"tiny": 1, "square": 2, "gpt2s": 3, "gpt2xl": 4, "nmuon": 5, "conv": 6}
+_WL_ID = {"tiny": 1, "square": 2, "gpt2s": 3, "gpt2xl": 4, "nmuon": 5, "conv": 6, "gpt2s_aux": 7}
 _KIND_ID = {"grad": 1, "mom": 2, "weight": 3, "acts": 4, "scale": 5,
             "gfac": 6, "gnoise": 7, "sigma": 8}
 
@@ -67,6 +67,8 @@ class TensorSpec:
     split_rows: int = 0   # >0: orthogonalise row blocks of this height
     precond: int = -1     # preconditioner slot, -1 = none
     precond_blocks: int = 1
+    kind: str = "muon"    # "muon" (hidden matrix) or "adamw" (embedding, gain, bias)
+    shape: tuple = ()     # the parameter's own shape when it is not rows x cols (vectors)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -117,6 +119,23 @@ def workload(name: str, layers: Optional[int] = None) -> Workload:
         ts = [t for l in range(n) for t in _gpt2_layer(l, 6 * l, 1600, BF16)]
         return Workload("gpt2xl", ts, grad_law="lowrank", grad_rank=64,
                         noise_std=1e-3)
+    if name == "gpt2s_aux":
+        # the GPT-2-small hidden matrices (Muon) plus every other parameter
+        # of the model (AdamW): token and position embeddings (the head is
+        # tied to the token embedding), per layer two layer-norm gains and
+        # biases and the four linear biases, and the final layer norm
+        d = 768
+        ts = [t for l in range(12) for t in _gpt2_layer(l, 6 * l, d, BF16)]
+        idx = 1000
+        aux = [("wte", 50257, d, ()), ("wpe", 1024, d, ())]
+        for l in range(12):
+            for nm, n in (("ln1_g", d), ("ln1_b", d), ("attn_b", 3 * d), ("proj_b", d), ("ln2_g", d),
+                          ("ln2_b", d), ("fc_b", 4 * d), ("fcproj_b", d)):
+                aux.append((f"{nm}{l}", 1, n, (n,)))
+        aux += [("lnf_g", 1, d, (d,)), ("lnf_b", 1, d, (d,))]
+        for k, (nm, r, c, shp) in enumerate(aux):
+            ts.append(TensorSpec(nm, -1, idx + k, r, c, BF16, kind="adamw", shape=shp))
+        return Workload("gpt2s_aux", ts, grad_law="gauss_scaled", grad_std=1e-2)
     if name == "conv":
         # convolution filters of a small CIFAR-10-style network as the 2-D
         # views Muon orthogonalises, out x (in*kh*kw): three blocks of two
@@ -138,7 +157,7 @@ def workload(name: str, layers: Optional[int] = None) -> Workload:
     raise KeyError(name)
 
 
-WORKLOADS = ("tiny", "square", "gpt2s", "gpt2xl", "conv", "nmuon")
+WORKLOADS = ("tiny", "square", "gpt2s", "gpt2xl", "conv", "nmuon", "gpt2s_aux")
 
 
 def _store(x: np.ndarray, dtype: str) -> np.ndarray:
