@@ -214,6 +214,24 @@ def second_moment(acts, damping=1e-4):
     return X.T @ X / n_rows + damping * np.eye(d)
 
 
+def second_moment_accumulated(batches, beta=1.0, damping=1e-4):
+    """S from activations that arrive in micro-batches X_1..X_K (the online
+    form of the second moment): Sigma = sum_k beta^(K-k) X_k^T X_k and
+    N = sum_k beta^(K-k) n_k, S = Sigma / N + damping*I.  beta = 1 is the plain
+    sum (S equals second_moment of all rows at once); beta < 1 weights older
+    micro-batches down exponentially.
+    READING: the pages build S from a layer's inputs and say it is refreshed
+    during training without fixing how samples are pooled; this is the
+    plainest pooling (a running sum, optionally decayed)."""
+    Sigma, N = None, 0.0
+    for X in batches:
+        X = np.asarray(X, dtype=np.float64)
+        XtX = X.T @ X
+        Sigma = XtX if Sigma is None else beta * Sigma + XtX
+        N = beta * N + X.shape[0]
+    return Sigma / N + damping * np.eye(Sigma.shape[0])
+
+
 def spd_inverse(S):
     """S^-1 of a symmetric positive definite S via its Cholesky factor:
     S = L L^T, so S^-1 = L^-T L^-1."""

@@ -415,3 +415,30 @@ def test_adamw_steps_count_from_one():
     W = np.zeros((2, 2))
     with pytest.raises(ValueError):
         orc.adamw_update(W, W, W, W, 0)
+
+
+# -- online second moment (accumulated over micro-batches) -------------------
+
+def test_accumulated_second_moment_equals_one_batch():
+    # beta = 1: the micro-batch sum is the full-batch X^T X over all rows
+    rng = np.random.default_rng(21)
+    parts = [rng.standard_normal((n, 6)) for n in (5, 9, 3)]
+    S_acc = orc.second_moment_accumulated(parts, beta=1.0, damping=1e-3)
+    S_all = orc.second_moment(np.vstack(parts), damping=1e-3)
+    assert np.allclose(S_acc, S_all, rtol=1e-13, atol=1e-15)
+
+
+def test_accumulated_second_moment_decay():
+    # a constant micro-batch repeated: any beta gives that batch's moment
+    rng = np.random.default_rng(22)
+    X = rng.standard_normal((7, 4))
+    for beta in (1.0, 0.9, 0.5, 0.0):
+        S = orc.second_moment_accumulated([X, X, X, X], beta=beta, damping=0.0)
+        assert np.allclose(S, X.T @ X / 7, rtol=1e-12)
+    # beta = 0 keeps only the last micro-batch
+    Y = rng.standard_normal((3, 4))
+    assert np.allclose(orc.second_moment_accumulated([X, Y], beta=0.0, damping=0.0), Y.T @ Y / 3, rtol=1e-12)
+    # two batches, beta = 0.5: brute-force weights 0.5 and 1 on the sums and counts
+    S = orc.second_moment_accumulated([X, Y], beta=0.5, damping=0.0)
+    ref = (0.5 * sum(np.outer(r, r) for r in X) + sum(np.outer(r, r) for r in Y)) / (0.5 * 7 + 3)
+    assert np.allclose(S, ref, rtol=1e-12)
