@@ -176,6 +176,26 @@ muon_status_t muon_precond_refresh(muon_handle_t h, int32_t slot, int32_t block,
                                    const void* acts, int64_t n_rows, int64_t ld,
                                    int32_t dtype, float damping, void* stream);
 
+/* Newton-Muon, online form (the second moment gathered from micro-batches
+ * as they pass, instead of one activation batch): adds the n_rows x d
+ * activations of one micro-batch to the running sums of block `block` of
+ * slot `slot`,
+ *     Sigma <- beta * Sigma + X^T X,    N <- beta * N + n_rows
+ * (beta = 1: plain sum over micro-batches; beta < 1: older micro-batches
+ * weighted down exponentially; 0 <= beta <= 1).  X^T X is formed as in
+ * muon_precond_refresh (bf16 or float32 MFMA, float32 sums).  Asynchronous
+ * on `stream`.  The sums start at zero at muon_init(). */
+muon_status_t muon_precond_accumulate(muon_handle_t h, int32_t slot, int32_t block, const void* acts,
+                                      int64_t n_rows, int64_t ld, int32_t dtype, float beta, void* stream);
+
+/* Rebuilds block `block` of slot `slot` from its running sums:
+ * S = Sigma / N + damping * I, then S^-1 exactly as muon_precond_refresh
+ * (a block with N = 0 gets S = damping * I).  reset != 0 clears Sigma and
+ * N afterwards.  Asynchronous on `stream`; flag bit 1 as for
+ * muon_precond_refresh. */
+muon_status_t muon_precond_refresh_accumulated(muon_handle_t h, int32_t slot, int32_t block, float damping,
+                                               int32_t reset, void* stream);
+
 /* One optimizer step over every registered tensor: Muon on the kind-MUON
  * matrices (lr < 0 uses hp.lr), AdamW on the kind-ADAMW tensors (hp.adam_lr).
  * Asynchronous on `stream`; no allocation, no synchronisation. */

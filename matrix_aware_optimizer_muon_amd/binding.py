@@ -91,6 +91,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "muon_workspace_size": (i32, [PT, i32, PP, i32, PH, ctypes.POINTER(sz)]),
         "muon_init": (i32, [ctypes.POINTER(vp), PT, i32, PP, i32, PH, vp, sz, vp]),
         "muon_precond_refresh": (i32, [vp, i32, i32, vp, i64, i64, i32, f32, vp]),
+        "muon_precond_accumulate": (i32, [vp, i32, i32, vp, i64, i64, i32, f32, vp]),
+        "muon_precond_refresh_accumulated": (i32, [vp, i32, i32, f32, i32, vp]),
         "muon_step": (i32, [vp, f32, vp]),
         "muon_step_timed": (i32, [vp, f32, vp, ctypes.POINTER(f32), i32, ctypes.POINTER(i32)]),
         "muon_phase_name": (ctypes.c_char_p, [vp, i32]),
@@ -314,6 +316,26 @@ class MuonStep:
         _check(self._lib.muon_precond_refresh(self._h, slot, block, ctypes.c_void_p(acts.data_ptr()),
                                               acts.shape[0], acts.stride(0), dt, ctypes.c_float(damping),
                                               self._stream(stream)))
+
+    def precond_accumulate(self, slot: int, block: int, acts, beta: float = 1.0, stream=None):
+        """Add one micro-batch of layer-input activations to the running
+        second moment of (slot, block): Sigma <- beta Sigma + X^T X."""
+        torch = _torch()
+        if acts.dim() != 2 or acts.stride(1) != 1:
+            raise ValueError("activations must be 2-D row-major")
+        dt = {torch.float32: MUON_F32, torch.bfloat16: MUON_BF16}.get(acts.dtype)
+        if dt is None:
+            raise ValueError(f"unsupported activation dtype {acts.dtype}")
+        self._keep.append(acts)      # asynchronous: kept alive until the next sync
+        _check(self._lib.muon_precond_accumulate(self._h, slot, block, ctypes.c_void_p(acts.data_ptr()),
+                                                 acts.shape[0], acts.stride(0), dt, ctypes.c_float(beta),
+                                                 self._stream(stream)))
+
+    def precond_refresh_accumulated(self, slot: int, block: int, damping: float = 1e-4, reset: bool = True,
+                                    stream=None):
+        """Rebuild S^-1 of (slot, block) from its running second moment."""
+        _check(self._lib.muon_precond_refresh_accumulated(self._h, slot, block, ctypes.c_float(damping),
+                                                          int(reset), self._stream(stream)))
 
     def set_adam_step(self, steps_taken: int, stream=None):
         """Resume the AdamW step count (steps already taken)."""

@@ -59,6 +59,7 @@ struct SlotPlan {
   int64_t d = 0;
   int nblocks = 0, dp = 0;
   size_t off_s = 0, off_l = 0, off_li = 0, off_sinv = 0;   // nblocks consecutive dp x dp blocks each
+  size_t off_acc = 0, off_cnt = 0;                          // running X^T X sums and sample counts
 };
 
 struct Plan {
@@ -358,6 +359,8 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
     sp.off_l = off; off = align_up(off + blk * sizeof(double));
     sp.off_li = off; off = align_up(off + blk * sizeof(double));
     sp.off_sinv = off; off = align_up(off + blk * sizeof(float));
+    sp.off_acc = off; off = align_up(off + blk * sizeof(float));
+    sp.off_cnt = off; off = align_up(off + size_t(sp.nblocks) * sizeof(double));
   }
   for (int ti : plan.prec_tensors) {
     plan.off_p.push_back(off);
@@ -727,27 +730,77 @@ muon_status_t muon_init(muon_handle_t* out, const muon_tensor_t* tensors, int32_
   return MUON_OK;
 }
 
-muon_status_t muon_precond_refresh(muon_handle_t h, int32_t slot, int32_t block, const void* acts, int64_t n_rows,
-                                   int64_t ld, int32_t dtype, float damping, void* stream) {
-  if (!h || !acts) return fail(MUON_ERR_NULL_ARG, "handle or activations is NULL");
-  if (slot < 0 || size_t(slot) >= h->plan.slots.size()) return fail(MUON_ERR_BAD_ARG, "no such preconditioner slot");
-  const SlotPlan& sp = h->plan.slots[size_t(slot)];
-  if (block < 0 || block >= sp.nblocks) return fail(MUON_ERR_BAD_ARG, "no such block in the slot");
-  if (dtype != MUON_F32 && dtype != MUON_BF16) return fail(MUON_ERR_BAD_DTYPE, "activations must be f32 or bf16");
-  if (n_rows < 1 || ld < sp.d) return fail(MUON_ERR_BAD_SHAPE, "activations need n_rows >= 1 and ld >= d");
-  if (!std::isfinite(damping) || damping < 0.f) return fail(MUON_ERR_BAD_ARG, "damping must be finite and >= 0");
-  const size_t es = dtype == MUON_F32 ? 4 : 2;
-  if (reinterpret_cast<uintptr_t>(acts) % es) return fail(MUON_ERR_ALIGNMENT, "activations misaligned");
+namespace {
+
+PrecondBlockDev block_dev(muon_handle_t h, const SlotPlan& sp, int32_t block) {
   const size_t bo = size_t(block) * sp.dp * sp.dp;
   PrecondBlockDev b;
   b.s = reinterpret_cast<float*>(h->ws + sp.off_s) + bo;
   b.l = reinterpret_cast<double*>(h->ws + sp.off_l) + bo;
   b.li = reinterpret_cast<double*>(h->ws + sp.off_li) + bo;
   b.sinv = reinterpret_cast<float*>(h->ws + sp.off_sinv) + bo;
+  b.acc = reinterpret_cast<float*>(h->ws + sp.off_acc) + bo;
+  b.cnt = reinterpret_cast<double*>(h->ws + sp.off_cnt) + block;
   b.d = int(sp.d);
   b.dp = sp.dp;
+  return b;
+}
+
+muon_status_t check_slot_block(muon_handle_t h, int32_t slot, int32_t block) {
+  if (!h) return fail(MUON_ERR_NULL_ARG, "handle is NULL");
+  if (slot < 0 || size_t(slot) >= h->plan.slots.size()) return fail(MUON_ERR_BAD_ARG, "no such preconditioner slot");
+  if (block < 0 || block >= h->plan.slots[size_t(slot)].nblocks) return fail(MUON_ERR_BAD_ARG, "no such block in the slot");
+  return MUON_OK;
+}
+
+muon_status_t check_acts(const SlotPlan& sp, const void* acts, int64_t n_rows, int64_t ld, int32_t dtype) {
+  if (!acts) return fail(MUON_ERR_NULL_ARG, "activations are NULL");
+  if (dtype != MUON_F32 && dtype != MUON_BF16) return fail(MUON_ERR_BAD_DTYPE, "activations must be f32 or bf16");
+  if (n_rows < 1 || ld < sp.d) return fail(MUON_ERR_BAD_SHAPE, "activations need n_rows >= 1 and ld >= d");
+  const size_t es = dtype == MUON_F32 ? 4 : 2;
+  if (reinterpret_cast<uintptr_t>(acts) % es) return fail(MUON_ERR_ALIGNMENT, "activations misaligned");
+  return MUON_OK;
+}
+
+}  // namespace
+
+muon_status_t muon_precond_accumulate(muon_handle_t h, int32_t slot, int32_t block, const void* acts,
+                                      int64_t n_rows, int64_t ld, int32_t dtype, float beta, void* stream) {
+  muon_status_t st = check_slot_block(h, slot, block);
+  if (st != MUON_OK) return st;
+  const SlotPlan& sp = h->plan.slots[size_t(slot)];
+  if ((st = check_acts(sp, acts, n_rows, ld, dtype)) != MUON_OK) return st;
+  if (!(beta >= 0.f && beta <= 1.f)) return fail(MUON_ERR_BAD_ARG, "beta must be in [0, 1]");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_precond_refresh(b, acts, n_rows, ld, dtype == MUON_F32, damping,
+  hipError_t e = launch_precond_accumulate(block_dev(h, sp, block), acts, n_rows, ld, dtype == MUON_F32, beta, s);
+  if (e != hipSuccess) return fail(MUON_ERR_HIP, std::string("precond accumulate launch: ") + hipGetErrorString(e));
+  h->last_stream = s;
+  return MUON_OK;
+}
+
+muon_status_t muon_precond_refresh_accumulated(muon_handle_t h, int32_t slot, int32_t block, float damping,
+                                               int32_t reset, void* stream) {
+  muon_status_t st = check_slot_block(h, slot, block);
+  if (st != MUON_OK) return st;
+  if (!std::isfinite(damping) || damping < 0.f) return fail(MUON_ERR_BAD_ARG, "damping must be finite and >= 0");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_precond_refresh_accumulated(block_dev(h, h->plan.slots[size_t(slot)], block), damping,
+                                                    reset != 0,
+                                                    reinterpret_cast<uint32_t*>(h->ws + h->plan.off_flags), s);
+  if (e != hipSuccess) return fail(MUON_ERR_HIP, std::string("precond refresh launch: ") + hipGetErrorString(e));
+  h->last_stream = s;
+  return MUON_OK;
+}
+
+muon_status_t muon_precond_refresh(muon_handle_t h, int32_t slot, int32_t block, const void* acts, int64_t n_rows,
+                                   int64_t ld, int32_t dtype, float damping, void* stream) {
+  muon_status_t st = check_slot_block(h, slot, block);
+  if (st != MUON_OK) return st;
+  const SlotPlan& sp = h->plan.slots[size_t(slot)];
+  if ((st = check_acts(sp, acts, n_rows, ld, dtype)) != MUON_OK) return st;
+  if (!std::isfinite(damping) || damping < 0.f) return fail(MUON_ERR_BAD_ARG, "damping must be finite and >= 0");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_precond_refresh(block_dev(h, sp, block), acts, n_rows, ld, dtype == MUON_F32, damping,
                                         reinterpret_cast<uint32_t*>(h->ws + h->plan.off_flags), s);
   if (e != hipSuccess) return fail(MUON_ERR_HIP, std::string("precond refresh launch: ") + hipGetErrorString(e));
   h->last_stream = s;

@@ -108,6 +108,8 @@ struct PrecondBlockDev {
   double* l;       // Cholesky factor, float64
   double* li;      // its inverse, float64
   float* sinv;     // S^-1, float32
+  float* acc;      // running sum of X^T X over micro-batches, float32, dp x dp
+  double* cnt;     // its running sample count
   int32_t d, dp;
 };
 
@@ -146,6 +148,10 @@ hipError_t launch_update(bool f32, const UnitDev* units, const EwTask* tasks, in
                          const K5Params& p, hipStream_t s);
 hipError_t launch_precond_refresh(const PrecondBlockDev& b, const void* acts, int64_t n_rows, int64_t ld,
                                   bool acts_f32, float damping, uint32_t* flags, hipStream_t s);
+hipError_t launch_precond_accumulate(const PrecondBlockDev& b, const void* acts, int64_t n_rows, int64_t ld,
+                                     bool acts_f32, float beta, hipStream_t s);
+hipError_t launch_precond_refresh_accumulated(const PrecondBlockDev& b, float damping, bool reset, uint32_t* flags,
+                                              hipStream_t s);
 hipError_t launch_precond_apply(const PrecondDev* pds, const ApplyTask* tasks, int n_tasks, hipStream_t s);
 hipError_t launch_identity(float* sinv, int dp, int nblocks, hipStream_t s);
 hipError_t launch_adam_tick(AdamState* st, float beta1, float beta2, hipStream_t s);

@@ -2,7 +2,10 @@
 // Newton-Muon?": each layer's gradient is right-multiplied by the inverse of
 // the layer input's d x d second moment before the usual Muon step).
 //
-//   moment_kernel      S = X^T X / N + damping * I from N x d activations
+//   moment_kernel      S = X^T X / N + damping * I from N x d activations,
+//                      or (accumulating form) Sigma <- beta Sigma + X^T X
+//                      for one micro-batch; finalize_kernel then forms
+//                      S = Sigma / N + damping * I from the running sums
 //                      (bf16 MFMA with float32 accumulation for bf16
 //                      activations, float32 MFMA for float32 ones); upper
 //                      tiles, mirror-stored; the padded diagonal is set to 1
@@ -49,7 +52,7 @@ template <> struct MomCfg<true> {
 template <bool F32>
 __global__ __launch_bounds__(kThreads)
 void moment_kernel(const void* __restrict__ acts, int64_t n_rows, int64_t ld, int d, int vec,
-                   float* __restrict__ S, int dp, float inv_n, float damping) {
+                   float* __restrict__ S, int dp, float inv_n, float damping, int accumulate, float beta) {
   using C = MomCfg<F32>;
   using E = typename C::E;
   constexpr int BT = C::BT, WT = C::WT, BK = C::BK;
@@ -162,7 +165,9 @@ void moment_kernel(const void* __restrict__ acts, int64_t n_rows, int64_t ld, in
     __syncthreads();
   }
 
-  // epilogue: S = acc / N (+ damping on the diagonal; padded diagonal = 1)
+  // epilogue: S = acc / N (+ damping on the diagonal; padded diagonal = 1),
+  // or, accumulating, S = beta * S + acc (every element belongs to one
+  // thread of one tile, so the read-modify-write needs no atomics)
   float* ep = reinterpret_cast<float*>(smem) + wave * (32 * EPP);
   const int row_base = ti * BT + wm * WT, col_base = tj * BT + wn * WT;
 #pragma unroll
@@ -176,6 +181,13 @@ void moment_kernel(const void* __restrict__ acts, int64_t n_rows, int64_t ld, in
     for (int s = lane; s < 32 * WT; s += 64) {
       const int row = s / WT, col = s % WT;
       const int gr = row_base + pi * 32 + row, gc = col_base + col;
+      if (accumulate) {
+        const float a = ep[row * EPP + col];
+        const size_t o = static_cast<size_t>(gr) * dp + gc, om = static_cast<size_t>(gc) * dp + gr;
+        S[o] = beta != 0.f ? fmaf(beta, S[o], a) : a;
+        if (ti != tj) S[om] = beta != 0.f ? fmaf(beta, S[om], a) : a;
+        continue;
+      }
       float v = ep[row * EPP + col] * inv_n;
       if (gr == gc) v = gr < d ? v + damping : 1.0f;
       S[static_cast<size_t>(gr) * dp + gc] = v;
@@ -476,6 +488,36 @@ void apply_kernel(const PrecondDev* __restrict__ pds, const ApplyTask* __restric
 }
 
 // S^-1 = I for every block (the state of a slot before its first refresh).
+// Running sample count of an accumulating block: N <- beta N + n_rows.
+__global__ void count_kernel(double* cnt, float beta, int64_t n_rows) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *cnt = static_cast<double>(beta) * *cnt + static_cast<double>(n_rows);
+}
+
+// S = Sigma / N + damping * I (padded diagonal 1); a block with no samples
+// gives S = damping * I.
+__global__ __launch_bounds__(kThreads) void finalize_kernel(const float* __restrict__ acc, const double* cnt,
+                                                            float* __restrict__ S, int d, int dp, float damping) {
+  const double n = *cnt;
+  const float inv_n = n > 0.0 ? static_cast<float>(1.0 / n) : 0.f;
+  const size_t total = static_cast<size_t>(dp) * dp;
+  for (size_t k = blockIdx.x * static_cast<size_t>(kThreads) + threadIdx.x; k < total;
+       k += static_cast<size_t>(gridDim.x) * kThreads) {
+    const int i = static_cast<int>(k / dp), j = static_cast<int>(k % dp);
+    float v = acc[k] * inv_n;
+    if (i == j) v = i < d ? v + damping : 1.0f;
+    S[k] = v;
+  }
+}
+
+// Clears a block's running sum and count.
+__global__ __launch_bounds__(kThreads) void clear_acc_kernel(float* __restrict__ acc, double* cnt, int dp) {
+  const size_t total = static_cast<size_t>(dp) * dp;
+  for (size_t k = blockIdx.x * static_cast<size_t>(kThreads) + threadIdx.x; k < total;
+       k += static_cast<size_t>(gridDim.x) * kThreads)
+    acc[k] = 0.f;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *cnt = 0.0;
+}
+
 __global__ __launch_bounds__(kThreads) void identity_kernel(float* __restrict__ sinv, int dp, int nblocks) {
   const size_t n = static_cast<size_t>(nblocks) * dp * dp;
   for (size_t k = blockIdx.x * static_cast<size_t>(kThreads) + threadIdx.x; k < n;
@@ -492,19 +534,28 @@ hipError_t launch_identity(float* sinv, int dp, int nblocks, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_precond_refresh(const PrecondBlockDev& b, const void* acts, int64_t n_rows, int64_t ld,
-                                  bool acts_f32, float damping, uint32_t* flags, hipStream_t s) {
-  const int dp = b.dp, nb = dp / kCb;
+namespace {
+
+// X^T X of one activation batch into `out`: normalised (inv_n, damping) or
+// accumulated (out = beta * out + X^T X).
+void launch_moment(const void* acts, int64_t n_rows, int64_t ld, bool acts_f32, int d, int dp, float* out,
+                   float inv_n, float damping, int accumulate, float beta, hipStream_t s) {
   const size_t es = acts_f32 ? 4 : 2;
   const int vec = (reinterpret_cast<uintptr_t>(acts) % 16 == 0) && ((ld * es) % 16 == 0);
-  const float inv_n = static_cast<float>(1.0 / static_cast<double>(n_rows));
   if (acts_f32) {
     const int nt = dp / MomCfg<true>::BT;
-    moment_kernel<true><<<nt * (nt + 1) / 2, kThreads, 0, s>>>(acts, n_rows, ld, b.d, vec, b.s, dp, inv_n, damping);
+    moment_kernel<true><<<nt * (nt + 1) / 2, kThreads, 0, s>>>(acts, n_rows, ld, d, vec, out, dp, inv_n, damping,
+                                                               accumulate, beta);
   } else {
     const int nt = dp / MomCfg<false>::BT;
-    moment_kernel<false><<<nt * (nt + 1) / 2, kThreads, 0, s>>>(acts, n_rows, ld, b.d, vec, b.s, dp, inv_n, damping);
+    moment_kernel<false><<<nt * (nt + 1) / 2, kThreads, 0, s>>>(acts, n_rows, ld, d, vec, out, dp, inv_n, damping,
+                                                                accumulate, beta);
   }
+}
+
+// S (in b.s) -> float64 Cholesky factor -> its inverse -> S^-1 (float32).
+void factor_and_invert(const PrecondBlockDev& b, uint32_t* flags, hipStream_t s) {
+  const int dp = b.dp, nb = dp / kCb;
   to_f64_kernel<<<256, kThreads, 0, s>>>(b.s, b.l, dp);
   for (int jb = 0; jb < nb; ++jb) {
     potrf_kernel<<<1, kThreads, 0, s>>>(b.l, dp, jb, flags);
@@ -517,6 +568,30 @@ hipError_t launch_precond_refresh(const PrecondBlockDev& b, const void* acts, in
   trinv_diag_kernel<<<nb, kThreads, 0, s>>>(b.l, b.li, dp);
   for (int ib = 1; ib < nb; ++ib) trinv_offdiag_kernel<<<ib, kThreads, 0, s>>>(b.l, b.li, dp, ib);
   inv_product_kernel<<<nb * nb, kThreads, 0, s>>>(b.li, b.sinv, dp);
+}
+
+}  // namespace
+
+hipError_t launch_precond_refresh(const PrecondBlockDev& b, const void* acts, int64_t n_rows, int64_t ld,
+                                  bool acts_f32, float damping, uint32_t* flags, hipStream_t s) {
+  const float inv_n = static_cast<float>(1.0 / static_cast<double>(n_rows));
+  launch_moment(acts, n_rows, ld, acts_f32, b.d, b.dp, b.s, inv_n, damping, 0, 0.f, s);
+  factor_and_invert(b, flags, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_precond_accumulate(const PrecondBlockDev& b, const void* acts, int64_t n_rows, int64_t ld,
+                                     bool acts_f32, float beta, hipStream_t s) {
+  launch_moment(acts, n_rows, ld, acts_f32, b.d, b.dp, b.acc, 0.f, 0.f, 1, beta, s);
+  count_kernel<<<1, 64, 0, s>>>(b.cnt, beta, n_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_precond_refresh_accumulated(const PrecondBlockDev& b, float damping, bool reset, uint32_t* flags,
+                                              hipStream_t s) {
+  finalize_kernel<<<256, kThreads, 0, s>>>(b.acc, b.cnt, b.s, b.d, b.dp, damping);
+  factor_and_invert(b, flags, s);
+  if (reset) clear_acc_kernel<<<256, kThreads, 0, s>>>(b.acc, b.cnt, b.dp);
   return hipGetLastError();
 }
 

@@ -297,3 +297,12 @@ def test_adam_default_hparams_are_the_pages_values():
     assert math.isclose(hp.adam_beta1, 0.9, rel_tol=1e-6) and math.isclose(hp.adam_beta2, 0.95, rel_tol=1e-6)
     assert math.isclose(hp.adam_weight_decay, 0.01, rel_tol=1e-6)
     assert math.isclose(hp.adam_eps, 1e-8, rel_tol=1e-6)
+
+
+def test_precond_calls_reject_a_null_handle():
+    # argument checks that need no GPU: a NULL handle is refused up front
+    assert B.STATUS_NAMES[lib.muon_precond_accumulate(None, 0, 0, None, 1, 1, 1, ctypes.c_float(1.0), None)] == \
+        "MUON_ERR_NULL_ARG"
+    assert B.STATUS_NAMES[lib.muon_precond_refresh_accumulated(None, 0, 0, ctypes.c_float(1e-4), 1, None)] == \
+        "MUON_ERR_NULL_ARG"
+    assert B.STATUS_NAMES[lib.muon_set_adam_step(None, 1, None)] == "MUON_ERR_NULL_ARG"

@@ -102,3 +102,57 @@ def test_singular_second_moment_sets_flag():
     torch.cuda.synchronize()
     assert st.flags() & 2
     st.close()
+
+
+def _check_slot0(wl, host, dev, hp, S_inv0, S_inv1, label):
+    """P (via momentum) of the slot-0 tensors against the oracle with the
+    given inverse for slot 0 (slot 1 kept at S_inv1)."""
+    slot_inv = {0: [S_inv0], 1: S_inv1}
+    for s, (G, W, M), (dw, dg, dm, do) in zip(wl.tensors, host, dev):
+        if s.precond != 0:
+            continue
+        ref = oracle_step(W, G, M, "bf16", hp, split_rows=s.split_rows, S_invs=slot_inv[s.precond])
+        eM = rel_f(dm.cpu().numpy(), ref["M"])
+        eO = rel_f(do.cpu().numpy(), ref["O"])
+        say(f"  {label} {s.name} {s.rows}x{s.cols}: P (via momentum) {eM:.2e}  O {eO:.2e}")
+        assert eM <= 2e-3
+        assert eO <= 2e-2
+
+
+def test_accumulated_second_moment_over_micro_batches():
+    # the online form: S gathered from four micro-batches (plain sum), then a
+    # decayed sum (beta 0.5) over three different ones after a reset
+    say("case: Newton-Muon S accumulated over micro-batches (sum, then beta = 0.5 after reset)")
+    wl = synth.workload("nmuon")
+    hp = mm.default_hparams()
+    acts = orc.bf16_bits_to_f64(synth.activations(wl, 0))
+    parts = [synth.to_bf16_bits(acts[k * 4096:(k + 1) * 4096]) for k in range(4)]
+    dparts = [to_device(torch, p, "bf16") for p in parts]
+    eye = [np.eye(768)] * 4
+    damp = float(np.float32(1e-4))
+
+    host, dev = _tensors(wl)
+    st = mm.MuonStep(_descs(wl, dev), hp, preconds=_precs())
+    for dp_ in dparts:
+        st.precond_accumulate(0, 0, dp_, beta=1.0)
+    st.precond_refresh_accumulated(0, 0, damping=1e-4, reset=True)
+    st.step()
+    torch.cuda.synchronize()
+    assert st.flags() == 0
+    st.close()
+    S0 = orc.second_moment_accumulated([orc.bf16_bits_to_f64(p) for p in parts], 1.0, damp)
+    _check_slot0(wl, host, dev, hp, orc.spd_inverse(S0), eye, "sum of 4")
+
+    host, dev = _tensors(wl)
+    st = mm.MuonStep(_descs(wl, dev), hp, preconds=_precs())
+    st.precond_accumulate(0, 0, dparts[3], beta=1.0)
+    st.precond_refresh_accumulated(0, 0, damping=1e-4, reset=True)     # cleared afterwards
+    for dp_ in dparts[:3]:
+        st.precond_accumulate(0, 0, dp_, beta=0.5)
+    st.precond_refresh_accumulated(0, 0, damping=1e-4, reset=False)
+    st.step()
+    torch.cuda.synchronize()
+    assert st.flags() == 0
+    st.close()
+    S1 = orc.second_moment_accumulated([orc.bf16_bits_to_f64(p) for p in parts[:3]], 0.5, damp)
+    _check_slot0(wl, host, dev, hp, orc.spd_inverse(S1), eye, "decayed 3")
