@@ -264,6 +264,30 @@ __device__ __forceinline__ void capture_master(const E* lbx, int kt, int kt0, in
   }
 }
 
+// B = b A + c A A: the A tile (ti, tj) the epilogue combines is part of the
+// A operand of the same block (rows ti, K columns tj), so each lane copies
+// its row segments out of LDS during the K step that holds its columns,
+// and the epilogue reads no A from memory.  A wave's WTN columns lie in one
+// K step (WTN divides BK).
+template <bool F32, int NBM, int RITER, int SEGS, int WTM, int WTN, int BK, typename E>
+__device__ __forceinline__ void capture_atile(const E* la, int kt, int kt_cap, int wm, int wn, int lane,
+                                              u32x4_t (&pre0)[NBM][RITER], u32x4_t (&pre1)[NBM][RITER]) {
+  static_assert(BK % WTN == 0, "a wave's columns must lie in one K step");
+  constexpr int EPE = 16 / sizeof(E);
+  if (kt != kt_cap) return;
+#pragma unroll
+  for (int pi = 0; pi < NBM; ++pi)
+#pragma unroll
+    for (int q = 0; q < RITER; ++q) {
+      const int sg = lane + 64 * q;
+      const int r = wm * WTM + pi * 32 + sg / SEGS;            // tile row = A-operand row
+      const int k = (wn * WTN + (sg % SEGS) * 8) % BK;         // column inside the K step
+      pre0[pi][q] = *reinterpret_cast<const u32x4_t*>(&la[r * BK + swz_kc(r, k / EPE) * EPE]);
+      if constexpr (F32)
+        pre1[pi][q] = *reinterpret_cast<const u32x4_t*>(&la[r * BK + swz_kc(r, k / EPE + 1) * EPE]);
+    }
+}
+
 template <bool F32, int PH>
 __global__ __launch_bounds__((64 * Cfg<F32, PH>::NWM * Cfg<F32, PH>::NWN), (Cfg<F32, PH>::OCC))
 void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restrict__ tasks,
@@ -354,7 +378,8 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   // row, RITER per lane
   constexpr int SEGS = WTN / 8;
   constexpr int RITER = 32 * SEGS / 64;
-  constexpr int NPRE = KMAJOR_B ? NBM : 1;
+  constexpr bool CAPTURE = KMAJOR_B || PH == kSquare;   // epilogue operand taken from LDS
+  constexpr int NPRE = CAPTURE ? NBM : 1;
   u32x4_t pre0[NPRE][RITER], pre1[NPRE][RITER];     // master: hi (bf16) / first..last 4 (float32)
   u32x2_t preq[NPRE][RITER];                          // master: int8 corrections (bf16)
   const int kt0 = ti * BT / BK;                      // K step of the tile's first row
@@ -384,6 +409,8 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
     const E* cs = smem + (kt % NS) * STAGE;
     if constexpr (KMAJOR_B)
       capture_master<F32, NPRE, RITER, SEGS, WTM, BK, BT>(cs + T_ELEMS, kt, kt0, wm, wn * WTN, lane, pre0, pre1);
+    else if constexpr (PH == kSquare)
+      capture_atile<F32, NPRE, RITER, SEGS, WTM, WTN, BK>(cs, kt, (tj * BT + wn * WTN) / BK, wm, wn, lane, pre0, pre1);
     mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, BT>(cs, cs + T_ELEMS, acc, lane, wm, wn);
   }
   wait_vmcnt<0>();   // the clamped copies of the last stage
@@ -448,11 +475,23 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
         for (int e = 0; e < 8; ++e) v[e] *= scale;
         st8<F32>(u.a, static_cast<size_t>(gr) * mp + gc, v);
       } else if constexpr (PH == kSquare) {
-        float av[8];
-        ld8<F32>(u.a, static_cast<size_t>(gr) * mp + gc, av);
+        float av[8];                                      // A at this segment, captured from LDS
+        if constexpr (F32) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            av[e] = __uint_as_float(pre0[pi][q][e]);
+            av[4 + e] = __uint_as_float(pre1[pi][q][e]);
+          }
+        } else {
+          unpack8_bf16(pre0[pi][q], av);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = fmaf(p.b, av[e], p.c * v[e]);
         st8<F32>(u.b, static_cast<size_t>(gr) * mp + gc, v);
+        if (mirror) {   // the mirror pass stores B^T from the staged values
+          *reinterpret_cast<f32x4_t*>(&ep[row * EPP + cseg * 8]) = f32x4_t{v[0], v[1], v[2], v[3]};
+          *reinterpret_cast<f32x4_t*>(&ep[row * EPP + cseg * 8 + 4]) = f32x4_t{v[4], v[5], v[6], v[7]};
+        }
       } else {
         const size_t off = static_cast<size_t>(gr) * np + gc;
         float xm[8];
@@ -501,11 +540,7 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
           for (int e = 0; e < 8; ++e) v[e] *= scale;
           st8<F32>(u.a, static_cast<size_t>(gc) * mp + gr, v);
         } else if constexpr (PH == kSquare) {
-          float av[8];   // A is exactly symmetric off the diagonal tiles
-          ld8<F32>(u.a, static_cast<size_t>(gc) * mp + gr, av);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = fmaf(p.b, av[e], p.c * v[e]);
-          st8<F32>(u.b, static_cast<size_t>(gc) * mp + gr, v);
+          st8<F32>(u.b, static_cast<size_t>(gc) * mp + gr, v);   // B is symmetric off the diagonal tiles
         } else {
           // tall matrix: O[i][j] = X[j][i], so X column gc is weight row gc
           if (gc < u.rows) update_w8(u, gc, gr, v, decay, step);
