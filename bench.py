@@ -215,6 +215,9 @@ def main():
                           for s in wl.tensors if s.kind == "adamw")
     totals = {k: sum(v) / nprof for k, v in per.items()}          # ms per step by kernel kind
     avg = {k: sum(v) / len(v) for k, v in per.items()}             # ms per launch
+    launches = {k: len(v) // nprof for k, v in per.items()}        # launches per step (two per phase with lanes)
+    # algorithmic work per step of each kind (NS phases run ns_steps times)
+    iters = {k: (hp.ns_steps if k in ("gram", "square", "bx") else 1) for k in per}
     ns_ms = sum(totals[k] for k in ("gram", "square", "bx"))
     ns_tflop = hp.ns_steps * sum(flops.values()) / 1e12
     dom = max(totals, key=totals.get)
@@ -223,22 +226,27 @@ def main():
     # intensity: below the bf16 ridge (peak flops / peak bytes) it is HBM.
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     intensity = flops.get(dom, 0) / nbytes[dom]
+    # per launch: the kind's work per step over its launches per step (with
+    # two lanes each phase is two launches of about half the work)
+    per_launch_flops = flops.get(dom, 0) * iters[dom] / launches[dom]
+    per_launch_bytes = nbytes[dom] * iters[dom] / launches[dom]
     if dom in flops and intensity >= ridge:
-        achieved = flops[dom] / (avg[dom] * 1e-3) / 1e12
+        achieved = per_launch_flops / (avg[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
     else:
-        achieved = nbytes[dom] / (avg[dom] * 1e-3) / 1e9
+        achieved = per_launch_bytes / (avg[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4)}
     roof["traffic"] = load_traffic(dom, src_hash)
     roof["kernel"] = dom
     roof["avg_launch_ms"] = round(avg[dom], 5)
-    roof["algorithmic_bytes"] = int(nbytes[dom])
+    roof["launches_per_step"] = launches[dom]
+    roof["algorithmic_bytes"] = int(per_launch_bytes)
     if dom in flops:
-        roof["algorithmic_flops"] = flops[dom]
+        roof["algorithmic_flops"] = int(per_launch_flops)
         roof["intensity_flop_per_byte"] = round(intensity, 1)
-        roof["mfma_tflops"] = round(flops[dom] / (avg[dom] * 1e-3) / 1e12, 2)
+        roof["mfma_tflops"] = round(per_launch_flops / (avg[dom] * 1e-3) / 1e12, 2)
 
     out = {
         "metric": METRIC,
@@ -265,7 +273,7 @@ def main():
         "wall_s_timed": round(wall, 3),
         "kernel_source_hash": src_hash,
         "roofline": roof,
-        "phase_hbm_gbs": {k: round(nbytes[k] / (avg[k] * 1e-3) / 1e9, 1) for k in avg if k in nbytes},
+        "phase_hbm_gbs": {k: round(nbytes[k] * iters[k] / (totals[k] * 1e-3) / 1e9, 1) for k in avg if k in nbytes},
         "cpu_baseline": None,
     }
     if args.workload != "gpt2s":

@@ -49,6 +49,7 @@ struct UnitPlan {
 
 struct Group {
   bool f32 = false;
+  int lane = 0;            // 0: caller's stream; 1: the handle's second stream
   std::vector<int> units;  // global unit ids
   std::vector<EwTask> ew;
   std::vector<GemmTask> gram, sq, bx;
@@ -69,7 +70,7 @@ struct Plan {
   std::vector<size_t> off_p;         // their P buffers (float32, rows x cols)
   std::vector<ApplyTask> apply;
   size_t off_pdev = 0, off_apply = 0;
-  Group groups[2];  // [0] bf16, [1] float32
+  std::vector<Group> groups;  // by NS precision (bf16 first) and lane
   std::vector<int> adam_tensors;     // kind-ADAMW tensors, in tensor order
   std::vector<AdamTask> adam_tasks;
   size_t off_adam_dev = 0, off_adam_tasks = 0, off_adam_state = 0;
@@ -175,6 +176,8 @@ muon_status_t validate(const muon_tensor_t* ts, int32_t n, const muon_precond_t*
 }
 
 constexpr int kXcds = 8;   // MI355X: 8 accelerator complex dies, one L2 each
+constexpr int kLaneMinUnits = 8;        // matrices of one precision needed for two lanes
+constexpr int64_t kLaneMaxBxTiles = 16384;   // ... and at most this many B X tiles per phase
 
 // XCD-aware order of one phase's tiles.  The dispatcher hands block b to XCD
 // b mod 8, and each XCD has its own L2, so tiles that share operand rows
@@ -297,11 +300,46 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
       u.k1_ntiles = u.k1_tr * u.k1_tc;
       u.k1_tile0 = plan.total_k1_tiles;
       plan.total_k1_tiles += u.k1_ntiles;
-      Group& g = plan.groups[u.f32 ? 1 : 0];
-      g.f32 = u.f32;
-      u.group_index = int(g.units.size());
-      g.units.push_back(int(plan.units.size()));
       plan.units.push_back(u);
+    }
+  }
+  // groups: one per NS precision; a precision with many matrices is split
+  // into two lanes of about equal Newton-Schulz work (longest first), which
+  // muon_step runs on two streams so one lane's memory-bound phases overlap
+  // the other's
+  for (int f = 0; f < 2; ++f) {
+    std::vector<int> ids;
+    for (size_t k = 0; k < plan.units.size(); ++k)
+      if (plan.units[k].f32 == (f == 1)) ids.push_back(int(k));
+    if (ids.empty()) continue;
+    // two lanes pay off when a phase is short (a few waves of tiles, so its
+    // ramp and tail are a large share); with very many tiles the second
+    // stream only adds cache contention
+    int64_t bx_tiles = 0;
+    for (int k : ids) {
+      const UnitPlan& u = plan.units[k];
+      const int tx = u.f32 ? kTileF32 : kTileBxBf16;
+      bx_tiles += int64_t(u.mp / tx) * (u.np / tx);
+    }
+    const int lanes = ids.size() >= size_t(kLaneMinUnits) && bx_tiles <= kLaneMaxBxTiles ? 2 : 1;
+    auto cost = [&](int k) {
+      const UnitPlan& u = plan.units[k];
+      return double(u.mp) * u.mp * (u.mp + 3.0 * u.np);
+    };
+    std::stable_sort(ids.begin(), ids.end(), [&](int a, int b) { return cost(a) > cost(b); });
+    std::vector<Group> lg(lanes);
+    std::vector<double> load(lanes, 0.0);
+    for (int k : ids) {
+      const int l = int(std::min_element(load.begin(), load.end()) - load.begin());
+      load[l] += cost(k);
+      lg[l].units.push_back(k);
+    }
+    for (int l = 0; l < lanes; ++l) {
+      lg[l].f32 = f == 1;
+      lg[l].lane = l;
+      std::sort(lg[l].units.begin(), lg[l].units.end());   // tensor order inside a lane
+      for (size_t gi = 0; gi < lg[l].units.size(); ++gi) plan.units[lg[l].units[gi]].group_index = int(gi);
+      plan.groups.push_back(std::move(lg[l]));
     }
   }
   // tile lists
@@ -482,6 +520,8 @@ struct muon_handle_s {
   uint8_t* ws = nullptr;
   std::vector<uint8_t> meta;  // host copy of the uploaded descriptors (kept for the async copy)
   hipStream_t last_stream = nullptr;
+  hipStream_t lane_stream = nullptr;                 // second lane (created when the plan has one)
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   std::vector<hipEvent_t> events;
   std::vector<std::string> phase_names;
 };
@@ -516,32 +556,45 @@ muon_status_t enqueue_step(muon_handle_t h, float lr, hipStream_t s, std::vector
                                         int(plan.apply.size()), s);
     if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("precond apply launch: ") + hipGetErrorString(e));
   }
+  // Two lanes: the second lane's groups run on the handle's second stream,
+  // forked from `s` here and joined back into it at the end (also under
+  // graph capture).  The timed variant keeps everything on `s`, in order.
+  const bool fork = !ev && h->lane_stream != nullptr;
+  if (fork) {
+    if (hipEventRecord(h->ev_fork, s) != hipSuccess || hipStreamWaitEvent(h->lane_stream, h->ev_fork, 0) != hipSuccess)
+      return fail(MUON_ERR_HIP, "lane fork failed");
+  }
   for (const Group& g : plan.groups) {
     if (g.units.empty()) continue;
+    const hipStream_t gs = fork && g.lane == 1 ? h->lane_stream : s;
     const UnitDev* units = reinterpret_cast<const UnitDev*>(h->ws + g.off_units);
     K1Params k1{hp.momentum, hp.nesterov, hp.momentum_form == MUON_MOM_SGD,
                 reinterpret_cast<uint32_t*>(h->ws + plan.off_flags)};
     hipError_t e = launch_momentum(g.f32, units, reinterpret_cast<const EwTask*>(h->ws + g.off_ew),
-                                   int(g.ew.size()), k1, s);
+                                   int(g.ew.size()), k1, gs);
     if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("momentum launch: ") + hipGetErrorString(e));
     for (int it = 0; it < hp.ns_steps; ++it) {
       GemmParams gp{hp.ns_a, hp.ns_b, hp.ns_c, hp.eps, it == 0, it == hp.ns_steps - 1, it & 1, 0,
                     lr, hp.weight_decay};
       e = launch_gemm(kGram, g.f32, units, reinterpret_cast<const GemmTask*>(h->ws + g.off_gram),
-                      int(g.gram.size()), gp, s);
+                      int(g.gram.size()), gp, gs);
       if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("gram launch: ") + hipGetErrorString(e));
       e = launch_gemm(kSquare, g.f32, units, reinterpret_cast<const GemmTask*>(h->ws + g.off_sq),
-                      int(g.sq.size()), gp, s);
+                      int(g.sq.size()), gp, gs);
       if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("square launch: ") + hipGetErrorString(e));
       e = launch_gemm(kBX, g.f32, units, reinterpret_cast<const GemmTask*>(h->ws + g.off_bx),
-                      int(g.bx.size()), gp, s);
+                      int(g.bx.size()), gp, gs);
       if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("bx launch: ") + hipGetErrorString(e));
     }
     if (hp.ns_steps == 0) {   // otherwise the last B X phase applies the update
       K5Params k5{lr, hp.weight_decay, hp.eps, 0};
-      e = launch_update(g.f32, units, reinterpret_cast<const EwTask*>(h->ws + g.off_ew), int(g.ew.size()), k5, s);
+      e = launch_update(g.f32, units, reinterpret_cast<const EwTask*>(h->ws + g.off_ew), int(g.ew.size()), k5, gs);
       if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("update launch: ") + hipGetErrorString(e));
     }
+  }
+  if (fork) {
+    if (hipEventRecord(h->ev_join, h->lane_stream) != hipSuccess || hipStreamWaitEvent(s, h->ev_join, 0) != hipSuccess)
+      return fail(MUON_ERR_HIP, "lane join failed");
   }
   h->last_stream = s;
   return MUON_OK;
@@ -568,10 +621,10 @@ std::string plan_json(const Plan& plan, const muon_hparams_t& hp) {
       return size_t(std::count_if(v.begin(), v.end(), [](const GemmTask& t) { return t.unit >= 0; }));
     };
     std::snprintf(buf, sizeof(buf),
-                  "%s{\"ns\":\"%s\",\"units\":%zu,\"momentum_tiles\":%zu,\"gram_tiles\":%zu,"
+                  "%s{\"ns\":\"%s\",\"lane\":%d,\"units\":%zu,\"momentum_tiles\":%zu,\"gram_tiles\":%zu,"
                   "\"square_tiles\":%zu,\"bx_tiles\":%zu,\"gram_blocks\":%zu,\"square_blocks\":%zu,"
                   "\"bx_blocks\":%zu,\"tile\":%d,\"bx_tile\":%d}",
-                  first ? "" : ",", g.f32 ? "f32" : "bf16", g.units.size(), g.ew.size(), real(g.gram),
+                  first ? "" : ",", g.f32 ? "f32" : "bf16", g.lane, g.units.size(), g.ew.size(), real(g.gram),
                   real(g.sq), real(g.bx), g.gram.size(), g.sq.size(), g.bx.size(), g.f32 ? kTileF32 : kTileGramBf16,
                   g.f32 ? kTileF32 : kTileBxBf16);
     s += buf;
@@ -713,11 +766,24 @@ muon_status_t muon_init(muon_handle_t* out, const muon_tensor_t* tensors, int32_
     return fail(MUON_ERR_HIP, std::string("workspace initialisation: ") + hipGetErrorString(e));
   }
   h->last_stream = s;
+  bool two_lanes = false;
+  for (const Group& g : h->plan.groups) two_lanes |= g.lane == 1;
+  if (two_lanes) {
+    e = hipStreamCreateWithFlags(&h->lane_stream, hipStreamNonBlocking);   // default priority
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+      if (h->lane_stream) (void)hipStreamDestroy(h->lane_stream);
+      delete h;
+      return fail(MUON_ERR_HIP, std::string("second lane stream: ") + hipGetErrorString(e));
+    }
+  }
   if (!h->plan.adam_tasks.empty()) h->phase_names.push_back("adamw");
   if (!h->plan.apply.empty()) h->phase_names.push_back("precond_apply");
   for (const Group& g : h->plan.groups) {
     if (g.units.empty()) continue;
-    const std::string dt = g.f32 ? "/f32" : "/bf16";
+    const std::string dt = std::string(g.f32 ? "/f32" : "/bf16") + (g.lane ? "@2" : "");
     h->phase_names.push_back("momentum" + dt);
     for (int it = 0; it < hp->ns_steps; ++it) {
       h->phase_names.push_back("gram" + dt + "#" + std::to_string(it + 1));
@@ -885,6 +951,13 @@ muon_status_t muon_get_flags(muon_handle_t h, void* stream, int32_t reset, uint3
 muon_status_t muon_destroy(muon_handle_t h) {
   if (!h) return MUON_OK;
   hipError_t e = hipStreamSynchronize(h->last_stream);
+  if (h->lane_stream) {
+    const hipError_t e2 = hipStreamSynchronize(h->lane_stream);
+    if (e == hipSuccess) e = e2;
+    (void)hipEventDestroy(h->ev_fork);
+    (void)hipEventDestroy(h->ev_join);
+    (void)hipStreamDestroy(h->lane_stream);
+  }
   for (hipEvent_t ev : h->events) (void)hipEventDestroy(ev);
   delete h;
   if (e != hipSuccess) return fail(MUON_ERR_HIP, std::string("destroy: ") + hipGetErrorString(e));
