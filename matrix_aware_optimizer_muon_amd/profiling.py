@@ -70,25 +70,50 @@ def _num(row, *keys, default=0.0):
     return default
 
 
+def _alone(spans):
+    """For dispatches given as (start, end), whether each one overlapped no
+    other dispatch in time (it had the GPU to itself)."""
+    order = sorted(range(len(spans)), key=lambda i: spans[i][0])
+    alone = [True] * len(spans)
+    max_end = float("-inf")
+    for pos, i in enumerate(order):
+        s, e = spans[i]
+        if max_end > s:
+            alone[i] = False
+        if pos + 1 < len(order) and spans[order[pos + 1]][0] < e:
+            alone[i] = False
+        max_end = max(max_end, e)
+    return alone
+
+
 def trace_table(dirpath):
     """Per-kernel rows from the kernel-trace CSV: calls, total/avg µs, grid
-    workgroups, LDS bytes."""
+    workgroups, LDS bytes, and the average over the dispatches that ran alone
+    (kernels of two streams overlap in time; a timing pass that keeps every
+    launch on one stream gives dispatches that do not)."""
     path = _one(dirpath, "*kernel_trace.csv")
-    rows = {}
+    recs = []
     with open(path) as f:
         for r in csv.DictReader(f):
-            name = r.get("Kernel_Name", "")
-            kind = kernel_kind(name)
-            dur = (_num(r, "End_Timestamp") - _num(r, "Start_Timestamp")) / 1e3
             wg = _num(r, "Workgroup_Size_X", "Workgroup_Size", default=1.0) or 1.0
-            grid = _num(r, "Grid_Size_X", "Grid_Size", default=0.0)
-            e = rows.setdefault(kind, {"calls": 0, "total_us": 0.0, "grid": int(grid // wg),
-                                       "lds": int(_num(r, "Group_Segment_Size", "LDS_Block_Size"))})
-            e["calls"] += 1
-            e["total_us"] += dur
+            recs.append((kernel_kind(r.get("Kernel_Name", "")), _num(r, "Start_Timestamp"),
+                         _num(r, "End_Timestamp"), int(_num(r, "Grid_Size_X", "Grid_Size", default=0.0) // wg),
+                         int(_num(r, "Group_Segment_Size", "LDS_Block_Size"))))
+    alone = _alone([(a, b) for _, a, b, _, _ in recs])
+    rows = {}
+    for (kind, t0, t1, grid, lds), al in zip(recs, alone):
+        dur = (t1 - t0) / 1e3
+        e = rows.setdefault(kind, {"calls": 0, "total_us": 0.0, "grid": grid, "lds": lds,
+                                   "alone_calls": 0, "alone_us": 0.0})
+        e["calls"] += 1
+        e["total_us"] += dur
+        if al:
+            e["alone_calls"] += 1
+            e["alone_us"] += dur
     tot = sum(e["total_us"] for e in rows.values()) or 1.0
     for e in rows.values():
         e["avg_us"] = e["total_us"] / e["calls"]
+        e["alone_avg_us"] = e["alone_us"] / e["alone_calls"] if e["alone_calls"] else float("nan")
         e["pct"] = 100.0 * e["total_us"] / tot
     return rows
 
@@ -97,11 +122,12 @@ def trace_markdown(dirpath, title, command):
     rows = trace_table(dirpath)
     out = [f"# {title}", "", "Commands (repository root on one MI355X, `libmuon.so` built):", "", "```",
            command.strip(), "```", "",
-           "| kernel | calls | total µs | avg µs | % | grid (workgroups) | LDS B |",
-           "|---|---:|---:|---:|---:|---:|---:|"]
+           "`alone`: dispatches that overlapped no other dispatch in time.", "",
+           "| kernel | calls | total µs | avg µs | % | alone calls | alone avg µs | grid (workgroups) | LDS B |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
     for k, e in sorted(rows.items(), key=lambda kv: -kv[1]["total_us"]):
         out.append(f"| {k} | {e['calls']} | {e['total_us']:.1f} | {e['avg_us']:.2f} | {e['pct']:.1f} | "
-                   f"{e['grid']} | {e['lds']} |")
+                   f"{e['alone_calls']} | {e['alone_avg_us']:.2f} | {e['grid']} | {e['lds']} |")
     return "\n".join(out) + "\n"
 
 

@@ -1,0 +1,118 @@
+"""Host-side checks of the measurement tools: the rocprofv3 summary readers
+(on small synthetic CSV files laid out as rocprofv3 writes them) and the
+bench's algorithmic work counts and its one-GPU guard."""
+
+import csv
+import os
+import subprocess
+import sys
+
+import pytest
+
+from matrix_aware_optimizer_muon_amd import profiling as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+BX = "void muon::ns_gemm_kernel<false, 2>(muon::UnitDev const*, muon::GemmTask const*, muon::GemmParams)"
+GRAM = "void muon::ns_gemm_kernel<false, 0>(muon::UnitDev const*, muon::GemmTask const*, muon::GemmParams)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def _write(path, fields, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_kernel_kind_names():
+    assert P.kernel_kind(BX) == "bx"
+    assert P.kernel_kind(GRAM) == "gram"
+    assert P.kernel_kind("void muon::ns_gemm_kernel<true, 1>(...)") == "square/f32"
+    assert P.kernel_kind("_ZN4muon14ns_gemm_kernelILb1ELi2EEEvPKNS_7UnitDevE") == "bx/f32"
+    assert P.kernel_kind("void muon::momentum_kernel<false>(...)") == "momentum"
+    assert P.kernel_kind(COPY) == "copy"
+
+
+def test_alone_dispatches():
+    # two overlapping launches (two streams), then serial ones
+    assert P._alone([(0, 1), (2, 3), (2.5, 4), (5, 6)]) == [True, False, False, True]
+    # a long launch overlapping two short ones further on
+    assert P._alone([(0, 10), (1, 2), (3, 4), (11, 12)]) == [False, False, False, True]
+    assert P._alone([]) == []
+
+
+def test_trace_table_separates_overlapping_dispatches(tmp_path):
+    fields = ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Workgroup_Size_X", "Grid_Size_X",
+              "Group_Segment_Size"]
+    us = 1000   # timestamps in ns
+    rows = [  # a two-stream phase: both launches take 200 us side by side
+        {"Kernel_Name": BX, "Start_Timestamp": 0, "End_Timestamp": 200 * us},
+        {"Kernel_Name": BX, "Start_Timestamp": 5 * us, "End_Timestamp": 205 * us},
+        # the same launches one after the other on one stream: 110 us each
+        {"Kernel_Name": BX, "Start_Timestamp": 300 * us, "End_Timestamp": 410 * us},
+        {"Kernel_Name": BX, "Start_Timestamp": 420 * us, "End_Timestamp": 530 * us},
+        {"Kernel_Name": GRAM, "Start_Timestamp": 540 * us, "End_Timestamp": 600 * us},
+    ]
+    for r in rows:
+        r.update({"Workgroup_Size_X": 512, "Grid_Size_X": 512 * 300, "Group_Segment_Size": 65536})
+    _write(str(tmp_path / "run" / "run_kernel_trace.csv"), fields, rows)
+    t = P.trace_table(str(tmp_path))
+    assert t["bx"]["calls"] == 4 and t["bx"]["alone_calls"] == 2
+    assert t["bx"]["avg_us"] == pytest.approx((200 + 200 + 110 + 110) / 4)
+    assert t["bx"]["alone_avg_us"] == pytest.approx(110)
+    assert t["bx"]["grid"] == 300 and t["bx"]["lds"] == 65536
+    assert t["gram"]["alone_avg_us"] == pytest.approx(60)
+    md = P.trace_markdown(str(tmp_path), "t", "cmd")
+    assert "| bx | 4 |" in md and "alone avg" in md
+
+
+def test_traffic_is_scaled_by_the_copy_calibration(tmp_path):
+    fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+    def counters(d, name, rows):
+        _write(str(tmp_path / d / "run_counter_collection.csv"), fields,
+               [{"Dispatch_Id": i, "Kernel_Name": k, "Counter_Name": name, "Counter_Value": v}
+                for i, k, v in rows])
+    # two bx dispatches; counter values of one dispatch come in two instances
+    counters("f", "FETCH_SIZE", [(1, BX, 100.0), (1, BX, 100.0), (2, BX, 300.0)])
+    counters("w", "WRITE_SIZE", [(1, BX, 50.0), (2, BX, 150.0)])
+    # a 1 MiB copy for which FETCH_SIZE reads half the bytes and WRITE_SIZE all
+    counters("cf", "FETCH_SIZE", [(1, COPY, 512.0)])
+    counters("cw", "WRITE_SIZE", [(1, COPY, 1024.0)])
+    d = P.traffic(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "cf"), str(tmp_path / "cw"),
+                  1 << 20, ["cmd"])
+    assert d["calibration"]["fetch_scale"] == pytest.approx(2.0)
+    assert d["calibration"]["write_scale"] == pytest.approx(1.0)
+    assert d["per_launch_read_bytes"]["bx"] == 2 * 250 * 1024      # mean of 200 and 300 KiB, x2
+    assert d["per_launch_write_bytes"]["bx"] == 100 * 1024
+    assert d["per_launch_bytes"]["bx"] == 600 * 1024
+    assert d["kernel_source_hash"] == P.kernel_source_hash()
+
+
+def test_bench_work_counts():
+    # symmetric products: Gram m(m+1)n, square m^2(m+1), update 2m^2n
+    f = bench.ns_flops(768, 3072)
+    assert f == {"gram": 768 * 769 * 3072, "square": 768 * 768 * 769, "bx": 2 * 768 * 768 * 3072}
+    m, n = 256, 512
+    # one iteration: B X reads B, X hi and its int8 correction, and reads and
+    # writes the weight; no X master is written
+    b1 = bench.ns_bytes(m, n, 2, 2, 1)
+    assert b1["bx"] == 2 * m * m + 3 * m * n + 4 * m * n
+    assert b1["gram"] == 2 * m * n + 2 * m * m and b1["square"] == 4 * m * m
+    # five iterations: four write the 3-byte master, the last the weight
+    b5 = bench.ns_bytes(m, n, 2, 2, 5)
+    assert b5["bx"] == pytest.approx((4 * (2 * m * m + 6 * m * n) + b1["bx"]) / 5)
+    # float32 NS: X is one float, no correction
+    b = bench.ns_bytes(m, n, 4, 4, 1)
+    assert b["bx"] == 4 * m * m + 4 * m * n + 8 * m * n
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode != 0 and "one GPU" in r.stderr
