@@ -198,7 +198,12 @@ muon_status_t muon_precond_refresh_accumulated(muon_handle_t h, int32_t slot, in
 
 /* One optimizer step over every registered tensor: Muon on the kind-MUON
  * matrices (lr < 0 uses hp.lr), AdamW on the kind-ADAMW tensors (hp.adam_lr).
- * Asynchronous on `stream`; no allocation, no synchronisation. */
+ * Asynchronous on `stream`; no allocation, no synchronisation.  Part of the
+ * work may run on streams the handle created at muon_init (large groups of
+ * matrices split in lanes; AdamW beside the Muon phases): they wait for an
+ * event recorded on `stream` at the start of the call and `stream` waits for
+ * theirs at the end, so to the caller the step is ordered on `stream` alone
+ * (also when `stream` is being captured into a graph). */
 muon_status_t muon_step(muon_handle_t h, float lr, void* stream);
 
 /* Like muon_step(), but records HIP events around each kernel phase and

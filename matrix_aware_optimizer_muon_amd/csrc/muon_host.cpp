@@ -49,7 +49,7 @@ struct UnitPlan {
 
 struct Group {
   bool f32 = false;
-  int lane = 0;            // 0: caller's stream; 1: the handle's second stream
+  int lane = 0;            // 0: caller's stream; l > 0: the handle's stream l
   std::vector<int> units;  // global unit ids
   std::vector<EwTask> ew;
   std::vector<GemmTask> gram, sq, bx;
@@ -176,7 +176,11 @@ muon_status_t validate(const muon_tensor_t* ts, int32_t n, const muon_precond_t*
 }
 
 constexpr int kXcds = 8;   // MI355X: 8 accelerator complex dies, one L2 each
-constexpr int kLaneMinUnits = 8;        // matrices of one precision needed for two lanes
+#ifndef MUON_LANES
+#define MUON_LANES 2
+#endif
+constexpr int kLanes = MUON_LANES;       // lanes (streams) a large precision group is split into
+constexpr int kLaneMinUnits = 4 * kLanes;    // matrices of one precision needed for that split
 constexpr int64_t kLaneMaxBxTiles = 16384;   // ... and at most this many B X tiles per phase
 
 // XCD-aware order of one phase's tiles.  The dispatcher hands block b to XCD
@@ -304,24 +308,24 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
     }
   }
   // groups: one per NS precision; a precision with many matrices is split
-  // into two lanes of about equal Newton-Schulz work (longest first), which
-  // muon_step runs on two streams so one lane's memory-bound phases overlap
-  // the other's
+  // into lanes of about equal Newton-Schulz work (longest first), which
+  // muon_step runs on separate streams so one lane's ramp-up and tail
+  // overlap another's tiles
   for (int f = 0; f < 2; ++f) {
     std::vector<int> ids;
     for (size_t k = 0; k < plan.units.size(); ++k)
       if (plan.units[k].f32 == (f == 1)) ids.push_back(int(k));
     if (ids.empty()) continue;
-    // two lanes pay off when a phase is short (a few waves of tiles, so its
-    // ramp and tail are a large share); with very many tiles the second
-    // stream only adds cache contention
+    // lanes pay off when a phase is short (a few waves of tiles, so its
+    // ramp and tail are a large share); with very many tiles more streams
+    // only add cache contention
     int64_t bx_tiles = 0;
     for (int k : ids) {
       const UnitPlan& u = plan.units[k];
       const int tx = u.f32 ? kTileF32 : kTileBxBf16;
       bx_tiles += int64_t(u.mp / tx) * (u.np / tx);
     }
-    const int lanes = ids.size() >= size_t(kLaneMinUnits) && bx_tiles <= kLaneMaxBxTiles ? 2 : 1;
+    const int lanes = ids.size() >= size_t(kLaneMinUnits) && bx_tiles <= kLaneMaxBxTiles ? kLanes : 1;
     auto cost = [&](int k) {
       const UnitPlan& u = plan.units[k];
       return double(u.mp) * u.mp * (u.mp + 3.0 * u.np);
@@ -520,8 +524,11 @@ struct muon_handle_s {
   uint8_t* ws = nullptr;
   std::vector<uint8_t> meta;  // host copy of the uploaded descriptors (kept for the async copy)
   hipStream_t last_stream = nullptr;
-  hipStream_t lane_stream = nullptr;                 // second lane (created when the plan has one)
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  std::vector<hipStream_t> lane_streams;              // lanes 1.. (created when the plan has them)
+  std::vector<hipEvent_t> ev_joins;                   // one per lane stream
+  hipStream_t aux_stream = nullptr;                   // AdamW beside the Muon phases
+  hipEvent_t ev_aux = nullptr, ev_adam = nullptr;
+  hipEvent_t ev_fork = nullptr;
   std::vector<hipEvent_t> events;
   std::vector<std::string> phase_names;
 };
@@ -539,40 +546,61 @@ muon_status_t enqueue_step(muon_handle_t h, float lr, hipStream_t s, std::vector
     return hipEventRecord((*ev)[ek++], s) == hipSuccess;
   };
   if (!mark()) return fail(MUON_ERR_HIP, "hipEventRecord failed");
-  if (!plan.adam_tasks.empty()) {
-    AdamState* st = reinterpret_cast<AdamState*>(h->ws + plan.off_adam_state);
-    hipError_t e = launch_adam_tick(st, hp.adam_beta1, hp.adam_beta2, s);
-    AdamParams ap{hp.adam_lr, hp.adam_beta1, hp.adam_beta2, hp.adam_eps, hp.adam_weight_decay, st,
-                  reinterpret_cast<uint32_t*>(h->ws + plan.off_flags)};
-    if (e == hipSuccess)
-      e = launch_adamw(reinterpret_cast<const AdamDev*>(h->ws + plan.off_adam_dev),
-                       reinterpret_cast<const AdamTask*>(h->ws + plan.off_adam_tasks), int(plan.adam_tasks.size()),
-                       ap, s);
-    if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("adamw launch: ") + hipGetErrorString(e));
-  }
   if (!plan.apply.empty()) {
     hipError_t e = launch_precond_apply(reinterpret_cast<const PrecondDev*>(h->ws + plan.off_pdev),
                                         reinterpret_cast<const ApplyTask*>(h->ws + plan.off_apply),
                                         int(plan.apply.size()), s);
     if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("precond apply launch: ") + hipGetErrorString(e));
   }
-  // Two lanes: the second lane's groups run on the handle's second stream,
-  // forked from `s` here and joined back into it at the end (also under
-  // graph capture).  The timed variant keeps everything on `s`, in order.
-  const bool fork = !ev && h->lane_stream != nullptr;
+  // Lanes: the groups of lane l > 0 run on the handle's stream l, and the
+  // AdamW launches on its auxiliary stream, all forked from `s` here (after
+  // the preconditioner, which the momentum phase reads) and joined back into
+  // it at the end (also under graph capture).  The timed variant keeps
+  // everything on `s`, in order (AdamW first).
+  const bool fork = !ev && (!h->lane_streams.empty() || h->aux_stream != nullptr);
   if (fork) {
-    if (hipEventRecord(h->ev_fork, s) != hipSuccess || hipStreamWaitEvent(h->lane_stream, h->ev_fork, 0) != hipSuccess)
+    if (hipEventRecord(h->ev_fork, s) != hipSuccess) return fail(MUON_ERR_HIP, "lane fork failed");
+    for (hipStream_t ls : h->lane_streams)
+      if (hipStreamWaitEvent(ls, h->ev_fork, 0) != hipSuccess) return fail(MUON_ERR_HIP, "lane fork failed");
+    if (h->aux_stream && hipStreamWaitEvent(h->aux_stream, h->ev_fork, 0) != hipSuccess)
       return fail(MUON_ERR_HIP, "lane fork failed");
   }
+  auto launch_adam = [&](hipStream_t as) -> muon_status_t {
+    AdamState* st = reinterpret_cast<AdamState*>(h->ws + plan.off_adam_state);
+    hipError_t e = launch_adam_tick(st, hp.adam_beta1, hp.adam_beta2, as);
+    AdamParams ap{hp.adam_lr, hp.adam_beta1, hp.adam_beta2, hp.adam_eps, hp.adam_weight_decay, st,
+                  reinterpret_cast<uint32_t*>(h->ws + plan.off_flags)};
+    if (e == hipSuccess)
+      e = launch_adamw(reinterpret_cast<const AdamDev*>(h->ws + plan.off_adam_dev),
+                       reinterpret_cast<const AdamTask*>(h->ws + plan.off_adam_tasks), int(plan.adam_tasks.size()),
+                       ap, as);
+    if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("adamw launch: ") + hipGetErrorString(e));
+    return MUON_OK;
+  };
+  // AdamW is HBM-bound like the momentum phase: on its own stream it starts
+  // once the first lane's momentum launch is done, beside the MFMA phases
+  const bool adam_aside = fork && h->aux_stream != nullptr && !plan.adam_tasks.empty();
+  if (!plan.adam_tasks.empty() && !adam_aside) {
+    const muon_status_t st = launch_adam(s);
+    if (st != MUON_OK) return st;
+  }
+  bool adam_pending = adam_aside;
   for (const Group& g : plan.groups) {
     if (g.units.empty()) continue;
-    const hipStream_t gs = fork && g.lane == 1 ? h->lane_stream : s;
+    const hipStream_t gs = fork && g.lane > 0 ? h->lane_streams[g.lane - 1] : s;
     const UnitDev* units = reinterpret_cast<const UnitDev*>(h->ws + g.off_units);
     K1Params k1{hp.momentum, hp.nesterov, hp.momentum_form == MUON_MOM_SGD,
                 reinterpret_cast<uint32_t*>(h->ws + plan.off_flags)};
     hipError_t e = launch_momentum(g.f32, units, reinterpret_cast<const EwTask*>(h->ws + g.off_ew),
                                    int(g.ew.size()), k1, gs);
     if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("momentum launch: ") + hipGetErrorString(e));
+    if (adam_pending && g.lane == 0) {
+      if (hipEventRecord(h->ev_adam, gs) != hipSuccess || hipStreamWaitEvent(h->aux_stream, h->ev_adam, 0) != hipSuccess)
+        return fail(MUON_ERR_HIP, "adamw stream wait failed");
+      const muon_status_t st = launch_adam(h->aux_stream);
+      if (st != MUON_OK) return st;
+      adam_pending = false;
+    }
     for (int it = 0; it < hp.ns_steps; ++it) {
       GemmParams gp{hp.ns_a, hp.ns_b, hp.ns_c, hp.eps, it == 0, it == hp.ns_steps - 1, it & 1, 0,
                     lr, hp.weight_decay};
@@ -592,8 +620,17 @@ muon_status_t enqueue_step(muon_handle_t h, float lr, hipStream_t s, std::vector
       if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("update launch: ") + hipGetErrorString(e));
     }
   }
+  if (adam_pending) {
+    const muon_status_t st = launch_adam(h->aux_stream);
+    if (st != MUON_OK) return st;
+  }
   if (fork) {
-    if (hipEventRecord(h->ev_join, h->lane_stream) != hipSuccess || hipStreamWaitEvent(s, h->ev_join, 0) != hipSuccess)
+    for (size_t l = 0; l < h->lane_streams.size(); ++l)
+      if (hipEventRecord(h->ev_joins[l], h->lane_streams[l]) != hipSuccess ||
+          hipStreamWaitEvent(s, h->ev_joins[l], 0) != hipSuccess)
+        return fail(MUON_ERR_HIP, "lane join failed");
+    if (h->aux_stream && (hipEventRecord(h->ev_aux, h->aux_stream) != hipSuccess ||
+                          hipStreamWaitEvent(s, h->ev_aux, 0) != hipSuccess))
       return fail(MUON_ERR_HIP, "lane join failed");
   }
   h->last_stream = s;
@@ -640,13 +677,13 @@ std::string plan_json(const Plan& plan, const muon_hparams_t& hp) {
                 "\"launch_order\":[", plan.apply.size(), plan.adam_tensors.size(), plan.adam_tasks.size());
   s += buf;
   first = true;
-  if (!plan.adam_tasks.empty()) {
-    s += "\"adam_tick\",\"adamw\"";
+  if (!plan.apply.empty()) {
+    s += "\"precond_apply\"";
     first = false;
   }
-  if (!plan.apply.empty()) {
+  if (!plan.adam_tasks.empty()) {
     if (!first) s += ",";
-    s += "\"precond_apply\"";
+    s += "\"adam_tick\",\"adamw\"";
     first = false;
   }
   for (const Group& g : plan.groups) {
@@ -766,24 +803,38 @@ muon_status_t muon_init(muon_handle_t* out, const muon_tensor_t* tensors, int32_
     return fail(MUON_ERR_HIP, std::string("workspace initialisation: ") + hipGetErrorString(e));
   }
   h->last_stream = s;
-  bool two_lanes = false;
-  for (const Group& g : h->plan.groups) two_lanes |= g.lane == 1;
-  if (two_lanes) {
-    e = hipStreamCreateWithFlags(&h->lane_stream, hipStreamNonBlocking);   // default priority
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming);
+  int max_lane = 0;
+  for (const Group& g : h->plan.groups) max_lane = std::max(max_lane, g.lane);
+  const bool aux = !h->plan.adam_tasks.empty() && !h->plan.units.empty();
+  if (max_lane > 0 || aux) {
+    e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);
+    if (aux && e == hipSuccess) e = hipStreamCreateWithFlags(&h->aux_stream, hipStreamNonBlocking);
+    if (aux && e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_aux, hipEventDisableTiming);
+    if (aux && e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_adam, hipEventDisableTiming);
+    for (int l = 0; l < max_lane && e == hipSuccess; ++l) {
+      hipStream_t ls = nullptr;
+      hipEvent_t ej = nullptr;
+      e = hipStreamCreateWithFlags(&ls, hipStreamNonBlocking);   // default priority
+      if (e == hipSuccess) h->lane_streams.push_back(ls);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&ej, hipEventDisableTiming);
+      if (e == hipSuccess) h->ev_joins.push_back(ej);
+    }
     if (e != hipSuccess) {
       if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
-      if (h->lane_stream) (void)hipStreamDestroy(h->lane_stream);
+      if (h->ev_aux) (void)hipEventDestroy(h->ev_aux);
+      if (h->ev_adam) (void)hipEventDestroy(h->ev_adam);
+      if (h->aux_stream) (void)hipStreamDestroy(h->aux_stream);
+      for (hipEvent_t ej : h->ev_joins) (void)hipEventDestroy(ej);
+      for (hipStream_t ls : h->lane_streams) (void)hipStreamDestroy(ls);
       delete h;
-      return fail(MUON_ERR_HIP, std::string("second lane stream: ") + hipGetErrorString(e));
+      return fail(MUON_ERR_HIP, std::string("lane streams: ") + hipGetErrorString(e));
     }
   }
-  if (!h->plan.adam_tasks.empty()) h->phase_names.push_back("adamw");
   if (!h->plan.apply.empty()) h->phase_names.push_back("precond_apply");
+  if (!h->plan.adam_tasks.empty()) h->phase_names.push_back("adamw");
   for (const Group& g : h->plan.groups) {
     if (g.units.empty()) continue;
-    const std::string dt = std::string(g.f32 ? "/f32" : "/bf16") + (g.lane ? "@2" : "");
+    const std::string dt = std::string(g.f32 ? "/f32" : "/bf16") + (g.lane ? "@" + std::to_string(g.lane + 1) : "");
     h->phase_names.push_back("momentum" + dt);
     for (int it = 0; it < hp->ns_steps; ++it) {
       h->phase_names.push_back("gram" + dt + "#" + std::to_string(it + 1));
@@ -951,13 +1002,20 @@ muon_status_t muon_get_flags(muon_handle_t h, void* stream, int32_t reset, uint3
 muon_status_t muon_destroy(muon_handle_t h) {
   if (!h) return MUON_OK;
   hipError_t e = hipStreamSynchronize(h->last_stream);
-  if (h->lane_stream) {
-    const hipError_t e2 = hipStreamSynchronize(h->lane_stream);
+  for (hipStream_t ls : h->lane_streams) {
+    const hipError_t e2 = hipStreamSynchronize(ls);
     if (e == hipSuccess) e = e2;
-    (void)hipEventDestroy(h->ev_fork);
-    (void)hipEventDestroy(h->ev_join);
-    (void)hipStreamDestroy(h->lane_stream);
+    (void)hipStreamDestroy(ls);
   }
+  if (h->aux_stream) {
+    const hipError_t e2 = hipStreamSynchronize(h->aux_stream);
+    if (e == hipSuccess) e = e2;
+    (void)hipStreamDestroy(h->aux_stream);
+  }
+  for (hipEvent_t ej : h->ev_joins) (void)hipEventDestroy(ej);
+  if (h->ev_aux) (void)hipEventDestroy(h->ev_aux);
+  if (h->ev_adam) (void)hipEventDestroy(h->ev_adam);
+  if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
   for (hipEvent_t ev : h->events) (void)hipEventDestroy(ev);
   delete h;
   if (e != hipSuccess) return fail(MUON_ERR_HIP, std::string("destroy: ") + hipGetErrorString(e));

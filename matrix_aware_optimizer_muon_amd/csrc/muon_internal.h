@@ -9,18 +9,12 @@
 namespace muon {
 
 // Output tiles of the Newton-Schulz GEMM phases.  bf16 matrices use 128x128
-// tiles (4 waves of 64x64, two blocks per CU).  B X can be built with
-// 256x256 tiles (MUON_TILE_BX_BF16=256: 8 waves of 128x64, one block per CU,
-// half the operand bytes per flop); that helps single large matrices but
-// not the GPT-2-sized sets, whose tile counts it quantises.  float32
-// matrices use 64x64 tiles everywhere.  Every NS buffer is zero-padded to a multiple of the
+// tiles (8 waves of 64x32, two blocks per CU); float32 matrices use 64x64
+// tiles everywhere.  Every NS buffer is zero-padded to a multiple of the
 // largest tile of its precision (kPadBf16 / kTileF32) in both dimensions;
 // zero padding is exact under X X^T, A A and B X.
-#ifndef MUON_TILE_BX_BF16
-#define MUON_TILE_BX_BF16 128
-#endif
 constexpr int kTileGramBf16 = 128;
-constexpr int kTileBxBf16 = MUON_TILE_BX_BF16;
+constexpr int kTileBxBf16 = 128;
 constexpr int kPadBf16 = kTileBxBf16 > kTileGramBf16 ? kTileBxBf16 : kTileGramBf16;
 constexpr int kTileF32 = 64;
 // Edge of the square tiles of the elementwise phases (momentum, update).
