@@ -74,13 +74,19 @@ template <int PH> struct Cfg<true, PH> {         // float32, all phases
 
 // LDS layout of a stage.  Tiles are stored unpadded as rows of 16-byte
 // chunks, with the chunk order of each row XOR-swizzled so the MFMA
-// fragment reads are free of bank conflicts:
-//   K-contiguous tile (row = M or N index, CPR chunks of K): chunk c of row
-//     r sits at position c ^ (r % 8);
+// fragment reads are free of bank conflicts.  gfx950's LDS serves 256 bytes
+// per clock, i.e. a 16-byte read of 16 lanes at a time:
+//   K-contiguous tile (row = M or N index, 8 chunks of K, 128 bytes): chunk
+//     c of row r sits at position c ^ ((r / 2) % 8).  Sixteen consecutive
+//     rows read at one chunk then cover the 16 distinct 16-byte slots of a
+//     256-byte bank line (the two rows sharing a line differ in r % 2, and
+//     the eight of one parity in (r / 2) % 8); c ^ (r % 8) would put rows r
+//     and r + 8 in one slot (a 2-way conflict, measured with the LDS bank
+//     conflict counter);
 //   K-major tile of B X (row = k, 16 chunks of columns): chunk c of row k
 //     sits at position c ^ 4 (k % 4), which spreads the four rows a
 //     transposing read touches over distinct banks.
-__device__ __forceinline__ int swz_kc(int r, int c) { return c ^ (r & 7); }
+__device__ __forceinline__ int swz_kc(int r, int c) { return c ^ ((r >> 1) & 7); }
 __device__ __forceinline__ int swz_km(int k, int c) { return c ^ ((k & 3) << 2); }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
