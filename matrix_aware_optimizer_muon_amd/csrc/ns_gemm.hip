@@ -39,13 +39,18 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(1))) const u32x4_t gu32x4_t;     // global memory
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;       // LDS
 
-// Tile configuration per precision and phase.  BT: square output tile;
+// Tile configuration per precision and phase (the defaults are the fastest
+// measured; 32-deep stages in a 3- or 4-stage ring, MUON_BK_BF16=32, were 9 %
+// slower on every workload).  BT: square output tile;
 // NWM x NWN waves, each owning a (BT/NWM) x (BT/NWN) block of 32x32 MFMA
 // tiles; BK: K depth of one LDS stage; NS: stages in the LDS ring (NS-1 in
 // flight while one is consumed); OCC: blocks per CU the registers and LDS
 // allow.
 #ifndef MUON_NS_BF16
 #define MUON_NS_BF16 2
+#endif
+#ifndef MUON_BK_BF16
+#define MUON_BK_BF16 64
 #endif
 #ifndef MUON_BX_NWN
 #define MUON_BX_NWN 4
@@ -59,13 +64,13 @@ template <bool F32, int PH> struct Cfg;
 #endif
 template <int PH> struct Cfg<false, PH> {        // bf16, Gram and square
   using E = uint16_t;
-  static constexpr int BT = kTileGramBf16, NWM = 2, NWN = MUON_G_NWN, BK = 64, NS = MUON_NS_BF16;
-  static constexpr int OCC = NS <= 2 ? 2 : 1;
+  static constexpr int BT = kTileGramBf16, NWM = 2, NWN = MUON_G_NWN, BK = MUON_BK_BF16, NS = MUON_NS_BF16;
+  static constexpr int OCC = NS * BK <= 128 ? 2 : 1;    // ring of 2 x 32 KB or 4 x 16 KB: two blocks per CU
 };
 template <> struct Cfg<false, kBX> {             // bf16, B X
   using E = uint16_t;
-  static constexpr int BT = kTileBxBf16, NWM = 2, NWN = MUON_BX_NWN, BK = 64, NS = MUON_NS_BF16;
-  static constexpr int OCC = NS <= 2 ? MUON_BX_OCC : 1;
+  static constexpr int BT = kTileBxBf16, NWM = 2, NWN = MUON_BX_NWN, BK = MUON_BK_BF16, NS = MUON_NS_BF16;
+  static constexpr int OCC = NS * BK <= 128 ? MUON_BX_OCC : 1;
 };
 template <int PH> struct Cfg<true, PH> {         // float32, all phases
   using E = float;
@@ -77,7 +82,8 @@ template <int PH> struct Cfg<true, PH> {         // float32, all phases
 // fragment reads are free of bank conflicts.  gfx950's LDS serves 256 bytes
 // per clock, i.e. a 16-byte read of 16 lanes at a time:
 //   K-contiguous tile (row = M or N index, 8 chunks of K, 128 bytes): chunk
-//     c of row r sits at position c ^ ((r / 2) % 8).  Sixteen consecutive
+//     c of row r sits at position c ^ ((r / 2) % 8) (with 32-deep stages,
+//     rows of 4 chunks: c ^ ((r / 4) % 4)).  Sixteen consecutive
 //     rows read at one chunk then cover the 16 distinct 16-byte slots of a
 //     256-byte bank line (the two rows sharing a line differ in r % 2, and
 //     the eight of one parity in (r / 2) % 8); c ^ (r % 8) would put rows r
@@ -86,7 +92,12 @@ template <int PH> struct Cfg<true, PH> {         // float32, all phases
 //   K-major tile of B X (row = k, 16 chunks of columns): chunk c of row k
 //     sits at position c ^ 4 (k % 4), which spreads the four rows a
 //     transposing read touches over distinct banks.
-__device__ __forceinline__ int swz_kc(int r, int c) { return c ^ ((r >> 1) & 7); }
+template <int CPR>
+__device__ __forceinline__ int swz_kc(int r, int c) {
+  static_assert(CPR == 8 || CPR == 4, "K rows of 8 or 4 chunks");
+  if constexpr (CPR == 8) return c ^ ((r >> 1) & 7);
+  else return c ^ ((r >> 2) & 3);   // 64-byte rows: four share a bank line
+}
 __device__ __forceinline__ int swz_km(int k, int c) { return c ^ ((k & 3) << 2); }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -168,13 +179,13 @@ __device__ __forceinline__ void mma_stage(const E* la, const E* lb, f32x16_t (&a
 #pragma unroll
       for (int i = 0; i < NBM; ++i) {
         const int r = wm * WTM + i * 32 + (lane & 31);
-        fa[i] = *reinterpret_cast<const bf16x8_t*>(&la[r * BK + swz_kc(r, kc) * 8]);
+        fa[i] = *reinterpret_cast<const bf16x8_t*>(&la[r * BK + swz_kc<BK / 8>(r, kc) * 8]);
       }
 #pragma unroll
       for (int j = 0; j < NBN; ++j) {
         if constexpr (!KMAJOR_B) {
           const int r = wn * WTN + j * 32 + (lane & 31);
-          fb[j] = *reinterpret_cast<const bf16x8_t*>(&lb[r * BK + swz_kc(r, kc) * 8]);
+          fb[j] = *reinterpret_cast<const bf16x8_t*>(&lb[r * BK + swz_kc<BK / 8>(r, kc) * 8]);
         } else {
           // lane group g = lane/16 covers columns 16*(g%2).. and k-half g/2;
           // lane r of the group points at row k + r/4, columns 4*(r%4)..
@@ -204,13 +215,13 @@ __device__ __forceinline__ void mma_stage(const E* la, const E* lb, f32x16_t (&a
 #pragma unroll
       for (int i = 0; i < NBM; ++i) {
         const int r = wm * WTM + i * 32 + (lane & 31);
-        fa[i] = *reinterpret_cast<const f32x4_t*>(&la[r * BK + swz_kc(r, kc) * 4]);
+        fa[i] = *reinterpret_cast<const f32x4_t*>(&la[r * BK + swz_kc<BK / 4>(r, kc) * 4]);
       }
 #pragma unroll
       for (int j = 0; j < NBN; ++j) {
         if constexpr (!KMAJOR_B) {
           const int r = wn * WTN + j * 32 + (lane & 31);
-          fb[j] = *reinterpret_cast<const f32x4_t*>(&lb[r * BK + swz_kc(r, kc) * 4]);
+          fb[j] = *reinterpret_cast<const f32x4_t*>(&lb[r * BK + swz_kc<BK / 4>(r, kc) * 4]);
         } else {
           const int col = wn * WTN + j * 32 + (lane & 31);
 #pragma unroll
@@ -288,9 +299,9 @@ __device__ __forceinline__ void capture_atile(const E* la, int kt, int kt_cap, i
       const int sg = lane + 64 * q;
       const int r = wm * WTM + pi * 32 + sg / SEGS;            // tile row = A-operand row
       const int k = (wn * WTN + (sg % SEGS) * 8) % BK;         // column inside the K step
-      pre0[pi][q] = *reinterpret_cast<const u32x4_t*>(&la[r * BK + swz_kc(r, k / EPE) * EPE]);
+      pre0[pi][q] = *reinterpret_cast<const u32x4_t*>(&la[r * BK + swz_kc<BK / EPE>(r, k / EPE) * EPE]);
       if constexpr (F32)
-        pre1[pi][q] = *reinterpret_cast<const u32x4_t*>(&la[r * BK + swz_kc(r, k / EPE + 1) * EPE]);
+        pre1[pi][q] = *reinterpret_cast<const u32x4_t*>(&la[r * BK + swz_kc<BK / EPE>(r, k / EPE + 1) * EPE]);
     }
 }
 
@@ -315,7 +326,7 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   constexpr int STAGE = 2 * T_ELEMS;               // A tile then B tile
   constexpr int EPP = WTN + 8;                     // epilogue LDS pitch (floats)
   static_assert(NI * NT == T_CH, "tile/thread mismatch");
-  static_assert(CPR == 8 && CPRX == 16, "swizzles assume 8-chunk K rows and 16-chunk K-major rows");
+  static_assert((CPR == 8 || CPR == 4) && CPRX == 16, "swizzles assume 8- or 4-chunk K rows and 16-chunk K-major rows");
   static_assert(NWM * NWN * 32 * EPP * 4 <= NS * STAGE * static_cast<int>(sizeof(E)),
                 "epilogue staging must fit in the operand LDS");
 
@@ -358,12 +369,12 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   for (int i = 0; i < NI; ++i) {
     const int c = (wave * NI + i) * 64 + lane;       // chunk position in the tile
     const int ar = c / CPR;
-    aoff[i] = static_cast<uint32_t>((ar * lda_g + swz_kc(ar, c % CPR) * EPE) * sizeof(E));
+    aoff[i] = static_cast<uint32_t>((ar * lda_g + swz_kc<CPR>(ar, c % CPR) * EPE) * sizeof(E));
     if constexpr (KMAJOR_B) {
       const int k = c / CPRX;
       boff[i] = static_cast<uint32_t>((k * ldb_g + swz_km(k, c % CPRX) * EPE) * sizeof(E));
     } else {
-      boff[i] = static_cast<uint32_t>((ar * ldb_g + swz_kc(ar, c % CPR) * EPE) * sizeof(E));
+      boff[i] = static_cast<uint32_t>((ar * ldb_g + swz_kc<CPR>(ar, c % CPR) * EPE) * sizeof(E));
     }
   }
   const uint32_t ring0 = lds_addr(smem);
