@@ -11,11 +11,13 @@
 //                    ns_steps == 0 only (otherwise the last Newton-Schulz
 //                    phase applies the update).
 //
-// Both walk 64x64 tiles of each matrix: every thread owns two 8-element row
-// segments, so global traffic is 16-byte vector accesses along rows; the
-// orientation swap needed for tall matrices goes through an LDS tile.  The
-// partial sums are folded later, in a fixed order, by the first Newton-
-// Schulz phase, so no block here waits on another.
+// Both walk tiles of 4096 elements in which every thread owns two 8-element
+// row segments, so global traffic is 16-byte vector accesses along rows:
+// 16 x 256 tiles for units whose X is U (a wave covers two 256-element runs
+// of one row each), 64 x 64 tiles for units whose X is U^T, whose
+// orientation swap goes through an LDS tile.  The partial sums are folded
+// later, in a fixed order, by the first Newton-Schulz phase, so no block
+// here waits on another.
 #include "device_common.h"
 #include "muon_internal.h"
 
@@ -50,7 +52,9 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const UnitDev* __res
 
   const EwTask t = tasks[blockIdx.x];
   const UnitDev& u = units[t.unit];
-  const int r0 = t.tr * kEwTile, c0 = t.tc * kEwTile;
+  const bool left = u.side == kLeft;
+  const int r0 = t.tr * (left ? kEwRows : kEwTile), c0 = t.tc * (left ? kEwCols : kEwTile);
+  const int seg_sh = left ? 5 : 3;                   // log2 of 8-element segments per tile row
   const int rows = u.rows, cols = u.cols;
   const float mu = p.mu;
   const float one_m = 1.0f - mu;
@@ -60,7 +64,7 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const UnitDev* __res
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int s = threadIdx.x + kThreads * q;
-    const int lr = s >> 3, lc = (s & 7) * 8;
+    const int lr = s >> seg_sh, lc = (s & ((1 << seg_sh) - 1)) * 8;
     const int i = r0 + lr, j0 = c0 + lc;
     float uv[8];
 #pragma unroll
@@ -89,15 +93,16 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const UnitDev* __res
       ss = fmaf(uv[e], uv[e], ss);
       bad |= !isfinite(uv[e]);
     }
-    if (u.side == kLeft) {
-      // X = U: rows of the unit stay rows (padding gets zeros)
-      store_seg<F32>(u.xh[0], u.xl, u.np, i, j0, uv);
+    if (left) {
+      // X = U: rows of the unit stay rows (padding inside the tile gets
+      // zeros; a 256-wide tile may reach past the padded width np)
+      if (j0 < u.np) store_seg<F32>(u.xh[0], u.xl, u.np, i, j0, uv);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) tile[lr][lc + e] = uv[e];
     }
   }
-  if (u.side == kRight) {
+  if (!left) {
     // X = U^T: column segments of the tile become row segments of X
     __syncthreads();
 #pragma unroll
@@ -141,7 +146,9 @@ __global__ __launch_bounds__(kThreads) void update_kernel(const UnitDev* __restr
   __shared__ float red[4];
   const EwTask t = tasks[blockIdx.x];
   const UnitDev& u = units[t.unit];
-  const int r0 = t.tr * kEwTile, c0 = t.tc * kEwTile;
+  const bool left = u.side == kLeft;
+  const int r0 = t.tr * (left ? kEwRows : kEwTile), c0 = t.tc * (left ? kEwCols : kEwTile);
+  const int seg_sh = left ? 5 : 3;                   // log2 of 8-element segments per tile row
   const int rows = u.rows;
   // with no Newton-Schulz iteration O is the normalised U itself
   const float inv = unit_inv_norm(u.partials, u.k1_ntiles, p.eps, red);
@@ -166,11 +173,11 @@ __global__ __launch_bounds__(kThreads) void update_kernel(const UnitDev* __restr
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int s = threadIdx.x + kThreads * q;
-    const int lr = s >> 3, lc = (s & 7) * 8;
+    const int lr = s >> seg_sh, lc = (s & ((1 << seg_sh) - 1)) * 8;
     const int i = r0 + lr, j0 = c0 + lc;
-    if (i >= rows) continue;
+    if (i >= rows || j0 >= u.cols) continue;
     float o[8];
-    if (u.side == kRight) {
+    if (!left) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = tile[lr][lc + e];
     } else {

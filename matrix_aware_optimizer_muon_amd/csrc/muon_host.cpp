@@ -299,8 +299,9 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
       u.mp = int(round_up(u.m, T));
       u.np = int(round_up(u.n, T));
       u.lr_scale = shape_scale(h, t.cols, hp->scale_mode) * t.lr_mult;
-      u.k1_tr = int((h + kEwTile - 1) / kEwTile);
-      u.k1_tc = int((t.cols + kEwTile - 1) / kEwTile);
+      const int ewr = u.side == kLeft ? kEwRows : kEwTile, ewc = u.side == kLeft ? kEwCols : kEwTile;
+      u.k1_tr = int((h + ewr - 1) / ewr);
+      u.k1_tc = int((t.cols + ewc - 1) / ewc);
       u.k1_ntiles = u.k1_tr * u.k1_tc;
       u.k1_tile0 = plan.total_k1_tiles;
       plan.total_k1_tiles += u.k1_ntiles;

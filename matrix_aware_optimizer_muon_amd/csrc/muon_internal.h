@@ -17,8 +17,12 @@ constexpr int kTileGramBf16 = 128;
 constexpr int kTileBxBf16 = 128;
 constexpr int kPadBf16 = kTileBxBf16 > kTileGramBf16 ? kTileBxBf16 : kTileGramBf16;
 constexpr int kTileF32 = 64;
-// Edge of the square tiles of the elementwise phases (momentum, update).
+// Tiles of the elementwise phases (momentum, update).  A unit whose X is U
+// itself (rows <= cols) is walked in kEwRows x kEwCols tiles along its rows,
+// so each wave reads and writes runs of 256 consecutive elements; a unit
+// whose X is U^T is walked in kEwTile x kEwTile tiles transposed through LDS.
 constexpr int kEwTile = 64;
+constexpr int kEwRows = 16, kEwCols = 256;
 // bf16 matrices whose short side is below this run their Newton-Schulz
 // iteration on the float32 path: at such sizes the bf16 iteration's own
 // rounding error approaches 2e-2 relative, and the float32 path costs
@@ -53,7 +57,7 @@ struct UnitDev {
   int32_t pad3;
 };
 
-struct EwTask { int32_t unit, tr, tc, local; };      // 64x64 tile of a unit
+struct EwTask { int32_t unit, tr, tc, local; };      // tile (tr, tc) of a unit
 struct GemmTask { int32_t unit, ti, tj, pad; };      // output tile (ti, tj)
 
 struct K1Params {
