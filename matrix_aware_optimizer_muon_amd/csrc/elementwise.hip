@@ -43,15 +43,11 @@ __device__ __forceinline__ void store_seg(void* hi, void* lo, int64_t ld, int r,
   }
 }
 
-template <bool F32>
-__global__ __launch_bounds__(kThreads) void momentum_kernel(const UnitDev* __restrict__ units,
-                                                            const EwTask* __restrict__ tasks,
-                                                            K1Params p) {
-  __shared__ float tile[kEwTile][kEwTile + 1];
-  __shared__ float wsum[kThreads / 64];
-
-  const EwTask t = tasks[blockIdx.x];
-  const UnitDev& u = units[t.unit];
+// One tile of the momentum phase; GF32: the gradient is float32 (else
+// bf16), a compile-time choice so the tile's loads are straight-line code.
+template <bool F32, bool GF32>
+__device__ __forceinline__ void momentum_tile(const UnitDev& u, const EwTask& t, const K1Params& p,
+                                              float (*tile)[kEwTile + 1], float* wsum) {
   const bool left = u.side == kLeft;
   const int r0 = t.tr * (left ? kEwRows : kEwTile), c0 = t.tc * (left ? kEwCols : kEwTile);
   const int seg_sh = left ? 5 : 3;                   // log2 of 8-element segments per tile row
@@ -61,33 +57,65 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const UnitDev* __res
   float ss = 0.f;
   bool bad = false;
 
+  // Interior tiles with 16-byte aligned rows take a branch-free path that
+  // issues every load of the thread before the first use, so the load
+  // latency is paid once per tile rather than once per access; edge tiles
+  // go element by element where needed.
+  const bool interior = r0 + (left ? kEwRows : kEwTile) <= rows && c0 + (left ? kEwCols : kEwTile) <= cols &&
+                        u.vec_grad && u.vec_mom;
+  int iq[2], jq[2], lrq[2], lcq[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int s = threadIdx.x + kThreads * q;
-    const int lr = s >> seg_sh, lc = (s & ((1 << seg_sh) - 1)) * 8;
-    const int i = r0 + lr, j0 = c0 + lc;
+    lrq[q] = s >> seg_sh;
+    lcq[q] = (s & ((1 << seg_sh) - 1)) * 8;
+    iq[q] = r0 + lrq[q];
+    jq[q] = c0 + lcq[q];
+  }
+  float g[2][8], m[2][8];
+  if (interior) {
+    ld8_f32(u.mom, static_cast<size_t>(iq[0]) * u.ld_mom + jq[0], m[0]);
+    ld8_f32(u.mom, static_cast<size_t>(iq[1]) * u.ld_mom + jq[1], m[1]);
+    const size_t og0 = static_cast<size_t>(iq[0]) * u.ld_grad + jq[0];
+    const size_t og1 = static_cast<size_t>(iq[1]) * u.ld_grad + jq[1];
+    if constexpr (GF32) {
+      ld8_f32(u.grad, og0, g[0]);
+      ld8_f32(u.grad, og1, g[1]);
+    } else {
+      ld8_bf16(u.grad, og0, g[0]);
+      ld8_bf16(u.grad, og1, g[1]);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g[q][e] = m[q][e] = 0.f;
+      if (iq[q] < rows) {
+        load_row8(u.grad, GF32, u.ld_grad, iq[q], jq[q], cols, u.vec_grad, g[q]);
+        load_row8(u.mom, true, u.ld_mom, iq[q], jq[q], cols, u.vec_mom, m[q]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int i = iq[q], j0 = jq[q], lr = lrq[q], lc = lcq[q];
     float uv[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) uv[e] = 0.f;
-    if (i < rows) {
-      float g[8], m[8];
-      load_row8(u.grad, u.grad_f32, u.ld_grad, i, j0, cols, u.vec_grad, g);
-      load_row8(u.mom, true, u.ld_mom, i, j0, cols, u.vec_mom, m);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float mn, un;
-        if (p.sgd_form) {
-          mn = fmaf(mu, m[e], g[e]);
-          un = p.nesterov ? fmaf(mu, mn, g[e]) : mn;
-        } else {
-          mn = fmaf(mu, m[e], one_m * g[e]);
-          un = p.nesterov ? fmaf(mu, mn, one_m * g[e]) : mn;
-        }
-        m[e] = mn;
-        uv[e] = (j0 + e < cols) ? un : 0.f;
+    for (int e = 0; e < 8; ++e) {
+      float mn, un;
+      if (p.sgd_form) {
+        mn = fmaf(mu, m[q][e], g[q][e]);
+        un = p.nesterov ? fmaf(mu, mn, g[q][e]) : mn;
+      } else {
+        mn = fmaf(mu, m[q][e], one_m * g[q][e]);
+        un = p.nesterov ? fmaf(mu, mn, one_m * g[q][e]) : mn;
       }
-      store_row8(u.mom, true, u.ld_mom, i, j0, cols, u.vec_mom, m);
+      m[q][e] = mn;
+      uv[e] = (i < rows && j0 + e < cols) ? un : 0.f;
     }
+    if (interior) st8_f32(u.mom, static_cast<size_t>(i) * u.ld_mom + j0, m[q]);
+    else if (i < rows) store_row8(u.mom, true, u.ld_mom, i, j0, cols, u.vec_mom, m[q]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       ss = fmaf(uv[e], uv[e], ss);
@@ -123,6 +151,18 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const UnitDev* __res
   if (__any(bad) && lane == 0) atomicOr(p.flags, 1u);
   __syncthreads();
   if (threadIdx.x == 0) gst(u.partials + t.local, (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]));
+}
+
+template <bool F32>
+__global__ __launch_bounds__(kThreads) void momentum_kernel(const UnitDev* __restrict__ units,
+                                                            const EwTask* __restrict__ tasks,
+                                                            K1Params p) {
+  __shared__ float tile[kEwTile][kEwTile + 1];
+  __shared__ float wsum[kThreads / 64];
+  const EwTask t = tasks[blockIdx.x];
+  const UnitDev& u = units[t.unit];
+  if (u.grad_f32) momentum_tile<F32, true>(u, t, p, tile, wsum);
+  else momentum_tile<F32, false>(u, t, p, tile, wsum);
 }
 
 // X master of the stand-alone update (ns_steps == 0: the iterate the
