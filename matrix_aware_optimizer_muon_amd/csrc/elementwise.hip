@@ -133,14 +133,16 @@ __device__ __forceinline__ void momentum_tile(const UnitDev& u, const EwTask& t,
   if (!left) {
     // X = U^T: column segments of the tile become row segments of X
     __syncthreads();
+    // eight lanes cover one X row (a 64-element run); LDS column reads at
+    // pitch kEwTile + 1 put the 64 lanes in distinct banks
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int s = threadIdx.x + kThreads * q;
-      const int lc = s & (kEwTile - 1), rseg = s >> 6;
+      const int xr = s >> 3, xs = s & 7;
       float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = tile[rseg * 8 + e][lc];
-      store_seg<F32>(u.xh[0], u.xl, u.np, c0 + lc, r0 + rseg * 8, v);
+      for (int e = 0; e < 8; ++e) v[e] = tile[xs * 8 + e][xr];
+      store_seg<F32>(u.xh[0], u.xl, u.np, c0 + xr, r0 + xs * 8, v);
     }
   }
 
