@@ -201,3 +201,20 @@ __device__ __forceinline__ void update_w8(const UnitDev& u, int i, int j0, const
 }
 
 }  // namespace muon
+
+namespace muon {
+
+// update_w8 for a bf16 weight segment that was loaded ahead (whole segment
+// inside the matrix, 16-byte aligned rows): the same float32 arithmetic and
+// one rounding, so the result is bit-identical to update_w8's.
+__device__ __forceinline__ void update_w8_loaded(const UnitDev& u, int i, int j0, const float* o, float decay,
+                                                 float step, const u32x4_t& wraw) {
+  float w[8];
+  unpack8_bf16(wraw, w);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) w[e] = w[e] - decay * w[e] - step * o[e];
+  st8_bf16(u.param, static_cast<size_t>(i) * u.ld_param + j0, w);
+  if (u.update_out) store_row8(u.update_out, true, u.ld_out, i, j0, u.cols, u.vec_out, o);
+}
+
+}  // namespace muon

@@ -439,6 +439,23 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   // paid per tile, not per strip.
   const int row_base = ti * BT + wm * WTM;
   const int col_base = tj * BT + wn * WTN;
+  // In the last iteration the weight segments this lane updates are
+  // requested at the same time (bf16 weights with aligned rows; the
+  // segments are rows of W for a wide unit, columns of the tile for a tall
+  // one, where X column j is weight row j).
+  static_assert(!KMAJOR_B || RITER == WTN * 4 / 64, "row and column passes give a lane equally many segments");
+  u32x4_t wpre[NPRE][RITER];
+  const bool wfast = KMAJOR_B && !F32 && p.last && !u.param_f32 && u.vec_param;
+  auto wseg = [&](int pi, int q, int& wi, int& wj) {
+    const int sg = lane + 64 * q;
+    if (u.side == kLeft) {
+      wi = row_base + pi * 32 + sg / SEGS;
+      wj = col_base + (sg % SEGS) * 8;
+    } else {
+      wi = col_base + sg % WTN;
+      wj = row_base + pi * 32 + (sg / WTN) * 8;
+    }
+  };
   if constexpr (KMAJOR_B && !F32) {
 #pragma unroll
     for (int pi = 0; pi < NBM; ++pi)
@@ -448,6 +465,17 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
         const size_t off = static_cast<size_t>(row_base + pi * 32 + sg / SEGS) * np + col_base + (sg % SEGS) * 8;
         preq[pi][q] = gld<u32x2_t>(static_cast<const int8_t*>(u.xl) + off);
       }
+    if (wfast) {
+#pragma unroll
+      for (int pi = 0; pi < NBM; ++pi)
+#pragma unroll
+        for (int q = 0; q < RITER; ++q) {
+          int wi, wj;
+          wseg(pi, q, wi, wj);
+          if (wi < u.rows && wj + 8 <= u.cols)
+            wpre[pi][q] = gld<u32x4_t>(static_cast<const uint16_t*>(u.param) + static_cast<size_t>(wi) * u.ld_param + wj);
+        }
+    }
   }
 
   // Each wave stages one 32-row strip of its accumulators in its own LDS
@@ -534,7 +562,10 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
             gst(static_cast<int8_t*>(u.xl) + off, lq);
           }
         } else if (u.side == kLeft) {
-          if (gr < u.rows) update_w8(u, gr, gc, v, decay, step);
+          if (gr < u.rows) {
+            if (wfast && gc + 8 <= u.cols) update_w8_loaded(u, gr, gc, v, decay, step, wpre[pi][q]);
+            else update_w8(u, gr, gc, v, decay, step);
+          }
         } else {
           *reinterpret_cast<f32x4_t*>(&ep[row * EPP + cseg * 8]) = f32x4_t{v[0], v[1], v[2], v[3]};
           *reinterpret_cast<f32x4_t*>(&ep[row * EPP + cseg * 8 + 4]) = f32x4_t{v[4], v[5], v[6], v[7]};
@@ -560,7 +591,15 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
           st8<F32>(u.b, static_cast<size_t>(gc) * mp + gr, v);   // B is symmetric off the diagonal tiles
         } else {
           // tall matrix: O[i][j] = X[j][i], so X column gc is weight row gc
-          if (gc < u.rows) update_w8(u, gc, gr, v, decay, step);
+          if (gc < u.rows) {
+            if constexpr (!F32) {
+              if (wfast && gr + 8 <= u.cols) {
+                update_w8_loaded(u, gc, gr, v, decay, step, wpre[pi][q]);
+                continue;
+              }
+            }
+            update_w8(u, gc, gr, v, decay, step);
+          }
         }
       }
     }
