@@ -74,7 +74,7 @@ struct Plan {
   std::vector<int> adam_tensors;     // kind-ADAMW tensors, in tensor order
   std::vector<AdamTask> adam_tasks;
   size_t off_adam_dev = 0, off_adam_tasks = 0, off_adam_state = 0;
-  size_t off_flags = 0, off_partials = 0;
+  size_t off_flags = 0, off_partials = 0, off_norms = 0;
   size_t meta_bytes = 0, total = 0;
   int total_k1_tiles = 0;
   int64_t zero_bytes = 0;  // bytes of NS buffers (zero-filled at init)
@@ -374,6 +374,7 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
   size_t off = 0;
   plan.off_flags = off; off += kAlign;
   plan.off_partials = off; off = align_up(off + sizeof(float) * plan.total_k1_tiles);
+  plan.off_norms = off; off = align_up(off + sizeof(float) * plan.units.size());
   for (Group& g : plan.groups) {
     g.off_units = off; off = align_up(off + sizeof(UnitDev) * g.units.size());
     g.off_ew = off; off = align_up(off + sizeof(EwTask) * g.ew.size());
@@ -456,6 +457,7 @@ std::vector<uint8_t> build_meta(const Plan& plan, const muon_tensor_t* ts, uint8
       d.a = ws + up.off_a;
       d.b = ws + up.off_b;
       d.partials = reinterpret_cast<float*>(ws + plan.off_partials) + up.k1_tile0;
+      d.norm = reinterpret_cast<float*>(ws + plan.off_norms) + g.units[gi];
       d.k1_tile0 = up.k1_tile0;
       d.k1_ntiles = up.k1_ntiles;
       d.lr_scale = up.lr_scale;

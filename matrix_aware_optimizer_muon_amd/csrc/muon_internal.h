@@ -52,6 +52,7 @@ struct UnitDev {
   // one; xl is read and written only by the tile that owns each region.
   void* xh[2]; void* xl; void* a; void* b;
   float* partials;           // one partial sum of squares per momentum tile
+  float* norm;               // 1 / (||U||_F + eps), folded by the first Gram phase
   int32_t k1_tile0, k1_ntiles;
   float lr_scale;            // shape scale * lr_mult
   int32_t pad3;

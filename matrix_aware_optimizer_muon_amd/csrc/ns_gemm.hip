@@ -336,6 +336,10 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   const GemmTask t = tasks[blockIdx.x];
   if (t.unit < 0) return;   // padding of the XCD-interleaved task order
   const UnitDev& u = units[t.unit];
+  // first iteration: B X applies the unit's 1/||U|| that the Gram phase
+  // folded (every Gram block folds the same bits; one stores them); the
+  // load is issued here so its latency hides behind the K loop
+  const float first_scale = PH == kBX && p.first ? gld<float>(u.norm) : 1.f;
   const int mp = u.mp, np = u.np;
   const int ti = t.ti, tj = t.tj;
 
@@ -484,11 +488,14 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   // needed, column segments (mirror tiles of A and B; weight rows of a tall
   // matrix in the last iteration) as 16-byte vector accesses.
   float scale = 1.f;
-  if constexpr (PH == kGram || PH == kBX) {
+  if constexpr (PH == kGram) {
     if (p.first) {
       const float iv = unit_inv_norm(u.partials, u.k1_ntiles, p.eps, red);
-      scale = PH == kGram ? iv * iv : iv;
+      scale = iv * iv;
+      if (ti == 0 && tj == 0 && threadIdx.x == 0) gst(u.norm, iv);   // for the first B X phase
     }
+  } else if constexpr (PH == kBX) {
+    scale = first_scale;
   }
   const bool last = PH == kBX && p.last;
   const bool mirror = PH == kBX ? (last && u.side == kRight) : (ti != tj);
