@@ -151,11 +151,14 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
 
 template <int NA, int NB, typename E>
 __device__ __forceinline__ void issue_stage(const E* ga, const E* gb, const uint32_t (&aoff)[NA],
-                                            const uint32_t (&boff)[NB], uint32_t la, uint32_t lb, int wave) {
+                                            const uint32_t (&boff)[NB], uint32_t la, uint32_t lb, int wave,
+                                            bool with_b) {
 #pragma unroll
   for (int i = 0; i < NA; ++i) dma16(ga, aoff[i], la + (wave * NA + i) * 1024);
+  if (with_b) {
 #pragma unroll
-  for (int i = 0; i < NB; ++i) dma16(gb, boff[i], lb + (wave * NB + i) * 1024);
+    for (int i = 0; i < NB; ++i) dma16(gb, boff[i], lb + (wave * NB + i) * 1024);
+  }
 }
 
 // LDS byte address of a shared-memory pointer.
@@ -382,6 +385,9 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
     }
   }
   const uint32_t ring0 = lds_addr(smem);
+  // diagonal tiles of the Gram and the square read the same rows as both
+  // operands: the stage is loaded once and both fragment reads use it
+  const bool diag = (PH == kGram || PH == kSquare) && ti == tj;
   // advance per K step: along the rows for K-contiguous tiles, down BK rows
   // for the K-major tile
   const size_t a_step = BK;
@@ -419,20 +425,21 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   for (int s = 0; s < NS - 1; ++s) {
     const int sc = min(s, KT - 1);
     issue_stage<NI, NI, E>(pa + sc * a_step, pb + sc * b_step, aoff, boff, ring0 + s * STAGE_B,
-                           ring0 + s * STAGE_B + TILE_B, wave);
+                           ring0 + s * STAGE_B + TILE_B, wave, !diag);
   }
   for (int kt = 0; kt < KT; ++kt) {
-    wait_vmcnt<(NS - 2) * 2 * NI>();
+    if (diag) wait_vmcnt<(NS - 2) * NI>();   // newer stages in flight: NS-2 of one operand each
+    else wait_vmcnt<(NS - 2) * 2 * NI>();
     ring_barrier();
     const int nx = min(kt + NS - 1, KT - 1);
     const uint32_t ls = ring0 + ((kt + NS - 1) % NS) * STAGE_B;
-    issue_stage<NI, NI, E>(pa + nx * a_step, pb + nx * b_step, aoff, boff, ls, ls + TILE_B, wave);
+    issue_stage<NI, NI, E>(pa + nx * a_step, pb + nx * b_step, aoff, boff, ls, ls + TILE_B, wave, !diag);
     const E* cs = smem + (kt % NS) * STAGE;
     if constexpr (KMAJOR_B)
       capture_master<F32, NPRE, RITER, SEGS, WTM, BK, BT>(cs + T_ELEMS, kt, kt0, wm, wn * WTN, lane, pre0, pre1);
     else if constexpr (PH == kSquare)
       capture_atile<F32, NPRE, RITER, SEGS, WTM, WTN, BK>(cs, kt, (tj * BT + wn * WTN) / BK, wm, wn, lane, pre0, pre1);
-    mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, BT>(cs, cs + T_ELEMS, acc, lane, wm, wn);
+    mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, BT>(cs, diag ? cs : cs + T_ELEMS, acc, lane, wm, wn);
   }
   wait_vmcnt<0>();   // the clamped copies of the last stage
   __syncthreads();   // the epilogue reuses the ring as staging
