@@ -11,6 +11,8 @@
 // launch over every AdamW tensor.  The step count t lives in the workspace
 // and is advanced by a one-thread launch before the update, so a captured
 // graph replays correctly.
+#include <type_traits>
+
 #include "device_common.h"
 #include "muon_internal.h"
 
@@ -43,44 +45,37 @@ __device__ __forceinline__ float adamw_elem(float w, float g, float& m, float& v
   return w - lr * p.weight_decay * w - lr * (mh / den);
 }
 
-__global__ __launch_bounds__(kThreads) void adamw_kernel(const AdamDev* __restrict__ tensors,
-                                                         const AdamTask* __restrict__ tasks, AdamParams p) {
-  const AdamTask tk = tasks[blockIdx.x];
-  const AdamDev& d = tensors[tk.tensor];
-  const float lr = p.lr * d.lr_mult;
-  const float inv_bc1 = p.state->inv_bc1, inv_sqrt_bc2 = p.state->inv_sqrt_bc2;
-  const int64_t j0 = tk.c0 + int64_t(threadIdx.x) * 8;
-  if (j0 >= d.len) return;
+// One thread's 8-element segment; WF32: the parameter and gradient are
+// float32 (else bf16), a compile-time choice so that every load of a full
+// segment is issued before the first wait.
+template <bool WF32>
+__device__ __forceinline__ void adamw_segment(const AdamDev& d, const AdamTask& tk, const AdamParams& p, float lr,
+                                              float inv_bc1, float inv_sqrt_bc2, int64_t j0) {
+  using W = typename std::conditional<WF32, float, uint16_t>::type;
   const int64_t r = tk.row;
-  char* prow = static_cast<char*>(d.param) + size_t(r * d.ld_param) * (d.f32 ? 4 : 2);
-  const char* grow = static_cast<const char*>(d.grad) + size_t(r * d.ld_grad) * (d.f32 ? 4 : 2);
+  W* prow = static_cast<W*>(d.param) + r * d.ld_param;
+  const W* grow = static_cast<const W*>(d.grad) + r * d.ld_grad;
   float* mrow = d.m + r * d.ld_mom;
   float* vrow = d.v + r * d.ld_mom;
   float w[8], g[8], m[8], v[8];
   const bool full = d.vec && j0 + 8 <= d.len;
   if (full) {
-    if (d.f32) {
-      ld8_f32(prow, j0, w);
-      ld8_f32(grow, j0, g);
-    } else {
-      ld8_bf16(prow, j0, w);
-      ld8_bf16(grow, j0, g);
-    }
     ld8_f32(mrow, j0, m);
     ld8_f32(vrow, j0, v);
+    ld8<WF32>(prow, j0, w);
+    ld8<WF32>(grow, j0, g);
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int64_t j = j0 + e;
-      const bool in = j < d.len;
       w[e] = g[e] = m[e] = v[e] = 0.f;
-      if (in) {
-        if (d.f32) {
-          w[e] = gld<float>(reinterpret_cast<const float*>(prow) + j);
-          g[e] = gld<float>(reinterpret_cast<const float*>(grow) + j);
+      if (j < d.len) {
+        if constexpr (WF32) {
+          w[e] = gld<float>(prow + j);
+          g[e] = gld<float>(grow + j);
         } else {
-          w[e] = bf16_to_f32(gld<uint16_t>(reinterpret_cast<const uint16_t*>(prow) + j));
-          g[e] = bf16_to_f32(gld<uint16_t>(reinterpret_cast<const uint16_t*>(grow) + j));
+          w[e] = bf16_to_f32(gld<uint16_t>(prow + j));
+          g[e] = bf16_to_f32(gld<uint16_t>(grow + j));
         }
         m[e] = gld<float>(mrow + j);
         v[e] = gld<float>(vrow + j);
@@ -94,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void adamw_kernel(const AdamDev* __restri
     w[e] = adamw_elem(w[e], g[e], m[e], v[e], p, lr, inv_bc1, inv_sqrt_bc2);
   }
   if (full) {
-    if (d.f32) st8_f32(prow, j0, w); else st8_bf16(prow, j0, w);
+    st8<WF32>(prow, j0, w);
     st8_f32(mrow, j0, m);
     st8_f32(vrow, j0, v);
   } else {
@@ -102,14 +97,26 @@ __global__ __launch_bounds__(kThreads) void adamw_kernel(const AdamDev* __restri
     for (int e = 0; e < 8; ++e) {
       const int64_t j = j0 + e;
       if (j < d.len) {
-        if (d.f32) gst(reinterpret_cast<float*>(prow) + j, w[e]);
-        else gst(reinterpret_cast<uint16_t*>(prow) + j, f32_to_bf16(w[e]));
+        if constexpr (WF32) gst(prow + j, w[e]);
+        else gst(prow + j, f32_to_bf16(w[e]));
         gst(mrow + j, m[e]);
         gst(vrow + j, v[e]);
       }
     }
   }
   if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(p.flags, 1u);
+}
+
+__global__ __launch_bounds__(kThreads) void adamw_kernel(const AdamDev* __restrict__ tensors,
+                                                         const AdamTask* __restrict__ tasks, AdamParams p) {
+  const AdamTask tk = tasks[blockIdx.x];
+  const AdamDev& d = tensors[tk.tensor];
+  const float lr = p.lr * d.lr_mult;
+  const float inv_bc1 = p.state->inv_bc1, inv_sqrt_bc2 = p.state->inv_sqrt_bc2;
+  const int64_t j0 = tk.c0 + int64_t(threadIdx.x) * 8;
+  if (j0 >= d.len) return;
+  if (d.f32) adamw_segment<true>(d, tk, p, lr, inv_bc1, inv_sqrt_bc2, j0);
+  else adamw_segment<false>(d, tk, p, lr, inv_bc1, inv_sqrt_bc2, j0);
 }
 
 }  // namespace
