@@ -209,7 +209,9 @@ muon_status_t muon_step(muon_handle_t h, float lr, void* stream);
 /* Like muon_step(), but records HIP events around each kernel phase and
  * synchronises `stream` at the end; phase_ms[i] receives the elapsed
  * milliseconds of phase i (see muon_phase_name) and *n_phases their count
- * (at most max_phases are written).  For profiling only. */
+ * (at most max_phases are written).  Every launch runs on `stream`, one
+ * after the other (no lanes), so each phase's time is that launch's alone.
+ * For profiling only. */
 muon_status_t muon_step_timed(muon_handle_t h, float lr, void* stream,
                               float* phase_ms, int32_t max_phases, int32_t* n_phases);
 const char* muon_phase_name(muon_handle_t h, int32_t phase);
