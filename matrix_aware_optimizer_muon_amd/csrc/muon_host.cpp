@@ -152,8 +152,8 @@ muon_status_t validate(const muon_tensor_t* ts, int32_t n, const muon_precond_t*
       return fail(MUON_ERR_ALIGNMENT, who + "pointers must be aligned to their element size");
     const int64_t h = t.split_rows ? t.split_rows : t.rows;
     const int64_t m = std::min<int64_t>(h, t.cols), nn = std::max<int64_t>(h, t.cols);
-    const int64_t T = t.dtype == MUON_F32 ? kTileF32 : kPadBf16;
-    if (!adam && round_up(m, T) * round_up(nn, T) > (int64_t(1) << 31))
+    const int64_t TR = t.dtype == MUON_F32 ? kTileF32 : kPadRowsBf16, TC = t.dtype == MUON_F32 ? kTileF32 : kPadColsBf16;
+    if (!adam && round_up(m, TR) * round_up(nn, TC) > (int64_t(1) << 31))
       return fail(MUON_ERR_UNSUPPORTED, who + "matrix too large for one orthogonalisation unit");
     auto add = [&](const void* p, int64_t ld, size_t esz, const char* what) {
       const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
@@ -295,9 +295,8 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
       u.m = int(std::min<int64_t>(h, t.cols));
       u.n = int(std::max<int64_t>(h, t.cols));
       u.f32 = t.dtype == MUON_F32 || u.m < kMinBf16NsSide;   // NS precision of the unit
-      const int T = u.f32 ? kTileF32 : kPadBf16;
-      u.mp = int(round_up(u.m, T));
-      u.np = int(round_up(u.n, T));
+      u.mp = int(round_up(u.m, u.f32 ? kTileF32 : kPadRowsBf16));
+      u.np = int(round_up(u.n, u.f32 ? kTileF32 : kPadColsBf16));
       u.lr_scale = shape_scale(h, t.cols, hp->scale_mode) * t.lr_mult;
       const int ewr = u.side == kLeft ? kEwRows : kEwTile, ewc = u.side == kLeft ? kEwCols : kEwTile;
       u.k1_tr = int((h + ewr - 1) / ewr);
@@ -323,8 +322,7 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
     int64_t bx_tiles = 0;
     for (int k : ids) {
       const UnitPlan& u = plan.units[k];
-      const int tx = u.f32 ? kTileF32 : kTileBxBf16;
-      bx_tiles += int64_t(u.mp / tx) * (u.np / tx);
+      bx_tiles += int64_t(u.mp / (u.f32 ? kTileF32 : kTileBxRowsBf16)) * (u.np / (u.f32 ? kTileF32 : kTileBxColsBf16));
     }
     const int lanes = ids.size() >= size_t(kLaneMinUnits) && bx_tiles <= kLaneMaxBxTiles ? kLanes : 1;
     auto cost = [&](int k) {
@@ -354,7 +352,8 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
       for (int r = 0; r < u.k1_tr; ++r)
         for (int c = 0; c < u.k1_tc; ++c) g.ew.push_back({int(gi), r, c, r * u.k1_tc + c});
       const int tg = u.f32 ? kTileF32 : kTileGramBf16;    // Gram / square tile
-      const int tx = u.f32 ? kTileF32 : kTileBxBf16;      // B X tile
+      const int txr = u.f32 ? kTileF32 : kTileBxRowsBf16;  // B X tile rows
+      const int txc = u.f32 ? kTileF32 : kTileBxColsBf16;  // ... and columns
       for (int a = 0; a < u.mp / tg; ++a)
         for (int b = a; b < u.mp / tg; ++b) {
           g.gram.push_back({int(gi), a, b, 0});
@@ -363,8 +362,8 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
       // B X tiles column by column: the tiles that run together then share
       // one column strip of X and all of B (a unit's B is the smaller
       // operand), so each strip of X comes from HBM about once.
-      for (int b = 0; b < u.np / tx; ++b)
-        for (int a = 0; a < u.mp / tx; ++a) g.bx.push_back({int(gi), a, b, 0});
+      for (int b = 0; b < u.np / txc; ++b)
+        for (int a = 0; a < u.mp / txr; ++a) g.bx.push_back({int(gi), a, b, 0});
     }
     g.gram = xcd_order(g.gram, plan.units, g, kGram);
     g.sq = xcd_order(g.sq, plan.units, g, kSquare);
@@ -663,10 +662,10 @@ std::string plan_json(const Plan& plan, const muon_hparams_t& hp) {
     std::snprintf(buf, sizeof(buf),
                   "%s{\"ns\":\"%s\",\"lane\":%d,\"units\":%zu,\"momentum_tiles\":%zu,\"gram_tiles\":%zu,"
                   "\"square_tiles\":%zu,\"bx_tiles\":%zu,\"gram_blocks\":%zu,\"square_blocks\":%zu,"
-                  "\"bx_blocks\":%zu,\"tile\":%d,\"bx_tile\":%d}",
+                  "\"bx_blocks\":%zu,\"tile\":%d,\"bx_tile\":[%d,%d]}",
                   first ? "" : ",", g.f32 ? "f32" : "bf16", g.lane, g.units.size(), g.ew.size(), real(g.gram),
                   real(g.sq), real(g.bx), g.gram.size(), g.sq.size(), g.bx.size(), g.f32 ? kTileF32 : kTileGramBf16,
-                  g.f32 ? kTileF32 : kTileBxBf16);
+                  g.f32 ? kTileF32 : kTileBxRowsBf16, g.f32 ? kTileF32 : kTileBxColsBf16);
     s += buf;
     first = false;
   }

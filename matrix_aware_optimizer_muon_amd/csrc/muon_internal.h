@@ -9,13 +9,21 @@
 namespace muon {
 
 // Output tiles of the Newton-Schulz GEMM phases.  bf16 matrices use 128x128
-// tiles (8 waves of 64x32, two blocks per CU); float32 matrices use 64x64
-// tiles everywhere.  Every NS buffer is zero-padded to a multiple of the
-// largest tile of its precision (kPadBf16 / kTileF32) in both dimensions;
-// zero padding is exact under X X^T, A A and B X.
+// tiles for the Gram and the square (8 waves of 64x32, two blocks per CU)
+// and kTileBxRowsBf16 x 128 tiles for B X (128: as the others; 256: 16
+// waves of 64x32, one block per CU, a quarter fewer operand bytes per
+// flop); float32 matrices use 64x64 tiles everywhere.  Every NS buffer is
+// zero-padded: m to a multiple of every row tile (kPadRowsBf16), n to one
+// of the B X column tile (kPadColsBf16), float32 to kTileF32; zero padding
+// is exact under X X^T, A A and B X.
+#ifndef MUON_BX_ROWS
+#define MUON_BX_ROWS 128
+#endif
 constexpr int kTileGramBf16 = 128;
-constexpr int kTileBxBf16 = 128;
-constexpr int kPadBf16 = kTileBxBf16 > kTileGramBf16 ? kTileBxBf16 : kTileGramBf16;
+constexpr int kTileBxRowsBf16 = MUON_BX_ROWS;
+constexpr int kTileBxColsBf16 = 128;
+constexpr int kPadRowsBf16 = kTileBxRowsBf16 > kTileGramBf16 ? kTileBxRowsBf16 : kTileGramBf16;
+constexpr int kPadColsBf16 = 128;
 constexpr int kTileF32 = 64;
 // Tiles of the elementwise phases (momentum, update).  A unit whose X is U
 // itself (rows <= cols) is walked in kEwRows x kEwCols tiles along its rows,

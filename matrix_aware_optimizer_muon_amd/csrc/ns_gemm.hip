@@ -41,11 +41,11 @@ typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;       // LDS
 
 // Tile configuration per precision and phase (the defaults are the fastest
 // measured; 32-deep stages in a 3- or 4-stage ring, MUON_BK_BF16=32, were 9 %
-// slower on every workload).  BT: square output tile;
-// NWM x NWN waves, each owning a (BT/NWM) x (BT/NWN) block of 32x32 MFMA
+// slower on every workload).  BTM x BTN: output tile (rows x columns);
+// NWM x NWN waves, each owning a (BTM/NWM) x (BTN/NWN) block of 32x32 MFMA
 // tiles; BK: K depth of one LDS stage; NS: stages in the LDS ring (NS-1 in
 // flight while one is consumed); OCC: blocks per CU the registers and LDS
-// allow.
+// allow.  BTM x BTN: output tile (rows x columns).
 #ifndef MUON_NS_BF16
 #define MUON_NS_BF16 2
 #endif
@@ -64,17 +64,19 @@ template <bool F32, int PH> struct Cfg;
 #endif
 template <int PH> struct Cfg<false, PH> {        // bf16, Gram and square
   using E = uint16_t;
-  static constexpr int BT = kTileGramBf16, NWM = 2, NWN = MUON_G_NWN, BK = MUON_BK_BF16, NS = MUON_NS_BF16;
+  static constexpr int BTM = kTileGramBf16, BTN = kTileGramBf16, NWM = 2, NWN = MUON_G_NWN, BK = MUON_BK_BF16,
+                       NS = MUON_NS_BF16;
   static constexpr int OCC = NS * BK <= 128 ? 2 : 1;    // ring of 2 x 32 KB or 4 x 16 KB: two blocks per CU
 };
 template <> struct Cfg<false, kBX> {             // bf16, B X
   using E = uint16_t;
-  static constexpr int BT = kTileBxBf16, NWM = 2, NWN = MUON_BX_NWN, BK = MUON_BK_BF16, NS = MUON_NS_BF16;
-  static constexpr int OCC = NS * BK <= 128 ? MUON_BX_OCC : 1;
+  static constexpr int BTM = kTileBxRowsBf16, BTN = kTileBxColsBf16, NWM = kTileBxRowsBf16 / 64, NWN = MUON_BX_NWN,
+                       BK = MUON_BK_BF16, NS = MUON_NS_BF16;
+  static constexpr int OCC = NWM * NWN > 8 ? 1 : NS * BK <= 128 ? MUON_BX_OCC : 1;
 };
 template <int PH> struct Cfg<true, PH> {         // float32, all phases
   using E = float;
-  static constexpr int BT = kTileF32, NWM = 2, NWN = 2, BK = 32, NS = 2, OCC = 2;
+  static constexpr int BTM = kTileF32, BTN = kTileF32, NWM = 2, NWN = 2, BK = 32, NS = 2, OCC = 2;
 };
 
 // LDS layout of a stage.  Tiles are stored unpadded as rows of 16-byte
@@ -167,11 +169,11 @@ __device__ __forceinline__ uint32_t lds_addr(const E* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const E*)(p)));
 }
 
-// MFMAs of one BK-deep stage held in LDS (la: K-contiguous A tile, BT rows
-// of BK; lb: the B tile, K-contiguous like A or K-major, BK rows of BT).
+// MFMAs of one BK-deep stage held in LDS (la: K-contiguous A tile, BTM rows
+// of BK; lb: the B tile, K-contiguous like A or K-major, BK rows of BTN).
 // The wave owns rows wm*WTM.. and columns wn*WTN.. of the block tile, as
 // NBM x NBN tiles of 32x32.
-template <bool F32, bool KMAJOR_B, int NBM, int NBN, int WTM, int WTN, int BK, int BT, typename E>
+template <bool F32, bool KMAJOR_B, int NBM, int NBN, int WTM, int WTN, int BK, int BTN, typename E>
 __device__ __forceinline__ void mma_stage(const E* la, const E* lb, f32x16_t (&acc)[NBM][NBN], int lane, int wm,
                                           int wn) {
   if constexpr (!F32) {
@@ -196,8 +198,8 @@ __device__ __forceinline__ void mma_stage(const E* la, const E* lb, f32x16_t (&a
           const int krow = ks * 16 + 8 * (g >> 1) + (r >> 2);
           const int col = wn * WTN + j * 32 + 16 * (g & 1) + 4 * (r & 3);
           const int cofs = swz_km(krow, col >> 3) * 8 + (col & 7);   // rows krow and krow+4 swizzle alike
-          const bf16x4_t lo = lds_read_tr(&lb[krow * BT + cofs]);
-          const bf16x4_t hi = lds_read_tr(&lb[(krow + 4) * BT + cofs]);
+          const bf16x4_t lo = lds_read_tr(&lb[krow * BTN + cofs]);
+          const bf16x4_t hi = lds_read_tr(&lb[(krow + 4) * BTN + cofs]);
           fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
       }
@@ -230,7 +232,7 @@ __device__ __forceinline__ void mma_stage(const E* la, const E* lb, f32x16_t (&a
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int k = k0 + kq * 4 + e;
-            fb[j][e] = lb[k * BT + swz_km(k, col >> 2) * 4 + (col & 3)];
+            fb[j][e] = lb[k * BTN + swz_km(k, col >> 2) * 4 + (col & 3)];
           }
         }
       }
@@ -261,7 +263,7 @@ __device__ __forceinline__ void stage_strip(const f32x16_t (&row)[NBN], float* e
 // r of X is K step r), so while a K step whose rows overlap the tile sits in
 // LDS each lane copies out its own row segments: bf16 the hi half (the lo
 // half is not an operand and comes from HBM), float32 all 8 values.
-template <bool F32, int NBM, int RITER, int SEGS, int WTM, int BK, int BT, typename E>
+template <bool F32, int NBM, int RITER, int SEGS, int WTM, int BK, int BTN, typename E>
 __device__ __forceinline__ void capture_master(const E* lbx, int kt, int kt0, int wm, int col0, int lane,
                                                u32x4_t (&pre0)[NBM][RITER], u32x4_t (&pre1)[NBM][RITER]) {
   static_assert(BK % 32 == 0, "32-row strips must not straddle K steps");
@@ -274,10 +276,10 @@ __device__ __forceinline__ void capture_master(const E* lbx, int kt, int kt0, in
         const int sg = lane + 64 * q;
         const int k = r0 % BK + sg / SEGS, col = col0 + (sg % SEGS) * 8;
         if constexpr (F32) {
-          pre0[pi][q] = *reinterpret_cast<const u32x4_t*>(&lbx[k * BT + swz_km(k, col >> 2) * 4]);
-          pre1[pi][q] = *reinterpret_cast<const u32x4_t*>(&lbx[k * BT + swz_km(k, (col >> 2) + 1) * 4]);
+          pre0[pi][q] = *reinterpret_cast<const u32x4_t*>(&lbx[k * BTN + swz_km(k, col >> 2) * 4]);
+          pre1[pi][q] = *reinterpret_cast<const u32x4_t*>(&lbx[k * BTN + swz_km(k, (col >> 2) + 1) * 4]);
         } else {
-          pre0[pi][q] = *reinterpret_cast<const u32x4_t*>(&lbx[k * BT + swz_km(k, col >> 3) * 8]);
+          pre0[pi][q] = *reinterpret_cast<const u32x4_t*>(&lbx[k * BTN + swz_km(k, col >> 3) * 8]);
         }
       }
     }
@@ -314,21 +316,21 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
                     GemmParams p) {
   using C = Cfg<F32, PH>;
   using E = typename C::E;
-  constexpr int BT = C::BT, BK = C::BK, NWM = C::NWM, NWN = C::NWN;
+  constexpr int BTM = C::BTM, BTN = C::BTN, BK = C::BK, NWM = C::NWM, NWN = C::NWN;
   constexpr int NT = 64 * NWM * NWN;               // threads per block
-  constexpr int WTM = BT / NWM, WTN = BT / NWN;    // wave tile
+  constexpr int WTM = BTM / NWM, WTN = BTN / NWN;  // wave tile
   constexpr int NBM = WTM / 32, NBN = WTN / 32;    // 32x32 MFMA tiles per wave
   constexpr bool KMAJOR_B = PH == kBX;             // X operand of B X is K-major
   constexpr int NS = C::NS;
   constexpr int EPE = 16 / sizeof(E);              // elements per 16-byte chunk
   constexpr int CPR = BK / EPE;                    // chunks per K-contiguous row
-  constexpr int CPRX = BT / EPE;                   // chunks per K-major row
-  constexpr int T_ELEMS = BT * BK;                 // one operand tile
-  constexpr int T_CH = T_ELEMS / EPE;              // its 16-byte chunks
-  constexpr int NI = T_CH / NT;                    // DMA instructions per lane per tile
-  constexpr int STAGE = 2 * T_ELEMS;               // A tile then B tile
+  constexpr int CPRX = BTN / EPE;                  // chunks per K-major row
+  constexpr int T_A = BTM * BK, T_B = BTN * BK;    // the two operand tiles (elements)
+  constexpr int NIA = T_A / EPE / NT;              // DMA instructions per lane per A tile
+  constexpr int NIB = T_B / EPE / NT;              // ... and per B tile
+  constexpr int STAGE = T_A + T_B;                 // A tile then B tile
   constexpr int EPP = WTN + 8;                     // epilogue LDS pitch (floats)
-  static_assert(NI * NT == T_CH, "tile/thread mismatch");
+  static_assert(NIA * NT * EPE == T_A && NIB * NT * EPE == T_B, "tile/thread mismatch");
   static_assert((CPR == 8 || CPR == 4) && CPRX == 16, "swizzles assume 8- or 4-chunk K rows and 16-chunk K-major rows");
   static_assert(NWM * NWN * 32 * EPP * 4 <= NS * STAGE * static_cast<int>(sizeof(E)),
                 "epilogue staging must fit in the operand LDS");
@@ -346,23 +348,23 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   const int mp = u.mp, np = u.np;
   const int ti = t.ti, tj = t.tj;
 
-  // operand A: rows [ti*BT, +BT) over K; operand B: rows [tj*BT, +BT) over K
-  // (Gram, square) or K rows x columns [tj*BT, +BT) (B X)
+  // operand A: rows [ti*BTM, +BTM) over K; operand B: rows [tj*BTN, +BTN)
+  // over K (Gram, square) or K rows x columns [tj*BTN, +BTN) (B X)
   const E* pa;
   const E* pb;
   int lda_g, ldb_g, K;
   const E* xcur = static_cast<const E*>(u.xh[p.x_in]);
   if constexpr (PH == kGram) {
-    pa = xcur + static_cast<size_t>(ti) * BT * np;
-    pb = xcur + static_cast<size_t>(tj) * BT * np;
+    pa = xcur + static_cast<size_t>(ti) * BTM * np;
+    pb = xcur + static_cast<size_t>(tj) * BTN * np;
     lda_g = ldb_g = np; K = np;
   } else if constexpr (PH == kSquare) {
-    pa = static_cast<const E*>(u.a) + static_cast<size_t>(ti) * BT * mp;
-    pb = static_cast<const E*>(u.a) + static_cast<size_t>(tj) * BT * mp;
+    pa = static_cast<const E*>(u.a) + static_cast<size_t>(ti) * BTM * mp;
+    pb = static_cast<const E*>(u.a) + static_cast<size_t>(tj) * BTN * mp;
     lda_g = ldb_g = mp; K = mp;
   } else {
-    pa = static_cast<const E*>(u.b) + static_cast<size_t>(ti) * BT * mp;
-    pb = xcur + static_cast<size_t>(tj) * BT;
+    pa = static_cast<const E*>(u.b) + static_cast<size_t>(ti) * BTM * mp;
+    pb = xcur + static_cast<size_t>(tj) * BTN;
     lda_g = mp; ldb_g = np; K = mp;
   }
 
@@ -371,17 +373,22 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   const int wm = wave / NWN, wn = wave % NWN;
 
   // each lane's global element offset (within a stage) for its DMA chunks
-  uint32_t aoff[NI], boff[NI];
+  uint32_t aoff[NIA], boff[NIB];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int c = (wave * NI + i) * 64 + lane;       // chunk position in the tile
+  for (int i = 0; i < NIA; ++i) {
+    const int c = (wave * NIA + i) * 64 + lane;      // chunk position in the A tile
     const int ar = c / CPR;
     aoff[i] = static_cast<uint32_t>((ar * lda_g + swz_kc<CPR>(ar, c % CPR) * EPE) * sizeof(E));
+  }
+#pragma unroll
+  for (int i = 0; i < NIB; ++i) {
+    const int c = (wave * NIB + i) * 64 + lane;      // chunk position in the B tile
     if constexpr (KMAJOR_B) {
       const int k = c / CPRX;
       boff[i] = static_cast<uint32_t>((k * ldb_g + swz_km(k, c % CPRX) * EPE) * sizeof(E));
     } else {
-      boff[i] = static_cast<uint32_t>((ar * ldb_g + swz_kc<CPR>(ar, c % CPR) * EPE) * sizeof(E));
+      const int br = c / CPR;
+      boff[i] = static_cast<uint32_t>((br * ldb_g + swz_kc<CPR>(br, c % CPR) * EPE) * sizeof(E));
     }
   }
   const uint32_t ring0 = lds_addr(smem);
@@ -409,7 +416,7 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   constexpr int NPRE = CAPTURE ? NBM : 1;
   u32x4_t pre0[NPRE][RITER], pre1[NPRE][RITER];     // master: hi (bf16) / first..last 4 (float32)
   u32x2_t preq[NPRE][RITER];                          // master: int8 corrections (bf16)
-  const int kt0 = ti * BT / BK;                      // K step of the tile's first row
+  const int kt0 = ti * BTM / BK;                     // K step of the tile's first row
 
   // K pipeline: a ring of NS stages filled by direct-to-LDS loads.  Step kt
   // waits for its own stage (the stages issued after it may stay in
@@ -420,26 +427,26 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   // in a buffer nobody reads again), so every step has the same NS-2 newer
   // stages in flight and a fixed wait count.
   const int KT = K / BK;
-  constexpr uint32_t STAGE_B = STAGE * sizeof(E), TILE_B = T_ELEMS * sizeof(E);
+  constexpr uint32_t STAGE_B = STAGE * sizeof(E), TILE_B = T_A * sizeof(E);
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) {
     const int sc = min(s, KT - 1);
-    issue_stage<NI, NI, E>(pa + sc * a_step, pb + sc * b_step, aoff, boff, ring0 + s * STAGE_B,
-                           ring0 + s * STAGE_B + TILE_B, wave, !diag);
+    issue_stage<NIA, NIB, E>(pa + sc * a_step, pb + sc * b_step, aoff, boff, ring0 + s * STAGE_B,
+                             ring0 + s * STAGE_B + TILE_B, wave, !diag);
   }
   for (int kt = 0; kt < KT; ++kt) {
-    if (diag) wait_vmcnt<(NS - 2) * NI>();   // newer stages in flight: NS-2 of one operand each
-    else wait_vmcnt<(NS - 2) * 2 * NI>();
+    if (diag) wait_vmcnt<(NS - 2) * NIA>();   // newer stages in flight: NS-2 of one operand each
+    else wait_vmcnt<(NS - 2) * (NIA + NIB)>();
     ring_barrier();
     const int nx = min(kt + NS - 1, KT - 1);
     const uint32_t ls = ring0 + ((kt + NS - 1) % NS) * STAGE_B;
-    issue_stage<NI, NI, E>(pa + nx * a_step, pb + nx * b_step, aoff, boff, ls, ls + TILE_B, wave, !diag);
+    issue_stage<NIA, NIB, E>(pa + nx * a_step, pb + nx * b_step, aoff, boff, ls, ls + TILE_B, wave, !diag);
     const E* cs = smem + (kt % NS) * STAGE;
     if constexpr (KMAJOR_B)
-      capture_master<F32, NPRE, RITER, SEGS, WTM, BK, BT>(cs + T_ELEMS, kt, kt0, wm, wn * WTN, lane, pre0, pre1);
+      capture_master<F32, NPRE, RITER, SEGS, WTM, BK, BTN>(cs + T_A, kt, kt0, wm, wn * WTN, lane, pre0, pre1);
     else if constexpr (PH == kSquare)
-      capture_atile<F32, NPRE, RITER, SEGS, WTM, WTN, BK>(cs, kt, (tj * BT + wn * WTN) / BK, wm, wn, lane, pre0, pre1);
-    mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, BT>(cs, diag ? cs : cs + T_ELEMS, acc, lane, wm, wn);
+      capture_atile<F32, NPRE, RITER, SEGS, WTM, WTN, BK>(cs, kt, (tj * BTN + wn * WTN) / BK, wm, wn, lane, pre0, pre1);
+    mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, BTN>(cs, diag ? cs : cs + T_A, acc, lane, wm, wn);
   }
   wait_vmcnt<0>();   // the clamped copies of the last stage
   __syncthreads();   // the epilogue reuses the ring as staging
@@ -448,8 +455,8 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   // B X, bf16: the lo half of the master (the hi half was captured from
   // LDS) is requested before the first LDS round, so one HBM latency is
   // paid per tile, not per strip.
-  const int row_base = ti * BT + wm * WTM;
-  const int col_base = tj * BT + wn * WTN;
+  const int row_base = ti * BTM + wm * WTM;
+  const int col_base = tj * BTN + wn * WTN;
   // In the last iteration the weight segments this lane updates are
   // requested at the same time (bf16 weights with aligned rows; the
   // segments are rows of W for a wide unit, columns of the tile for a tall
