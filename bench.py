@@ -39,6 +39,9 @@ WORKLOAD_TEXT = {
     "conv": "conv: 3x3 convolution filters of a CIFAR-10-style network as out x (in*9) matrices, 6 bf16 "
             "filters (64x288, 64x576, 256x576, 3 x 256x2304); " + STEP_TEXT,
     "tiny": "tiny: one 256x512 fp32 matrix; " + STEP_TEXT,
+    "nmuon": "nmuon: one Newton-Muon layer at d=768 (QKV 2304x768 as three 768x768 blocks, O 768x768 and MLP-up "
+             "3072x768 sharing one S^-1; MLP-down 768x3072 with four 768x768 S^-1 blocks; activations 16384x768 "
+             "bf16 per S); preconditioned step: P = G S^-1 (fp32), then " + STEP_TEXT,
 }
 
 
@@ -63,10 +66,13 @@ def ns_bytes(m, n, es, w_es, ns_steps):
     return {"gram": es * m * n + es * m * m, "square": 2 * es * m * m, "bx": bx}
 
 
-def load_traffic(kernel, src_hash):
+def load_traffic(kernel, src_hash, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary
     (written by `python -m matrix_aware_optimizer_muon_amd.profiling
-    traffic`), if it was taken on the current kernel sources."""
+    traffic`), if it was taken on the current kernel sources and on this
+    workload (the summary covers the GPT-2-small step)."""
+    if workload != "gpt2s":
+        return None
     p = os.path.join(ROOT, "profiles", "traffic_gpt2s.json")
     try:
         with open(p) as f:
@@ -115,7 +121,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="gpt2s", choices=["gpt2s", "gpt2s_aux", "square", "gpt2xl", "conv", "tiny"],
+    ap.add_argument("--workload", default="gpt2s", choices=["gpt2s", "gpt2s_aux", "square", "gpt2xl", "conv", "tiny", "nmuon"],
                     help="weight set to step (the headline metric is quoted on gpt2s)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 3 device-to-device copies of BYTES each (HBM counter calibration)")
@@ -163,9 +169,24 @@ def main():
             descs.append(mm.adam_tensor_desc(tw, tg, tm, tv))
             continue
         keep += [tg, tw, tm]
-        descs.append(mm.tensor_desc(tw, tg, tm))
-    st = mm.MuonStep(descs, hp, device=dev)
+        descs.append(mm.tensor_desc(tw, tg, tm, split_rows=s.split_rows, precond=s.precond))
+    # Newton-Muon slots: one per preconditioner index, d = the activation width
+    slots = sorted({s.precond for s in wl.tensors if s.precond >= 0})
+    preconds = []
+    for sl in slots:
+        pc = mm.MuonPrecond()
+        pc.d = wl.act_dim
+        pc.nblocks = max(s.precond_blocks for s in wl.tensors if s.precond == sl)
+        preconds.append(pc)
+    st = mm.MuonStep(descs, hp, preconds=preconds, device=dev)
     stream = torch.cuda.current_stream(dev)
+    acts = []          # (slot, block, activations) in the order the workload draws them
+    for sl, pc in zip(slots, preconds):
+        for blk in range(pc.nblocks):
+            A = synth.activations(wl, len(acts))
+            acts.append((sl, blk, torch.from_numpy(A.view(np.int16).copy()).view(torch.bfloat16).to(dev)))
+    for sl, blk, a in acts:
+        st.precond_refresh(sl, blk, a, damping=1e-4)
 
     for _ in range(args.warmup):
         st.step()
@@ -189,6 +210,34 @@ def main():
             kind = name.split("/")[0]
             per.setdefault(kind, []).append(ms)
     assert st.flags() == 0, "non-finite values in the benchmark step"
+    precond_info = None
+    if acts:
+        # refresh (S = X^T X / N + damping I from one activation batch, then
+        # its float64 Cholesky inverse) and one micro-batch accumulation,
+        # each timed alone per block
+        reps = 10
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            for sl, blk, a in acts:
+                st.precond_refresh(sl, blk, a, damping=1e-4)
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        refresh_ms = e0.elapsed_time(e1) / (reps * len(acts))
+        e0.record(stream)
+        for _ in range(reps):
+            for sl, blk, a in acts:
+                st.precond_accumulate(sl, blk, a, beta=1.0)
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        acc_ms = e0.elapsed_time(e1) / (reps * len(acts))
+        n, d = wl.act_rows, wl.act_dim
+        syrk_flop = n * d * (d + 1)             # upper tiles of X^T X (symmetric)
+        precond_info = {"blocks": len(acts), "act_rows": n, "d": d,
+                        "refresh_ms_per_block": round(refresh_ms, 4),
+                        "accumulate_ms_per_block": round(acc_ms, 4),
+                        "accumulate_tflops": round(syrk_flop / (acc_ms * 1e-3) / 1e12, 2)}
+        assert st.flags() == 0, "non-finite values in the preconditioner timing"
     st.close()
 
     units = []
@@ -208,6 +257,11 @@ def main():
         for k, v in ns_bytes(m, n, es, w_es, max(1, hp.ns_steps)).items():
             nbytes[k] += v
     elems = sum(s.rows * s.cols for s in wl.tensors if s.kind == "muon")
+    # P = G S^-1: per preconditioned tensor rows x (cols/d blocks) x d x d
+    # multiply-adds in float32; G read (stored dtype), P written (float32)
+    flops["precond_apply"] = sum(2 * s.rows * s.cols * wl.act_dim for s in wl.tensors if s.precond >= 0)
+    nbytes["precond_apply"] = sum(s.rows * s.cols * ((4 if s.dtype == "f32" else 2) + 4)
+                                  for s in wl.tensors if s.precond >= 0)
     nbytes["momentum"] = 13 * elems          # G (bf16) + M read, M + X master (hi, int8) written
     nbytes["update"] = 8 * elems
     # AdamW: W read and written, G read, both float32 moments read and written
@@ -219,26 +273,27 @@ def main():
     # algorithmic work per step of each kind (NS phases run ns_steps times)
     iters = {k: (hp.ns_steps if k in ("gram", "square", "bx") else 1) for k in per}
     ns_ms = sum(totals[k] for k in ("gram", "square", "bx"))
-    ns_tflop = hp.ns_steps * sum(flops.values()) / 1e12
+    ns_tflop = hp.ns_steps * sum(flops[k] for k in ("gram", "square", "bx")) / 1e12
     dom = max(totals, key=totals.get)
     src_hash = kernel_source_hash()
     # The dominant kernel's roofline bound follows from its algorithmic
-    # intensity: below the bf16 ridge (peak flops / peak bytes) it is HBM.
-    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    # intensity: below the ridge of its MFMA type (peak flops / peak bytes)
+    # it is HBM.
     intensity = flops.get(dom, 0) / nbytes[dom]
     # per launch: the kind's work per step over its launches per step (with
     # two lanes each phase is two launches of about half the work)
     per_launch_flops = flops.get(dom, 0) * iters[dom] / launches[dom]
     per_launch_bytes = nbytes[dom] * iters[dom] / launches[dom]
-    if dom in flops and intensity >= ridge:
+    peak = PEAK_F32_TFLOPS if dom == "precond_apply" else PEAK_BF16_TFLOPS   # float32 MFMA
+    if dom in flops and intensity >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
         achieved = per_launch_flops / (avg[dom] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4)}
     else:
         achieved = per_launch_bytes / (avg[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = load_traffic(dom, src_hash)
+    roof["traffic"] = load_traffic(dom, src_hash, args.workload)
     roof["kernel"] = dom
     roof["avg_launch_ms"] = round(avg[dom], 5)
     roof["launches_per_step"] = launches[dom]
@@ -276,6 +331,9 @@ def main():
         "phase_hbm_gbs": {k: round(nbytes[k] * iters[k] / (totals[k] * 1e-3) / 1e9, 1) for k in avg if k in nbytes},
         "cpu_baseline": None,
     }
+    if precond_info is not None:
+        precond_info["apply_tflops_f32"] = round(flops["precond_apply"] / (totals["precond_apply"] * 1e-3) / 1e12, 2)
+        out["precond"] = precond_info
     if args.workload != "gpt2s":
         out["metric"] = f"Muon steps/sec, {args.workload} weight set (not the headline workload)"
         out["dtype"] = "f32" if args.workload == "tiny" else "bf16"
