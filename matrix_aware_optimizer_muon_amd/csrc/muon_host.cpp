@@ -75,6 +75,7 @@ struct Plan {
   std::vector<AdamTask> adam_tasks;
   size_t off_adam_dev = 0, off_adam_tasks = 0, off_adam_state = 0;
   size_t off_flags = 0, off_partials = 0, off_norms = 0;
+  size_t off_mpart = 0;              // refresh scratch (moment partials, float64 S^-1 sum), all slots
   size_t meta_bytes = 0, total = 0;
   int total_k1_tiles = 0;
   int64_t zero_bytes = 0;  // bytes of NS buffers (zero-filled at init)
@@ -405,6 +406,15 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
     sp.off_acc = off; off = align_up(off + blk * sizeof(float));
     sp.off_cnt = off; off = align_up(off + size_t(sp.nblocks) * sizeof(double));
   }
+  // scratch of the refresh (one at a time per handle): the split partials
+  // of the second moment, then the float64 sum of S^-1
+  size_t mpart = 0;
+  for (const SlotPlan& sp : plan.slots) {
+    const int splits = moment_splits(sp.dp, false, INT64_MAX);   // bf16 tiles split the most
+    const size_t sq = size_t(sp.dp) * sp.dp;
+    mpart = std::max({mpart, sq * sizeof(double), splits > 1 ? size_t(splits) * sq * sizeof(float) : size_t(0)});
+  }
+  if (mpart) { plan.off_mpart = off; off = align_up(off + mpart); }
   for (int ti : plan.prec_tensors) {
     plan.off_p.push_back(off);
     off = align_up(off + size_t(ts[ti].rows) * ts[ti].cols * sizeof(float));
@@ -860,6 +870,7 @@ PrecondBlockDev block_dev(muon_handle_t h, const SlotPlan& sp, int32_t block) {
   b.sinv = reinterpret_cast<float*>(h->ws + sp.off_sinv) + bo;
   b.acc = reinterpret_cast<float*>(h->ws + sp.off_acc) + bo;
   b.cnt = reinterpret_cast<double*>(h->ws + sp.off_cnt) + block;
+  b.part = h->plan.off_mpart ? reinterpret_cast<float*>(h->ws + h->plan.off_mpart) : nullptr;
   b.d = int(sp.d);
   b.dp = sp.dp;
   return b;

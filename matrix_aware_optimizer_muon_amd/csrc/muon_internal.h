@@ -117,8 +117,29 @@ struct PrecondBlockDev {
   float* sinv;     // S^-1, float32
   float* acc;      // running sum of X^T X over micro-batches, float32, dp x dp
   double* cnt;     // its running sample count
+  float* part;     // scratch shared by every block of every slot: the split partial sums of
+                   // X^T X (moment_splits(dp) dp x dp float32 slabs), then the float64 dp x dp
+                   // sum that collects S^-1 during the factorisation
   int32_t d, dp;
 };
+
+// Split of the second-moment product X^T X over ranges of sample rows: a
+// d = 768 layer has only 21 upper tiles, so without it a batch occupies 21
+// of the 256 CUs.  The split count aims at kMomentTargetBlocks blocks, keeps
+// at least kMomentMinRows rows per range, and the partial sums are added in
+// range order by a second pass (deterministic).
+constexpr int kMomentTargetBlocks = 512;
+constexpr int kMomentMaxSplits = 16;
+constexpr int64_t kMomentMinRows = 256;
+inline int moment_splits(int dp, bool f32, int64_t n_rows) {
+  const int nt = dp / (f32 ? 64 : 128);
+  const int tiles = nt * (nt + 1) / 2;
+  int sp = (kMomentTargetBlocks + tiles - 1) / tiles;
+  if (sp > kMomentMaxSplits) sp = kMomentMaxSplits;
+  const int64_t by_rows = n_rows / kMomentMinRows + (n_rows % kMomentMinRows != 0);
+  if (sp > by_rows) sp = static_cast<int>(by_rows);
+  return sp < 1 ? 1 : sp;
+}
 
 // Launchers (defined in the .hip files).
 // AdamW tensors (parameters Muon does not take).  Each is stepped as a set

@@ -11,9 +11,10 @@
 //                      tiles, mirror-stored; the padded diagonal is set to 1
 //                      so the padded matrix stays positive definite.
 //   potrf / trsm / syrk_update    blocked right-looking Cholesky S = L L^T in
-//                      float64 (64 x 64 blocks)
-//   trinv_diag / trinv_offdiag    L^-1, blocked forward substitution
-//   inv_product        S^-1 = L^-T L^-1, stored as float32
+//                      float64 (64 x 64 blocks), with L^-1 formed alongside
+//                      by blocked forward substitution of L X = I
+//   sinv_store         S^-1 = L^-T L^-1 (summed in float64 during the
+//                      factorisation), stored as float32
 //   apply_kernel       P = G S^-1 (block-wise for block-diagonal S), float32
 //                      MFMA, read by the momentum phase in place of G.
 #include "device_common.h"
@@ -52,7 +53,8 @@ template <> struct MomCfg<true> {
 template <bool F32>
 __global__ __launch_bounds__(kThreads)
 void moment_kernel(const void* __restrict__ acts, int64_t n_rows, int64_t ld, int d, int vec,
-                   float* __restrict__ S, int dp, float inv_n, float damping, int accumulate, float beta) {
+                   float* __restrict__ S, int dp, float inv_n, float damping, int accumulate, float beta,
+                   float* __restrict__ part, int64_t split_rows) {
   using C = MomCfg<F32>;
   using E = typename C::E;
   constexpr int BT = C::BT, WT = C::WT, BK = C::BK;
@@ -76,6 +78,9 @@ void moment_kernel(const void* __restrict__ acts, int64_t n_rows, int64_t ld, in
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int brow = tid / CPRX, bchunk = tid % CPRX;
+  // sample rows of this block: all of them, or (split) range blockIdx.y
+  const int64_t r_begin = static_cast<int64_t>(blockIdx.y) * split_rows;
+  const int64_t r_end = r_begin + split_rows < n_rows ? r_begin + split_rows : n_rows;
 
   f32x16_t acc[NB][NB];
 #pragma unroll
@@ -88,7 +93,7 @@ void moment_kernel(const void* __restrict__ acts, int64_t n_rows, int64_t ld, in
   // load one chunk (EPE elements) of the slab, zero outside the tensor
   auto load_chunk = [&](int64_t r, int c) -> u32x4_t {
     u32x4_t v = {0u, 0u, 0u, 0u};
-    if (r >= n_rows || c >= d) return v;
+    if (r >= r_end || c >= d) return v;
     const size_t off = static_cast<size_t>(r) * ld + c;
     if (vec && c + EPE <= d) return gld<u32x4_t>(static_cast<const E*>(acts) + off);
     E tmp[EPE];
@@ -98,11 +103,11 @@ void moment_kernel(const void* __restrict__ acts, int64_t n_rows, int64_t ld, in
   };
 
   u32x4_t ra[NPX], rb[NPX];
-  const int KT = static_cast<int>((n_rows + BK - 1) / BK);
+  const int KT = static_cast<int>((r_end - r_begin + BK - 1) / BK);
   auto gload = [&](int kt) {
 #pragma unroll
     for (int q = 0; q < NPX; ++q) {
-      const int64_t r = static_cast<int64_t>(kt) * BK + brow + q * RPPX;
+      const int64_t r = r_begin + static_cast<int64_t>(kt) * BK + brow + q * RPPX;
       ra[q] = load_chunk(r, ti * BT + bchunk * EPE);
       rb[q] = load_chunk(r, tj * BT + bchunk * EPE);
     }
@@ -181,6 +186,10 @@ void moment_kernel(const void* __restrict__ acts, int64_t n_rows, int64_t ld, in
     for (int s = lane; s < 32 * WT; s += 64) {
       const int row = s / WT, col = s % WT;
       const int gr = row_base + pi * 32 + row, gc = col_base + col;
+      if (part) {   // split: raw partial sum of this row range, upper tile only
+        part[static_cast<size_t>(blockIdx.y) * dp * dp + static_cast<size_t>(gr) * dp + gc] = ep[row * EPP + col];
+        continue;
+      }
       if (accumulate) {
         const float a = ep[row * EPP + col];
         const size_t o = static_cast<size_t>(gr) * dp + gc, om = static_cast<size_t>(gc) * dp + gr;
@@ -197,197 +206,339 @@ void moment_kernel(const void* __restrict__ acts, int64_t n_rows, int64_t ld, in
   }
 }
 
+// Sum of the split partials (in split order, so the result does not depend
+// on the schedule), then the same finish as the unsplit epilogue.  One block
+// per 16-row quarter of a 64 x 64 sub-tile (a, b), a <= b, of the upper tile
+// region: thread t adds the float4 at row t/16, columns 4(t%16).. over the
+// splits; the mirror (b, a) is written through an LDS transpose so both
+// stores are coalesced.  Diagonal sub-tiles keep their own values and have
+// no mirror.
+__global__ __launch_bounds__(kThreads)
+void moment_reduce_kernel(const float* __restrict__ part, int splits, float* __restrict__ S, int d, int dp,
+                          float inv_n, float damping, int accumulate, float beta) {
+  __shared__ float T[16][65];
+  const int quarter = blockIdx.x & 3;
+  int a = 0, rem = blockIdx.x >> 2;
+  const int ns = dp / 64;
+  while (rem >= ns - a) { rem -= ns - a; ++a; }
+  const int b = a + rem;
+  const int c4 = (threadIdx.x & 15) * 4, row = threadIdx.x >> 4;
+  const size_t slab = static_cast<size_t>(dp) * dp;
+  const int gr = a * 64 + quarter * 16 + row;
+  const size_t o = static_cast<size_t>(gr) * dp + b * 64 + c4;
+  f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+  int sp = 0;
+  for (; sp + 4 <= splits; sp += 4) {   // four loads in flight, added in split order
+    const f32x4_t p0 = gld<f32x4_t>(part + (sp + 0) * slab + o), p1 = gld<f32x4_t>(part + (sp + 1) * slab + o);
+    const f32x4_t p2 = gld<f32x4_t>(part + (sp + 2) * slab + o), p3 = gld<f32x4_t>(part + (sp + 3) * slab + o);
+    sum += p0;
+    sum += p1;
+    sum += p2;
+    sum += p3;
+  }
+  for (; sp < splits; ++sp) sum += gld<f32x4_t>(part + sp * slab + o);
+  f32x4_t v;
+  if (accumulate) {
+    const f32x4_t old = gld<f32x4_t>(S + o);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = beta != 0.f ? fmaf(beta, old[e], sum[e]) : sum[e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int gc = b * 64 + c4 + e;
+      v[e] = sum[e] * inv_n;
+      if (gr == gc) v[e] = gr < d ? v[e] + damping : 1.0f;
+    }
+  }
+  *reinterpret_cast<f32x4_t*>(S + o) = v;
+  if (a == b) return;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) T[row][c4 + e] = v[e];
+  __syncthreads();
+  // mirror: 64 rows (columns of (a, b)) of 16 values; 4 threads per row
+  const int mr = threadIdx.x >> 2, mc = (threadIdx.x & 3) * 4;
+  f32x4_t m;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) m[e] = T[mc + e][mr];
+  *reinterpret_cast<f32x4_t*>(S + static_cast<size_t>(b * 64 + mr) * dp + a * 64 + quarter * 16 + mc) = m;
+}
+
 // ---------------------------------------------------------------- Cholesky
-// S (float32, dp x dp) -> L (float64, lower triangle; upper set to zero).
+// 64 x 64 float64 block products from two LDS tiles (pitch kCb + 1): thread
+// t owns the 4 x 4 register tile of rows 4*(t/16).., columns 4*(t%16).., so
+// each K step reads 8 values for 16 multiply-adds.  TA: P is read as [m][i]
+// (P^T), else [i][m]; TB: Q is read as [j][m] (Q^T), else [m][j].
+template <bool TA, bool TB>
+__device__ __forceinline__ void mm64_acc(const double (*P)[kCb + 1], const double (*Q)[kCb + 1],
+                                         double (&c)[4][4]) {
+  static_assert(kThreads == 256 && kCb == 64, "16 x 16 threads of 4 x 4 cover a 64 x 64 block");
+  const int i0 = (threadIdx.x >> 4) * 4, j0 = (threadIdx.x & 15) * 4;
+#pragma unroll 4
+  for (int m = 0; m < kCb; ++m) {
+    double a[4], b[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      a[r] = TA ? P[m][i0 + r] : P[i0 + r][m];
+      b[r] = TB ? Q[j0 + r][m] : Q[m][j0 + r];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) c[r][q] = fma(a[r], b[q], c[r][q]);
+  }
+}
+
+__device__ __forceinline__ void zero44(double (&c)[4][4]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) c[r][q] = 0.0;
+}
+
+// S (float32, dp x dp) -> L (float64, lower triangle; upper set to zero);
+// L^-1's storage cleared (the right-hand side B of L X = I starts at zero off
+// the diagonal blocks, which potrf_kernel writes) and so is the float64 sum
+// that collects S^-1.
 __global__ __launch_bounds__(kThreads) void to_f64_kernel(const float* __restrict__ S, double* __restrict__ L,
+                                                          double* __restrict__ Li, double* __restrict__ sacc,
                                                           int dp) {
   const size_t n = static_cast<size_t>(dp) * dp;
   for (size_t k = blockIdx.x * static_cast<size_t>(kThreads) + threadIdx.x; k < n;
        k += static_cast<size_t>(gridDim.x) * kThreads) {
     const int i = static_cast<int>(k / dp), j = static_cast<int>(k % dp);
     L[k] = j <= i ? static_cast<double>(S[k]) : 0.0;
+    Li[k] = 0.0;
+    sacc[k] = 0.0;
   }
 }
 
-// Factor the diagonal block jb in place (unblocked, in LDS).
-__global__ __launch_bounds__(kThreads) void potrf_kernel(double* __restrict__ L, int dp, int jb,
-                                                         uint32_t* __restrict__ flags) {
-  __shared__ double T[kCb][kCb + 1];
+// The factor and L^-1 are built together, one 64-column block step jb at
+// a time (right-looking):
+//   potrf_kernel   D = L[jb][jb] and X[jb][jb] = D^-1
+//   trsm_kernel    L[ib][jb] = A[ib][jb] D^-T            (ib > jb)
+//                  X[jb][cb] = D^-1 B[jb][cb]            (cb < jb)
+//   syrk_update    A[ib][kb] -= L[ib][jb] L[kb][jb]^T    (jb < kb <= ib)
+//                  B[ib][cb] -= L[ib][jb] X[jb][cb]      (ib > jb, cb <= jb)
+//                  Z[ib][cb] += X[jb][ib]^T X[jb][cb]    (ib <= cb <= jb)
+// where X = L^-1 and B (held in the same storage, zero off the diagonal at
+// the start) is the right-hand side of the block forward substitution
+// L X = I: X[jb][cb] = D^-1 (I[jb][cb] - sum_{kb<jb} L[jb][kb] X[kb][cb]),
+// each term subtracted at step kb once both of its factors are final.  Row
+// jb of X is final after trsm_kernel of step jb, so the same launch also
+// adds its term of S^-1 = L^-T L^-1 = sum_jb X[jb]^T X[jb] to the float64
+// sum Z (upper blocks); a last launch adds the final row's term and
+// sinv_store_kernel writes S^-1 in float32.  The inverse and the product
+// add blocks to launches the factorisation makes anyway.
+
+// Diagonal block jb: factor in place and store D^-1 as X[jb][jb].
+// Right-looking, with the block in registers: thread t holds the 2 x 2
+// entries at rows 2(t/32).., columns 2(t%32).. of the trailing matrix (a) and
+// of the running right-hand side of D X = I (x).  Step k: the owners of
+// column k publish it and the owners of row k of x publish that row
+// (double-buffered in LDS, so one barrier per step); then every thread forms
+// l_i = A[i][k] / sqrt(A[k][k]) for its rows and columns, updates
+// A[i][j] -= l_i l_j (i, j > k) and x[i][:] -= l_i X[k][:] (i > k), with
+// X[k][:] = x[k][:] / L[k][k] the finished row k of D^-1.
+constexpr int kPotrfThreads = 1024;
+__global__ __launch_bounds__(kPotrfThreads) void potrf_kernel(double* __restrict__ L, double* __restrict__ Li, int dp,
+                                                              int jb, uint32_t* __restrict__ flags) {
+  static_assert(kPotrfThreads * 4 == kCb * kCb, "2 x 2 entries per thread cover the block");
+  __shared__ double colk[2][kCb];
+  __shared__ double rowk[2][kCb];
   double* base = L + static_cast<size_t>(jb) * kCb * dp + jb * kCb;
-  for (int s = threadIdx.x; s < kCb * kCb; s += kThreads) T[s / kCb][s % kCb] = base[(s / kCb) * static_cast<size_t>(dp) + s % kCb];
-  __syncthreads();
+  const int i0 = (threadIdx.x >> 5) * 2, j0 = (threadIdx.x & 31) * 2;
+  double a[2][2], x[2][2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      a[r][q] = base[(i0 + r) * static_cast<size_t>(dp) + j0 + q];
+      x[r][q] = i0 + r == j0 + q ? 1.0 : 0.0;
+    }
   for (int k = 0; k < kCb; ++k) {
-    if (threadIdx.x == 0) {
-      const double piv = T[k][k];
-      if (!(piv > 0.0)) atomicOr(flags, 2u);
-      T[k][k] = sqrt(piv);   // NaN for a non-positive pivot; it propagates into S^-1
+    const int buf = k & 1, kq = k & 1;
+    if (j0 == (k & ~1)) {
+      colk[buf][i0] = kq ? a[0][1] : a[0][0];
+      colk[buf][i0 + 1] = kq ? a[1][1] : a[1][0];
+    }
+    if (i0 == (k & ~1)) {
+      rowk[buf][j0] = kq ? x[1][0] : x[0][0];
+      rowk[buf][j0 + 1] = kq ? x[1][1] : x[0][1];
     }
     __syncthreads();
-    const double dk = T[k][k];
-    for (int i = k + 1 + threadIdx.x; i < kCb; i += kThreads) T[i][k] /= dk;
-    __syncthreads();
-    const int n = kCb - k - 1;   // trailing lower triangle of order n
-    for (int s = threadIdx.x; s < n * n; s += kThreads) {
-      const int i = k + 1 + s / n, j = k + 1 + s % n;
-      if (j <= i) T[i][j] -= T[i][k] * T[j][k];
+    // a non-positive pivot gives NaN or inf, which propagates into S^-1,
+    // and sets the flag
+    const double piv = colk[buf][k];
+    const double rdk = rsqrt(piv);
+    if (threadIdx.x == 0 && !(piv > 0.0)) atomicOr(flags, 2u);
+    // rows of this wave: 4 (t / 64) .. + 3; a wave whose rows are all <= k
+    // has nothing left to update
+    if (4 * (threadIdx.x >> 6) + 3 > k) {
+      // l_i = 0 for i <= k and l_j = 0 for j <= k, so the trailing update
+      // leaves finished rows and columns as they are
+      double li[2], lj[2], xk[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        li[r] = i0 + r > k ? colk[buf][i0 + r] * rdk : 0.0;
+        lj[r] = j0 + r > k ? colk[buf][j0 + r] * rdk : 0.0;
+        xk[r] = rowk[buf][j0 + r] * rdk;
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          a[r][q] = fma(-li[r], lj[q], a[r][q]);
+          x[r][q] = fma(-li[r], xk[q], x[r][q]);
+        }
     }
-    __syncthreads();
+    if (j0 == (k & ~1)) {   // column k of L (L[k][k] = piv / sqrt(piv))
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const double v = colk[buf][i0 + r] * rdk;
+        if (kq) a[r][1] = v;
+        else a[r][0] = v;
+      }
+    }
+    if (i0 == (k & ~1)) {   // row k of D^-1
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const double v = rowk[buf][j0 + q] * rdk;
+        if (kq) x[1][q] = v;
+        else x[0][q] = v;
+      }
+    }
   }
-  for (int s = threadIdx.x; s < kCb * kCb; s += kThreads) {
-    const int i = s / kCb, j = s % kCb;
-    base[i * static_cast<size_t>(dp) + j] = j <= i ? T[i][j] : 0.0;
-  }
+  double* di = Li + static_cast<size_t>(jb) * kCb * dp + jb * kCb;
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      base[(i0 + r) * static_cast<size_t>(dp) + j0 + q] = j0 + q <= i0 + r ? a[r][q] : 0.0;
+      di[(i0 + r) * static_cast<size_t>(dp) + j0 + q] = x[r][q];
+    }
 }
 
-// Panel below the diagonal block: L[ib][jb] = A[ib][jb] L[jb][jb]^-T.
-__global__ __launch_bounds__(kThreads) void trsm_kernel(double* __restrict__ L, int dp, int jb) {
-  __shared__ double D[kCb][kCb + 1];
-  __shared__ double X[kCb][kCb + 1];
-  const int ib = jb + 1 + blockIdx.x;
-  const double* dg = L + static_cast<size_t>(jb) * kCb * dp + jb * kCb;
-  double* pb = L + static_cast<size_t>(ib) * kCb * dp + jb * kCb;
-  for (int s = threadIdx.x; s < kCb * kCb; s += kThreads) {
-    D[s / kCb][s % kCb] = dg[(s / kCb) * static_cast<size_t>(dp) + s % kCb];
-    X[s / kCb][s % kCb] = pb[(s / kCb) * static_cast<size_t>(dp) + s % kCb];
-  }
-  __syncthreads();
-  // row r of X solves x D^T = a: x_k = (a_k - sum_{m<k} x_m D[k][m]) / D[k][k]
-  if (threadIdx.x < kCb) {
-    const int r = threadIdx.x;
-    for (int k = 0; k < kCb; ++k) {
-      double v = X[r][k];
-      for (int m = 0; m < k; ++m) v -= X[r][m] * D[k][m];
-      X[r][k] = v / D[k][k];
-    }
-  }
-  __syncthreads();
-  for (int s = threadIdx.x; s < kCb * kCb; s += kThreads) pb[(s / kCb) * static_cast<size_t>(dp) + s % kCb] = X[s / kCb][s % kCb];
+// Load a 64 x 64 float64 block (leading dimension dp) into an LDS tile.
+__device__ __forceinline__ void load_block(double (*T)[kCb + 1], const double* __restrict__ src, int dp) {
+  for (int s = threadIdx.x; s < kCb * kCb; s += kThreads) T[s / kCb][s % kCb] = src[(s / kCb) * static_cast<size_t>(dp) + s % kCb];
 }
 
-// Trailing update A[ib][kb] -= L[ib][jb] L[kb][jb]^T for jb < kb <= ib.
-__global__ __launch_bounds__(kThreads) void syrk_update_kernel(double* __restrict__ L, int dp, int jb) {
+// Step jb, after potrf_kernel: blocks [0, below) form the panel
+// L[ib][jb] = A[ib][jb] D^-T (ib = jb + 1 + block); blocks [below, below + jb)
+// finish row jb of L^-1 left of the diagonal, X[jb][cb] = D^-1 B[jb][cb].
+__global__ __launch_bounds__(kThreads) void trsm_kernel(double* __restrict__ L, double* __restrict__ Li, int dp,
+                                                        int jb, int below) {
   __shared__ double P[kCb][kCb + 1];
   __shared__ double Q[kCb][kCb + 1];
-  int ib = jb + 1, rem = blockIdx.x;   // lower-triangle pair index -> (ib, kb)
-  while (rem >= ib - jb) { rem -= ib - jb; ++ib; }
-  const int kb = jb + 1 + rem;
-  const double* pi = L + static_cast<size_t>(ib) * kCb * dp + jb * kCb;
-  const double* pk = L + static_cast<size_t>(kb) * kCb * dp + jb * kCb;
-  for (int s = threadIdx.x; s < kCb * kCb; s += kThreads) {
-    P[s / kCb][s % kCb] = pi[(s / kCb) * static_cast<size_t>(dp) + s % kCb];
-    Q[s / kCb][s % kCb] = pk[(s / kCb) * static_cast<size_t>(dp) + s % kCb];
+  const double* dinv = Li + static_cast<size_t>(jb) * kCb * dp + jb * kCb;
+  const bool panel = static_cast<int>(blockIdx.x) < below;
+  double* out = panel ? L + static_cast<size_t>(jb + 1 + blockIdx.x) * kCb * dp + jb * kCb
+                      : Li + static_cast<size_t>(jb) * kCb * dp + (blockIdx.x - below) * kCb;
+  double c[4][4];
+  zero44(c);
+  if (panel) {
+    load_block(P, out, dp);
+    load_block(Q, dinv, dp);
+    __syncthreads();
+    mm64_acc<false, true>(P, Q, c);   // sum_m A[i][m] D^-1[j][m]
+  } else {
+    load_block(P, dinv, dp);
+    load_block(Q, out, dp);
+    __syncthreads();
+    mm64_acc<false, false>(P, Q, c);  // sum_m D^-1[i][m] B[m][j]
   }
-  __syncthreads();
-  double* out = L + static_cast<size_t>(ib) * kCb * dp + kb * kCb;
-  for (int s = threadIdx.x; s < kCb * kCb; s += kThreads) {
-    const int i = s / kCb, j = s % kCb;
-    double v = 0.0;
-    for (int m = 0; m < kCb; ++m) v += P[i][m] * Q[j][m];
-    out[i * static_cast<size_t>(dp) + j] -= v;
-  }
+  const int i0 = (threadIdx.x >> 4) * 4, j0 = (threadIdx.x & 15) * 4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) out[(i0 + r) * static_cast<size_t>(dp) + j0 + q] = c[r][q];
 }
 
-// Inverse of each diagonal block of L (lower triangular, in LDS).
-__global__ __launch_bounds__(kThreads) void trinv_diag_kernel(const double* __restrict__ L, double* __restrict__ Li,
+// Step jb, after trsm_kernel: blocks [0, npairs) update the trailing matrix,
+// A[ib][kb] -= L[ib][jb] L[kb][jb]^T for jb < kb <= ib; the next nrhs update
+// the right-hand side of L X = I, B[ib][cb] -= L[ib][jb] X[jb][cb] for
+// ib > jb, cb <= jb; the rest add row jb's term of S^-1,
+// Z[ib][cb] += X[jb][ib]^T X[jb][cb] for ib <= cb <= jb.
+__global__ __launch_bounds__(kThreads) void syrk_update_kernel(double* __restrict__ L, double* __restrict__ Li,
+                                                               double* __restrict__ sacc, int dp, int jb, int npairs,
+                                                               int nrhs) {
+  __shared__ double P[kCb][kCb + 1];
+  __shared__ double Q[kCb][kCb + 1];
+  double* out;
+  double c[4][4];
+  zero44(c);
+  const int i0 = (threadIdx.x >> 4) * 4, j0 = (threadIdx.x & 15) * 4;
+  if (static_cast<int>(blockIdx.x) >= npairs + nrhs) {
+    int ib = 0, rem = blockIdx.x - npairs - nrhs;   // upper pair index over 0..jb -> (ib, cb)
+    while (rem >= jb + 1 - ib) { rem -= jb + 1 - ib; ++ib; }
+    const int cb = ib + rem;
+    load_block(P, Li + static_cast<size_t>(jb) * kCb * dp + ib * kCb, dp);
+    load_block(Q, Li + static_cast<size_t>(jb) * kCb * dp + cb * kCb, dp);
+    out = sacc + static_cast<size_t>(ib) * kCb * dp + cb * kCb;
+    __syncthreads();
+    mm64_acc<true, false>(P, Q, c);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) out[(i0 + r) * static_cast<size_t>(dp) + j0 + q] += c[r][q];
+    return;
+  }
+  if (static_cast<int>(blockIdx.x) < npairs) {
+    int ib = jb + 1, rem = blockIdx.x;   // lower-triangle pair index -> (ib, kb)
+    while (rem >= ib - jb) { rem -= ib - jb; ++ib; }
+    const int kb = jb + 1 + rem;
+    load_block(P, L + static_cast<size_t>(ib) * kCb * dp + jb * kCb, dp);
+    load_block(Q, L + static_cast<size_t>(kb) * kCb * dp + jb * kCb, dp);
+    out = L + static_cast<size_t>(ib) * kCb * dp + kb * kCb;
+    __syncthreads();
+    mm64_acc<false, true>(P, Q, c);
+  } else {
+    const int idx = blockIdx.x - npairs;
+    const int ib = jb + 1 + idx / (jb + 1), cb = idx % (jb + 1);
+    load_block(P, L + static_cast<size_t>(ib) * kCb * dp + jb * kCb, dp);
+    load_block(Q, Li + static_cast<size_t>(jb) * kCb * dp + cb * kCb, dp);
+    out = Li + static_cast<size_t>(ib) * kCb * dp + cb * kCb;
+    __syncthreads();
+    mm64_acc<false, false>(P, Q, c);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) out[(i0 + r) * static_cast<size_t>(dp) + j0 + q] -= c[r][q];
+}
+
+// S^-1 (float32) from the float64 sum Z, which holds the upper blocks
+// (ib <= jb); a lower block is the transpose of its mirror, staged through
+// LDS so that reads and writes are both along rows.  One block per 64 x 64
+// block of S^-1, 16 rows per pass.
+__global__ __launch_bounds__(kThreads) void sinv_store_kernel(const double* __restrict__ sacc, float* __restrict__ Sinv,
                                                               int dp) {
-  __shared__ double D[kCb][kCb + 1];
-  __shared__ double X[kCb][kCb + 1];
-  const int b = blockIdx.x;
-  const double* dg = L + static_cast<size_t>(b) * kCb * dp + b * kCb;
-  for (int s = threadIdx.x; s < kCb * kCb; s += kThreads) D[s / kCb][s % kCb] = dg[(s / kCb) * static_cast<size_t>(dp) + s % kCb];
-  __syncthreads();
-  // column c of D^-1 solves D x = e_c by forward substitution
-  if (threadIdx.x < kCb) {
-    const int c = threadIdx.x;
-    for (int i = 0; i < kCb; ++i) {
-      double v = i == c ? 1.0 : 0.0;
-      for (int m = c; m < i; ++m) v -= D[i][m] * X[m][c];
-      X[i][c] = i < c ? 0.0 : v / D[i][i];
-    }
-  }
-  __syncthreads();
-  double* out = Li + static_cast<size_t>(b) * kCb * dp + b * kCb;
-  for (int s = threadIdx.x; s < kCb * kCb; s += kThreads) out[(s / kCb) * static_cast<size_t>(dp) + s % kCb] = X[s / kCb][s % kCb];
-}
-
-// Block row ib of L^-1 left of the diagonal:
-// Li[ib][jb] = -Li[ib][ib] * sum_{kb=jb}^{ib-1} L[ib][kb] Li[kb][jb].
-__global__ __launch_bounds__(kThreads) void trinv_offdiag_kernel(const double* __restrict__ L, double* __restrict__ Li,
-                                                                 int dp, int ib) {
-  __shared__ double P[kCb][kCb + 1];
-  __shared__ double Q[kCb][kCb + 1];
-  const int jb = blockIdx.x;
-  double acc[kCb * kCb / kThreads];
-#pragma unroll
-  for (int q = 0; q < kCb * kCb / kThreads; ++q) acc[q] = 0.0;
-  for (int kb = jb; kb < ib; ++kb) {
-    const double* pl = L + static_cast<size_t>(ib) * kCb * dp + kb * kCb;
-    const double* pq = Li + static_cast<size_t>(kb) * kCb * dp + jb * kCb;
-    __syncthreads();
-    for (int s = threadIdx.x; s < kCb * kCb; s += kThreads) {
-      P[s / kCb][s % kCb] = pl[(s / kCb) * static_cast<size_t>(dp) + s % kCb];
-      Q[s / kCb][s % kCb] = pq[(s / kCb) * static_cast<size_t>(dp) + s % kCb];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < kCb * kCb / kThreads; ++q) {
-      const int s = threadIdx.x + q * kThreads, i = s / kCb, j = s % kCb;
-      double v = 0.0;
-      for (int m = 0; m < kCb; ++m) v += P[i][m] * Q[m][j];
-      acc[q] += v;
-    }
-  }
-  // multiply by -Li[ib][ib]
-  const double* pd = Li + static_cast<size_t>(ib) * kCb * dp + ib * kCb;
-  __syncthreads();
-  for (int s = threadIdx.x; s < kCb * kCb; s += kThreads) P[s / kCb][s % kCb] = pd[(s / kCb) * static_cast<size_t>(dp) + s % kCb];
-#pragma unroll
-  for (int q = 0; q < kCb * kCb / kThreads; ++q) {
-    const int s = threadIdx.x + q * kThreads;
-    Q[s / kCb][s % kCb] = acc[q];
-  }
-  __syncthreads();
-  double* out = Li + static_cast<size_t>(ib) * kCb * dp + jb * kCb;
-  for (int s = threadIdx.x; s < kCb * kCb; s += kThreads) {
-    const int i = s / kCb, j = s % kCb;
-    double v = 0.0;
-    for (int m = 0; m <= i; ++m) v += P[i][m] * Q[m][j];
-    out[i * static_cast<size_t>(dp) + j] = -v;
-  }
-}
-
-// S^-1 = L^-T L^-1: block (ib, jb) = sum_{kb >= max(ib, jb)} Li[kb][ib]^T Li[kb][jb].
-__global__ __launch_bounds__(kThreads) void inv_product_kernel(const double* __restrict__ Li, float* __restrict__ Sinv,
-                                                               int dp) {
-  __shared__ double P[kCb][kCb + 1];
-  __shared__ double Q[kCb][kCb + 1];
+  __shared__ double T[16][kCb + 1];
   const int nb = dp / kCb;
   const int ib = blockIdx.x / nb, jb = blockIdx.x % nb;
-  double acc[kCb * kCb / kThreads];
+  const int c = threadIdx.x & 63, r = threadIdx.x >> 6;
+  for (int p = 0; p < kCb; p += 16) {
+    if (ib <= jb) {
 #pragma unroll
-  for (int q = 0; q < kCb * kCb / kThreads; ++q) acc[q] = 0.0;
-  for (int kb = ib > jb ? ib : jb; kb < nb; ++kb) {
-    const double* pi = Li + static_cast<size_t>(kb) * kCb * dp + ib * kCb;
-    const double* pj = Li + static_cast<size_t>(kb) * kCb * dp + jb * kCb;
+      for (int q = 0; q < 4; ++q) {
+        const int row = p + r + 4 * q;
+        Sinv[static_cast<size_t>(ib * kCb + row) * dp + jb * kCb + c] =
+            static_cast<float>(sacc[static_cast<size_t>(ib * kCb + row) * dp + jb * kCb + c]);
+      }
+      continue;
+    }
+    // rows p..p+15 of lower block (ib, jb) = columns p..p+15 of Z[jb][ib]
     __syncthreads();
-    for (int s = threadIdx.x; s < kCb * kCb; s += kThreads) {
-      P[s / kCb][s % kCb] = pi[(s / kCb) * static_cast<size_t>(dp) + s % kCb];
-      Q[s / kCb][s % kCb] = pj[(s / kCb) * static_cast<size_t>(dp) + s % kCb];
+    for (int s = threadIdx.x; s < 16 * kCb; s += kThreads) {
+      const int zr = s >> 4, zc = s & 15;   // row of Z[jb][ib], column p + zc
+      T[zc][zr] = sacc[static_cast<size_t>(jb * kCb + zr) * dp + ib * kCb + p + zc];
     }
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < kCb * kCb / kThreads; ++q) {
-      const int s = threadIdx.x + q * kThreads, i = s / kCb, j = s % kCb;
-      double v = 0.0;
-      for (int m = 0; m < kCb; ++m) v += P[m][i] * Q[m][j];
-      acc[q] += v;
+    for (int q = 0; q < 4; ++q) {
+      const int row = r + 4 * q;
+      Sinv[static_cast<size_t>(ib * kCb + p + row) * dp + jb * kCb + c] = static_cast<float>(T[row][c]);
     }
-  }
-  float* out = Sinv + static_cast<size_t>(ib) * kCb * dp + jb * kCb;
-#pragma unroll
-  for (int q = 0; q < kCb * kCb / kThreads; ++q) {
-    const int s = threadIdx.x + q * kThreads, i = s / kCb, j = s % kCb;
-    out[i * static_cast<size_t>(dp) + j] = static_cast<float>(acc[q]);
   }
 }
 
@@ -538,36 +689,44 @@ namespace {
 
 // X^T X of one activation batch into `out`: normalised (inv_n, damping) or
 // accumulated (out = beta * out + X^T X).
-void launch_moment(const void* acts, int64_t n_rows, int64_t ld, bool acts_f32, int d, int dp, float* out,
+void launch_moment(const PrecondBlockDev& b, const void* acts, int64_t n_rows, int64_t ld, bool acts_f32, float* out,
                    float inv_n, float damping, int accumulate, float beta, hipStream_t s) {
+  const int d = b.d, dp = b.dp;
   const size_t es = acts_f32 ? 4 : 2;
   const int vec = (reinterpret_cast<uintptr_t>(acts) % 16 == 0) && ((ld * es) % 16 == 0);
-  if (acts_f32) {
-    const int nt = dp / MomCfg<true>::BT;
-    moment_kernel<true><<<nt * (nt + 1) / 2, kThreads, 0, s>>>(acts, n_rows, ld, d, vec, out, dp, inv_n, damping,
-                                                               accumulate, beta);
-  } else {
-    const int nt = dp / MomCfg<false>::BT;
-    moment_kernel<false><<<nt * (nt + 1) / 2, kThreads, 0, s>>>(acts, n_rows, ld, d, vec, out, dp, inv_n, damping,
-                                                                accumulate, beta);
+  const int splits = b.part ? moment_splits(dp, acts_f32, n_rows) : 1;
+  const int bk = acts_f32 ? MomCfg<true>::BK : MomCfg<false>::BK;
+  const int64_t per = splits > 1 ? ((n_rows + splits - 1) / splits + bk - 1) / bk * bk : n_rows;
+  const int used = static_cast<int>((n_rows + per - 1) / per);   // splits that hold rows
+  float* part = used > 1 ? b.part : nullptr;
+  const int nt = dp / (acts_f32 ? MomCfg<true>::BT : MomCfg<false>::BT);
+  const dim3 grid(nt * (nt + 1) / 2, used);
+  if (acts_f32)
+    moment_kernel<true><<<grid, kThreads, 0, s>>>(acts, n_rows, ld, d, vec, out, dp, inv_n, damping, accumulate, beta,
+                                                  part, per);
+  else
+    moment_kernel<false><<<grid, kThreads, 0, s>>>(acts, n_rows, ld, d, vec, out, dp, inv_n, damping, accumulate,
+                                                   beta, part, per);
+  if (part) {
+    const int ns = dp / 64;
+    moment_reduce_kernel<<<4 * (ns * (ns + 1) / 2), kThreads, 0, s>>>(part, used, out, d, dp, inv_n, damping, accumulate,
+                                                                beta);
   }
 }
 
 // S (in b.s) -> float64 Cholesky factor -> its inverse -> S^-1 (float32).
 void factor_and_invert(const PrecondBlockDev& b, uint32_t* flags, hipStream_t s) {
   const int dp = b.dp, nb = dp / kCb;
-  to_f64_kernel<<<256, kThreads, 0, s>>>(b.s, b.l, dp);
+  double* sacc = reinterpret_cast<double*>(b.part);   // the scratch holds dp x dp float64
+  to_f64_kernel<<<256, kThreads, 0, s>>>(b.s, b.l, b.li, sacc, dp);
   for (int jb = 0; jb < nb; ++jb) {
-    potrf_kernel<<<1, kThreads, 0, s>>>(b.l, dp, jb, flags);
+    potrf_kernel<<<1, kPotrfThreads, 0, s>>>(b.l, b.li, dp, jb, flags);
     const int below = nb - jb - 1;
-    if (below > 0) {
-      trsm_kernel<<<below, kThreads, 0, s>>>(b.l, dp, jb);
-      syrk_update_kernel<<<below * (below + 1) / 2, kThreads, 0, s>>>(b.l, dp, jb);
-    }
+    if (below + jb > 0) trsm_kernel<<<below + jb, kThreads, 0, s>>>(b.l, b.li, dp, jb, below);
+    const int npairs = below * (below + 1) / 2, nrhs = below * (jb + 1), nz = (jb + 1) * (jb + 2) / 2;
+    syrk_update_kernel<<<npairs + nrhs + nz, kThreads, 0, s>>>(b.l, b.li, sacc, dp, jb, npairs, nrhs);
   }
-  trinv_diag_kernel<<<nb, kThreads, 0, s>>>(b.l, b.li, dp);
-  for (int ib = 1; ib < nb; ++ib) trinv_offdiag_kernel<<<ib, kThreads, 0, s>>>(b.l, b.li, dp, ib);
-  inv_product_kernel<<<nb * nb, kThreads, 0, s>>>(b.li, b.sinv, dp);
+  sinv_store_kernel<<<nb * nb, kThreads, 0, s>>>(sacc, b.sinv, dp);
 }
 
 }  // namespace
@@ -575,14 +734,14 @@ void factor_and_invert(const PrecondBlockDev& b, uint32_t* flags, hipStream_t s)
 hipError_t launch_precond_refresh(const PrecondBlockDev& b, const void* acts, int64_t n_rows, int64_t ld,
                                   bool acts_f32, float damping, uint32_t* flags, hipStream_t s) {
   const float inv_n = static_cast<float>(1.0 / static_cast<double>(n_rows));
-  launch_moment(acts, n_rows, ld, acts_f32, b.d, b.dp, b.s, inv_n, damping, 0, 0.f, s);
+  launch_moment(b, acts, n_rows, ld, acts_f32, b.s, inv_n, damping, 0, 0.f, s);
   factor_and_invert(b, flags, s);
   return hipGetLastError();
 }
 
 hipError_t launch_precond_accumulate(const PrecondBlockDev& b, const void* acts, int64_t n_rows, int64_t ld,
                                      bool acts_f32, float beta, hipStream_t s) {
-  launch_moment(acts, n_rows, ld, acts_f32, b.d, b.dp, b.acc, 0.f, 0.f, 1, beta, s);
+  launch_moment(b, acts, n_rows, ld, acts_f32, b.acc, 0.f, 0.f, 1, beta, s);
   count_kernel<<<1, 64, 0, s>>>(b.cnt, beta, n_rows);
   return hipGetLastError();
 }

@@ -156,3 +156,70 @@ def test_accumulated_second_moment_over_micro_batches():
     st.close()
     S1 = orc.second_moment_accumulated([orc.bf16_bits_to_f64(p) for p in parts[:3]], 0.5, damp)
     _check_slot0(wl, host, dev, hp, orc.spd_inverse(S1), eye, "decayed 3")
+
+
+def _inverse_via_momentum(d, fill, damping):
+    """S^-1 of one slot as the GPU forms it: a d x d float32 tensor with
+    G = I preconditioned by the slot gives P = S^-1, read back from the
+    momentum buffer (M0 = 0, M' = (1 - mu) P)."""
+    hp = mm.default_hparams()
+    w = torch.zeros(d, d, device="cuda")
+    g = torch.eye(d, device="cuda")
+    m = torch.zeros(d, d, device="cuda")
+    p = B.MuonPrecond()
+    p.d, p.nblocks = d, 1
+    st = mm.MuonStep([mm.tensor_desc(w, g, m, precond=0)], hp, preconds=[p])
+    fill(st)
+    st.step()
+    torch.cuda.synchronize()
+    assert st.flags() == 0
+    st.close()
+    return m.cpu().numpy().astype(np.float64) / (1.0 - hp.momentum)
+
+
+def _acts(n, d, seed, dtype):
+    x = np.random.default_rng(seed).standard_normal((n, d))
+    if dtype == "bf16":
+        bits = synth.to_bf16_bits(x)
+        return orc.bf16_bits_to_f64(bits), to_device(torch, bits, "bf16")
+    x32 = x.astype(np.float32)
+    return x32.astype(np.float64), to_device(torch, x32, "f32")
+
+
+# S^-1 itself against the oracle, over sample counts that leave the second-
+# moment product unsplit (100 rows), split into ragged row ranges (300, 5000
+# rows) and split at every range (4096), for both activation dtypes and a d
+# that is not a multiple of the 64 x 64 Cholesky block.  Damping 1e-2 keeps
+# kappa(S) below ~1e3, so float32 sums (relative error ~1e-6) give S^-1 to
+# ~1e-3 or better; the bar is 2e-3.
+@pytest.mark.parametrize("d", [200, 768])
+@pytest.mark.parametrize("n", [100, 300, 4096, 5000])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_second_moment_inverse_split_rows(d, n, dtype):
+    say(f"case: S^-1 from {n} x {d} {dtype} activations (one refresh)")
+    X, dx = _acts(n, d, 1000 + n + d, dtype)
+    damp = float(np.float32(1e-2))
+    got = _inverse_via_momentum(d, lambda st: st.precond_refresh(0, 0, dx, damping=1e-2), damp)
+    ref = orc.spd_inverse(orc.second_moment(X, damp))
+    e = rel_f(got, ref)
+    say(f"  S^-1 rel {e:.2e}")
+    assert e <= 2e-3
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_second_moment_inverse_accumulated_ragged(dtype):
+    say(f"case: S^-1 accumulated over ragged {dtype} micro-batches (beta 0.5)")
+    d = 200
+    parts = [_acts(n, d, 77 + k, dtype) for k, n in enumerate((300, 700, 33))]
+    damp = float(np.float32(1e-2))
+
+    def fill(st):
+        for _, dx in parts:
+            st.precond_accumulate(0, 0, dx, beta=0.5)
+        st.precond_refresh_accumulated(0, 0, damping=1e-2, reset=True)
+
+    got = _inverse_via_momentum(d, fill, damp)
+    ref = orc.spd_inverse(orc.second_moment_accumulated([X for X, _ in parts], 0.5, damp))
+    e = rel_f(got, ref)
+    say(f"  S^-1 rel {e:.2e}")
+    assert e <= 2e-3
