@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 output for the Muon step kernels.
 
-    python -m matrix_aware_optimizer_muon_amd.profiling trace DIR [--title T] [--command C]
+    python -m matrix_aware_optimizer_muon_amd.profiling trace DIR [--title T] [--command C ...]
         Markdown table of a `rocprofv3 --kernel-trace --stats --output-format csv`
         run (per-kernel calls, total and average duration, grid, LDS bytes).
 
@@ -46,9 +46,9 @@ def kernel_kind(name):
     if m:
         f32 = m.group(1) in ("true", "1")
         return ["gram", "square", "bx"][int(m.group(2))] + ("/f32" if f32 else "")
-    for k, v in (("momentum_kernel", "momentum"), ("update_kernel", "update"), ("copyBuffer", "copy"),
+    for k, v in (("momentum_kernel", "momentum"), ("(?<!syrk_)update_kernel", "update"), ("copyBuffer", "copy"),
                  ("fillBuffer", "fill")):
-        if k in name:
+        if re.search(k, name):   # the Cholesky's syrk_update_kernel is not the update phase
             m2 = re.search(r"<(\w+)>", name) or re.search(r"ILb(\d)E", name)
             f32 = bool(m2) and m2.group(1) in ("true", "1")
             return v + ("/f32" if f32 and v in ("momentum", "update") else "")
@@ -95,9 +95,15 @@ def trace_table(dirpath):
     recs = []
     with open(path) as f:
         for r in csv.DictReader(f):
+            # workgroups over all grid dimensions (the Y and Z sizes are 1
+            # when absent)
             wg = _num(r, "Workgroup_Size_X", "Workgroup_Size", default=1.0) or 1.0
+            groups = int(_num(r, "Grid_Size_X", "Grid_Size", default=0.0) // wg)
+            for d in ("Y", "Z"):
+                wd = _num(r, f"Workgroup_Size_{d}", default=1.0) or 1.0
+                groups *= max(1, int(_num(r, f"Grid_Size_{d}", default=1.0) // wd))
             recs.append((kernel_kind(r.get("Kernel_Name", "")), _num(r, "Start_Timestamp"),
-                         _num(r, "End_Timestamp"), int(_num(r, "Grid_Size_X", "Grid_Size", default=0.0) // wg),
+                         _num(r, "End_Timestamp"), groups,
                          int(_num(r, "Group_Segment_Size", "LDS_Block_Size"))))
     alone = _alone([(a, b) for _, a, b, _, _ in recs])
     rows = {}
@@ -119,9 +125,11 @@ def trace_table(dirpath):
 
 
 def trace_markdown(dirpath, title, command):
+    """`command`: one command line, or a list of them."""
     rows = trace_table(dirpath)
+    lines = [command] if isinstance(command, str) else list(command)
     out = [f"# {title}", "", "Commands (repository root on one MI355X, `libmuon.so` built):", "", "```",
-           command.strip(), "```", "",
+           *[c.strip() for c in lines], "```", "",
            "`alone`: dispatches that overlapped no other dispatch in time.", "",
            "| kernel | calls | total µs | avg µs | % | alone calls | alone avg µs | grid (workgroups) | LDS B |",
            "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
@@ -182,7 +190,7 @@ def main(argv=None):
     t = sub.add_parser("trace")
     t.add_argument("dir")
     t.add_argument("--title", default="Kernel trace")
-    t.add_argument("--command", default="")
+    t.add_argument("--command", action="append", default=[])
     t.add_argument("--out")
     c = sub.add_parser("traffic")
     for a in ("--fetch", "--write", "--copy-fetch", "--copy-write"):

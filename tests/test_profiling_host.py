@@ -36,6 +36,8 @@ def test_kernel_kind_names():
     assert P.kernel_kind("_ZN4muon14ns_gemm_kernelILb1ELi2EEEvPKNS_7UnitDevE") == "bx/f32"
     assert P.kernel_kind("void muon::momentum_kernel<false>(...)") == "momentum"
     assert P.kernel_kind(COPY) == "copy"
+    assert P.kernel_kind("void muon::update_kernel<false>(...)") == "update"
+    assert P.kernel_kind("muon::(anonymous namespace)::syrk_update_kernel(double*, double*)") == "syrk_update_kernel"
 
 
 def test_alone_dispatches():
