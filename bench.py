@@ -139,7 +139,7 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (no collectives); use --gpus 1", file=sys.stderr)
+        print("bench.py: the Muon step here runs on one GPU only (no collectives); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
