@@ -53,22 +53,25 @@ __device__ __forceinline__ void unpack8_bf16(const u32x4_t& w, float* v) {
 }
 
 // Two-part X master of the bf16 Newton-Schulz path: hi = bf16(x) (the MFMA
-// operand) and an int8 correction q with x ~= hi + q * ulp(hi)/256, i.e. 15
-// more bits below hi's last one (|x - hi| <= ulp(hi)/2, so |q| <= 128, kept
-// in [-127, 127]).  For bf16 exponent field E the step ulp(hi)/256 is
-// 2^(E-142) (ldexp underflows gracefully for tiny hi); hi + q*step has at
-// most 16 significant bits, so the float32 sum is exact.
-__device__ __forceinline__ int master_exp(uint32_t hi_bits) { return static_cast<int>((hi_bits >> 7) & 0xFFu); }
-
-// hi (bf16 bits) and q of 8 values; q packed little-endian into 2 words.
+// operand) and an int8 correction q counted in the float32 bit pattern,
+// x ~= float_from_bits(bits(hi) + 256 q).  Within hi's binade 256 float32
+// ulps are ulp_bf16(hi)/256, so q carries 8 more bits below hi's last one
+// (round-to-nearest-even gives |bits(x) - bits(hi)| <= 2^15, so |q| <= 128,
+// kept in [-127, 127]).  Where the rounding carried hi up to a power of two
+// the count runs in the binade below, and the decode, adding in the same bit
+// space, lands there too.  Sign-magnitude patterns make the count a
+// magnitude offset for negative x as well.  Integer arithmetic only: a
+// subtraction and a rounding shift to encode, a shift-add to decode.
 __device__ __forceinline__ void master_encode8(const float* v, u32x4_t& hi, u32x2_t& lo) {
   uint32_t q[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint16_t h = f32_to_bf16(v[e]);
-    const float r = ldexpf(v[e] - bf16_to_f32(h), 142 - master_exp(h));   // exact: a power-of-2 scale
-    q[e] = static_cast<uint32_t>(static_cast<int>(rintf(__builtin_amdgcn_fmed3f(r, -127.f, 127.f)))) & 0xFFu;
-    if (e & 1) hi[e >> 1] |= static_cast<uint32_t>(h) << 16; else hi[e >> 1] = h;
+  for (int e = 0; e < 8; e += 2) {
+    const uint32_t hp = static_cast<uint32_t>(f32_to_bf16(v[e])) | (static_cast<uint32_t>(f32_to_bf16(v[e + 1])) << 16);
+    hi[e >> 1] = hp;
+    const int d0 = __float_as_int(v[e]) - static_cast<int>(hp << 16);
+    const int d1 = __float_as_int(v[e + 1]) - static_cast<int>(hp & 0xFFFF0000u);
+    q[e] = static_cast<uint32_t>(min(max((d0 + 128) >> 8, -127), 127)) & 0xFFu;
+    q[e + 1] = static_cast<uint32_t>(min(max((d1 + 128) >> 8, -127), 127)) & 0xFFu;
   }
   lo[0] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
   lo[1] = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
@@ -77,9 +80,9 @@ __device__ __forceinline__ void master_encode8(const float* v, u32x4_t& hi, u32x
 __device__ __forceinline__ void master_decode8(const u32x4_t& hi, const u32x2_t& lo, float* v) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const uint32_t h = (e & 1) ? (hi[e >> 1] >> 16) : (hi[e >> 1] & 0xFFFFu);
+    const uint32_t h32 = (e & 1) ? (hi[e >> 1] & 0xFFFF0000u) : (hi[e >> 1] << 16);
     const int q = static_cast<int8_t>((lo[e >> 2] >> (8 * (e & 3))) & 0xFFu);
-    v[e] = ldexpf(static_cast<float>(q), master_exp(h) - 142) + __uint_as_float(h << 16);
+    v[e] = __int_as_float(static_cast<int>(h32) + q * 256);
   }
 }
 

@@ -54,7 +54,8 @@ struct UnitDev {
   int32_t side, m, n, mp, np, pad2;
   // workspace buffers (row-major, leading dimension np for X, mp for A/B).
   // bf16 NS: xh is bf16(X) (also the MFMA operand) and xl one int8
-  // correction per element (X ~= xh + xl * ulp(xh)/256); a and b are bf16.
+  // correction per element (X ~= the float32 with bits(xh) + 256 xl, i.e.
+  // xh + xl * ulp(xh)/256 within xh's binade); a and b are bf16.
   // float32 NS: xh is the float32 X, xl is unused, a and b are float32.  xh is double-buffered: the B X phase reads
   // the whole current iterate as an operand while its tiles write the next
   // one; xl is read and written only by the tile that owns each region.
