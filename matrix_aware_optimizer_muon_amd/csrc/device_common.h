@@ -35,13 +35,38 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Two floats to bf16 (round to nearest even) packed in one word, a first,
+// in one conversion instruction.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt2_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 __device__ __forceinline__ u32x4_t pack8_bf16(const float* v) {
   u32x4_t w;
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    w[e] = static_cast<uint32_t>(f32_to_bf16(v[2 * e])) |
-           (static_cast<uint32_t>(f32_to_bf16(v[2 * e + 1])) << 16);
+  for (int e = 0; e < 4; ++e) w[e] = cvt2_bf16(v[2 * e], v[2 * e + 1]);
   return w;
+}
+
+// A wave-uniform pointer held as a computed scalar value: a pointer read from
+// a descriptor in memory may otherwise be re-read from it after each store
+// (a scalar load and a wait per use), since the compiler is free to reload
+// what it knows is unchanged rather than keep it in registers.
+__device__ __forceinline__ int32_t sreg_i32(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t sreg_i64(int64_t v) {
+  const uint64_t u = static_cast<uint64_t>(v);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+template <typename T>
+__device__ __forceinline__ T* sreg_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
 __device__ __forceinline__ void unpack8_bf16(const u32x4_t& w, float* v) {
@@ -66,7 +91,7 @@ __device__ __forceinline__ void master_encode8(const float* v, u32x4_t& hi, u32x
   uint32_t q[8];
 #pragma unroll
   for (int e = 0; e < 8; e += 2) {
-    const uint32_t hp = static_cast<uint32_t>(f32_to_bf16(v[e])) | (static_cast<uint32_t>(f32_to_bf16(v[e + 1])) << 16);
+    const uint32_t hp = cvt2_bf16(v[e], v[e + 1]);
     hi[e >> 1] = hp;
     const int d0 = __float_as_int(v[e]) - static_cast<int>(hp << 16);
     const int d1 = __float_as_int(v[e + 1]) - static_cast<int>(hp & 0xFFFF0000u);

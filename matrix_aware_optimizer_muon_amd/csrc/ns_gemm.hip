@@ -517,6 +517,24 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   const float step = p.lr * u.lr_scale;
   float* ep = reinterpret_cast<float*>(smem) + wave * (32 * EPP);
   constexpr int CITER = WTN * 4 / 64;                // column segments per lane
+  // the output pointers, kept in scalar registers for the whole epilogue;
+  // so are the weight fields of the last iteration's update (wu: a copy of
+  // the descriptor whose fields the update reads are pinned)
+  void* const out_ab = PH == kGram ? sreg_ptr(u.a) : PH == kSquare ? sreg_ptr(u.b) : nullptr;
+  void* const out_xh = PH == kBX ? sreg_ptr(u.xh[p.x_in ^ 1]) : nullptr;
+  int8_t* const out_xl = PH == kBX ? sreg_ptr(static_cast<int8_t*>(u.xl)) : nullptr;
+  UnitDev wu;
+  if (last) {
+    wu.param = sreg_ptr(u.param);
+    wu.ld_param = sreg_i64(u.ld_param);
+    wu.param_f32 = sreg_i32(u.param_f32);
+    wu.vec_param = sreg_i32(u.vec_param);
+    wu.update_out = sreg_ptr(u.update_out);
+    wu.ld_out = sreg_i64(u.ld_out);
+    wu.vec_out = sreg_i32(u.vec_out);
+    wu.rows = sreg_i32(u.rows);
+    wu.cols = sreg_i32(u.cols);
+  }
 
   // acc and the master registers are only ever indexed with constants (a
   // runtime index would move the whole array to scratch memory), so the
@@ -539,7 +557,7 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
       if constexpr (PH == kGram) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] *= scale;
-        st8<F32>(u.a, static_cast<size_t>(gr) * mp + gc, v);
+        st8<F32>(out_ab, static_cast<size_t>(gr) * mp + gc, v);
       } else if constexpr (PH == kSquare) {
         float av[8];                                      // A at this segment, captured from LDS
         if constexpr (F32) {
@@ -553,7 +571,7 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = fmaf(p.b, av[e], p.c * v[e]);
-        st8<F32>(u.b, static_cast<size_t>(gr) * mp + gc, v);
+        st8<F32>(out_ab, static_cast<size_t>(gr) * mp + gc, v);
         if (mirror) {   // the mirror pass stores B^T from the staged values
           *reinterpret_cast<f32x4_t*>(&ep[row * EPP + cseg * 8]) = f32x4_t{v[0], v[1], v[2], v[3]};
           *reinterpret_cast<f32x4_t*>(&ep[row * EPP + cseg * 8 + 4]) = f32x4_t{v[4], v[5], v[6], v[7]};
@@ -574,18 +592,18 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
         for (int e = 0; e < 8; ++e) v[e] = scale * fmaf(p.a, xm[e], v[e]);
         if (!last) {
           if constexpr (F32) {
-            st8<true>(u.xh[p.x_in ^ 1], off, v);
+            st8<true>(out_xh, off, v);
           } else {
             u32x4_t hq;
             u32x2_t lq;
             master_encode8(v, hq, lq);
-            gst(static_cast<uint16_t*>(u.xh[p.x_in ^ 1]) + off, hq);
-            gst(static_cast<int8_t*>(u.xl) + off, lq);
+            gst(static_cast<uint16_t*>(out_xh) + off, hq);
+            gst(out_xl + off, lq);
           }
         } else if (u.side == kLeft) {
-          if (gr < u.rows) {
-            if (wfast && gc + 8 <= u.cols) update_w8_loaded(u, gr, gc, v, decay, step, wpre[pi][q]);
-            else update_w8(u, gr, gc, v, decay, step);
+          if (gr < wu.rows) {
+            if (wfast && gc + 8 <= wu.cols) update_w8_loaded(wu, gr, gc, v, decay, step, wpre[pi][q]);
+            else update_w8(wu, gr, gc, v, decay, step);
           }
         } else {
           *reinterpret_cast<f32x4_t*>(&ep[row * EPP + cseg * 8]) = f32x4_t{v[0], v[1], v[2], v[3]};
@@ -607,19 +625,19 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
         if constexpr (PH == kGram) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] *= scale;
-          st8<F32>(u.a, static_cast<size_t>(gc) * mp + gr, v);
+          st8<F32>(out_ab, static_cast<size_t>(gc) * mp + gr, v);
         } else if constexpr (PH == kSquare) {
-          st8<F32>(u.b, static_cast<size_t>(gc) * mp + gr, v);   // B is symmetric off the diagonal tiles
+          st8<F32>(out_ab, static_cast<size_t>(gc) * mp + gr, v);   // B is symmetric off the diagonal tiles
         } else {
           // tall matrix: O[i][j] = X[j][i], so X column gc is weight row gc
-          if (gc < u.rows) {
+          if (gc < wu.rows) {
             if constexpr (!F32) {
-              if (wfast && gr + 8 <= u.cols) {
-                update_w8_loaded(u, gc, gr, v, decay, step, wpre[pi][q]);
+              if (wfast && gr + 8 <= wu.cols) {
+                update_w8_loaded(wu, gc, gr, v, decay, step, wpre[pi][q]);
                 continue;
               }
             }
-            update_w8(u, gc, gr, v, decay, step);
+            update_w8(wu, gc, gr, v, decay, step);
           }
         }
       }
