@@ -258,8 +258,12 @@ def main():
             nbytes[k] += v
     elems = sum(s.rows * s.cols for s in wl.tensors if s.kind == "muon")
     # P = G S^-1: per preconditioned tensor rows x (cols/d blocks) x d x d
-    # multiply-adds in float32; G read (stored dtype), P written (float32)
+    # multiply-adds of a float32 GEMM; G read (stored dtype), P written
+    # (float32).  The kernel forms it from bf16 plane products: three per
+    # float32 product for a bf16 G, six for a float32 G (apply_mfma_flops).
     flops["precond_apply"] = sum(2 * s.rows * s.cols * wl.act_dim for s in wl.tensors if s.precond >= 0)
+    apply_mfma_flops = sum((6 if s.dtype == "f32" else 3) * 2 * s.rows * s.cols * wl.act_dim
+                           for s in wl.tensors if s.precond >= 0)
     nbytes["precond_apply"] = sum(s.rows * s.cols * ((4 if s.dtype == "f32" else 2) + 4)
                                   for s in wl.tensors if s.precond >= 0)
     nbytes["momentum"] = 13 * elems          # G (bf16) + M read, M + X master (hi, int8) written
@@ -284,7 +288,14 @@ def main():
     # two lanes each phase is two launches of about half the work)
     per_launch_flops = flops.get(dom, 0) * iters[dom] / launches[dom]
     per_launch_bytes = nbytes[dom] * iters[dom] / launches[dom]
-    peak = PEAK_F32_TFLOPS if dom == "precond_apply" else PEAK_BF16_TFLOPS   # float32 MFMA
+    # the NS phases run on bf16 MFMA unless every unit takes the float32 path
+    # (float32 matrices, or a short side under 128); the apply issues bf16
+    # plane products
+    ns_f32_only = bool(units) and all(es == 4 for _, _, es, _ in units)
+    peak = PEAK_F32_TFLOPS if (ns_f32_only and dom in ("gram", "square", "bx")) else PEAK_BF16_TFLOPS
+    if dom == "precond_apply":                 # priced by the bf16 MFMA work it issues
+        intensity = apply_mfma_flops / nbytes[dom]
+        per_launch_flops = apply_mfma_flops / launches[dom]
     if dom in flops and intensity >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
         achieved = per_launch_flops / (avg[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
@@ -332,7 +343,9 @@ def main():
         "cpu_baseline": None,
     }
     if precond_info is not None:
-        precond_info["apply_tflops_f32"] = round(flops["precond_apply"] / (totals["precond_apply"] * 1e-3) / 1e12, 2)
+        t_apply = totals["precond_apply"] * 1e-3
+        precond_info["apply_tflops"] = round(flops["precond_apply"] / t_apply / 1e12, 2)          # float32 GEMM work
+        precond_info["apply_mfma_tflops"] = round(apply_mfma_flops / t_apply / 1e12, 2)           # bf16 plane products
         out["precond"] = precond_info
     if args.workload != "gpt2s":
         out["metric"] = f"Muon steps/sec, {args.workload} weight set (not the headline workload)"

@@ -15,8 +15,9 @@
 //                      by blocked forward substitution of L X = I
 //   sinv_store         S^-1 = L^-T L^-1 (summed in float64 during the
 //                      factorisation), stored as float32
-//   apply_kernel       P = G S^-1 (block-wise for block-diagonal S), float32
-//                      MFMA, read by the momentum phase in place of G.
+//   apply_kernel       P = G S^-1 (block-wise for block-diagonal S), a float32
+//                      product formed from exact bf16 planes on bf16 MFMA,
+//                      read by the momentum phase in place of G.
 #include "device_common.h"
 #include "muon_internal.h"
 
@@ -566,90 +567,176 @@ __global__ __launch_bounds__(kThreads) void sinv_store_kernel(const double* __re
 
 // ---------------------------------------------------------------- apply
 // P[i][k*d + j] = sum_c G[i][k*d + c] * Sinv_k[j][c]   (S^-1 is symmetric,
-// so its rows are the K-contiguous operand).  64x64 output tiles, 4 waves of
-// 32x32, float32 MFMA 32x32x2; G (bf16 or float32) is converted to float32
-// while it is staged.
-__global__ __launch_bounds__(kThreads)
-void apply_kernel(const PrecondDev* __restrict__ pds, const ApplyTask* __restrict__ tasks) {
-  constexpr int BT = 64, WT = 32, BK = 32, LDA = BK + 4, EPP = WT + 8;
-  constexpr int TILE = BT * LDA;
-  static_assert(4 * 32 * EPP <= 4 * TILE, "epilogue staging");
-  __shared__ __attribute__((aligned(16))) float smem[4 * TILE];   // [operand][buf][BT][LDA]
-  auto sa = [&](int buf, int r, int k) -> float* { return smem + buf * TILE + r * LDA + k; };
-  auto sb = [&](int buf, int r, int k) -> float* { return smem + (2 + buf) * TILE + r * LDA + k; };
-  const ApplyTask t = tasks[blockIdx.x];
-  const PrecondDev& pd = pds[t.tensor];
+// so its rows are the K-contiguous operand).  The float32 product is formed
+// on bf16 matrix cores: while a tile is staged, each float32 value x is
+// split into three bf16 planes, x = h + m + l exactly (h = bf16(x),
+// m = bf16(x - h), l = x - h - m, which has at most 8 significant bits), and
+// the tile product sums the plane products i + j <= 2 with float32
+// accumulation (bf16 products are exact in float32).  A bf16 gradient is its
+// own single plane, so P = G (h + m + l) is the float32 GEMM up to the order
+// of the additions; a float32 gradient drops only the products of two small
+// planes (each below 2^-16 of the leading one).  64x64 output tiles, 4 waves
+// of 32x32 (v_mfma_f32_32x32x16_bf16), 32-deep K stages double-buffered in
+// LDS with a padded row pitch (conflict-free 16-byte fragment reads).
+constexpr int kApBT = 64, kApBK = 32, kApLDK = kApBK + 8;
+constexpr int kApPlane = kApBT * kApLDK;             // bf16 elements per plane
+constexpr int kApSmem = 2 * 6 * kApPlane;             // two stages of up to 3 + 3 planes
+
+template <bool GF32, bool VEC>
+__device__ __forceinline__ void apply_tile(const PrecondDev& pd, const ApplyTask& t, uint16_t* smem) {
+  constexpr int BT = kApBT, WT = 32, BK = kApBK, LDK = kApLDK, EPP = WT + 8;
+  constexpr int NG = GF32 ? 3 : 1;                 // planes of the gradient tile
+  constexpr int PLANE = kApPlane;
+  constexpr int STAGE = (NG + 3) * PLANE;
+  static_assert(2 * STAGE <= kApSmem, "stages fit");
+  static_assert(4 * 32 * EPP * 4 <= 2 * STAGE * 2, "epilogue staging");
   const int d = pd.d, dp = pd.dp;
   const int r0 = t.tr * BT, c0 = t.tc * BT;            // rows of G, columns within block t.blk
   const int gcol0 = t.blk * d;                          // first column of the block in G and P
   const float* sinv = pd.sinv + static_cast<size_t>(t.blk) * dp * dp;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int lrow = tid >> 3, lk = (tid & 7) * 4;        // 32 rows x 8 chunks of 4 per pass
+  const int lrow = tid >> 2, lk = (tid & 3) * 8;        // 64 rows x 4 chunks of 8 per stage
 
   f32x16_t acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
-  f32x4_t ra[2], rb[2];
-  auto gload = [&](int k0) {
+  // NR register sets of staged operands (stage kt+s in set (kt+s) % NR),
+  // used with static indices: the loop is unrolled by NR.
+  // The gradient is staged as raw bits (8 bf16, or 8 float32 in two words
+  // of four) and decoded only when the tile is stored, so no wait follows
+  // a load.  Aligned rows (VEC) take a branch-free path: the address is clamped
+  // into the tensor and a chunk outside it (rows past the end, columns past
+  // d, which is a multiple of 8 there) is zeroed at decode time.
+  constexpr int GW = GF32 ? 2 : 1;
+  constexpr int NR = 4;
+  u32x4_t gr[NR][GW];
+  bool gok[NR];
+  float sb[NR][8];
+  auto gload = [&](int k0, u32x4_t (&g)[GW], bool& ok, float (&sv)[8]) {
+    const int gi = r0 + lrow, kc = k0 + lk;
+    ok = gi < pd.rows && kc < d;
+    if constexpr (VEC) {
+      const int gic = gi < pd.rows ? gi : pd.rows - 1, kcc = kc < d ? kc : 0;
+      const size_t off = static_cast<size_t>(gic) * pd.ld_grad + gcol0 + kcc;
+      if constexpr (GF32) {
+        g[0] = gld<u32x4_t>(static_cast<const float*>(pd.grad) + off);
+        g[1] = gld<u32x4_t>(static_cast<const float*>(pd.grad) + off + 4);
+      } else {
+        g[0] = gld<u32x4_t>(static_cast<const uint16_t*>(pd.grad) + off);
+      }
+    } else {   // unaligned rows: element loads, packed into the same raw layout
+      float v[8];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int row = lrow + 32 * q;
-      // operand A: G rows r0+row, columns k0+lk.. of the block (bounds-checked)
-      const int gi = r0 + row, kc = k0 + lk;
-      f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
       if (gi < pd.rows) {
         const size_t off = static_cast<size_t>(gi) * pd.ld_grad + gcol0 + kc;
-        if (pd.vec_grad && kc + 4 <= d) {
-          if (pd.grad_f32) {
-            v = gld<f32x4_t>(static_cast<const float*>(pd.grad) + off);
-          } else {
-            const u32x2_t w = gld<u32x2_t>(static_cast<const uint16_t*>(pd.grad) + off);
-            v[0] = __uint_as_float(w[0] << 16); v[1] = __uint_as_float(w[0] & 0xffff0000u);
-            v[2] = __uint_as_float(w[1] << 16); v[3] = __uint_as_float(w[1] & 0xffff0000u);
-          }
-        } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (kc + e < d)
-              v[e] = pd.grad_f32 ? gld<float>(static_cast<const float*>(pd.grad) + off + e)
-                                 : bf16_to_f32(gld<uint16_t>(static_cast<const uint16_t*>(pd.grad) + off + e));
-        }
+        for (int e = 0; e < 8; ++e)
+          if (kc + e < d)
+            v[e] = GF32 ? gld<float>(static_cast<const float*>(pd.grad) + off + e)
+                        : bf16_to_f32(gld<uint16_t>(static_cast<const uint16_t*>(pd.grad) + off + e));
       }
-      ra[q] = v;
-      // operand B: rows c0+row of S^-1 (padded to dp, always in bounds)
-      rb[q] = gld<f32x4_t>(sinv + static_cast<size_t>(c0 + row) * dp + k0 + lk);
-    }
-  };
-  auto sstore = [&](int buf) {
+      if constexpr (GF32) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      *reinterpret_cast<f32x4_t*>(sa(buf, lrow + 32 * q, lk)) = ra[q];
-      *reinterpret_cast<f32x4_t*>(sb(buf, lrow + 32 * q, lk)) = rb[q];
+        for (int e = 0; e < 4; ++e) {
+          g[0][e] = __float_as_uint(v[e]);
+          g[1][e] = __float_as_uint(v[4 + e]);
+        }
+      } else {
+        g[0] = pack8_bf16(v);   // exact: the values are bf16
+      }
+      ok = true;
+    }
+    // operand B: row c0+lrow of S^-1 (padded to dp, always in bounds)
+    const float* sp = sinv + static_cast<size_t>(c0 + lrow) * dp + k0 + lk;
+    const f32x4_t s0 = gld<f32x4_t>(sp), s1 = gld<f32x4_t>(sp + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { sv[e] = s0[e]; sv[4 + e] = s1[e]; }
+  };
+  // split 8 floats into bf16 planes h, m, l and store them (16 bytes each)
+  auto split_store = [&](const float* x, int nplanes, uint16_t* dst) {
+    float r[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = x[e];
+#pragma unroll
+    for (int pl = 0; pl < 3; ++pl) {
+      if (pl >= nplanes) break;
+      u32x4_t w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = cvt2_bf16(r[2 * e], r[2 * e + 1]);
+      *reinterpret_cast<u32x4_t*>(dst + pl * PLANE) = w;
+      if (pl + 1 < nplanes) {
+        float hv[8];
+        unpack8_bf16(w, hv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] -= hv[e];   // exact: the residual of a round-to-nearest
+      }
     }
   };
-  const int KT = dp / BK;
-  gload(0);
-  sstore(0);
+  auto sstore = [&](int buf, const u32x4_t (&g)[GW], bool ok, const float (&sv)[8]) {
+    uint16_t* st = smem + buf * STAGE + lrow * LDK + lk;
+    float gv[8];
+    if constexpr (GF32) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        gv[e] = __uint_as_float(g[0][e]);
+        gv[4 + e] = __uint_as_float(g[1][e]);
+      }
+    } else {
+      unpack8_bf16(g[0], gv);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gv[e] = ok ? gv[e] : 0.f;
+    split_store(gv, NG, st);
+    split_store(sv, 3, st + NG * PLANE);
+  };
+  // K pipeline: LDS buffer kt&1 holds stage kt; iteration kt requests
+  // stage kt+3 (into the set stage kt-1 left, stored two iterations ago),
+  // runs the MFMAs of stage kt, then stores stage kt+1, requested two
+  // iterations earlier, so a full iteration separates each load from its
+  // use.  Stage indices past the end are clamped to the last stage and every
+  // request is stored (the copies land in a buffer nobody reads again), so
+  // on every path each set's loads are consumed before the set is reloaded
+  // and the compiler's waits cover only the stage being stored.
+  const int KT = dp / BK;                          // a multiple of 4 (dp is of 128)
+  static_assert(NR == 4, "KT is a multiple of the unroll");
+  gload(0, gr[0], gok[0], sb[0]);
+  gload(BK, gr[1], gok[1], sb[1]);
+  gload(2 * BK, gr[2], gok[2], sb[2]);
+  sstore(0, gr[0], gok[0], sb[0]);
   __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < KT;
-    if (more) gload((kt + 1) * BK);
-    const int k0 = (lane >> 5) * 16;
+  for (int k4 = 0; k4 < KT; k4 += NR)
 #pragma unroll
-    for (int kq = 0; kq < 4; ++kq) {
-      const f32x4_t a = *reinterpret_cast<const f32x4_t*>(sa(buf, wm * WT + (lane & 31), k0 + kq * 4));
-      const f32x4_t b = *reinterpret_cast<const f32x4_t*>(sb(buf, wn * WT + (lane & 31), k0 + kq * 4));
+  for (int h = 0; h < NR; ++h) {
+    const int kt = k4 + h, buf = h & 1;
+    gload(min(kt + 3, KT - 1) * BK, gr[(h + 3) % NR], gok[(h + 3) % NR], sb[(h + 3) % NR]);
+    const uint16_t* st = smem + buf * STAGE;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], acc, 0, 0, 0);
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int kk = ks * 16 + 8 * (lane >> 5);
+      bf16x8_t fa[NG], fb[3];
+#pragma unroll
+      for (int pl = 0; pl < NG; ++pl)
+        fa[pl] = *reinterpret_cast<const bf16x8_t*>(st + pl * PLANE + (wm * WT + (lane & 31)) * LDK + kk);
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl)
+        fb[pl] = *reinterpret_cast<const bf16x8_t*>(st + (NG + pl) * PLANE + (wn * WT + (lane & 31)) * LDK + kk);
+      // small products first
+#pragma unroll
+      for (int sum = 2; sum >= 0; --sum)
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+          const int j = sum - i;
+          if (j >= 0 && j < 3) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc, 0, 0, 0);
+        }
     }
-    if (more) sstore(buf ^ 1);
+    sstore(buf ^ 1, gr[(h + 1) % NR], gok[(h + 1) % NR], sb[(h + 1) % NR]);
     __syncthreads();
   }
   // epilogue through LDS: row segments of P
-  float* ep = smem + wave * (32 * EPP);
+  float* ep = reinterpret_cast<float*>(smem) + wave * (32 * EPP);
 #pragma unroll
   for (int r = 0; r < 16; ++r) ep[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * EPP + (lane & 31)] = acc[r];
   __syncthreads();
@@ -657,6 +744,21 @@ void apply_kernel(const PrecondDev* __restrict__ pds, const ApplyTask* __restric
     const int row = s / WT, col = s % WT;
     const int gi = r0 + wm * WT + row, cj = c0 + wn * WT + col;
     if (gi < pd.rows && cj < d) pd.p[static_cast<size_t>(gi) * pd.ld_p + gcol0 + cj] = ep[row * EPP + col];
+  }
+}
+
+__global__ __launch_bounds__(kThreads)
+void apply_kernel(const PrecondDev* __restrict__ pds, const ApplyTask* __restrict__ tasks) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kApSmem];   // [buf][G planes, S planes][BT][LDK]
+  const ApplyTask t = tasks[blockIdx.x];
+  const PrecondDev& pd = pds[t.tensor];
+  // both flags are uniform over the block
+  if (pd.grad_f32) {
+    if (pd.vec_grad) apply_tile<true, true>(pd, t, smem);
+    else apply_tile<true, false>(pd, t, smem);
+  } else {
+    if (pd.vec_grad) apply_tile<false, true>(pd, t, smem);
+    else apply_tile<false, false>(pd, t, smem);
   }
 }
 

@@ -223,3 +223,42 @@ def test_second_moment_inverse_accumulated_ragged(dtype):
     e = rel_f(got, ref)
     say(f"  S^-1 rel {e:.2e}")
     assert e <= 2e-3
+
+
+@pytest.mark.parametrize("gdtype", ["bf16", "f32"])
+def test_apply_is_the_float32_product(gdtype):
+    """P = G S^-1 against float64 products with the GPU's own S^-1 (read
+    through a G = I tensor on the same slot), so only the apply's arithmetic
+    is measured.  The apply splits float32 operands into bf16 planes; with
+    float32 accumulation over K = 200 the bar is 1e-5 relative (Frobenius)."""
+    say(f"case: P = G S^-1 arithmetic, {gdtype} gradient")
+    d = 200
+    hp = mm.default_hparams()
+    X, dx = _acts(1000, d, 4242, "f32")
+    rng = np.random.default_rng(99)
+    Graw = rng.standard_normal((300, d)) * np.exp(rng.uniform(-2, 2, (300, 1)))
+    if gdtype == "bf16":
+        gbits = synth.to_bf16_bits(Graw)
+        G = orc.bf16_bits_to_f64(gbits)
+        g = to_device(torch, gbits, "bf16")
+        w = torch.zeros(300, d, dtype=torch.bfloat16, device="cuda")
+    else:
+        G = Graw.astype(np.float32).astype(np.float64)
+        g = to_device(torch, G, "f32")
+        w = torch.zeros(300, d, device="cuda")
+    m = torch.zeros(300, d, device="cuda")
+    wi, gi, mi = torch.zeros(d, d, device="cuda"), torch.eye(d, device="cuda"), torch.zeros(d, d, device="cuda")
+    p = B.MuonPrecond()
+    p.d, p.nblocks = d, 1
+    st = mm.MuonStep([mm.tensor_desc(wi, gi, mi, precond=0), mm.tensor_desc(w, g, m, precond=0)], hp, preconds=[p])
+    st.precond_refresh(0, 0, dx, damping=1e-2)
+    st.step()
+    torch.cuda.synchronize()
+    assert st.flags() == 0
+    st.close()
+    scale = 1.0 / (1.0 - hp.momentum)
+    S_inv = mi.cpu().numpy().astype(np.float64) * scale
+    P = m.cpu().numpy().astype(np.float64) * scale
+    e = rel_f(P, G @ S_inv)
+    say(f"  P rel to G S^-1 (float64 products) {e:.2e}")
+    assert e <= 1e-5
