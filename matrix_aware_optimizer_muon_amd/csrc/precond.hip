@@ -51,9 +51,11 @@ template <> struct MomCfg<true> {
   static constexpr int BT = 64, WT = 32, BK = 32, XPAD = 4;
 };
 
-template <bool F32>
+// VEC: 16-byte aligned rows and d a multiple of a chunk (every chunk lies
+// wholly inside or wholly outside the d columns).
+template <bool F32, bool VEC>
 __global__ __launch_bounds__(kThreads)
-void moment_kernel(const void* __restrict__ acts, int64_t n_rows, int64_t ld, int d, int vec,
+void moment_kernel(const void* __restrict__ acts, int64_t n_rows, int64_t ld, int d,
                    float* __restrict__ S, int dp, float inv_n, float damping, int accumulate, float beta,
                    float* __restrict__ part, int64_t split_rows) {
   using C = MomCfg<F32>;
@@ -91,45 +93,70 @@ void moment_kernel(const void* __restrict__ acts, int64_t n_rows, int64_t ld, in
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // load one chunk (EPE elements) of the slab, zero outside the tensor
-  auto load_chunk = [&](int64_t r, int c) -> u32x4_t {
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (r >= r_end || c >= d) return v;
-    const size_t off = static_cast<size_t>(r) * ld + c;
-    if (vec && c + EPE <= d) return gld<u32x4_t>(static_cast<const E*>(acts) + off);
-    E tmp[EPE];
+  // K pipeline: NR register sets of staged chunks (stage s in set s % NR)
+  // and two LDS buffers.  Iteration kt requests stage kt+3, runs the MFMAs
+  // of stage kt and stores stage kt+1 (requested two iterations earlier).
+  // Every request is issued and stored (stage indices clamped, KT rounded
+  // up to the unroll: stages past the rows are all zero), so the waits the
+  // compiler places cover only the stage being stored.  A chunk outside the
+  // tensor (rows past this block's range, columns past d) is loaded from a
+  // clamped address and zeroed when it is stored.
+  constexpr int NR = 4;
+  const int ca = ti * BT + bchunk * EPE, cb = tj * BT + bchunk * EPE;   // this thread's columns
+  const bool ca_ok = ca < d, cb_ok = cb < d;
+  u32x4_t ra[NR][NPX], rb[NR][NPX];
+  uint32_t rok[NR];                                  // bit q: row of chunk q inside the range
+  auto load_chunk = [&](int64_t r, int c, bool ok) -> u32x4_t {
+    if constexpr (VEC) {
+      const int64_t rc = r < r_end ? r : r_end - 1;
+      const size_t off = static_cast<size_t>(rc) * ld + (ok ? c : 0);
+      return gld<u32x4_t>(static_cast<const E*>(acts) + off);
+    } else {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (r >= r_end || !ok) return v;
+      const size_t off = static_cast<size_t>(r) * ld + c;
+      E tmp[EPE];
 #pragma unroll
-    for (int e = 0; e < EPE; ++e) tmp[e] = (c + e < d) ? gld<E>(static_cast<const E*>(acts) + off + e) : E(0);
-    return __builtin_bit_cast(u32x4_t, tmp);
+      for (int e = 0; e < EPE; ++e) tmp[e] = (c + e < d) ? gld<E>(static_cast<const E*>(acts) + off + e) : E(0);
+      return __builtin_bit_cast(u32x4_t, tmp);
+    }
   };
-
-  u32x4_t ra[NPX], rb[NPX];
-  const int KT = static_cast<int>((r_end - r_begin + BK - 1) / BK);
-  auto gload = [&](int kt) {
+  const int KT0 = static_cast<int>((r_end - r_begin + BK - 1) / BK);
+  const int KT = (KT0 + NR - 1) / NR * NR;
+  auto gload = [&](int kt, u32x4_t (&a)[NPX], u32x4_t (&b)[NPX], uint32_t& ok) {
+    ok = 0;
 #pragma unroll
     for (int q = 0; q < NPX; ++q) {
       const int64_t r = r_begin + static_cast<int64_t>(kt) * BK + brow + q * RPPX;
-      ra[q] = load_chunk(r, ti * BT + bchunk * EPE);
-      rb[q] = load_chunk(r, tj * BT + bchunk * EPE);
+      ok |= (r < r_end ? 1u : 0u) << q;
+      a[q] = load_chunk(r, ca, ca_ok);
+      b[q] = load_chunk(r, cb, cb_ok);
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, const u32x4_t (&a)[NPX], const u32x4_t (&b)[NPX], uint32_t ok) {
+    const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int q = 0; q < NPX; ++q) {
-      *reinterpret_cast<u32x4_t*>(&smem[(buf * 2 + 0) * TILE + (brow + q * RPPX) * LDX + bchunk * EPE]) = ra[q];
-      *reinterpret_cast<u32x4_t*>(&smem[(buf * 2 + 1) * TILE + (brow + q * RPPX) * LDX + bchunk * EPE]) = rb[q];
+      const bool rq = (ok >> q) & 1u;
+      *reinterpret_cast<u32x4_t*>(&smem[(buf * 2 + 0) * TILE + (brow + q * RPPX) * LDX + bchunk * EPE]) =
+          rq && ca_ok ? a[q] : z;
+      *reinterpret_cast<u32x4_t*>(&smem[(buf * 2 + 1) * TILE + (brow + q * RPPX) * LDX + bchunk * EPE]) =
+          rq && cb_ok ? b[q] : z;
     }
   };
 
-  gload(0);
-  sstore(0);
+  gload(0, ra[0], rb[0], rok[0]);
+  gload(min(1, KT - 1), ra[1], rb[1], rok[1]);
+  gload(min(2, KT - 1), ra[2], rb[2], rok[2]);
+  sstore(0, ra[0], rb[0], rok[0]);
   __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
+  for (int k4 = 0; k4 < KT; k4 += NR)
+#pragma unroll
+  for (int h = 0; h < NR; ++h) {
+    const int kt = k4 + h, buf = h & 1;
     const E* la = smem + (buf * 2 + 0) * TILE;
     const E* lb = smem + (buf * 2 + 1) * TILE;
-    const bool more = kt + 1 < KT;
-    if (more) gload(kt + 1);
+    gload(min(kt + 3, KT - 1), ra[(h + 3) % NR], rb[(h + 3) % NR], rok[(h + 3) % NR]);
     if constexpr (!F32) {
       const int g = lane >> 4, r = lane & 15;
 #pragma unroll
@@ -167,7 +194,7 @@ void moment_kernel(const void* __restrict__ acts, int64_t n_rows, int64_t ld, in
                 lb[(k0 + e) * LDX + wn * WT + j * 32 + (lane & 31)], acc[i][j], 0, 0, 0);
       }
     }
-    if (more) sstore(buf ^ 1);
+    sstore(buf ^ 1, ra[(h + 1) % NR], rb[(h + 1) % NR], rok[(h + 1) % NR]);
     __syncthreads();
   }
 
@@ -817,7 +844,7 @@ void launch_moment(const PrecondBlockDev& b, const void* acts, int64_t n_rows, i
                    float inv_n, float damping, int accumulate, float beta, hipStream_t s) {
   const int d = b.d, dp = b.dp;
   const size_t es = acts_f32 ? 4 : 2;
-  const int vec = (reinterpret_cast<uintptr_t>(acts) % 16 == 0) && ((ld * es) % 16 == 0);
+  const bool vec = (reinterpret_cast<uintptr_t>(acts) % 16 == 0) && ((ld * es) % 16 == 0) && (d * es) % 16 == 0;
   const int splits = b.part ? moment_splits(dp, acts_f32, n_rows) : 1;
   const int bk = acts_f32 ? MomCfg<true>::BK : MomCfg<false>::BK;
   const int64_t per = splits > 1 ? ((n_rows + splits - 1) / splits + bk - 1) / bk * bk : n_rows;
@@ -825,12 +852,21 @@ void launch_moment(const PrecondBlockDev& b, const void* acts, int64_t n_rows, i
   float* part = used > 1 ? b.part : nullptr;
   const int nt = dp / (acts_f32 ? MomCfg<true>::BT : MomCfg<false>::BT);
   const dim3 grid(nt * (nt + 1) / 2, used);
-  if (acts_f32)
-    moment_kernel<true><<<grid, kThreads, 0, s>>>(acts, n_rows, ld, d, vec, out, dp, inv_n, damping, accumulate, beta,
-                                                  part, per);
-  else
-    moment_kernel<false><<<grid, kThreads, 0, s>>>(acts, n_rows, ld, d, vec, out, dp, inv_n, damping, accumulate,
-                                                   beta, part, per);
+  if (acts_f32) {
+    if (vec)
+      moment_kernel<true, true><<<grid, kThreads, 0, s>>>(acts, n_rows, ld, d, out, dp, inv_n, damping, accumulate,
+                                                          beta, part, per);
+    else
+      moment_kernel<true, false><<<grid, kThreads, 0, s>>>(acts, n_rows, ld, d, out, dp, inv_n, damping, accumulate,
+                                                           beta, part, per);
+  } else {
+    if (vec)
+      moment_kernel<false, true><<<grid, kThreads, 0, s>>>(acts, n_rows, ld, d, out, dp, inv_n, damping, accumulate,
+                                                           beta, part, per);
+    else
+      moment_kernel<false, false><<<grid, kThreads, 0, s>>>(acts, n_rows, ld, d, out, dp, inv_n, damping,
+                                                            accumulate, beta, part, per);
+  }
   if (part) {
     const int ns = dp / 64;
     moment_reduce_kernel<<<4 * (ns * (ns + 1) / 2), kThreads, 0, s>>>(part, used, out, d, dp, inv_n, damping, accumulate,
