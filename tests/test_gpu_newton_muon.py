@@ -262,3 +262,19 @@ def test_apply_is_the_float32_product(gdtype):
     e = rel_f(P, G @ S_inv)
     say(f"  P rel to G S^-1 (float64 products) {e:.2e}")
     assert e <= 1e-5
+
+
+# The factorisation at its extremes: one 64 x 64 block (no panel or trailing
+# update; the last step's S^-1 launch only), and d = 1600 (26 blocks, up to
+# 325 trailing-update and 325 right-hand-side blocks in one launch).
+@pytest.mark.parametrize("d", [64, 1600])
+@pytest.mark.parametrize("n", [300, 5000])
+def test_second_moment_inverse_block_counts(d, n):
+    say(f"case: S^-1 from {n} x {d} bf16 activations ({-(-d // 64)} Cholesky blocks)")
+    X, dx = _acts(n, d, 7000 + n + d, "bf16")
+    damp = float(np.float32(1e-2))
+    got = _inverse_via_momentum(d, lambda st: st.precond_refresh(0, 0, dx, damping=1e-2), damp)
+    ref = orc.spd_inverse(orc.second_moment(X, damp))
+    e = rel_f(got, ref)
+    say(f"  S^-1 rel {e:.2e}  (kappa {np.linalg.cond(orc.second_moment(X, damp)):.1e})")
+    assert e <= 2e-3
