@@ -70,6 +70,7 @@ struct Plan {
   std::vector<size_t> off_p;         // their P buffers (float32, rows x cols)
   std::vector<ApplyTask> apply;
   size_t off_pdev = 0, off_apply = 0;
+  int apply_bf16 = 0;                // apply tasks of bf16-gradient tensors, first in `apply`
   std::vector<Group> groups;  // by NS precision (bf16 first) and lane
   std::vector<int> adam_tensors;     // kind-ADAMW tensors, in tensor order
   std::vector<AdamTask> adam_tasks;
@@ -258,16 +259,22 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
     sp.dp = int(round_up(sp.d, kPrecondPad));
     plan.slots.push_back(sp);
   }
+  // apply tiles: those of bf16-gradient tensors first, then float32 ones
+  // (each dtype has its own kernel, with the LDS its planes need)
+  std::vector<ApplyTask> apply_f32;
   for (int32_t i = 0; i < n; ++i) {
     if (ts[i].precond < 0) continue;
     const int pi = int(plan.prec_tensors.size());
     plan.prec_tensors.push_back(i);
     const SlotPlan& sp = plan.slots[ts[i].precond];
     const int trs = int((ts[i].rows + 63) / 64), tcs = int((sp.d + 63) / 64);
+    std::vector<ApplyTask>& dst = ts[i].dtype == MUON_F32 ? apply_f32 : plan.apply;
     for (int blk = 0; blk < sp.nblocks; ++blk)
       for (int r = 0; r < trs; ++r)
-        for (int c = 0; c < tcs; ++c) plan.apply.push_back({pi, r, c, blk});
+        for (int c = 0; c < tcs; ++c) dst.push_back({pi, r, c, blk});
   }
+  plan.apply_bf16 = int(plan.apply.size());
+  plan.apply.insert(plan.apply.end(), apply_f32.begin(), apply_f32.end());
   // AdamW tensors: rows of `len` elements in chunks of kAdamChunk; a fully
   // contiguous tensor is one row of rows*cols elements
   for (int32_t i = 0; i < n; ++i) {
@@ -402,7 +409,7 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
     sp.off_s = off; off = align_up(off + blk * sizeof(float));
     sp.off_l = off; off = align_up(off + blk * sizeof(double));
     sp.off_li = off; off = align_up(off + blk * sizeof(double));
-    sp.off_sinv = off; off = align_up(off + blk * sizeof(float));
+    sp.off_sinv = off; off = align_up(off + blk * kSinvPlanes * sizeof(uint16_t));
     sp.off_acc = off; off = align_up(off + blk * sizeof(float));
     sp.off_cnt = off; off = align_up(off + size_t(sp.nblocks) * sizeof(double));
   }
@@ -492,7 +499,7 @@ std::vector<uint8_t> build_meta(const Plan& plan, const muon_tensor_t* ts, uint8
     pd.vec_grad = reinterpret_cast<uintptr_t>(t.grad) % 16 == 0 && (t.ld_grad * es) % 16 == 0 && sp.d % 8 == 0;
     pd.p = reinterpret_cast<float*>(ws + plan.off_p[pi]);
     pd.ld_p = t.cols;
-    pd.sinv = reinterpret_cast<const float*>(ws + sp.off_sinv);
+    pd.sinv = reinterpret_cast<const uint16_t*>(ws + sp.off_sinv);
     pd.rows = int(t.rows);
     pd.d = int(sp.d);
     pd.dp = sp.dp;
@@ -561,7 +568,7 @@ muon_status_t enqueue_step(muon_handle_t h, float lr, hipStream_t s, std::vector
   if (!plan.apply.empty()) {
     hipError_t e = launch_precond_apply(reinterpret_cast<const PrecondDev*>(h->ws + plan.off_pdev),
                                         reinterpret_cast<const ApplyTask*>(h->ws + plan.off_apply),
-                                        int(plan.apply.size()), s);
+                                        plan.apply_bf16, int(plan.apply.size()) - plan.apply_bf16, s);
     if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("precond apply launch: ") + hipGetErrorString(e));
   }
   // Lanes: the groups of lane l > 0 run on the handle's stream l, and the
@@ -808,7 +815,7 @@ muon_status_t muon_init(muon_handle_t* out, const muon_tensor_t* tensors, int32_
   hipError_t e = hipMemsetAsync(h->ws, 0, h->plan.total, s);
   if (e == hipSuccess) e = hipMemcpyAsync(h->ws, h->meta.data(), h->meta.size(), hipMemcpyHostToDevice, s);
   for (const SlotPlan& sp : h->plan.slots)   // S^-1 = I until the slot's first refresh
-    if (e == hipSuccess) e = launch_identity(reinterpret_cast<float*>(h->ws + sp.off_sinv), sp.dp, sp.nblocks, s);
+    if (e == hipSuccess) e = launch_identity(reinterpret_cast<uint16_t*>(h->ws + sp.off_sinv), sp.dp, sp.nblocks, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);  // the host copy of meta may be reused after init
   if (e != hipSuccess) {
     delete h;
@@ -867,7 +874,7 @@ PrecondBlockDev block_dev(muon_handle_t h, const SlotPlan& sp, int32_t block) {
   b.s = reinterpret_cast<float*>(h->ws + sp.off_s) + bo;
   b.l = reinterpret_cast<double*>(h->ws + sp.off_l) + bo;
   b.li = reinterpret_cast<double*>(h->ws + sp.off_li) + bo;
-  b.sinv = reinterpret_cast<float*>(h->ws + sp.off_sinv) + bo;
+  b.sinv = reinterpret_cast<uint16_t*>(h->ws + sp.off_sinv) + bo * kSinvPlanes;
   b.acc = reinterpret_cast<float*>(h->ws + sp.off_acc) + bo;
   b.cnt = reinterpret_cast<double*>(h->ws + sp.off_cnt) + block;
   b.part = h->plan.off_mpart ? reinterpret_cast<float*>(h->ws + h->plan.off_mpart) : nullptr;

@@ -101,11 +101,16 @@ enum Phase : int32_t { kGram = 0, kSquare = 1, kBX = 2 };
 constexpr int kCholBlock = 64;    // Cholesky / inverse block edge (float64)
 constexpr int kPrecondPad = 128;  // S and S^-1 are padded to multiples of this
 
+// S^-1 is stored as three bf16 planes per block, h + m + l = the float32
+// value exactly (h = bf16(x), m = bf16(x - h), l = x - h - m), so the apply
+// reads operands its bf16 matrix cores take as they are.
+constexpr int kSinvPlanes = 3;
+
 // One preconditioned tensor of the apply phase: P = G S^-1 (block-wise).
 struct PrecondDev {
   const void* grad; int64_t ld_grad; int32_t grad_f32; int32_t vec_grad;
   float* p;         int64_t ld_p;     // P, float32, rows x (d * nblocks)
-  const float* sinv;                  // nblocks inverses of the slot, dp x dp each
+  const uint16_t* sinv;               // nblocks inverses of the slot, kSinvPlanes bf16 dp x dp planes each
   int32_t rows, d, dp, nblocks;
 };
 struct ApplyTask { int32_t tensor, tr, tc, blk; };   // 64x64 tile (tr, tc) of block blk
@@ -115,7 +120,7 @@ struct PrecondBlockDev {
   float* s;        // S, float32, dp x dp
   double* l;       // Cholesky factor, float64
   double* li;      // its inverse, float64
-  float* sinv;     // S^-1, float32
+  uint16_t* sinv;  // S^-1, kSinvPlanes bf16 planes
   float* acc;      // running sum of X^T X over micro-batches, float32, dp x dp
   double* cnt;     // its running sample count
   float* part;     // scratch shared by every block of every slot: the split partial sums of
@@ -181,8 +186,9 @@ hipError_t launch_precond_accumulate(const PrecondBlockDev& b, const void* acts,
                                      bool acts_f32, float beta, hipStream_t s);
 hipError_t launch_precond_refresh_accumulated(const PrecondBlockDev& b, float damping, bool reset, uint32_t* flags,
                                               hipStream_t s);
-hipError_t launch_precond_apply(const PrecondDev* pds, const ApplyTask* tasks, int n_tasks, hipStream_t s);
-hipError_t launch_identity(float* sinv, int dp, int nblocks, hipStream_t s);
+// tasks: n_bf16 tiles of bf16-gradient tensors, then n_f32 of float32 ones
+hipError_t launch_precond_apply(const PrecondDev* pds, const ApplyTask* tasks, int n_bf16, int n_f32, hipStream_t s);
+hipError_t launch_identity(uint16_t* sinv, int dp, int nblocks, hipStream_t s);
 hipError_t launch_adam_tick(AdamState* st, float beta1, float beta2, hipStream_t s);
 hipError_t launch_adam_set(AdamState* st, uint32_t t, hipStream_t s);
 hipError_t launch_adamw(const AdamDev* tensors, const AdamTask* tasks, int n_tasks, const AdamParams& p,

@@ -14,7 +14,8 @@
 //                      float64 (64 x 64 blocks), with L^-1 formed alongside
 //                      by blocked forward substitution of L X = I
 //   sinv_store         S^-1 = L^-T L^-1 (summed in float64 during the
-//                      factorisation), stored as float32
+//                      factorisation), rounded to float32 and stored as three
+//                      exact bf16 planes
 //   apply_kernel       P = G S^-1 (block-wise for block-diagonal S), a float32
 //                      product formed from exact bf16 planes on bf16 MFMA,
 //                      read by the momentum phase in place of G.
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void to_f64_kernel(const float* __restric
 // jb of X is final after trsm_kernel of step jb, so the same launch also
 // adds its term of S^-1 = L^-T L^-1 = sum_jb X[jb]^T X[jb] to the float64
 // sum Z (upper blocks); a last launch adds the final row's term and
-// sinv_store_kernel writes S^-1 in float32.  The inverse and the product
+// sinv_store_kernel writes S^-1 (float32 values as bf16 planes).  The inverse and the product
 // add blocks to launches the factorisation makes anyway.
 
 // Diagonal block jb: factor in place and store D^-1 as X[jb][jb].
@@ -557,14 +558,27 @@ __global__ __launch_bounds__(kThreads) void syrk_update_kernel(double* __restric
     for (int q = 0; q < 4; ++q) out[(i0 + r) * static_cast<size_t>(dp) + j0 + q] -= c[r][q];
 }
 
-// S^-1 (float32) from the float64 sum Z, which holds the upper blocks
-// (ib <= jb); a lower block is the transpose of its mirror, staged through
-// LDS so that reads and writes are both along rows.  One block per 64 x 64
-// block of S^-1, 16 rows per pass.
-__global__ __launch_bounds__(kThreads) void sinv_store_kernel(const double* __restrict__ sacc, float* __restrict__ Sinv,
-                                                              int dp) {
+// S^-1 from the float64 sum Z, which holds the upper blocks (ib <= jb); a
+// lower block is the transpose of its mirror, staged through LDS so that
+// reads and writes are both along rows.  Each value is rounded to float32
+// and stored as its three bf16 planes.  One block per 64 x 64 block of S^-1,
+// 16 rows per pass.
+__device__ __forceinline__ void store_planes(uint16_t* sinv, size_t plane, size_t idx, double z) {
+  const float x = static_cast<float>(z);
+  const uint16_t h = f32_to_bf16(x);
+  const float r = x - bf16_to_f32(h);               // exact
+  const uint16_t m = f32_to_bf16(r);
+  const uint16_t l = f32_to_bf16(r - bf16_to_f32(m));   // exact: at most 8 significant bits
+  sinv[idx] = h;
+  sinv[plane + idx] = m;
+  sinv[2 * plane + idx] = l;
+}
+
+__global__ __launch_bounds__(kThreads) void sinv_store_kernel(const double* __restrict__ sacc,
+                                                              uint16_t* __restrict__ Sinv, int dp) {
   __shared__ double T[16][kCb + 1];
   const int nb = dp / kCb;
+  const size_t plane = static_cast<size_t>(dp) * dp;
   const int ib = blockIdx.x / nb, jb = blockIdx.x % nb;
   const int c = threadIdx.x & 63, r = threadIdx.x >> 6;
   for (int p = 0; p < kCb; p += 16) {
@@ -572,8 +586,8 @@ __global__ __launch_bounds__(kThreads) void sinv_store_kernel(const double* __re
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int row = p + r + 4 * q;
-        Sinv[static_cast<size_t>(ib * kCb + row) * dp + jb * kCb + c] =
-            static_cast<float>(sacc[static_cast<size_t>(ib * kCb + row) * dp + jb * kCb + c]);
+        const size_t idx = static_cast<size_t>(ib * kCb + row) * dp + jb * kCb + c;
+        store_planes(Sinv, plane, idx, sacc[idx]);
       }
       continue;
     }
@@ -587,7 +601,7 @@ __global__ __launch_bounds__(kThreads) void sinv_store_kernel(const double* __re
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int row = r + 4 * q;
-      Sinv[static_cast<size_t>(ib * kCb + p + row) * dp + jb * kCb + c] = static_cast<float>(T[row][c]);
+      store_planes(Sinv, plane, static_cast<size_t>(ib * kCb + p + row) * dp + jb * kCb + c, T[row][c]);
     }
   }
 }
@@ -599,15 +613,19 @@ __global__ __launch_bounds__(kThreads) void sinv_store_kernel(const double* __re
 // split into three bf16 planes, x = h + m + l exactly (h = bf16(x),
 // m = bf16(x - h), l = x - h - m, which has at most 8 significant bits), and
 // the tile product sums the plane products i + j <= 2 with float32
-// accumulation (bf16 products are exact in float32).  A bf16 gradient is its
-// own single plane, so P = G (h + m + l) is the float32 GEMM up to the order
+// accumulation (bf16 products are exact in float32).  S^-1 arrives as its
+// planes (the refresh stores them), so its tiles are staged as raw bits; a
+// float32 gradient is split while staged.  A bf16 gradient is its own single
+// plane, so P = G (h + m + l) is the float32 GEMM up to the order
 // of the additions; a float32 gradient drops only the products of two small
 // planes (each below 2^-16 of the leading one).  64x64 output tiles, 4 waves
 // of 32x32 (v_mfma_f32_32x32x16_bf16), 32-deep K stages double-buffered in
 // LDS with a padded row pitch (conflict-free 16-byte fragment reads).
 constexpr int kApBT = 64, kApBK = 32, kApLDK = kApBK + 8;
 constexpr int kApPlane = kApBT * kApLDK;             // bf16 elements per plane
-constexpr int kApSmem = 2 * 6 * kApPlane;             // two stages of up to 3 + 3 planes
+// two stages of the gradient's planes (1 for bf16, 3 for float32) and S^-1's 3
+template <bool GF32>
+constexpr int ap_smem() { return 2 * ((GF32 ? 3 : 1) + kSinvPlanes) * kApPlane; }
 
 template <bool GF32, bool VEC>
 __device__ __forceinline__ void apply_tile(const PrecondDev& pd, const ApplyTask& t, uint16_t* smem) {
@@ -615,12 +633,13 @@ __device__ __forceinline__ void apply_tile(const PrecondDev& pd, const ApplyTask
   constexpr int NG = GF32 ? 3 : 1;                 // planes of the gradient tile
   constexpr int PLANE = kApPlane;
   constexpr int STAGE = (NG + 3) * PLANE;
-  static_assert(2 * STAGE <= kApSmem, "stages fit");
+  static_assert(2 * STAGE <= ap_smem<GF32>(), "stages fit");
   static_assert(4 * 32 * EPP * 4 <= 2 * STAGE * 2, "epilogue staging");
   const int d = pd.d, dp = pd.dp;
   const int r0 = t.tr * BT, c0 = t.tc * BT;            // rows of G, columns within block t.blk
   const int gcol0 = t.blk * d;                          // first column of the block in G and P
-  const float* sinv = pd.sinv + static_cast<size_t>(t.blk) * dp * dp;
+  const size_t splane = static_cast<size_t>(dp) * dp;
+  const uint16_t* sinv = pd.sinv + static_cast<size_t>(t.blk) * kSinvPlanes * splane;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int lrow = tid >> 2, lk = (tid & 3) * 8;        // 64 rows x 4 chunks of 8 per stage
@@ -640,8 +659,8 @@ __device__ __forceinline__ void apply_tile(const PrecondDev& pd, const ApplyTask
   constexpr int NR = 4;
   u32x4_t gr[NR][GW];
   bool gok[NR];
-  float sb[NR][8];
-  auto gload = [&](int k0, u32x4_t (&g)[GW], bool& ok, float (&sv)[8]) {
+  u32x4_t sb[NR][kSinvPlanes];
+  auto gload = [&](int k0, u32x4_t (&g)[GW], bool& ok, u32x4_t (&sv)[kSinvPlanes]) {
     const int gi = r0 + lrow, kc = k0 + lk;
     ok = gi < pd.rows && kc < d;
     if constexpr (VEC) {
@@ -676,11 +695,10 @@ __device__ __forceinline__ void apply_tile(const PrecondDev& pd, const ApplyTask
       }
       ok = true;
     }
-    // operand B: row c0+lrow of S^-1 (padded to dp, always in bounds)
-    const float* sp = sinv + static_cast<size_t>(c0 + lrow) * dp + k0 + lk;
-    const f32x4_t s0 = gld<f32x4_t>(sp), s1 = gld<f32x4_t>(sp + 4);
+    // operand B: row c0+lrow of the S^-1 planes (padded to dp, always in bounds)
+    const uint16_t* sp = sinv + static_cast<size_t>(c0 + lrow) * dp + k0 + lk;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { sv[e] = s0[e]; sv[4 + e] = s1[e]; }
+    for (int pl = 0; pl < kSinvPlanes; ++pl) sv[pl] = gld<u32x4_t>(sp + pl * splane);
   };
   // split 8 floats into bf16 planes h, m, l and store them (16 bytes each)
   auto split_store = [&](const float* x, int nplanes, uint16_t* dst) {
@@ -702,22 +720,22 @@ __device__ __forceinline__ void apply_tile(const PrecondDev& pd, const ApplyTask
       }
     }
   };
-  auto sstore = [&](int buf, const u32x4_t (&g)[GW], bool ok, const float (&sv)[8]) {
+  auto sstore = [&](int buf, const u32x4_t (&g)[GW], bool ok, const u32x4_t (&sv)[kSinvPlanes]) {
     uint16_t* st = smem + buf * STAGE + lrow * LDK + lk;
-    float gv[8];
     if constexpr (GF32) {
+      float gv[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        gv[e] = __uint_as_float(g[0][e]);
-        gv[4 + e] = __uint_as_float(g[1][e]);
+        gv[e] = ok ? __uint_as_float(g[0][e]) : 0.f;
+        gv[4 + e] = ok ? __uint_as_float(g[1][e]) : 0.f;
       }
+      split_store(gv, NG, st);
     } else {
-      unpack8_bf16(g[0], gv);
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4_t*>(st) = ok ? g[0] : z;   // bf16: its own plane
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) gv[e] = ok ? gv[e] : 0.f;
-    split_store(gv, NG, st);
-    split_store(sv, 3, st + NG * PLANE);
+    for (int pl = 0; pl < kSinvPlanes; ++pl) *reinterpret_cast<u32x4_t*>(st + (NG + pl) * PLANE) = sv[pl];
   };
   // K pipeline: LDS buffer kt&1 holds stage kt; iteration kt requests
   // stage kt+3 (into the set stage kt-1 left, stored two iterations ago),
@@ -774,19 +792,16 @@ __device__ __forceinline__ void apply_tile(const PrecondDev& pd, const ApplyTask
   }
 }
 
+// One launch per gradient dtype, with the LDS its planes need (bf16: 40 KB,
+// four blocks per CU; float32: 60 KB, two).
+template <bool GF32>
 __global__ __launch_bounds__(kThreads)
 void apply_kernel(const PrecondDev* __restrict__ pds, const ApplyTask* __restrict__ tasks) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[kApSmem];   // [buf][G planes, S planes][BT][LDK]
+  __shared__ __attribute__((aligned(16))) uint16_t smem[ap_smem<GF32>()];   // [buf][G planes, S planes][BT][LDK]
   const ApplyTask t = tasks[blockIdx.x];
   const PrecondDev& pd = pds[t.tensor];
-  // both flags are uniform over the block
-  if (pd.grad_f32) {
-    if (pd.vec_grad) apply_tile<true, true>(pd, t, smem);
-    else apply_tile<true, false>(pd, t, smem);
-  } else {
-    if (pd.vec_grad) apply_tile<false, true>(pd, t, smem);
-    else apply_tile<false, false>(pd, t, smem);
-  }
+  if (pd.vec_grad) apply_tile<GF32, true>(pd, t, smem);   // uniform over the block
+  else apply_tile<GF32, false>(pd, t, smem);
 }
 
 // S^-1 = I for every block (the state of a slot before its first refresh).
@@ -820,18 +835,20 @@ __global__ __launch_bounds__(kThreads) void clear_acc_kernel(float* __restrict__
   if (blockIdx.x == 0 && threadIdx.x == 0) *cnt = 0.0;
 }
 
-__global__ __launch_bounds__(kThreads) void identity_kernel(float* __restrict__ sinv, int dp, int nblocks) {
-  const size_t n = static_cast<size_t>(nblocks) * dp * dp;
+__global__ __launch_bounds__(kThreads) void identity_kernel(uint16_t* __restrict__ sinv, int dp, int nblocks) {
+  const size_t plane = static_cast<size_t>(dp) * dp;
+  const size_t n = static_cast<size_t>(nblocks) * kSinvPlanes * plane;
   for (size_t k = blockIdx.x * static_cast<size_t>(kThreads) + threadIdx.x; k < n;
        k += static_cast<size_t>(gridDim.x) * kThreads) {
-    const size_t e = k % (static_cast<size_t>(dp) * dp);
-    sinv[k] = (e / dp == e % dp) ? 1.0f : 0.0f;
+    const size_t e = k % plane;
+    const bool lead = (k / plane) % kSinvPlanes == 0;   // h plane: 1 on the diagonal; m, l: 0
+    sinv[k] = lead && e / dp == e % dp ? static_cast<uint16_t>(0x3F80u) : static_cast<uint16_t>(0u);
   }
 }
 
 }  // namespace
 
-hipError_t launch_identity(float* sinv, int dp, int nblocks, hipStream_t s) {
+hipError_t launch_identity(uint16_t* sinv, int dp, int nblocks, hipStream_t s) {
   identity_kernel<<<256, kThreads, 0, s>>>(sinv, dp, nblocks);
   return hipGetLastError();
 }
@@ -914,9 +931,9 @@ hipError_t launch_precond_refresh_accumulated(const PrecondBlockDev& b, float da
   return hipGetLastError();
 }
 
-hipError_t launch_precond_apply(const PrecondDev* pds, const ApplyTask* tasks, int n_tasks, hipStream_t s) {
-  if (n_tasks <= 0) return hipSuccess;
-  apply_kernel<<<n_tasks, kThreads, 0, s>>>(pds, tasks);
+hipError_t launch_precond_apply(const PrecondDev* pds, const ApplyTask* tasks, int n_bf16, int n_f32, hipStream_t s) {
+  if (n_bf16 > 0) apply_kernel<false><<<n_bf16, kThreads, 0, s>>>(pds, tasks);
+  if (n_f32 > 0) apply_kernel<true><<<n_f32, kThreads, 0, s>>>(pds, tasks + n_bf16);
   return hipGetLastError();
 }
 
