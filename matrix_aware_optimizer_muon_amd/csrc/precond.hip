@@ -360,93 +360,114 @@ __global__ __launch_bounds__(kThreads) void to_f64_kernel(const float* __restric
 // add blocks to launches the factorisation makes anyway.
 
 // Diagonal block jb: factor in place and store D^-1 as X[jb][jb].
-// Right-looking, with the block in registers: thread t holds the T x T
-// entries at rows T(t/(64/T)).., columns T(t%(64/T)).. of the trailing
-// matrix (a) and of the running right-hand side of D X = I (x).  Step k: the
-// owners of column k publish it and the owners of row k of x publish that
-// row (double-buffered in LDS, so one barrier per step); then every thread
-// forms l_i = A[i][k] / sqrt(A[k][k]) for its rows and columns (zero for
-// i <= k, so the update leaves finished rows and columns alone), updates
-// A[i][j] -= l_i l_j and x[i][:] -= l_i X[k][:], with X[k][:] =
-// x[k][:] / L[k][k] the finished row k of D^-1.  The step loop is unrolled
-// by T so that the register column of step k is static.  T = 4 (256
-// threads) measured 6 % faster over a whole refresh than T = 2 (1024
-// threads): the step is a chain of latencies (LDS, barrier, rsqrt), and more
-// waves only repeat its fixed work.
-#ifndef MUON_POTRF_TILE
-#define MUON_POTRF_TILE 4
-#endif
-constexpr int kPotrfTile = MUON_POTRF_TILE;
-constexpr int kPotrfThreads = (kCb / kPotrfTile) * (kCb / kPotrfTile);
+// Right-looking, with the block in registers: thread t holds the 4 x 4
+// entries at rows 4(t/16).., columns 4(t%16).. of the trailing matrix (a)
+// and of the running right-hand side of D X = I (x).  Two columns per
+// barrier: the owners of columns k and k+1 publish them as they stand (k+1
+// not yet reduced by k), and the owners of rows k and k+1 of x publish
+// those rows (double-buffered in LDS).  Every thread then forms
+//   l0_i = A[i][k] / sqrt(A[k][k]),
+//   u_i  = A[i][k+1] - l0_i l0_{k+1}        (column k+1 reduced by column k),
+//   l1_i = u_i / sqrt(u_{k+1}),
+// (l0 zero for i <= k, l1 zero for i <= k+1, so the update leaves finished
+// rows and columns alone), applies A[i][j] -= l0_i l0_j + l1_i l1_j and
+// x[i][:] -= l0_i X[k][:] + l1_i X[k+1][:], with X[k][:] = x[k][:] / L[k][k]
+// and X[k+1][:] = (x[k+1][:] - l0_{k+1} X[k][:]) / L[k+1][k+1] the finished
+// rows of D^-1.  The step is a chain of latencies (LDS, barrier, rsqrt), so
+// halving the barriers shortens the factor; the column loop is unrolled so
+// register columns are static.  (One column per barrier with 4 x 4 tiles
+// measured 29 us per block; with 2 x 2 tiles and 1024 threads, slower.)
+constexpr int kPotrfThreads = 256;
 __global__ __launch_bounds__(kPotrfThreads) void potrf_kernel(double* __restrict__ L, double* __restrict__ Li, int dp,
                                                               int jb, uint32_t* __restrict__ flags) {
-  constexpr int T = kPotrfTile, TPR = kCb / T;
-  __shared__ double colk[2][kCb];
-  __shared__ double rowk[2][kCb];
+  static_assert(kPotrfThreads * 16 == kCb * kCb, "4 x 4 entries per thread cover the block");
+  __shared__ double col0[2][kCb], col1[2][kCb];
+  __shared__ double row0[2][kCb], row1[2][kCb];
   double* base = L + static_cast<size_t>(jb) * kCb * dp + jb * kCb;
-  const int i0 = (threadIdx.x / TPR) * T, j0 = (threadIdx.x % TPR) * T;
-  double a[T][T], x[T][T];
+  const int i0 = (threadIdx.x >> 4) * 4, j0 = (threadIdx.x & 15) * 4;
+  double a[4][4], x[4][4];
 #pragma unroll
-  for (int r = 0; r < T; ++r)
+  for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int q = 0; q < T; ++q) {
+    for (int q = 0; q < 4; ++q) {
       a[r][q] = base[(i0 + r) * static_cast<size_t>(dp) + j0 + q];
       x[r][q] = i0 + r == j0 + q ? 1.0 : 0.0;
     }
-  for (int k0 = 0; k0 < kCb; k0 += T)
+  for (int k0 = 0; k0 < kCb; k0 += 4)
 #pragma unroll
-  for (int kq = 0; kq < T; ++kq) {
-    const int k = k0 + kq, buf = k & 1;
+  for (int kq = 0; kq < 4; kq += 2) {
+    const int k = k0 + kq, buf = (kq >> 1) & 1;
     if (j0 == k0) {
 #pragma unroll
-      for (int r = 0; r < T; ++r) colk[buf][i0 + r] = a[r][kq];
+      for (int r = 0; r < 4; ++r) {
+        col0[buf][i0 + r] = a[r][kq];
+        col1[buf][i0 + r] = a[r][kq + 1];
+      }
     }
     if (i0 == k0) {
 #pragma unroll
-      for (int q = 0; q < T; ++q) rowk[buf][j0 + q] = x[kq][q];
+      for (int q = 0; q < 4; ++q) {
+        row0[buf][j0 + q] = x[kq][q];
+        row1[buf][j0 + q] = x[kq + 1][q];
+      }
     }
     __syncthreads();
     // a non-positive pivot gives NaN or inf, which propagates into S^-1,
     // and sets the flag
-    const double piv = colk[buf][k];
-    const double rdk = rsqrt(piv);
-    if (threadIdx.x == 0 && !(piv > 0.0)) atomicOr(flags, 2u);
-    double ci[T], cj[T], xk[T];
+    const double p0 = col0[buf][k];
+    const double rd0 = rsqrt(p0);
+    const double l0k1 = col0[buf][k + 1] * rd0;          // L[k+1][k]
+    const double p1 = col1[buf][k + 1] - l0k1 * l0k1;
+    const double rd1 = rsqrt(p1);
+    if (threadIdx.x == 0 && !(p0 > 0.0 && p1 > 0.0)) atomicOr(flags, 2u);
+    double c0i[4], c0j[4], u_i[4], u_j[4], xk0[4], xk1[4];
 #pragma unroll
-    for (int r = 0; r < T; ++r) {
-      ci[r] = colk[buf][i0 + r] * rdk;
-      cj[r] = colk[buf][j0 + r] * rdk;
-      xk[r] = rowk[buf][j0 + r] * rdk;
+    for (int r = 0; r < 4; ++r) {
+      c0i[r] = col0[buf][i0 + r] * rd0;
+      c0j[r] = col0[buf][j0 + r] * rd0;
+      u_i[r] = fma(-c0i[r], l0k1, col1[buf][i0 + r]);
+      u_j[r] = fma(-c0j[r], l0k1, col1[buf][j0 + r]);
+      xk0[r] = row0[buf][j0 + r] * rd0;
     }
-    if (i0 + T - 1 > k) {
-      double li[T], lj[T];
 #pragma unroll
-      for (int r = 0; r < T; ++r) {
-        li[r] = i0 + r > k ? ci[r] : 0.0;
-        lj[r] = j0 + r > k ? cj[r] : 0.0;
+    for (int r = 0; r < 4; ++r) xk1[r] = fma(-l0k1, xk0[r], row1[buf][j0 + r]) * rd1;
+    if (i0 + 3 > k) {
+      double li0[4], lj0[4], li1[4], lj1[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        li0[r] = i0 + r > k ? c0i[r] : 0.0;
+        lj0[r] = j0 + r > k ? c0j[r] : 0.0;
+        li1[r] = i0 + r > k + 1 ? u_i[r] * rd1 : 0.0;
+        lj1[r] = j0 + r > k + 1 ? u_j[r] * rd1 : 0.0;
       }
 #pragma unroll
-      for (int r = 0; r < T; ++r)
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int q = 0; q < T; ++q) {
-          a[r][q] = fma(-li[r], lj[q], a[r][q]);
-          x[r][q] = fma(-li[r], xk[q], x[r][q]);
+        for (int q = 0; q < 4; ++q) {
+          a[r][q] = fma(-li1[r], lj1[q], fma(-li0[r], lj0[q], a[r][q]));
+          x[r][q] = fma(-li1[r], xk1[q], fma(-li0[r], xk0[q], x[r][q]));
         }
     }
-    if (j0 == k0) {   // column k of L (L[k][k] = piv / sqrt(piv))
+    if (j0 == k0) {   // columns k and k+1 of L (L[k][k] = p0 rd0, L[k+1][k+1] = p1 rd1)
 #pragma unroll
-      for (int r = 0; r < T; ++r) a[r][kq] = ci[r];
+      for (int r = 0; r < 4; ++r) {
+        a[r][kq] = c0i[r];
+        a[r][kq + 1] = u_i[r] * rd1;
+      }
     }
-    if (i0 == k0) {   // row k of D^-1
+    if (i0 == k0) {   // rows k and k+1 of D^-1
 #pragma unroll
-      for (int q = 0; q < T; ++q) x[kq][q] = xk[q];
+      for (int q = 0; q < 4; ++q) {
+        x[kq][q] = xk0[q];
+        x[kq + 1][q] = xk1[q];
+      }
     }
   }
   double* di = Li + static_cast<size_t>(jb) * kCb * dp + jb * kCb;
 #pragma unroll
-  for (int r = 0; r < T; ++r)
+  for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int q = 0; q < T; ++q) {
+    for (int q = 0; q < 4; ++q) {
       base[(i0 + r) * static_cast<size_t>(dp) + j0 + q] = j0 + q <= i0 + r ? a[r][q] : 0.0;
       di[(i0 + r) * static_cast<size_t>(dp) + j0 + q] = x[r][q];
     }
