@@ -324,6 +324,48 @@ __device__ __forceinline__ void zero44(double (&c)[4][4]) {
     for (int q = 0; q < 4; ++q) c[r][q] = 0.0;
 }
 
+// Load two 64 x 64 float64 blocks (leading dimension dp) into LDS tiles:
+// all sixteen 16-byte loads of a thread are issued before the first LDS
+// store, so the two blocks cost one memory latency, not sixteen.
+typedef double f64x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void load_blocks(double (*P)[kCb + 1], const double* __restrict__ sp,
+                                            double (*Q)[kCb + 1], const double* __restrict__ sq, int dp) {
+  constexpr int kPer = kCb * kCb / 2 / kThreads;   // 16-byte pieces per thread and block
+  f64x2_t vp[kPer], vq[kPer];
+#pragma unroll
+  for (int p = 0; p < kPer; ++p) {
+    const int e = threadIdx.x + p * kThreads, row = e / (kCb / 2), col = (e % (kCb / 2)) * 2;
+    vp[p] = gld<f64x2_t>(sp + row * static_cast<size_t>(dp) + col);
+    vq[p] = gld<f64x2_t>(sq + row * static_cast<size_t>(dp) + col);
+  }
+#pragma unroll
+  for (int p = 0; p < kPer; ++p) {
+    const int e = threadIdx.x + p * kThreads, row = e / (kCb / 2), col = (e % (kCb / 2)) * 2;
+    P[row][col] = vp[p][0];
+    P[row][col + 1] = vp[p][1];
+    Q[row][col] = vq[p][0];
+    Q[row][col + 1] = vq[p][1];
+  }
+}
+
+// Load one 64 x 64 float64 block (leading dimension dp) into an LDS tile,
+// all of a thread's 16-byte loads issued before its first LDS store.
+__device__ __forceinline__ void load_block(double (*P)[kCb + 1], const double* __restrict__ sp, int dp) {
+  constexpr int kPer = kCb * kCb / 2 / kThreads;
+  f64x2_t vp[kPer];
+#pragma unroll
+  for (int p = 0; p < kPer; ++p) {
+    const int e = threadIdx.x + p * kThreads, row = e / (kCb / 2), col = (e % (kCb / 2)) * 2;
+    vp[p] = gld<f64x2_t>(sp + row * static_cast<size_t>(dp) + col);
+  }
+#pragma unroll
+  for (int p = 0; p < kPer; ++p) {
+    const int e = threadIdx.x + p * kThreads, row = e / (kCb / 2), col = (e % (kCb / 2)) * 2;
+    P[row][col] = vp[p][0];
+    P[row][col + 1] = vp[p][1];
+  }
+}
+
 // S (float32, dp x dp) -> L (float64, lower triangle; upper set to zero);
 // L^-1's storage cleared (the right-hand side B of L X = I starts at zero off
 // the diagonal blocks, which potrf_kernel writes) and so is the float64 sum
@@ -377,10 +419,13 @@ __global__ __launch_bounds__(kThreads) void to_f64_kernel(const float* __restric
 // halving the barriers shortens the factor; the column loop is unrolled so
 // register columns are static.  (One column per barrier with 4 x 4 tiles
 // measured 29 us per block; with 2 x 2 tiles and 1024 threads, slower.)
+// With P (an LDS tile) the block first applies the previous step's update
+// to itself, A[jb][jb] -= L[jb][jb-1] L[jb][jb-1]^T (see step_kernel).
 constexpr int kPotrfThreads = 256;
-__global__ __launch_bounds__(kPotrfThreads) void potrf_kernel(double* __restrict__ L, double* __restrict__ Li, int dp,
-                                                              int jb, uint32_t* __restrict__ flags) {
-  static_assert(kPotrfThreads * 16 == kCb * kCb, "4 x 4 entries per thread cover the block");
+__device__ __forceinline__ void potrf_block(double* __restrict__ L, double* __restrict__ Li, int dp, int jb,
+                                            uint32_t* __restrict__ flags, double (*P)[kCb + 1]) {
+  static_assert(kPotrfThreads == kThreads && kPotrfThreads * 16 == kCb * kCb,
+                "4 x 4 entries per thread cover the block");
   __shared__ double col0[2][kCb], col1[2][kCb];
   __shared__ double row0[2][kCb], row1[2][kCb];
   double* base = L + static_cast<size_t>(jb) * kCb * dp + jb * kCb;
@@ -393,6 +438,17 @@ __global__ __launch_bounds__(kPotrfThreads) void potrf_kernel(double* __restrict
       a[r][q] = base[(i0 + r) * static_cast<size_t>(dp) + j0 + q];
       x[r][q] = i0 + r == j0 + q ? 1.0 : 0.0;
     }
+  if (P) {
+    load_block(P, L + static_cast<size_t>(jb) * kCb * dp + (jb - 1) * kCb, dp);
+    __syncthreads();
+    double c[4][4];
+    zero44(c);
+    mm64_acc<false, true>(P, P, c);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a[r][q] -= c[r][q];
+  }
   for (int k0 = 0; k0 < kCb; k0 += 4)
 #pragma unroll
   for (int kq = 0; kq < 4; kq += 2) {
@@ -473,29 +529,12 @@ __global__ __launch_bounds__(kPotrfThreads) void potrf_kernel(double* __restrict
     }
 }
 
-// Load two 64 x 64 float64 blocks (leading dimension dp) into LDS tiles:
-// all sixteen 16-byte loads of a thread are issued before the first LDS
-// store, so the two blocks cost one memory latency, not sixteen.
-typedef double f64x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void load_blocks(double (*P)[kCb + 1], const double* __restrict__ sp,
-                                            double (*Q)[kCb + 1], const double* __restrict__ sq, int dp) {
-  constexpr int kPer = kCb * kCb / 2 / kThreads;   // 16-byte pieces per thread and block
-  f64x2_t vp[kPer], vq[kPer];
-#pragma unroll
-  for (int p = 0; p < kPer; ++p) {
-    const int e = threadIdx.x + p * kThreads, row = e / (kCb / 2), col = (e % (kCb / 2)) * 2;
-    vp[p] = gld<f64x2_t>(sp + row * static_cast<size_t>(dp) + col);
-    vq[p] = gld<f64x2_t>(sq + row * static_cast<size_t>(dp) + col);
-  }
-#pragma unroll
-  for (int p = 0; p < kPer; ++p) {
-    const int e = threadIdx.x + p * kThreads, row = e / (kCb / 2), col = (e % (kCb / 2)) * 2;
-    P[row][col] = vp[p][0];
-    P[row][col + 1] = vp[p][1];
-    Q[row][col] = vq[p][0];
-    Q[row][col + 1] = vq[p][1];
-  }
+// The first diagonal block (no previous step).
+__global__ __launch_bounds__(kPotrfThreads) void potrf_kernel(double* __restrict__ L, double* __restrict__ Li, int dp,
+                                                              uint32_t* __restrict__ flags) {
+  potrf_block(L, Li, dp, 0, flags, nullptr);
 }
+
 
 // Step jb, after potrf_kernel: blocks [0, below) form the panel
 // L[ib][jb] = A[ib][jb] D^-T (ib = jb + 1 + block); blocks [below, below + jb)
@@ -531,17 +570,15 @@ __global__ __launch_bounds__(kThreads) void trsm_kernel(double* __restrict__ L, 
 // the right-hand side of L X = I, B[ib][cb] -= L[ib][jb] X[jb][cb] for
 // ib > jb, cb <= jb; the rest add row jb's term of S^-1,
 // Z[ib][cb] += X[jb][ib]^T X[jb][cb] for ib <= cb <= jb.
-__global__ __launch_bounds__(kThreads) void syrk_update_kernel(double* __restrict__ L, double* __restrict__ Li,
-                                                               double* __restrict__ sacc, int dp, int jb, int npairs,
-                                                               int nrhs) {
-  __shared__ double P[kCb][kCb + 1];
-  __shared__ double Q[kCb][kCb + 1];
+__device__ __forceinline__ void syrk_task(double* __restrict__ L, double* __restrict__ Li, double* __restrict__ sacc,
+                                          int dp, int jb, int npairs, int nrhs, int task, double (*P)[kCb + 1],
+                                          double (*Q)[kCb + 1]) {
   double* out;
   double c[4][4];
   zero44(c);
   const int i0 = (threadIdx.x >> 4) * 4, j0 = (threadIdx.x & 15) * 4;
-  if (static_cast<int>(blockIdx.x) >= npairs + nrhs) {
-    int ib = 0, rem = blockIdx.x - npairs - nrhs;   // upper pair index over 0..jb -> (ib, cb)
+  if (task >= npairs + nrhs) {
+    int ib = 0, rem = task - npairs - nrhs;   // upper pair index over 0..jb -> (ib, cb)
     while (rem >= jb + 1 - ib) { rem -= jb + 1 - ib; ++ib; }
     const int cb = ib + rem;
     load_blocks(P, Li + static_cast<size_t>(jb) * kCb * dp + ib * kCb, Q, Li + static_cast<size_t>(jb) * kCb * dp + cb * kCb,
@@ -555,8 +592,8 @@ __global__ __launch_bounds__(kThreads) void syrk_update_kernel(double* __restric
       for (int q = 0; q < 4; ++q) out[(i0 + r) * static_cast<size_t>(dp) + j0 + q] += c[r][q];
     return;
   }
-  if (static_cast<int>(blockIdx.x) < npairs) {
-    int ib = jb + 1, rem = blockIdx.x;   // lower-triangle pair index -> (ib, kb)
+  if (task < npairs) {
+    int ib = jb + 1, rem = task;   // lower-triangle pair index -> (ib, kb); pair 0 is (jb+1, jb+1)
     while (rem >= ib - jb) { rem -= ib - jb; ++ib; }
     const int kb = jb + 1 + rem;
     load_blocks(P, L + static_cast<size_t>(ib) * kCb * dp + jb * kCb, Q, L + static_cast<size_t>(kb) * kCb * dp + jb * kCb,
@@ -565,7 +602,7 @@ __global__ __launch_bounds__(kThreads) void syrk_update_kernel(double* __restric
     __syncthreads();
     mm64_acc<false, true>(P, Q, c);
   } else {
-    const int idx = blockIdx.x - npairs;
+    const int idx = task - npairs;
     const int ib = jb + 1 + idx / (jb + 1), cb = idx % (jb + 1);
     load_blocks(P, L + static_cast<size_t>(ib) * kCb * dp + jb * kCb, Q, Li + static_cast<size_t>(jb) * kCb * dp + cb * kCb,
                 dp);
@@ -577,6 +614,28 @@ __global__ __launch_bounds__(kThreads) void syrk_update_kernel(double* __restric
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int q = 0; q < 4; ++q) out[(i0 + r) * static_cast<size_t>(dp) + j0 + q] -= c[r][q];
+}
+
+__global__ __launch_bounds__(kThreads) void syrk_update_kernel(double* __restrict__ L, double* __restrict__ Li,
+                                                               double* __restrict__ sacc, int dp, int jb, int npairs,
+                                                               int nrhs) {
+  __shared__ double P[kCb][kCb + 1];
+  __shared__ double Q[kCb][kCb + 1];
+  syrk_task(L, Li, sacc, dp, jb, npairs, nrhs, blockIdx.x, P, Q);
+}
+
+// Step jb's first launch: block 0 factors diagonal block jb after applying
+// the previous step's update to it (pair 0 of that step's updates); blocks
+// 1.. run the previous step's other updates (trailing matrix, right-hand
+// side, S^-1 term), which the factor does not read, beside it.  So the
+// update launch leaves the chain of dependent launches: two per step.
+__global__ __launch_bounds__(kThreads) void step_kernel(double* __restrict__ L, double* __restrict__ Li,
+                                                        double* __restrict__ sacc, int dp, int jb, int npairs,
+                                                        int nrhs, uint32_t* __restrict__ flags) {
+  __shared__ double P[kCb][kCb + 1];
+  __shared__ double Q[kCb][kCb + 1];
+  if (blockIdx.x == 0) potrf_block(L, Li, dp, jb, flags, P);
+  else syrk_task(L, Li, sacc, dp, jb - 1, npairs, nrhs, blockIdx.x, P, Q);
 }
 
 // S^-1 from the float64 sum Z, which holds the upper blocks (ib <= jb); a
@@ -917,12 +976,28 @@ void factor_and_invert(const PrecondBlockDev& b, uint32_t* flags, hipStream_t s)
   const int dp = b.dp, nb = dp / kCb;
   double* sacc = reinterpret_cast<double*>(b.part);   // the scratch holds dp x dp float64
   to_f64_kernel<<<256, kThreads, 0, s>>>(b.s, b.l, b.li, sacc, dp);
+  // update counts of step j: trailing pairs, right-hand-side blocks, S^-1 terms
+  auto counts = [nb](int j, int& npairs, int& nrhs, int& nz) {
+    const int below = nb - j - 1;
+    npairs = below * (below + 1) / 2;
+    nrhs = below * (j + 1);
+    nz = (j + 1) * (j + 2) / 2;
+  };
   for (int jb = 0; jb < nb; ++jb) {
-    potrf_kernel<<<1, kPotrfThreads, 0, s>>>(b.l, b.li, dp, jb, flags);
+    if (jb == 0) {
+      potrf_kernel<<<1, kPotrfThreads, 0, s>>>(b.l, b.li, dp, flags);
+    } else {
+      int npairs, nrhs, nz;
+      counts(jb - 1, npairs, nrhs, nz);   // npairs >= 1: pair 0, block (jb, jb), is the factor's own
+      step_kernel<<<npairs + nrhs + nz, kThreads, 0, s>>>(b.l, b.li, sacc, dp, jb, npairs, nrhs, flags);
+    }
     const int below = nb - jb - 1;
     if (below + jb > 0) trsm_kernel<<<below + jb, kThreads, 0, s>>>(b.l, b.li, dp, jb, below);
-    const int npairs = below * (below + 1) / 2, nrhs = below * (jb + 1), nz = (jb + 1) * (jb + 2) / 2;
-    syrk_update_kernel<<<npairs + nrhs + nz, kThreads, 0, s>>>(b.l, b.li, sacc, dp, jb, npairs, nrhs);
+  }
+  {
+    int npairs, nrhs, nz;
+    counts(nb - 1, npairs, nrhs, nz);     // the last step: its S^-1 term only
+    syrk_update_kernel<<<npairs + nrhs + nz, kThreads, 0, s>>>(b.l, b.li, sacc, dp, nb - 1, npairs, nrhs);
   }
   sinv_store_kernel<<<nb * nb, kThreads, 0, s>>>(sacc, b.sinv, dp);
 }
