@@ -171,7 +171,8 @@ muon_status_t muon_init(muon_handle_t* out, const muon_tensor_t* tensors, int32_
  * layer input: S = X^T X / n_rows + damping * I (float32), then S^-1 by a
  * Cholesky factorisation done in float64 (Newton-Muon README, "What Is
  * Newton-Muon?").  Asynchronous on `stream`.  If S is not numerically
- * positive definite the slot is filled with NaN and flag bit 1 is set. */
+ * positive definite, the non-finite pivot propagates through the factor, so
+ * the block's S^-1 is not finite (NaN), and flag bit 1 is set. */
 muon_status_t muon_precond_refresh(muon_handle_t h, int32_t slot, int32_t block,
                                    const void* acts, int64_t n_rows, int64_t ld,
                                    int32_t dtype, float damping, void* stream);
