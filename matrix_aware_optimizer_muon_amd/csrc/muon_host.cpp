@@ -267,7 +267,7 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
     const int pi = int(plan.prec_tensors.size());
     plan.prec_tensors.push_back(i);
     const SlotPlan& sp = plan.slots[ts[i].precond];
-    const int trs = int((ts[i].rows + 63) / 64), tcs = int((sp.d + 63) / 64);
+    const int trs = int((ts[i].rows + 127) / 128), tcs = int((sp.d + 63) / 64);   // 128 x 64 tiles
     std::vector<ApplyTask>& dst = ts[i].dtype == MUON_F32 ? apply_f32 : plan.apply;
     for (int blk = 0; blk < sp.nblocks; ++blk)
       for (int r = 0; r < trs; ++r)

@@ -113,7 +113,7 @@ struct PrecondDev {
   const uint16_t* sinv;               // nblocks inverses of the slot, kSinvPlanes bf16 dp x dp planes each
   int32_t rows, d, dp, nblocks;
 };
-struct ApplyTask { int32_t tensor, tr, tc, blk; };   // 64x64 tile (tr, tc) of block blk
+struct ApplyTask { int32_t tensor, tr, tc, blk; };   // 128x64 tile (tr, tc) of block blk
 
 // Buffers of one S^-1 block for a refresh.
 struct PrecondBlockDev {

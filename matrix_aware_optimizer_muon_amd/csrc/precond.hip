@@ -698,35 +698,41 @@ __global__ __launch_bounds__(kThreads) void sinv_store_kernel(const double* __re
 // float32 gradient is split while staged.  A bf16 gradient is its own single
 // plane, so P = G (h + m + l) is the float32 GEMM up to the order
 // of the additions; a float32 gradient drops only the products of two small
-// planes (each below 2^-16 of the leading one).  64x64 output tiles, 4 waves
-// of 32x32 (v_mfma_f32_32x32x16_bf16), 32-deep K stages double-buffered in
-// LDS with a padded row pitch (conflict-free 16-byte fragment reads).
-constexpr int kApBT = 64, kApBK = 32, kApLDK = kApBK + 8;
-constexpr int kApPlane = kApBT * kApLDK;             // bf16 elements per plane
+// planes (each below 2^-16 of the leading one).  Output tiles of 128 rows
+// of G by 64 columns (S^-1 rows), 4 waves of 64x32 (two 32x32 blocks of
+// v_mfma_f32_32x32x16_bf16 sharing each S^-1 fragment), 32-deep K stages
+// double-buffered in LDS with a padded row pitch (conflict-free 16-byte
+// fragment reads).
+constexpr int kApRows = 128, kApCols = 64, kApBK = 32, kApLDK = kApBK + 8;
+constexpr int kApGPlane = kApRows * kApLDK;          // bf16 elements per gradient plane
+constexpr int kApSPlane = kApCols * kApLDK;          // ... per S^-1 plane
 // two stages of the gradient's planes (1 for bf16, 3 for float32) and S^-1's 3
 template <bool GF32>
-constexpr int ap_smem() { return 2 * ((GF32 ? 3 : 1) + kSinvPlanes) * kApPlane; }
+constexpr int ap_smem() { return 2 * ((GF32 ? 3 : 1) * kApGPlane + kSinvPlanes * kApSPlane); }
 
 template <bool GF32, bool VEC>
 __device__ __forceinline__ void apply_tile(const PrecondDev& pd, const ApplyTask& t, uint16_t* smem) {
-  constexpr int BT = kApBT, WT = 32, BK = kApBK, LDK = kApLDK, EPP = WT + 8;
+  constexpr int WR = 64, WC = 32, MB = WR / 32, BK = kApBK, LDK = kApLDK, EPP = WC + 8;
   constexpr int NG = GF32 ? 3 : 1;                 // planes of the gradient tile
-  constexpr int PLANE = kApPlane;
-  constexpr int STAGE = (NG + 3) * PLANE;
+  constexpr int GPLANE = kApGPlane, SPLANE = kApSPlane;
+  constexpr int STAGE = NG * GPLANE + kSinvPlanes * SPLANE;
+  constexpr int GQ = kApRows / 64;                 // gradient chunks per thread and stage
   static_assert(2 * STAGE <= ap_smem<GF32>(), "stages fit");
   static_assert(4 * 32 * EPP * 4 <= 2 * STAGE * 2, "epilogue staging");
   const int d = pd.d, dp = pd.dp;
-  const int r0 = t.tr * BT, c0 = t.tc * BT;            // rows of G, columns within block t.blk
+  const int r0 = t.tr * kApRows, c0 = t.tc * kApCols;   // rows of G, columns within block t.blk
   const int gcol0 = t.blk * d;                          // first column of the block in G and P
   const size_t splane = static_cast<size_t>(dp) * dp;
   const uint16_t* sinv = pd.sinv + static_cast<size_t>(t.blk) * kSinvPlanes * splane;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int lrow = tid >> 2, lk = (tid & 3) * 8;        // 64 rows x 4 chunks of 8 per stage
+  const int lrow = tid >> 2, lk = (tid & 3) * 8;        // 64 rows x 4 chunks of 8 per pass
 
-  f32x16_t acc;
+  f32x16_t acc[MB];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  for (int b = 0; b < MB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
 
   // NR register sets of staged operands (stage kt+s in set (kt+s) % NR),
   // used with static indices: the loop is unrolled by NR.
@@ -737,11 +743,12 @@ __device__ __forceinline__ void apply_tile(const PrecondDev& pd, const ApplyTask
   // d, which is a multiple of 8 there) is zeroed at decode time.
   constexpr int GW = GF32 ? 2 : 1;
   constexpr int NR = 4;
-  u32x4_t gr[NR][GW];
-  bool gok[NR];
+  u32x4_t gr[NR][GQ][GW];
+  bool gok[NR][GQ];
   u32x4_t sb[NR][kSinvPlanes];
-  auto gload = [&](int k0, u32x4_t (&g)[GW], bool& ok, u32x4_t (&sv)[kSinvPlanes]) {
-    const int gi = r0 + lrow, kc = k0 + lk;
+  // one chunk of the gradient: row r0+lrow+64q, 8 columns from kc
+  auto gchunk = [&](int q, int kc, u32x4_t (&g)[GW], bool& ok) {
+    const int gi = r0 + lrow + 64 * q;
     ok = gi < pd.rows && kc < d;
     if constexpr (VEC) {
       const int gic = gi < pd.rows ? gi : pd.rows - 1, kcc = kc < d ? kc : 0;
@@ -775,6 +782,10 @@ __device__ __forceinline__ void apply_tile(const PrecondDev& pd, const ApplyTask
       }
       ok = true;
     }
+  };
+  auto gload = [&](int k0, u32x4_t (&g)[GQ][GW], bool (&ok)[GQ], u32x4_t (&sv)[kSinvPlanes]) {
+#pragma unroll
+    for (int q = 0; q < GQ; ++q) gchunk(q, k0 + lk, g[q], ok[q]);
     // operand B: row c0+lrow of the S^-1 planes (padded to dp, always in bounds)
     const uint16_t* sp = sinv + static_cast<size_t>(c0 + lrow) * dp + k0 + lk;
 #pragma unroll
@@ -791,7 +802,7 @@ __device__ __forceinline__ void apply_tile(const PrecondDev& pd, const ApplyTask
       u32x4_t w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = cvt2_bf16(r[2 * e], r[2 * e + 1]);
-      *reinterpret_cast<u32x4_t*>(dst + pl * PLANE) = w;
+      *reinterpret_cast<u32x4_t*>(dst + pl * GPLANE) = w;
       if (pl + 1 < nplanes) {
         float hv[8];
         unpack8_bf16(w, hv);
@@ -800,22 +811,28 @@ __device__ __forceinline__ void apply_tile(const PrecondDev& pd, const ApplyTask
       }
     }
   };
-  auto sstore = [&](int buf, const u32x4_t (&g)[GW], bool ok, const u32x4_t (&sv)[kSinvPlanes]) {
-    uint16_t* st = smem + buf * STAGE + lrow * LDK + lk;
-    if constexpr (GF32) {
-      float gv[8];
+  auto sstore = [&](int buf, const u32x4_t (&g)[GQ][GW], const bool (&ok)[GQ],
+                    const u32x4_t (&sv)[kSinvPlanes]) {
+    uint16_t* st = smem + buf * STAGE;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        gv[e] = ok ? __uint_as_float(g[0][e]) : 0.f;
-        gv[4 + e] = ok ? __uint_as_float(g[1][e]) : 0.f;
+    for (int q = 0; q < GQ; ++q) {
+      uint16_t* gs = st + (lrow + 64 * q) * LDK + lk;
+      if constexpr (GF32) {
+        float gv[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          gv[e] = ok[q] ? __uint_as_float(g[q][0][e]) : 0.f;
+          gv[4 + e] = ok[q] ? __uint_as_float(g[q][1][e]) : 0.f;
+        }
+        split_store(gv, NG, gs);
+      } else {
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4_t*>(gs) = ok[q] ? g[q][0] : z;   // bf16: its own plane
       }
-      split_store(gv, NG, st);
-    } else {
-      const u32x4_t z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4_t*>(st) = ok ? g[0] : z;   // bf16: its own plane
     }
+    uint16_t* ss = st + NG * GPLANE + lrow * LDK + lk;
 #pragma unroll
-    for (int pl = 0; pl < kSinvPlanes; ++pl) *reinterpret_cast<u32x4_t*>(st + (NG + pl) * PLANE) = sv[pl];
+    for (int pl = 0; pl < kSinvPlanes; ++pl) *reinterpret_cast<u32x4_t*>(ss + pl * SPLANE) = sv[pl];
   };
   // K pipeline: LDS buffer kt&1 holds stage kt; iteration kt requests
   // stage kt+3 (into the set stage kt-1 left, stored two iterations ago),
@@ -841,39 +858,49 @@ __device__ __forceinline__ void apply_tile(const PrecondDev& pd, const ApplyTask
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       const int kk = ks * 16 + 8 * (lane >> 5);
-      bf16x8_t fa[NG], fb[3];
+      bf16x8_t fa[MB][NG], fb[3];
 #pragma unroll
-      for (int pl = 0; pl < NG; ++pl)
-        fa[pl] = *reinterpret_cast<const bf16x8_t*>(st + pl * PLANE + (wm * WT + (lane & 31)) * LDK + kk);
+      for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int pl = 0; pl < NG; ++pl)
+          fa[b][pl] = *reinterpret_cast<const bf16x8_t*>(st + pl * GPLANE + (wm * WR + b * 32 + (lane & 31)) * LDK + kk);
 #pragma unroll
       for (int pl = 0; pl < 3; ++pl)
-        fb[pl] = *reinterpret_cast<const bf16x8_t*>(st + (NG + pl) * PLANE + (wn * WT + (lane & 31)) * LDK + kk);
+        fb[pl] = *reinterpret_cast<const bf16x8_t*>(st + NG * GPLANE + pl * SPLANE + (wn * WC + (lane & 31)) * LDK + kk);
       // small products first
 #pragma unroll
       for (int sum = 2; sum >= 0; --sum)
 #pragma unroll
         for (int i = 0; i < NG; ++i) {
           const int j = sum - i;
-          if (j >= 0 && j < 3) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc, 0, 0, 0);
+          if (j >= 0 && j < 3) {
+#pragma unroll
+            for (int b = 0; b < MB; ++b) acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[b][i], fb[j], acc[b], 0, 0, 0);
+          }
         }
     }
     sstore(buf ^ 1, gr[(h + 1) % NR], gok[(h + 1) % NR], sb[(h + 1) % NR]);
     __syncthreads();
   }
-  // epilogue through LDS: row segments of P
+  // epilogue through LDS (each wave its own area): row segments of P, one
+  // 32-row block at a time
   float* ep = reinterpret_cast<float*>(smem) + wave * (32 * EPP);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) ep[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * EPP + (lane & 31)] = acc[r];
-  __syncthreads();
-  for (int s = lane; s < 32 * WT; s += 64) {
-    const int row = s / WT, col = s % WT;
-    const int gi = r0 + wm * WT + row, cj = c0 + wn * WT + col;
-    if (gi < pd.rows && cj < d) pd.p[static_cast<size_t>(gi) * pd.ld_p + gcol0 + cj] = ep[row * EPP + col];
+  for (int b = 0; b < MB; ++b) {
+    if (b > 0) __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ep[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * EPP + (lane & 31)] = acc[b][r];
+    __syncthreads();
+    for (int s = lane; s < 32 * WC; s += 64) {
+      const int row = s / WC, col = s % WC;
+      const int gi = r0 + wm * WR + b * 32 + row, cj = c0 + wn * WC + col;
+      if (gi < pd.rows && cj < d) pd.p[static_cast<size_t>(gi) * pd.ld_p + gcol0 + cj] = ep[row * EPP + col];
+    }
   }
 }
 
-// One launch per gradient dtype, with the LDS its planes need (bf16: 40 KB,
-// four blocks per CU; float32: 60 KB, two).
+// One launch per gradient dtype, with the LDS its planes need (bf16: 50 KB,
+// three blocks per CU; float32: 90 KB, one).
 template <bool GF32>
 __global__ __launch_bounds__(kThreads)
 void apply_kernel(const PrecondDev* __restrict__ pds, const ApplyTask* __restrict__ tasks) {

@@ -230,8 +230,9 @@ def test_plan_newton_muon_layer():
         pcs.append(p)
     plan = mm.plan_describe(ts, mm.default_hparams(), pcs)
     assert plan["preconds"] == [{"d": 768, "nblocks": 1, "dp": 768}, {"d": 768, "nblocks": 4, "dp": 768}]
-    # 64x64 tiles of P: (2304 + 768 + 3072) x 768 with one block, 768 x 768 x 4 blocks
-    assert plan["apply_tiles"] == (36 + 12 + 48) * 12 + 4 * 12 * 12
+    # tiles of P, 128 rows x 64 columns: QKV 2304, O 768, up 3072 rows against one
+    # 768-wide S^-1 (12 column tiles); down 768 rows against four
+    assert plan["apply_tiles"] == (18 + 6 + 24) * 12 + 4 * 6 * 12
     assert plan["launch_order"][0] == "precond_apply"
     assert len(plan["units"]) == 3 + 1 + 1 + 1          # packed QKV split into three blocks
     # a preconditioned tensor must match d * nblocks of its slot
