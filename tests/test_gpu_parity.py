@@ -364,3 +364,41 @@ def test_step_timed_reports_every_launch():
     names = [n for n, _ in ph]
     assert names[0] == "momentum/bf16" and names[-1] == "bx/bf16#5" and len(names) == 16
     assert all(ms >= 0 for _, ms in ph)
+
+
+def test_degenerate_handles_step_cleanly():
+    """Handles with nothing for some phases: no tensors at all; only AdamW
+    tensors (no Newton-Schulz group); a preconditioner slot that no tensor
+    uses, refreshed anyway.  Each steps without error or flag, and leaves
+    what it does not own untouched."""
+    say("case: degenerate handles (empty, AdamW only, unused slot)")
+    hp = mm.default_hparams()
+    st = mm.MuonStep([], hp)
+    st.step()
+    torch.cuda.synchronize()
+    assert st.flags() == 0
+    st.close()
+
+    w = torch.full((4, 6), 0.5, device="cuda")
+    g = torch.full((4, 6), 0.25, device="cuda")
+    m, v = torch.zeros_like(w), torch.zeros_like(w)
+    st = mm.MuonStep([mm.adam_tensor_desc(w, g, m, v)], hp)
+    st.step()
+    torch.cuda.synchronize()
+    assert st.flags() == 0 and bool(torch.isfinite(w).all()) and not bool((w == 0.5).all())
+    st.close()
+
+    p = B.MuonPrecond()
+    p.d, p.nblocks = 64, 1
+    W = torch.zeros(8, 16, device="cuda")
+    G = torch.randn(8, 16, device="cuda", generator=torch.Generator("cuda").manual_seed(5))
+    M = torch.zeros_like(W)
+    st = mm.MuonStep([mm.tensor_desc(W, G, M)], hp, preconds=[p])
+    acts = torch.randn(100, 64, device="cuda", generator=torch.Generator("cuda").manual_seed(6))
+    st.precond_refresh(0, 0, acts, damping=1e-2)
+    st.step()
+    torch.cuda.synchronize()
+    assert st.flags() == 0
+    st.close()
+    # the matrix ignored the slot: its momentum is the plain (1 - mu) G
+    assert torch.allclose(M, (1.0 - hp.momentum) * G, rtol=1e-6, atol=0)
