@@ -318,7 +318,10 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
   // groups: one per NS precision; a precision with many matrices is split
   // into lanes of about equal Newton-Schulz work (longest first), which
   // muon_step runs on separate streams so one lane's ramp-up and tail
-  // overlap another's tiles
+  // overlap another's tiles.  The float32 group takes the lanes after the
+  // bf16 group's while both fit in kLanes, so two small groups of different
+  // precision (launch-bound chains) run side by side.
+  int bf16_lanes = 0;
   for (int f = 0; f < 2; ++f) {
     std::vector<int> ids;
     for (size_t k = 0; k < plan.units.size(); ++k)
@@ -345,9 +348,11 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
       load[l] += cost(k);
       lg[l].units.push_back(k);
     }
+    const int lane0 = f == 1 && bf16_lanes + lanes <= kLanes ? bf16_lanes : 0;
+    if (f == 0) bf16_lanes = lanes;
     for (int l = 0; l < lanes; ++l) {
       lg[l].f32 = f == 1;
-      lg[l].lane = l;
+      lg[l].lane = lane0 + l;
       std::sort(lg[l].units.begin(), lg[l].units.end());   // tensor order inside a lane
       for (size_t gi = 0; gi < lg[l].units.size(); ++gi) plan.units[lg[l].units[gi]].group_index = int(gi);
       plan.groups.push_back(std::move(lg[l]));

@@ -199,6 +199,7 @@ def test_plan_split_rows_and_fp32():
     assert u[4]["ns"] == "f32" and (u[4]["mp"], u[4]["np"]) == (64, 64)
     assert [g["ns"] for g in plan["groups"]] == ["bf16", "f32"]
     assert [g["units"] for g in plan["groups"]] == [3, 2]
+    assert [g["lane"] for g in plan["groups"]] == [0, 1]
     assert len(plan["launch_order"]) == 32
     p0 = mm.plan_describe([t], mm.default_hparams(ns_steps=0))
     assert p0["launch_order"] == ["momentum/bf16", "update/bf16"]
@@ -261,6 +262,9 @@ def test_filter_tensors_become_matrices():
     plan = mm.plan_describe(ts, mm.default_hparams())
     assert sorted(u["m"] for u in plan["units"]) == [64, 64, 256, 256, 256, 256]
     assert [g["units"] for g in plan["groups"]] == [4, 2]
+    # two single-lane groups of different precision take lanes 0 and 1 (their
+    # launch-bound chains run side by side on two streams)
+    assert [g["lane"] for g in plan["groups"]] == [0, 1]
 
 
 def fake_adam(rows, cols, base, dtype=B.MUON_BF16, ld=None):
