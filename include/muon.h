@@ -201,7 +201,8 @@ muon_status_t muon_precond_refresh_accumulated(muon_handle_t h, int32_t slot, in
  * matrices (lr < 0 uses hp.lr), AdamW on the kind-ADAMW tensors (hp.adam_lr).
  * Asynchronous on `stream`; no allocation, no synchronisation.  Part of the
  * work may run on streams the handle created at muon_init (large groups of
- * matrices split in lanes; AdamW beside the Muon phases): they wait for an
+ * matrices split in lanes; a float32 group beside a single-lane bf16 group;
+ * AdamW beside the Muon phases): they wait for an
  * event recorded on `stream` at the start of the call and `stream` waits for
  * theirs at the end, so to the caller the step is ordered on `stream` alone
  * (also when `stream` is being captured into a graph). */
