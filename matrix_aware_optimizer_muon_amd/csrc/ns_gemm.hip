@@ -418,49 +418,16 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   u32x2_t preq[NPRE][RITER];                          // master: int8 corrections (bf16)
   const int kt0 = ti * BTM / BK;                     // K step of the tile's first row
 
-  // K pipeline: a ring of NS stages filled by direct-to-LDS loads.  Step kt
-  // waits for its own stage (the stages issued after it may stay in
-  // flight), passes a barrier (every wave's part of the stage has landed,
-  // and every wave is done with step kt-1, whose buffer is refilled next),
-  // issues stage kt+NS-1 into that buffer and runs the MFMAs of stage kt.
-  // Stage indices past the end are clamped to the last stage (its copy lands
-  // in a buffer nobody reads again), so every step has the same NS-2 newer
-  // stages in flight and a fixed wait count.
   const int KT = K / BK;
-  constexpr uint32_t STAGE_B = STAGE * sizeof(E), TILE_B = T_A * sizeof(E);
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s) {
-    const int sc = min(s, KT - 1);
-    issue_stage<NIA, NIB, E>(pa + sc * a_step, pb + sc * b_step, aoff, boff, ring0 + s * STAGE_B,
-                             ring0 + s * STAGE_B + TILE_B, wave, !diag);
-  }
-  for (int kt = 0; kt < KT; ++kt) {
-    if (diag) wait_vmcnt<(NS - 2) * NIA>();   // newer stages in flight: NS-2 of one operand each
-    else wait_vmcnt<(NS - 2) * (NIA + NIB)>();
-    ring_barrier();
-    const int nx = min(kt + NS - 1, KT - 1);
-    const uint32_t ls = ring0 + ((kt + NS - 1) % NS) * STAGE_B;
-    issue_stage<NIA, NIB, E>(pa + nx * a_step, pb + nx * b_step, aoff, boff, ls, ls + TILE_B, wave, !diag);
-    const E* cs = smem + (kt % NS) * STAGE;
-    if constexpr (KMAJOR_B)
-      capture_master<F32, NPRE, RITER, SEGS, WTM, BK, BTN>(cs + T_A, kt, kt0, wm, wn * WTN, lane, pre0, pre1);
-    else if constexpr (PH == kSquare)
-      capture_atile<F32, NPRE, RITER, SEGS, WTM, WTN, BK>(cs, kt, (tj * BTN + wn * WTN) / BK, wm, wn, lane, pre0, pre1);
-    mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, BTN>(cs, diag ? cs : cs + T_A, acc, lane, wm, wn);
-  }
-  wait_vmcnt<0>();   // the clamped copies of the last stage
-  __syncthreads();   // the epilogue reuses the ring as staging
 
-  // ---------------------------------------------------------------- epilogue
-  // B X, bf16: the lo half of the master (the hi half was captured from
-  // LDS) is requested before the first LDS round, so one HBM latency is
-  // paid per tile, not per strip.
+  // B X, bf16: the epilogue's HBM operands are the lo half of the master
+  // (the hi half is captured from LDS) and, in the last iteration, the
+  // weight segments this lane updates (bf16 weights with aligned rows; the
+  // segments are rows of W for a wide unit, columns of the tile for a tall
+  // one, where X column j is weight row j).  They are requested once per
+  // tile, behind the last K step's MFMAs.
   const int row_base = ti * BTM + wm * WTM;
   const int col_base = tj * BTN + wn * WTN;
-  // In the last iteration the weight segments this lane updates are
-  // requested at the same time (bf16 weights with aligned rows; the
-  // segments are rows of W for a wide unit, columns of the tile for a tall
-  // one, where X column j is weight row j).
   static_assert(!KMAJOR_B || RITER == WTN * 4 / 64, "row and column passes give a lane equally many segments");
   u32x4_t wpre[NPRE][RITER];
   const bool wfast = KMAJOR_B && !F32 && p.last && !u.param_f32 && u.vec_param;
@@ -474,28 +441,77 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
       wj = row_base + pi * 32 + (sg / WTN) * 8;
     }
   };
-  if constexpr (KMAJOR_B && !F32) {
-#pragma unroll
-    for (int pi = 0; pi < NBM; ++pi)
-#pragma unroll
-      for (int q = 0; q < RITER; ++q) {
-        const int sg = lane + 64 * q;
-        const size_t off = static_cast<size_t>(row_base + pi * 32 + sg / SEGS) * np + col_base + (sg % SEGS) * 8;
-        preq[pi][q] = gld<u32x2_t>(static_cast<const int8_t*>(u.xl) + off);
-      }
-    if (wfast) {
+  auto epilogue_loads = [&]() {
+    if constexpr (KMAJOR_B && !F32) {
 #pragma unroll
       for (int pi = 0; pi < NBM; ++pi)
 #pragma unroll
         for (int q = 0; q < RITER; ++q) {
-          int wi, wj;
-          wseg(pi, q, wi, wj);
-          if (wi < u.rows && wj + 8 <= u.cols)
-            wpre[pi][q] = gld<u32x4_t>(static_cast<const uint16_t*>(u.param) + static_cast<size_t>(wi) * u.ld_param + wj);
+          const int sg = lane + 64 * q;
+          const size_t off = static_cast<size_t>(row_base + pi * 32 + sg / SEGS) * np + col_base + (sg % SEGS) * 8;
+          preq[pi][q] = gld<u32x2_t>(static_cast<const int8_t*>(u.xl) + off);
         }
+      if (wfast) {
+#pragma unroll
+        for (int pi = 0; pi < NBM; ++pi)
+#pragma unroll
+          for (int q = 0; q < RITER; ++q) {
+            int wi, wj;
+            wseg(pi, q, wi, wj);
+            if (wi < u.rows && wj + 8 <= u.cols)
+              wpre[pi][q] = gld<u32x4_t>(static_cast<const uint16_t*>(u.param) + static_cast<size_t>(wi) * u.ld_param + wj);
+          }
+      }
     }
+  };
+
+  // K pipeline: a ring of NS stages filled by direct-to-LDS loads.  Step kt
+  // waits for its own stage (the stages issued after it may stay in
+  // flight), passes a barrier (every wave's part of the stage has landed,
+  // and every wave is done with step kt-1, whose buffer is refilled next),
+  // issues stage kt+NS-1 into that buffer and runs the MFMAs of stage kt.
+  // With more than two stages, indices past the end are clamped to the last
+  // stage (its copy lands in a buffer nobody reads again), so every step has
+  // the same NS-2 newer stages in flight and a fixed wait count.  With two
+  // stages every step waits for everything, so the last step issues no copy
+  // and sends the epilogue's HBM loads out in its place: they overlap the
+  // final MFMAs and the epilogue does not wait for a dead copy.
+  constexpr uint32_t STAGE_B = STAGE * sizeof(E), TILE_B = T_A * sizeof(E);
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) {
+    const int sc = min(s, KT - 1);
+    issue_stage<NIA, NIB, E>(pa + sc * a_step, pb + sc * b_step, aoff, boff, ring0 + s * STAGE_B,
+                             ring0 + s * STAGE_B + TILE_B, wave, !diag);
+  }
+  auto kstep = [&](int kt, bool tail) {
+    if (diag) wait_vmcnt<(NS - 2) * NIA>();   // newer stages in flight: NS-2 of one operand each
+    else wait_vmcnt<(NS - 2) * (NIA + NIB)>();
+    ring_barrier();
+    if (!tail) {
+      const int nx = min(kt + NS - 1, KT - 1);
+      const uint32_t ls = ring0 + ((kt + NS - 1) % NS) * STAGE_B;
+      issue_stage<NIA, NIB, E>(pa + nx * a_step, pb + nx * b_step, aoff, boff, ls, ls + TILE_B, wave, !diag);
+    }
+    const E* cs = smem + (kt % NS) * STAGE;
+    if constexpr (KMAJOR_B)
+      capture_master<F32, NPRE, RITER, SEGS, WTM, BK, BTN>(cs + T_A, kt, kt0, wm, wn * WTN, lane, pre0, pre1);
+    else if constexpr (PH == kSquare)
+      capture_atile<F32, NPRE, RITER, SEGS, WTM, WTN, BK>(cs, kt, (tj * BTN + wn * WTN) / BK, wm, wn, lane, pre0, pre1);
+    if (tail) epilogue_loads();
+    mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, BTN>(cs, diag ? cs : cs + T_A, acc, lane, wm, wn);
+  };
+  if constexpr (NS == 2) {
+    for (int kt = 0; kt < KT - 1; ++kt) kstep(kt, false);
+    kstep(KT - 1, true);
+    ring_barrier();    // no copy in flight; every wave is done reading the ring
+  } else {
+    for (int kt = 0; kt < KT; ++kt) kstep(kt, false);
+    epilogue_loads();
+    wait_vmcnt<0>();   // the clamped copies of the last stage
+    __syncthreads();   // the epilogue reuses the ring as staging
   }
 
+  // ---------------------------------------------------------------- epilogue
   // Each wave stages one 32-row strip of its accumulators in its own LDS
   // area (so the strips need no block barrier: one wave's LDS accesses take
   // effect in order), then writes row segments (natural layout) and, where
