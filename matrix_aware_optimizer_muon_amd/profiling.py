@@ -4,6 +4,11 @@
         Markdown table of a `rocprofv3 --kernel-trace --stats --output-format csv`
         run (per-kernel calls, total and average duration, grid, LDS bytes).
 
+    python -m matrix_aware_optimizer_muon_amd.profiling mfma DIR [--title T] [--command C ...]
+        Markdown table of one `rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16
+        SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE` pass: MFMA flops per
+        dispatch, rate against the bf16 peak, MFMA busy share.
+
     python -m matrix_aware_optimizer_muon_amd.profiling traffic \
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --copy-bytes N \
         [--out JSON] [--command C ...]
@@ -155,6 +160,76 @@ def counter_per_dispatch(dirpath, counter):
     return {k: sum(v.values()) / len(v) for k, v in per.items()}
 
 
+def _agent(dirpath):
+    """SIMD count, XCD count and peak engine clock (MHz) of the GPU agent."""
+    with open(_one(dirpath, "*agent_info.csv")) as f:
+        for r in csv.DictReader(f):
+            if int(_num(r, "Simd_Count")) > 0:
+                return int(_num(r, "Simd_Count")), int(_num(r, "Num_Xcc", default=1.0)) or 1, \
+                    _num(r, "Max_Engine_Clk_Fcompute")
+    raise RuntimeError("no GPU agent in the run")
+
+
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+
+
+def mfma_table(dirpath, peak_tflops):
+    """Per kernel kind, from one `--pmc` pass of MFMA_COUNTERS (which also
+    records each dispatch's start and end):
+      gflop      MFMA flops per dispatch (the bf16 op counter counts units of
+                 512 flops);
+      avg_us     dispatch duration (dispatches run one at a time while
+                 counters are collected);
+      tflops     the two combined, and `frac` of `peak_tflops`;
+      busy_pct   MFMA busy cycles as a share of the SIMD cycles of the
+                 counter window (GRBM_GUI_ACTIVE arrives summed over the XCDs,
+                 so one XCD's active cycles are the sum / Num_Xcc; the window
+                 is somewhat longer than the dispatch, so this reads low)."""
+    simds, xcc, _ = _agent(dirpath)
+    disp = {}
+    with open(_one(dirpath, "*counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            d = disp.setdefault(key, {"kind": kernel_kind(r.get("Kernel_Name", "")),
+                                      "ns": _num(r, "End_Timestamp") - _num(r, "Start_Timestamp")})
+            c = r.get("Counter_Name")
+            d[c] = d.get(c, 0.0) + float(r["Counter_Value"])
+    rows = {}
+    for d in disp.values():
+        e = rows.setdefault(d["kind"], {"dispatches": 0, "flop": 0.0, "ns": 0.0, "busy": 0.0, "gui": 0.0})
+        e["dispatches"] += 1
+        e["flop"] += 512.0 * d.get(MFMA_COUNTERS[0], 0.0)
+        e["busy"] += d.get(MFMA_COUNTERS[1], 0.0)
+        e["gui"] += d.get(MFMA_COUNTERS[2], 0.0) / xcc
+        e["ns"] += d["ns"]
+    out = {}
+    for k, e in rows.items():
+        if e["flop"] <= 0:
+            continue
+        n = e["dispatches"]
+        tflops = e["flop"] / e["ns"] / 1e3 if e["ns"] > 0 else float("nan")
+        out[k] = {"dispatches": n, "gflop": e["flop"] / n / 1e9, "avg_us": e["ns"] / n / 1e3,
+                  "tflops": tflops, "frac": tflops / peak_tflops,
+                  "busy_pct": 100.0 * e["busy"] / (e["gui"] * simds) if e["gui"] else float("nan")}
+    return out
+
+
+def mfma_markdown(dirpath, title, command, peak_tflops):
+    rows = mfma_table(dirpath, peak_tflops)
+    lines = [command] if isinstance(command, str) else list(command)
+    out = [f"# {title}", "", "Commands (repository root on one MI355X, `libmuon.so` built):", "", "```",
+           *[c.strip() for c in lines], "```", "",
+           f"MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; peak {peak_tflops:.0f} TFLOP/s (dense bf16). "
+           "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x SIMDs), over the counter window. "
+           f"Kernel sources: {kernel_source_hash()}.", "",
+           "| kernel | dispatches | MFMA GFLOP per dispatch | avg µs | MFMA TFLOP/s | % of peak | MFMA busy % |",
+           "|---|---:|---:|---:|---:|---:|---:|"]
+    for k, e in sorted(rows.items(), key=lambda kv: -kv[1]["gflop"] * kv[1]["dispatches"]):
+        out.append(f"| {k} | {e['dispatches']} | {e['gflop']:.2f} | {e['avg_us']:.1f} | {e['tflops']:.0f} | "
+                   f"{100 * e['frac']:.1f} | {e['busy_pct']:.1f} |")
+    return "\n".join(out) + "\n"
+
+
 def traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes, commands):
     fetch = counter_per_dispatch(fetch_dir, "FETCH_SIZE")
     write = counter_per_dispatch(write_dir, "WRITE_SIZE")
@@ -192,6 +267,12 @@ def main(argv=None):
     t.add_argument("--title", default="Kernel trace")
     t.add_argument("--command", action="append", default=[])
     t.add_argument("--out")
+    m = sub.add_parser("mfma")
+    m.add_argument("dir")
+    m.add_argument("--title", default="MFMA counters")
+    m.add_argument("--command", action="append", default=[])
+    m.add_argument("--peak-tflops", type=float, default=2500.0)
+    m.add_argument("--out")
     c = sub.add_parser("traffic")
     for a in ("--fetch", "--write", "--copy-fetch", "--copy-write"):
         c.add_argument(a, required=True)
@@ -201,6 +282,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.cmd == "trace":
         text = trace_markdown(args.dir, args.title, args.command)
+    elif args.cmd == "mfma":
+        text = mfma_markdown(args.dir, args.title, args.command, args.peak_tflops)
     else:
         text = json.dumps(traffic(args.fetch, args.write, args.copy_fetch, args.copy_write, args.copy_bytes,
                                   args.command), indent=1) + "\n"

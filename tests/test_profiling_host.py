@@ -96,6 +96,33 @@ def test_traffic_is_scaled_by_the_copy_calibration(tmp_path):
     assert d["kernel_source_hash"] == P.kernel_source_hash()
 
 
+def test_mfma_table_from_counters(tmp_path):
+    _write(str(tmp_path / "run_agent_info.csv"), ["Simd_Count", "Num_Xcc", "Max_Engine_Clk_Fcompute"],
+           [{"Simd_Count": 0, "Num_Xcc": 0, "Max_Engine_Clk_Fcompute": 0},      # the CPU agent
+            {"Simd_Count": 1024, "Num_Xcc": 8, "Max_Engine_Clk_Fcompute": 2400}])
+    fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    us = 1000
+    rows = []
+    # two bx dispatches of 100 us: 50 G MFMA flops each, active 2 GHz on
+    # each of 8 XCDs, MFMA busy a quarter of the SIMD cycles
+    for d, t0 in ((1, 0), (2, 200 * us)):
+        for c, v in (("SQ_INSTS_VALU_MFMA_MOPS_BF16", 50e9 / 512), ("GRBM_GUI_ACTIVE", 8 * 2e9 * 100e-6),
+                     ("SQ_VALU_MFMA_BUSY_CYCLES", 0.25 * 1024 * 2e9 * 100e-6)):
+            rows.append({"Dispatch_Id": d, "Kernel_Name": BX, "Counter_Name": c, "Counter_Value": v,
+                         "Start_Timestamp": t0, "End_Timestamp": t0 + 100 * us})
+    # a copy does no MFMA work and is left out
+    rows.append({"Dispatch_Id": 3, "Kernel_Name": COPY, "Counter_Name": "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                 "Counter_Value": 0, "Start_Timestamp": 0, "End_Timestamp": 1})
+    _write(str(tmp_path / "run_counter_collection.csv"), fields, rows)
+    t = P.mfma_table(str(tmp_path), 2500.0)
+    assert set(t) == {"bx"}
+    e = t["bx"]
+    assert e["dispatches"] == 2 and e["gflop"] == pytest.approx(50.0) and e["avg_us"] == pytest.approx(100.0)
+    assert e["tflops"] == pytest.approx(500.0) and e["frac"] == pytest.approx(0.2)
+    assert e["busy_pct"] == pytest.approx(25.0)
+    assert "| bx | 2 | 50.00 | 100.0 | 500 | 20.0 | 25.0 |" in P.mfma_markdown(str(tmp_path), "t", "cmd", 2500.0)
+
+
 def test_bench_work_counts():
     # symmetric products: Gram m(m+1)n, square m^2(m+1), update 2m^2n
     f = bench.ns_flops(768, 3072)
