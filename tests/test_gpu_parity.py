@@ -122,7 +122,8 @@ def test_tiny_fp32_workload():
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_ragged_shapes(dtype):
     shapes = [(300, 520), (520, 300), (17, 33), (33, 17), (1, 7), (7, 1), (1, 1),
-              (257, 1000), (1000, 257), (64, 64), (3 * 96, 96), (129, 129)]
+              (257, 1000), (1000, 257), (64, 64), (3 * 96, 96), (129, 129),
+              (128, 200), (200, 128)]   # bf16 m = 128: two K steps in the square and B X
     say(f"case: ragged shapes {dtype}")
     wl = adhoc("ragged", shapes, dtype, split={10: 96})
     c = Case(wl, wl.tensors)
