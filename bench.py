@@ -106,12 +106,68 @@ def cpu_baseline(wl, hp, budget_s):
         done += 1
         if spent >= budget_s:
             break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    threads = max([i.get("num_threads", 1) for i in blas] or [1])
     frac = done / len(layers)
     return {"value": frac / spent, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
             "sample": f"float64 oracle on {done} layer steps ({6 * done} matrix steps; one whole step is "
                       f"{len(layers)} layers, {len(wl.tensors)} matrices) in {spent:.1f} s, scaled to one "
-                      f"whole step"}
+                      f"whole step",
+            "cpu_model": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0)),
+            "blas": [{"name": i.get("internal_api"), "version": i.get("version"), "threads": i.get("num_threads"),
+                      "architecture": i.get("architecture")} for i in blas]}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def gpu_clock_mhz(run_steps, seconds=2.0):
+    """Shader clock (MHz) as rocm-smi reports it while the step runs: a
+    thread keeps stepping for about `seconds` while rocm-smi is read once.
+    None if rocm-smi is unavailable or its output is not understood."""
+    import re
+    import subprocess
+    import threading
+    done = threading.Event()
+
+    def busy():
+        t0 = time.perf_counter()
+        while not done.is_set() and time.perf_counter() - t0 < seconds + 5.0:
+            run_steps()
+
+    th = threading.Thread(target=busy, daemon=True)
+    th.start()
+    time.sleep(0.3)
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], stdout=subprocess.PIPE,
+                           stderr=subprocess.DEVNULL, text=True, timeout=20)
+        text = r.stdout
+    except (OSError, subprocess.SubprocessError):
+        text = ""
+    finally:
+        done.set()
+        th.join()
+    try:
+        d = json.loads(text)
+    except ValueError:
+        return None
+    for card in d.values():
+        if not isinstance(card, dict):
+            continue
+        for k, v in card.items():
+            if "sclk" in k.lower():
+                m = re.search(r"(\d+)\s*mhz", str(v).lower())
+                if m:
+                    return int(m.group(1))
+    return None
 
 
 def main():
@@ -238,6 +294,14 @@ def main():
                         "accumulate_ms_per_block": round(acc_ms, 4),
                         "accumulate_tflops": round(syrk_flop / (acc_ms * 1e-3) / 1e12, 2)}
         assert st.flags() == 0, "non-finite values in the preconditioner timing"
+    def burst():
+        for _ in range(10):
+            st.step()
+        torch.cuda.synchronize(dev)
+
+    clock = gpu_clock_mhz(burst)
+    peak_mem = torch.cuda.max_memory_allocated(dev)
+    ws_bytes = st.workspace_bytes
     st.close()
 
     units = []
@@ -280,9 +344,10 @@ def main():
     ns_tflop = hp.ns_steps * sum(flops[k] for k in ("gram", "square", "bx")) / 1e12
     dom = max(totals, key=totals.get)
     src_hash = kernel_source_hash()
-    # The dominant kernel's roofline bound follows from its algorithmic
-    # intensity: below the ridge of its MFMA type (peak flops / peak bytes)
-    # it is HBM.
+    # The Newton-Schulz products are dense contractions: their roofline is
+    # the MFMA peak of their type, whatever their intensity; the element-wise
+    # kernels are bound by HBM.  The apply is priced by the bf16 MFMA work it
+    # issues.  Either way the HBM view is reported beside it.
     intensity = flops.get(dom, 0) / nbytes[dom]
     # per launch: the kind's work per step over its launches per step (with
     # two lanes each phase is two launches of about half the work)
@@ -296,14 +361,14 @@ def main():
     if dom == "precond_apply":                 # priced by the bf16 MFMA work it issues
         intensity = apply_mfma_flops / nbytes[dom]
         per_launch_flops = apply_mfma_flops / launches[dom]
-    if dom in flops and intensity >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+    hbm_gbs = per_launch_bytes / (avg[dom] * 1e-3) / 1e9
+    if dom in flops:
         achieved = per_launch_flops / (avg[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4)}
     else:
-        achieved = per_launch_bytes / (avg[dom] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+        roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(hbm_gbs / PEAK_HBM_GBS, 4)}
     roof["traffic"] = load_traffic(dom, src_hash, args.workload)
     roof["kernel"] = dom
     roof["avg_launch_ms"] = round(avg[dom], 5)
@@ -312,7 +377,8 @@ def main():
     if dom in flops:
         roof["algorithmic_flops"] = int(per_launch_flops)
         roof["intensity_flop_per_byte"] = round(intensity, 1)
-        roof["mfma_tflops"] = round(per_launch_flops / (avg[dom] * 1e-3) / 1e12, 2)
+        roof["hbm_view"] = {"achieved": round(hbm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(hbm_gbs / PEAK_HBM_GBS, 4)}
 
     out = {
         "metric": METRIC,
@@ -340,6 +406,12 @@ def main():
         "kernel_source_hash": src_hash,
         "roofline": roof,
         "phase_hbm_gbs": {k: round(nbytes[k] * iters[k] / (totals[k] * 1e-3) / 1e9, 1) for k in avg if k in nbytes},
+        "ns_kernel_frac_bf16_peak": {k: round(flops[k] * iters[k] / launches[k] / (avg[k] * 1e-3) / 1e12
+                                              / PEAK_BF16_TFLOPS, 4)
+                                     for k in ("gram", "square", "bx") if k in avg},
+        "gpu_clock_mhz": clock,
+        "peak_device_memory_gb": round(peak_mem / 1e9, 3),
+        "workspace_gb": round(ws_bytes / 1e9, 3),
         "cpu_baseline": None,
     }
     if precond_info is not None:

@@ -285,10 +285,27 @@ class MuonStep:
                                    self.workspace.numel(), self._stream(None)))
         self._h = h
 
-    def _stream(self, stream):
+    def _torch_stream(self, stream):
         torch = _torch()
-        s = stream if stream is not None else torch.cuda.current_stream(self.device)
-        return ctypes.c_void_p(s.cuda_stream)
+        return stream if stream is not None else torch.cuda.current_stream(self.device)
+
+    def _stream(self, stream):
+        return ctypes.c_void_p(self._torch_stream(stream).cuda_stream)
+
+    @staticmethod
+    def _guard(acts, stream):
+        """The activations are read asynchronously on `stream`.  Instead of
+        holding a reference (which would pin every micro-batch until a
+        synchronising call), tell torch's caching allocator that `stream`
+        uses the memory: once the caller drops the tensor, its block is not
+        handed out again before the work queued on `stream` so far is done."""
+        acts.record_stream(stream)
+
+    def plan(self) -> dict:
+        """The plan of this handle (muon_plan_describe of its tensors)."""
+        descs = [self._descs[i] for i in range(self._n)]
+        pcs = [self._pcs[i] for i in range(self._npc)]
+        return plan_describe(descs, self.hp, pcs)
 
     def step(self, lr: float = -1.0, stream=None):
         _check(self._lib.muon_step(self._h, ctypes.c_float(lr), self._stream(stream)))
@@ -310,12 +327,11 @@ class MuonStep:
         dt = {torch.float32: MUON_F32, torch.bfloat16: MUON_BF16}.get(acts.dtype)
         if dt is None:
             raise ValueError(f"unsupported activation dtype {acts.dtype}")
-        self._keep.append(acts)
-        # the refresh is asynchronous: keep the activations alive until the
-        # stream has consumed them (the next flags()/close() synchronises)
+        s = self._torch_stream(stream)
         _check(self._lib.muon_precond_refresh(self._h, slot, block, ctypes.c_void_p(acts.data_ptr()),
                                               acts.shape[0], acts.stride(0), dt, ctypes.c_float(damping),
-                                              self._stream(stream)))
+                                              ctypes.c_void_p(s.cuda_stream)))
+        self._guard(acts, s)
 
     def precond_accumulate(self, slot: int, block: int, acts, beta: float = 1.0, stream=None):
         """Add one micro-batch of layer-input activations to the running
@@ -326,10 +342,11 @@ class MuonStep:
         dt = {torch.float32: MUON_F32, torch.bfloat16: MUON_BF16}.get(acts.dtype)
         if dt is None:
             raise ValueError(f"unsupported activation dtype {acts.dtype}")
-        self._keep.append(acts)      # asynchronous: kept alive until the next sync
+        s = self._torch_stream(stream)
         _check(self._lib.muon_precond_accumulate(self._h, slot, block, ctypes.c_void_p(acts.data_ptr()),
                                                  acts.shape[0], acts.stride(0), dt, ctypes.c_float(beta),
-                                                 self._stream(stream)))
+                                                 ctypes.c_void_p(s.cuda_stream)))
+        self._guard(acts, s)
 
     def precond_refresh_accumulated(self, slot: int, block: int, damping: float = 1e-4, reset: bool = True,
                                     stream=None):

@@ -693,8 +693,11 @@ std::string plan_json(const Plan& plan, const muon_hparams_t& hp) {
   }
   s += "],\"preconds\":[";
   for (size_t k = 0; k < plan.slots.size(); ++k) {
-    std::snprintf(buf, sizeof(buf), "%s{\"d\":%lld,\"nblocks\":%d,\"dp\":%d}", k ? "," : "",
-                  (long long)plan.slots[k].d, plan.slots[k].nblocks, plan.slots[k].dp);
+    // s_offset / sinv_offset: workspace byte offsets of the slot's S blocks
+    // (float32, dp x dp each) and of its S^-1 (three bf16 planes per block)
+    std::snprintf(buf, sizeof(buf), "%s{\"d\":%lld,\"nblocks\":%d,\"dp\":%d,\"s_offset\":%zu,\"sinv_offset\":%zu}",
+                  k ? "," : "", (long long)plan.slots[k].d, plan.slots[k].nblocks, plan.slots[k].dp,
+                  plan.slots[k].off_s, plan.slots[k].off_sinv);
     s += buf;
   }
   std::snprintf(buf, sizeof(buf), "],\"apply_tiles\":%zu,\"adamw_tensors\":%zu,\"adamw_tasks\":%zu,"

@@ -101,3 +101,25 @@ def check_w_bf16(W_gpu_bits, ref, lr, scales, tol_o=2e-2):
              + 1e-6 * float(np.linalg.norm(Wr)))
     frac = float(np.mean(W_gpu_bits == ref["W_bits"]))
     return err, bound, frac
+
+
+def check_w_update_elementwise(W_gpu_bits, W0_bits, O_gpu, lr, weight_decay, scales):
+    """The fused weight update, element by element: given the GPU's own
+    orthogonalised update O (read back through update_out), each new bf16
+    weight must be one of the two bf16 neighbours of W - lr*wd*W - lr*s*O
+    (decoupled decay, Muon README "Usage").  The kernel evaluates that in
+    float32 and rounds once; its float32 roundings move the value by at most a
+    few float32 ulps of the operands, which matters only where W and lr*s*O
+    nearly cancel.  So |W'_gpu - W'| <= ulp_bf16(W') + 8 * 2^-24 (|W| +
+    lr*s*|O|), with W' in float64.  Returns (max of |W'_gpu - W'| / that
+    bound, fraction not bitwise equal to RNE(W'))."""
+    s = np.asarray(scales, np.float64).reshape(-1, 1)
+    W0 = orc.bf16_bits_to_f64(W0_bits)
+    O = np.asarray(O_gpu, np.float64)
+    W_exp = orc.apply_update(W0, O, lr, weight_decay, s)
+    Wg = orc.bf16_bits_to_f64(np.asarray(W_gpu_bits))
+    allowed = bf16_ulp(W_exp) + 8.0 * 2.0 ** -24 * (np.abs(W0) + lr * np.abs(s * O))
+    ratio = np.abs(Wg - W_exp) / allowed
+    exp_bits = orc.f64_to_bf16_bits(W_exp)
+    off = np.asarray(W_gpu_bits) != exp_bits
+    return (float(ratio.max()) if ratio.size else 0.0), (float(np.mean(off)) if off.size else 0.0)

@@ -230,7 +230,16 @@ def test_plan_newton_muon_layer():
         p.d, p.nblocks = d, nb
         pcs.append(p)
     plan = mm.plan_describe(ts, mm.default_hparams(), pcs)
-    assert plan["preconds"] == [{"d": 768, "nblocks": 1, "dp": 768}, {"d": 768, "nblocks": 4, "dp": 768}]
+    assert [{k: pc[k] for k in ("d", "nblocks", "dp")} for pc in plan["preconds"]] == \
+        [{"d": 768, "nblocks": 1, "dp": 768}, {"d": 768, "nblocks": 4, "dp": 768}]
+    # the slots' S and S^-1 lie inside the workspace, apart, 256-byte aligned
+    spans = []
+    for pc in plan["preconds"]:
+        blk = pc["dp"] * pc["dp"] * pc["nblocks"]
+        spans += [(pc["s_offset"], pc["s_offset"] + 4 * blk), (pc["sinv_offset"], pc["sinv_offset"] + 6 * blk)]
+    spans.sort()
+    assert all(a % 256 == 0 for a, _ in spans) and spans[-1][1] <= plan["workspace_bytes"]
+    assert all(spans[i][1] <= spans[i + 1][0] for i in range(len(spans) - 1))
     # tiles of P, 128 rows x 64 columns: QKV 2304, O 768, up 3072 rows against one
     # 768-wide S^-1 (12 column tiles); down 768 rows against four
     assert plan["apply_tiles"] == (18 + 6 + 24) * 12 + 4 * 6 * 12
