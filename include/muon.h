@@ -21,7 +21,8 @@
  *   All tensor pointers are DEVICE pointers owned by the caller (param,
  *   grad, momentum, update_out, activations) together with one caller-
  *   allocated device WORKSPACE whose size muon_workspace_size() reports.  The
- *   library never allocates device memory.  Everything registered at
+ *   library never allocates device memory (muon_init_static uses instead a
+ *   fixed array that is part of the loaded library).  Everything registered at
  *   muon_init() must stay allocated and unmoved until muon_destroy(); re-init
  *   after reallocating any of it.  The library owns only a small host-side
  *   handle.
@@ -165,6 +166,24 @@ muon_status_t muon_init(muon_handle_t* out, const muon_tensor_t* tensors, int32_
                         const muon_precond_t* preconds, int32_t n_preconds,
                         const muon_hparams_t* hp, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same as
+ * muon_init, but the workspace is the library's own static device array of
+ * 64 MiB per GPU (held by each GPU the library runs on until the process
+ * ends), so the call takes no workspace and allocates nothing on the device.
+ * The handle creates no streams or events either: muon_step runs every launch
+ * on the caller's stream.  Requests whose workspace (muon_workspace_size)
+ * exceeds 64 MiB return MUON_ERR_WORKSPACE_TOO_SMALL before any GPU call.
+ * The array belongs to the calling thread's current device.  All static
+ * handles of one GPU share it: each muon_init_static zero-fills it for its
+ * own plan, which supersedes every earlier static handle of that GPU (their
+ * calls then return MUON_ERR_BAD_ARG; muon_destroy still releases them).
+ * Work of a superseded handle still queued, or of two static handles used on
+ * one GPU at once, races on the array. */
+muon_status_t muon_init_static(muon_handle_t* out, const muon_tensor_t* tensors, int32_t n_tensors,
+                               const muon_precond_t* preconds, int32_t n_preconds,
+                               const muon_hparams_t* hp, void* stream);
 
 /* Newton-Muon: rebuilds block `block` of preconditioner slot `slot` from
  * n_rows x d activations (row-major, leading dimension ld, dtype) of the

@@ -90,6 +90,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "muon_default_hparams": (None, [PH]),
         "muon_workspace_size": (i32, [PT, i32, PP, i32, PH, ctypes.POINTER(sz)]),
         "muon_init": (i32, [ctypes.POINTER(vp), PT, i32, PP, i32, PH, vp, sz, vp]),
+        "muon_init_static": (i32, [ctypes.POINTER(vp), PT, i32, PP, i32, PH, vp]),
         "muon_precond_refresh": (i32, [vp, i32, i32, vp, i64, i64, i32, f32, vp]),
         "muon_precond_accumulate": (i32, [vp, i32, i32, vp, i64, i64, i32, f32, vp]),
         "muon_precond_refresh_accumulated": (i32, [vp, i32, i32, f32, i32, vp]),
@@ -269,7 +270,11 @@ class MuonStep:
     """
 
     def __init__(self, descs: Sequence[MuonTensor], hp: Optional[MuonHparams] = None,
-                 preconds: Sequence[MuonPrecond] = (), device=None, keepalive=()):
+                 preconds: Sequence[MuonPrecond] = (), device=None, keepalive=(), static_scratch=False):
+        """static_scratch=True binds the handle to the library's static
+        device scratch (muon_init_static): no workspace is allocated, the
+        request must fit in it, and a later static handle on the same GPU
+        supersedes this one."""
         torch = _torch()
         self._lib = load_library()
         self.hp = hp if hp is not None else default_hparams()
@@ -277,12 +282,18 @@ class MuonStep:
         self._pcs, self._npc = _array(list(preconds), MuonPrecond)
         self.workspace_bytes = workspace_size(descs, self.hp, preconds)
         self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
-        self.workspace = torch.empty(max(self.workspace_bytes, 256), dtype=torch.uint8, device=self.device)
         self._keep = list(keepalive)
         h = ctypes.c_void_p()
-        _check(self._lib.muon_init(ctypes.byref(h), self._descs, self._n, self._pcs, self._npc,
-                                   ctypes.byref(self.hp), ctypes.c_void_p(self.workspace.data_ptr()),
-                                   self.workspace.numel(), self._stream(None)))
+        if static_scratch:
+            self.workspace = None
+            with torch.cuda.device(self.device):
+                _check(self._lib.muon_init_static(ctypes.byref(h), self._descs, self._n, self._pcs, self._npc,
+                                                  ctypes.byref(self.hp), self._stream(None)))
+        else:
+            self.workspace = torch.empty(max(self.workspace_bytes, 256), dtype=torch.uint8, device=self.device)
+            _check(self._lib.muon_init(ctypes.byref(h), self._descs, self._n, self._pcs, self._npc,
+                                       ctypes.byref(self.hp), ctypes.c_void_p(self.workspace.data_ptr()),
+                                       self.workspace.numel(), self._stream(None)))
         self._h = h
 
     def _torch_stream(self, stream):

@@ -15,6 +15,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -247,7 +248,7 @@ std::vector<GemmTask> xcd_order(const std::vector<GemmTask>& tiles, const std::v
 }
 
 muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_t* pcs, int32_t npc,
-                         const muon_hparams_t* hp, Plan& plan) {
+                         const muon_hparams_t* hp, Plan& plan, bool single_lane = false) {
   muon_status_t st = validate(ts, n, pcs, npc, hp);
   if (st != MUON_OK) return st;
   plan = Plan();
@@ -335,7 +336,7 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
       const UnitPlan& u = plan.units[k];
       bx_tiles += int64_t(u.mp / (u.f32 ? kTileF32 : kTileBxRowsBf16)) * (u.np / (u.f32 ? kTileF32 : kTileBxColsBf16));
     }
-    const int lanes = ids.size() >= size_t(kLaneMinUnits) && bx_tiles <= kLaneMaxBxTiles ? kLanes : 1;
+    const int lanes = !single_lane && ids.size() >= size_t(kLaneMinUnits) && bx_tiles <= kLaneMaxBxTiles ? kLanes : 1;
     auto cost = [&](int k) {
       const UnitPlan& u = plan.units[k];
       return double(u.mp) * u.mp * (u.mp + 3.0 * u.np);
@@ -348,7 +349,7 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
       load[l] += cost(k);
       lg[l].units.push_back(k);
     }
-    const int lane0 = f == 1 && bf16_lanes + lanes <= kLanes ? bf16_lanes : 0;
+    const int lane0 = !single_lane && f == 1 && bf16_lanes + lanes <= kLanes ? bf16_lanes : 0;
     if (f == 0) bf16_lanes = lanes;
     for (int l = 0; l < lanes; ++l) {
       lg[l].f32 = f == 1;
@@ -555,6 +556,8 @@ struct muon_handle_s {
   hipEvent_t ev_fork = nullptr;
   std::vector<hipEvent_t> events;
   std::vector<std::string> phase_names;
+  int static_device = -1;        // muon_init_static: the GPU whose scratch array holds the workspace
+  uint64_t static_generation = 0;  // ... and which of its static inits this handle is
 };
 
 namespace {
@@ -783,20 +786,48 @@ muon_status_t muon_plan_describe(const muon_tensor_t* tensors, int32_t n_tensors
   return MUON_OK;
 }
 
-muon_status_t muon_init(muon_handle_t* out, const muon_tensor_t* tensors, int32_t n_tensors,
-                        const muon_precond_t* preconds, int32_t n_preconds, const muon_hparams_t* hp,
-                        void* workspace, size_t workspace_bytes, void* stream) {
-  if (!out) return fail(MUON_ERR_NULL_ARG, "out is NULL");
-  *out = nullptr;
-  Plan plan;
-  muon_status_t st = build_plan(tensors, n_tensors, preconds, n_preconds, hp, plan);
-  if (st != MUON_OK) return st;
-  if (!workspace) return fail(MUON_ERR_NULL_ARG, "workspace is NULL");
-  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
-    return fail(MUON_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
-  if (workspace_bytes < plan.total)
-    return fail(MUON_ERR_WORKSPACE_TOO_SMALL,
-                "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " + std::to_string(plan.total));
+}  // extern "C"
+
+namespace {
+
+// Static device scratch of muon_init_static, for callers that cannot
+// allocate device memory.  Each GPU the library runs on holds one copy until
+// the process ends; host code must use the address hipGetSymbolAddress
+// returns for the current device (the array's name is a host-side stand-in).
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+std::mutex g_static_mu;
+void* g_static_ptr[kMaxDevices] = {};
+uint64_t g_static_gen[kMaxDevices] = {};
+
+// The calling thread's current device and its scratch address (looked up
+// once per device, with that device current).
+muon_status_t static_scratch(int* dev_out, void** ptr_out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MUON_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MUON_ERR_UNSUPPORTED, "device index beyond the static scratch table");
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  if (!g_static_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(MUON_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_static_ptr[dev] = ptr;
+  }
+  *dev_out = dev;
+  *ptr_out = g_static_ptr[dev];
+  return MUON_OK;
+}
+
+// Body shared by muon_init and muon_init_static: `plan` is built and checked
+// against the workspace already.  With `with_streams` false the handle
+// creates no streams or events: every launch of muon_step then runs on the
+// caller's stream.
+muon_status_t init_handle(muon_handle_t* out, Plan&& plan, const muon_tensor_t* tensors, int32_t n_tensors,
+                          const muon_hparams_t* hp, void* workspace, void* stream, bool with_streams) {
   const uintptr_t wlo = reinterpret_cast<uintptr_t>(workspace), whi = wlo + plan.total;
   for (int32_t i = 0; i < n_tensors; ++i) {
     const muon_tensor_t& t = tensors[i];
@@ -832,8 +863,8 @@ muon_status_t muon_init(muon_handle_t* out, const muon_tensor_t* tensors, int32_
   h->last_stream = s;
   int max_lane = 0;
   for (const Group& g : h->plan.groups) max_lane = std::max(max_lane, g.lane);
-  const bool aux = !h->plan.adam_tasks.empty() && !h->plan.units.empty();
-  if (max_lane > 0 || aux) {
+  const bool aux = with_streams && !h->plan.adam_tasks.empty() && !h->plan.units.empty();
+  if (with_streams && (max_lane > 0 || aux)) {
     e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);
     if (aux && e == hipSuccess) e = hipStreamCreateWithFlags(&h->aux_stream, hipStreamNonBlocking);
     if (aux && e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_aux, hipEventDisableTiming);
@@ -874,6 +905,65 @@ muon_status_t muon_init(muon_handle_t* out, const muon_tensor_t* tensors, int32_
   return MUON_OK;
 }
 
+// A static handle may only launch while its init is the latest one on its
+// GPU: a later muon_init_static reuses the same array for another plan.
+muon_status_t check_live(muon_handle_t h) {
+  if (h->static_device < 0) return MUON_OK;
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  if (g_static_gen[h->static_device] != h->static_generation)
+    return fail(MUON_ERR_BAD_ARG, "a later muon_init_static on this GPU has taken over the static scratch; "
+                                  "initialise this handle again");
+  return MUON_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+muon_status_t muon_init(muon_handle_t* out, const muon_tensor_t* tensors, int32_t n_tensors,
+                        const muon_precond_t* preconds, int32_t n_preconds, const muon_hparams_t* hp,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!out) return fail(MUON_ERR_NULL_ARG, "out is NULL");
+  *out = nullptr;
+  Plan plan;
+  muon_status_t st = build_plan(tensors, n_tensors, preconds, n_preconds, hp, plan);
+  if (st != MUON_OK) return st;
+  if (!workspace) return fail(MUON_ERR_NULL_ARG, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(MUON_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  if (workspace_bytes < plan.total)
+    return fail(MUON_ERR_WORKSPACE_TOO_SMALL,
+                "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " + std::to_string(plan.total));
+  return init_handle(out, std::move(plan), tensors, n_tensors, hp, workspace, stream, true);
+}
+
+muon_status_t muon_init_static(muon_handle_t* out, const muon_tensor_t* tensors, int32_t n_tensors,
+                               const muon_precond_t* preconds, int32_t n_preconds, const muon_hparams_t* hp,
+                               void* stream) {
+  if (!out) return fail(MUON_ERR_NULL_ARG, "out is NULL");
+  *out = nullptr;
+  Plan plan;
+  muon_status_t st = build_plan(tensors, n_tensors, preconds, n_preconds, hp, plan, /*single_lane=*/true);
+  if (st != MUON_OK) return st;
+  if (plan.total > kStaticScratchBytes)
+    return fail(MUON_ERR_WORKSPACE_TOO_SMALL,
+                "the request needs " + std::to_string(plan.total) + " bytes of workspace; the static scratch holds " +
+                    std::to_string(kStaticScratchBytes) + " (use muon_init with a caller workspace)");
+  int dev = -1;
+  void* ptr = nullptr;
+  if ((st = static_scratch(&dev, &ptr)) != MUON_OK) return st;
+  uint64_t gen;
+  {
+    std::lock_guard<std::mutex> lk(g_static_mu);
+    gen = ++g_static_gen[dev];
+  }
+  st = init_handle(out, std::move(plan), tensors, n_tensors, hp, ptr, stream, false);
+  if (st != MUON_OK) return st;
+  (*out)->static_device = dev;
+  (*out)->static_generation = gen;
+  return MUON_OK;
+}
+
 namespace {
 
 PrecondBlockDev block_dev(muon_handle_t h, const SlotPlan& sp, int32_t block) {
@@ -893,6 +983,7 @@ PrecondBlockDev block_dev(muon_handle_t h, const SlotPlan& sp, int32_t block) {
 
 muon_status_t check_slot_block(muon_handle_t h, int32_t slot, int32_t block) {
   if (!h) return fail(MUON_ERR_NULL_ARG, "handle is NULL");
+  if (check_live(h) != MUON_OK) return MUON_ERR_BAD_ARG;
   if (slot < 0 || size_t(slot) >= h->plan.slots.size()) return fail(MUON_ERR_BAD_ARG, "no such preconditioner slot");
   if (block < 0 || block >= h->plan.slots[size_t(slot)].nblocks) return fail(MUON_ERR_BAD_ARG, "no such block in the slot");
   return MUON_OK;
@@ -955,6 +1046,7 @@ muon_status_t muon_precond_refresh(muon_handle_t h, int32_t slot, int32_t block,
 muon_status_t muon_step(muon_handle_t h, float lr, void* stream) {
   if (!h) return fail(MUON_ERR_NULL_ARG, "handle is NULL");
   if (!std::isfinite(lr)) return fail(MUON_ERR_BAD_ARG, "lr is not finite");
+  if (check_live(h) != MUON_OK) return MUON_ERR_BAD_ARG;
   return enqueue_step(h, lr < 0.f ? h->hp.lr : lr, static_cast<hipStream_t>(stream), nullptr);
 }
 
@@ -962,6 +1054,7 @@ muon_status_t muon_step_timed(muon_handle_t h, float lr, void* stream, float* ph
                               int32_t* n_phases) {
   if (!h) return fail(MUON_ERR_NULL_ARG, "handle is NULL");
   if (!std::isfinite(lr)) return fail(MUON_ERR_BAD_ARG, "lr is not finite");
+  if (check_live(h) != MUON_OK) return MUON_ERR_BAD_ARG;
   const size_t np = h->phase_names.size();
   if (h->events.size() < np + 1) {
     while (h->events.size() < np + 1) {
@@ -992,6 +1085,7 @@ const char* muon_phase_name(muon_handle_t h, int32_t phase) {
 
 muon_status_t muon_set_adam_step(muon_handle_t h, int64_t steps_taken, void* stream) {
   if (!h) return fail(MUON_ERR_NULL_ARG, "handle is NULL");
+  if (check_live(h) != MUON_OK) return MUON_ERR_BAD_ARG;
   if (steps_taken < 0 || steps_taken > int64_t(UINT32_MAX) - 1) return fail(MUON_ERR_BAD_ARG, "step count out of range");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_adam_set(reinterpret_cast<AdamState*>(h->ws + h->plan.off_adam_state),
@@ -1003,6 +1097,7 @@ muon_status_t muon_set_adam_step(muon_handle_t h, int64_t steps_taken, void* str
 
 muon_status_t muon_get_adam_step(muon_handle_t h, void* stream, int64_t* steps_taken) {
   if (!h || !steps_taken) return fail(MUON_ERR_NULL_ARG, "handle or output is NULL");
+  if (check_live(h) != MUON_OK) return MUON_ERR_BAD_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   AdamState st;
   hipError_t e = hipMemcpyAsync(&st, h->ws + h->plan.off_adam_state, sizeof(st), hipMemcpyDeviceToHost, s);
@@ -1014,6 +1109,7 @@ muon_status_t muon_get_adam_step(muon_handle_t h, void* stream, int64_t* steps_t
 
 muon_status_t muon_get_flags(muon_handle_t h, void* stream, int32_t reset, uint32_t* flags) {
   if (!h || !flags) return fail(MUON_ERR_NULL_ARG, "handle or flags is NULL");
+  if (check_live(h) != MUON_OK) return MUON_ERR_BAD_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint32_t v = 0;
   hipError_t e = hipStreamSynchronize(s);

@@ -134,6 +134,28 @@ def test_init_rejects_bad_workspace_without_touching_the_gpu():
     assert B.STATUS_NAMES[lib.muon_step(None, 0.02, None)] == "MUON_ERR_NULL_ARG"
 
 
+def test_init_static_rejects_oversized_requests_without_touching_the_gpu():
+    # the static scratch holds 64 MiB: a 4096 x 4096 bf16 matrix needs more
+    # (two bf16 X buffers, the int8 corrections, A and B: 160 MiB), and the
+    # call fails before any GPU call; invalid requests fail as for muon_init
+    pa, npc = B._array([], B.MuonPrecond)
+    hp = mm.default_hparams()
+    h = ctypes.c_void_p()
+    big = fakes([(4096, 4096)])
+    assert ws_status(big)[1] > 64 << 20
+    ta, n = B._array(big, B.MuonTensor)
+    st = lib.muon_init_static(ctypes.byref(h), ta, n, pa, npc, ctypes.byref(hp), None)
+    assert B.STATUS_NAMES[st] == "MUON_ERR_WORKSPACE_TOO_SMALL" and not h.value
+    assert b"static scratch" in lib.muon_last_error()
+    bad = fakes([(64, 128)])
+    bad[0].ld_param = 100
+    ta, n = B._array(bad, B.MuonTensor)
+    st = lib.muon_init_static(ctypes.byref(h), ta, n, pa, npc, ctypes.byref(hp), None)
+    assert B.STATUS_NAMES[st] == "MUON_ERR_BAD_SHAPE"
+    st = lib.muon_init_static(None, ta, n, pa, npc, ctypes.byref(hp), None)
+    assert B.STATUS_NAMES[st] == "MUON_ERR_NULL_ARG"
+
+
 def _workload_fakes(name, layers=None):
     w = synth.workload(name, layers)
     ts, base = [], BASE
