@@ -177,6 +177,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true", help="skip reading the shader clock (profiled runs)")
     ap.add_argument("--workload", default="gpt2s", choices=["gpt2s", "gpt2s_aux", "square", "gpt2xl", "conv", "tiny", "nmuon"],
                     help="weight set to step (the headline metric is quoted on gpt2s)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -299,7 +300,7 @@ def main():
             st.step()
         torch.cuda.synchronize(dev)
 
-    clock = gpu_clock_mhz(burst)
+    clock = None if args.no_clock else gpu_clock_mhz(burst)
     peak_mem = torch.cuda.max_memory_allocated(dev)
     ws_bytes = st.workspace_bytes
     st.close()

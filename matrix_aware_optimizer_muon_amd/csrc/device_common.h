@@ -102,6 +102,29 @@ __device__ __forceinline__ void master_encode8(const float* v, u32x4_t& hi, u32x
   lo[1] = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
 }
 
+// The correction of one element: q = round((bits(x) - bits(bf16(x))) / 256),
+// clamped to [-127, 127], as its byte.
+__device__ __forceinline__ uint32_t master_corr(float x) {
+  const uint32_t hb = static_cast<uint32_t>(f32_to_bf16(x)) << 16;
+  const int d = __float_as_int(x) - static_cast<int>(hb);
+  return static_cast<uint32_t>(min(max((d + 128) >> 8, -127), 127)) & 0xFFu;
+}
+
+// Layout of the correction array (one byte per element of the padded m_p x
+// n_p master): 32 x 32 blocks of 1 KB, block (bi, bj) at (bi * n_p/32 + bj)
+// KB; inside a block, the 16 bytes of lane l hold, in MFMA accumulator
+// register order r = 4q + e, the elements at row 8q + 4(l/32) + e, column
+// l%32 -- the positions the B X kernel's accumulators hold.
+__device__ __forceinline__ size_t corr_block_offset(int np, int r0, int c0) {   // r0, c0 multiples of 32
+  return (static_cast<size_t>(r0 >> 5) * (np >> 5) + (c0 >> 5)) * 1024;
+}
+__device__ __forceinline__ size_t corr_index(int np, int r, int c) {
+  const int lr = r & 31;
+  const int lane = (c & 31) + 32 * ((lr >> 2) & 1);
+  const int reg = 4 * (lr >> 3) + (lr & 3);
+  return corr_block_offset(np, r & ~31, c & ~31) + lane * 16 + reg;
+}
+
 __device__ __forceinline__ void master_decode8(const u32x4_t& hi, const u32x2_t& lo, float* v) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {

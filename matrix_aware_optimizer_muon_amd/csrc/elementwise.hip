@@ -25,29 +25,38 @@ namespace muon {
 namespace {
 
 constexpr int kThreads = 256;
+// LDS tile of a momentum block: 64 x (64 + 1) floats for the transposed
+// (right-side) walk, 16 x (256 + 8) for the correction blocks of a
+// left-side one (pitch 264 puts the two half-waves of a column read in
+// different banks).
+constexpr int kLeftPitch = kEwCols + 8;
+constexpr int kTileFloats = kEwTile * (kEwTile + 1) > kEwRows * kLeftPitch ? kEwTile * (kEwTile + 1)
+                                                                            : kEwRows * kLeftPitch;
 
-// Store one 8-element row segment of the X master: bf16 hi and its int8
-// correction (element offsets are shared, the correction array holds one
-// byte per element), or float32.
+// Store one 8-element row segment of X: the bf16 hi part of the master (its
+// int8 corrections are written separately, in their blocked layout), or the
+// float32 value.
 template <bool F32>
-__device__ __forceinline__ void store_seg(void* hi, void* lo, int64_t ld, int r, int c, const float* v) {
+__device__ __forceinline__ void store_seg(void* hi, int64_t ld, int r, int c, const float* v) {
   const size_t off = static_cast<size_t>(r) * ld + c;
-  if constexpr (F32) {
-    st8_f32(hi, off, v);
-  } else {
-    u32x4_t h;
-    u32x2_t q;
-    master_encode8(v, h, q);
-    gst(static_cast<uint16_t*>(hi) + off, h);
-    gst(static_cast<int8_t*>(lo) + off, q);
-  }
+  if constexpr (F32) st8_f32(hi, off, v);
+  else gst(static_cast<uint16_t*>(hi) + off, pack8_bf16(v));
+}
+
+// Four consecutive X rows of one column (values x[0..3]) as their four int8
+// master corrections, packed low byte first.
+__device__ __forceinline__ uint32_t corr4(const float* x) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w |= static_cast<uint32_t>(master_corr(x[e])) << (8 * e);
+  return w;
 }
 
 // One tile of the momentum phase; GF32: the gradient is float32 (else
 // bf16), a compile-time choice so the tile's loads are straight-line code.
 template <bool F32, bool GF32>
 __device__ __forceinline__ void momentum_tile(const UnitDev& u, const EwTask& t, const K1Params& p,
-                                              float (*tile)[kEwTile + 1], float* wsum) {
+                                              float* tile, float* wsum) {
   const bool left = u.side == kLeft;
   const int r0 = t.tr * (left ? kEwRows : kEwTile), c0 = t.tc * (left ? kEwCols : kEwTile);
   const int seg_sh = left ? 5 : 3;                   // log2 of 8-element segments per tile row
@@ -124,10 +133,14 @@ __device__ __forceinline__ void momentum_tile(const UnitDev& u, const EwTask& t,
     if (left) {
       // X = U: rows of the unit stay rows (padding inside the tile gets
       // zeros; a 256-wide tile may reach past the padded width np)
-      if (j0 < u.np) store_seg<F32>(u.xh[0], u.xl, u.np, i, j0, uv);
+      if (j0 < u.np) store_seg<F32>(u.xh[0], u.np, i, j0, uv);
+      if constexpr (!F32) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tile[lr * kLeftPitch + lc + e] = uv[e];
+      }
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) tile[lr][lc + e] = uv[e];
+      for (int e = 0; e < 8; ++e) tile[lr * (kEwTile + 1) + lc + e] = uv[e];
     }
   }
   if (!left) {
@@ -141,8 +154,44 @@ __device__ __forceinline__ void momentum_tile(const UnitDev& u, const EwTask& t,
       const int xr = s >> 3, xs = s & 7;
       float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = tile[xs * 8 + e][xr];
-      store_seg<F32>(u.xh[0], u.xl, u.np, c0 + xr, r0 + xs * 8, v);
+      for (int e = 0; e < 8; ++e) v[e] = tile[(xs * 8 + e) * (kEwTile + 1) + xr];
+      store_seg<F32>(u.xh[0], u.np, c0 + xr, r0 + xs * 8, v);
+    }
+    if constexpr (!F32) {
+      // corrections: the 64 x 64 X tile is 2 x 2 whole 32 x 32 blocks; thread
+      // t writes lane t%64's 16 bytes of block t/64 (X row c0 + 32 bi + 8q +
+      // 4h + e, column r0 + 32 bj + l%32, i.e. U-tile element [32 bj + l%32]
+      // [32 bi + 8q + 4h + e])
+      const int blk = threadIdx.x >> 6, l = threadIdx.x & 63;
+      const int bi = blk >> 1, bj = blk & 1;
+      const float* trow = &tile[(32 * bj + (l & 31)) * (kEwTile + 1) + 32 * bi + 4 * (l >> 5)];
+      u32x4_t w;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[q] = corr4(trow + 8 * q);
+      gst(static_cast<int8_t*>(u.xl) + corr_block_offset(u.np, c0 + 32 * bi, r0 + 32 * bj) + l * 16, w);
+    }
+  } else if constexpr (!F32) {
+    // corrections of a left tile: its 16 rows are half of a row of 32 x 32
+    // blocks (register groups q = 0, 1 or 2, 3 of each lane); thread t writes
+    // 8 bytes of lane t%64 of block t/64, both halves of the wave.
+    __syncthreads();
+    const int half = (r0 & 31) >> 4;        // rows 0..15 or 16..31 of the block row
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      const int s = threadIdx.x + kThreads * q2;
+      const int jb = s >> 6, l = s & 63;
+      const int col = c0 + 32 * jb;
+      if (col >= u.np) continue;
+      const float* tcol = &tile[4 * (l >> 5) * kLeftPitch + 32 * jb + (l & 31)];
+      float x[8];
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * qq + e] = tcol[(8 * qq + e) * kLeftPitch];
+      u32x2_t w;
+      w[0] = corr4(x);
+      w[1] = corr4(x + 4);
+      gst(static_cast<int8_t*>(u.xl) + corr_block_offset(u.np, r0 - 16 * half, col) + l * 16 + 8 * half, w);
     }
   }
 
@@ -159,7 +208,7 @@ template <bool F32>
 __global__ __launch_bounds__(kThreads) void momentum_kernel(const UnitDev* __restrict__ units,
                                                             const EwTask* __restrict__ tasks,
                                                             K1Params p) {
-  __shared__ float tile[kEwTile][kEwTile + 1];
+  __shared__ float tile[kTileFloats];
   __shared__ float wsum[kThreads / 64];
   const EwTask t = tasks[blockIdx.x];
   const UnitDev& u = units[t.unit];
@@ -175,8 +224,13 @@ __device__ __forceinline__ void load_master_seg(const UnitDev& u, int r, int c, 
   if constexpr (F32) {
     ld8_f32(u.xh[0], off, v);
   } else {
-    master_decode8(gld<u32x4_t>(static_cast<const uint16_t*>(u.xh[0]) + off),
-                   gld<u32x2_t>(static_cast<const int8_t*>(u.xl) + off), v);
+    const uint16_t* hp = static_cast<const uint16_t*>(u.xh[0]) + off;
+    const int8_t* xl = static_cast<const int8_t*>(u.xl);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int hb = static_cast<int>(static_cast<uint32_t>(gld<uint16_t>(hp + e)) << 16);
+      v[e] = __int_as_float(hb + 256 * static_cast<int>(gld<int8_t>(xl + corr_index(u.np, r, c + e))));
+    }
   }
 }
 

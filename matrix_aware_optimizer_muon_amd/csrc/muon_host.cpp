@@ -42,6 +42,7 @@ struct UnitPlan {
   int64_t row0 = 0;
   int rows = 0, cols = 0, side = 0, m = 0, n = 0, mp = 0, np = 0;
   bool f32 = false;
+  int tile = kTileM;     // bf16 GEMM tile shape (TileCfg)
   float lr_scale = 1.f;
   size_t off_xh0 = 0, off_xh1 = 0, off_xl = 0, off_a = 0, off_b = 0;
   int k1_tile0 = 0, k1_ntiles = 0, k1_tr = 0, k1_tc = 0;
@@ -53,9 +54,35 @@ struct Group {
   int lane = 0;            // 0: caller's stream; l > 0: the handle's stream l
   std::vector<int> units;  // global unit ids
   std::vector<EwTask> ew;
-  std::vector<GemmTask> gram, sq, bx;
-  size_t off_units = 0, off_ew = 0, off_gram = 0, off_sq = 0, off_bx = 0;
+  // per GEMM phase and tile shape (TileCfg): the tiles of the group's units
+  // of that shape, in launch order (one launch per non-empty list)
+  std::vector<GemmTask> gemm[3][kTileCfgs];
+  size_t off_units = 0, off_ew = 0;
+  size_t off_gemm[3][kTileCfgs] = {};
 };
+
+const char* kPhaseNames[3] = {"gram", "square", "bx"};
+const int kLaunchOrder[kTileCfgs] = {kTileL, kTileM};   // per phase: the longer 256-tile launch first
+
+// bf16 tile edge of a unit.  The 256 x 256 tiles (one block of eight
+// 128 x 64-wave tiles per CU) halve the operand bytes per flop and read a
+// third of the LDS bytes per flop of the 128 x 128 ones; measured, they are
+// faster once m reaches 2048 (4096 x 4096: 580 steps/s against 535) and no
+// faster below (GPT-2-XL's 1600-row units: even; GPT-2-small's 768: 20 %
+// slower Gram phases, whose few tiles then fill the chip in fewer, emptier
+// waves).  MUON_TILE_POLICY 1 / 2 force 128 / 256 (measurement builds).
+#ifndef MUON_TILE_POLICY
+#define MUON_TILE_POLICY 0
+#endif
+constexpr int kTileLMinRows = 2048;
+int choose_tile(int m) {
+  if (MUON_TILE_POLICY == 1) return kTileM;
+  if (MUON_TILE_POLICY == 2) return kTileL;
+  return m >= kTileLMinRows ? kTileL : kTileM;
+}
+
+// suffix of a GEMM launch's phase name per tile edge
+const char* tile_tag(bool f32, int cfg) { return !f32 && cfg == kTileL ? "x256" : ""; }
 
 struct SlotPlan {
   int64_t d = 0;
@@ -106,6 +133,9 @@ muon_status_t validate(const muon_tensor_t* ts, int32_t n, const muon_precond_t*
       !finite(hp->ns_a) || !finite(hp->ns_b) || !finite(hp->ns_c))
     return fail(MUON_ERR_BAD_ARG, "non-finite hyper-parameter");
   if (hp->eps < 0.f) return fail(MUON_ERR_BAD_ARG, "eps must be >= 0");
+  // the square phase folds b A into c (A A + (b/c) A)
+  if (hp->ns_steps > 0 && hp->ns_c == 0.f)
+    return fail(MUON_ERR_BAD_ARG, "ns_c must be nonzero (the quintic's A^2 coefficient)");
   if (hp->scale_mode < MUON_SCALE_NONE || hp->scale_mode > MUON_SCALE_MATCH_RMS_ADAMW)
     return fail(MUON_ERR_BAD_ARG, "unknown scale_mode");
   if (hp->momentum_form != MUON_MOM_EMA && hp->momentum_form != MUON_MOM_SGD)
@@ -155,8 +185,8 @@ muon_status_t validate(const muon_tensor_t* ts, int32_t n, const muon_precond_t*
       return fail(MUON_ERR_ALIGNMENT, who + "pointers must be aligned to their element size");
     const int64_t h = t.split_rows ? t.split_rows : t.rows;
     const int64_t m = std::min<int64_t>(h, t.cols), nn = std::max<int64_t>(h, t.cols);
-    const int64_t TR = t.dtype == MUON_F32 ? kTileF32 : kPadRowsBf16, TC = t.dtype == MUON_F32 ? kTileF32 : kPadColsBf16;
-    if (!adam && round_up(m, TR) * round_up(nn, TC) > (int64_t(1) << 31))
+    const int64_t TE = t.dtype == MUON_F32 ? kTileF32 : kTileEdgeL;
+    if (!adam && round_up(m, TE) * round_up(nn, TE) > (int64_t(1) << 31))
       return fail(MUON_ERR_UNSUPPORTED, who + "matrix too large for one orthogonalisation unit");
     auto add = [&](const void* p, int64_t ld, size_t esz, const char* what) {
       const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
@@ -304,8 +334,9 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
       u.m = int(std::min<int64_t>(h, t.cols));
       u.n = int(std::max<int64_t>(h, t.cols));
       u.f32 = t.dtype == MUON_F32 || u.m < kMinBf16NsSide;   // NS precision of the unit
-      u.mp = int(round_up(u.m, u.f32 ? kTileF32 : kPadRowsBf16));
-      u.np = int(round_up(u.n, u.f32 ? kTileF32 : kPadColsBf16));
+      u.tile = u.f32 ? kTileM : choose_tile(u.m);
+      u.mp = int(round_up(u.m, tile_edge(u.f32, u.tile)));
+      u.np = int(round_up(u.n, tile_edge(u.f32, u.tile)));
       u.lr_scale = shape_scale(h, t.cols, hp->scale_mode) * t.lr_mult;
       const int ewr = u.side == kLeft ? kEwRows : kEwTile, ewc = u.side == kLeft ? kEwCols : kEwTile;
       u.k1_tr = int((h + ewr - 1) / ewr);
@@ -334,7 +365,8 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
     int64_t bx_tiles = 0;
     for (int k : ids) {
       const UnitPlan& u = plan.units[k];
-      bx_tiles += int64_t(u.mp / (u.f32 ? kTileF32 : kTileBxRowsBf16)) * (u.np / (u.f32 ? kTileF32 : kTileBxColsBf16));
+      const int te = tile_edge(u.f32, u.tile);
+      bx_tiles += int64_t(u.mp / te) * (u.np / te);
     }
     const int lanes = !single_lane && ids.size() >= size_t(kLaneMinUnits) && bx_tiles <= kLaneMaxBxTiles ? kLanes : 1;
     auto cost = [&](int k) {
@@ -365,23 +397,20 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
       const UnitPlan& u = plan.units[g.units[gi]];
       for (int r = 0; r < u.k1_tr; ++r)
         for (int c = 0; c < u.k1_tc; ++c) g.ew.push_back({int(gi), r, c, r * u.k1_tc + c});
-      const int tg = u.f32 ? kTileF32 : kTileGramBf16;    // Gram / square tile
-      const int txr = u.f32 ? kTileF32 : kTileBxRowsBf16;  // B X tile rows
-      const int txc = u.f32 ? kTileF32 : kTileBxColsBf16;  // ... and columns
-      for (int a = 0; a < u.mp / tg; ++a)
-        for (int b = a; b < u.mp / tg; ++b) {
-          g.gram.push_back({int(gi), a, b, 0});
-          g.sq.push_back({int(gi), a, b, 0});
+      const int te = tile_edge(u.f32, u.tile);   // output tile edge of every phase
+      for (int a = 0; a < u.mp / te; ++a)
+        for (int b = a; b < u.mp / te; ++b) {
+          g.gemm[kGram][u.tile].push_back({int(gi), a, b, 0});
+          g.gemm[kSquare][u.tile].push_back({int(gi), a, b, 0});
         }
       // B X tiles column by column: the tiles that run together then share
       // one column strip of X and all of B (a unit's B is the smaller
       // operand), so each strip of X comes from HBM about once.
-      for (int b = 0; b < u.np / txc; ++b)
-        for (int a = 0; a < u.mp / txr; ++a) g.bx.push_back({int(gi), a, b, 0});
+      for (int b = 0; b < u.np / te; ++b)
+        for (int a = 0; a < u.mp / te; ++a) g.gemm[kBX][u.tile].push_back({int(gi), a, b, 0});
     }
-    g.gram = xcd_order(g.gram, plan.units, g, kGram);
-    g.sq = xcd_order(g.sq, plan.units, g, kSquare);
-    g.bx = xcd_order(g.bx, plan.units, g, kBX);
+    for (int ph = 0; ph < 3; ++ph)
+      for (int tc = 0; tc < kTileCfgs; ++tc) g.gemm[ph][tc] = xcd_order(g.gemm[ph][tc], plan.units, g, ph);
   }
   // workspace: metadata first, then the NS buffers
   size_t off = 0;
@@ -391,9 +420,11 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
   for (Group& g : plan.groups) {
     g.off_units = off; off = align_up(off + sizeof(UnitDev) * g.units.size());
     g.off_ew = off; off = align_up(off + sizeof(EwTask) * g.ew.size());
-    g.off_gram = off; off = align_up(off + sizeof(GemmTask) * g.gram.size());
-    g.off_sq = off; off = align_up(off + sizeof(GemmTask) * g.sq.size());
-    g.off_bx = off; off = align_up(off + sizeof(GemmTask) * g.bx.size());
+    for (int ph = 0; ph < 3; ++ph)
+      for (int tc = 0; tc < kTileCfgs; ++tc) {
+        g.off_gemm[ph][tc] = off;
+        off = align_up(off + sizeof(GemmTask) * g.gemm[ph][tc].size());
+      }
   }
   plan.off_pdev = off; off = align_up(off + sizeof(PrecondDev) * plan.prec_tensors.size());
   plan.off_apply = off; off = align_up(off + sizeof(ApplyTask) * plan.apply.size());
@@ -489,9 +520,9 @@ std::vector<uint8_t> build_meta(const Plan& plan, const muon_tensor_t* ts, uint8
       if (bytes) std::memcpy(meta.data() + o, src, bytes);
     };
     put(g.off_ew, g.ew.data(), g.ew.size() * sizeof(EwTask));
-    put(g.off_gram, g.gram.data(), g.gram.size() * sizeof(GemmTask));
-    put(g.off_sq, g.sq.data(), g.sq.size() * sizeof(GemmTask));
-    put(g.off_bx, g.bx.data(), g.bx.size() * sizeof(GemmTask));
+    for (int ph = 0; ph < 3; ++ph)
+      for (int tc = 0; tc < kTileCfgs; ++tc)
+        put(g.off_gemm[ph][tc], g.gemm[ph][tc].data(), g.gemm[ph][tc].size() * sizeof(GemmTask));
   }
   for (size_t pi = 0; pi < plan.prec_tensors.size(); ++pi) {
     const muon_tensor_t& t = ts[plan.prec_tensors[pi]];
@@ -631,15 +662,15 @@ muon_status_t enqueue_step(muon_handle_t h, float lr, hipStream_t s, std::vector
     for (int it = 0; it < hp.ns_steps; ++it) {
       GemmParams gp{hp.ns_a, hp.ns_b, hp.ns_c, hp.eps, it == 0, it == hp.ns_steps - 1, it & 1, 0,
                     lr, hp.weight_decay};
-      e = launch_gemm(kGram, g.f32, units, reinterpret_cast<const GemmTask*>(h->ws + g.off_gram),
-                      int(g.gram.size()), gp, gs);
-      if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("gram launch: ") + hipGetErrorString(e));
-      e = launch_gemm(kSquare, g.f32, units, reinterpret_cast<const GemmTask*>(h->ws + g.off_sq),
-                      int(g.sq.size()), gp, gs);
-      if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("square launch: ") + hipGetErrorString(e));
-      e = launch_gemm(kBX, g.f32, units, reinterpret_cast<const GemmTask*>(h->ws + g.off_bx),
-                      int(g.bx.size()), gp, gs);
-      if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("bx launch: ") + hipGetErrorString(e));
+      for (int ph = 0; ph < 3; ++ph)
+        for (int tc : kLaunchOrder) {   // the 256-row tiles (the longer launches) first
+          const std::vector<GemmTask>& tl = g.gemm[ph][tc];
+          if (tl.empty()) continue;
+          e = launch_gemm(ph, g.f32, tc, units, reinterpret_cast<const GemmTask*>(h->ws + g.off_gemm[ph][tc]),
+                          int(tl.size()), gp, gs);
+          if (e != hipSuccess || !mark())
+            return fail(MUON_ERR_HIP, std::string(kPhaseNames[ph]) + " launch: " + hipGetErrorString(e));
+        }
     }
     if (hp.ns_steps == 0) {   // otherwise the last B X phase applies the update
       K5Params k5{lr, hp.weight_decay, hp.eps, 0};
@@ -671,10 +702,11 @@ std::string plan_json(const Plan& plan, const muon_hparams_t& hp) {
     const UnitPlan& u = plan.units[i];
     std::snprintf(buf, sizeof(buf),
                   "%s{\"tensor\":%d,\"block\":%d,\"row0\":%lld,\"rows\":%d,\"cols\":%d,\"side\":\"%s\","
-                  "\"m\":%d,\"n\":%d,\"mp\":%d,\"np\":%d,\"ns\":\"%s\",\"lr_scale\":%.9g,\"k1_tiles\":%d}",
+                  "\"m\":%d,\"n\":%d,\"mp\":%d,\"np\":%d,\"ns\":\"%s\",\"tile\":%d,\"lr_scale\":%.9g,"
+                  "\"k1_tiles\":%d}",
                   i ? "," : "", u.tensor, u.block, (long long)u.row0, u.rows, u.cols,
                   u.side == kLeft ? "left" : "right", u.m, u.n, u.mp, u.np, u.f32 ? "f32" : "bf16",
-                  double(u.lr_scale), u.k1_ntiles);
+                  tile_edge(u.f32, u.tile), double(u.lr_scale), u.k1_ntiles);
     s += buf;
   }
   s += "],\"groups\":[";
@@ -684,14 +716,30 @@ std::string plan_json(const Plan& plan, const muon_hparams_t& hp) {
     auto real = [](const std::vector<GemmTask>& v) {
       return size_t(std::count_if(v.begin(), v.end(), [](const GemmTask& t) { return t.unit >= 0; }));
     };
+    // per phase: real tiles and launched blocks (with the XCD padding) of all
+    // tile shapes, and per shape the tile counts
+    size_t tiles[3] = {}, blocks[3] = {};
+    for (int ph = 0; ph < 3; ++ph)
+      for (int tc = 0; tc < kTileCfgs; ++tc) {
+        tiles[ph] += real(g.gemm[ph][tc]);
+        blocks[ph] += g.gemm[ph][tc].size();
+      }
     std::snprintf(buf, sizeof(buf),
                   "%s{\"ns\":\"%s\",\"lane\":%d,\"units\":%zu,\"momentum_tiles\":%zu,\"gram_tiles\":%zu,"
                   "\"square_tiles\":%zu,\"bx_tiles\":%zu,\"gram_blocks\":%zu,\"square_blocks\":%zu,"
-                  "\"bx_blocks\":%zu,\"tile\":%d,\"bx_tile\":[%d,%d]}",
-                  first ? "" : ",", g.f32 ? "f32" : "bf16", g.lane, g.units.size(), g.ew.size(), real(g.gram),
-                  real(g.sq), real(g.bx), g.gram.size(), g.sq.size(), g.bx.size(), g.f32 ? kTileF32 : kTileGramBf16,
-                  g.f32 ? kTileF32 : kTileBxRowsBf16, g.f32 ? kTileF32 : kTileBxColsBf16);
+                  "\"bx_blocks\":%zu,\"tiles_by_edge\":{",
+                  first ? "" : ",", g.f32 ? "f32" : "bf16", g.lane, g.units.size(), g.ew.size(), tiles[0], tiles[1],
+                  tiles[2], blocks[0], blocks[1], blocks[2]);
     s += buf;
+    bool fe = true;
+    for (int tc = 0; tc < kTileCfgs; ++tc) {
+      if (g.gemm[kGram][tc].empty() && g.gemm[kBX][tc].empty()) continue;
+      std::snprintf(buf, sizeof(buf), "%s\"%d\":[%zu,%zu,%zu]", fe ? "" : ",", tile_edge(g.f32, tc),
+                    real(g.gemm[kGram][tc]), real(g.gemm[kSquare][tc]), real(g.gemm[kBX][tc]));
+      s += buf;
+      fe = false;
+    }
+    s += "}}";
     first = false;
   }
   s += "],\"preconds\":[";
@@ -722,10 +770,13 @@ std::string plan_json(const Plan& plan, const muon_hparams_t& hp) {
     std::snprintf(buf, sizeof(buf), "%s\"momentum/%s\"", first ? "" : ",", dt);
     s += buf;
     first = false;
-    for (int it = 0; it < hp.ns_steps; ++it) {
-      std::snprintf(buf, sizeof(buf), ",\"gram/%s\",\"square/%s\",\"bx/%s\"", dt, dt, dt);
-      s += buf;
-    }
+    for (int it = 0; it < hp.ns_steps; ++it)
+      for (int ph = 0; ph < 3; ++ph)
+        for (int tc : kLaunchOrder) {
+          if (g.gemm[ph][tc].empty()) continue;
+          std::snprintf(buf, sizeof(buf), ",\"%s/%s%s\"", kPhaseNames[ph], dt, tile_tag(g.f32, tc));
+          s += buf;
+        }
     if (hp.ns_steps == 0) {
       std::snprintf(buf, sizeof(buf), ",\"update/%s\"", dt);
       s += buf;
@@ -894,11 +945,13 @@ muon_status_t init_handle(muon_handle_t* out, Plan&& plan, const muon_tensor_t* 
     if (g.units.empty()) continue;
     const std::string dt = std::string(g.f32 ? "/f32" : "/bf16") + (g.lane ? "@" + std::to_string(g.lane + 1) : "");
     h->phase_names.push_back("momentum" + dt);
-    for (int it = 0; it < hp->ns_steps; ++it) {
-      h->phase_names.push_back("gram" + dt + "#" + std::to_string(it + 1));
-      h->phase_names.push_back("square" + dt + "#" + std::to_string(it + 1));
-      h->phase_names.push_back("bx" + dt + "#" + std::to_string(it + 1));
-    }
+    for (int it = 0; it < hp->ns_steps; ++it)
+      for (int ph = 0; ph < 3; ++ph)
+        for (int tc : kLaunchOrder) {
+          if (g.gemm[ph][tc].empty()) continue;
+          h->phase_names.push_back(std::string(kPhaseNames[ph]) + dt + tile_tag(g.f32, tc) + "#" +
+                                   std::to_string(it + 1));
+        }
     if (hp->ns_steps == 0) h->phase_names.push_back("update" + dt);
   }
   *out = h;

@@ -8,23 +8,17 @@
 
 namespace muon {
 
-// Output tiles of the Newton-Schulz GEMM phases.  bf16 matrices use 128x128
-// tiles for the Gram and the square (8 waves of 64x32, two blocks per CU)
-// and kTileBxRowsBf16 x 128 tiles for B X (128: as the others; 256: 16
-// waves of 64x32, one block per CU, a quarter fewer operand bytes per
-// flop); float32 matrices use 64x64 tiles everywhere.  Every NS buffer is
-// zero-padded: m to a multiple of every row tile (kPadRowsBf16), n to one
-// of the B X column tile (kPadColsBf16), float32 to kTileF32; zero padding
-// is exact under X X^T, A A and B X.
-#ifndef MUON_BX_ROWS
-#define MUON_BX_ROWS 128
-#endif
-constexpr int kTileGramBf16 = 128;
-constexpr int kTileBxRowsBf16 = MUON_BX_ROWS;
-constexpr int kTileBxColsBf16 = 128;
-constexpr int kPadRowsBf16 = kTileBxRowsBf16 > kTileGramBf16 ? kTileBxRowsBf16 : kTileGramBf16;
-constexpr int kPadColsBf16 = 128;
+// Output tiles of the Newton-Schulz GEMM phases.  A bf16 unit takes one tile
+// edge for all three phases: 128 (kTileM) or, for large matrices, 256
+// (kTileL), chosen per unit by the planner; float32 units use 64.  Every NS
+// buffer of a unit is zero-padded to a multiple of its tile edge, which is
+// exact under X X^T, A A and B X.
+enum TileCfg : int32_t { kTileM = 0, kTileL = 1 };
+constexpr int kTileCfgs = 2;
+constexpr int kTileEdgeM = 128;
+constexpr int kTileEdgeL = 256;
 constexpr int kTileF32 = 64;
+inline int tile_edge(bool f32, int cfg) { return f32 ? kTileF32 : cfg == kTileL ? kTileEdgeL : kTileEdgeM; }
 // Tiles of the elementwise phases (momentum, update).  A unit whose X is U
 // itself (rows <= cols) is walked in kEwRows x kEwCols tiles along its rows,
 // so each wave reads and writes runs of 256 consecutive elements; a unit
@@ -55,7 +49,9 @@ struct UnitDev {
   // workspace buffers (row-major, leading dimension np for X, mp for A/B).
   // bf16 NS: xh is bf16(X) (also the MFMA operand) and xl one int8
   // correction per element (X ~= the float32 with bits(xh) + 256 xl, i.e.
-  // xh + xl * ulp(xh)/256 within xh's binade); a and b are bf16.
+  // xh + xl * ulp(xh)/256 within xh's binade), stored in 32 x 32 blocks in
+  // the MFMA accumulator order (corr_index in device_common.h); a and b are
+  // bf16.
   // float32 NS: xh is the float32 X, xl is unused, a and b are float32.  xh is double-buffered: the B X phase reads
   // the whole current iterate as an operand while its tiles write the next
   // one; xl is read and written only by the tile that owns each region.
@@ -176,7 +172,7 @@ struct AdamParams {
 
 hipError_t launch_momentum(bool f32, const UnitDev* units, const EwTask* tasks, int n_tasks,
                            const K1Params& p, hipStream_t s);
-hipError_t launch_gemm(int phase, bool f32, const UnitDev* units, const GemmTask* tasks,
+hipError_t launch_gemm(int phase, bool f32, int tile, const UnitDev* units, const GemmTask* tasks,
                        int n_tasks, const GemmParams& p, hipStream_t s);
 hipError_t launch_update(bool f32, const UnitDev* units, const EwTask* tasks, int n_tasks,
                          const K5Params& p, hipStream_t s);

@@ -19,14 +19,33 @@
 // layout and the MFMA fragments are read with gfx950's transposing LDS read
 // (ds_read_b64_tr_b16), so no transposed copy of X is ever stored.
 //
-// bf16 path: 128x128 output tile, 8 waves of 64x32 (2x1 blocks of
-// v_mfma_f32_32x32x16_bf16), K staged through LDS 64 deep in a two-stage
-// ring filled by direct-to-LDS loads (global_load_lds_dwordx4: no VGPR
-// staging, no LDS store instructions); two blocks fit per CU (64 KB LDS
-// each) so one block's epilogue overlaps the other's MFMA loop.  X is held
-// as a bf16 hi/lo pair so the a*X term keeps ~16 significant bits while the MFMA
-// operand is the hi part.
-// fp32 path: 64x64 tile, 4 waves of 32x32, v_mfma_f32_32x32x2f32.
+// The linear terms.  b A (square) and a X (B X) need the operand at the
+// output tile's own positions.  Those values pass through the block's LDS
+// anyway: A[i][j] = A[j][i] is row j, K index i of the square's second
+// operand, and row i of X is K row i of B X's second operand.  While the K
+// step that holds them sits in LDS, each lane reads the values of its own
+// accumulator registers (MFMA output layout: four consecutive rows of one
+// column per read) and adds (b/c) A or a X to the accumulators; the
+// epilogue then only scales (by c, or by s).  For X this needs the int8
+// correction of the bf16 master at the same positions, so the correction
+// array is stored in that layout (32 x 32 blocks, 16 bytes per lane), read
+// once per tile with one 16-byte load per block, and written back the same
+// way from the accumulators.
+//
+// bf16 tile shapes (the planner picks one per matrix):
+//   kTileM  128 x 128 output tiles, 8 waves of 64 x 32 (2 x 1 blocks of
+//           v_mfma_f32_32x32x16_bf16), 64-deep K stages in a two-stage
+//           ring (64 KB of LDS): two blocks per CU, so one block's epilogue
+//           overlaps the other's MFMA loop.
+//   kTileL  256 x 256 output tiles, 4 waves of 128 x 128 (4 x 4 blocks, the
+//           accumulators fill the wave's 256 AGPRs), a 128 KB ring: one
+//           block per CU, with half the operand bytes per flop of kTileM,
+//           which the L2 -> LDS path needs to keep the MFMAs fed.
+// The K stages are filled by direct-to-LDS loads (global_load_lds_dwordx4:
+// no VGPR staging, no LDS store instructions).
+// float32 path: 64x64 tile, 4 waves of 32x32, v_mfma_f32_32x32x2f32.
+#include <type_traits>
+
 #include "device_common.h"
 #include "muon_internal.h"
 
@@ -36,45 +55,31 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(1))) const u32x4_t gu32x4_t;     // global memory
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;       // LDS
 
-// Tile configuration per precision and phase (the defaults are the fastest
-// measured; 32-deep stages in a 3- or 4-stage ring, MUON_BK_BF16=32, were 9 %
-// slower on every workload).  BTM x BTN: output tile (rows x columns);
-// NWM x NWN waves, each owning a (BTM/NWM) x (BTN/NWN) block of 32x32 MFMA
-// tiles; BK: K depth of one LDS stage; NS: stages in the LDS ring (NS-1 in
-// flight while one is consumed); OCC: blocks per CU the registers and LDS
-// allow.  BTM x BTN: output tile (rows x columns).
-#ifndef MUON_NS_BF16
-#define MUON_NS_BF16 2
-#endif
-#ifndef MUON_BK_BF16
-#define MUON_BK_BF16 64
-#endif
-#ifndef MUON_BX_NWN
-#define MUON_BX_NWN 4
-#endif
-#ifndef MUON_BX_OCC
-#define MUON_BX_OCC 2
-#endif
-template <bool F32, int PH> struct Cfg;
-#ifndef MUON_G_NWN
-#define MUON_G_NWN 4
-#endif
-template <int PH> struct Cfg<false, PH> {        // bf16, Gram and square
+// Tile configuration per precision, phase and shape.  BTM x BTN: output
+// tile (rows x columns); NWM x NWN waves, each owning a (BTM/NWM) x
+// (BTN/NWN) block of 32x32 MFMA tiles; BK: K depth of one LDS stage; NS:
+// stages in the LDS ring (NS-1 in flight while one is consumed); OCC: the
+// launch bound's minimum waves per SIMD.
+//   128 x 128: 8 waves of 64 x 32, 64 KB of stages, two blocks (four waves
+//     per SIMD) per CU;
+//   256 x 256: 8 waves of 128 x 64 (accumulators in the AGPRs), 128 KB of
+//     stages, one block per CU.
+// Measured alternatives, slower on every workload here: 256 x 128 with four
+// waves of 128 x 64 (two blocks per CU, 32-deep stages, three of them, with
+// or without the next stage's barrier moved before the last slice); 128 x
+// 128 with four waves of 64 x 64; 32-deep stages with 3 or 4 in the ring.
+template <bool F32, int PH, int TC> struct Cfg;
+template <int PH> struct Cfg<false, PH, kTileM> {
   using E = uint16_t;
-  static constexpr int BTM = kTileGramBf16, BTN = kTileGramBf16, NWM = 2, NWN = MUON_G_NWN, BK = MUON_BK_BF16,
-                       NS = MUON_NS_BF16;
-  static constexpr int OCC = NS * BK <= 128 ? 2 : 1;    // ring of 2 x 32 KB or 4 x 16 KB: two blocks per CU
+  static constexpr int BTM = kTileEdgeM, BTN = kTileEdgeM, NWM = 2, NWN = 4, BK = 64, NS = 2, OCC = 2;
 };
-template <> struct Cfg<false, kBX> {             // bf16, B X
+template <int PH> struct Cfg<false, PH, kTileL> {
   using E = uint16_t;
-  static constexpr int BTM = kTileBxRowsBf16, BTN = kTileBxColsBf16, NWM = kTileBxRowsBf16 / 64, NWN = MUON_BX_NWN,
-                       BK = MUON_BK_BF16, NS = MUON_NS_BF16;
-  static constexpr int OCC = NWM * NWN > 8 ? 1 : NS * BK <= 128 ? MUON_BX_OCC : 1;
+  static constexpr int BTM = kTileEdgeL, BTN = kTileEdgeL, NWM = 2, NWN = 4, BK = 64, NS = 2, OCC = 1;
 };
-template <int PH> struct Cfg<true, PH> {         // float32, all phases
+template <int PH, int TC> struct Cfg<true, PH, TC> {
   using E = float;
   static constexpr int BTM = kTileF32, BTN = kTileF32, NWM = 2, NWN = 2, BK = 32, NS = 2, OCC = 2;
 };
@@ -91,8 +96,8 @@ template <int PH> struct Cfg<true, PH> {         // float32, all phases
 //     the eight of one parity in (r / 2) % 8); c ^ (r % 8) would put rows r
 //     and r + 8 in one slot (a 2-way conflict, measured with the LDS bank
 //     conflict counter);
-//   K-major tile of B X (row = k, 16 chunks of columns): chunk c of row k
-//     sits at position c ^ 4 (k % 4), which spreads the four rows a
+//   K-major tile of B X (row = k, 16 or 32 chunks of columns): chunk c of
+//     row k sits at position c ^ 4 (k % 4), which spreads the four rows a
 //     transposing read touches over distinct banks.
 template <int CPR>
 __device__ __forceinline__ int swz_kc(int r, int c) {
@@ -101,9 +106,6 @@ __device__ __forceinline__ int swz_kc(int r, int c) {
   else return c ^ ((r >> 2) & 3);   // 64-byte rows: four share a bank line
 }
 __device__ __forceinline__ int swz_km(int k, int c) { return c ^ ((k & 3) << 2); }
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 // Wait until at most N vector-memory operations of this wave are pending
 // (asm, so the compiler, which does not see the asm loads, keeps it).
@@ -125,6 +127,16 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Orders one wave's LDS writes before its other lanes read them back (the
+// epilogue's staging area is private to the wave): a release and an acquire
+// fence at wavefront scope around a wave barrier, so neither the compiler
+// nor the hardware lets a read move above the writes it depends on.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Transposing LDS read (gfx950).  Within each 16-lane group the 8-byte words
 // addressed by the lanes form a 16 x 4 matrix W[lane][e]; lane i receives
 // W[4e + i/4][i%4] for e = 0..3.  If lane 4e+q points at X[k+e][j+4q..+3],
@@ -135,10 +147,13 @@ __device__ __forceinline__ bf16x4_t lds_read_tr(const uint16_t* p) {
 }
 
 // Direct-to-LDS loads of one stage (global_load_lds_dwordx4): instruction i
-// of wave w fills the 1 KB at chunk (w*NI + i)*64 of the tile, lane L
-// writing chunk +L; aoff/boff hold each lane's byte offset of the global
-// chunk that belongs there (swizzle included).  No VGPR holds the data and
-// no LDS store instruction is issued.
+// of wave w (of NW) fills the 1 KB at chunk (i*NW + w)*64 of the tile, lane
+// L writing chunk +L; aoff/boff hold each lane's byte offset of the global
+// chunk that belongs there for i = 0 (swizzle included).  Instruction i
+// lands NW*64 chunks further, a whole number of rows whose swizzle repeats,
+// so its global chunk is the same offset from a base advanced by astep /
+// bstep bytes (one VGPR per operand instead of one per instruction).  No
+// VGPR holds the data and no LDS store instruction is issued.
 //
 // The instruction is written as inline asm (it has no register result): the
 // compiler treats the builtin form as an LDS store and puts a wait for every
@@ -151,15 +166,16 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
                : "memory", "m0");
 }
 
-template <int NA, int NB, typename E>
-__device__ __forceinline__ void issue_stage(const E* ga, const E* gb, const uint32_t (&aoff)[NA],
-                                            const uint32_t (&boff)[NB], uint32_t la, uint32_t lb, int wave,
-                                            bool with_b) {
+template <int NA, int NB, int NW, typename E>
+__device__ __forceinline__ void issue_stage(const E* ga, const E* gb, uint32_t aoff, uint32_t boff, size_t astep,
+                                            size_t bstep, uint32_t la, uint32_t lb, int wave, bool with_b) {
 #pragma unroll
-  for (int i = 0; i < NA; ++i) dma16(ga, aoff[i], la + (wave * NA + i) * 1024);
+  for (int i = 0; i < NA; ++i)
+    dma16(reinterpret_cast<const char*>(ga) + i * astep, aoff, la + (i * NW + wave) * 1024);
   if (with_b) {
 #pragma unroll
-    for (int i = 0; i < NB; ++i) dma16(gb, boff[i], lb + (wave * NB + i) * 1024);
+    for (int i = 0; i < NB; ++i)
+      dma16(reinterpret_cast<const char*>(gb) + i * bstep, boff, lb + (i * NW + wave) * 1024);
   }
 }
 
@@ -169,45 +185,78 @@ __device__ __forceinline__ uint32_t lds_addr(const E* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const E*)(p)));
 }
 
+// The lane's index in its wave, from the lane masks rather than the thread
+// index: the epilogue recomputes its lane-derived offsets from it instead of
+// keeping the K loop's copies alive through the loop (which spilled them).
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time (a
+// loop left rolled would index the accumulator array at run time and move
+// it to scratch memory).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Fragments of one 16-deep K slice (bf16) for the wave's blocks.
+template <bool KMAJOR_B, int NBM, int NBN, int WTM, int WTN, int BK, int BTN>
+__device__ __forceinline__ void load_frags(const uint16_t* la, const uint16_t* lb, int ks, int lane, int wm, int wn,
+                                           bf16x8_t (&fa)[NBM], bf16x8_t (&fb)[NBN]) {
+  const int kc = ks * 2 + (lane >> 5);           // 16-byte chunk of K (8 bf16)
+#pragma unroll
+  for (int i = 0; i < NBM; ++i) {
+    const int r = wm * WTM + i * 32 + (lane & 31);
+    fa[i] = *reinterpret_cast<const bf16x8_t*>(&la[r * BK + swz_kc<BK / 8>(r, kc) * 8]);
+  }
+#pragma unroll
+  for (int j = 0; j < NBN; ++j) {
+    if constexpr (!KMAJOR_B) {
+      const int r = wn * WTN + j * 32 + (lane & 31);
+      fb[j] = *reinterpret_cast<const bf16x8_t*>(&lb[r * BK + swz_kc<BK / 8>(r, kc) * 8]);
+    } else {
+      // lane group g = lane/16 covers columns 16*(g%2).. and k-half g/2;
+      // lane r of the group points at row k + r/4, columns 4*(r%4)..
+      const int g = lane >> 4, r = lane & 15;
+      const int krow = ks * 16 + 8 * (g >> 1) + (r >> 2);
+      const int col = wn * WTN + j * 32 + 16 * (g & 1) + 4 * (r & 3);
+      const int cofs = swz_km(krow, col >> 3) * 8 + (col & 7);   // rows krow and krow+4 swizzle alike
+      const bf16x4_t lo = lds_read_tr(&lb[krow * BTN + cofs]);
+      const bf16x4_t hi = lds_read_tr(&lb[(krow + 4) * BTN + cofs]);
+      fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+}
+
 // MFMAs of one BK-deep stage held in LDS (la: K-contiguous A tile, BTM rows
 // of BK; lb: the B tile, K-contiguous like A or K-major, BK rows of BTN).
 // The wave owns rows wm*WTM.. and columns wn*WTN.. of the block tile, as
-// NBM x NBN tiles of 32x32.
+// NBM x NBN tiles of 32x32.  bf16: the fragments of slice ks+1 are read
+// before the MFMAs of slice ks are issued, and a scheduling barrier keeps
+// the compiler from hoisting further slices, so the LDS reads overlap the
+// MFMAs while only two slices' fragments occupy registers.  (Interleaving
+// each read with an MFMA through scheduling-group barriers was measured:
+// no faster with 64 x 32 wave tiles, 20 % slower with 128 x 64.)
 template <bool F32, bool KMAJOR_B, int NBM, int NBN, int WTM, int WTN, int BK, int BTN, typename E>
 __device__ __forceinline__ void mma_stage(const E* la, const E* lb, f32x16_t (&acc)[NBM][NBN], int lane, int wm,
                                           int wn) {
   if constexpr (!F32) {
+    constexpr int NKS = BK / 16;
+    bf16x8_t fa[2][NBM], fb[2][NBN];
+    load_frags<KMAJOR_B, NBM, NBN, WTM, WTN, BK, BTN>(la, lb, 0, lane, wm, wn, fa[0], fb[0]);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8_t fa[NBM], fb[NBN];
-      const int kc = ks * 2 + (lane >> 5);           // 16-byte chunk of K (8 bf16)
-#pragma unroll
-      for (int i = 0; i < NBM; ++i) {
-        const int r = wm * WTM + i * 32 + (lane & 31);
-        fa[i] = *reinterpret_cast<const bf16x8_t*>(&la[r * BK + swz_kc<BK / 8>(r, kc) * 8]);
-      }
-#pragma unroll
-      for (int j = 0; j < NBN; ++j) {
-        if constexpr (!KMAJOR_B) {
-          const int r = wn * WTN + j * 32 + (lane & 31);
-          fb[j] = *reinterpret_cast<const bf16x8_t*>(&lb[r * BK + swz_kc<BK / 8>(r, kc) * 8]);
-        } else {
-          // lane group g = lane/16 covers columns 16*(g%2).. and k-half g/2;
-          // lane r of the group points at row k + r/4, columns 4*(r%4)..
-          const int g = lane >> 4, r = lane & 15;
-          const int krow = ks * 16 + 8 * (g >> 1) + (r >> 2);
-          const int col = wn * WTN + j * 32 + 16 * (g & 1) + 4 * (r & 3);
-          const int cofs = swz_km(krow, col >> 3) * 8 + (col & 7);   // rows krow and krow+4 swizzle alike
-          const bf16x4_t lo = lds_read_tr(&lb[krow * BTN + cofs]);
-          const bf16x4_t hi = lds_read_tr(&lb[(krow + 4) * BTN + cofs]);
-          fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-      }
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (ks + 1 < NKS)
+        load_frags<KMAJOR_B, NBM, NBN, WTM, WTN, BK, BTN>(la, lb, ks + 1, lane, wm, wn, fa[(ks + 1) & 1],
+                                                         fb[(ks + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < NBM; ++i)
 #pragma unroll
         for (int j = 0; j < NBN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   } else {
     // v_mfma_f32_32x32x2f32: lane half h holds k = h*16 + e at step e of the
@@ -247,74 +296,171 @@ __device__ __forceinline__ void mma_stage(const E* la, const E* lb, f32x16_t (&a
   }
 }
 
-// Accumulators of one 32-row strip (NBN tiles of 32x32) into the wave's LDS
-// staging area, in row-major order (pitch EPP floats).  v_mfma 32x32 output:
-// lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
-template <int NBN, int EPP>
-__device__ __forceinline__ void stage_strip(const f32x16_t (&row)[NBN], float* ep, int lane) {
+// An accumulator element, read in the epilogue.  The 128 accumulators of a
+// 128 x 64 wave tile live in the AGPRs; reading them through an asm operand
+// that must be an AGPR keeps them there until each is read (left to itself
+// the register allocator copies them all to VGPRs where the K loop ends,
+// which spills).  The compiler's hazard check does not cover these reads,
+// so the epilogue first waits out the MFMA latency.  Smaller wave tiles keep
+// their accumulators in VGPRs and read them plainly, as do the folds inside
+// the K loop (the compiler then inserts the waits it needs).
+template <bool AGPR>
+__device__ __forceinline__ float acc_get(const f32x16_t& v, int r) {
+  if constexpr (AGPR) {
+    float x;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(v[r]));
+    return x;
+  } else {
+    return v[r];
+  }
+}
+
+// MFMA 32x32 output layout: lane l, register r holds row 8*(r/4) + 4*(l/32)
+// + r%4, column l%32 of its 32x32 block.  The "linear term" folds below read
+// the operand in that layout: for r = 4q..4q+3 the four rows
+// 8q + 4(l/32) + 0..3 of column l%32.
+
+// B X: acc += a * X at the wave's output positions, during the K step that
+// holds the block's rows of X (the K-major second operand, BK rows of BTN).
+// bf16: X = the master hi (read from LDS with the transposing read) plus its
+// int8 correction (xq: the part's blocks, loaded from the correction array
+// one K step ahead).
+// PART (a compile-time constant, so no branch joins accumulator blocks) is
+// the wave's fold in this step: the block rows i whose 32 rows lie in the
+// PART-th K step of the wave's rows (BK / 32 of them per step).  Each quad
+// of rows is read, widened and added before the next, so few registers
+// beside the accumulators are live.
+template <int PART, bool F32, bool AGPR, int NBM, int NBN, int WTM, int WTN, int BK, int BTN, typename E>
+__device__ __forceinline__ void fold_master(const E* lbx, int wn, int lane, float a,
+                                            const u32x4_t (&xq)[BK / 32][NBN], f32x16_t (&acc)[NBM][NBN]) {
+  static_assert(WTM % BK == 0, "a wave's rows start on a K step");
+  static_for<0, NBM>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr ((i * 32) / BK == PART) {
+      constexpr int kr = (i * 32) % BK;              // the block's first row inside the stage
+#pragma unroll
+      for (int j = 0; j < NBN; ++j) {
+        const int c0 = wn * WTN + j * 32;
+        if constexpr (!F32) {
+          const int g = lane >> 4, r = lane & 15;
+          const int col = c0 + 16 * (g & 1) + 4 * (r & 3);
+          u32x2_t hw[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            // the four bf16 values as two words (element e in half e%2 of
+            // word e/2)
+            const int krow = kr + 8 * q + 4 * (g >> 1) + (r >> 2);
+            hw[q] = __builtin_bit_cast(u32x2_t,
+                                       lds_read_tr(&lbx[krow * BTN + swz_km(krow, col >> 3) * 8 + (col & 7)]));
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t qw = xq[i - PART * (BK / 32)][j][q];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t hb = (e & 1) ? (hw[q][e >> 1] & 0xFFFF0000u) : (hw[q][e >> 1] << 16);
+              const int qq = static_cast<int8_t>((qw >> (8 * e)) & 0xFFu);
+              const float x = __int_as_float(static_cast<int>(hb) + qq * 256);
+              acc[i][j][4 * q + e] = fmaf(a, x, acc[i][j][4 * q + e]);
+            }
+            // AGPR accumulators: a quad at a time through the VGPRs
+            if constexpr (AGPR) __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+          const int col = c0 + (lane & 31);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int krow = kr + 8 * q + 4 * (lane >> 5) + e;
+              const float x = lbx[krow * BTN + swz_km(krow, col >> 2) * 4 + (col & 3)];
+              acc[i][j][4 * q + e] = fmaf(a, x, acc[i][j][4 * q + e]);
+            }
+        }
+      }
+    }
+  });
+}
+
+// B = b A + c A A: acc += (b/c) A at the wave's output positions (the
+// epilogue scales by c).  A[i][j] = A[j][i]: row j of the second operand
+// (K-contiguous, BK columns of K per row), K index i, so during the K step
+// that holds k = the block's rows each lane reads four consecutive k of its
+// column's row.  PART as for fold_master.
+template <int PART, bool F32, bool AGPR, int NBM, int NBN, int WTM, int WTN, int BK, typename E>
+__device__ __forceinline__ void fold_atile(const E* lb, int wn, int lane, float bc, f32x16_t (&acc)[NBM][NBN]) {
+  constexpr int EPE = 16 / sizeof(E);        // elements per 16-byte chunk
+  static_assert(WTM % BK == 0, "a wave's rows start on a K step");
+  static_for<0, NBM>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr ((i * 32) / BK == PART) {
+      constexpr int kr = (i * 32) % BK;
+#pragma unroll
+      for (int j = 0; j < NBN; ++j) {
+        const int brow = wn * WTN + j * 32 + (lane & 31);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int k = kr + 8 * q + 4 * (lane >> 5);      // first of four consecutive k
+          const int pos = brow * BK + swz_kc<BK / EPE>(brow, k / EPE) * EPE + (k % EPE);
+          float x[4];
+          if constexpr (!F32) {
+            const u32x2_t w = *reinterpret_cast<const u32x2_t*>(&lb[pos]);
+            x[0] = __uint_as_float(w[0] << 16);
+            x[1] = __uint_as_float(w[0] & 0xFFFF0000u);
+            x[2] = __uint_as_float(w[1] << 16);
+            x[3] = __uint_as_float(w[1] & 0xFFFF0000u);
+          } else {
+            const f32x4_t w = *reinterpret_cast<const f32x4_t*>(&lb[pos]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = w[e];
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = fmaf(bc, x[e], acc[i][j][4 * q + e]);
+          if constexpr (AGPR) __builtin_amdgcn_sched_barrier(0);   // a quad at a time
+        }
+      }
+    }
+  });
+}
+
+// One 32-row strip (NBN tiles of 32x32) of the accumulators, times s, into
+// the wave's LDS staging area in row-major order (pitch EPP floats).
+template <bool AGPR, int NBN, int EPP>
+__device__ __forceinline__ void stage_strip(const f32x16_t (&row)[NBN], float s, float* ep, int lane) {
 #pragma unroll
   for (int j = 0; j < NBN; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      ep[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * EPP + j * 32 + (lane & 31)] = row[j][r];
+      ep[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * EPP + j * 32 + (lane & 31)] = s * acc_get<AGPR>(row[j], r);
 }
 
-// B X: the X master of the output tile's rows is part of the X operand (row
-// r of X is K step r), so while a K step whose rows overlap the tile sits in
-// LDS each lane copies out its own row segments: bf16 the hi half (the lo
-// half is not an operand and comes from HBM), float32 all 8 values.
-template <bool F32, int NBM, int RITER, int SEGS, int WTM, int BK, int BTN, typename E>
-__device__ __forceinline__ void capture_master(const E* lbx, int kt, int kt0, int wm, int col0, int lane,
-                                               u32x4_t (&pre0)[NBM][RITER], u32x4_t (&pre1)[NBM][RITER]) {
-  static_assert(BK % 32 == 0, "32-row strips must not straddle K steps");
+// The int8 correction of the next bf16 master for one 32x32 block, from the
+// accumulator registers (values already scaled): the same encoding as
+// master_encode8, element by element, 16 bytes per lane in register order.
+__device__ __forceinline__ u32x4_t encode_corr16(const float* v) {
+  u32x4_t out;
 #pragma unroll
-  for (int pi = 0; pi < NBM; ++pi) {
-    const int r0 = wm * WTM + pi * 32;      // first tile row of the strip
-    if (kt == kt0 + r0 / BK) {
+  for (int w = 0; w < 4; ++w) {
+    uint32_t word = 0;
 #pragma unroll
-      for (int q = 0; q < RITER; ++q) {
-        const int sg = lane + 64 * q;
-        const int k = r0 % BK + sg / SEGS, col = col0 + (sg % SEGS) * 8;
-        if constexpr (F32) {
-          pre0[pi][q] = *reinterpret_cast<const u32x4_t*>(&lbx[k * BTN + swz_km(k, col >> 2) * 4]);
-          pre1[pi][q] = *reinterpret_cast<const u32x4_t*>(&lbx[k * BTN + swz_km(k, (col >> 2) + 1) * 4]);
-        } else {
-          pre0[pi][q] = *reinterpret_cast<const u32x4_t*>(&lbx[k * BTN + swz_km(k, col >> 3) * 8]);
-        }
-      }
+    for (int e = 0; e < 4; e += 2) {
+      const float a0 = v[4 * w + e], a1 = v[4 * w + e + 1];
+      const uint32_t hp = cvt2_bf16(a0, a1);
+      const int d0 = __float_as_int(a0) - static_cast<int>(hp << 16);
+      const int d1 = __float_as_int(a1) - static_cast<int>(hp & 0xFFFF0000u);
+      const uint32_t q0 = static_cast<uint32_t>(min(max((d0 + 128) >> 8, -127), 127)) & 0xFFu;
+      const uint32_t q1 = static_cast<uint32_t>(min(max((d1 + 128) >> 8, -127), 127)) & 0xFFu;
+      word |= (q0 << (8 * e)) | (q1 << (8 * (e + 1)));
     }
+    out[w] = word;
   }
+  return out;
 }
 
-// B = b A + c A A: the A tile (ti, tj) the epilogue combines is part of the
-// A operand of the same block (rows ti, K columns tj), so each lane copies
-// its row segments out of LDS during the K step that holds its columns,
-// and the epilogue reads no A from memory.  A wave's WTN columns lie in one
-// K step (WTN divides BK).
-template <bool F32, int NBM, int RITER, int SEGS, int WTM, int WTN, int BK, typename E>
-__device__ __forceinline__ void capture_atile(const E* la, int kt, int kt_cap, int wm, int wn, int lane,
-                                              u32x4_t (&pre0)[NBM][RITER], u32x4_t (&pre1)[NBM][RITER]) {
-  static_assert(BK % WTN == 0, "a wave's columns must lie in one K step");
-  constexpr int EPE = 16 / sizeof(E);
-  if (kt != kt_cap) return;
-#pragma unroll
-  for (int pi = 0; pi < NBM; ++pi)
-#pragma unroll
-    for (int q = 0; q < RITER; ++q) {
-      const int sg = lane + 64 * q;
-      const int r = wm * WTM + pi * 32 + sg / SEGS;            // tile row = A-operand row
-      const int k = (wn * WTN + (sg % SEGS) * 8) % BK;         // column inside the K step
-      pre0[pi][q] = *reinterpret_cast<const u32x4_t*>(&la[r * BK + swz_kc<BK / EPE>(r, k / EPE) * EPE]);
-      if constexpr (F32)
-        pre1[pi][q] = *reinterpret_cast<const u32x4_t*>(&la[r * BK + swz_kc<BK / EPE>(r, k / EPE + 1) * EPE]);
-    }
-}
-
-template <bool F32, int PH>
-__global__ __launch_bounds__((64 * Cfg<F32, PH>::NWM * Cfg<F32, PH>::NWN), (Cfg<F32, PH>::OCC))
-void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restrict__ tasks,
-                    GemmParams p) {
-  using C = Cfg<F32, PH>;
+template <bool F32, int PH, int TC, bool LAST>
+__global__ __launch_bounds__((64 * Cfg<F32, PH, TC>::NWM * Cfg<F32, PH, TC>::NWN), (Cfg<F32, PH, TC>::OCC))
+void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restrict__ tasks, GemmParams p) {
+  using C = Cfg<F32, PH, TC>;
   using E = typename C::E;
   constexpr int BTM = C::BTM, BTN = C::BTN, BK = C::BK, NWM = C::NWM, NWN = C::NWN;
   constexpr int NT = 64 * NWM * NWN;               // threads per block
@@ -330,10 +476,16 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   constexpr int NIB = T_B / EPE / NT;              // ... and per B tile
   constexpr int STAGE = T_A + T_B;                 // A tile then B tile
   constexpr int EPP = WTN + 8;                     // epilogue LDS pitch (floats)
+  constexpr int NFOLD = WTM / BK;                  // K steps holding a wave's rows (B X, square)
+  constexpr bool FOLD = PH == kBX || PH == kSquare;
+  constexpr bool AGPR = NBM * NBN >= 8;            // accumulators in the AGPRs (128 x 128 wave tiles)
   static_assert(NIA * NT * EPE == T_A && NIB * NT * EPE == T_B, "tile/thread mismatch");
-  static_assert((CPR == 8 || CPR == 4) && CPRX == 16, "swizzles assume 8- or 4-chunk K rows and 16-chunk K-major rows");
+  static_assert((CPR == 8 || CPR == 4) && (CPRX == 16 || CPRX == 32),
+                "swizzles assume 8- or 4-chunk K rows and 16- or 32-chunk K-major rows");
+  static_assert(BK % 32 == 0 && WTM % BK == 0 && NFOLD >= 1 && NFOLD <= 4, "a wave's rows fill whole K steps");
   static_assert(NWM * NWN * 32 * EPP * 4 <= NS * STAGE * static_cast<int>(sizeof(E)),
                 "epilogue staging must fit in the operand LDS");
+  static_assert(!LAST || PH == kBX, "only B X has a last-iteration variant");
 
   __shared__ __attribute__((aligned(16))) E smem[NS * STAGE];
   __shared__ float red[4];
@@ -341,12 +493,26 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   const GemmTask t = tasks[blockIdx.x];
   if (t.unit < 0) return;   // padding of the XCD-interleaved task order
   const UnitDev& u = units[t.unit];
-  // first iteration: B X applies the unit's 1/||U|| that the Gram phase
-  // folded (every Gram block folds the same bits; one stores them); the
-  // load is issued here so its latency hides behind the K loop
-  const float first_scale = PH == kBX && p.first ? gld<float>(u.norm) : 1.f;
   const int mp = u.mp, np = u.np;
   const int ti = t.ti, tj = t.tj;
+
+  // The epilogue's scale, known before the K loop (so no control flow
+  // joins while the accumulators are live): the first Gram folds the
+  // per-tile partial sums into 1/(||U|| + eps) (every block in the same
+  // order; tile (0, 0) stores it for the first B X), which that B X loads;
+  // the square scales by c.
+  float scale = 1.f;
+  if constexpr (PH == kGram) {
+    if (p.first) {
+      const float iv = unit_inv_norm(u.partials, u.k1_ntiles, p.eps, red);
+      scale = iv * iv;
+      if (ti == 0 && tj == 0 && threadIdx.x == 0) gst(u.norm, iv);
+    }
+  } else if constexpr (PH == kSquare) {
+    scale = p.c;
+  } else {
+    scale = p.first ? gld<float>(u.norm) : 1.f;
+  }
 
   // operand A: rows [ti*BTM, +BTM) over K; operand B: rows [tj*BTN, +BTN)
   // over K (Gram, square) or K rows x columns [tj*BTN, +BTN) (B X)
@@ -371,26 +537,52 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / NWN, wn = wave % NWN;
+  const int row_base = ti * BTM + wm * WTM;
+  const int col_base = tj * BTN + wn * WTN;
 
-  // each lane's global element offset (within a stage) for its DMA chunks
-  uint32_t aoff[NIA], boff[NIB];
+  // B X, bf16: the int8 corrections of the X master at the wave's output
+  // blocks (correction array: 32 x 32 blocks of 1 KB, row of blocks after
+  // row of blocks, 16 bytes per lane in accumulator register order).  Only
+  // one fold part's blocks are held at a time (XPP block rows): each part's
+  // are requested a K step ahead, after the previous part's fold.
+  constexpr int XPP = BK / 32;
+  u32x4_t xq[XPP][NBN];
+  auto load_xq = [&](auto partc) {
+    constexpr int P = decltype(partc)::value;
+    if constexpr (PH == kBX && !F32 && P < WTM / BK) {
+      const int8_t* xl = static_cast<const int8_t*>(u.xl);
+      const size_t nbc = static_cast<size_t>(np / 32);
 #pragma unroll
-  for (int i = 0; i < NIA; ++i) {
-    const int c = (wave * NIA + i) * 64 + lane;      // chunk position in the A tile
+      for (int i = 0; i < XPP; ++i)
+#pragma unroll
+        for (int j = 0; j < NBN; ++j) {
+          const size_t bi = (row_base + (P * XPP + i) * 32) / 32, bj = (col_base + j * 32) / 32;
+          xq[i][j] = gld<u32x4_t>(xl + (bi * nbc + bj) * 1024 + lane * 16);
+        }
+    }
+  };
+
+  // each lane's global byte offset (within a stage) of its first DMA chunk
+  // per operand, and the advance of the global base per instruction (NW*64
+  // chunks: whole rows, a multiple of the swizzle period of 16 K-contiguous
+  // rows or 4 K-major rows)
+  constexpr int NW = NWM * NWN;
+  static_assert((NW * 64 / CPR) % 16 == 0 && (NW * 64 / CPRX) % 4 == 0 && 64 % CPRX == 0,
+                "DMA instructions advance by whole swizzle periods");
+  uint32_t aoff, boff;
+  {
+    const int c = wave * 64 + lane;                  // chunk position in the A tile
     const int ar = c / CPR;
-    aoff[i] = static_cast<uint32_t>((ar * lda_g + swz_kc<CPR>(ar, c % CPR) * EPE) * sizeof(E));
-  }
-#pragma unroll
-  for (int i = 0; i < NIB; ++i) {
-    const int c = (wave * NIB + i) * 64 + lane;      // chunk position in the B tile
+    aoff = static_cast<uint32_t>((ar * lda_g + swz_kc<CPR>(ar, c % CPR) * EPE) * sizeof(E));
     if constexpr (KMAJOR_B) {
       const int k = c / CPRX;
-      boff[i] = static_cast<uint32_t>((k * ldb_g + swz_km(k, c % CPRX) * EPE) * sizeof(E));
+      boff = static_cast<uint32_t>((k * ldb_g + swz_km(k, c % CPRX) * EPE) * sizeof(E));
     } else {
-      const int br = c / CPR;
-      boff[i] = static_cast<uint32_t>((br * ldb_g + swz_kc<CPR>(br, c % CPR) * EPE) * sizeof(E));
+      boff = static_cast<uint32_t>((ar * ldb_g + swz_kc<CPR>(ar, c % CPR) * EPE) * sizeof(E));
     }
   }
+  const size_t astep = static_cast<size_t>(NW * 64 / CPR) * lda_g * sizeof(E);
+  const size_t bstep = static_cast<size_t>(KMAJOR_B ? NW * 64 / CPRX : NW * 64 / CPR) * ldb_g * sizeof(E);
   const uint32_t ring0 = lds_addr(smem);
   // diagonal tiles of the Gram and the square read the same rows as both
   // operands: the stage is loaded once and both fragment reads use it
@@ -408,31 +600,22 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // row segments of the epilogue: per 32-row strip, SEGS segments of 8 per
-  // row, RITER per lane
+  const int KT = K / BK;
+  const float bc = p.b / p.c;                        // square: b A folded as (b/c) A, scaled by c
+
+  // The epilogue's 32-row strips: SEGS segments of 8 per row, RITER per lane
+  // (row pass) and CITER per lane (column pass: mirror tiles, weight rows of
+  // a tall matrix).
   constexpr int SEGS = WTN / 8;
   constexpr int RITER = 32 * SEGS / 64;
-  constexpr bool CAPTURE = KMAJOR_B || PH == kSquare;   // epilogue operand taken from LDS
-  constexpr int NPRE = CAPTURE ? NBM : 1;
-  u32x4_t pre0[NPRE][RITER], pre1[NPRE][RITER];     // master: hi (bf16) / first..last 4 (float32)
-  u32x2_t preq[NPRE][RITER];                          // master: int8 corrections (bf16)
-  const int kt0 = ti * BTM / BK;                     // K step of the tile's first row
-
-  const int KT = K / BK;
-
-  // B X, bf16: the epilogue's HBM operands are the lo half of the master
-  // (the hi half is captured from LDS) and, in the last iteration, the
-  // weight segments this lane updates (bf16 weights with aligned rows; the
-  // segments are rows of W for a wide unit, columns of the tile for a tall
-  // one, where X column j is weight row j).  They are requested once per
-  // tile, behind the last K step's MFMAs.
-  const int row_base = ti * BTM + wm * WTM;
-  const int col_base = tj * BTN + wn * WTN;
-  static_assert(!KMAJOR_B || RITER == WTN * 4 / 64, "row and column passes give a lane equally many segments");
-  u32x4_t wpre[NPRE][RITER];
-  const bool wfast = KMAJOR_B && !F32 && p.last && !u.param_f32 && u.vec_param;
-  auto wseg = [&](int pi, int q, int& wi, int& wj) {
-    const int sg = lane + 64 * q;
+  constexpr int CITER = WTN * 4 / 64;
+  static_assert(RITER == CITER, "row and column passes give a lane equally many segments");
+  // Last B X, bf16 weights with aligned rows: each strip's weight segments
+  // (rows of W for a wide unit; columns of the tile, i.e. rows of W, for a
+  // tall one) are requested one strip ahead, the first as the K loop ends.
+  const bool wfast = LAST && !F32 && !u.param_f32 && u.vec_param;
+  auto wseg = [&](int pi, int q, int ln, int& wi, int& wj) {
+    const int sg = ln + 64 * q;
     if (u.side == kLeft) {
       wi = row_base + pi * 32 + sg / SEGS;
       wj = col_base + (sg % SEGS) * 8;
@@ -441,27 +624,14 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
       wj = row_base + pi * 32 + (sg / WTN) * 8;
     }
   };
-  auto epilogue_loads = [&]() {
-    if constexpr (KMAJOR_B && !F32) {
+  u32x4_t wbuf[2][RITER];
+  auto load_w = [&](int pi, int ln, u32x4_t (&dst)[RITER]) {
 #pragma unroll
-      for (int pi = 0; pi < NBM; ++pi)
-#pragma unroll
-        for (int q = 0; q < RITER; ++q) {
-          const int sg = lane + 64 * q;
-          const size_t off = static_cast<size_t>(row_base + pi * 32 + sg / SEGS) * np + col_base + (sg % SEGS) * 8;
-          preq[pi][q] = gld<u32x2_t>(static_cast<const int8_t*>(u.xl) + off);
-        }
-      if (wfast) {
-#pragma unroll
-        for (int pi = 0; pi < NBM; ++pi)
-#pragma unroll
-          for (int q = 0; q < RITER; ++q) {
-            int wi, wj;
-            wseg(pi, q, wi, wj);
-            if (wi < u.rows && wj + 8 <= u.cols)
-              wpre[pi][q] = gld<u32x4_t>(static_cast<const uint16_t*>(u.param) + static_cast<size_t>(wi) * u.ld_param + wj);
-          }
-      }
+    for (int q = 0; q < RITER; ++q) {
+      int wi, wj;
+      wseg(pi, q, ln, wi, wj);
+      if (wi < u.rows && wj + 8 <= u.cols)
+        dst[q] = gld<u32x4_t>(static_cast<const uint16_t*>(u.param) + static_cast<size_t>(wi) * u.ld_param + wj);
     }
   };
 
@@ -473,66 +643,83 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   // With more than two stages, indices past the end are clamped to the last
   // stage (its copy lands in a buffer nobody reads again), so every step has
   // the same NS-2 newer stages in flight and a fixed wait count.  With two
-  // stages every step waits for everything, so the last step issues no copy
-  // and sends the epilogue's HBM loads out in its place: they overlap the
-  // final MFMAs and the epilogue does not wait for a dead copy.
+  // stages every step waits for everything, so the last step issues no copy.
+  //
+  // The linear term is folded during the NFOLD steps that hold the wave's
+  // own rows (B X: rows of X; square: K indices of A).
   constexpr uint32_t STAGE_B = STAGE * sizeof(E), TILE_B = T_A * sizeof(E);
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) {
     const int sc = min(s, KT - 1);
-    issue_stage<NIA, NIB, E>(pa + sc * a_step, pb + sc * b_step, aoff, boff, ring0 + s * STAGE_B,
+    issue_stage<NIA, NIB, NW, E>(pa + sc * a_step, pb + sc * b_step, aoff, boff, astep, bstep, ring0 + s * STAGE_B,
                              ring0 + s * STAGE_B + TILE_B, wave, !diag);
   }
-  auto kstep = [&](int kt, bool tail) {
+  // One K step; FP >= 0: the step holding part FP of the wave's own rows,
+  // which also folds the linear term.  `hook` runs once the step's copy is
+  // issued.
+  auto kstep = [&](int kt, auto fpc, auto&& hook) {
+    constexpr int FP = decltype(fpc)::value;
     if (diag) wait_vmcnt<(NS - 2) * NIA>();   // newer stages in flight: NS-2 of one operand each
     else wait_vmcnt<(NS - 2) * (NIA + NIB)>();
     ring_barrier();
-    if (!tail) {
+    if (NS > 2 || kt + 1 < KT) {   // with two stages the last step issues no copy
       const int nx = min(kt + NS - 1, KT - 1);
       const uint32_t ls = ring0 + ((kt + NS - 1) % NS) * STAGE_B;
-      issue_stage<NIA, NIB, E>(pa + nx * a_step, pb + nx * b_step, aoff, boff, ls, ls + TILE_B, wave, !diag);
+      issue_stage<NIA, NIB, NW, E>(pa + nx * a_step, pb + nx * b_step, aoff, boff, astep, bstep, ls, ls + TILE_B,
+                                   wave, !diag);
     }
+    hook();
     const E* cs = smem + (kt % NS) * STAGE;
-    if constexpr (KMAJOR_B)
-      capture_master<F32, NPRE, RITER, SEGS, WTM, BK, BTN>(cs + T_A, kt, kt0, wm, wn * WTN, lane, pre0, pre1);
-    else if constexpr (PH == kSquare)
-      capture_atile<F32, NPRE, RITER, SEGS, WTM, WTN, BK>(cs, kt, (tj * BTN + wn * WTN) / BK, wm, wn, lane, pre0, pre1);
-    if (tail) epilogue_loads();
-    mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, BTN>(cs, diag ? cs : cs + T_A, acc, lane, wm, wn);
+    const E* csb = diag ? cs : cs + T_A;
+    if constexpr (FP >= 0) {
+      if constexpr (PH == kBX) {
+        fold_master<FP, F32, AGPR, NBM, NBN, WTM, WTN, BK, BTN>(csb, wn, lane, p.a, xq, acc);
+        load_xq(std::integral_constant<int, FP + 1>{});
+      } else {
+        fold_atile<FP, F32, AGPR, NBM, NBN, WTM, WTN, BK>(csb, wn, lane, bc, acc);
+      }
+    }
+    mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, BTN>(cs, csb, acc, lane, wm, wn);
   };
+  using NoFold = std::integral_constant<int, -1>;
+  auto nohook = [] {};
+  if constexpr (FOLD) {
+    // the wave's rows are K steps f0 .. f0 + NFOLD - 1 (K index = tile row);
+    // all waves pass the same steps and barriers, each with its own split
+    const int f0 = (ti * BTM + wm * WTM) / BK;
+    using Part0 = std::integral_constant<int, 0>;
+    if (f0 == 0) load_xq(Part0{});
+    for (int kt = 0; kt + 1 < f0; ++kt) kstep(kt, NoFold{}, nohook);
+    if (f0 > 0) kstep(f0 - 1, NoFold{}, [&] { load_xq(Part0{}); });
+    static_for<0, NFOLD>([&](auto pc) { kstep(f0 + decltype(pc)::value, pc, nohook); });
+    for (int kt = f0 + NFOLD; kt < KT; ++kt) kstep(kt, NoFold{}, nohook);
+  } else {
+    for (int kt = 0; kt < KT; ++kt) kstep(kt, NoFold{}, nohook);
+  }
+  const int el = lane_id();   // the epilogue's lane index
+  if (wfast) load_w(0, el, wbuf[0]);
   if constexpr (NS == 2) {
-    for (int kt = 0; kt < KT - 1; ++kt) kstep(kt, false);
-    kstep(KT - 1, true);
     ring_barrier();    // no copy in flight; every wave is done reading the ring
   } else {
-    for (int kt = 0; kt < KT; ++kt) kstep(kt, false);
-    epilogue_loads();
     wait_vmcnt<0>();   // the clamped copies of the last stage
     __syncthreads();   // the epilogue reuses the ring as staging
   }
 
   // ---------------------------------------------------------------- epilogue
-  // Each wave stages one 32-row strip of its accumulators in its own LDS
-  // area (so the strips need no block barrier: one wave's LDS accesses take
-  // effect in order), then writes row segments (natural layout) and, where
-  // needed, column segments (mirror tiles of A and B; weight rows of a tall
-  // matrix in the last iteration) as 16-byte vector accesses.
-  float scale = 1.f;
-  if constexpr (PH == kGram) {
-    if (p.first) {
-      const float iv = unit_inv_norm(u.partials, u.k1_ntiles, p.eps, red);
-      scale = iv * iv;
-      if (ti == 0 && tj == 0 && threadIdx.x == 0) gst(u.norm, iv);   // for the first B X phase
-    }
-  } else if constexpr (PH == kBX) {
-    scale = first_scale;
+  // The epilogue reads AGPR accumulators with inline asm, which the
+  // compiler's hazard check does not see: wait out the MFMA result latency
+  // first (24 wait states; the scheduling barriers keep every MFMA above the
+  // wait and every read below it).
+  if constexpr (AGPR) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  const bool last = PH == kBX && p.last;
-  const bool mirror = PH == kBX ? (last && u.side == kRight) : (ti != tj);
+  // Gram and square: the tiles above the diagonal are also stored transposed
+  const bool mirror = PH == kBX ? (LAST && u.side == kRight) : (ti != tj);
   const float decay = p.lr * p.weight_decay;
   const float step = p.lr * u.lr_scale;
   float* ep = reinterpret_cast<float*>(smem) + wave * (32 * EPP);
-  constexpr int CITER = WTN * 4 / 64;                // column segments per lane
   // the output pointers, kept in scalar registers for the whole epilogue;
   // so are the weight fields of the last iteration's update (wu: a copy of
   // the descriptor whose fields the update reads are pinned)
@@ -540,7 +727,7 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   void* const out_xh = PH == kBX ? sreg_ptr(u.xh[p.x_in ^ 1]) : nullptr;
   int8_t* const out_xl = PH == kBX ? sreg_ptr(static_cast<int8_t*>(u.xl)) : nullptr;
   UnitDev wu;
-  if (last) {
+  if constexpr (LAST) {
     wu.param = sreg_ptr(u.param);
     wu.ld_param = sreg_i64(u.ld_param);
     wu.param_f32 = sreg_i32(u.param_f32);
@@ -552,16 +739,47 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
     wu.cols = sreg_i32(u.cols);
   }
 
-  // acc and the master registers are only ever indexed with constants (a
-  // runtime index would move the whole array to scratch memory), so the
-  // strip loop is unrolled.
+  // B X, bf16, not last: the corrections of the next master go straight from
+  // the accumulators to the correction array, one 16-byte store per block
+  if constexpr (PH == kBX && !F32 && !LAST) {
+    const size_t nbc = static_cast<size_t>(np / 32);
 #pragma unroll
-  for (int pi = 0; pi < NBM; ++pi) {
-    stage_strip<NBN, EPP>(acc[pi], ep, lane);
+    for (int i = 0; i < NBM; ++i)
+#pragma unroll
+      for (int j = 0; j < NBN; ++j) {
+        // one block's accumulators at a time: keep the compiler from reading
+        // all of them out of the AGPRs at once
+        __builtin_amdgcn_sched_barrier(0);
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = scale * acc_get<AGPR>(acc[i][j], r);
+        const size_t bi = (row_base + i * 32) / 32, bj = (col_base + j * 32) / 32;
+        gst(out_xl + (bi * nbc + bj) * 1024 + el * 16, encode_corr16(v));
+      }
+  }
+
+  // Each wave stages one 32-row strip of its scaled accumulators in its own
+  // LDS area (so the strips need no block barrier), then writes row segments
+  // (natural layout) and, where needed, column segments (mirror tiles of A
+  // and B; weight rows of a tall matrix in the last iteration) as 16-byte
+  // vector accesses.  acc and wbuf are only ever indexed with constants (a
+  // runtime index would move the arrays to scratch memory), so the strip
+  // loop is unrolled at compile time.
+  static_for<0, NBM>([&](auto pic) {
+    constexpr int pi = decltype(pic)::value;
+    // strip by strip: a later strip's accumulators stay in the AGPRs until
+    // its turn (reading them all out at once would exceed the VGPRs)
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (pi + 1 < NBM) {
+      if (wfast) load_w(pi + 1, el, wbuf[(pi + 1) & 1]);
+    }
+    if constexpr (pi > 0) wave_sync();      // the previous strip's reads are done
+    stage_strip<AGPR, NBN, EPP>(acc[pi], scale, ep, el);
+    wave_sync();
 
 #pragma unroll
     for (int q = 0; q < RITER; ++q) {
-      const int s = lane + 64 * q;
+      const int s = el + 64 * q;
       const int row = s / SEGS, cseg = s % SEGS;
       float v[8];
       const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(&ep[row * EPP + cseg * 8]);
@@ -570,60 +788,15 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
       for (int e = 0; e < 4; ++e) { v[e] = v0[e]; v[4 + e] = v1[e]; }
       const int gr = row_base + pi * 32 + row;
       const int gc = col_base + cseg * 8;
-      if constexpr (PH == kGram) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] *= scale;
+      if constexpr (PH == kGram || PH == kSquare) {
         st8<F32>(out_ab, static_cast<size_t>(gr) * mp + gc, v);
-      } else if constexpr (PH == kSquare) {
-        float av[8];                                      // A at this segment, captured from LDS
-        if constexpr (F32) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            av[e] = __uint_as_float(pre0[pi][q][e]);
-            av[4 + e] = __uint_as_float(pre1[pi][q][e]);
-          }
-        } else {
-          unpack8_bf16(pre0[pi][q], av);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = fmaf(p.b, av[e], p.c * v[e]);
-        st8<F32>(out_ab, static_cast<size_t>(gr) * mp + gc, v);
-        if (mirror) {   // the mirror pass stores B^T from the staged values
-          *reinterpret_cast<f32x4_t*>(&ep[row * EPP + cseg * 8]) = f32x4_t{v[0], v[1], v[2], v[3]};
-          *reinterpret_cast<f32x4_t*>(&ep[row * EPP + cseg * 8 + 4]) = f32x4_t{v[4], v[5], v[6], v[7]};
-        }
-      } else {
-        const size_t off = static_cast<size_t>(gr) * np + gc;
-        float xm[8];
-        if constexpr (F32) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            xm[e] = __uint_as_float(pre0[pi][q][e]);
-            xm[4 + e] = __uint_as_float(pre1[pi][q][e]);
-          }
-        } else {
-          master_decode8(pre0[pi][q], preq[pi][q], xm);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = scale * fmaf(p.a, xm[e], v[e]);
-        if (!last) {
-          if constexpr (F32) {
-            st8<true>(out_xh, off, v);
-          } else {
-            u32x4_t hq;
-            u32x2_t lq;
-            master_encode8(v, hq, lq);
-            gst(static_cast<uint16_t*>(out_xh) + off, hq);
-            gst(out_xl + off, lq);
-          }
-        } else if (u.side == kLeft) {
-          if (gr < wu.rows) {
-            if (wfast && gc + 8 <= wu.cols) update_w8_loaded(wu, gr, gc, v, decay, step, wpre[pi][q]);
-            else update_w8(wu, gr, gc, v, decay, step);
-          }
-        } else {
-          *reinterpret_cast<f32x4_t*>(&ep[row * EPP + cseg * 8]) = f32x4_t{v[0], v[1], v[2], v[3]};
-          *reinterpret_cast<f32x4_t*>(&ep[row * EPP + cseg * 8 + 4]) = f32x4_t{v[4], v[5], v[6], v[7]};
+      } else if constexpr (!LAST) {
+        if constexpr (F32) st8<true>(out_xh, static_cast<size_t>(gr) * np + gc, v);
+        else gst(static_cast<uint16_t*>(out_xh) + static_cast<size_t>(gr) * np + gc, pack8_bf16(v));
+      } else if (u.side == kLeft) {
+        if (gr < wu.rows) {
+          if (wfast && gc + 8 <= wu.cols) update_w8_loaded(wu, gr, gc, v, decay, step, wbuf[pi & 1][q]);
+          else update_w8(wu, gr, gc, v, decay, step);
         }
       }
     }
@@ -631,60 +804,55 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
     if (mirror) {
 #pragma unroll
       for (int q = 0; q < CITER; ++q) {
-        const int s = lane + 64 * q;
+        const int s = el + 64 * q;
         const int col = s % WTN, rseg = s / WTN;
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = ep[(rseg * 8 + e) * EPP + col];
         const int gc = col_base + col;                 // mirror row
         const int gr = row_base + pi * 32 + rseg * 8;  // mirror column start
-        if constexpr (PH == kGram) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] *= scale;
-          st8<F32>(out_ab, static_cast<size_t>(gc) * mp + gr, v);
-        } else if constexpr (PH == kSquare) {
-          st8<F32>(out_ab, static_cast<size_t>(gc) * mp + gr, v);   // B is symmetric off the diagonal tiles
-        } else {
+        if constexpr (PH == kGram || PH == kSquare) {
+          st8<F32>(out_ab, static_cast<size_t>(gc) * mp + gr, v);   // A and B are symmetric
+        } else if constexpr (LAST) {
           // tall matrix: O[i][j] = X[j][i], so X column gc is weight row gc
           if (gc < wu.rows) {
-            if constexpr (!F32) {
-              if (wfast && gr + 8 <= wu.cols) {
-                update_w8_loaded(wu, gc, gr, v, decay, step, wpre[pi][q]);
-                continue;
-              }
-            }
-            update_w8(wu, gc, gr, v, decay, step);
+            if (!F32 && wfast && gr + 8 <= wu.cols) update_w8_loaded(wu, gc, gr, v, decay, step, wbuf[pi & 1][q]);
+            else update_w8(wu, gc, gr, v, decay, step);
           }
         }
       }
     }
-  }
+  });
 }
 
-template <bool F32, int PH>
+template <bool F32, int PH, int TC, bool LAST>
 void launch_one(const UnitDev* units, const GemmTask* tasks, int n, const GemmParams& p, hipStream_t s) {
-  constexpr int nt = 64 * Cfg<F32, PH>::NWM * Cfg<F32, PH>::NWN;
-  ns_gemm_kernel<F32, PH><<<n, nt, 0, s>>>(units, tasks, p);
+  constexpr int nt = 64 * Cfg<F32, PH, TC>::NWM * Cfg<F32, PH, TC>::NWN;
+  ns_gemm_kernel<F32, PH, TC, LAST><<<n, nt, 0, s>>>(units, tasks, p);
 }
 
-template <bool F32>
+template <bool F32, int TC>
 hipError_t launch_phase(int phase, const UnitDev* units, const GemmTask* tasks, int n,
                         const GemmParams& p, hipStream_t s) {
   switch (phase) {
-    case kGram: launch_one<F32, kGram>(units, tasks, n, p, s); break;
-    case kSquare: launch_one<F32, kSquare>(units, tasks, n, p, s); break;
-    default: launch_one<F32, kBX>(units, tasks, n, p, s); break;
+    case kGram: launch_one<F32, kGram, TC, false>(units, tasks, n, p, s); break;
+    case kSquare: launch_one<F32, kSquare, TC, false>(units, tasks, n, p, s); break;
+    default:
+      if (p.last) launch_one<F32, kBX, TC, true>(units, tasks, n, p, s);
+      else launch_one<F32, kBX, TC, false>(units, tasks, n, p, s);
+      break;
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm(int phase, bool f32, const UnitDev* units, const GemmTask* tasks,
+hipError_t launch_gemm(int phase, bool f32, int tile, const UnitDev* units, const GemmTask* tasks,
                        int n_tasks, const GemmParams& p, hipStream_t s) {
   if (n_tasks <= 0) return hipSuccess;
-  return f32 ? launch_phase<true>(phase, units, tasks, n_tasks, p, s)
-             : launch_phase<false>(phase, units, tasks, n_tasks, p, s);
+  if (f32) return launch_phase<true, kTileM>(phase, units, tasks, n_tasks, p, s);
+  return tile == kTileL ? launch_phase<false, kTileL>(phase, units, tasks, n_tasks, p, s)
+                        : launch_phase<false, kTileM>(phase, units, tasks, n_tasks, p, s);
 }
 
 }  // namespace muon

@@ -47,7 +47,8 @@ def kernel_source_hash():
 
 
 def kernel_kind(name):
-    m = re.search(r"ns_gemm_kernel<(\w+), (\d)>", name) or re.search(r"ns_gemm_kernelILb(\d)ELi(\d)E", name)
+    # ns_gemm_kernel<f32, phase, tile shape, last iteration>
+    m = re.search(r"ns_gemm_kernel<(\w+), (\d)[,>]", name) or re.search(r"ns_gemm_kernelILb(\d)ELi(\d)E", name)
     if m:
         f32 = m.group(1) in ("true", "1")
         return ["gram", "square", "bx"][int(m.group(2))] + ("/f32" if f32 else "")

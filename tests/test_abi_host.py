@@ -110,6 +110,11 @@ def test_validation_errors():
     assert ws_status(ok, hp)[0] == "MUON_ERR_BAD_ARG"
     hp = mm.default_hparams(momentum_form=5)
     assert ws_status(ok, hp)[0] == "MUON_ERR_BAD_ARG"
+    # the square phase computes c (A A + (b/c) A): c = 0 is refused unless no
+    # iteration runs
+    assert ws_status(ok, mm.default_hparams(ns_c=0.0))[0] == "MUON_ERR_BAD_ARG"
+    assert "ns_c" in lib.muon_last_error().decode()
+    assert ws_status(ok, mm.default_hparams(ns_c=0.0, ns_steps=0))[0] == "MUON_OK"
     # the message names the offending tensor
     t = fakes([(64, 128)])[0]; t.ld_param = 3
     ws_status([t])
@@ -180,9 +185,12 @@ def test_plan_gpt2_small():
     # 24 attention matrices each
     g0, g1 = plan["groups"]
     assert (g0["lane"], g1["lane"]) == (0, 1) and g0["units"] == g1["units"] == 36
+    # m = 768 is below the 256-tile threshold: 128 x 128 tiles everywhere
+    assert all(u["tile"] == 128 and u["mp"] == 768 for u in units)
     for k, total in (("gram", 72 * 21), ("square", 72 * 21), ("bx", 48 * 36 + 24 * 144),
                      ("momentum", 12 * (4 * 144 + 2 * 576))):
         assert g0[f"{k}_tiles"] + g1[f"{k}_tiles"] == total
+    assert g0["tiles_by_edge"] == {"128": [g0["gram_tiles"], g0["square_tiles"], g0["bx_tiles"]]}
     assert g0["bx_tiles"] == g1["bx_tiles"]
     # the XCD interleave pads the shorter per-XCD sequences with empty blocks
     # (the Gram's tiles differ 4x in cost, so its sequences differ in length)
@@ -198,13 +206,27 @@ def test_plan_gpt2_small():
 def test_plan_gpt2_xl_and_padding():
     plan = mm.plan_describe(_workload_fakes("gpt2xl", layers=2), mm.default_hparams())
     units = plan["units"]
-    assert all(u["m"] == 1600 and u["mp"] == 1664 for u in units)
+    assert all(u["m"] == 1600 and u["mp"] == 1664 and u["tile"] == 128 for u in units)
     assert {u["np"] for u in units} == {1664, 6400}
     assert sum(u["side"] == "right" for u in units) == 2
     # the full 48-layer set has far more B X tiles per phase than two lanes
     # help with: one group on one stream
     full = mm.plan_describe(_workload_fakes("gpt2xl"), mm.default_hparams())
     assert [g["lane"] for g in full["groups"]] == [0] and full["groups"][0]["units"] == 288
+
+
+def test_plan_large_units_take_256_tiles():
+    # m >= 2048 takes 256 x 256 tiles (padding to 256); below, 128 x 128; one
+    # group holding both runs two launches per phase, the 256 one first
+    ts = fakes([(4096, 4096), (2100, 3000), (1024, 4096)])
+    plan = mm.plan_describe(ts, mm.default_hparams())
+    u = plan["units"]
+    assert [(x["tile"], x["mp"], x["np"]) for x in u] == [(256, 4096, 4096), (256, 2304, 3072), (128, 1024, 4096)]
+    g = plan["groups"][0]
+    assert g["tiles_by_edge"]["256"] == [16 * 17 // 2 + 9 * 10 // 2] * 2 + [16 * 16 + 9 * 12]
+    assert g["tiles_by_edge"]["128"] == [8 * 9 // 2] * 2 + [8 * 32]
+    assert plan["launch_order"][1:7] == ["gram/bf16x256", "gram/bf16", "square/bf16x256", "square/bf16",
+                                          "bx/bf16x256", "bx/bf16"]
 
 
 def test_plan_split_rows_and_fp32():

@@ -227,6 +227,21 @@ def test_low_rank_plus_noise_mid_sizes(rank):
     assert w["O"] < 2e-2
 
 
+def test_large_ragged_256_tiles():
+    # a short side of 2048 or more takes the 256 x 256 tiles: ragged padding
+    # (2100 -> 2304, 2300 -> 2304), Gram and square tiles above the diagonal
+    # stored twice, a tall matrix (the last B X writes weight rows from tile
+    # columns) and an exact multiple of the tile
+    shapes = [(2100, 2300), (2300, 2100), (2048, 2048)]
+    say("case: large ragged bf16 (256 x 256 tiles)")
+    wl = adhoc("large", shapes, "bf16")
+    c = Case(wl, wl.tensors)
+    hp = mm.default_hparams()
+    assert c.run(hp) == 0
+    w = check(c, hp, label="large/256")
+    assert w["O"] < 2e-2
+
+
 def test_zero_gradient_and_nonfinite_flag():
     say("case: zero gradient / non-finite flag")
     wl = adhoc("zero", [(64, 96)], "bf16", mom0=0.0)

@@ -15,8 +15,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
-BX = "void muon::ns_gemm_kernel<false, 2>(muon::UnitDev const*, muon::GemmTask const*, muon::GemmParams)"
-GRAM = "void muon::ns_gemm_kernel<false, 0>(muon::UnitDev const*, muon::GemmTask const*, muon::GemmParams)"
+BX = "void muon::ns_gemm_kernel<false, 2, 1, false>(muon::UnitDev const*, muon::GemmTask const*, muon::GemmParams)"
+GRAM = "void muon::ns_gemm_kernel<false, 0, 0, false>(muon::UnitDev const*, muon::GemmTask const*, muon::GemmParams)"
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -32,8 +32,9 @@ def _write(path, fields, rows):
 def test_kernel_kind_names():
     assert P.kernel_kind(BX) == "bx"
     assert P.kernel_kind(GRAM) == "gram"
-    assert P.kernel_kind("void muon::ns_gemm_kernel<true, 1>(...)") == "square/f32"
-    assert P.kernel_kind("_ZN4muon14ns_gemm_kernelILb1ELi2EEEvPKNS_7UnitDevE") == "bx/f32"
+    assert P.kernel_kind("void muon::ns_gemm_kernel<true, 1, 0, false>(...)") == "square/f32"
+    assert P.kernel_kind("void muon::ns_gemm_kernel<false, 2, 1, true>(...)") == "bx"
+    assert P.kernel_kind("_ZN4muon14ns_gemm_kernelILb1ELi2ELi0ELb0EEEvPKNS_7UnitDevE") == "bx/f32"
     assert P.kernel_kind("void muon::momentum_kernel<false>(...)") == "momentum"
     assert P.kernel_kind(COPY) == "copy"
     assert P.kernel_kind("void muon::update_kernel<false>(...)") == "update"
