@@ -71,6 +71,9 @@ typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;       // LDS
 // or without the next stage's barrier moved before the last slice); 128 x
 // 128 with four waves of 64 x 64; 32-deep stages with 3 or 4 in the ring.
 template <bool F32, int PH, int TC> struct Cfg;
+#ifndef MUON_PINGPONG
+#define MUON_PINGPONG 1
+#endif
 template <int PH> struct Cfg<false, PH, kTileM> {
   using E = uint16_t;
   static constexpr int BTM = kTileEdgeM, BTN = kTileEdgeM, NWM = 2, NWN = 4, BK = 64, NS = 2, OCC = 2;
@@ -478,6 +481,14 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   constexpr int EPP = WTN + 8;                     // epilogue LDS pitch (floats)
   constexpr int NFOLD = WTM / BK;                  // K steps holding a wave's rows (B X, square)
   constexpr bool FOLD = PH == kBX || PH == kSquare;
+  // ping-pong K loop: the Gram phase of 256 x 256 tiles (one block per CU,
+  // two groups of four waves, one wave of each on every SIMD).  Measured on
+  // 4096 x 4096: Gram 101 -> 91 us per launch; the square and B X phases,
+  // whose memory phases carry the fold (and for B X twice the LDS read
+  // instructions: transposing 8-byte reads), ran 3 % faster and 25 % slower
+  // and keep the plain loop.
+  constexpr bool PING = !F32 && TC == kTileL && PH == kGram && MUON_PINGPONG;
+  static_assert(!PING || (NS == 2 && NWM == 2 && NWN == 4 && BK % 32 == 0 && !FOLD), "ping-pong layout");
   constexpr bool AGPR = NBM * NBN >= 8;            // accumulators in the AGPRs (128 x 128 wave tiles)
   static_assert(NIA * NT * EPE == T_A && NIB * NT * EPE == T_B, "tile/thread mismatch");
   static_assert((CPR == 8 || CPR == 4) && (CPRX == 16 || CPRX == 32),
@@ -648,6 +659,76 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   // The linear term is folded during the NFOLD steps that hold the wave's
   // own rows (B X: rows of X; square: K indices of A).
   constexpr uint32_t STAGE_B = STAGE * sizeof(E), TILE_B = T_A * sizeof(E);
+  using NoFold = std::integral_constant<int, -1>;
+  auto nohook = [] {};
+  if constexpr (PING) {
+    // Ping-pong (256 x 256 tiles, one block per CU).  The two waves sharing
+    // a SIMD belong to different groups (wave w runs on SIMD w % 4; group =
+    // the wave's row half wm), and the groups alternate, one phase apart,
+    // between MFMA phases (half a stage: NKS/2 slices of MFMAs from
+    // registers) and memory phases (the fragment reads of the next half
+    // stage, copy issue and waits, the fold), with a block barrier between
+    // phases: at every moment one group feeds the matrix pipe while the
+    // other prepares, instead of both idling at each stage's barrier.
+    //   phase 4k   (memory): issue stage k+1 (its buffer's last reader, the
+    //              other group, finished before this phase's barrier);
+    //              read slices of half 0 of stage k;
+    //   phase 4k+1 (MFMA)  : half 0;
+    //   phase 4k+2 (memory): wait for this wave's part of stage k+1; read
+    //              half 1;
+    //   phase 4k+3 (MFMA)  : half 1.
+    // Group 1 starts one barrier later and skips the last one, so both pass
+    // the same number of barriers.  Every memory phase ends with its reads
+    // complete (lgkmcnt(0) in the barrier), so a stage is visible to all
+    // after the barrier that follows both groups' waits for it, and free
+    // once both groups' last reads of it precede a barrier.
+    constexpr int HALF = BK / 32;   // slices per half stage
+    bf16x8_t fa[HALF][NBM], fb[HALF][NBN];
+    auto read_half = [&](const E* cs, const E* csb, int h) {
+#pragma unroll
+      for (int q = 0; q < HALF; ++q)
+        load_frags<KMAJOR_B, NBM, NBN, WTM, WTN, BK, BTN>(reinterpret_cast<const uint16_t*>(cs),
+                                                         reinterpret_cast<const uint16_t*>(csb), h * HALF + q, lane,
+                                                         wm, wn, fa[q], fb[q]);
+    };
+    auto mfma_half = [&]() {
+#pragma unroll
+      for (int q = 0; q < HALF; ++q)
+#pragma unroll
+        for (int i = 0; i < NBM; ++i)
+#pragma unroll
+          for (int j = 0; j < NBN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q][i], fb[q][j], acc[i][j], 0, 0, 0);
+    };
+    auto phase_barrier = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      ring_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto pstage = [&](int k) {
+      const E* cs = smem + (k & 1) * STAGE;
+      const E* csb = diag ? cs : cs + T_A;
+      if (k + 1 < KT) {
+        const uint32_t ls = ring0 + ((k + 1) & 1) * STAGE_B;
+        issue_stage<NIA, NIB, NW, E>(pa + (k + 1) * a_step, pb + (k + 1) * b_step, aoff, boff, astep, bstep, ls,
+                                     ls + TILE_B, wave, !diag);
+      }
+      read_half(cs, csb, 0);
+      phase_barrier();
+      mfma_half();
+      phase_barrier();
+      wait_vmcnt<0>();
+      read_half(cs, csb, 1);
+      phase_barrier();
+      mfma_half();
+      if (wm == 0 || k + 1 < KT) phase_barrier();
+    };
+    issue_stage<NIA, NIB, NW, E>(pa, pb, aoff, boff, astep, bstep, ring0, ring0 + TILE_B, wave, !diag);
+    wait_vmcnt<0>();
+    ring_barrier();
+    if (wm == 1) phase_barrier();
+    for (int kt = 0; kt < KT; ++kt) pstage(kt);
+  } else {
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) {
     const int sc = min(s, KT - 1);
@@ -681,8 +762,6 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
     }
     mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, BTN>(cs, csb, acc, lane, wm, wn);
   };
-  using NoFold = std::integral_constant<int, -1>;
-  auto nohook = [] {};
   if constexpr (FOLD) {
     // the wave's rows are K steps f0 .. f0 + NFOLD - 1 (K index = tile row);
     // all waves pass the same steps and barriers, each with its own split
@@ -696,9 +775,14 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   } else {
     for (int kt = 0; kt < KT; ++kt) kstep(kt, NoFold{}, nohook);
   }
+  }
   const int el = lane_id();   // the epilogue's lane index
   if (wfast) load_w(0, el, wbuf[0]);
-  if constexpr (NS == 2) {
+  if constexpr (PING) {
+    // nothing in flight, every read of the ring done: group 0 passed the
+    // last barrier after group 1's last reads, and group 1 (in its last
+    // MFMA phase) reads no LDS while group 0 stages its epilogue
+  } else if constexpr (NS == 2) {
     ring_barrier();    // no copy in flight; every wave is done reading the ring
   } else {
     wait_vmcnt<0>();   // the clamped copies of the last stage
