@@ -42,7 +42,7 @@ struct UnitPlan {
   int64_t row0 = 0;
   int rows = 0, cols = 0, side = 0, m = 0, n = 0, mp = 0, np = 0;
   bool f32 = false;
-  int tile = kTileM;     // bf16 GEMM tile shape (TileCfg)
+  int tile[3] = {kTileM, kTileM, kTileM};   // GEMM tile shape (TileCfg) per phase
   float lr_scale = 1.f;
   size_t off_xh0 = 0, off_xh1 = 0, off_xl = 0, off_a = 0, off_b = 0;
   int k1_tile0 = 0, k1_ntiles = 0, k1_tr = 0, k1_tc = 0;
@@ -64,21 +64,28 @@ struct Group {
 const char* kPhaseNames[3] = {"gram", "square", "bx"};
 const int kLaunchOrder[kTileCfgs] = {kTileL, kTileM};   // per phase: the longer 256-tile launch first
 
-// bf16 tile edge of a unit.  The 256 x 256 tiles (one block of eight
-// 128 x 64-wave tiles per CU) halve the operand bytes per flop and read a
-// third of the LDS bytes per flop of the 128 x 128 ones; measured, they are
-// faster once m reaches 2048 (4096 x 4096: 580 steps/s against 535) and no
-// faster below (GPT-2-XL's 1600-row units: even; GPT-2-small's 768: 20 %
-// slower Gram phases, whose few tiles then fill the chip in fewer, emptier
-// waves).  MUON_TILE_POLICY 1 / 2 force 128 / 256 (measurement builds).
+// bf16 tile edge of a unit's GEMM phase.  The 256 x 256 tiles (one block
+// of 128 x 128-wave tiles per CU) halve the operand bytes per flop and read
+// a third of the LDS bytes per flop of the 128 x 128 ones; measured, they are
+// faster in every phase once m reaches 2048 (4096 x 4096: 580 steps/s
+// against 535).  Below that the Gram keeps 128 x 128 tiles (GPT-2-small's
+// 768-row units: 256-tile Gram launches take 84 instead of 59 us, its few
+// tiles filling the chip in fewer, emptier waves), while the square and
+// B X take 256 x 256 from m = 768 on when that pads neither side further
+// (GPT-2-small 477-479 against 466-470 steps/s: each launch alone is a
+// little slower, but the two lanes fill each other's last waves).
+// MUON_TILE_POLICY 1 / 2 force 128 / 256 (measurement builds).
 #ifndef MUON_TILE_POLICY
 #define MUON_TILE_POLICY 0
 #endif
-constexpr int kTileLMinRows = 2048;
-int choose_tile(int m) {
+constexpr int kTileLMinRows = 2048;      // every phase at 256 from here
+constexpr int kTileLMidRows = 768;       // square and B X at 256 from here
+int choose_tile(int m, int n, int phase) {
   if (MUON_TILE_POLICY == 1) return kTileM;
   if (MUON_TILE_POLICY == 2) return kTileL;
-  return m >= kTileLMinRows ? kTileL : kTileM;
+  if (m >= kTileLMinRows) return kTileL;
+  const bool no_extra_pad = round_up(m, 256) == round_up(m, 128) && round_up(n, 256) == round_up(n, 128);
+  return phase != kGram && m >= kTileLMidRows && no_extra_pad ? kTileL : kTileM;
 }
 
 // suffix of a GEMM launch's phase name per tile edge
@@ -334,9 +341,13 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
       u.m = int(std::min<int64_t>(h, t.cols));
       u.n = int(std::max<int64_t>(h, t.cols));
       u.f32 = t.dtype == MUON_F32 || u.m < kMinBf16NsSide;   // NS precision of the unit
-      u.tile = u.f32 ? kTileM : choose_tile(u.m);
-      u.mp = int(round_up(u.m, tile_edge(u.f32, u.tile)));
-      u.np = int(round_up(u.n, tile_edge(u.f32, u.tile)));
+      int edge = 0;
+      for (int ph = 0; ph < 3; ++ph) {
+        u.tile[ph] = u.f32 ? kTileM : choose_tile(u.m, u.n, ph);
+        edge = std::max(edge, tile_edge(u.f32, u.tile[ph]));
+      }
+      u.mp = int(round_up(u.m, edge));
+      u.np = int(round_up(u.n, edge));
       u.lr_scale = shape_scale(h, t.cols, hp->scale_mode) * t.lr_mult;
       const int ewr = u.side == kLeft ? kEwRows : kEwTile, ewc = u.side == kLeft ? kEwCols : kEwTile;
       u.k1_tr = int((h + ewr - 1) / ewr);
@@ -365,7 +376,7 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
     int64_t bx_tiles = 0;
     for (int k : ids) {
       const UnitPlan& u = plan.units[k];
-      const int te = tile_edge(u.f32, u.tile);
+      const int te = tile_edge(u.f32, u.tile[kBX]);
       bx_tiles += int64_t(u.mp / te) * (u.np / te);
     }
     const int lanes = !single_lane && ids.size() >= size_t(kLaneMinUnits) && bx_tiles <= kLaneMaxBxTiles ? kLanes : 1;
@@ -397,17 +408,17 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
       const UnitPlan& u = plan.units[g.units[gi]];
       for (int r = 0; r < u.k1_tr; ++r)
         for (int c = 0; c < u.k1_tc; ++c) g.ew.push_back({int(gi), r, c, r * u.k1_tc + c});
-      const int te = tile_edge(u.f32, u.tile);   // output tile edge of every phase
-      for (int a = 0; a < u.mp / te; ++a)
-        for (int b = a; b < u.mp / te; ++b) {
-          g.gemm[kGram][u.tile].push_back({int(gi), a, b, 0});
-          g.gemm[kSquare][u.tile].push_back({int(gi), a, b, 0});
-        }
+      for (int ph : {kGram, kSquare}) {
+        const int te = tile_edge(u.f32, u.tile[ph]);
+        for (int a = 0; a < u.mp / te; ++a)
+          for (int b = a; b < u.mp / te; ++b) g.gemm[ph][u.tile[ph]].push_back({int(gi), a, b, 0});
+      }
       // B X tiles column by column: the tiles that run together then share
       // one column strip of X and all of B (a unit's B is the smaller
       // operand), so each strip of X comes from HBM about once.
+      const int te = tile_edge(u.f32, u.tile[kBX]);
       for (int b = 0; b < u.np / te; ++b)
-        for (int a = 0; a < u.mp / te; ++a) g.gemm[kBX][u.tile].push_back({int(gi), a, b, 0});
+        for (int a = 0; a < u.mp / te; ++a) g.gemm[kBX][u.tile[kBX]].push_back({int(gi), a, b, 0});
     }
     for (int ph = 0; ph < 3; ++ph)
       for (int tc = 0; tc < kTileCfgs; ++tc) g.gemm[ph][tc] = xcd_order(g.gemm[ph][tc], plan.units, g, ph);
@@ -702,11 +713,12 @@ std::string plan_json(const Plan& plan, const muon_hparams_t& hp) {
     const UnitPlan& u = plan.units[i];
     std::snprintf(buf, sizeof(buf),
                   "%s{\"tensor\":%d,\"block\":%d,\"row0\":%lld,\"rows\":%d,\"cols\":%d,\"side\":\"%s\","
-                  "\"m\":%d,\"n\":%d,\"mp\":%d,\"np\":%d,\"ns\":\"%s\",\"tile\":%d,\"lr_scale\":%.9g,"
+                  "\"m\":%d,\"n\":%d,\"mp\":%d,\"np\":%d,\"ns\":\"%s\",\"tiles\":[%d,%d,%d],\"lr_scale\":%.9g,"
                   "\"k1_tiles\":%d}",
                   i ? "," : "", u.tensor, u.block, (long long)u.row0, u.rows, u.cols,
                   u.side == kLeft ? "left" : "right", u.m, u.n, u.mp, u.np, u.f32 ? "f32" : "bf16",
-                  tile_edge(u.f32, u.tile), double(u.lr_scale), u.k1_ntiles);
+                  tile_edge(u.f32, u.tile[kGram]), tile_edge(u.f32, u.tile[kSquare]),
+                  tile_edge(u.f32, u.tile[kBX]), double(u.lr_scale), u.k1_ntiles);
     s += buf;
   }
   s += "],\"groups\":[";

@@ -185,12 +185,14 @@ def test_plan_gpt2_small():
     # 24 attention matrices each
     g0, g1 = plan["groups"]
     assert (g0["lane"], g1["lane"]) == (0, 1) and g0["units"] == g1["units"] == 36
-    # m = 768 is below the 256-tile threshold: 128 x 128 tiles everywhere
-    assert all(u["tile"] == 128 and u["mp"] == 768 for u in units)
-    for k, total in (("gram", 72 * 21), ("square", 72 * 21), ("bx", 48 * 36 + 24 * 144),
+    # m = 768: 128 x 128 Gram tiles, 256 x 256 square and B X tiles (768 and
+    # 3072 are multiples of 256, so no extra padding)
+    assert all(u["tiles"] == [128, 256, 256] and u["mp"] == 768 for u in units)
+    for k, total in (("gram", 72 * 21), ("square", 72 * 6), ("bx", 48 * 9 + 24 * 36),
                      ("momentum", 12 * (4 * 144 + 2 * 576))):
         assert g0[f"{k}_tiles"] + g1[f"{k}_tiles"] == total
-    assert g0["tiles_by_edge"] == {"128": [g0["gram_tiles"], g0["square_tiles"], g0["bx_tiles"]]}
+    assert g0["tiles_by_edge"] == {"256": [0, g0["square_tiles"], g0["bx_tiles"]],
+                                   "128": [g0["gram_tiles"], 0, 0]}
     assert g0["bx_tiles"] == g1["bx_tiles"]
     # the XCD interleave pads the shorter per-XCD sequences with empty blocks
     # (the Gram's tiles differ 4x in cost, so its sequences differ in length)
@@ -199,14 +201,15 @@ def test_plan_gpt2_small():
         for k in ("gram", "square"):
             assert g[f"{k}_tiles"] <= g[f"{k}_blocks"] <= g[f"{k}_tiles"] * 1.4 + 8
     order = plan["launch_order"]
-    assert order[0] == "momentum/bf16" and order[-1] == "bx/bf16" and len(order) == 32
-    assert order[1:4] == ["gram/bf16", "square/bf16", "bx/bf16"]
+    assert order[0] == "momentum/bf16" and order[-1] == "bx/bf16x256" and len(order) == 32
+    assert order[1:4] == ["gram/bf16", "square/bf16x256", "bx/bf16x256"]
 
 
 def test_plan_gpt2_xl_and_padding():
     plan = mm.plan_describe(_workload_fakes("gpt2xl", layers=2), mm.default_hparams())
     units = plan["units"]
-    assert all(u["m"] == 1600 and u["mp"] == 1664 and u["tile"] == 128 for u in units)
+    # 1600 would pad to 1792 at 256: 128 x 128 tiles in every phase
+    assert all(u["m"] == 1600 and u["mp"] == 1664 and u["tiles"] == [128] * 3 for u in units)
     assert {u["np"] for u in units} == {1664, 6400}
     assert sum(u["side"] == "right" for u in units) == 2
     # the full 48-layer set has far more B X tiles per phase than two lanes
@@ -216,15 +219,20 @@ def test_plan_gpt2_xl_and_padding():
 
 
 def test_plan_large_units_take_256_tiles():
-    # m >= 2048 takes 256 x 256 tiles (padding to 256); below, 128 x 128; one
+    # m >= 2048 takes 256 x 256 tiles in every phase (padding to 256); from
+    # m = 768 the square and B X do where 256 pads no further than 128 (not
+    # for 1000 x 1100: 1152 against 1280), the Gram keeps 128 x 128; one
     # group holding both runs two launches per phase, the 256 one first
-    ts = fakes([(4096, 4096), (2100, 3000), (1024, 4096)])
+    ts = fakes([(4096, 4096), (2100, 3000), (1024, 4096), (1000, 1100), (640, 2048)])
     plan = mm.plan_describe(ts, mm.default_hparams())
     u = plan["units"]
-    assert [(x["tile"], x["mp"], x["np"]) for x in u] == [(256, 4096, 4096), (256, 2304, 3072), (128, 1024, 4096)]
+    assert [(x["tiles"], x["mp"], x["np"]) for x in u] == [
+        ([256] * 3, 4096, 4096), ([256] * 3, 2304, 3072), ([128, 256, 256], 1024, 4096),
+        ([128] * 3, 1024, 1152), ([128] * 3, 640, 2048)]
     g = plan["groups"][0]
-    assert g["tiles_by_edge"]["256"] == [16 * 17 // 2 + 9 * 10 // 2] * 2 + [16 * 16 + 9 * 12]
-    assert g["tiles_by_edge"]["128"] == [8 * 9 // 2] * 2 + [8 * 32]
+    assert g["tiles_by_edge"]["256"] == [16 * 17 // 2 + 9 * 10 // 2, 16 * 17 // 2 + 9 * 10 // 2 + 4 * 5 // 2,
+                                         16 * 16 + 9 * 12 + 4 * 16]
+    assert g["tiles_by_edge"]["128"] == [8 * 9 // 2 * 2 + 5 * 6 // 2, 8 * 9 // 2 + 5 * 6 // 2, 8 * 9 + 5 * 16]
     assert plan["launch_order"][1:7] == ["gram/bf16x256", "gram/bf16", "square/bf16x256", "square/bf16",
                                           "bx/bf16x256", "bx/bf16"]
 
