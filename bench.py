@@ -170,6 +170,52 @@ def gpu_clock_mhz(run_steps, seconds=2.0):
     return None
 
 
+def blas_context(units, ns_ms, dev, reps=20):
+    """The vendor BLAS (torch.bmm in bf16, hipBLASLt on this stack) timed on
+    the same products as the Newton-Schulz phases, one batched call per
+    shape: the full X X^T, A A and B X of every bf16 unit.  Context for the
+    GEMM kernels' rates only; the step never calls it.  ns_ms: the library's
+    milliseconds per iteration of each phase (all lanes, one launch at a
+    time)."""
+    import torch
+    from collections import Counter
+    shapes = Counter((m, n) for m, n, es, _ in units if es == 2)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) / reps
+
+    ms = {"gram": 0.0, "square": 0.0, "bx": 0.0}
+    fl = {"gram": 0.0, "square": 0.0, "bx": 0.0}
+    for (m, n), b in sorted(shapes.items()):
+        X = torch.randn(b, m, n, device=dev, generator=gen).to(torch.bfloat16)
+        Xt = X.transpose(1, 2).contiguous()
+        A = torch.randn(b, m, m, device=dev, generator=gen).to(torch.bfloat16)
+        ms["gram"] += timed(lambda: torch.bmm(X, Xt))
+        ms["square"] += timed(lambda: torch.bmm(A, A))
+        ms["bx"] += timed(lambda: torch.bmm(A, X))
+        fl["gram"] += 2.0 * b * m * m * n
+        fl["square"] += 2.0 * b * m ** 3
+        fl["bx"] += 2.0 * b * m * m * n
+        del X, Xt, A
+    out = {"library": f"torch.bmm bf16 (torch {torch.__version__})", "shapes": len(shapes)}
+    for k in ms:
+        out[k] = {"vendor_ms": round(ms[k], 4), "vendor_tflops": round(fl[k] / (ms[k] * 1e-3) / 1e12, 1),
+                  "vendor_frac_bf16_peak": round(fl[k] / (ms[k] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                  "library_ms": round(ns_ms[k], 4)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +228,8 @@ def main():
                     help="weight set to step (the headline metric is quoted on gpt2s)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 3 device-to-device copies of BYTES each (HBM counter calibration)")
+    ap.add_argument("--blas-context", action="store_true",
+                    help="also time the vendor BLAS on the same Newton-Schulz products (context)")
     args = ap.parse_args()
     if args.copy_calibration:
         import torch
@@ -423,6 +471,8 @@ def main():
     if args.workload != "gpt2s":
         out["metric"] = f"Muon steps/sec, {args.workload} weight set (not the headline workload)"
         out["dtype"] = "f32" if args.workload == "tiny" else "bf16"
+    if args.blas_context and any(es == 2 for _, _, es, _ in units):
+        out["blas_context"] = blas_context(units, {k: totals[k] / hp.ns_steps for k in ("gram", "square", "bx")}, dev)
     if not args.no_cpu_baseline and args.workload == "gpt2s":
         out["cpu_baseline"] = cpu_baseline(wl, hp, args.cpu_budget)
     print(json.dumps(out), flush=True)

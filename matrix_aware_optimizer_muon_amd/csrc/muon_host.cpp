@@ -64,28 +64,33 @@ struct Group {
 const char* kPhaseNames[3] = {"gram", "square", "bx"};
 const int kLaunchOrder[kTileCfgs] = {kTileL, kTileM};   // per phase: the longer 256-tile launch first
 
-// bf16 tile edge of a unit's GEMM phase.  The 256 x 256 tiles (one block
-// of 128 x 128-wave tiles per CU) halve the operand bytes per flop and read
-// a third of the LDS bytes per flop of the 128 x 128 ones; measured, they are
-// faster in every phase once m reaches 2048 (4096 x 4096: 580 steps/s
-// against 535).  Below that the Gram keeps 128 x 128 tiles (GPT-2-small's
-// 768-row units: 256-tile Gram launches take 84 instead of 59 us, its few
-// tiles filling the chip in fewer, emptier waves), while the square and
-// B X take 256 x 256 from m = 768 on when that pads neither side further
-// (GPT-2-small 477-479 against 466-470 steps/s: each launch alone is a
-// little slower, but the two lanes fill each other's last waves).
+// bf16 tile shape of a unit's GEMM phase.  The 256 x 256 tiles (one block
+// of 128 x 64-wave tiles per CU) halve the operand bytes per flop and read
+// a third of the LDS bytes per flop of the 128 x 128 ones.  Units are padded
+// to 128 only: a phase of 256-tiles covers the unit's largest multiple of
+// 256 with them and the strips beyond with 128-tiles (unit_tiles), in a
+// second launch.  Measured (steps/s against 128-tiles everywhere):
+//   B X     256 from m = 768: GPT-2-small (768) 474-476 against 466-470,
+//           GPT-2-XL (1600) B X 6.1 against 6.4 ms per phase;
+//   Gram    256 from m = 1536: GPT-2-XL Gram 2.9 against 3.1 ms per phase;
+//           GPT-2-small's 256-tile Gram launches take 84 instead of 59 us
+//           (few tiles, filling the chip in fewer, emptier waves);
+//   square  256 where m is a multiple of 256 (GPT-2-small with it: 477-479)
+//           or from m = 2048; GPT-2-XL's remainder strip makes its square
+//           slower (1.86 against 1.66 ms per phase).
+// 4096 x 4096: 256-tiles in every phase, 580 against 535 steps/s.
 // MUON_TILE_POLICY 1 / 2 force 128 / 256 (measurement builds).
 #ifndef MUON_TILE_POLICY
 #define MUON_TILE_POLICY 0
 #endif
-constexpr int kTileLMinRows = 2048;      // every phase at 256 from here
-constexpr int kTileLMidRows = 768;       // square and B X at 256 from here
-int choose_tile(int m, int n, int phase) {
+int choose_tile(int m, int phase) {
   if (MUON_TILE_POLICY == 1) return kTileM;
   if (MUON_TILE_POLICY == 2) return kTileL;
-  if (m >= kTileLMinRows) return kTileL;
-  const bool no_extra_pad = round_up(m, 256) == round_up(m, 128) && round_up(n, 256) == round_up(n, 128);
-  return phase != kGram && m >= kTileLMidRows && no_extra_pad ? kTileL : kTileM;
+  bool large = false;
+  if (phase == kGram) large = m >= 1536;
+  else if (phase == kSquare) large = m >= 2048 || (m >= 768 && m % 256 == 0);
+  else large = m >= 768;
+  return large ? kTileL : kTileM;
 }
 
 // suffix of a GEMM launch's phase name per tile edge
@@ -192,7 +197,7 @@ muon_status_t validate(const muon_tensor_t* ts, int32_t n, const muon_precond_t*
       return fail(MUON_ERR_ALIGNMENT, who + "pointers must be aligned to their element size");
     const int64_t h = t.split_rows ? t.split_rows : t.rows;
     const int64_t m = std::min<int64_t>(h, t.cols), nn = std::max<int64_t>(h, t.cols);
-    const int64_t TE = t.dtype == MUON_F32 ? kTileF32 : kTileEdgeL;
+    const int64_t TE = t.dtype == MUON_F32 ? kTileF32 : kTileEdgeM;   // units are padded to 128
     if (!adam && round_up(m, TE) * round_up(nn, TE) > (int64_t(1) << 31))
       return fail(MUON_ERR_UNSUPPORTED, who + "matrix too large for one orthogonalisation unit");
     auto add = [&](const void* p, int64_t ld, size_t esz, const char* what) {
@@ -222,6 +227,44 @@ constexpr int kXcds = 8;   // MI355X: 8 accelerator complex dies, one L2 each
 constexpr int kLanes = MUON_LANES;       // lanes (streams) a large precision group is split into
 constexpr int kLaneMinUnits = 4 * kLanes;    // matrices of one precision needed for that split
 constexpr int64_t kLaneMaxBxTiles = 16384;   // ... and at most this many B X tiles per phase
+
+// The output tiles of one unit's GEMM phase, appended to the lists of their
+// shape (unit index gi within its group).  The Gram and the square compute
+// the upper tiles (i <= j) of the mp x mp product, B X every tile of mp x np.
+// A phase of 128-tiles (or float32 tiles) tiles the whole padded unit; a
+// phase of 256-tiles covers [0, 256 floor(mp / 256)) x [0, 256 floor(np /
+// 256)) with them and the remaining strips (at most 128 wide, as mp and np
+// are multiples of 128) with 128 x 128 tiles: for the square products the
+// upper tiles of the last column strip, for B X the last column strip and
+// then the last row strip.  B X tiles go column by column: the tiles that
+// run together then share one column strip of X and all of B (a unit's B is
+// the smaller operand), so each strip of X comes from HBM about once.
+void unit_tiles(const UnitPlan& u, int ph, int gi, std::vector<GemmTask> (&lists)[kTileCfgs]) {
+  const int tc = u.tile[ph];
+  const int te = tile_edge(u.f32, tc);
+  const int nm = u.mp / te, nn = u.np / te;     // whole tiles of this shape
+  std::vector<GemmTask>& main = lists[tc];
+  if (ph != kBX) {
+    for (int a = 0; a < nm; ++a)
+      for (int b = a; b < nm; ++b) main.push_back({gi, a, b, 0});
+  } else {
+    for (int b = 0; b < nn; ++b)
+      for (int a = 0; a < nm; ++a) main.push_back({gi, a, b, 0});
+  }
+  if (tc != kTileL) return;
+  std::vector<GemmTask>& rest = lists[kTileM];
+  const int r = te / kTileEdgeM;                // 128-tiles per 256-tile edge
+  const int mm = u.mp / kTileEdgeM, mn = u.np / kTileEdgeM;
+  if (ph != kBX) {
+    for (int j = r * nm; j < mm; ++j)
+      for (int i = 0; i <= j; ++i) rest.push_back({gi, i, j, 0});
+  } else {
+    for (int j = r * nn; j < mn; ++j)
+      for (int i = 0; i < mm; ++i) rest.push_back({gi, i, j, 0});
+    for (int j = 0; j < r * nn; ++j)
+      for (int i = r * nm; i < mm; ++i) rest.push_back({gi, i, j, 0});
+  }
+}
 
 // XCD-aware order of one phase's tiles.  The dispatcher hands block b to XCD
 // b mod 8, and each XCD has its own L2, so tiles that share operand rows
@@ -341,13 +384,9 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
       u.m = int(std::min<int64_t>(h, t.cols));
       u.n = int(std::max<int64_t>(h, t.cols));
       u.f32 = t.dtype == MUON_F32 || u.m < kMinBf16NsSide;   // NS precision of the unit
-      int edge = 0;
-      for (int ph = 0; ph < 3; ++ph) {
-        u.tile[ph] = u.f32 ? kTileM : choose_tile(u.m, u.n, ph);
-        edge = std::max(edge, tile_edge(u.f32, u.tile[ph]));
-      }
-      u.mp = int(round_up(u.m, edge));
-      u.np = int(round_up(u.n, edge));
+      for (int ph = 0; ph < 3; ++ph) u.tile[ph] = u.f32 ? kTileM : choose_tile(u.m, ph);
+      u.mp = int(round_up(u.m, tile_edge(u.f32, kTileM)));
+      u.np = int(round_up(u.n, tile_edge(u.f32, kTileM)));
       u.lr_scale = shape_scale(h, t.cols, hp->scale_mode) * t.lr_mult;
       const int ewr = u.side == kLeft ? kEwRows : kEwTile, ewc = u.side == kLeft ? kEwCols : kEwTile;
       u.k1_tr = int((h + ewr - 1) / ewr);
@@ -375,9 +414,9 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
     // only add cache contention
     int64_t bx_tiles = 0;
     for (int k : ids) {
-      const UnitPlan& u = plan.units[k];
-      const int te = tile_edge(u.f32, u.tile[kBX]);
-      bx_tiles += int64_t(u.mp / te) * (u.np / te);
+      std::vector<GemmTask> lists[kTileCfgs];
+      unit_tiles(plan.units[k], kBX, 0, lists);
+      for (const auto& l : lists) bx_tiles += int64_t(l.size());
     }
     const int lanes = !single_lane && ids.size() >= size_t(kLaneMinUnits) && bx_tiles <= kLaneMaxBxTiles ? kLanes : 1;
     auto cost = [&](int k) {
@@ -408,17 +447,7 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
       const UnitPlan& u = plan.units[g.units[gi]];
       for (int r = 0; r < u.k1_tr; ++r)
         for (int c = 0; c < u.k1_tc; ++c) g.ew.push_back({int(gi), r, c, r * u.k1_tc + c});
-      for (int ph : {kGram, kSquare}) {
-        const int te = tile_edge(u.f32, u.tile[ph]);
-        for (int a = 0; a < u.mp / te; ++a)
-          for (int b = a; b < u.mp / te; ++b) g.gemm[ph][u.tile[ph]].push_back({int(gi), a, b, 0});
-      }
-      // B X tiles column by column: the tiles that run together then share
-      // one column strip of X and all of B (a unit's B is the smaller
-      // operand), so each strip of X comes from HBM about once.
-      const int te = tile_edge(u.f32, u.tile[kBX]);
-      for (int b = 0; b < u.np / te; ++b)
-        for (int a = 0; a < u.mp / te; ++a) g.gemm[kBX][u.tile[kBX]].push_back({int(gi), a, b, 0});
+      for (int ph = 0; ph < 3; ++ph) unit_tiles(u, ph, int(gi), g.gemm[ph]);
     }
     for (int ph = 0; ph < 3; ++ph)
       for (int tc = 0; tc < kTileCfgs; ++tc) g.gemm[ph][tc] = xcd_order(g.gemm[ph][tc], plan.units, g, ph);

@@ -32,15 +32,15 @@
 // once per tile with one 16-byte load per block, and written back the same
 // way from the accumulators.
 //
-// bf16 tile shapes (the planner picks one per matrix):
+// bf16 tile shapes (the planner picks one per matrix and phase):
 //   kTileM  128 x 128 output tiles, 8 waves of 64 x 32 (2 x 1 blocks of
 //           v_mfma_f32_32x32x16_bf16), 64-deep K stages in a two-stage
 //           ring (64 KB of LDS): two blocks per CU, so one block's epilogue
 //           overlaps the other's MFMA loop.
-//   kTileL  256 x 256 output tiles, 4 waves of 128 x 128 (4 x 4 blocks, the
-//           accumulators fill the wave's 256 AGPRs), a 128 KB ring: one
-//           block per CU, with half the operand bytes per flop of kTileM,
-//           which the L2 -> LDS path needs to keep the MFMAs fed.
+//   kTileL  256 x 256 output tiles, 8 waves of 128 x 64 (4 x 2 blocks, the
+//           accumulators in 128 AGPRs), a 128 KB ring: one block per CU,
+//           with half the operand bytes per flop of kTileM, which the
+//           L2 -> LDS path needs to keep the MFMAs fed.
 // The K stages are filled by direct-to-LDS loads (global_load_lds_dwordx4:
 // no VGPR staging, no LDS store instructions).
 // float32 path: 64x64 tile, 4 waves of 32x32, v_mfma_f32_32x32x2f32.

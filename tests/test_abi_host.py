@@ -208,8 +208,10 @@ def test_plan_gpt2_small():
 def test_plan_gpt2_xl_and_padding():
     plan = mm.plan_describe(_workload_fakes("gpt2xl", layers=2), mm.default_hparams())
     units = plan["units"]
-    # 1600 would pad to 1792 at 256: 128 x 128 tiles in every phase
-    assert all(u["m"] == 1600 and u["mp"] == 1664 and u["tiles"] == [128] * 3 for u in units)
+    # 1600 = 6 x 256 + 64: units padded to 1664 only; the Gram and B X cover
+    # 1536 x 1536 (1536 x 6400) with 256-tiles and the rest with 128-tiles,
+    # the square stays at 128
+    assert all(u["m"] == 1600 and u["mp"] == 1664 and u["tiles"] == [256, 128, 256] for u in units)
     assert {u["np"] for u in units} == {1664, 6400}
     assert sum(u["side"] == "right" for u in units) == 2
     # the full 48-layer set has far more B X tiles per phase than two lanes
@@ -219,20 +221,24 @@ def test_plan_gpt2_xl_and_padding():
 
 
 def test_plan_large_units_take_256_tiles():
-    # m >= 2048 takes 256 x 256 tiles in every phase (padding to 256); from
-    # m = 768 the square and B X do where 256 pads no further than 128 (not
-    # for 1000 x 1100: 1152 against 1280), the Gram keeps 128 x 128; one
-    # group holding both runs two launches per phase, the 256 one first
+    # Tile shape per phase: the Gram at 256 from m = 1536, the square where m
+    # is a multiple of 256 (from 768) or from 2048, B X from 768.  Units are
+    # padded to 128; a 256-tile phase covers the largest multiple of 256 and
+    # the remaining 128-strips with 128-tiles.  One group holding both shapes
+    # runs two launches per phase, the 256 one first.
     ts = fakes([(4096, 4096), (2100, 3000), (1024, 4096), (1000, 1100), (640, 2048)])
     plan = mm.plan_describe(ts, mm.default_hparams())
     u = plan["units"]
     assert [(x["tiles"], x["mp"], x["np"]) for x in u] == [
-        ([256] * 3, 4096, 4096), ([256] * 3, 2304, 3072), ([128, 256, 256], 1024, 4096),
-        ([128] * 3, 1024, 1152), ([128] * 3, 640, 2048)]
+        ([256] * 3, 4096, 4096), ([256] * 3, 2176, 3072), ([128, 256, 256], 1024, 4096),
+        ([128, 128, 256], 1024, 1152), ([128] * 3, 640, 2048)]
     g = plan["groups"][0]
-    assert g["tiles_by_edge"]["256"] == [16 * 17 // 2 + 9 * 10 // 2, 16 * 17 // 2 + 9 * 10 // 2 + 4 * 5 // 2,
-                                         16 * 16 + 9 * 12 + 4 * 16]
-    assert g["tiles_by_edge"]["128"] == [8 * 9 // 2 * 2 + 5 * 6 // 2, 8 * 9 // 2 + 5 * 6 // 2, 8 * 9 + 5 * 16]
+    sym = lambda k: k * (k + 1) // 2          # upper tiles of a k x k tile grid
+    # 2100 x 3000: 256-tiles over 2048 x 3072, then the 128-row strip 2048..2175
+    # (17 upper tiles in its column for the square products, 24 in its row for B X);
+    # 1000 x 1100 B X: 256-tiles over 1024 x 1024, the 128-column strip 1024..1151
+    assert g["tiles_by_edge"]["256"] == [sym(16) + sym(8), sym(16) + sym(8) + sym(4), 16 * 16 + 8 * 12 + 4 * 16 + 4 * 4]
+    assert g["tiles_by_edge"]["128"] == [17 + sym(8) + sym(8) + sym(5), 17 + sym(8) + sym(5), 24 + 8 + 5 * 16]
     assert plan["launch_order"][1:7] == ["gram/bf16x256", "gram/bf16", "square/bf16x256", "square/bf16",
                                           "bx/bf16x256", "bx/bf16"]
 

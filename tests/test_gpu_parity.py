@@ -228,10 +228,12 @@ def test_low_rank_plus_noise_mid_sizes(rank):
 
 
 def test_large_ragged_256_tiles():
-    # a short side of 2048 or more takes the 256 x 256 tiles: ragged padding
-    # (2100 -> 2304, 2300 -> 2304), Gram and square tiles above the diagonal
-    # stored twice, a tall matrix (the last B X writes weight rows from tile
-    # columns) and an exact multiple of the tile
+    # a short side of 2048 or more takes 256 x 256 tiles in every phase: the
+    # units are padded to 128 (2100 -> 2176) and the strip past the last
+    # whole 256-tile is covered by 128-tiles (a row and a column strip for
+    # the Gram and square, mirror-stored; a row strip for B X); a tall
+    # matrix (the last B X writes weight rows from tile columns) and an exact
+    # multiple of the tile
     shapes = [(2100, 2300), (2300, 2100), (2048, 2048)]
     say("case: large ragged bf16 (256 x 256 tiles)")
     wl = adhoc("large", shapes, "bf16")
@@ -239,6 +241,23 @@ def test_large_ragged_256_tiles():
     hp = mm.default_hparams()
     assert c.run(hp) == 0
     w = check(c, hp, label="large/256")
+    assert w["O"] < 2e-2
+
+
+def test_mid_ragged_mixed_tiles():
+    # mid-sized short sides: B X at 256 x 256 with 128-tile strips past the
+    # last whole 256-tile (1000 x 1100: a column strip; 1100 x 1000 tall: the
+    # column strip holds weight rows), the Gram and square at 128; 1600 x
+    # 1700: the Gram at 256 with its 128-strip too, the square at 128
+    shapes = [(1000, 1100), (1100, 1000), (1600, 1700)]
+    say("case: mid ragged bf16 (256- and 128-tiles in one phase)")
+    wl = adhoc("mid", shapes, "bf16")
+    c = Case(wl, wl.tensors)
+    plan = mm.plan_describe(c.descs(), mm.default_hparams())
+    assert [u["tiles"] for u in plan["units"]] == [[128, 128, 256]] * 2 + [[256, 128, 256]]
+    hp = mm.default_hparams()
+    assert c.run(hp) == 0
+    w = check(c, hp, label="mid/mixed")
     assert w["O"] < 2e-2
 
 
