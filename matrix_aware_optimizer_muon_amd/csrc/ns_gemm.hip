@@ -426,15 +426,13 @@ __device__ __forceinline__ void fold_atile(const E* lb, int wn, int lane, float 
   });
 }
 
-// One 32-row strip (NBN tiles of 32x32) of the accumulators, times s, into
-// the wave's LDS staging area in row-major order (pitch EPP floats).
-template <bool AGPR, int NBN, int EPP>
-__device__ __forceinline__ void stage_strip(const f32x16_t (&row)[NBN], float s, float* ep, int lane) {
+// One 32x32 block of a 32-row strip (block column j; v: the lane's 16
+// values in accumulator register order) into the wave's LDS staging area in
+// row-major order (pitch EPP floats).
+template <int EPP>
+__device__ __forceinline__ void stage_block(const float* v, int j, float* ep, int lane) {
 #pragma unroll
-  for (int j = 0; j < NBN; ++j)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      ep[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * EPP + j * 32 + (lane & 31)] = s * acc_get<AGPR>(row[j], r);
+  for (int r = 0; r < 16; ++r) ep[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * EPP + j * 32 + (lane & 31)] = v[r];
 }
 
 // The int8 correction of the next bf16 master for one 32x32 block, from the
@@ -508,11 +506,15 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   const int ti = t.ti, tj = t.tj;
 
   // The epilogue's scale, known before the K loop (so no control flow
-  // joins while the accumulators are live): the first Gram folds the
-  // per-tile partial sums into 1/(||U|| + eps) (every block in the same
-  // order; tile (0, 0) stores it for the first B X), which that B X loads;
-  // the square scales by c.
+  // joins while the accumulators are live).  The first Gram folds the
+  // per-tile partial sums into s = 1/(||U|| + eps) (every block in the same
+  // order; tile (0, 0) stores it) and scales by s^2.  The square scales by
+  // c, in the first iteration by c s: B' = s B, so that the first B X,
+  // s (a X + B X) = (s a) X + B' X, only needs s in the fold's coefficient
+  // and its epilogue (which runs with its block alone on the CU at 256 x
+  // 256) multiplies nothing.
   float scale = 1.f;
+  float a_fold = p.a;                                // B X: coefficient of the a X fold
   if constexpr (PH == kGram) {
     if (p.first) {
       const float iv = unit_inv_norm(u.partials, u.k1_ntiles, p.eps, red);
@@ -520,9 +522,9 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
       if (ti == 0 && tj == 0 && threadIdx.x == 0) gst(u.norm, iv);
     }
   } else if constexpr (PH == kSquare) {
-    scale = p.c;
+    scale = p.first ? p.c * gld<float>(u.norm) : p.c;
   } else {
-    scale = p.first ? gld<float>(u.norm) : 1.f;
+    if (p.first) a_fold = p.a * gld<float>(u.norm);
   }
 
   // operand A: rows [ti*BTM, +BTM) over K; operand B: rows [tj*BTN, +BTN)
@@ -754,7 +756,7 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
     const E* csb = diag ? cs : cs + T_A;
     if constexpr (FP >= 0) {
       if constexpr (PH == kBX) {
-        fold_master<FP, F32, AGPR, NBM, NBN, WTM, WTN, BK, BTN>(csb, wn, lane, p.a, xq, acc);
+        fold_master<FP, F32, AGPR, NBM, NBN, WTM, WTN, BK, BTN>(csb, wn, lane, a_fold, xq, acc);
         load_xq(std::integral_constant<int, FP + 1>{});
       } else {
         fold_atile<FP, F32, AGPR, NBM, NBN, WTM, WTN, BK>(csb, wn, lane, bc, acc);
@@ -823,32 +825,17 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
     wu.cols = sreg_i32(u.cols);
   }
 
-  // B X, bf16, not last: the corrections of the next master go straight from
-  // the accumulators to the correction array, one 16-byte store per block
-  if constexpr (PH == kBX && !F32 && !LAST) {
-    const size_t nbc = static_cast<size_t>(np / 32);
-#pragma unroll
-    for (int i = 0; i < NBM; ++i)
-#pragma unroll
-      for (int j = 0; j < NBN; ++j) {
-        // one block's accumulators at a time: keep the compiler from reading
-        // all of them out of the AGPRs at once
-        __builtin_amdgcn_sched_barrier(0);
-        float v[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) v[r] = scale * acc_get<AGPR>(acc[i][j], r);
-        const size_t bi = (row_base + i * 32) / 32, bj = (col_base + j * 32) / 32;
-        gst(out_xl + (bi * nbc + bj) * 1024 + el * 16, encode_corr16(v));
-      }
-  }
-
   // Each wave stages one 32-row strip of its scaled accumulators in its own
   // LDS area (so the strips need no block barrier), then writes row segments
   // (natural layout) and, where needed, column segments (mirror tiles of A
   // and B; weight rows of a tall matrix in the last iteration) as 16-byte
-  // vector accesses.  acc and wbuf are only ever indexed with constants (a
-  // runtime index would move the arrays to scratch memory), so the strip
-  // loop is unrolled at compile time.
+  // vector accesses.  In B X (bf16, not last) each accumulator block read
+  // for the strip also gives the int8 corrections of the next master, stored
+  // straight from the registers (one 16-byte store per block).  acc and wbuf
+  // are only ever indexed with constants (a runtime index would move the
+  // arrays to scratch memory), so the strip loop is unrolled at compile time.
+  const float es = PH == kBX ? 1.f : scale;          // B X: the scale is folded upstream
+  const size_t nbc = static_cast<size_t>(np / 32);
   static_for<0, NBM>([&](auto pic) {
     constexpr int pi = decltype(pic)::value;
     // strip by strip: a later strip's accumulators stay in the AGPRs until
@@ -858,7 +845,17 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
       if (wfast) load_w(pi + 1, el, wbuf[(pi + 1) & 1]);
     }
     if constexpr (pi > 0) wave_sync();      // the previous strip's reads are done
-    stage_strip<AGPR, NBN, EPP>(acc[pi], scale, ep, el);
+#pragma unroll
+    for (int j = 0; j < NBN; ++j) {
+      float v[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[r] = es * acc_get<AGPR>(acc[pi][j], r);
+      if constexpr (PH == kBX && !F32 && !LAST) {
+        const size_t bi = (row_base + pi * 32) / 32, bj = (col_base + j * 32) / 32;
+        gst(out_xl + (bi * nbc + bj) * 1024 + el * 16, encode_corr16(v));
+      }
+      stage_block<EPP>(v, j, ep, el);
+    }
     wave_sync();
 
 #pragma unroll
