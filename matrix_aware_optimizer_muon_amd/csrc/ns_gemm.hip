@@ -438,22 +438,28 @@ __device__ __forceinline__ void stage_block(const float* v, int j, float* ep, in
 // The int8 correction of the next bf16 master for one 32x32 block, from the
 // accumulator registers (values already scaled): the same encoding as
 // master_encode8, element by element, 16 bytes per lane in register order.
+// With t = d + 128 clamped to [-32512, 32767] (d: the bit-pattern difference
+// to hi), bits 8..15 of t are exactly the clamped round(d / 256) of
+// master_encode8, so byte selects pack the four bytes of a word without a
+// shift or mask per element.
 __device__ __forceinline__ u32x4_t encode_corr16(const float* v) {
   u32x4_t out;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    uint32_t word = 0;
+    uint32_t t[4];
 #pragma unroll
     for (int e = 0; e < 4; e += 2) {
       const float a0 = v[4 * w + e], a1 = v[4 * w + e + 1];
       const uint32_t hp = cvt2_bf16(a0, a1);
-      const int d0 = __float_as_int(a0) - static_cast<int>(hp << 16);
-      const int d1 = __float_as_int(a1) - static_cast<int>(hp & 0xFFFF0000u);
-      const uint32_t q0 = static_cast<uint32_t>(min(max((d0 + 128) >> 8, -127), 127)) & 0xFFu;
-      const uint32_t q1 = static_cast<uint32_t>(min(max((d1 + 128) >> 8, -127), 127)) & 0xFFu;
-      word |= (q0 << (8 * e)) | (q1 << (8 * (e + 1)));
+      const int d0 = __float_as_int(a0) - static_cast<int>(hp << 16) + 128;
+      const int d1 = __float_as_int(a1) - static_cast<int>(hp & 0xFFFF0000u) + 128;
+      t[e] = static_cast<uint32_t>(min(max(d0, -32512), 32767));
+      t[e + 1] = static_cast<uint32_t>(min(max(d1, -32512), 32767));
     }
-    out[w] = word;
+    // byte 1 of t0, t1 (then t2, t3) into bytes 0, 1; then the two halves
+    const uint32_t lo = __builtin_amdgcn_perm(t[1], t[0], 0x0c0c0501u);
+    const uint32_t hi = __builtin_amdgcn_perm(t[3], t[2], 0x0c0c0501u);
+    out[w] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
   }
   return out;
 }
