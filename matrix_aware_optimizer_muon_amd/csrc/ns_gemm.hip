@@ -61,7 +61,13 @@ typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;       // LDS
 // tile (rows x columns); NWM x NWN waves, each owning a (BTM/NWM) x
 // (BTN/NWN) block of 32x32 MFMA tiles; BK: K depth of one LDS stage; NS:
 // stages in the LDS ring (NS-1 in flight while one is consumed); OCC: the
-// launch bound's minimum waves per SIMD.
+// launch bound's minimum waves per SIMD.  DMAW: where a K step issues the
+// next stage's copies: 0 right after the stage barrier, 2 after the first
+// 16-deep slice of MFMAs (so the matrix pipe starts as soon as the first
+// fragments arrive).  Measured: 2 makes the 256 x 256 kernels faster (4096 x
+// 4096 square 102 -> 95 us, B X 120 -> 117 us per launch; GPT-2-small B X
+// 106 -> 103.5 us) and the 128 x 128 ones slower (GPT-2-small Gram 60 -> 63
+// us, GPT-2-XL square 1.57 -> 1.65 ms).
 //   128 x 128: 8 waves of 64 x 32, 64 KB of stages, two blocks (four waves
 //     per SIMD) per CU;
 //   256 x 256: 8 waves of 128 x 64 (accumulators in the AGPRs), 128 KB of
@@ -76,15 +82,15 @@ template <bool F32, int PH, int TC> struct Cfg;
 #endif
 template <int PH> struct Cfg<false, PH, kTileM> {
   using E = uint16_t;
-  static constexpr int BTM = kTileEdgeM, BTN = kTileEdgeM, NWM = 2, NWN = 4, BK = 64, NS = 2, OCC = 2;
+  static constexpr int BTM = kTileEdgeM, BTN = kTileEdgeM, NWM = 2, NWN = 4, BK = 64, NS = 2, OCC = 2, DMAW = 0;
 };
 template <int PH> struct Cfg<false, PH, kTileL> {
   using E = uint16_t;
-  static constexpr int BTM = kTileEdgeL, BTN = kTileEdgeL, NWM = 2, NWN = 4, BK = 64, NS = 2, OCC = 1;
+  static constexpr int BTM = kTileEdgeL, BTN = kTileEdgeL, NWM = 2, NWN = 4, BK = 64, NS = 2, OCC = 1, DMAW = 2;
 };
 template <int PH, int TC> struct Cfg<true, PH, TC> {
   using E = float;
-  static constexpr int BTM = kTileF32, BTN = kTileF32, NWM = 2, NWN = 2, BK = 32, NS = 2, OCC = 2;
+  static constexpr int BTM = kTileF32, BTN = kTileF32, NWM = 2, NWN = 2, BK = 32, NS = 2, OCC = 2, DMAW = 0;
 };
 
 // LDS layout of a stage.  Tiles are stored unpadded as rows of 16-byte
@@ -242,13 +248,19 @@ __device__ __forceinline__ void load_frags(const uint16_t* la, const uint16_t* l
 // MFMAs while only two slices' fragments occupy registers.  (Interleaving
 // each read with an MFMA through scheduling-group barriers was measured:
 // no faster with 64 x 32 wave tiles, 20 % slower with 128 x 64.)
-template <bool F32, bool KMAJOR_B, int NBM, int NBN, int WTM, int WTN, int BK, int BTN, typename E>
+template <bool F32, bool KMAJOR_B, int NBM, int NBN, int WTM, int WTN, int BK, int BTN, int WHEN = 0, typename E,
+          typename H>
 __device__ __forceinline__ void mma_stage(const E* la, const E* lb, f32x16_t (&acc)[NBM][NBN], int lane, int wm,
-                                          int wn) {
+                                          int wn, H&& mid) {
   if constexpr (!F32) {
     constexpr int NKS = BK / 16;
     bf16x8_t fa[2][NBM], fb[2][NBN];
     load_frags<KMAJOR_B, NBM, NBN, WTM, WTN, BK, BTN>(la, lb, 0, lane, wm, wn, fa[0], fb[0]);
+    if constexpr (WHEN == 1) {
+      __builtin_amdgcn_sched_barrier(0);
+      mid();
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       if (ks + 1 < NKS)
@@ -260,8 +272,15 @@ __device__ __forceinline__ void mma_stage(const E* la, const E* lb, f32x16_t (&a
         for (int j = 0; j < NBN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (WHEN == 2) {
+        if (ks == 0) {
+          mid();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     }
   } else {
+    if constexpr (WHEN != 0) mid();
     // v_mfma_f32_32x32x2f32: lane half h holds k = h*16 + e at step e of the
     // 32-deep slab, for both operands
     const int k0 = (lane >> 5) * 16;
@@ -751,12 +770,15 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
     if (diag) wait_vmcnt<(NS - 2) * NIA>();   // newer stages in flight: NS-2 of one operand each
     else wait_vmcnt<(NS - 2) * (NIA + NIB)>();
     ring_barrier();
-    if (NS > 2 || kt + 1 < KT) {   // with two stages the last step issues no copy
-      const int nx = min(kt + NS - 1, KT - 1);
-      const uint32_t ls = ring0 + ((kt + NS - 1) % NS) * STAGE_B;
-      issue_stage<NIA, NIB, NW, E>(pa + nx * a_step, pb + nx * b_step, aoff, boff, astep, bstep, ls, ls + TILE_B,
-                                   wave, !diag);
-    }
+    auto issue = [&] {
+      if (NS > 2 || kt + 1 < KT) {   // with two stages the last step issues no copy
+        const int nx = min(kt + NS - 1, KT - 1);
+        const uint32_t ls = ring0 + ((kt + NS - 1) % NS) * STAGE_B;
+        issue_stage<NIA, NIB, NW, E>(pa + nx * a_step, pb + nx * b_step, aoff, boff, astep, bstep, ls, ls + TILE_B,
+                                     wave, !diag);
+      }
+    };
+    if constexpr (C::DMAW == 0) issue();
     hook();
     const E* cs = smem + (kt % NS) * STAGE;
     const E* csb = diag ? cs : cs + T_A;
@@ -768,7 +790,7 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
         fold_atile<FP, F32, AGPR, NBM, NBN, WTM, WTN, BK>(csb, wn, lane, bc, acc);
       }
     }
-    mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, BTN>(cs, csb, acc, lane, wm, wn);
+    mma_stage<F32, KMAJOR_B, NBM, NBN, WTM, WTN, BK, BTN, C::DMAW>(cs, csb, acc, lane, wm, wn, issue);
   };
   if constexpr (FOLD) {
     // the wave's rows are K steps f0 .. f0 + NFOLD - 1 (K index = tile row);
