@@ -86,7 +86,11 @@ __device__ __forceinline__ void unpack8_bf16(const u32x4_t& w, float* v) {
 // the count runs in the binade below, and the decode, adding in the same bit
 // space, lands there too.  Sign-magnitude patterns make the count a
 // magnitude offset for negative x as well.  Integer arithmetic only: a
-// subtraction and a rounding shift to encode, a shift-add to decode.
+// subtraction and a rounding shift to encode, a shift-add to decode.  The
+// decode holds for any hi within 2^15 bit steps of x whose q was counted
+// against that hi: the B X epilogue writes its masters with hi rounded
+// half-up at a threshold 128 steps below the tie (q in [-128, 127], same
+// 128-step accuracy), which it packs with fewer instructions.
 __device__ __forceinline__ void master_encode8(const float* v, u32x4_t& hi, u32x2_t& lo) {
   uint32_t q[8];
 #pragma unroll

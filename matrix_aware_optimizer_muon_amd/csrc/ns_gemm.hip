@@ -454,33 +454,42 @@ __device__ __forceinline__ void stage_block(const float* v, int j, float* ep, in
   for (int r = 0; r < 16; ++r) ep[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * EPP + j * 32 + (lane & 31)] = v[r];
 }
 
-// The int8 correction of the next bf16 master for one 32x32 block, from the
-// accumulator registers (values already scaled): the same encoding as
-// master_encode8, element by element, 16 bytes per lane in register order.
-// With t = d + 128 clamped to [-32512, 32767] (d: the bit-pattern difference
-// to hi), bits 8..15 of t are exactly the clamped round(d / 256) of
-// master_encode8, so byte selects pack the four bytes of a word without a
-// shift or mask per element.
-__device__ __forceinline__ u32x4_t encode_corr16(const float* v) {
+// The next bf16 master as B X writes it, from one 32x32 block of
+// accumulators (16 values per lane in register order, already scaled): with
+// y = bits(x) + 0x8080, hi = the upper half of y (x rounded to bf16 half-up
+// with the threshold 1/256 ulp below the tie, so within a bf16 half-ulp plus
+// 2^-8 of one) and the int8 correction q = byte 1 of y, xor 0x80.  Then
+// d = bits(x) - bits(hi) = (y mod 2^16) - 0x8080 lies in [-32896, 32639] and
+// q = floor((d + 128) / 256) in [-128, 127]: the decode bits(hi) + 256 q
+// (master_decode8, the folds) lands within 128 float32 ulps of x, as with
+// the round-to-nearest-even encoding of master_encode8, for either sign and
+// across binades (bit-pattern arithmetic).  y replaces x in place; the
+// function returns the 16 correction bytes in register order.
+__device__ __forceinline__ u32x4_t encode_master16(float* v) {
+  uint32_t y[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    y[r] = __float_as_uint(v[r]) + 0x8080u;
+    v[r] = __uint_as_float(y[r]);
+  }
   u32x4_t out;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    uint32_t t[4];
-#pragma unroll
-    for (int e = 0; e < 4; e += 2) {
-      const float a0 = v[4 * w + e], a1 = v[4 * w + e + 1];
-      const uint32_t hp = cvt2_bf16(a0, a1);
-      const int d0 = __float_as_int(a0) - static_cast<int>(hp << 16) + 128;
-      const int d1 = __float_as_int(a1) - static_cast<int>(hp & 0xFFFF0000u) + 128;
-      t[e] = static_cast<uint32_t>(min(max(d0, -32512), 32767));
-      t[e + 1] = static_cast<uint32_t>(min(max(d1, -32512), 32767));
-    }
-    // byte 1 of t0, t1 (then t2, t3) into bytes 0, 1; then the two halves
-    const uint32_t lo = __builtin_amdgcn_perm(t[1], t[0], 0x0c0c0501u);
-    const uint32_t hi = __builtin_amdgcn_perm(t[3], t[2], 0x0c0c0501u);
-    out[w] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    // byte 1 of y0, y1 (then y2, y3) into bytes 0, 1; then the two halves
+    const uint32_t lo = __builtin_amdgcn_perm(y[4 * w + 1], y[4 * w], 0x0c0c0501u);
+    const uint32_t hi = __builtin_amdgcn_perm(y[4 * w + 3], y[4 * w + 2], 0x0c0c0501u);
+    out[w] = __builtin_amdgcn_perm(hi, lo, 0x05040100u) ^ 0x80808080u;
   }
   return out;
+}
+
+// Eight staged y patterns (encode_master16) to their eight bf16 hi halves,
+// element 2e in the low half of word e.
+__device__ __forceinline__ u32x4_t pack8_hi(const float* v) {
+  u32x4_t w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = __builtin_amdgcn_perm(__float_as_uint(v[2 * e + 1]), __float_as_uint(v[2 * e]), 0x07060302u);
+  return w;
 }
 
 template <bool F32, int PH, int TC, bool LAST>
@@ -879,8 +888,9 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
 #pragma unroll
       for (int r = 0; r < 16; ++r) v[r] = es * acc_get<AGPR>(acc[pi][j], r);
       if constexpr (PH == kBX && !F32 && !LAST) {
+        // the strip then holds y = bits(x) + 0x8080, whose upper halves are hi
         const size_t bi = (row_base + pi * 32) / 32, bj = (col_base + j * 32) / 32;
-        gst(out_xl + (bi * nbc + bj) * 1024 + el * 16, encode_corr16(v));
+        gst(out_xl + (bi * nbc + bj) * 1024 + el * 16, encode_master16(v));
       }
       stage_block<EPP>(v, j, ep, el);
     }
@@ -901,7 +911,7 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
         st8<F32>(out_ab, static_cast<size_t>(gr) * mp + gc, v);
       } else if constexpr (!LAST) {
         if constexpr (F32) st8<true>(out_xh, static_cast<size_t>(gr) * np + gc, v);
-        else gst(static_cast<uint16_t*>(out_xh) + static_cast<size_t>(gr) * np + gc, pack8_bf16(v));
+        else gst(static_cast<uint16_t*>(out_xh) + static_cast<size_t>(gr) * np + gc, pack8_hi(v));
       } else if (u.side == kLeft) {
         if (gr < wu.rows) {
           if (wfast && gc + 8 <= wu.cols) update_w8_loaded(wu, gr, gc, v, decay, step, wbuf[pi & 1][q]);
