@@ -11,11 +11,12 @@
 //                    ns_steps == 0 only (otherwise the last Newton-Schulz
 //                    phase applies the update).
 //
-// Both walk tiles of 4096 elements in which every thread owns two 8-element
+// Both walk tiles of 8192 elements in which every thread owns four 8-element
 // row segments, so global traffic is 16-byte vector accesses along rows:
-// 16 x 256 tiles for units whose X is U (a wave covers two 256-element runs
-// of one row each), 64 x 64 tiles for units whose X is U^T, whose
-// orientation swap goes through an LDS tile.  The partial sums are folded
+// 32 x 256 tiles for units whose X is U (a wave covers two 256-element runs
+// of one row each; the 32 rows are one row of whole correction blocks, so
+// each block's 16-byte lane chunks are written whole), 64 x 128 tiles (of U)
+// for units whose X is U^T, whose orientation swap goes through an LDS tile.  The partial sums are folded
 // later, in a fixed order, by the first Newton-Schulz phase, so no block
 // here waits on another.
 #include "device_common.h"
@@ -25,13 +26,17 @@ namespace muon {
 namespace {
 
 constexpr int kThreads = 256;
-// LDS tile of a momentum block: 64 x (64 + 1) floats for the transposed
-// (right-side) walk, 16 x (256 + 8) for the correction blocks of a
-// left-side one (pitch 264 puts the two half-waves of a column read in
-// different banks).
+constexpr int kSegs = 4;   // 8-element row segments per thread and tile
+static_assert(kEwRows * kEwCols == kThreads * kSegs * 8 && kEwRRows * kEwRCols == kThreads * kSegs * 8,
+              "a tile is kSegs segments per thread");
+// LDS tile of a momentum block: 64 x (128 + 1) floats for the transposed
+// (right-side) walk (column reads at pitch 129 put the 64 lanes in distinct
+// banks), 32 x (256 + 8) for the correction blocks of a left-side one (pitch
+// 264 puts the two half-waves of a column read in different banks).
+constexpr int kRightPitch = kEwRCols + 1;
 constexpr int kLeftPitch = kEwCols + 8;
-constexpr int kTileFloats = kEwTile * (kEwTile + 1) > kEwRows * kLeftPitch ? kEwTile * (kEwTile + 1)
-                                                                            : kEwRows * kLeftPitch;
+constexpr int kTileFloats = kEwRRows * kRightPitch > kEwRows * kLeftPitch ? kEwRRows * kRightPitch
+                                                                          : kEwRows * kLeftPitch;
 
 // Store one 8-element row segment of X: the bf16 hi part of the master (its
 // int8 corrections are written separately, in their blocked layout), or the
@@ -58,8 +63,8 @@ template <bool F32, bool GF32>
 __device__ __forceinline__ void momentum_tile(const UnitDev& u, const EwTask& t, const K1Params& p,
                                               float* tile, float* wsum) {
   const bool left = u.side == kLeft;
-  const int r0 = t.tr * (left ? kEwRows : kEwTile), c0 = t.tc * (left ? kEwCols : kEwTile);
-  const int seg_sh = left ? 5 : 3;                   // log2 of 8-element segments per tile row
+  const int r0 = t.tr * (left ? kEwRows : kEwRRows), c0 = t.tc * (left ? kEwCols : kEwRCols);
+  const int seg_sh = left ? 5 : 4;                   // log2 of 8-element segments per tile row
   const int rows = u.rows, cols = u.cols;
   const float mu = p.mu;
   const float one_m = 1.0f - mu;
@@ -70,33 +75,30 @@ __device__ __forceinline__ void momentum_tile(const UnitDev& u, const EwTask& t,
   // issues every load of the thread before the first use, so the load
   // latency is paid once per tile rather than once per access; edge tiles
   // go element by element where needed.
-  const bool interior = r0 + (left ? kEwRows : kEwTile) <= rows && c0 + (left ? kEwCols : kEwTile) <= cols &&
+  const bool interior = r0 + (left ? kEwRows : kEwRRows) <= rows && c0 + (left ? kEwCols : kEwRCols) <= cols &&
                         u.vec_grad && u.vec_mom;
-  int iq[2], jq[2], lrq[2], lcq[2];
+  int iq[kSegs], jq[kSegs], lrq[kSegs], lcq[kSegs];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+  for (int q = 0; q < kSegs; ++q) {
     const int s = threadIdx.x + kThreads * q;
     lrq[q] = s >> seg_sh;
     lcq[q] = (s & ((1 << seg_sh) - 1)) * 8;
     iq[q] = r0 + lrq[q];
     jq[q] = c0 + lcq[q];
   }
-  float g[2][8], m[2][8];
+  float g[kSegs][8], m[kSegs][8];
   if (interior) {
-    ld8_f32(u.mom, static_cast<size_t>(iq[0]) * u.ld_mom + jq[0], m[0]);
-    ld8_f32(u.mom, static_cast<size_t>(iq[1]) * u.ld_mom + jq[1], m[1]);
-    const size_t og0 = static_cast<size_t>(iq[0]) * u.ld_grad + jq[0];
-    const size_t og1 = static_cast<size_t>(iq[1]) * u.ld_grad + jq[1];
-    if constexpr (GF32) {
-      ld8_f32(u.grad, og0, g[0]);
-      ld8_f32(u.grad, og1, g[1]);
-    } else {
-      ld8_bf16(u.grad, og0, g[0]);
-      ld8_bf16(u.grad, og1, g[1]);
+#pragma unroll
+    for (int q = 0; q < kSegs; ++q) ld8_f32(u.mom, static_cast<size_t>(iq[q]) * u.ld_mom + jq[q], m[q]);
+#pragma unroll
+    for (int q = 0; q < kSegs; ++q) {
+      const size_t og = static_cast<size_t>(iq[q]) * u.ld_grad + jq[q];
+      if constexpr (GF32) ld8_f32(u.grad, og, g[q]);
+      else ld8_bf16(u.grad, og, g[q]);
     }
   } else {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kSegs; ++q) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) g[q][e] = m[q][e] = 0.f;
       if (iq[q] < rows) {
@@ -107,7 +109,7 @@ __device__ __forceinline__ void momentum_tile(const UnitDev& u, const EwTask& t,
   }
 
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+  for (int q = 0; q < kSegs; ++q) {
     const int i = iq[q], j0 = jq[q], lr = lrq[q], lc = lcq[q];
     float uv[8];
 #pragma unroll
@@ -140,42 +142,47 @@ __device__ __forceinline__ void momentum_tile(const UnitDev& u, const EwTask& t,
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) tile[lr * (kEwTile + 1) + lc + e] = uv[e];
+      for (int e = 0; e < 8; ++e) tile[lr * kRightPitch + lc + e] = uv[e];
     }
   }
   if (!left) {
-    // X = U^T: column segments of the tile become row segments of X
+    // X = U^T: column segments of the tile become row segments of X (128 X
+    // rows of 64 elements; eight lanes cover one row); X rows past the
+    // padded m (a 128-wide tile of a float32 unit padded to 64) are skipped
     __syncthreads();
-    // eight lanes cover one X row (a 64-element run); LDS column reads at
-    // pitch kEwTile + 1 put the 64 lanes in distinct banks
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kSegs; ++q) {
       const int s = threadIdx.x + kThreads * q;
       const int xr = s >> 3, xs = s & 7;
+      if (c0 + xr >= u.mp) continue;
       float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = tile[(xs * 8 + e) * (kEwTile + 1) + xr];
+      for (int e = 0; e < 8; ++e) v[e] = tile[(xs * 8 + e) * kRightPitch + xr];
       store_seg<F32>(u.xh[0], u.np, c0 + xr, r0 + xs * 8, v);
     }
     if constexpr (!F32) {
-      // corrections: the 64 x 64 X tile is 2 x 2 whole 32 x 32 blocks; thread
-      // t writes lane t%64's 16 bytes of block t/64 (X row c0 + 32 bi + 8q +
-      // 4h + e, column r0 + 32 bj + l%32, i.e. U-tile element [32 bj + l%32]
-      // [32 bi + 8q + 4h + e])
-      const int blk = threadIdx.x >> 6, l = threadIdx.x & 63;
-      const int bi = blk >> 1, bj = blk & 1;
-      const float* trow = &tile[(32 * bj + (l & 31)) * (kEwTile + 1) + 32 * bi + 4 * (l >> 5)];
-      u32x4_t w;
+      // corrections: the 128 x 64 X tile is 4 x 2 whole 32 x 32 blocks;
+      // thread t writes lane l = t%64's 16 bytes of block t/64 and of block
+      // t/64 + 4 (X row c0 + 32 bi + 8q + 4h + e, column r0 + 32 bj + l%32,
+      // i.e. U-tile element [32 bj + l%32][32 bi + 8q + 4h + e])
 #pragma unroll
-      for (int q = 0; q < 4; ++q) w[q] = corr4(trow + 8 * q);
-      gst(static_cast<int8_t*>(u.xl) + corr_block_offset(u.np, c0 + 32 * bi, r0 + 32 * bj) + l * 16, w);
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const int s = threadIdx.x + kThreads * q2;
+        const int blk = s >> 6, l = s & 63;
+        const int bi = blk >> 1, bj = blk & 1;
+        if (c0 + 32 * bi >= u.mp) continue;
+        const float* trow = &tile[(32 * bj + (l & 31)) * kRightPitch + 32 * bi + 4 * (l >> 5)];
+        u32x4_t w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = corr4(trow + 8 * q);
+        gst(static_cast<int8_t*>(u.xl) + corr_block_offset(u.np, c0 + 32 * bi, r0 + 32 * bj) + l * 16, w);
+      }
     }
   } else if constexpr (!F32) {
-    // corrections of a left tile: its 16 rows are half of a row of 32 x 32
-    // blocks (register groups q = 0, 1 or 2, 3 of each lane); thread t writes
-    // 8 bytes of lane t%64 of block t/64, both halves of the wave.
+    // corrections of a left tile: its 32 rows are one row of 32 x 32 blocks;
+    // thread t writes lane l = t%64's 16 bytes of block t/64 and of block
+    // t/64 + 4 (rows 8q + 4h + e, column 32 jb + l%32)
     __syncthreads();
-    const int half = (r0 & 31) >> 4;        // rows 0..15 or 16..31 of the block row
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
       const int s = threadIdx.x + kThreads * q2;
@@ -183,15 +190,15 @@ __device__ __forceinline__ void momentum_tile(const UnitDev& u, const EwTask& t,
       const int col = c0 + 32 * jb;
       if (col >= u.np) continue;
       const float* tcol = &tile[4 * (l >> 5) * kLeftPitch + 32 * jb + (l & 31)];
-      float x[8];
+      u32x4_t w;
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq)
+      for (int q = 0; q < 4; ++q) {
+        float x[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * qq + e] = tcol[(8 * qq + e) * kLeftPitch];
-      u32x2_t w;
-      w[0] = corr4(x);
-      w[1] = corr4(x + 4);
-      gst(static_cast<int8_t*>(u.xl) + corr_block_offset(u.np, r0 - 16 * half, col) + l * 16 + 8 * half, w);
+        for (int e = 0; e < 4; ++e) x[e] = tcol[(8 * q + e) * kLeftPitch];
+        w[q] = corr4(x);
+      }
+      gst(static_cast<int8_t*>(u.xl) + corr_block_offset(u.np, r0, col) + l * 16, w);
     }
   }
 
@@ -238,26 +245,31 @@ template <bool F32>
 __global__ __launch_bounds__(kThreads) void update_kernel(const UnitDev* __restrict__ units,
                                                           const EwTask* __restrict__ tasks,
                                                           K5Params p) {
-  __shared__ float tile[kEwTile][kEwTile + 1];
+  __shared__ float tile[kEwRRows][kRightPitch];
   __shared__ float red[4];
   const EwTask t = tasks[blockIdx.x];
   const UnitDev& u = units[t.unit];
   const bool left = u.side == kLeft;
-  const int r0 = t.tr * (left ? kEwRows : kEwTile), c0 = t.tc * (left ? kEwCols : kEwTile);
-  const int seg_sh = left ? 5 : 3;                   // log2 of 8-element segments per tile row
+  const int r0 = t.tr * (left ? kEwRows : kEwRRows), c0 = t.tc * (left ? kEwCols : kEwRCols);
+  const int seg_sh = left ? 5 : 4;                   // log2 of 8-element segments per tile row
   const int rows = u.rows;
   // with no Newton-Schulz iteration O is the normalised U itself
   const float inv = unit_inv_norm(u.partials, u.k1_ntiles, p.eps, red);
 
   if (u.side == kRight) {
     // O[i][j] = X[j][i]: read X row segments (j fixed, i contiguous) into
-    // the tile transposed.
+    // the tile transposed (X rows past the padded m read as zeros)
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kSegs; ++q) {
       const int s = threadIdx.x + kThreads * q;
       const int lj = s >> 3, li = (s & 7) * 8;
       float v[8];
-      load_master_seg<F32>(u, c0 + lj, r0 + li, v);
+      if (c0 + lj < u.mp) {
+        load_master_seg<F32>(u, c0 + lj, r0 + li, v);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) tile[li + e][lj] = v[e];
     }
@@ -267,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void update_kernel(const UnitDev* __restr
   const float decay = p.lr * p.weight_decay;
   const float step = p.lr * u.lr_scale;
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+  for (int q = 0; q < kSegs; ++q) {
     const int s = threadIdx.x + kThreads * q;
     const int lr = s >> seg_sh, lc = (s & ((1 << seg_sh) - 1)) * 8;
     const int i = r0 + lr, j0 = c0 + lc;

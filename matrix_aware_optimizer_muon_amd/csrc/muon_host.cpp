@@ -388,7 +388,7 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
       u.mp = int(round_up(u.m, tile_edge(u.f32, kTileM)));
       u.np = int(round_up(u.n, tile_edge(u.f32, kTileM)));
       u.lr_scale = shape_scale(h, t.cols, hp->scale_mode) * t.lr_mult;
-      const int ewr = u.side == kLeft ? kEwRows : kEwTile, ewc = u.side == kLeft ? kEwCols : kEwTile;
+      const int ewr = u.side == kLeft ? kEwRows : kEwRRows, ewc = u.side == kLeft ? kEwCols : kEwRCols;
       u.k1_tr = int((h + ewr - 1) / ewr);
       u.k1_tc = int((t.cols + ewc - 1) / ewc);
       u.k1_ntiles = u.k1_tr * u.k1_tc;

@@ -19,12 +19,14 @@ constexpr int kTileEdgeM = 128;
 constexpr int kTileEdgeL = 256;
 constexpr int kTileF32 = 64;
 inline int tile_edge(bool f32, int cfg) { return f32 ? kTileF32 : cfg == kTileL ? kTileEdgeL : kTileEdgeM; }
-// Tiles of the elementwise phases (momentum, update).  A unit whose X is U
-// itself (rows <= cols) is walked in kEwRows x kEwCols tiles along its rows,
-// so each wave reads and writes runs of 256 consecutive elements; a unit
-// whose X is U^T is walked in kEwTile x kEwTile tiles transposed through LDS.
-constexpr int kEwTile = 64;
-constexpr int kEwRows = 16, kEwCols = 256;
+// Tiles of the elementwise phases (momentum, update), 8192 elements each.
+// A unit whose X is U itself (rows <= cols) is walked in kEwRows x kEwCols
+// tiles along its rows, so each wave reads and writes runs of 256
+// consecutive elements, and a tile's 32 rows are one row of whole 32 x 32
+// correction blocks; a unit whose X is U^T is walked in kEwRRows x kEwRCols
+// tiles (rows x columns of U) transposed through LDS.
+constexpr int kEwRows = 32, kEwCols = 256;
+constexpr int kEwRRows = 64, kEwRCols = 128;
 // bf16 matrices whose short side is below this run their Newton-Schulz
 // iteration on the float32 path: at such sizes the bf16 iteration's own
 // rounding error approaches 2e-2 relative, and the float32 path costs

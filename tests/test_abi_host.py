@@ -189,7 +189,7 @@ def test_plan_gpt2_small():
     # 3072 are multiples of 256, so no extra padding)
     assert all(u["tiles"] == [128, 256, 256] and u["mp"] == 768 for u in units)
     for k, total in (("gram", 72 * 21), ("square", 72 * 6), ("bx", 48 * 9 + 24 * 36),
-                     ("momentum", 12 * (4 * 144 + 2 * 576))):
+                     ("momentum", 12 * (4 * 72 + 2 * 288))):
         assert g0[f"{k}_tiles"] + g1[f"{k}_tiles"] == total
     assert g0["tiles_by_edge"] == {"256": [0, g0["square_tiles"], g0["bx_tiles"]],
                                    "128": [g0["gram_tiles"], 0, 0]}
