@@ -327,6 +327,49 @@ std::vector<GemmTask> xcd_order(const std::vector<GemmTask>& tiles, const std::v
   return out;
 }
 
+// Self-check of a group's GEMM task lists, run on every plan: counted on the
+// grid of g x g blocks (g: the 128-tile edge, 64 for float32 units), B X's
+// tiles cover every block of each unit's m_p x n_p output exactly once, and
+// the Gram's and the square's tiles every block on or above the diagonal
+// exactly once, reaching below it only inside diagonal tiles (whose lower
+// part they store directly; the other tiles are mirror-stored).
+bool tiles_cover_exactly(const std::vector<UnitPlan>& units, const Group& g) {
+  for (int ph = 0; ph < 3; ++ph) {
+    std::vector<std::vector<uint8_t>> cnt(g.units.size());
+    std::vector<int> gr(g.units.size()), gc(g.units.size());
+    for (size_t gi = 0; gi < g.units.size(); ++gi) {
+      const UnitPlan& u = units[g.units[gi]];
+      const int e = tile_edge(u.f32, kTileM);
+      if (u.mp % e || u.np % e) return false;
+      gr[gi] = u.mp / e;
+      gc[gi] = ph == kBX ? u.np / e : u.mp / e;
+      cnt[gi].assign(size_t(gr[gi]) * gc[gi], 0);
+    }
+    for (int tc = 0; tc < kTileCfgs; ++tc)
+      for (const GemmTask& t : g.gemm[ph][tc]) {
+        if (t.unit < 0) continue;
+        if (size_t(t.unit) >= g.units.size()) return false;
+        const UnitPlan& u = units[g.units[t.unit]];
+        const int r = tile_edge(u.f32, tc) / tile_edge(u.f32, kTileM);
+        if (u.f32 && tc != kTileM) return false;
+        for (int bi = t.ti * r; bi < (t.ti + 1) * r; ++bi)
+          for (int bj = t.tj * r; bj < (t.tj + 1) * r; ++bj) {
+            if (bi < 0 || bj < 0 || bi >= gr[t.unit] || bj >= gc[t.unit]) return false;
+            if (ph != kBX && bi > bj) {
+              if (t.ti != t.tj) return false;
+              continue;
+            }
+            if (++cnt[t.unit][size_t(bi) * gc[t.unit] + bj] > 1) return false;
+          }
+      }
+    for (size_t gi = 0; gi < g.units.size(); ++gi)
+      for (int bi = 0; bi < gr[gi]; ++bi)
+        for (int bj = ph == kBX ? 0 : bi; bj < gc[gi]; ++bj)
+          if (cnt[gi][size_t(bi) * gc[gi] + bj] != 1) return false;
+  }
+  return true;
+}
+
 muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_t* pcs, int32_t npc,
                          const muon_hparams_t* hp, Plan& plan, bool single_lane = false) {
   muon_status_t st = validate(ts, n, pcs, npc, hp);
@@ -451,6 +494,8 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
     }
     for (int ph = 0; ph < 3; ++ph)
       for (int tc = 0; tc < kTileCfgs; ++tc) g.gemm[ph][tc] = xcd_order(g.gemm[ph][tc], plan.units, g, ph);
+    if (!tiles_cover_exactly(plan.units, g))
+      return fail(MUON_ERR_UNSUPPORTED, "internal: GEMM tile lists do not cover the outputs exactly once");
   }
   // workspace: metadata first, then the NS buffers
   size_t off = 0;

@@ -245,7 +245,7 @@ def test_plan_large_units_take_256_tiles():
 
 def test_plan_split_rows_and_fp32():
     t = fakes([(3 * 128, 128)])[0]
-    t.split_rows = 128   # 128-row blocks pad to 256 for the B X tile
+    t.split_rows = 128   # three 128 x 128 units (a QKV-style row split)
     f = fake(256, 512, B.MUON_F32, base=BASE + (1 << 30))[0]
     small = fake(17, 33, B.MUON_BF16, base=BASE + (1 << 31))[0]
     plan = mm.plan_describe([t, f, small], mm.default_hparams())
@@ -261,6 +261,38 @@ def test_plan_split_rows_and_fp32():
     assert len(plan["launch_order"]) == 32
     p0 = mm.plan_describe([t], mm.default_hparams(ns_steps=0))
     assert p0["launch_order"] == ["momentum/bf16", "update/bf16"]
+
+
+def test_plan_tiles_cover_every_output_exactly_once():
+    """The planner checks its own GEMM task lists on every plan (every
+    128 x 128 block of a unit's B X output covered exactly once, every block
+    on or above the diagonal of its Gram and square exactly once) and fails
+    the plan otherwise; so planning many seeded random shapes -- ragged,
+    tall and wide, both precisions, row splits, the 256-tile thresholds and
+    the strips past the last whole 256-tile -- must succeed, with the tile
+    counts of each plan consistent with its units."""
+    import random
+    rng = random.Random(7)
+    sizes = [1, 7, 64, 127, 128, 129, 255, 256, 300, 640, 767, 768, 769, 1000, 1024, 1100, 1535, 1536,
+             1600, 2047, 2048, 2100, 2304, 3000, 4096]
+    for case in range(60):
+        shapes, base, ts = [], BASE, []
+        for _ in range(rng.randint(1, 4)):
+            r, c = rng.choice(sizes), rng.choice(sizes)
+            dt = B.MUON_F32 if rng.random() < 0.25 else B.MUON_BF16
+            split = 0
+            if r % 2 == 0 and r >= 256 and rng.random() < 0.3:
+                split = r // 2
+            t, span = fake(r, c, dt, base, split=split)
+            ts.append(t)
+            base += span
+            shapes.append((r, c, dt, split))
+        plan = mm.plan_describe(ts, mm.default_hparams())
+        assert len(plan["units"]) == sum(2 if s else 1 for _, _, _, s in shapes), (case, shapes)
+        for g in plan["groups"]:
+            for k in ("gram", "square", "bx"):
+                assert g[f"{k}_tiles"] == sum(v[("gram", "square", "bx").index(k)]
+                                              for v in g["tiles_by_edge"].values()), (case, shapes)
 
 
 def test_workspace_size_formula():
