@@ -657,9 +657,11 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   constexpr int RITER = 32 * SEGS / 64;
   constexpr int CITER = WTN * 4 / 64;
   static_assert(RITER == CITER, "row and column passes give a lane equally many segments");
-  // Last B X, bf16 weights with aligned rows: each strip's weight segments
-  // (rows of W for a wide unit; columns of the tile, i.e. rows of W, for a
-  // tall one) are requested one strip ahead, the first as the K loop ends.
+  // Last B X, bf16 weights with aligned rows: the weight segments of every
+  // strip (rows of W for a wide unit; columns of the tile, i.e. rows of W,
+  // for a tall one) are requested together as the K loop ends, so the
+  // strips wait on one HBM latency instead of one each (the K loop's
+  // registers are free by then; the epilogue holds NBM * RITER segments).
   const bool wfast = LAST && !F32 && !u.param_f32 && u.vec_param;
   auto wseg = [&](int pi, int q, int ln, int& wi, int& wj) {
     const int sg = ln + 64 * q;
@@ -671,7 +673,7 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
       wj = row_base + pi * 32 + (sg / WTN) * 8;
     }
   };
-  u32x4_t wbuf[2][RITER];
+  u32x4_t wbuf[NBM][RITER];
   auto load_w = [&](int pi, int ln, u32x4_t (&dst)[RITER]) {
 #pragma unroll
     for (int q = 0; q < RITER; ++q) {
@@ -816,7 +818,7 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   }
   }
   const int el = lane_id();   // the epilogue's lane index
-  if (wfast) load_w(0, el, wbuf[0]);
+  if (wfast) static_for<0, NBM>([&](auto pc) { load_w(decltype(pc)::value, el, wbuf[decltype(pc)::value]); });
   if constexpr (PING) {
     // nothing in flight, every read of the ring done: group 0 passed the
     // last barrier after group 1's last reads, and group 1 (in its last
@@ -878,9 +880,6 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
     // strip by strip: a later strip's accumulators stay in the AGPRs until
     // its turn (reading them all out at once would exceed the VGPRs)
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (pi + 1 < NBM) {
-      if (wfast) load_w(pi + 1, el, wbuf[(pi + 1) & 1]);
-    }
     if constexpr (pi > 0) wave_sync();      // the previous strip's reads are done
 #pragma unroll
     for (int j = 0; j < NBN; ++j) {
@@ -914,7 +913,7 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
         else gst(static_cast<uint16_t*>(out_xh) + static_cast<size_t>(gr) * np + gc, pack8_hi(v));
       } else if (u.side == kLeft) {
         if (gr < wu.rows) {
-          if (wfast && gc + 8 <= wu.cols) update_w8_loaded(wu, gr, gc, v, decay, step, wbuf[pi & 1][q]);
+          if (wfast && gc + 8 <= wu.cols) update_w8_loaded(wu, gr, gc, v, decay, step, wbuf[pi][q]);
           else update_w8(wu, gr, gc, v, decay, step);
         }
       }
@@ -935,7 +934,7 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
         } else if constexpr (LAST) {
           // tall matrix: O[i][j] = X[j][i], so X column gc is weight row gc
           if (gc < wu.rows) {
-            if (!F32 && wfast && gr + 8 <= wu.cols) update_w8_loaded(wu, gc, gr, v, decay, step, wbuf[pi & 1][q]);
+            if (!F32 && wfast && gr + 8 <= wu.cols) update_w8_loaded(wu, gc, gr, v, decay, step, wbuf[pi][q]);
             else update_w8(wu, gc, gr, v, decay, step);
           }
         }
