@@ -77,8 +77,9 @@ __device__ __forceinline__ void unpack8_bf16(const u32x4_t& w, float* v) {
   }
 }
 
-// Two-part X master of the bf16 Newton-Schulz path: hi = bf16(x) (the MFMA
-// operand) and an int8 correction q counted in the float32 bit pattern,
+// Two-part X master of the bf16 Newton-Schulz path: hi = x rounded to bf16
+// (the MFMA operand; here to nearest even) and an int8 correction q counted
+// in the float32 bit pattern,
 // x ~= float_from_bits(bits(hi) + 256 q).  Within hi's binade 256 float32
 // ulps are ulp_bf16(hi)/256, so q carries 8 more bits below hi's last one
 // (round-to-nearest-even gives |bits(x) - bits(hi)| <= 2^15, so |q| <= 128,

@@ -6,7 +6,8 @@
 //             Muon README "Usage"
 // then per NS-precision group, all matrices of the group at once:
 //   momentum  (1 launch)      Muon README "Hyperparameter tuning"
-//   ns_steps x {gram, square, bx}  (3 launches each)   Muon blog sec. 3;
+//   ns_steps x {gram, square, bx}  (per phase one launch per tile shape,
+//             on each lane's stream)   Muon blog sec. 3;
 //             the last bx applies the update (Muon README "Usage")
 //   update    (1 launch, only when ns_steps == 0)
 #include <hip/hip_runtime.h>

@@ -49,14 +49,16 @@ struct UnitDev {
   int32_t rows, cols;        // stored shape of the unit
   int32_t side, m, n, mp, np, pad2;
   // workspace buffers (row-major, leading dimension np for X, mp for A/B).
-  // bf16 NS: xh is bf16(X) (also the MFMA operand) and xl one int8
-  // correction per element (X ~= the float32 with bits(xh) + 256 xl, i.e.
-  // xh + xl * ulp(xh)/256 within xh's binade), stored in 32 x 32 blocks in
-  // the MFMA accumulator order (corr_index in device_common.h); a and b are
-  // bf16.
-  // float32 NS: xh is the float32 X, xl is unused, a and b are float32.  xh is double-buffered: the B X phase reads
-  // the whole current iterate as an operand while its tiles write the next
-  // one; xl is read and written only by the tile that owns each region.
+  // bf16 NS: xh is X rounded to bf16 (the MFMA operand; nearest-even as the
+  // momentum phase writes it, half-up just below the tie as B X writes it)
+  // and xl one int8 correction per element counted against that xh (X ~=
+  // the float32 with bits(xh) + 256 xl, i.e. xh + xl * ulp(xh)/256 within
+  // xh's binade), stored in 32 x 32 blocks in the MFMA accumulator order
+  // (corr_index in device_common.h); a and b are bf16.
+  // float32 NS: xh is the float32 X, xl is unused, a and b are float32.
+  // xh is double-buffered: the B X phase reads the whole current iterate as
+  // an operand while its tiles write the next one; xl is read and written
+  // only by the tile that owns each region.
   void* xh[2]; void* xl; void* a; void* b;
   float* partials;           // one partial sum of squares per momentum tile
   float* norm;               // 1 / (||U||_F + eps), folded by the first Gram phase
