@@ -28,6 +28,11 @@ HIP_FLAGS = [
 ]
 
 
+# roctx (named host-side ranges for rocprofv3's marker trace)
+ROCM_LIB = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
+LINK_FLAGS = [f"-L{ROCM_LIB}", f"-Wl,-rpath,{ROCM_LIB}", "-lrocprofiler-sdk-roctx"]
+
+
 def _hipcc():
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -64,7 +69,7 @@ def build(verbose=False, extra_flags=(), out=None, objdir=None):
     with ThreadPoolExecutor(max_workers=min(len(cmds), 4)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = lib + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *LINK_FLAGS, "-o", tmp], verbose)
     os.replace(tmp, lib)
     return lib
 

@@ -11,6 +11,7 @@
 //             the last bx applies the update (Muon README "Usage")
 //   update    (1 launch, only when ns_steps == 0)
 #include <hip/hip_runtime.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include <algorithm>
 #include <cmath>
@@ -28,6 +29,16 @@ using namespace muon;
 namespace {
 
 thread_local std::string g_last_error;
+
+// A host-side range naming the launches it encloses, for rocprofv3's marker
+// trace (`--marker-trace`); with no tool attached a push and a pop cost a few
+// tens of nanoseconds.
+struct Range {
+  explicit Range(const char* name) { roctxRangePushA(name); }
+  ~Range() { roctxRangePop(); }
+  Range(const Range&) = delete;
+  Range& operator=(const Range&) = delete;
+};
 
 muon_status_t fail(muon_status_t s, const std::string& msg) {
   g_last_error = msg;
@@ -689,8 +700,10 @@ muon_status_t enqueue_step(muon_handle_t h, float lr, hipStream_t s, std::vector
     if (!ev) return true;
     return hipEventRecord((*ev)[ek++], s) == hipSuccess;
   };
+  Range step_range("muon.step");
   if (!mark()) return fail(MUON_ERR_HIP, "hipEventRecord failed");
   if (!plan.apply.empty()) {
+    Range r("muon.precond_apply");
     hipError_t e = launch_precond_apply(reinterpret_cast<const PrecondDev*>(h->ws + plan.off_pdev),
                                         reinterpret_cast<const ApplyTask*>(h->ws + plan.off_apply),
                                         plan.apply_bf16, int(plan.apply.size()) - plan.apply_bf16, s);
@@ -710,6 +723,7 @@ muon_status_t enqueue_step(muon_handle_t h, float lr, hipStream_t s, std::vector
       return fail(MUON_ERR_HIP, "lane fork failed");
   }
   auto launch_adam = [&](hipStream_t as) -> muon_status_t {
+    Range r("muon.adamw");
     AdamState* st = reinterpret_cast<AdamState*>(h->ws + plan.off_adam_state);
     hipError_t e = launch_adam_tick(st, hp.adam_beta1, hp.adam_beta2, as);
     AdamParams ap{hp.adam_lr, hp.adam_beta1, hp.adam_beta2, hp.adam_eps, hp.adam_weight_decay, st,
@@ -735,8 +749,11 @@ muon_status_t enqueue_step(muon_handle_t h, float lr, hipStream_t s, std::vector
     const UnitDev* units = reinterpret_cast<const UnitDev*>(h->ws + g.off_units);
     K1Params k1{hp.momentum, hp.nesterov, hp.momentum_form == MUON_MOM_SGD,
                 reinterpret_cast<uint32_t*>(h->ws + plan.off_flags)};
-    hipError_t e = launch_momentum(g.f32, units, reinterpret_cast<const EwTask*>(h->ws + g.off_ew),
-                                   int(g.ew.size()), k1, gs);
+    hipError_t e;
+    {
+      Range r("muon.momentum");
+      e = launch_momentum(g.f32, units, reinterpret_cast<const EwTask*>(h->ws + g.off_ew), int(g.ew.size()), k1, gs);
+    }
     if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("momentum launch: ") + hipGetErrorString(e));
     if (adam_pending && g.lane == 0) {
       if (hipEventRecord(h->ev_adam, gs) != hipSuccess || hipStreamWaitEvent(h->aux_stream, h->ev_adam, 0) != hipSuccess)
@@ -752,14 +769,19 @@ muon_status_t enqueue_step(muon_handle_t h, float lr, hipStream_t s, std::vector
         for (int tc : kLaunchOrder) {   // the 256-row tiles (the longer launches) first
           const std::vector<GemmTask>& tl = g.gemm[ph][tc];
           if (tl.empty()) continue;
-          e = launch_gemm(ph, g.f32, tc, units, reinterpret_cast<const GemmTask*>(h->ws + g.off_gemm[ph][tc]),
-                          int(tl.size()), gp, gs);
+          {
+            static const char* const kRangeNames[3] = {"muon.gram", "muon.square", "muon.bx"};
+            Range r(kRangeNames[ph]);
+            e = launch_gemm(ph, g.f32, tc, units, reinterpret_cast<const GemmTask*>(h->ws + g.off_gemm[ph][tc]),
+                            int(tl.size()), gp, gs);
+          }
           if (e != hipSuccess || !mark())
             return fail(MUON_ERR_HIP, std::string(kPhaseNames[ph]) + " launch: " + hipGetErrorString(e));
         }
     }
     if (hp.ns_steps == 0) {   // otherwise the last B X phase applies the update
       K5Params k5{lr, hp.weight_decay, hp.eps, 0};
+      Range r("muon.update");
       e = launch_update(g.f32, units, reinterpret_cast<const EwTask*>(h->ws + g.off_ew), int(g.ew.size()), k5, gs);
       if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("update launch: ") + hipGetErrorString(e));
     }
@@ -1148,6 +1170,7 @@ muon_status_t muon_precond_accumulate(muon_handle_t h, int32_t slot, int32_t blo
   if ((st = check_acts(sp, acts, n_rows, ld, dtype)) != MUON_OK) return st;
   if (!(beta >= 0.f && beta <= 1.f)) return fail(MUON_ERR_BAD_ARG, "beta must be in [0, 1]");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  Range r("muon.precond_accumulate");
   hipError_t e = launch_precond_accumulate(block_dev(h, sp, block), acts, n_rows, ld, dtype == MUON_F32, beta, s);
   if (e != hipSuccess) return fail(MUON_ERR_HIP, std::string("precond accumulate launch: ") + hipGetErrorString(e));
   h->last_stream = s;
@@ -1160,6 +1183,7 @@ muon_status_t muon_precond_refresh_accumulated(muon_handle_t h, int32_t slot, in
   if (st != MUON_OK) return st;
   if (!std::isfinite(damping) || damping < 0.f) return fail(MUON_ERR_BAD_ARG, "damping must be finite and >= 0");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  Range r("muon.precond_refresh_accumulated");
   hipError_t e = launch_precond_refresh_accumulated(block_dev(h, h->plan.slots[size_t(slot)], block), damping,
                                                     reset != 0,
                                                     reinterpret_cast<uint32_t*>(h->ws + h->plan.off_flags), s);
@@ -1176,6 +1200,7 @@ muon_status_t muon_precond_refresh(muon_handle_t h, int32_t slot, int32_t block,
   if ((st = check_acts(sp, acts, n_rows, ld, dtype)) != MUON_OK) return st;
   if (!std::isfinite(damping) || damping < 0.f) return fail(MUON_ERR_BAD_ARG, "damping must be finite and >= 0");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  Range r("muon.precond_refresh");
   hipError_t e = launch_precond_refresh(block_dev(h, sp, block), acts, n_rows, ld, dtype == MUON_F32, damping,
                                         reinterpret_cast<uint32_t*>(h->ws + h->plan.off_flags), s);
   if (e != hipSuccess) return fail(MUON_ERR_HIP, std::string("precond refresh launch: ") + hipGetErrorString(e));

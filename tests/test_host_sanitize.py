@@ -58,7 +58,7 @@ def driver(tmp_path_factory):
     nm = _run(["nm", "-u", objs[0]]).stdout
     assert "__asan_report_load" in nm and "__ubsan_handle_" in nm
     exe = str(d / "planner_san")
-    _run([HIPCC, f"--offload-arch={BLD.ARCH}", *SAN, *objs, "-o", exe])
+    _run([HIPCC, f"--offload-arch={BLD.ARCH}", *SAN, *objs, *BLD.LINK_FLAGS, "-o", exe])
     return exe
 
 
