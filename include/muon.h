@@ -248,7 +248,9 @@ muon_status_t muon_get_adam_step(muon_handle_t h, void* stream, int64_t* steps_t
 
 /* Synchronises `stream` and returns the sticky flag word:
  * bit 0 = a non-finite value was seen in an update, bit 1 = a
- * preconditioner factorisation failed.  reset != 0 clears it. */
+ * preconditioner factorisation failed, bit 2 = (only in a library built
+ * with MUON_DEBUG_BOUNDS=1) a kernel task failed its bounds check and was
+ * skipped.  reset != 0 clears it. */
 muon_status_t muon_get_flags(muon_handle_t h, void* stream, int32_t reset, uint32_t* flags);
 
 /* Synchronises the last stream used and frees the host handle. */

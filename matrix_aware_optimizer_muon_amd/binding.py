@@ -270,13 +270,16 @@ class MuonStep:
     """
 
     def __init__(self, descs: Sequence[MuonTensor], hp: Optional[MuonHparams] = None,
-                 preconds: Sequence[MuonPrecond] = (), device=None, keepalive=(), static_scratch=False):
+                 preconds: Sequence[MuonPrecond] = (), device=None, keepalive=(), static_scratch=False,
+                 library: Optional[str] = None):
         """static_scratch=True binds the handle to the library's static
         device scratch (muon_init_static): no workspace is allocated, the
         request must fit in it, and a later static handle on the same GPU
-        supersedes this one."""
+        supersedes this one.  `library`: path of another build of the
+        library to run this handle on (e.g. the bounds-checking debug build,
+        build.DEBUG_LIB); default the one load_library() returns."""
         torch = _torch()
-        self._lib = load_library()
+        self._lib = load_library(library)
         self.hp = hp if hp is not None else default_hparams()
         self._descs, self._n = _array(list(descs), MuonTensor)
         self._pcs, self._npc = _array(list(preconds), MuonPrecond)

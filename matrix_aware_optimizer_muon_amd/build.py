@@ -15,6 +15,11 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(CSRC, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libmuon.so")
+# debug build: every GEMM and elementwise task checks its tile against the
+# unit's padded sizes and sets flag bit 2 instead of running out of bounds
+DEBUG_LIB = os.path.join(LIBDIR, "libmuon_debug.so")
+DEBUG_OBJ = os.path.join(CSRC, "_build_debug")
+DEBUG_FLAGS = ["-DMUON_DEBUG_BOUNDS=1"]
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 
 SOURCES = ["muon_host.cpp", "elementwise.hip", "ns_gemm.hip", "precond.hip", "adamw.hip"]
@@ -74,5 +79,11 @@ def build(verbose=False, extra_flags=(), out=None, objdir=None):
     return lib
 
 
+def build_debug(verbose=False):
+    """The bounds-checking variant, lib/libmuon_debug.so."""
+    return build(verbose=verbose, extra_flags=DEBUG_FLAGS, out=DEBUG_LIB, objdir=DEBUG_OBJ)
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_debug(verbose="-v" in sys.argv))

@@ -38,6 +38,16 @@ constexpr int kLeftPitch = kEwCols + 8;
 constexpr int kTileFloats = kEwRRows * kRightPitch > kEwRows * kLeftPitch ? kEwRRows * kRightPitch
                                                                           : kEwRows * kLeftPitch;
 
+// Debug builds: an elementwise tile starts inside its unit, and the X rows
+// (left side) or X columns (right side) it writes stay inside the padded
+// master.
+__device__ __forceinline__ bool ew_tile_in_bounds(const UnitDev& u, const EwTask& t) {
+  const bool left = u.side == kLeft;
+  const int r0 = t.tr * (left ? kEwRows : kEwRRows), c0 = t.tc * (left ? kEwCols : kEwRCols);
+  if (t.tr < 0 || t.tc < 0 || r0 >= u.rows || c0 >= u.cols) return false;
+  return left ? r0 + kEwRows <= u.mp : r0 + kEwRRows <= u.np;
+}
+
 // Store one 8-element row segment of X: the bf16 hi part of the master (its
 // int8 corrections are written separately, in their blocked layout), or the
 // float32 value.
@@ -219,6 +229,12 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const UnitDev* __res
   __shared__ float wsum[kThreads / 64];
   const EwTask t = tasks[blockIdx.x];
   const UnitDev& u = units[t.unit];
+  if constexpr (MUON_DEBUG_BOUNDS) {
+    if (!ew_tile_in_bounds(u, t)) {
+      if (threadIdx.x == 0) atomicOr(p.flags, kFlagBounds);
+      return;
+    }
+  }
   if (u.grad_f32) momentum_tile<F32, true>(u, t, p, tile, wsum);
   else momentum_tile<F32, false>(u, t, p, tile, wsum);
 }
@@ -249,6 +265,12 @@ __global__ __launch_bounds__(kThreads) void update_kernel(const UnitDev* __restr
   __shared__ float red[4];
   const EwTask t = tasks[blockIdx.x];
   const UnitDev& u = units[t.unit];
+  if constexpr (MUON_DEBUG_BOUNDS) {
+    if (!ew_tile_in_bounds(u, t)) {
+      if (threadIdx.x == 0) atomicOr(p.flags, kFlagBounds);
+      return;
+    }
+  }
   const bool left = u.side == kLeft;
   const int r0 = t.tr * (left ? kEwRows : kEwRRows), c0 = t.tc * (left ? kEwCols : kEwRCols);
   const int seg_sh = left ? 5 : 4;                   // log2 of 8-element segments per tile row

@@ -764,7 +764,7 @@ muon_status_t enqueue_step(muon_handle_t h, float lr, hipStream_t s, std::vector
     }
     for (int it = 0; it < hp.ns_steps; ++it) {
       GemmParams gp{hp.ns_a, hp.ns_b, hp.ns_c, hp.eps, it == 0, it == hp.ns_steps - 1, it & 1, 0,
-                    lr, hp.weight_decay};
+                    lr, hp.weight_decay, reinterpret_cast<uint32_t*>(h->ws + plan.off_flags)};
       for (int ph = 0; ph < 3; ++ph)
         for (int tc : kLaunchOrder) {   // the 256-row tiles (the longer launches) first
           const std::vector<GemmTask>& tl = g.gemm[ph][tc];
@@ -780,7 +780,7 @@ muon_status_t enqueue_step(muon_handle_t h, float lr, hipStream_t s, std::vector
         }
     }
     if (hp.ns_steps == 0) {   // otherwise the last B X phase applies the update
-      K5Params k5{lr, hp.weight_decay, hp.eps, 0};
+      K5Params k5{lr, hp.weight_decay, hp.eps, 0, reinterpret_cast<uint32_t*>(h->ws + plan.off_flags)};
       Range r("muon.update");
       e = launch_update(g.f32, units, reinterpret_cast<const EwTask*>(h->ws + g.off_ew), int(g.ew.size()), k5, gs);
       if (e != hipSuccess || !mark()) return fail(MUON_ERR_HIP, std::string("update launch: ") + hipGetErrorString(e));

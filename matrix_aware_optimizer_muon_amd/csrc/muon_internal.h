@@ -86,6 +86,7 @@ struct GemmParams {
   int32_t pad;
   float lr;            // weight update of the last iteration
   float weight_decay;
+  uint32_t* flags;     // the handle's flag word (bounds checks of a debug build)
 };
 
 struct K5Params {      // stand-alone update, used when ns_steps == 0
@@ -93,7 +94,16 @@ struct K5Params {      // stand-alone update, used when ns_steps == 0
   float weight_decay;
   float eps;
   int32_t pad;
+  uint32_t* flags;     // the handle's flag word (bounds checks of a debug build)
 };
+
+// Flag word bits (muon_get_flags): 1 = a non-finite value in an update,
+// 2 = a preconditioner factorisation failed, 4 = a task of a build with
+// MUON_DEBUG_BOUNDS=1 failed its bounds check (the task was skipped).
+constexpr uint32_t kFlagBounds = 4u;
+#ifndef MUON_DEBUG_BOUNDS
+#define MUON_DEBUG_BOUNDS 0
+#endif
 
 enum Phase : int32_t { kGram = 0, kSquare = 1, kBX = 2 };
 

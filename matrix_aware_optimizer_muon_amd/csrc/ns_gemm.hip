@@ -538,6 +538,17 @@ void ns_gemm_kernel(const UnitDev* __restrict__ units, const GemmTask* __restric
   const UnitDev& u = units[t.unit];
   const int mp = u.mp, np = u.np;
   const int ti = t.ti, tj = t.tj;
+  if constexpr (MUON_DEBUG_BOUNDS) {
+    // debug build: the tile and its K extent lie inside the unit's padded
+    // operands, and the symmetric products list upper tiles only
+    const int out_cols = PH == kBX ? np : mp, kext = PH == kGram ? np : mp;
+    const bool ok = ti >= 0 && tj >= 0 && (ti + 1) * BTM <= mp && (tj + 1) * BTN <= out_cols && kext >= BK &&
+                    kext % BK == 0 && (PH == kBX || ti <= tj);
+    if (!ok) {
+      if (threadIdx.x == 0) atomicOr(p.flags, kFlagBounds);
+      return;
+    }
+  }
 
   // The epilogue's scale, known before the K loop (so no control flow
   // joins while the accumulators are live).  The first Gram folds the
