@@ -15,6 +15,7 @@ _ORIG_NS = orc.newton_schulz
 _ORIG_NORM = orc.frobenius_normalise
 _ORIG_MOM = orc.momentum_update
 _ORIG_ORTHO = orc.orthogonalise
+_ORIG_APPLY = orc.apply_update
 
 
 def _ns_coeffs(a_f, b_f, c_f):
@@ -104,7 +105,13 @@ def _adam_betas_swapped(W, G, M, V, t, lr=orc.DEFAULT_ADAM_LR, betas=orc.DEFAULT
     return _ORIG_ADAM(W, G, M, V, t, lr, (betas[1], betas[0]), eps, weight_decay)
 
 
+def _muon_decay_after_update(W, O, lr, weight_decay, scale):
+    W1 = _ORIG_APPLY(W, O, lr, 0.0, scale)
+    return W1 - lr * weight_decay * W1
+
+
 MUTANTS = {
+    "muon_decay_after_update": ("apply_update", _muon_decay_after_update),
     "adam_no_bias_correction": ("adamw_update", _adam_no_bias_correction),
     "adam_eps_inside_sqrt": ("adamw_update", _adam_eps_in_sqrt),
     "adam_decay_after_update": ("adamw_update", _adam_decay_after_update),
@@ -129,6 +136,7 @@ PIN_TESTS = [
     pins.test_transpose_equivariance,
     pins.test_momentum_geometric_series,
     pins.test_split_rows_blocks_are_independent,
+    pins.test_update_decays_the_pre_update_weight,
     pins.test_adamw_first_step_is_a_signed_step,
     pins.test_adamw_constant_gradient_keeps_the_signed_step,
     pins.test_adamw_first_moment_off_sees_every_gradient_alone,

@@ -239,6 +239,23 @@ def test_update_special_cases():
     assert np.abs((W - rw["W"]) - 0.02 * rw["scale"][:, None] * rw["O"]).max() < 1e-16
 
 
+def test_update_decays_the_pre_update_weight():
+    """Reading R4 (decoupled decay on the pre-update weight), with lr, wd and
+    the gradient all nonzero: W' = (1 - lr*wd) W - lr*scale*O to rounding.
+    Applying the decay after the step instead differs by lr^2*wd*scale*O
+    (here about 4e-6 |O|), far above the 1e-13 bar.  The pages do not fix
+    the order, so this pins the oracle to the documented reading only."""
+    rng = np.random.default_rng(31)
+    W = rng.standard_normal((12, 20)) * 0.02
+    G = rng.standard_normal((12, 20))
+    M = rng.standard_normal((12, 20)) * 0.01
+    lr, wd = 0.02, 0.01
+    r = orc.muon_step(W, G, M, lr=lr, weight_decay=wd)
+    expect = (1.0 - lr * wd) * W - lr * r["scale"][:, None] * r["O"]
+    assert np.abs(r["W"] - expect).max() < 1e-13
+    assert np.abs(r["W"] - W).max() > 1e-5          # the update is not trivial
+
+
 def test_split_rows_blocks_are_independent():
     rng = np.random.default_rng(29)
     G = rng.standard_normal((3 * 8, 8))
