@@ -496,6 +496,31 @@ muon_status_t build_plan(const muon_tensor_t* ts, int32_t n, const muon_precond_
       plan.groups.push_back(std::move(lg[l]));
     }
   }
+  // Small phases take 128-tiles.  A group's phase with fewer 256-tiles than
+  // CUs runs them as one partial round, one block per CU; when the same
+  // phase as 128-tiles fits in one round of the chip's block slots (two per
+  // CU), those finish in about half the time, a 256-tile being four
+  // 128-tiles' work on one CU.  (The Newton-Muon layer's six 768-row units,
+  // 36 square and 108 B X 256-tiles: 1985 steps/s with them.)  Larger
+  // phases keep the per-unit choice.
+  constexpr int64_t kCUs = 256, kSlots128 = 2 * kCUs;
+  for (Group& g : plan.groups) {
+    if (g.f32 || MUON_TILE_POLICY != 0) continue;
+    for (int ph = 0; ph < 3; ++ph) {
+      int64_t n256 = 0, n128 = 0;   // the phase's 256-tiles, and its 128-tiles were every unit to take them
+      for (int k : g.units) {
+        const UnitPlan& u = plan.units[k];
+        const int64_t rm = u.mp / kTileEdgeM, rn = (ph == kBX ? u.np : u.mp) / kTileEdgeM;
+        n128 += ph == kBX ? rm * rn : rm * (rm + 1) / 2;
+        if (u.tile[ph] == kTileL) {
+          const int64_t lm = u.mp / kTileEdgeL, ln = (ph == kBX ? u.np : u.mp) / kTileEdgeL;
+          n256 += ph == kBX ? lm * ln : lm * (lm + 1) / 2;
+        }
+      }
+      if (n256 > 0 && n256 < kCUs && n128 <= kSlots128)
+        for (int k : g.units) plan.units[k].tile[ph] = kTileM;
+    }
+  }
   // tile lists
   for (Group& g : plan.groups) {
     for (size_t gi = 0; gi < g.units.size(); ++gi) {

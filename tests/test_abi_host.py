@@ -263,6 +263,20 @@ def test_plan_split_rows_and_fp32():
     assert p0["launch_order"] == ["momentum/bf16", "update/bf16"]
 
 
+def test_plan_small_phases_take_128_tiles():
+    # A group's phase with fewer 256-tiles than CUs whose 128-tiles fit in
+    # one round of the 512 block slots takes 128-tiles: the Newton-Muon
+    # layer's six 768-row units (36 square and 108 B X 256-tiles) run on
+    # 128-tiles in every phase; GPT-2-small's lanes (216 square 256-tiles
+    # each, 756 as 128-tiles) and the 4096^2 matrix (136 / 544) keep 256
+    plan = mm.plan_describe(_workload_fakes("nmuon"), mm.default_hparams())
+    assert all(u["tiles"] == [128] * 3 for u in plan["units"] if u["ns"] == "bf16")
+    assert plan["groups"][0]["tiles_by_edge"] == {"128": [6 * 21, 6 * 21, 4 * 36 + 2 * 144]}
+    assert all(u["tiles"] == [128, 256, 256] for u in mm.plan_describe(_workload_fakes("gpt2s"),
+                                                                       mm.default_hparams())["units"])
+    assert mm.plan_describe(fakes([(4096, 4096)]), mm.default_hparams())["units"][0]["tiles"] == [256] * 3
+
+
 def test_plan_tiles_cover_every_output_exactly_once():
     """The planner checks its own GEMM task lists on every plan (every
     128 x 128 block of a unit's B X output covered exactly once, every block

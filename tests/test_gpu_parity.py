@@ -233,11 +233,15 @@ def test_large_ragged_256_tiles():
     # whole 256-tile is covered by 128-tiles (a row and a column strip for
     # the Gram and square, mirror-stored; a row strip for B X); a tall
     # matrix (the last B X writes weight rows from tile columns) and an exact
-    # multiple of the tile
-    shapes = [(2100, 2300), (2300, 2100), (2048, 2048)]
+    # multiple of the tile; enough units that no phase counts as small (the
+    # planner gives a phase that fits one round of 128-tiles 128-tiles)
+    shapes = [(2100, 2300), (2300, 2100), (2048, 2048), (2100, 2500)]
     say("case: large ragged bf16 (256 x 256 tiles)")
     wl = adhoc("large", shapes, "bf16")
     c = Case(wl, wl.tensors)
+    plan = mm.plan_describe(c.descs(), mm.default_hparams())
+    assert [u["tiles"] for u in plan["units"]] == [[256] * 3] * 4
+    assert all(v > 0 for v in plan["groups"][0]["tiles_by_edge"]["128"])   # the strips past 2048
     hp = mm.default_hparams()
     assert c.run(hp) == 0
     w = check(c, hp, label="large/256")
@@ -247,14 +251,15 @@ def test_large_ragged_256_tiles():
 def test_mid_ragged_mixed_tiles():
     # mid-sized short sides: B X at 256 x 256 with 128-tile strips past the
     # last whole 256-tile (1000 x 1100: a column strip; 1100 x 1000 tall: the
-    # column strip holds weight rows), the Gram and square at 128; 1600 x
-    # 1700: the Gram at 256 with its 128-strip too, the square at 128
-    shapes = [(1000, 1100), (1100, 1000), (1600, 1700)]
+    # column strip holds weight rows), the Gram and square at 128; the
+    # 1600-row units: the Gram at 256 with its 128-strip too, the square at
+    # 128.  Seven units (one lane), so that no phase counts as small.
+    shapes = [(1000, 1100), (1100, 1000), (1600, 1700), (1700, 1600), (1600, 3000), (1600, 1700), (1700, 1600)]
     say("case: mid ragged bf16 (256- and 128-tiles in one phase)")
     wl = adhoc("mid", shapes, "bf16")
     c = Case(wl, wl.tensors)
     plan = mm.plan_describe(c.descs(), mm.default_hparams())
-    assert [u["tiles"] for u in plan["units"]] == [[128, 128, 256]] * 2 + [[256, 128, 256]]
+    assert [u["tiles"] for u in plan["units"]] == [[128, 128, 256]] * 2 + [[256, 128, 256]] * 5
     hp = mm.default_hparams()
     assert c.run(hp) == 0
     w = check(c, hp, label="mid/mixed")
