@@ -147,8 +147,10 @@ def _array(items, cls):
 
 
 def workspace_size(tensors: Sequence[MuonTensor], hp: MuonHparams,
-                   preconds: Sequence[MuonPrecond] = ()) -> int:
-    lib = load_library()
+                   preconds: Sequence[MuonPrecond] = (), lib: Optional[ctypes.CDLL] = None) -> int:
+    """Workspace bytes a handle over these tensors needs (with `lib`, as
+    that build of the library plans them)."""
+    lib = lib or load_library()
     ta, n = _array(tensors, MuonTensor)
     pa, npc = _array(preconds, MuonPrecond)
     out = ctypes.c_size_t(0)
@@ -280,21 +282,22 @@ class MuonStep:
         build.DEBUG_LIB); default the one load_library() returns."""
         torch = _torch()
         self._lib = load_library(library)
+        self._check = lambda status: _check(status, self._lib)   # error text from this handle's library
         self.hp = hp if hp is not None else default_hparams()
         self._descs, self._n = _array(list(descs), MuonTensor)
         self._pcs, self._npc = _array(list(preconds), MuonPrecond)
-        self.workspace_bytes = workspace_size(descs, self.hp, preconds)
+        self.workspace_bytes = workspace_size(descs, self.hp, preconds, lib=self._lib)
         self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
         self._keep = list(keepalive)
         h = ctypes.c_void_p()
         if static_scratch:
             self.workspace = None
             with torch.cuda.device(self.device):
-                _check(self._lib.muon_init_static(ctypes.byref(h), self._descs, self._n, self._pcs, self._npc,
+                self._check(self._lib.muon_init_static(ctypes.byref(h), self._descs, self._n, self._pcs, self._npc,
                                                   ctypes.byref(self.hp), self._stream(None)))
         else:
             self.workspace = torch.empty(max(self.workspace_bytes, 256), dtype=torch.uint8, device=self.device)
-            _check(self._lib.muon_init(ctypes.byref(h), self._descs, self._n, self._pcs, self._npc,
+            self._check(self._lib.muon_init(ctypes.byref(h), self._descs, self._n, self._pcs, self._npc,
                                        ctypes.byref(self.hp), ctypes.c_void_p(self.workspace.data_ptr()),
                                        self.workspace.numel(), self._stream(None)))
         self._h = h
@@ -322,7 +325,7 @@ class MuonStep:
         return plan_describe(descs, self.hp, pcs)
 
     def step(self, lr: float = -1.0, stream=None):
-        _check(self._lib.muon_step(self._h, ctypes.c_float(lr), self._stream(stream)))
+        self._check(self._lib.muon_step(self._h, ctypes.c_float(lr), self._stream(stream)))
 
     def step_timed(self, lr: float = -1.0, stream=None):
         """Run one step with HIP events between launches; returns
@@ -330,7 +333,7 @@ class MuonStep:
         cap = 4096
         ms = (ctypes.c_float * cap)()
         n = ctypes.c_int32(0)
-        _check(self._lib.muon_step_timed(self._h, ctypes.c_float(lr), self._stream(stream), ms, cap,
+        self._check(self._lib.muon_step_timed(self._h, ctypes.c_float(lr), self._stream(stream), ms, cap,
                                          ctypes.byref(n)))
         return [(self._lib.muon_phase_name(self._h, i).decode(), ms[i]) for i in range(min(n.value, cap))]
 
@@ -342,7 +345,7 @@ class MuonStep:
         if dt is None:
             raise ValueError(f"unsupported activation dtype {acts.dtype}")
         s = self._torch_stream(stream)
-        _check(self._lib.muon_precond_refresh(self._h, slot, block, ctypes.c_void_p(acts.data_ptr()),
+        self._check(self._lib.muon_precond_refresh(self._h, slot, block, ctypes.c_void_p(acts.data_ptr()),
                                               acts.shape[0], acts.stride(0), dt, ctypes.c_float(damping),
                                               ctypes.c_void_p(s.cuda_stream)))
         self._guard(acts, s)
@@ -357,7 +360,7 @@ class MuonStep:
         if dt is None:
             raise ValueError(f"unsupported activation dtype {acts.dtype}")
         s = self._torch_stream(stream)
-        _check(self._lib.muon_precond_accumulate(self._h, slot, block, ctypes.c_void_p(acts.data_ptr()),
+        self._check(self._lib.muon_precond_accumulate(self._h, slot, block, ctypes.c_void_p(acts.data_ptr()),
                                                  acts.shape[0], acts.stride(0), dt, ctypes.c_float(beta),
                                                  ctypes.c_void_p(s.cuda_stream)))
         self._guard(acts, s)
@@ -365,27 +368,27 @@ class MuonStep:
     def precond_refresh_accumulated(self, slot: int, block: int, damping: float = 1e-4, reset: bool = True,
                                     stream=None):
         """Rebuild S^-1 of (slot, block) from its running second moment."""
-        _check(self._lib.muon_precond_refresh_accumulated(self._h, slot, block, ctypes.c_float(damping),
+        self._check(self._lib.muon_precond_refresh_accumulated(self._h, slot, block, ctypes.c_float(damping),
                                                           int(reset), self._stream(stream)))
 
     def set_adam_step(self, steps_taken: int, stream=None):
         """Resume the AdamW step count (steps already taken)."""
-        _check(self._lib.muon_set_adam_step(self._h, int(steps_taken), self._stream(stream)))
+        self._check(self._lib.muon_set_adam_step(self._h, int(steps_taken), self._stream(stream)))
 
     def adam_step(self, stream=None) -> int:
         """AdamW steps taken so far (synchronises the stream)."""
         v = ctypes.c_int64(0)
-        _check(self._lib.muon_get_adam_step(self._h, self._stream(stream), ctypes.byref(v)))
+        self._check(self._lib.muon_get_adam_step(self._h, self._stream(stream), ctypes.byref(v)))
         return v.value
 
     def flags(self, reset: bool = False, stream=None) -> int:
         v = ctypes.c_uint32(0)
-        _check(self._lib.muon_get_flags(self._h, self._stream(stream), int(reset), ctypes.byref(v)))
+        self._check(self._lib.muon_get_flags(self._h, self._stream(stream), int(reset), ctypes.byref(v)))
         return v.value
 
     def close(self):
         if getattr(self, "_h", None):
-            _check(self._lib.muon_destroy(self._h))
+            self._check(self._lib.muon_destroy(self._h))
             self._h = None
 
     def __del__(self):
