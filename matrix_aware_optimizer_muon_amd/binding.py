@@ -282,7 +282,6 @@ class MuonStep:
         build.DEBUG_LIB); default the one load_library() returns."""
         torch = _torch()
         self._lib = load_library(library)
-        self._check = lambda status: _check(status, self._lib)   # error text from this handle's library
         self.hp = hp if hp is not None else default_hparams()
         self._descs, self._n = _array(list(descs), MuonTensor)
         self._pcs, self._npc = _array(list(preconds), MuonPrecond)
@@ -323,6 +322,10 @@ class MuonStep:
         descs = [self._descs[i] for i in range(self._n)]
         pcs = [self._pcs[i] for i in range(self._npc)]
         return plan_describe(descs, self.hp, pcs)
+
+    def _check(self, status):
+        """Raise on a non-zero status with the error text of this handle's own library."""
+        _check(status, self._lib)
 
     def step(self, lr: float = -1.0, stream=None):
         self._check(self._lib.muon_step(self._h, ctypes.c_float(lr), self._stream(stream)))
