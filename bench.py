@@ -224,6 +224,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clock", action="store_true", help="skip reading the shader clock (profiled runs)")
+    ap.add_argument("--graph", action="store_true", help="time replays of the step captured in a HIP graph")
     ap.add_argument("--workload", default="gpt2s", choices=["gpt2s", "gpt2s_aux", "square", "gpt2xl", "conv", "tiny", "nmuon"],
                     help="weight set to step (the headline metric is quoted on gpt2s)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -296,11 +297,24 @@ def main():
     for _ in range(args.warmup):
         st.step()
     torch.cuda.synchronize(dev)
+    run_step = st.step
+    if args.graph:
+        # the whole step (both lanes' fork and join included) captured once
+        # in a HIP graph and replayed: no host launch work between kernels
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream(dev)
+        with torch.cuda.graph(graph, stream=cap):
+            st.step()
+        torch.cuda.synchronize(dev)
+        run_step = graph.replay
+        for _ in range(max(1, args.warmup)):
+            run_step()
+        torch.cuda.synchronize(dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        st.step()
+        run_step()
     ev1.record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
@@ -445,7 +459,7 @@ def main():
         "config": {"workload": WORKLOAD_TEXT[args.workload],
                    "matrices": sum(1 for s in wl.tensors if s.kind == "muon"), "params": elems,
                    "adamw_params": sum(s.rows * s.cols for s in wl.tensors if s.kind == "adamw"),
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "launch": "graph" if args.graph else "eager"},
         "matrices_per_s": round(sum(1 for s in wl.tensors if s.kind == "muon") * 1000.0 / ms_per_step, 1),
         "ns_tflops": round(ns_tflop / (ns_ms * 1e-3), 2),
         "ns_frac_bf16_peak": round(ns_tflop / (ns_ms * 1e-3) / PEAK_BF16_TFLOPS, 4),

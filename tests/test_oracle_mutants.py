@@ -110,7 +110,22 @@ def _muon_decay_after_update(W, O, lr, weight_decay, scale):
     return W1 - lr * weight_decay * W1
 
 
+_ORIG_SCALE = orc.shape_scale
+
+
+def _scale_rows_cols_exchanged(rows, cols, mode=orc.SCALE_ORIGINAL):
+    return _ORIG_SCALE(cols, rows, mode) if mode == orc.SCALE_ORIGINAL else _ORIG_SCALE(rows, cols, mode)
+
+
+def _scale_match_uses_min(rows, cols, mode=orc.SCALE_ORIGINAL):
+    if mode == orc.SCALE_MATCH_RMS_ADAMW:
+        return float(0.2 * np.sqrt(min(rows, cols)))
+    return _ORIG_SCALE(rows, cols, mode)
+
+
 MUTANTS = {
+    "scale_rows_cols_exchanged": ("shape_scale", _scale_rows_cols_exchanged),
+    "scale_match_rms_uses_min": ("shape_scale", _scale_match_uses_min),
     "muon_decay_after_update": ("apply_update", _muon_decay_after_update),
     "adam_no_bias_correction": ("adamw_update", _adam_no_bias_correction),
     "adam_eps_inside_sqrt": ("adamw_update", _adam_eps_in_sqrt),
@@ -137,6 +152,7 @@ PIN_TESTS = [
     pins.test_momentum_geometric_series,
     pins.test_split_rows_blocks_are_independent,
     pins.test_update_decays_the_pre_update_weight,
+    pins.test_shape_scale_rms_properties,
     pins.test_adamw_first_step_is_a_signed_step,
     pins.test_adamw_constant_gradient_keeps_the_signed_step,
     pins.test_adamw_first_moment_off_sees_every_gradient_alone,

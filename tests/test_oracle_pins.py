@@ -283,6 +283,30 @@ def test_shape_scale_conventions():
     assert abs(orc.shape_scale(768, 3072, orc.SCALE_MATCH_RMS_ADAMW) - 0.2 * np.sqrt(3072)) < 1e-12
 
 
+def test_shape_scale_rms_properties():
+    """What each named convention does to the update's RMS, checked on
+    exactly semi-orthogonal matrices (all singular values 1, from the
+    library's QR) rather than by retyping the factors.  The blog's guidance
+    section names an RMS-matching variant: its scaled update must have one
+    RMS whatever the shape.  The original convention leaves the RMS of the
+    scaled update depending on the input width only (1/sqrt(cols)), so a
+    factor with rows and cols exchanged, or sqrt(min) for sqrt(max), fails.
+    The common RMS level of the matching variant (0.2) stays a reading."""
+    rng = np.random.default_rng(77)
+    shapes = [(64, 64), (48, 192), (192, 48), (100, 300), (300, 100), (7, 40)]
+    rms_match, rms_orig = [], []
+    for r, c in shapes:
+        q, _ = np.linalg.qr(rng.standard_normal((max(r, c), min(r, c))))
+        O = q if r >= c else q.T                      # r x c, orthonormal columns or rows
+        assert np.allclose(np.linalg.svd(O, compute_uv=False), 1.0, atol=1e-12)
+        rms = lambda X: float(np.sqrt(np.mean(X * X)))
+        rms_match.append(rms(orc.shape_scale(r, c, orc.SCALE_MATCH_RMS_ADAMW) * O))
+        rms_orig.append(rms(orc.shape_scale(r, c, orc.SCALE_ORIGINAL) * O) * np.sqrt(c))
+    assert max(rms_match) - min(rms_match) <= 1e-12 * max(rms_match)
+    assert abs(rms_match[0] - 0.2) <= 1e-12                  # the reading's level
+    assert np.allclose(rms_orig, 1.0, rtol=1e-12, atol=0)
+
+
 # -- bfloat16 rounding vs the library's conversion ----------------------------
 
 def test_bf16_rounding_matches_library():
