@@ -69,16 +69,22 @@ typedef enum {
 
 typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype_t;
 
-/* Shape-dependent lr factor.  The pages name several conventions without
- * printing a formula; the library offers:
+/* Shape-dependent lr factor.  The pages name three conventions (Muon blog,
+ * the practical-guidance section: the original implementation's, an
+ * RMS-matching variant and a theoretical rule) without printing a formula;
+ * the library offers:
  *   NONE            1
  *   ORIGINAL        sqrt(max(1, rows/cols))          (default)
  *   MATCH_RMS_ADAMW 0.2*sqrt(max(rows, cols))
+ *   SPECTRAL        sqrt(rows/cols): a semi-orthogonal update then has RMS->RMS
+ *                   operator norm 1 (blog section 4 defines that norm as
+ *                   sqrt(d_in/d_out) times the spectral norm; rows = d_out)
  * rows/cols are those of the orthogonalised block (split_rows if set). */
 typedef enum {
   MUON_SCALE_NONE = 0,
   MUON_SCALE_ORIGINAL = 1,
-  MUON_SCALE_MATCH_RMS_ADAMW = 2
+  MUON_SCALE_MATCH_RMS_ADAMW = 2,
+  MUON_SCALE_SPECTRAL = 3
 } muon_scale_t;
 
 /* Momentum form (the pages give "momentum 0.95, nesterov" only):

@@ -24,7 +24,7 @@ STATUS_NAMES = {
     7: "MUON_ERR_UNSUPPORTED", 8: "MUON_ERR_HIP", 9: "MUON_ERR_BAD_ARG",
 }
 MUON_F32, MUON_BF16 = 0, 1
-SCALE_NONE, SCALE_ORIGINAL, SCALE_MATCH_RMS_ADAMW = 0, 1, 2
+SCALE_NONE, SCALE_ORIGINAL, SCALE_MATCH_RMS_ADAMW, SCALE_SPECTRAL = 0, 1, 2, 3
 MOM_EMA, MOM_SGD = 0, 1
 KIND_MUON, KIND_ADAMW = 0, 1
 

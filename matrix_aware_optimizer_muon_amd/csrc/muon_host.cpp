@@ -141,6 +141,7 @@ float shape_scale(int64_t rows, int64_t cols, int mode) {
     case MUON_SCALE_NONE: return 1.f;
     case MUON_SCALE_ORIGINAL: return std::sqrt(std::max(1.0, double(rows) / double(cols)));
     case MUON_SCALE_MATCH_RMS_ADAMW: return float(0.2 * std::sqrt(double(std::max(rows, cols))));
+    case MUON_SCALE_SPECTRAL: return float(std::sqrt(double(rows) / double(cols)));
     default: return 1.f;
   }
 }
@@ -160,7 +161,7 @@ muon_status_t validate(const muon_tensor_t* ts, int32_t n, const muon_precond_t*
   // the square phase folds b A into c (A A + (b/c) A)
   if (hp->ns_steps > 0 && hp->ns_c == 0.f)
     return fail(MUON_ERR_BAD_ARG, "ns_c must be nonzero (the quintic's A^2 coefficient)");
-  if (hp->scale_mode < MUON_SCALE_NONE || hp->scale_mode > MUON_SCALE_MATCH_RMS_ADAMW)
+  if (hp->scale_mode < MUON_SCALE_NONE || hp->scale_mode > MUON_SCALE_SPECTRAL)
     return fail(MUON_ERR_BAD_ARG, "unknown scale_mode");
   if (hp->momentum_form != MUON_MOM_EMA && hp->momentum_form != MUON_MOM_SGD)
     return fail(MUON_ERR_BAD_ARG, "unknown momentum_form");

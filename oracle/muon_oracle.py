@@ -63,6 +63,7 @@ DEFAULT_EPS = 1e-7
 SCALE_NONE = "none"
 SCALE_ORIGINAL = "original"
 SCALE_MATCH_RMS_ADAMW = "match_rms_adamw"
+SCALE_SPECTRAL = "spectral"
 
 
 # ----------------------------------------------------------------------------
@@ -185,6 +186,9 @@ def shape_scale(rows, cols, mode=SCALE_ORIGINAL):
     """Shape-dependent learning-rate factor.  READING: the pages name three
     conventions without printing a formula; "original" is
     sqrt(max(1, rows/cols)), "match_rms_adamw" is 0.2*sqrt(max(rows, cols)),
+    "spectral" (the theoretical rule) is sqrt(rows/cols), the factor that
+    gives a semi-orthogonal update an RMS->RMS operator norm of 1 under the
+    blog's section-4 definition of that norm (rows = output width), and
     "none" is 1."""
     if mode == SCALE_NONE:
         return 1.0
@@ -192,6 +196,8 @@ def shape_scale(rows, cols, mode=SCALE_ORIGINAL):
         return float(np.sqrt(max(1.0, rows / cols)))
     if mode == SCALE_MATCH_RMS_ADAMW:
         return float(0.2 * np.sqrt(max(rows, cols)))
+    if mode == SCALE_SPECTRAL:
+        return float(np.sqrt(rows / cols))
     raise ValueError(f"unknown scale mode {mode!r}")
 
 

@@ -7,7 +7,7 @@ import numpy as np
 
 from oracle import muon_oracle as orc
 
-SCALE_NAMES = {0: orc.SCALE_NONE, 1: orc.SCALE_ORIGINAL, 2: orc.SCALE_MATCH_RMS_ADAMW}
+SCALE_NAMES = {0: orc.SCALE_NONE, 1: orc.SCALE_ORIGINAL, 2: orc.SCALE_MATCH_RMS_ADAMW, 3: orc.SCALE_SPECTRAL}
 
 
 def say(msg):

@@ -184,7 +184,7 @@ def test_strided_rows(dtype):
 
 
 @pytest.mark.parametrize("variant", ["sgd", "no_nesterov", "ns0", "ns1", "ns3", "scale_none",
-                                     "scale_rms", "lr_mult", "wd0", "lr0", "lr_override"])
+                                     "scale_rms", "scale_spectral", "lr_mult", "wd0", "lr0", "lr_override"])
 def test_hyperparameter_variants(variant):
     shapes = [(200, 136), (136, 200), (3 * 64, 64)]
     say(f"case: variant {variant}")
@@ -198,6 +198,7 @@ def test_hyperparameter_variants(variant):
     if variant == "ns3": kw = dict(ns_steps=3)
     if variant == "scale_none": kw = dict(scale_mode=B.SCALE_NONE)
     if variant == "scale_rms": kw = dict(scale_mode=B.SCALE_MATCH_RMS_ADAMW)
+    if variant == "scale_spectral": kw = dict(scale_mode=B.SCALE_SPECTRAL)
     if variant == "wd0": kw = dict(weight_decay=0.0)
     if variant == "lr0": lr = 0.0
     if variant == "lr_override": lr = 0.05

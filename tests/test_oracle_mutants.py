@@ -123,7 +123,14 @@ def _scale_match_uses_min(rows, cols, mode=orc.SCALE_ORIGINAL):
     return _ORIG_SCALE(rows, cols, mode)
 
 
+def _scale_spectral_inverted(rows, cols, mode=orc.SCALE_ORIGINAL):
+    if mode == orc.SCALE_SPECTRAL:
+        return float(np.sqrt(cols / rows))
+    return _ORIG_SCALE(rows, cols, mode)
+
+
 MUTANTS = {
+    "scale_spectral_inverted": ("shape_scale", _scale_spectral_inverted),
     "scale_rows_cols_exchanged": ("shape_scale", _scale_rows_cols_exchanged),
     "scale_match_rms_uses_min": ("shape_scale", _scale_match_uses_min),
     "muon_decay_after_update": ("apply_update", _muon_decay_after_update),

@@ -281,6 +281,7 @@ def test_shape_scale_conventions():
     assert orc.shape_scale(3072, 768) == 2.0
     assert orc.shape_scale(7, 9, orc.SCALE_NONE) == 1.0
     assert abs(orc.shape_scale(768, 3072, orc.SCALE_MATCH_RMS_ADAMW) - 0.2 * np.sqrt(3072)) < 1e-12
+    assert orc.shape_scale(512, 512, orc.SCALE_SPECTRAL) == 1.0
 
 
 def test_shape_scale_rms_properties():
@@ -291,10 +292,15 @@ def test_shape_scale_rms_properties():
     RMS whatever the shape.  The original convention leaves the RMS of the
     scaled update depending on the input width only (1/sqrt(cols)), so a
     factor with rows and cols exchanged, or sqrt(min) for sqrt(max), fails.
-    The common RMS level of the matching variant (0.2) stays a reading."""
+    The common RMS level of the matching variant (0.2) stays a reading.
+    The theoretical rule is held to the blog's section-4 definitions: with
+    ||x||_RMS = sqrt(mean(x^2)), the RMS->RMS operator norm of a d_out x d_in
+    matrix is the largest ratio ||M x||_RMS / ||x||_RMS, here measured
+    directly from the spectral norm of the library's SVD and the two RMS
+    normalisations, and the scaled update must reach exactly 1."""
     rng = np.random.default_rng(77)
     shapes = [(64, 64), (48, 192), (192, 48), (100, 300), (300, 100), (7, 40)]
-    rms_match, rms_orig = [], []
+    rms_match, rms_orig, opnorm = [], [], []
     for r, c in shapes:
         q, _ = np.linalg.qr(rng.standard_normal((max(r, c), min(r, c))))
         O = q if r >= c else q.T                      # r x c, orthonormal columns or rows
@@ -302,9 +308,13 @@ def test_shape_scale_rms_properties():
         rms = lambda X: float(np.sqrt(np.mean(X * X)))
         rms_match.append(rms(orc.shape_scale(r, c, orc.SCALE_MATCH_RMS_ADAMW) * O))
         rms_orig.append(rms(orc.shape_scale(r, c, orc.SCALE_ORIGINAL) * O) * np.sqrt(c))
+        # max over x of ||S x||_RMS / ||x||_RMS = sigma_max(S) * sqrt(c) / sqrt(r), S = scaled O
+        S = orc.shape_scale(r, c, orc.SCALE_SPECTRAL) * O
+        opnorm.append(float(np.linalg.norm(S, 2)) * np.sqrt(c) / np.sqrt(r))
     assert max(rms_match) - min(rms_match) <= 1e-12 * max(rms_match)
     assert abs(rms_match[0] - 0.2) <= 1e-12                  # the reading's level
     assert np.allclose(rms_orig, 1.0, rtol=1e-12, atol=0)
+    assert np.allclose(opnorm, 1.0, rtol=1e-12, atol=0)
 
 
 # -- bfloat16 rounding vs the library's conversion ----------------------------
