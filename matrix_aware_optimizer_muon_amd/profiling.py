@@ -260,6 +260,70 @@ def traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes, co
     }
 
 
+def _command_block(commands):
+    return ["Commands (repository root on one MI355X, `libmuon.so` built):", "", "```", *commands, "```", ""]
+
+
+def markers_markdown(trace_dir, title, commands):
+    """Named host-side ranges (rocprofv3 --marker-trace): count and mean
+    duration per range name, largest total first."""
+    rows = {}
+    with open(_one(trace_dir, "*marker_api_trace.csv")) as f:
+        recs = list(csv.DictReader(f))
+    for r in recs:
+        e = rows.setdefault(r["Function"], [0, 0.0])
+        e[0] += 1
+        e[1] += (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    out = [f"# {title}", ""] + _command_block(commands) + [
+        "The library pushes a named host-side range around each step and each launch (`Range` in "
+        "`muon_host.cpp`). Durations are host time inside the enclosed enqueue calls. The host runs ahead of the "
+        "GPU until the runtime's queue is full; from then on each enqueue waits for a slot, so these durations "
+        "track the kernels' own (the kernel trace of the same run has those).", "",
+        "| range | count | mean host µs |", "|---|---:|---:|"]
+    for name, (n, us) in sorted(rows.items(), key=lambda kv: -kv[1][1]):
+        out.append(f"| `{name}` | {n} | {us / n:.1f} |")
+    return "\n".join(out) + "\n"
+
+
+BLAS_LABELS = {
+    "gpt2s": "GPT-2-small (72 units: 48 of 768x768, 24 of 768x3072)",
+    "square": "one 4096x4096 unit",
+    "gpt2xl": "GPT-2-XL (288 units: 192 of 1600x1600, 96 of 1600x6400)",
+}
+
+
+def blas_markdown(bench_lines, commands):
+    """Vendor BLAS beside the library's Newton-Schulz phases, from bench.py
+    --blas-context lines (workload name = file stem after "blas_")."""
+    recs = []
+    for path in bench_lines:
+        with open(path) as f:
+            line = [l for l in f.read().splitlines() if l.startswith("{")][-1]
+        w = os.path.splitext(os.path.basename(path))[0].split("blas_", 1)[-1]
+        recs.append((w, json.loads(line)))
+    lib = recs[0][1]["blas_context"]["library"]
+    out = ["# Vendor BLAS beside the library's Newton-Schulz phases (context, not part of the step)", "",
+           "The same products as one Newton-Schulz iteration, timed with the vendor BLAS: one batched `torch.bmm` "
+           "in bf16 per distinct unit shape (hipBLASLt underneath), for X X^T (full product), A A and B X of every "
+           "bf16 unit, 20 repetitions after 3 warm-up calls, on the bench's stream. `library ms` is the library's "
+           "time for the same phase, all lanes, one launch at a time (the bench's timing pass, averaged over the "
+           "five iterations). The library's Gram and square compute only the tiles on and above the diagonal and "
+           "store the rest mirrored; its B X also folds in a X, reads and writes the int8 master corrections and, "
+           f"in the last iteration, applies the weight update. Library: {lib}.", ""] + _command_block(commands) + [
+           f"Kernel sources: {kernel_source_hash()}.", "",
+           "| workload | phase | vendor ms | vendor TFLOP/s | vendor % of bf16 peak | library ms | "
+           "vendor / library time |", "|---|---|---:|---:|---:|---:|---:|"]
+    for w, d in recs:
+        for ph in ("gram", "square", "bx"):
+            e = d["blas_context"][ph]
+            out.append(f"| {BLAS_LABELS.get(w, w)} | {ph} | {e['vendor_ms']:.4f} | {e['vendor_tflops']:.0f} | "
+                       f"{100 * e['vendor_frac_bf16_peak']:.1f} | {e['library_ms']:.4f} | "
+                       f"{e['vendor_ms'] / e['library_ms']:.2f} |")
+    out += ["", "Shader clock read during each run's timed steps (MHz): " +
+            ", ".join(f"{w} {d.get('gpu_clock_mhz')}" for w, d in recs) + "."]
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(prog="python -m matrix_aware_optimizer_muon_amd.profiling")
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -280,11 +344,24 @@ def main(argv=None):
     c.add_argument("--copy-bytes", type=int, required=True)
     c.add_argument("--command", action="append", default=[])
     c.add_argument("--out")
+    k = sub.add_parser("markers")
+    k.add_argument("dir")
+    k.add_argument("--title", default="roctx ranges")
+    k.add_argument("--command", action="append", default=[])
+    k.add_argument("--out")
+    b = sub.add_parser("blas")
+    b.add_argument("lines", nargs="+", help="bench.py --blas-context outputs named blas_<workload>.json")
+    b.add_argument("--command", action="append", default=[])
+    b.add_argument("--out")
     args = ap.parse_args(argv)
     if args.cmd == "trace":
         text = trace_markdown(args.dir, args.title, args.command)
     elif args.cmd == "mfma":
         text = mfma_markdown(args.dir, args.title, args.command, args.peak_tflops)
+    elif args.cmd == "markers":
+        text = markers_markdown(args.dir, args.title, args.command)
+    elif args.cmd == "blas":
+        text = blas_markdown(args.lines, args.command)
     else:
         text = json.dumps(traffic(args.fetch, args.write, args.copy_fetch, args.copy_write, args.copy_bytes,
                                   args.command), indent=1) + "\n"
