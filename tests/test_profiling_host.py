@@ -124,6 +124,36 @@ def test_mfma_table_from_counters(tmp_path):
     assert "| bx | 2 | 50.00 | 100.0 | 500 | 20.0 | 25.0 |" in P.mfma_markdown(str(tmp_path), "t", "cmd", 2500.0)
 
 
+def test_marker_table_counts_and_means(tmp_path):
+    d = tmp_path / "markers"
+    fields = ["Domain", "Function", "Process_Id", "Thread_Id", "Correlation_Id", "Start_Timestamp", "End_Timestamp"]
+    rows = [{"Domain": "MARKER_CORE_RANGE_API", "Function": n, "Process_Id": 1, "Thread_Id": 1,
+             "Correlation_Id": i, "Start_Timestamp": t0, "End_Timestamp": t0 + dur}
+            for i, (n, t0, dur) in enumerate([("muon.step", 0, 9000), ("muon.gram", 10, 2000),
+                                              ("muon.gram", 5000, 4000), ("muon.bx", 9000, 1500)])]
+    _write(str(d / "run_marker_api_trace.csv"), fields, rows)
+    text = P.markers_markdown(str(d), "roctx", ["cmd"])
+    lines = [l for l in text.splitlines() if l.startswith("| `")]
+    # largest total first; means in microseconds (timestamps in ns)
+    assert lines == ["| `muon.step` | 1 | 9.0 |", "| `muon.gram` | 2 | 3.0 |", "| `muon.bx` | 1 | 1.5 |"]
+
+
+def test_blas_table_from_bench_lines(tmp_path):
+    import json
+    line = {"gpu_clock_mhz": 2000, "blas_context": {
+        "library": "torch.bmm bf16", "shapes": 1,
+        "gram": {"vendor_ms": 0.2, "vendor_tflops": 500.0, "vendor_frac_bf16_peak": 0.2, "library_ms": 0.1},
+        "square": {"vendor_ms": 0.1, "vendor_tflops": 400.0, "vendor_frac_bf16_peak": 0.16, "library_ms": 0.1},
+        "bx": {"vendor_ms": 0.3, "vendor_tflops": 600.0, "vendor_frac_bf16_peak": 0.24, "library_ms": 0.4}}}
+    f = tmp_path / "blas_square.json"
+    f.write_text("warning text\n" + json.dumps(line) + "\n")
+    text = P.blas_markdown([str(f)], ["cmd"])
+    rows = [l for l in text.splitlines() if l.startswith("| one 4096x4096")]
+    assert [r.split(" | ")[1] for r in rows] == ["gram", "square", "bx"]
+    assert rows[0].endswith("| 2.00 |") and rows[2].endswith("| 0.75 |")
+    assert "square 2000" in text and P.kernel_source_hash() in text
+
+
 def test_bench_work_counts():
     # symmetric products: Gram m(m+1)n, square m^2(m+1), update 2m^2n
     f = bench.ns_flops(768, 3072)
