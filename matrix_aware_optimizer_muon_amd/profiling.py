@@ -260,6 +260,72 @@ def traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes, co
     }
 
 
+LDS_COUNTERS = ["SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS", "SQ_INSTS_MFMA", "SQ_WAIT_INST_LDS",
+                "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"]
+
+
+def lds_table(dirpath):
+    """Per kernel kind, from one `--pmc` pass of LDS_COUNTERS:
+      lds_busy_pct  cycles the CU's LDS serves indexed accesses, as a share
+                    of the CU cycles of the counter window (the counter is
+                    summed over every CU; GRBM_GUI_ACTIVE over the XCDs);
+      conflict_pct  bank-conflict cycles as a share of those LDS cycles;
+      lds_per_mfma  LDS instructions (the direct-to-LDS copies included) per
+                    MFMA instruction;
+      wait_lds_pct  wave time spent waiting to issue an LDS instruction, and
+      wait_any_pct  waiting to issue any instruction, as shares of the wave
+                    time (both counters and SQ_WAVE_CYCLES are in units of
+                    four cycles)."""
+    simds, xcc, _ = _agent(dirpath)
+    cus = max(1, simds // 4)
+    disp = {}
+    with open(_one(dirpath, "*counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            d = disp.setdefault(key, {"kind": kernel_kind(r.get("Kernel_Name", "")),
+                                      "ns": _num(r, "End_Timestamp") - _num(r, "Start_Timestamp")})
+            c = r.get("Counter_Name")
+            d[c] = d.get(c, 0.0) + float(r["Counter_Value"])
+    rows = {}
+    for d in disp.values():
+        e = rows.setdefault(d["kind"], {"dispatches": 0, "ns": 0.0, **{c: 0.0 for c in LDS_COUNTERS}})
+        e["dispatches"] += 1
+        e["ns"] += d["ns"]
+        for c in LDS_COUNTERS:
+            e[c] += d.get(c, 0.0)
+    out = {}
+    for k, e in rows.items():
+        gui = e["GRBM_GUI_ACTIVE"] / xcc
+        idx, wave = e["SQ_LDS_IDX_ACTIVE"], e["SQ_WAVE_CYCLES"]
+        out[k] = {"dispatches": e["dispatches"], "avg_us": e["ns"] / e["dispatches"] / 1e3,
+                  "lds_busy_pct": 100.0 * idx / (gui * cus) if gui else float("nan"),
+                  "conflict_pct": 100.0 * e["SQ_LDS_BANK_CONFLICT"] / idx if idx else float("nan"),
+                  "lds_per_mfma": e["SQ_INSTS_LDS"] / e["SQ_INSTS_MFMA"] if e["SQ_INSTS_MFMA"] else float("nan"),
+                  "wait_lds_pct": 100.0 * e["SQ_WAIT_INST_LDS"] / wave if wave else float("nan"),
+                  "wait_any_pct": 100.0 * e["SQ_WAIT_INST_ANY"] / wave if wave else float("nan")}
+    return out
+
+
+def lds_markdown(dirpath, title, commands):
+    rows = lds_table(dirpath)
+    out = [f"# {title}", ""] + _command_block(commands) + [
+        "LDS busy = SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE per XCD x CUs); conflicts = SQ_LDS_BANK_CONFLICT / "
+        "SQ_LDS_IDX_ACTIVE; LDS per MFMA = SQ_INSTS_LDS / SQ_INSTS_MFMA (the direct-to-LDS copies count as LDS "
+        "instructions); waits = SQ_WAIT_INST_LDS and SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES. Dispatches run one at a "
+        f"time while counters are collected; the counter window is a little longer than a dispatch. Kernel "
+        f"sources: {kernel_source_hash()}.", "",
+        "| kernel | dispatches | avg µs | LDS busy % | bank conflicts % of LDS cycles | LDS instr. per MFMA | "
+        "wave time waiting for LDS issue % | waiting for any issue % |",
+        "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for k, e in sorted(rows.items(), key=lambda kv: -kv[1]["avg_us"] * kv[1]["dispatches"]):
+        if k in ("copy", "fill"):
+            continue
+        out.append(f"| {k} | {e['dispatches']} | {e['avg_us']:.1f} | {e['lds_busy_pct']:.1f} | "
+                   f"{e['conflict_pct']:.1f} | {e['lds_per_mfma']:.2f} | {e['wait_lds_pct']:.1f} | "
+                   f"{e['wait_any_pct']:.1f} |")
+    return "\n".join(out) + "\n"
+
+
 def _command_block(commands):
     return ["Commands (repository root on one MI355X, `libmuon.so` built):", "", "```", *commands, "```", ""]
 
@@ -344,6 +410,11 @@ def main(argv=None):
     c.add_argument("--copy-bytes", type=int, required=True)
     c.add_argument("--command", action="append", default=[])
     c.add_argument("--out")
+    l = sub.add_parser("lds")
+    l.add_argument("dir")
+    l.add_argument("--title", default="LDS counters")
+    l.add_argument("--command", action="append", default=[])
+    l.add_argument("--out")
     k = sub.add_parser("markers")
     k.add_argument("dir")
     k.add_argument("--title", default="roctx ranges")
@@ -358,6 +429,8 @@ def main(argv=None):
         text = trace_markdown(args.dir, args.title, args.command)
     elif args.cmd == "mfma":
         text = mfma_markdown(args.dir, args.title, args.command, args.peak_tflops)
+    elif args.cmd == "lds":
+        text = lds_markdown(args.dir, args.title, args.command)
     elif args.cmd == "markers":
         text = markers_markdown(args.dir, args.title, args.command)
     elif args.cmd == "blas":
