@@ -124,6 +124,24 @@ def test_mfma_table_from_counters(tmp_path):
     assert "| bx | 2 | 50.00 | 100.0 | 500 | 20.0 | 25.0 |" in P.mfma_markdown(str(tmp_path), "t", "cmd", 2500.0)
 
 
+def test_lds_table_shares(tmp_path):
+    d = tmp_path / "lds"
+    _write(str(d / "run_agent_info.csv"), ["Simd_Count", "Num_Xcc", "Max_Engine_Clk_Fcompute"],
+           [{"Simd_Count": 1024, "Num_Xcc": 8, "Max_Engine_Clk_Fcompute": 2400}])
+    fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    vals = {"SQ_LDS_IDX_ACTIVE": 2560.0, "SQ_LDS_BANK_CONFLICT": 256.0, "SQ_INSTS_LDS": 300.0,
+            "SQ_INSTS_MFMA": 200.0, "SQ_WAIT_INST_LDS": 30.0, "SQ_WAIT_INST_ANY": 250.0, "SQ_WAVE_CYCLES": 1000.0,
+            "GRBM_GUI_ACTIVE": 800.0}
+    rows = [{"Dispatch_Id": 1, "Kernel_Name": BX, "Counter_Name": c, "Counter_Value": v,
+             "Start_Timestamp": 0, "End_Timestamp": 5000} for c, v in vals.items()]
+    _write(str(d / "run_counter_collection.csv"), fields, rows)
+    e = P.lds_table(str(d))["bx"]
+    # 2560 LDS cycles over 256 CUs x (800 / 8) cycles: 10 %
+    assert abs(e["lds_busy_pct"] - 10.0) < 1e-9 and abs(e["conflict_pct"] - 10.0) < 1e-9
+    assert abs(e["lds_per_mfma"] - 1.5) < 1e-12 and abs(e["wait_lds_pct"] - 3.0) < 1e-9
+    assert abs(e["wait_any_pct"] - 25.0) < 1e-9 and abs(e["avg_us"] - 5.0) < 1e-9
+
+
 def test_marker_table_counts_and_means(tmp_path):
     d = tmp_path / "markers"
     fields = ["Domain", "Function", "Process_Id", "Thread_Id", "Correlation_Id", "Start_Timestamp", "End_Timestamp"]
