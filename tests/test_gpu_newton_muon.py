@@ -335,3 +335,78 @@ def test_cholesky_inverse_of_an_exact_second_moment(d):
     # rounding, 2^-24 relative), up to float64 rounding in the factorisation
     bound = 2.0 ** -24 * np.abs(ref) + kappa * 1e-15 * np.max(np.abs(ref))
     assert bool(np.all(np.abs(Sinv_dev - ref) <= bound))
+
+
+# The preconditioner at its largest size (d = 16384, the planner's limit: the
+# float64 factor arrays pass 2 GiB).  The oracle cannot factor that in
+# seconds, so S is built with a closed-form inverse.  Activations of N = 2d
+# rows: 2 e_i for i < d, one row v of small integers, zeros after it, so
+# X^T X / N + damping = alpha I + beta v v^T, exact in float32, and by
+# Sherman-Morrison S^-1 = I / alpha - beta / (alpha (alpha + beta |v|^2)) v v^T
+# (Newton-Muon README, "What Is Newton-Muon?": G <- G S^-1).
+@pytest.mark.parametrize("d", [4096, 16384])
+def test_largest_preconditioner_closed_form(d):
+    say(f"case: Newton-Muon preconditioner at d = {d}, closed-form S^-1 (Sherman-Morrison)")
+    n, lam = 2 * d, 0.25
+    rng = np.random.default_rng(7070 + d)
+    v = rng.integers(-3, 4, size=d).astype(np.float64)
+    acts = torch.zeros(n, d, dtype=torch.bfloat16, device="cuda")
+    acts[torch.arange(d, device="cuda"), torch.arange(d, device="cuda")] = 2.0
+    acts[d] = torch.from_numpy(v).to(device="cuda", dtype=torch.bfloat16)
+    alpha, beta = 4.0 / n + lam, 1.0 / n
+    vv = float(v @ v)
+    gamma = beta / (alpha * (alpha + beta * vv))
+    kappa = (alpha + beta * vv) / alpha
+
+    rows = 64
+    gbits = synth.to_bf16_bits(rng.standard_normal((rows, d)))
+    g = to_device(torch, gbits, "bf16")
+    w = torch.zeros(rows, d, dtype=torch.bfloat16, device="cuda")
+    m = torch.zeros(rows, d, device="cuda")
+    p = B.MuonPrecond()
+    p.d, p.nblocks = d, 1
+    hp = mm.default_hparams()
+    st = mm.MuonStep([mm.tensor_desc(w, g, m, precond=0)], hp, preconds=[p])
+    say(f"  workspace {st.workspace_bytes / 2**30:.1f} GiB; refresh and step")
+    st.precond_refresh(0, 0, acts, damping=lam)
+    st.step()
+    torch.cuda.synchronize()
+    assert st.flags() == 0
+    say("  done; comparing")
+    pc = st.plan()["preconds"][0]
+    dp = pc["dp"]
+    ws = st.workspace
+    S_dev = ws[pc["s_offset"]:pc["s_offset"] + 4 * dp * dp].view(torch.float32).reshape(dp, dp)[:d, :d]
+    planes = ws[pc["sinv_offset"]:pc["sinv_offset"] + 6 * dp * dp].view(torch.bfloat16).reshape(3, dp, dp)
+    Sinv_dev = planes[:, :d, :d].to(torch.float64).sum(0)
+    del acts
+
+    # S exactly: every entry is a small integer times 2^-k plus the damping
+    vt = torch.from_numpy(v).cuda()
+    S_ref = (torch.outer(vt, vt) * beta + alpha * torch.eye(d, dtype=torch.float64, device="cuda"))
+    s_exact = bool(torch.equal(S_dev.to(torch.float64), S_ref))
+    del S_ref
+    # S^-1: one float32 rounding of each float64 value (2^-24 relative),
+    # plus the float64 factorisation's backward error, d * kappa * 1e-16 of
+    # the largest element
+    ref = torch.eye(d, dtype=torch.float64, device="cuda") / alpha - gamma * torch.outer(vt, vt)
+    top = float(ref.abs().max())
+    err = (Sinv_dev - ref).abs()
+    bound = 2.0 ** -24 * ref.abs() + d * kappa * 1e-16 * top
+    viol = int((err > bound).sum())
+    e_sinv = float(torch.linalg.norm(Sinv_dev - ref) / torch.linalg.norm(ref))
+    del err, bound, ref
+    # P = G S^-1 from the momentum buffer (zero start: M' = (1 - mu) P),
+    # against the float64 product with the GPU's own S^-1
+    P = m.to(torch.float64) / (1.0 - hp.momentum)
+    G64 = torch.from_numpy(orc.bf16_bits_to_f64(gbits)).cuda()
+    PR = G64 @ Sinv_dev
+    e_p = float(torch.linalg.norm(P - PR) / torch.linalg.norm(PR))
+    st.close()
+    say(f"  kappa {kappa:.2f}: S exact {s_exact}; S^-1 rel_F {e_sinv:.2e}, elements over the bound {viol}; "
+        f"P rel to G S^-1 {e_p:.2e}")
+    del Sinv_dev, S_dev, planes, ws, st
+    torch.cuda.empty_cache()
+    assert s_exact
+    assert e_sinv <= 6e-8 + d * kappa * 1e-16 and viol == 0
+    assert e_p <= 1e-5
