@@ -16,7 +16,10 @@ are held to the bf16 bar, and the momentum to its bar.  Everything off the
 blocks must be exactly zero, in O and in the momentum.  The weights must
 follow the decoupled update (Muon README "Usage"): on the blocks as checked
 element by element from the GPU's own O, and elsewhere as pure decay, at
-sampled positions, bitwise against the oracle's rounding.
+sampled positions, bitwise against the oracle's rounding.  The same step
+also runs on the bounds-checking debug build, whose every GEMM and
+elementwise task checks its tile against the unit's padded sizes and sets a
+flag instead of running past them: no flag may be set.
 """
 
 import numpy as np
@@ -25,6 +28,7 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import matrix_aware_optimizer_muon_amd as mm
+from matrix_aware_optimizer_muon_amd import build
 from oracle import muon_oracle as orc
 from tests.parity_common import SCALE_NAMES, check_w_update_elementwise, oracle_step, rel_f, say
 
@@ -48,10 +52,11 @@ def _layout(orient):
     return (WIDE[1], WIDE[0]), [(c0, r0, w, h) for r0, c0, h, w in BLOCKS_WIDE]
 
 
+@pytest.mark.parametrize("lib", ["release", "debug"])
 @pytest.mark.parametrize("orient", ["wide", "tall"])
-def test_maximum_unit_block_structured(orient):
+def test_maximum_unit_block_structured(orient, lib):
     (R, C), blocks = _layout(orient)
-    say(f"case: maximum unit {R}x{C} bf16 ({orient}), three blocks of gradient, zeros elsewhere")
+    say(f"case: maximum unit {R}x{C} bf16 ({orient}, {lib} build), three blocks of gradient, zeros elsewhere")
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([9300, R, C])))
     gblocks = [orc.f64_to_bf16_bits(rng.standard_normal((h, w)) * s)
                for (_, _, h, w), s in zip(blocks, (1.0, 3.0, 0.5))]
@@ -78,7 +83,8 @@ def test_maximum_unit_block_structured(orient):
     w0_samp = W[si, sj].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
     hp = mm.default_hparams()
-    st = mm.MuonStep([mm.tensor_desc(W, G, M, update_out=O)], hp)
+    st = mm.MuonStep([mm.tensor_desc(W, G, M, update_out=O)], hp,
+                     library=build.DEBUG_LIB if lib == "debug" else None)
     say(f"  workspace {st.workspace_bytes / 2**30:.1f} GiB; stepping")
     st.step()
     torch.cuda.synchronize()
