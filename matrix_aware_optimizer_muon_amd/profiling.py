@@ -130,6 +130,47 @@ def trace_table(dirpath):
     return rows
 
 
+def step_windows(dirpath):
+    """Occupancy of each step in a kernel trace.  Every lane group's first
+    launch of a step is its momentum launch, one per group, and the timed
+    steps run the groups on queues of their own; so the number of queues the
+    momentum launches use is the number per step, and a step starts at every
+    such count of momentum launches and ends where the next starts (the last
+    at its last dispatch).  Per step: its length, the time some kernel is
+    running, the queues it used and, per queue, the idle time between
+    consecutive dispatches on that queue (up to its first dispatch of the
+    next step, where it has one)."""
+    with open(_one(dirpath, "*kernel_trace.csv")) as f:
+        ev = sorted((int(_num(r, "Start_Timestamp")), int(_num(r, "End_Timestamp")),
+                     kernel_kind(r.get("Kernel_Name", "")), r.get("Queue_Id", "")) for r in csv.DictReader(f))
+    mom = [e for e in ev if e[2].startswith("momentum")]
+    per_step = max(1, len({e[3] for e in mom}))
+    firsts = [e[0] for e in mom[::per_step]]
+    out = []
+    for k, a in enumerate(firsts):
+        b = firsts[k + 1] if k + 1 < len(firsts) else None
+        seg = [e for e in ev if e[0] >= a and (b is None or e[0] < b)]
+        nxt = {e[3] for e in ev if b is not None and e[0] >= b and (k + 2 >= len(firsts) or e[0] < firsts[k + 2])}
+        end = b if b is not None else max(e[1] for e in seg)
+        busy, cs, ce = 0, seg[0][0], seg[0][1]
+        for s0, e0, _, _ in seg[1:]:
+            if s0 > ce:
+                busy, cs, ce = busy + ce - cs, s0, e0
+            else:
+                ce = max(ce, e0)
+        busy += min(ce, end) - cs
+        gaps = {}
+        for q in sorted({e[3] for e in seg}):
+            qe = [(e[0], e[1]) for e in seg if e[3] == q]
+            g = sum(max(0, qe[i + 1][0] - qe[i][1]) for i in range(len(qe) - 1))
+            if q in nxt:   # idle until this queue's first launch of the next step
+                g += max(0, end - max(e1 for _, e1 in qe))
+            gaps[q] = g / 1e3
+        out.append({"us": (end - a) / 1e3, "busy_us": busy / 1e3, "dispatches": len(seg), "queues": len(gaps),
+                    "queue_gap_us": gaps})
+    return out
+
+
 def trace_markdown(dirpath, title, command):
     """`command`: one command line, or a list of them."""
     rows = trace_table(dirpath)
@@ -142,6 +183,17 @@ def trace_markdown(dirpath, title, command):
     for k, e in sorted(rows.items(), key=lambda kv: -kv[1]["total_us"]):
         out.append(f"| {k} | {e['calls']} | {e['total_us']:.1f} | {e['avg_us']:.2f} | {e['pct']:.1f} | "
                    f"{e['alone_calls']} | {e['alone_avg_us']:.2f} | {e['grid']} | {e['lds']} |")
+    steps = step_windows(dirpath)
+    if steps:
+        out += ["", "Steps (from the first momentum launch of one step to that of the next, warm-up steps "
+                "included): time some kernel is running, and idle time between consecutive dispatches of each "
+                "queue. Steps on one queue are the timing pass's, one launch at a time.", "",
+                "| step | µs | dispatches | queues | kernel running % | idle between dispatches per queue, µs |",
+                "|---:|---:|---:|---:|---:|---|"]
+        for i, st in enumerate(steps):
+            gaps = ", ".join(f"{v:.1f}" for v in st["queue_gap_us"].values())
+            out.append(f"| {i + 1} | {st['us']:.0f} | {st['dispatches']} | {st['queues']} | "
+                       f"{100.0 * st['busy_us'] / st['us']:.1f} | {gaps} |")
     return "\n".join(out) + "\n"
 
 

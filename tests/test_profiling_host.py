@@ -124,6 +124,26 @@ def test_mfma_table_from_counters(tmp_path):
     assert "| bx | 2 | 50.00 | 100.0 | 500 | 20.0 | 25.0 |" in P.mfma_markdown(str(tmp_path), "t", "cmd", 2500.0)
 
 
+def test_step_windows_busy_share_and_queue_gaps(tmp_path):
+    d = tmp_path / "trace"
+    mom = "void muon::momentum_kernel<false>(muon::UnitDev const*, muon::EwTask const*, muon::K1Params)"
+    fields = ["Kernel_Name", "Queue_Id", "Start_Timestamp", "End_Timestamp"]
+    # step 1: two lanes on two queues, back to back; step 2: one queue with a
+    # 10 us gap between its two launches and a 5 us gap before the next lane
+    ev = [(mom, 1, 0, 100), (mom, 2, 0, 100), (BX, 1, 100, 300), (GRAM, 2, 100, 300),
+          (mom, 1, 1000, 1100), (BX, 1, 1110, 1300), (mom, 1, 1305, 1400), (GRAM, 1, 1400, 2000)]
+    rows = [{"Kernel_Name": k, "Queue_Id": q, "Start_Timestamp": a * 1000, "End_Timestamp": b * 1000}
+            for k, q, a, b in ev]
+    _write(str(d / "run_kernel_trace.csv"), fields, rows)
+    st = P.step_windows(str(d))
+    assert len(st) == 2
+    assert st[0]["queues"] == 2 and st[0]["dispatches"] == 4
+    assert abs(st[0]["us"] - 1000.0) < 1e-9 and abs(st[0]["busy_us"] - 300.0) < 1e-9
+    assert st[0]["queue_gap_us"] == {"1": 700.0, "2": 0.0}
+    assert st[1]["queues"] == 1 and st[1]["dispatches"] == 4
+    assert abs(st[1]["busy_us"] - 985.0) < 1e-9 and st[1]["queue_gap_us"] == {"1": 15.0}
+
+
 def test_lds_table_shares(tmp_path):
     d = tmp_path / "lds"
     _write(str(d / "run_agent_info.csv"), ["Simd_Count", "Num_Xcc", "Max_Engine_Clk_Fcompute"],
