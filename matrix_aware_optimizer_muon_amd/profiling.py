@@ -184,7 +184,7 @@ def trace_markdown(dirpath, title, command):
         out.append(f"| {k} | {e['calls']} | {e['total_us']:.1f} | {e['avg_us']:.2f} | {e['pct']:.1f} | "
                    f"{e['alone_calls']} | {e['alone_avg_us']:.2f} | {e['grid']} | {e['lds']} |")
     steps = step_windows(dirpath)
-    if steps:
+    if 0 < len(steps) <= 40:   # a bench of a few whole steps (not a refresh-dominated run)
         out += ["", "Steps (from the first momentum launch of one step to that of the next, warm-up steps "
                 "included): time some kernel is running, and idle time between consecutive dispatches of each "
                 "queue. Steps on one queue are the timing pass's, one launch at a time.", "",
